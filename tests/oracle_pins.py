@@ -1,0 +1,718 @@
+"""Pins that tie the CPU oracle to what the pages and the mathematics fix.
+
+Each pin raises AssertionError when the oracle disagrees.  They are run
+against the real oracle (tests/test_oracle_pins.py) and against builds of the
+oracle with a planted mistake (tests/test_oracle_mutants.py), where at least
+one pin must fail.
+
+Nothing here computes an expected value with the oracle's own code path:
+expected values come from printed tables (tests/golden), closed forms, exact
+rational arithmetic (tests/ieee_exact.py), element-by-element brute force,
+or torch's CPU bfloat16 conversion.
+"""
+import itertools
+import math
+import os
+import random
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from tests import ieee_exact as X
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+BF16, F32 = oracle.BF16, oracle.F32
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def one_task_flush(W, dtype, rows, pre_div, comm=(None, None), owner=None):
+    """Flush one task covering every column of `rows` ([W, n] bits or floats)."""
+    rows = np.ascontiguousarray(rows)
+    n = rows.shape[1]
+    out = np.zeros_like(rows)
+    if comm[0] is None:
+        cs, cst, tc = [W], [1], 0
+    else:
+        cs, cst, tc = [W, comm[0]], [1, comm[1]], 1
+    ow = None if owner is None else np.array([owner], np.int32)
+    oracle.flush(W, dtype, rows, out, 0, [0], [n], [0], [tc], ow, cs, cst, pre_div)
+    return out
+
+
+def random_bits(rng, dtype, shape, wide=True):
+    """Random finite patterns over a range of exponents, including zeros of
+    both signs and subnormals (bf16 exponent field 0), far from overflow."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint32)
+    for k in range(n):
+        sign = rng.getrandbits(1)
+        pick = rng.random()
+        if pick < 0.05:
+            e = 0
+            man = 0
+        elif pick < 0.2 and wide:
+            e = 0
+            man = rng.getrandbits(7 if dtype == BF16 else 23) or 1
+        elif pick < 0.3 and wide:
+            e = rng.randint(1, 4)
+            man = rng.getrandbits(7 if dtype == BF16 else 23)
+        else:
+            e = rng.randint(110, 135)
+            man = rng.getrandbits(7 if dtype == BF16 else 23)
+        if dtype == BF16:
+            out[k] = (sign << 15) | (e << 7) | man
+        else:
+            out[k] = (sign << 31) | (e << 23) | man
+    if dtype == BF16:
+        return out.astype(np.uint16).reshape(shape)
+    return out.view(np.float32).reshape(shape)
+
+
+def to_floats(dtype, arr):
+    if dtype == BF16:
+        return [X.bf16_bits_to_float(int(b)) for b in np.asarray(arr).ravel()]
+    return [float(v) for v in np.asarray(arr, np.float32).ravel()]
+
+
+def bits_of(dtype, v):
+    return X.float_to_bf16_bits(v) if dtype == BF16 else X.float_to_f32_bits(v)
+
+
+def out_bits(dtype, arr):
+    a = np.asarray(arr)
+    return a.astype(np.uint32) if dtype == BF16 else a.view(np.uint32)
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding
+# ---------------------------------------------------------------------------
+
+def _definitional_bf16(u):
+    """Nearest bf16 neighbour by exact distance (double arithmetic holds every
+    difference exactly), ties to the even pattern; unbounded exponent for the
+    upper neighbour so the overflow threshold falls at max + half an ulp."""
+    u = u.astype(np.uint64)
+    sign = (u >> 31) & 1
+    mag = u & 0x7FFFFFFF
+    e32 = (mag >> 23).astype(np.int64)
+    m32 = (mag & 0x7FFFFF).astype(np.float64)
+    f = np.where(e32 == 0, np.ldexp(m32, -149), np.ldexp(m32 + 2.0 ** 23, (e32 - 150).astype(np.int32)))
+
+    def val16(p):
+        e = (p >> 7).astype(np.int64)
+        m = (p & 0x7F).astype(np.float64)
+        return np.where(e == 0, np.ldexp(m, -133), np.ldexp(m + 128.0, (e - 134).astype(np.int32)))
+
+    lo = (mag >> 16)
+    hi = lo + 1
+    dlo = f - val16(lo)
+    dhi = val16(hi) - f
+    pick = np.where((dhi < dlo) | ((dhi == dlo) & ((lo & 1) == 1)), hi, lo)
+    return ((sign << 15) | pick).astype(np.uint16)
+
+
+def pin_bf16_rounding():
+    rng = np.random.default_rng(11)
+    highs = np.arange(65536, dtype=np.uint64)
+    highs = highs[((highs >> 7) & 0xFF) != 0xFF]          # finite only
+    lows = np.array([0, 1, 2, 0x7FFF, 0x8000, 0x8001, 0xFFFE, 0xFFFF], np.uint64)
+    lows = np.concatenate([lows, rng.integers(0, 65536, 24).astype(np.uint64)])
+    u = ((highs[:, None] << 16) | lows[None, :]).ravel().astype(np.uint32)
+    got = oracle.bf16_round(u.view(np.float32))
+    want = _definitional_bf16(u)
+    bad = np.nonzero(got != want)[0]
+    assert len(bad) == 0, f"bf16 rounding differs at {u[bad[:5]]}: {got[bad[:5]]} vs {want[bad[:5]]}"
+    # specials: infinities stay, every NaN becomes the quiet NaN with its sign
+    sp = np.array([0x7F800000, 0xFF800000, 0x7F800001, 0xFFC00000, 0x7FFFFFFF, 0x7FBF0000],
+                  np.uint32)
+    got = oracle.bf16_round(sp.view(np.float32))
+    assert list(got) == [0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7FC0, 0x7FC0], [hex(g) for g in got]
+
+
+def pin_bf16_rounding_matches_torch():
+    import torch
+    rng = np.random.default_rng(12)
+    u = rng.integers(0, 2 ** 32, 1 << 20, dtype=np.uint64).astype(np.uint32)
+    u = u[((u >> 23) & 0xFF) != 0xFF]
+    got = oracle.bf16_round(u.view(np.float32))
+    want = torch.from_numpy(u.view(np.float32).copy()).to(torch.bfloat16).view(torch.int16)
+    want = want.numpy().view(np.uint16)
+    assert np.array_equal(got, want), "bf16 rounding differs from torch's CPU conversion"
+
+
+# ---------------------------------------------------------------------------
+# the fold (flush, reduce-scatter, deferred reduce)
+# ---------------------------------------------------------------------------
+
+def pin_fold_rank_order():
+    """Hand-derived: rows (2^24, 1, -2^24, 1) summed in rank order give
+    2^24 + 1 -> 2^24 (a tie, to even), then 0, then 1.  Any other order of
+    the first two additions gives a different answer (reversed: 2)."""
+    for dtype in (F32, BF16):
+        if dtype == F32:
+            col = np.array([[2.0 ** 24], [1.0], [-(2.0 ** 24)], [1.0]], np.float32)
+        else:
+            col = np.array([[0x4B80], [0x3F80], [0xCB80], [0x3F80]], np.uint16)
+        out = one_task_flush(4, dtype, col, pre_div=0)
+        want = 0x3F800000 if dtype == F32 else 0x3F80
+        got = out_bits(dtype, out)
+        assert np.all(got[:, 0] == want), f"rank-order fold gave {got[:, 0]} (dtype {dtype})"
+
+
+def pin_fold_exact_sums():
+    """Values k * 2^-20 with |k| < 256: every partial sum is exact in fp32, so
+    the result is the exact rational sum for any W (pre-division by a power of
+    two is exact too)."""
+    rng = random.Random(21)
+    for dtype in (BF16, F32):
+        for W in (1, 2, 3, 4, 5, 8, 16):
+            n = 17
+            ks = [[rng.randint(-255, 255) for _ in range(n)] for _ in range(W)]
+            vals = np.array(ks, np.float64) * 2.0 ** -20
+            rows = vals.astype(np.float32)
+            if dtype == BF16:
+                rows = (rows.view(np.uint32) >> 16).astype(np.uint16)
+            for pre in ((0, 1) if (W & (W - 1)) == 0 else (0,)):
+                out = one_task_flush(W, dtype, rows, pre_div=pre)
+                got = np.array(to_floats(dtype, out[0]))
+                exact = [Fraction(sum(ks[r][j] for r in range(W)), 2 ** 20) / (W if pre else 1)
+                         for j in range(n)]
+                want = [X.round_to(q, X.BFLOAT16 if dtype == BF16 else X.BINARY32) for q in exact]
+                assert np.array_equal(got, np.array(want)), f"exact sums wrong, W={W} dtype={dtype}"
+
+
+def pin_fold_identical_rows():
+    """DeepSpeed issue, Numerics: identical input on every rank reproduces
+    exactly.  With pre-division by W = 2^k each bf16 contribution is x/W and the
+    k-fold sum is exactly x; without it the sum is exactly W*x."""
+    rng = random.Random(22)
+    for W in (2, 4, 8, 16):
+        row = np.array([(rng.getrandbits(1) << 15) | (rng.randint(100, 140) << 7) |
+                        rng.getrandbits(7) for _ in range(40)], np.uint16)
+        rows = np.tile(row, (W, 1))
+        out = one_task_flush(W, BF16, rows, pre_div=1)
+        assert np.array_equal(out, rows), f"identical rows with pre-division not reproduced, W={W}"
+        out = one_task_flush(W, BF16, rows, pre_div=0)
+        want = np.array([X.float_to_bf16_bits(W * X.bf16_bits_to_float(int(b))) for b in row],
+                        np.uint16)
+        assert np.all(out == want[None, :]), f"identical rows without pre-division, W={W}"
+
+
+def pin_fold_brute_force():
+    """Random tiny slabs (subnormals and signed zeros included, W up to 16,
+    sub-communicators, pre-division on and off) against the exact-rational
+    model of the rank-order fp32 fold."""
+    rng = random.Random(23)
+    for trial in range(90):
+        dtype = (BF16, F32)[trial % 2]
+        W = (1, 2, 3, 4, 5, 6, 7, 8, 16)[trial % 9]
+        pre = (trial // 9) % 2
+        divs = [c for c in range(1, W + 1) if W % c == 0 and c < W]
+        comm = (None, None)
+        if divs and trial % 3 == 2:
+            c = rng.choice(divs)
+            comm = (c, rng.choice([1, W // c]) if c > 1 else 1)
+        n = rng.randint(1, 12)
+        rows = random_bits(rng, dtype, (W, n))
+        out = one_task_flush(W, dtype, rows, pre_div=pre, comm=comm)
+        vals = [to_floats(dtype, rows[r]) for r in range(W)]
+        c, s = (W, 1) if comm[0] is None else comm
+        for b in range(W // c):
+            base = b * c if s == 1 else b
+            members = [base + i * s for i in range(c)]
+            for j in range(n):
+                y = X.fold([vals[m][j] for m in members], dtype == BF16, bool(pre), c)
+                for m in members:
+                    got = int(out_bits(dtype, out)[m, j])
+                    want = bits_of(dtype, y)
+                    assert got == want, (f"fold differs: trial {trial} W={W} c={c} s={s} "
+                                         f"pre={pre} col {j} row {m}: {got:#x} vs {want:#x}")
+
+
+def pin_fold_error_bound():
+    """|fold - exact| <= gamma_{W-1} * sum|x| (Higham, Accuracy and Stability of
+    Numerical Algorithms, ch. 4, recursive summation), fp32, no pre-division."""
+    rng = np.random.default_rng(24)
+    for W in (2, 3, 8, 16, 64):
+        rows = (rng.standard_normal((W, 500)) * 10.0 ** rng.integers(-3, 3, (W, 500))).astype(np.float32)
+        out = one_task_flush(W, F32, rows, pre_div=0)
+        exact = rows.astype(np.float64).sum(axis=0)          # exact enough: 64 fp32 terms in fp64
+        u = 2.0 ** -24
+        gamma = (W - 1) * u / (1 - (W - 1) * u)
+        bound = gamma * np.abs(rows.astype(np.float64)).sum(axis=0)
+        err = np.abs(out[0].astype(np.float64) - exact)
+        assert np.all(err <= bound * 1.0000001 + 1e-45), f"error bound violated at W={W}"
+
+
+def pin_prediv_non_power_of_two():
+    """W in {3, 5, 7}: each contribution is x/W correctly rounded to fp32 and
+    then to bf16; checked against the exact model, which decides the reading
+    column by column."""
+    rng = random.Random(25)
+    for W in (3, 5, 7):
+        rows = random_bits(rng, BF16, (W, 64))
+        out = one_task_flush(W, BF16, rows, pre_div=1)
+        vals = [to_floats(BF16, rows[r]) for r in range(W)]
+        for j in range(64):
+            y = X.fold([vals[r][j] for r in range(W)], True, True, W)
+            assert int(out[0, j]) == X.float_to_bf16_bits(y), f"pre-division W={W} col {j}"
+
+
+def pin_reduce_scatter_all_gather():
+    """AllGather page: AllReduce = ReduceScatter + AllGather, bit for bit; the
+    reduce-scatter shard sizes follow the duality table (M in, M/N out)."""
+    rng = random.Random(26)
+    for dtype, W, L, pre in ((BF16, 4, 9, 1), (F32, 8, 5, 0), (BF16, 3, 7, 1), (F32, 1, 4, 0)):
+        M = W * L
+        rows = random_bits(rng, dtype, (W, M), wide=False)
+        ar = one_task_flush(W, dtype, rows, pre_div=pre)
+        shards = np.zeros((W, L), rows.dtype)
+        oracle.reduce_scatter(W, dtype, rows, shards, M, pre)
+        assert shards.shape == (W, M // W)
+        full = np.zeros((W, M), rows.dtype)
+        oracle.all_gather(W, dtype, shards, full, L, 0)
+        assert np.array_equal(out_bits(dtype, full), out_bits(dtype, ar)), \
+            f"AllReduce != ReduceScatter + AllGather (W={W})"
+        vals = [to_floats(dtype, rows[r]) for r in range(W)]
+        for s in range(W):
+            for k in range(L):
+                y = X.fold([vals[r][s * L + k] for r in range(W)], dtype == BF16, bool(pre), W)
+                assert int(out_bits(dtype, shards)[s, k]) == bits_of(dtype, y)
+
+
+# ---------------------------------------------------------------------------
+# partitions and the owner map
+# ---------------------------------------------------------------------------
+
+def _brute_pids(sizes, p):
+    T = sum(sizes)
+    S = -(-T // p) if T else 0
+    out, a = [], 0
+    for n in sizes:
+        out.append(sorted({e // S for e in range(a, a + n)}) if n else [])
+        a += n
+    return out
+
+
+def pin_partition_brute_force():
+    """Element-by-element: partition of element e is floor(e / S) with
+    S = ceil(T / p); a parameter's partition list is the set over its
+    elements.  All size lists of up to 5 params with sizes 0..4, p = 1..4."""
+    for k in range(1, 6):
+        for sizes in itertools.product(range(5), repeat=k):
+            for p in range(1, 5):
+                flat, ps, off, pids = oracle.partition_ids(sizes, [0, k], [p])
+                want = _brute_pids(sizes, p)
+                for i in range(k):
+                    got = list(pids[off[i]:off[i + 1]])
+                    assert got == want[i], f"sizes {sizes} p={p} param {i}: {got} vs {want[i]}"
+                    assert flat[i] == sum(sizes[:i])
+
+
+def pin_owner_rules():
+    """DeepSpeed issue, Design points: exactly one entry means that entry is
+    the owner; straddlers (2+ entries) and empty params keep AllReduce (-1);
+    at most p-1 straddlers per group; an excluded group has no owners."""
+    rng = random.Random(31)
+    for trial in range(300):
+        G = rng.randint(1, 3)
+        sizes, gb, parts, elig = [], [0], [], []
+        for g in range(G):
+            k = rng.randint(1, 8)
+            sizes += [rng.choice([0, 1, 2, 3, 5, 8, 13, 40]) for _ in range(k)]
+            gb.append(len(sizes))
+            parts.append(rng.randint(1, 8))
+            elig.append(rng.getrandbits(1))
+        flat, ps, off, pids = oracle.partition_ids(sizes, gb, parts)
+        owner, counts = oracle.owner_map(off, pids, gb, elig)
+        for g in range(G):
+            gs = sizes[gb[g]:gb[g + 1]]
+            want = _brute_pids(gs, parts[g])
+            n_own = n_str = 0
+            T = sum(gs)
+            S = -(-T // parts[g]) if T else 0
+            inner = 0
+            a = 0
+            for i, n in enumerate(gs):
+                ent = want[i]
+                exp_owner = ent[0] if (elig[g] and len(ent) == 1) else -1
+                assert owner[gb[g] + i] == exp_owner, (sizes, gb, parts, elig, g, i)
+                n_own += exp_owner >= 0
+                n_str += len(ent) >= 2
+                if S and any(a < b * S < a + n for b in range(1, parts[g])):
+                    inner += 1
+                a += n
+            assert counts[2 * g] == n_own and counts[2 * g + 1] == n_str
+            assert n_str <= parts[g] - 1, "more than p-1 straddlers in a group"
+            assert n_str == inner, "straddlers != params holding an interior partition boundary"
+
+
+def pin_group_eligibility():
+    """DeepSpeed issue, Design points: a group is excluded unless its world
+    size matches and group rank i is global rank i."""
+    W = 4
+    cs = [4, 2, 4, 4, 2]
+    r2g = [[0, 1, 2, 3], [0, 1, -1, -1], [0, 1, 3, 2], [1, 2, 3, 0], [0, 1, 2, 3]]
+    assert list(oracle.group_eligible(W, cs, r2g)) == [1, 0, 0, 0, 0]
+
+
+# ---------------------------------------------------------------------------
+# the probe
+# ---------------------------------------------------------------------------
+
+def _golden_lines():
+    with open(os.path.join(GOLDEN, "probe_lines.txt")) as f:
+        return [ln.rstrip("\n") for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def pin_probe_printed_example():
+    """The printed probe report: 118 tasks, 52,428,800 elements, rank 0 keeps
+    6,553,600, 87.5% discarded, owner path off.  Rebuilt from a bucket of 118
+    whole params laid out so that each of the 8 partitions is 6,553,600
+    elements of whole params (so every param has exactly one holder)."""
+    W, part = 8, 6_553_600
+    sizes = []
+    for q in range(W):
+        k = 15 if q < 6 else 14
+        base = part // k
+        sz = [base] * k
+        sz[-1] += part - base * k
+        sizes += sz
+    assert len(sizes) == 118 and sum(sizes) == 52_428_800
+    flat, ps, off, pids = oracle.partition_ids(sizes, [0, len(sizes)], [W])
+    arrival = list(range(len(sizes) - 1, -1, -1))
+    t_numel = [sizes[p] for p in arrival]
+    pr = oracle.probe(W, t_numel, arrival, [0] * len(arrival), None, off, pids, [W], [1])
+    line = oracle.probe_line(0, 3, BF16, pr, 1)
+    assert line == _golden_lines()[0], line
+
+
+def _group_with_cuts(n_params, n_cut, W=8, part=1000):
+    """W partitions of `part` elements made of whole params, except that the
+    first n_cut partition boundaries each fall inside one (merged) param."""
+    total = n_params + n_cut
+    counts = [total // W + (1 if q < total % W else 0) for q in range(W)]
+    sizes = []
+    for q in range(W):
+        c = counts[q]
+        sz = [part // c] * c
+        sz[-1] += part - (part // c) * c
+        if 0 < q <= n_cut:
+            sizes[-1] += sz[0]
+            sz = sz[1:]
+        sizes += sz
+    return sizes
+
+
+def pin_ratio_printed_example():
+    """The printed init report "291/302": two groups of 8 partitions whose
+    boundaries cut 6 and 5 params leave 291 of 302 params with one owner."""
+    W = 8
+    g0, g1 = _group_with_cuts(151, 6), _group_with_cuts(151, 5)
+    sizes, gb = g0 + g1, [0, len(g0), len(g0) + len(g1)]
+    flat, ps, off, pids = oracle.partition_ids(sizes, gb, [W, W])
+    owner, counts = oracle.owner_map(off, pids, gb, [1, 1])
+    assert list(counts[1::2]) == [6, 5]
+    line = oracle.ratio_line(int(counts[0::2].sum()), len(sizes))
+    assert line == _golden_lines()[1], line
+
+
+def pin_probe_closed_forms():
+    """With the owner path off every rank is written the whole bucket, so
+    sum_r discarded_r = (W-1)*reduced - sum_t (|holders_t| - 1) * n_t; with
+    one holder per task that is exactly (W-1)/W of W*reduced (87.5% at W=8).
+    With the owner path on, an owned task is written only to its owner, who
+    keeps it, so it adds nothing to discarded; owner_tasks/elems are 0 when
+    the map is empty."""
+    rng = random.Random(41)
+    for trial in range(60):
+        W = rng.choice([2, 4, 8, 16])
+        sizes = [rng.randint(0, 300) for _ in range(rng.randint(1, 40))]
+        flat, ps, off, pids = oracle.partition_ids(sizes, [0, len(sizes)], [W])
+        owner, counts = oracle.owner_map(off, pids, [0, len(sizes)], [1])
+        arrival = list(range(len(sizes) - 1, -1, -1))
+        t_numel = [sizes[p] for p in arrival]
+        holders = [len(pids[off[p]:off[p + 1]]) for p in arrival]
+        off_pr = oracle.probe(W, t_numel, arrival, [0] * len(arrival), None, off, pids, [W], [1])
+        red = sum(t_numel)
+        assert off_pr["reduced_elems"] == red and off_pr["owner_tasks"] == 0
+        assert off_pr["owner_elems"] == 0
+        extra = sum((h - 1) * n for h, n in zip(holders, t_numel) if h > 0)
+        assert int(off_pr["discarded"].sum()) == (W - 1) * red - extra
+        if all(h == 1 for h, n in zip(holders, t_numel) if n > 0):
+            assert int(off_pr["discarded"].sum()) * W == (W - 1) * W * red
+        on_pr = oracle.probe(W, t_numel, arrival, [0] * len(arrival), owner, off, pids, [W], [1])
+        own_elems = sum(n for p, n in zip(arrival, t_numel) if owner[p] >= 0)
+        assert on_pr["owner_elems"] == own_elems
+        assert on_pr["owner_tasks"] == sum(1 for p in arrival if owner[p] >= 0)
+        stra = sum((W - h) * n for p, h, n in zip(arrival, holders, t_numel) if owner[p] < 0)
+        assert int(on_pr["discarded"].sum()) == stra
+
+
+# ---------------------------------------------------------------------------
+# the owner path and the AllReduce path
+# ---------------------------------------------------------------------------
+
+def pin_owner_path_equivalences():
+    """DeepSpeed issue: the owner path is the same reduction in the same
+    operand order, to one destination; with an empty map the flush is the
+    AllReduce path bit for bit; rows the owner path does not write keep what
+    they held; every holder of a param ends with the sum (copy-out)."""
+    rng = random.Random(51)
+    for trial in range(20):
+        W = rng.choice([2, 4, 8])
+        dtype = rng.choice([BF16, F32])
+        sizes = [rng.randint(0, 30) for _ in range(rng.randint(2, 12))]
+        P = len(sizes)
+        flat, ps, off, pids = oracle.partition_ids(sizes, [0, P], [W])
+        owner, counts = oracle.owner_map(off, pids, [0, P], [1])
+        arrival = list(range(P - 1, -1, -1))
+        t_numel = [sizes[p] for p in arrival]
+        t_off = np.concatenate([[0], np.cumsum(t_numel)[:-1]]).astype(np.int64)
+        T = sum(sizes)
+        ld = max(8, T + 3)
+        rows = random_bits(rng, dtype, (W, ld), wide=False)
+        sentinel = np.full_like(rows, 0x7E7E if dtype == BF16 else 0)
+        if dtype == F32:
+            sentinel = np.full((W, ld), 1234.5, np.float32)
+        ar = sentinel.copy()
+        oracle.flush(W, dtype, rows, ar, 0, t_off, t_numel, arrival, [0] * P, None, [W], [1], 1)
+        ow = sentinel.copy()
+        oracle.flush(W, dtype, rows, ow, 0, t_off, t_numel, arrival, [0] * P, owner, [W], [1], 1)
+        empty = sentinel.copy()
+        oracle.flush(W, dtype, rows, empty, 0, t_off, t_numel, arrival, [0] * P,
+                     np.full(P, -1, np.int32), [W], [1], 1)
+        assert np.array_equal(out_bits(dtype, empty), out_bits(dtype, ar))
+        for t, p in enumerate(arrival):
+            cols = slice(t_off[t], t_off[t] + t_numel[t])
+            for r in range(W):
+                if owner[p] >= 0 and r != owner[p]:
+                    assert np.array_equal(out_bits(dtype, ow[r, cols]), out_bits(dtype, sentinel[r, cols]))
+                else:
+                    assert np.array_equal(out_bits(dtype, ow[r, cols]), out_bits(dtype, ar[r, cols]))
+            for q in pids[off[p]:off[p + 1]]:
+                assert np.array_equal(out_bits(dtype, ow[q, cols]), out_bits(dtype, ar[q, cols]))
+        # columns outside every task are untouched
+        assert np.array_equal(out_bits(dtype, ar[:, T:]), out_bits(dtype, sentinel[:, T:]))
+
+
+# ---------------------------------------------------------------------------
+# ring and recursive-doubling all-gather
+# ---------------------------------------------------------------------------
+
+def _ring_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "ring_allgather_n4.txt")) as f:
+        for ln in f:
+            if ln.strip() and not ln.startswith("#"):
+                parts = ln.split()
+                rows.append([[ord(ch) - ord("A") for ch in cell] for cell in parts[1:]])
+    return rows
+
+
+def pin_ring_table():
+    """The printed N=4 ring table, cell by cell, from the simulated ring; the
+    gathered RING layout; every node receives N-1 chunks of M/N."""
+    table = _ring_table()
+    order, sends = oracle.ring_ag_schedule(4)
+    for step, row in enumerate(table):
+        for i in range(4):
+            assert list(order[i, :step + 1]) == row[i], (step, i, list(order[i]), row[i])
+    recv = np.bincount(sends[:, 2], minlength=4)
+    assert list(recv) == [3, 3, 3, 3]
+    # the gathered layout follows the table's final row
+    W, L = 4, 3
+    shards = np.arange(W * L, dtype=np.float32).reshape(W, L)
+    out = np.zeros((W, W * L), np.float32)
+    oracle.all_gather(W, F32, shards, out, L, 1)
+    for i in range(W):
+        for p in range(W):
+            assert np.array_equal(out[i, p * L:(p + 1) * L], shards[table[-1][i][p]])
+
+
+def pin_ring_closed_form():
+    """Position p of node i holds chunk (i - p) mod N, for N up to 64; per-node
+    receive volume is (N-1) chunks, the bandwidth lower bound's (N-1)M/N."""
+    for N in range(1, 65):
+        order, sends = oracle.ring_ag_schedule(N)
+        for i in range(N):
+            assert list(order[i]) == [(i - p) % N for p in range(N)], N
+        if N > 1:
+            assert np.all(np.bincount(sends[:, 2], minlength=N) == N - 1)
+            # each step forwards the chunk received in the previous step
+            for rec in sends:
+                step, src, dst, chunk = rec
+                assert dst == (src + 1) % N and chunk == (src - (step - 1)) % N
+
+
+def pin_rd_table():
+    """The printed N=8 recursive-doubling table (pairs, per-step volume,
+    holdings); for every N = 2^k the per-step volumes M*2^(j-1)/N sum to
+    (N-1)M/N in log2 N steps (the latency lower bound)."""
+    partner, recv, held = oracle.rd_ag_schedule(8)
+    with open(os.path.join(GOLDEN, "rd_allgather_n8.txt")) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    frac = {"M/8": 1, "M/4": 2, "M/2": 4, "M": 8}
+    assert len(rows) == len(partner) == 3
+    for j, (step, pairs, exch, held_after) in enumerate(rows):
+        want_pairs = [tuple(int(x) for x in pr.split(",")) for pr in pairs.strip("()").split(")(")]
+        got_pairs = sorted({tuple(sorted((i, int(partner[j, i])))) for i in range(8)})
+        assert got_pairs == sorted(want_pairs), (j, got_pairs, want_pairs)
+        assert recv[j] == frac[exch] and held[j] == frac[held_after]
+    for k in range(0, 7):
+        N = 1 << k
+        partner, recv, held = oracle.rd_ag_schedule(N)
+        assert len(recv) == k == math.ceil(math.log2(N)) if N > 1 else len(recv) == 0
+        assert int(recv.sum()) == N - 1
+        assert list(recv) == [1 << j for j in range(k)]
+
+
+def pin_ring_step_replay():
+    """RING layout built one step at a time (step mode) equals the full
+    gather, and after replaying steps 0..s node i holds the table's row s."""
+    W, L = 4, 5
+    rng = np.random.default_rng(61)
+    shards = rng.standard_normal((W, L)).astype(np.float32)
+    full = np.zeros((W, W * L), np.float32)
+    oracle.all_gather(W, F32, shards, full, L, 1)
+    part = np.full((W, W * L), np.nan, np.float32)
+    table = _ring_table()
+    for s in range(W):
+        oracle.all_gather(W, F32, shards, part, L, 1, s)
+        for i in range(W):
+            for p in range(s + 1):
+                assert np.array_equal(part[i, p * L:(p + 1) * L], shards[table[s][i][p]])
+            assert np.all(np.isnan(part[i, (s + 1) * L:]))
+    assert np.array_equal(part, full)
+
+
+# ---------------------------------------------------------------------------
+# deferred reduction under gradient accumulation
+# ---------------------------------------------------------------------------
+
+def _per_microbatch(W, xs, M):
+    """Status quo: reduce each micro-batch across replicas, accumulate the
+    reduced gradients from a zero start."""
+    A = np.zeros((1, M), np.float32)
+    for k, x in enumerate(xs):
+        g = np.zeros((1, M), np.float32)
+        oracle.deferred_reduce(W, x, g, M, 1)
+        oracle.accumulate(1, g, A, M, 1 if k == 0 else 0)
+    return A
+
+
+def _deferred(W, xs, M, out_rows=1):
+    acc = np.zeros((W, M), np.float32)
+    for k, x in enumerate(xs):
+        oracle.accumulate(W, x, acc, M, 1 if k == 0 else 0)
+    D = np.zeros((out_rows, M), np.float32)
+    oracle.deferred_reduce(W, acc, D, M, out_rows)
+    return D, acc
+
+
+def pin_deferred_ga1_identity():
+    """GA = 1: deferring changes nothing, bit for bit (signed zeros included,
+    since both accumulators start from +0); every output row gets the sum."""
+    rng = random.Random(71)
+    for W in (1, 2, 4, 5):
+        x = random_bits(rng, F32, (W, 40))
+        D, _ = _deferred(W, [x], 40, out_rows=W)
+        A = _per_microbatch(W, [x], 40)
+        for i in range(W):
+            assert np.array_equal(D[i].view(np.uint32), A[0].view(np.uint32)), (W, i)
+
+
+def pin_accumulate_zero_start():
+    """The accumulator starts from a zero tree: +0 + x, so a -0 gradient
+    starts the accumulator at +0 (IEEE: +0 + -0 = +0 under round to
+    nearest); later micro-batches add in fp32."""
+    x = np.array([[-0.0, 1.5, -2.0, 3e-45]], np.float32)
+    acc = np.full((1, 4), 7.0, np.float32)
+    oracle.accumulate(1, x, acc, 4, 1)
+    assert list(acc[0].view(np.uint32)) == [0, 0x3FC00000, 0xC0000000, 0x2]
+    y = np.array([[-0.0, 2.0 ** -24, 2.0, -3e-45]], np.float32)
+    oracle.accumulate(1, y, acc, 4, 0)
+    assert list(acc[0].view(np.uint32)) == [0, 0x3FC00000, 0, 0]
+
+
+def pin_deferred_exact_reassociation():
+    """MaxText PR, Results: where the reassociation is exact the two orders
+    agree bit for bit.  Values k*2^-20 (|k| < 2^10) keep every partial sum
+    exact, so both equal the exact rational total for any K."""
+    rng = random.Random(72)
+    for W, K in ((4, 1), (4, 4), (4, 8), (3, 5)):
+        ks = [[[rng.randint(-1023, 1023) for _ in range(30)] for _ in range(W)] for _ in range(K)]
+        xs = [(np.array(k, np.float64) * 2.0 ** -20).astype(np.float32) for k in ks]
+        D, _ = _deferred(W, xs, 30)
+        A = _per_microbatch(W, xs, 30)
+        exact = [float(Fraction(sum(ks[k][r][j] for k in range(K) for r in range(W)), 2 ** 20))
+                 for j in range(30)]
+        assert np.array_equal(D[0], np.array(exact, np.float32))
+        assert np.array_equal(A[0], np.array(exact, np.float32))
+
+
+def pin_deferred_tolerance():
+    """|D - A| <= 5e-5 * sum|x| elementwise, and within the exact bound
+    2 * gamma_{WK} * sum|x| (Higham ch. 4)."""
+    rng = np.random.default_rng(73)
+    for W, K in ((4, 1), (4, 4), (4, 8)):
+        xs = [(rng.standard_normal((W, 2000)) * 1e-3).astype(np.float32) for _ in range(K)]
+        D, _ = _deferred(W, xs, 2000)
+        A = _per_microbatch(W, xs, 2000)
+        S = sum(np.abs(x.astype(np.float64)).sum(axis=0) for x in xs)
+        err = np.abs(D[0].astype(np.float64) - A[0].astype(np.float64))
+        u = 2.0 ** -24
+        n = W * K
+        assert np.all(err <= 5e-5 * S)
+        assert np.all(err <= 2 * (n * u / (1 - n * u)) * S + 1e-45)
+
+
+def pin_deferred_restore():
+    """MaxText PR, Accumulator lifetime: placing a reduced total T onto the
+    unreduced accumulator leaves T on one replica and zeros elsewhere, and the
+    deferred reduce reproduces T exactly (-0 comes back as +0)."""
+    rng = random.Random(74)
+    W = 4
+    T = random_bits(rng, F32, (1, 50))
+    acc = np.zeros((W, 50), np.float32)
+    acc[0] = T[0]
+    D = np.zeros((1, 50), np.float32)
+    oracle.deferred_reduce(W, acc, D, 50, 1)
+    want = np.where(T[0] == 0, np.float32(0.0), T[0])
+    assert np.array_equal(D[0].view(np.uint32), want.view(np.uint32))
+
+
+def pin_deferred_round_trip():
+    """Mid-step checkpoint: accumulate k1 micro-batches, reduce (save),
+    restore onto replica 0, accumulate the rest, reduce: within the
+    tolerance of the uninterrupted step."""
+    rng = np.random.default_rng(75)
+    W, K, M = 4, 8, 500
+    xs = [(rng.standard_normal((W, M)) * 1e-3).astype(np.float32) for _ in range(K)]
+    D, _ = _deferred(W, xs, M)
+    Dsave, acc = _deferred(W, xs[:3], M)
+    acc = np.zeros((W, M), np.float32)
+    acc[0] = Dsave[0]
+    for x in xs[3:]:
+        oracle.accumulate(W, x, acc, M, 0)
+    D2 = np.zeros((1, M), np.float32)
+    oracle.deferred_reduce(W, acc, D2, M, 1)
+    S = sum(np.abs(x.astype(np.float64)).sum(axis=0) for x in xs)
+    assert np.all(np.abs(D2[0].astype(np.float64) - D[0]) <= 5e-5 * S)
+
+
+ALL_PINS = [
+    pin_bf16_rounding, pin_bf16_rounding_matches_torch, pin_fold_rank_order, pin_fold_exact_sums,
+    pin_fold_identical_rows, pin_fold_brute_force, pin_fold_error_bound,
+    pin_prediv_non_power_of_two, pin_reduce_scatter_all_gather, pin_partition_brute_force,
+    pin_owner_rules, pin_group_eligibility, pin_probe_printed_example, pin_ratio_printed_example,
+    pin_probe_closed_forms, pin_owner_path_equivalences, pin_ring_table, pin_ring_closed_form,
+    pin_rd_table, pin_ring_step_replay, pin_deferred_ga1_identity,
+    pin_accumulate_zero_start, pin_deferred_exact_reassociation, pin_deferred_tolerance, pin_deferred_restore,
+    pin_deferred_round_trip,
+]

@@ -1,0 +1,92 @@
+"""Every plausible mistake planted in the oracle must fail at least one pin.
+
+Each mutant is oracle.c with one snippet replaced, compiled on the CPU into a
+temporary directory; the pins of tests/oracle_pins.py then run against it.
+A mutant that passes every pin would mean the pins cannot see that mistake.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "fold_reverse_rank_order": (
+        "load_val(dtype, in, ld_in, member(b, i, c, s), j)",
+        "load_val(dtype, in, ld_in, member(b, c - 1 - i, c, s), j)"),
+    "fold_drops_last_rank": (
+        "        for (int i = 0; i < c; ++i) {\n          float v",
+        "        for (int i = 0; i < (c > 1 ? c - 1 : 1); ++i) {\n          float v"),
+    "prediv_not_rounded_to_dtype": (
+        "return round_dtype(dtype, x / (float)c);",
+        "return x / (float)c;"),
+    "prediv_by_world_not_comm": (
+        "float v = contribution(dtype, load_val(dtype, in, ld_in, member(b, i, c, s), j), pre_div, c);",
+        "float v = contribution(dtype, load_val(dtype, in, ld_in, member(b, i, c, s), j), pre_div, W);"),
+    "owner_row_off_by_one": (
+        "store_val(dtype, out, ld_out, root, j, acc);",
+        "store_val(dtype, out, ld_out, (root + 1) % W, j, acc);"),
+    "rne_ties_away_from_zero": (
+        "(lo == 0x8000u && (hi & 1u))",
+        "(lo == 0x8000u)"),
+    "rne_truncates": (
+        "if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u))) hi += 1u;",
+        ";"),
+    "partition_size_floor": (
+        "int64_t S = (T + p - 1) / p;",
+        "int64_t S = T / p > 0 ? T / p : 1;"),
+    "straddler_gets_owner": (
+        "owner[i] = (eligible[g] && n == 1) ? pids[pid_offsets[i]] : -1;",
+        "owner[i] = (eligible[g] && n >= 1) ? pids[pid_offsets[i]] : -1;"),
+    "eligibility_ignored": (
+        "int ok = comm_size[g] == W;",
+        "int ok = 1;"),
+    "ring_sends_left": (
+        "int dst = (src + 1) % N;",
+        "int dst = (src + N - 1) % N;"),
+    "rs_interleaved_shards": (
+        "load_val(dtype, in, ld_in, r, s * L + k)",
+        "load_val(dtype, in, ld_in, r, k * W + s)"),
+    "accumulate_init_copies": (
+        "acc[r * ld_acc + j] = a + x[r * ld_x + j];",
+        "acc[r * ld_acc + j] = init ? x[r * ld_x + j] : a + x[r * ld_x + j];"),
+    "deferred_writes_row0_only": (
+        "for (int i = 0; i < out_rows; ++i) out[i * ld_out + j] = s;",
+        "out[j] = s;"),
+    "probe_kept_counts_written": (
+        "if (hd[r]) kept[r] += n;",
+        "if (wr[r]) kept[r] += n;"),
+    "rd_partner_plus": (
+        "int q = i ^ d;",
+        "int q = (i + d) % N;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = tmp_path / "oracle_mut.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+                    "-shared", "-w", "-o", str(so), str(path)], check=True)
+    saved = oracle._lib
+    oracle._lib = oracle.load_library(str(so))
+    failed = []
+    try:
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin()
+            except (AssertionError, ValueError, RuntimeError, IndexError):
+                failed.append(pin.__name__)
+                break
+    finally:
+        oracle._lib = saved
+    assert failed, f"mutant {name} passes every pin"
