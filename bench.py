@@ -1,0 +1,363 @@
+"""Benchmark of the data-parallel gradient-reduction hot path on one MI355X.
+
+Default workload: the W=8 reduce-to-owner bucket flush of a 402.8M-element
+bf16 gradient (DeepSpeed issue "DeepCompile ZeRO-1: reduce-to-owner instead
+of AllReduce", "Additional context": 8 ranks, 402.8M parameters, buckets of
+52,428,800 elements, about 118 tasks per bucket), held as a [8, M] slab in HBM.
+
+One step = the owner map (partition lists + owner map kernels) and the flush
+of every bucket, in arrival order.  Metric: algorithmic bytes read + written
+per step / step time (GB/s), and the flush kernel against MI355X's 8 TB/s HBM
+peak.  Algorithmic bytes of a task of n elements over W ranks, b bytes each:
+W*n*b read + (owner ? 1 : W)*n*b written + its 32-byte task record.
+
+Other workloads (--workload): mixed (W=16 fp32 1.2B-element flush), deferred
+(qwen3-0.6b W=4 fp32 gradient accumulation), rs_ag (7B layer reduce-scatter +
+all-gather), tiny (W=4 flush).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flush_bytes(w, owner):
+    """Algorithmic bytes of every flush launch of workload w."""
+    b = w.elem_bytes()
+    per = []
+    for bk in w.buckets:
+        tot = 0
+        for t in bk.tasks:
+            own = owner is not None and t.comm == 0 and owner[t.param] >= 0
+            tot += w.W * t.numel * b + (1 if own else w.W) * t.numel * b + 32
+        per.append(tot)
+    return per
+
+
+def owner_map_bytes(w):
+    P, G = w.P, w.G
+    pids = P + sum(p - 1 for p in w.group_parts())
+    # numel read twice, offsets and CSR written, CSR read, owner and counts written
+    return 16 * P + 8 * P + 8 * G + 4 * (P + 1) + 4 * pids + 4 * (P + 1) + 4 * pids + 4 * P + 8 * G
+
+
+class Timer:
+    """HIP events on the stream the kernels are launched on (torch's current
+    stream: the library enqueues on the stream it is given)."""
+
+    def __init__(self, torch, n):
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.ev]
+
+
+def bench_flush(args, w, reduce_to_owner=True):
+    import torch
+    import synth
+    from gradient_reduction_amd import executor
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    ld = w.ld
+    dt = torch.int16 if w.dtype == 0 else torch.int32
+    log(f"[bench] {w.name}: W={w.W} elements={w.total} buckets={len(w.buckets)} "
+        f"tasks={[len(b.tasks) for b in w.buckets]} slab={w.W * ld * w.elem_bytes() / 1e9:.2f} GB")
+    x = torch.empty((w.W, ld), dtype=dt, device=dev)
+    synth.fill_slab_device(w.dtype, w.value_seed, 0, w.scale, w.W, ld, w.total, x.data_ptr(),
+                           stream.cuda_stream)
+    y = torch.zeros((w.W, ld), dtype=dt, device=dev)
+    ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner, log=log)
+    ex.build_owner_map()
+    ex.fetch_metadata()
+    log("[bench] " + ex.ratio_line())
+    for b in range(min(len(w.buckets), 3)):
+        log("[bench] " + ex.probe_line(b, b))
+    owner = ex.h_owner if reduce_to_owner else None
+    per_launch = flush_bytes(w, owner)
+    step_bytes = sum(per_launch) + owner_map_bytes(w)
+    nb = len(w.buckets)
+
+    def step(timer=None):
+        ex.build_owner_map()
+        for b in range(nb):
+            if timer is not None:
+                timer.ev[b][0].record()
+            ex.flush(b, x, ld, y, ld)
+            if timer is not None:
+                timer.ev[b][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [Timer(torch, nb) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for k in range(args.steps):
+        step(timers[k])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    kern = np.array([tm.ms() for tm in timers])          # [steps, buckets]
+    avg_launch_ms = float(kern.mean())
+    flush_gbs = sum(per_launch) / (kern.sum(axis=1).mean() / 1e3) / 1e9
+    value = step_bytes / (ms_step / 1e3) / 1e9
+    log(f"[bench] step {ms_step:.3f} ms, {value:.1f} GB/s; flush kernels {kern.sum(axis=1).mean():.3f} ms "
+        f"({flush_gbs:.1f} GB/s); per bucket ms {np.round(kern.mean(axis=0), 4).tolist()}")
+    roofline = {"bound": "hbm", "achieved": round(flush_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(flush_gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile(w, per_launch),
+                "kernel": "k_flush", "launch_ms_avg": round(avg_launch_ms, 4),
+                "bytes_per_launch_avg": int(np.mean(per_launch))}
+    extra = {"per_bucket_gbs": [round(b / (m / 1e3) / 1e9, 1) for b, m in zip(per_launch, kern.mean(axis=0))]}
+    del x, y
+    torch.cuda.empty_cache()
+    return ms_step, value, step_bytes, roofline, extra
+
+
+def traffic_from_profile(w, per_launch):
+    """Measured HBM bytes per flush launch from the committed counter summary,
+    if it was taken on the current flush source; else None."""
+    path = os.path.join(ROOT, "profiles", "flush_w8_402m_traffic.json")
+    if not os.path.exists(path):
+        return None
+    import hashlib
+    src = open(os.path.join(ROOT, "gradient_reduction_amd", "csrc", "flush.hip"), "rb").read()
+    rec = json.load(open(path))
+    if rec.get("flush_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    if rec.get("workload") != w.name:
+        return None
+    return rec.get("hbm_bytes_per_launch_avg")
+
+
+def cpu_baseline_flush(w, reduce_to_owner=True, max_buckets=2):
+    """The oracle, single-threaded, on the first buckets of the same workload
+    (host inputs from the same generator; generation untimed)."""
+    import oracle
+    import synth
+    flat, ps, off, pids = oracle.partition_ids(w.numel, w.group_begin, w.group_parts())
+    comm_sizes = [w.comms[c].size for c in w.group_comm]
+    elig = oracle.group_eligible(w.W, comm_sizes, w.group_rank_to_global())
+    owner, _ = oracle.owner_map(off, pids, w.group_begin, elig)
+    own = owner if reduce_to_owner else None
+    per = flush_bytes(w, own)
+    secs = 0.0
+    nbytes = 0
+    used = []
+    for b, bk in enumerate(w.buckets[:max_buckets]):
+        n = bk.numel
+        ld = -(-n // 8) * 8
+        rows = np.zeros((w.W, ld), synth.np_dtype(w.dtype))
+        for r in range(w.W):
+            rows[r, :n] = synth.fill_row(w.dtype, w.value_seed, r, w.scale, bk.col, n)
+        if w.dtype == 1:
+            rows = rows.view(np.float32)
+        out = np.zeros_like(rows)
+        t = time.perf_counter()
+        oracle.flush(w.W, w.dtype, rows, out, 0, [t_.offset for t_ in bk.tasks],
+                     [t_.numel for t_ in bk.tasks], [t_.param for t_ in bk.tasks],
+                     [t_.comm for t_ in bk.tasks], own, [c.size for c in w.comms],
+                     [c.stride for c in w.comms], w.pre_div)
+        secs += time.perf_counter() - t
+        nbytes += per[b]
+        used.append(b)
+        del rows, out
+    log(f"[bench] cpu oracle: {nbytes / 1e9:.2f} GB in {secs:.2f} s")
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"buckets {used} of {len(w.buckets)} ({sum(w.buckets[b].numel for b in used)} "
+                      f"columns, {sum(len(w.buckets[b].tasks) for b in used)} tasks), oracle.c "
+                      f"single thread, {nbytes} algorithmic bytes, {secs:.2f} s"}
+
+
+def bench_deferred(args):
+    import torch
+    import synth
+    from gradient_reduction_amd import dc
+    from synth import workloads as wl
+    w = wl.deferred_ga_w4(args.ga)
+    W, M, ld = w.W, w.M, w.ld
+    dev = torch.device("cuda:0")
+    xs = torch.empty((args.ga, W, ld), dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream().cuda_stream
+    for k in range(args.ga):
+        synth.fill_slab_device(1, w.value_seed, wl.microbatch_stream(k, W, 0), w.scale, W, ld, M,
+                               xs[k].data_ptr(), s)
+    acc = torch.empty((W, ld), dtype=torch.float32, device=dev)
+    out = torch.empty((W, ld), dtype=torch.float32, device=dev)
+    acc_b = [(2 if k else 1) * W * M * 4 + W * M * 4 for k in range(args.ga)]
+    red_b = W * M * 4 + W * M * 4
+    step_bytes = sum(acc_b) + red_b
+    n = args.ga + 1
+
+    def step(tm=None):
+        for k in range(args.ga):
+            if tm: tm.ev[k][0].record()
+            dc.dc_accumulate(W, xs[k], ld, acc, ld, M, 1 if k == 0 else 0)
+            if tm: tm.ev[k][1].record()
+        if tm: tm.ev[args.ga][0].record()
+        dc.dc_deferred_reduce(W, acc, ld, out, ld, M, W)
+        if tm: tm.ev[args.ga][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [Timer(torch, n) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for k in range(args.steps):
+        step(timers[k])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    kern = np.array([tm.ms() for tm in timers]).mean(axis=0)
+    red_gbs = red_b / (kern[-1] / 1e3) / 1e9
+    acc_gbs = sum(acc_b) / (kern[:-1].sum() / 1e3) / 1e9
+    log(f"[bench] deferred K={args.ga}: step {ms_step:.3f} ms; accumulate {acc_gbs:.1f} GB/s; "
+        f"reduce {red_gbs:.1f} GB/s ({kern[-1]:.3f} ms)")
+    roofline = {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(red_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_deferred", "launch_ms_avg": round(float(kern[-1]), 4),
+                "bytes_per_launch_avg": red_b}
+    extra = {"accumulate_gbs": round(acc_gbs, 1)}
+    return w.name, ms_step, step_bytes / (ms_step / 1e3) / 1e9, roofline, extra, "f32"
+
+
+def bench_rs_ag(args):
+    import torch
+    import synth
+    from gradient_reduction_amd import dc
+    from synth import workloads as wl
+    w = wl.rs_ag_w8()
+    W, M, L = w.W, w.M, w.M // w.W
+    dev = torch.device("cuda:0")
+    x = torch.empty((W, w.ld), dtype=torch.int16, device=dev)
+    synth.fill_slab_device(0, w.value_seed, 0, w.scale, W, w.ld, M, x.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream)
+    ld_sh = wl.round_up(L, 64)
+    sh = torch.empty((W, ld_sh), dtype=torch.int16, device=dev)
+    out = torch.empty((W, w.ld), dtype=torch.int16, device=dev)
+    rs_b = W * M * 2 + M * 2
+    ag_b = M * 2 + W * M * 2
+
+    def step(tm=None):
+        if tm: tm.ev[0][0].record()
+        dc.dc_reduce_scatter(W, 0, x, w.ld, sh, ld_sh, M, 0)
+        if tm: tm.ev[0][1].record(); tm.ev[1][0].record()
+        dc.dc_all_gather(W, 0, sh, ld_sh, out, w.ld, L, dc.DC_ORDER_RANK, -1)
+        if tm: tm.ev[1][1].record(); tm.ev[2][0].record()
+        dc.dc_all_gather(W, 0, sh, ld_sh, out, w.ld, L, dc.DC_ORDER_RING, -1)
+        if tm: tm.ev[2][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [Timer(torch, 3) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for k in range(args.steps):
+        step(timers[k])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    kern = np.array([tm.ms() for tm in timers]).mean(axis=0)
+    gbs = [rs_b / (kern[0] / 1e3) / 1e9, ag_b / (kern[1] / 1e3) / 1e9, ag_b / (kern[2] / 1e3) / 1e9]
+    log(f"[bench] rs {gbs[0]:.1f} GB/s, ag rank {gbs[1]:.1f} GB/s, ag ring {gbs[2]:.1f} GB/s")
+    roofline = {"bound": "hbm", "achieved": round(gbs[0], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs[0] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_rs_vec",
+                "launch_ms_avg": round(float(kern[0]), 4), "bytes_per_launch_avg": rs_b}
+    extra = {"all_gather_rank_gbs": round(gbs[1], 1), "all_gather_ring_gbs": round(gbs[2], 1)}
+    return w.name, ms_step, (rs_b + 2 * ag_b) / (ms_step / 1e3) / 1e9, roofline, extra, "bf16"
+
+
+def copy_calibration():
+    """Achievable bandwidth of a plain 16-byte streaming copy (1 GiB)."""
+    import torch
+    from gradient_reduction_amd import dc
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        dc.dc_stream_copy(a, b, n)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dc.dc_stream_copy(a, b, n)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    return round(2 * n / (ms / 1e3) / 1e9, 1)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="owner_w8",
+                    choices=["owner_w8", "allreduce_w8", "mixed", "deferred", "rs_ag", "tiny"])
+    ap.add_argument("--ga", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path simulates W data-parallel ranks as rows "
+              f"of one GPU's gradient slab, so --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from gradient_reduction_amd import dc
+    dc.lib()
+    from synth import workloads as wl
+
+    calib = copy_calibration()
+    log(f"[bench] streaming copy reference: {calib} GB/s")
+    cpu = None
+    if args.workload in ("owner_w8", "allreduce_w8", "mixed", "tiny"):
+        w = {"owner_w8": wl.owner_flush_w8, "allreduce_w8": wl.owner_flush_w8,
+             "mixed": wl.mixed_flush_w16, "tiny": wl.tiny_flush}[args.workload]()
+        owner_mode = args.workload != "allreduce_w8"
+        ms, value, step_bytes, roof, extra = bench_flush(args, w, owner_mode)
+        name, dtype = w.name, wl.DTYPE_NAME[w.dtype]
+        config = {"workload": name, "W": w.W, "elements": w.total, "buckets": len(w.buckets),
+                  "tasks_per_bucket": [len(b.tasks) for b in w.buckets],
+                  "bucket_capacity": w.capacity, "mode": "reduce_to_owner" if owner_mode else "allreduce",
+                  "pre_div": w.pre_div, "step": "owner map + every bucket flush",
+                  "step_bytes": step_bytes}
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline_flush(w, owner_mode, max_buckets=2 if w.total > 1e8 else 1)
+    elif args.workload == "deferred":
+        name, ms, value, roof, extra, dtype = bench_deferred(args)
+        config = {"workload": name, "W": 4, "K": args.ga, "step": "K accumulates + deferred reduce"}
+    else:
+        name, ms, value, roof, extra, dtype = bench_rs_ag(args)
+        config = {"workload": name, "W": 8, "step": "reduce-scatter + all-gather rank + all-gather ring"}
+    roof["copy_reference_gbs"] = calib
+    line = {"metric": "bucket-flush GB/s (bytes read+written/time) and % of MI355X HBM peak, W=8",
+            "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic (seeded SplitMix64 Irwin-Hall gradients, random-init shapes)",
+            "config": config, "roofline": roof, "cpu_baseline": cpu, "detail": extra}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,365 @@
+// C ABI of libdc (declared in include/dc.h): host-side argument checks,
+// error reporting, the host-only probe and task-table check, and the kernel
+// launches.  Every check runs before the first HIP call, so a rejected call
+// touches no device state.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dc.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dc_status fail(dc_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+dc_status ok() {
+  g_last_error.clear();
+  return DC_OK;
+}
+
+dc_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(int32_t dtype) { return dtype == DC_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) share a byte.
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+dc_status check_w(int32_t W) {
+  if (W < 1 || W > DC_MAX_W) return fail(DC_ERR_ARG, "W=%d outside [1, %d]", W, DC_MAX_W);
+  return DC_OK;
+}
+
+dc_status check_dtype(int32_t dtype) {
+  if (dtype != DC_BF16 && dtype != DC_F32) return fail(DC_ERR_DTYPE, "unknown dtype %d", dtype);
+  return DC_OK;
+}
+
+// A [rows, ld] slab: non-NULL, 16-byte aligned base and stride, ld >= cols.
+dc_status check_slab(const char* name, const void* p, int64_t ld, int64_t cols, int32_t dtype) {
+  if (p == nullptr) return fail(DC_ERR_NULL, "%s is NULL", name);
+  if (ld < 1 || ld < cols) return fail(DC_ERR_SHAPE, "%s: ld=%lld < %lld columns", name, (long long)ld, (long long)cols);
+  if (!aligned16(p) || (ld * elem_bytes(dtype)) % 16 != 0)
+    return fail(DC_ERR_ALIGN, "%s: base or row stride (ld=%lld) not 16-byte aligned", name, (long long)ld);
+  return DC_OK;
+}
+
+dc_status check_groups(int32_t num_params, int32_t num_groups, const int32_t* group_begin) {
+  if (num_params < 0) return fail(DC_ERR_ARG, "num_params=%d < 0", num_params);
+  if (num_groups < 1 || num_groups > DC_MAX_GROUPS)
+    return fail(DC_ERR_ARG, "num_groups=%d outside [1, %d]", num_groups, DC_MAX_GROUPS);
+  if (group_begin == nullptr) return fail(DC_ERR_NULL, "group_begin is NULL");
+  if (group_begin[0] != 0 || group_begin[num_groups] != num_params)
+    return fail(DC_ERR_SHAPE, "group_begin must run from 0 to num_params=%d", num_params);
+  for (int g = 0; g < num_groups; ++g)
+    if (group_begin[g + 1] < group_begin[g]) return fail(DC_ERR_SHAPE, "group_begin decreases at group %d", g);
+  return DC_OK;
+}
+
+dc_status check_comms(int32_t W, const dc_comm* comms, int32_t num_comms) {
+  if (comms == nullptr) return fail(DC_ERR_NULL, "comms is NULL");
+  if (num_comms < 1 || num_comms > DC_MAX_COMMS)
+    return fail(DC_ERR_ARG, "num_comms=%d outside [1, %d]", num_comms, DC_MAX_COMMS);
+  if (comms[0].size != W || comms[0].stride != 1)
+    return fail(DC_ERR_ARG, "comms[0] must be the data-parallel comm {W=%d, 1}", W);
+  for (int k = 0; k < num_comms; ++k) {
+    const int32_t c = comms[k].size, s = comms[k].stride;
+    if (c < 1 || W % c != 0) return fail(DC_ERR_ARG, "comms[%d].size=%d does not divide W=%d", k, c, W);
+    if (s != 1 && s != W / c) return fail(DC_ERR_ARG, "comms[%d].stride=%d is neither 1 nor W/size", k, s);
+  }
+  return DC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dc_version(void) { return "dc 0.1.0 (gfx950)"; }
+
+const char* dc_strerror(dc_status status) {
+  switch (status) {
+    case DC_OK: return "ok";
+    case DC_ERR_NULL: return "a required pointer is NULL";
+    case DC_ERR_ARG: return "an argument is out of range or buffers overlap";
+    case DC_ERR_SHAPE: return "sizes or strides do not fit together";
+    case DC_ERR_ALIGN: return "a slab base or stride is not 16-byte aligned";
+    case DC_ERR_DTYPE: return "unknown dtype";
+    case DC_ERR_TASKS: return "the task table breaks its contract";
+    case DC_ERR_HIP: return "a HIP call failed";
+    case DC_ERR_UNSUPPORTED: return "not supported by this build";
+    default: return "unknown status";
+  }
+}
+
+const char* dc_last_error(void) { return g_last_error.c_str(); }
+
+dc_status dc_partition_ids(int32_t W, int32_t num_params, const int64_t* numel,
+                           int32_t num_groups, const int32_t* group_begin,
+                           const int32_t* group_parts, int64_t* flat_offset, int64_t* part_size,
+                           int32_t* pid_offsets, int32_t* pids, int64_t pids_capacity,
+                           void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_groups(num_params, num_groups, group_begin))) return st;
+  if (group_parts == nullptr) return fail(DC_ERR_NULL, "group_parts is NULL");
+  if (part_size == nullptr || pid_offsets == nullptr) return fail(DC_ERR_NULL, "part_size or pid_offsets is NULL");
+  if (num_params > 0 && (numel == nullptr || flat_offset == nullptr || pids == nullptr))
+    return fail(DC_ERR_NULL, "numel, flat_offset or pids is NULL");
+  int64_t need = num_params;
+  for (int g = 0; g < num_groups; ++g) {
+    if (group_parts[g] < 1 || group_parts[g] > DC_MAX_W)
+      return fail(DC_ERR_ARG, "group_parts[%d]=%d outside [1, %d]", g, group_parts[g], DC_MAX_W);
+    need += group_parts[g] - 1;
+  }
+  if (pids_capacity < need || pids_capacity > INT32_MAX)
+    return fail(DC_ERR_SHAPE, "pids_capacity=%lld, need %lld (at most 2^31-1)", (long long)pids_capacity, (long long)need);
+  dc::GroupTable g{};
+  g.num_groups = num_groups;
+  for (int k = 0; k <= num_groups; ++k) g.begin[k] = group_begin[k];
+  for (int k = 0; k < num_groups; ++k) g.parts[k] = group_parts[k];
+  return hip_status(dc::launch_partition_ids(num_params, numel, g, flat_offset, part_size,
+                                             pid_offsets, pids, pids_capacity,
+                                             static_cast<hipStream_t>(stream)),
+                    "partition ids launch");
+}
+
+dc_status dc_build_owner_map(int32_t W, int32_t num_params, const int32_t* pid_offsets,
+                             const int32_t* pids, int64_t pids_capacity, int32_t num_groups,
+                             const int32_t* group_begin, const int32_t* group_comm_size,
+                             const int32_t* group_rank_to_global, int32_t* owner, int32_t* counts,
+                             void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_groups(num_params, num_groups, group_begin))) return st;
+  if (group_comm_size == nullptr || group_rank_to_global == nullptr)
+    return fail(DC_ERR_NULL, "group_comm_size or group_rank_to_global is NULL");
+  if (pid_offsets == nullptr || counts == nullptr) return fail(DC_ERR_NULL, "pid_offsets or counts is NULL");
+  if (num_params > 0 && owner == nullptr) return fail(DC_ERR_NULL, "owner is NULL");
+  if (pids_capacity < 0) return fail(DC_ERR_ARG, "pids_capacity < 0");
+  if (pids_capacity > 0 && pids == nullptr) return fail(DC_ERR_NULL, "pids is NULL");
+  dc::GroupTable g{};
+  g.num_groups = num_groups;
+  for (int k = 0; k <= num_groups; ++k) g.begin[k] = group_begin[k];
+  for (int k = 0; k < num_groups; ++k) {
+    // the data-parallel group: same world size, group rank i is global rank i
+    int elig = group_comm_size[k] == W;
+    for (int i = 0; elig && i < W; ++i) elig = group_rank_to_global[(int64_t)k * W + i] == i;
+    g.eligible[k] = elig;
+    g.parts[k] = group_comm_size[k];
+  }
+  return hip_status(dc::launch_owner_map(W, num_params, pid_offsets, pids, pids_capacity, g, owner,
+                                         counts, static_cast<hipStream_t>(stream)),
+                    "owner map launch");
+}
+
+dc_status dc_validate_tasks(int32_t W, const dc_task* tasks, int32_t num_tasks,
+                            int64_t bucket_numel, int32_t num_params, const dc_comm* comms,
+                            int32_t num_comms) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_comms(W, comms, num_comms))) return st;
+  if (num_tasks < 0) return fail(DC_ERR_ARG, "num_tasks=%d < 0", num_tasks);
+  if (num_tasks > 0 && tasks == nullptr) return fail(DC_ERR_NULL, "tasks is NULL");
+  int64_t pos = 0;
+  for (int32_t t = 0; t < num_tasks; ++t) {
+    const dc_task& k = tasks[t];
+    if (k.offset != pos) return fail(DC_ERR_TASKS, "task %d: offset %lld, expected %lld (sorted and packed)", t, (long long)k.offset, (long long)pos);
+    if (k.numel < 0) return fail(DC_ERR_TASKS, "task %d: numel %lld < 0", t, (long long)k.numel);
+    if (k.param < 0 || k.param >= num_params) return fail(DC_ERR_TASKS, "task %d: param %d outside [0, %d)", t, k.param, num_params);
+    if (k.comm < 0 || k.comm >= num_comms) return fail(DC_ERR_TASKS, "task %d: comm %d outside [0, %d)", t, k.comm, num_comms);
+    pos += k.numel;
+  }
+  if (pos != bucket_numel) return fail(DC_ERR_TASKS, "tasks cover %lld columns, bucket has %lld", (long long)pos, (long long)bucket_numel);
+  return ok();
+}
+
+dc_status dc_flush_bucket(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                          void* slab_out, int64_t ld_out, int64_t bucket_col,
+                          int64_t bucket_numel, const dc_task* tasks, int32_t num_tasks,
+                          const int32_t* owner, int32_t num_params, const dc_comm* comms,
+                          int32_t num_comms, int32_t pre_div, void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype)) || (st = check_comms(W, comms, num_comms))) return st;
+  if (bucket_col < 0 || bucket_numel < 0)
+    return fail(DC_ERR_ARG, "bucket_col=%lld, bucket_numel=%lld", (long long)bucket_col, (long long)bucket_numel);
+  const int64_t end = bucket_col + bucket_numel;
+  if ((st = check_slab("slab_in", slab_in, ld_in, end, dtype)) ||
+      (st = check_slab("slab_out", slab_out, ld_out, end, dtype)))
+    return st;
+  if (num_tasks < 0 || num_params < 0) return fail(DC_ERR_ARG, "num_tasks or num_params < 0");
+  if (num_tasks > 0 && tasks == nullptr) return fail(DC_ERR_NULL, "tasks is NULL");
+  if (pre_div != 0 && pre_div != 1) return fail(DC_ERR_ARG, "pre_div=%d", pre_div);
+  const int64_t b = elem_bytes(dtype);
+  if (slab_in == slab_out) {
+    if (ld_in != ld_out) return fail(DC_ERR_ARG, "in-place flush needs ld_in == ld_out");
+  } else if (overlaps(slab_in, W * ld_in * b, slab_out, W * ld_out * b)) {
+    return fail(DC_ERR_ARG, "slab_in and slab_out overlap without being the same slab");
+  }
+  dc::FlushLaunch a{};
+  a.W = W;
+  a.dtype = dtype;
+  a.pre_div = pre_div;
+  a.in = slab_in;
+  a.out = slab_out;
+  a.ld_in = ld_in;
+  a.ld_out = ld_out;
+  a.c0 = bucket_col;
+  a.c1 = end;
+  a.tasks = tasks;
+  a.ntasks = num_tasks;
+  a.owner = owner;
+  a.nparams = num_params;
+  a.ncomms = num_comms;
+  for (int k = 0; k < num_comms; ++k) a.comms[k] = {comms[k].size, comms[k].stride};
+  return hip_status(dc::launch_flush(a, static_cast<hipStream_t>(stream)), "flush launch");
+}
+
+dc_status dc_probe_flush(int32_t W, int32_t dtype, const dc_task* tasks, int32_t num_tasks,
+                         const int32_t* owner, int32_t num_params, const int32_t* pid_offsets,
+                         const int32_t* pids, const dc_comm* comms, int32_t num_comms,
+                         int32_t pre_div, dc_probe* out) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype)) || (st = check_comms(W, comms, num_comms))) return st;
+  if (out == nullptr) return fail(DC_ERR_NULL, "out is NULL");
+  if (num_tasks < 0 || num_params < 0) return fail(DC_ERR_ARG, "num_tasks or num_params < 0");
+  if (num_tasks > 0 && (tasks == nullptr || pid_offsets == nullptr))
+    return fail(DC_ERR_NULL, "tasks or pid_offsets is NULL");
+  std::memset(out, 0, sizeof *out);
+  out->tasks = num_tasks;
+  out->pre_div = pre_div;
+  out->dtype = dtype;
+  std::vector<char> wr(W), hd(W);
+  for (int32_t t = 0; t < num_tasks; ++t) {
+    const dc_task& k = tasks[t];
+    if (k.param < 0 || k.param >= num_params || k.comm < 0 || k.comm >= num_comms || k.numel < 0)
+      return fail(DC_ERR_TASKS, "task %d has an out-of-range param, comm or numel", t);
+    const int32_t c = comms[k.comm].size, s = comms[k.comm].stride;
+    int32_t root = (k.comm == 0 && owner != nullptr) ? owner[k.param] : -1;
+    if (root >= W) root = -1;
+    out->reduced_elems += k.numel;
+    if (root >= 0) {
+      out->owner_tasks += 1;
+      out->owner_elems += k.numel;
+    }
+    std::fill(wr.begin(), wr.end(), 0);
+    std::fill(hd.begin(), hd.end(), 0);
+    if (root >= 0) wr[root] = 1;
+    else std::fill(wr.begin(), wr.end(), 1);
+    const int32_t o0 = pid_offsets[k.param], o1 = pid_offsets[k.param + 1];
+    if (o1 > o0 && pids == nullptr) return fail(DC_ERR_NULL, "pids is NULL");
+    for (int32_t e = o0; e < o1; ++e) {
+      const int32_t q = pids[e];
+      if (q < 0 || q >= c) return fail(DC_ERR_TASKS, "param %d: partition %d outside its comm of %d", k.param, q, c);
+      for (int32_t blk = 0; blk < W / c; ++blk) hd[(s == 1 ? blk * c : blk) + q * s] = 1;
+    }
+    for (int r = 0; r < W; ++r) {
+      if (wr[r]) out->written[r] += k.numel;
+      if (hd[r]) out->kept[r] += k.numel;
+    }
+  }
+  for (int r = 0; r < W; ++r) out->discarded[r] = out->written[r] - out->kept[r];
+  return ok();
+}
+
+dc_status dc_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                            int64_t ld_out, int64_t M, int32_t pre_div, void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype))) return st;
+  if (M < 0) return fail(DC_ERR_ARG, "M=%lld < 0", (long long)M);
+  if (M % W != 0) return fail(DC_ERR_SHAPE, "M=%lld is not a multiple of W=%d (pad with zeros)", (long long)M, W);
+  if (pre_div != 0 && pre_div != 1) return fail(DC_ERR_ARG, "pre_div=%d", pre_div);
+  if ((st = check_slab("in", in, ld_in, M, dtype)) || (st = check_slab("out", out, ld_out, M / W, dtype))) return st;
+  const int64_t b = elem_bytes(dtype);
+  if (overlaps(in, W * ld_in * b, out, W * ld_out * b)) return fail(DC_ERR_ARG, "in and out overlap");
+  return hip_status(dc::launch_reduce_scatter(W, dtype, in, ld_in, out, ld_out, M, pre_div,
+                                              static_cast<hipStream_t>(stream)),
+                    "reduce-scatter launch");
+}
+
+dc_status dc_all_gather(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                        int64_t ld_out, int64_t shard_numel, int32_t order, int32_t step,
+                        void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype))) return st;
+  if (shard_numel < 0) return fail(DC_ERR_ARG, "shard_numel < 0");
+  if (order != DC_ORDER_RANK && order != DC_ORDER_RING) return fail(DC_ERR_ARG, "order=%d", order);
+  if (step < -1 || step >= W) return fail(DC_ERR_ARG, "step=%d outside [-1, W)", step);
+  if ((st = check_slab("in", in, ld_in, shard_numel, dtype)) ||
+      (st = check_slab("out", out, ld_out, W * shard_numel, dtype)))
+    return st;
+  const int64_t b = elem_bytes(dtype);
+  if (overlaps(in, W * ld_in * b, out, W * ld_out * b)) return fail(DC_ERR_ARG, "in and out overlap");
+  return hip_status(dc::launch_all_gather(W, dtype, in, ld_in, out, ld_out, shard_numel, order, step,
+                                          static_cast<hipStream_t>(stream)),
+                    "all-gather launch");
+}
+
+dc_status dc_accumulate(int32_t rows, const float* x, int64_t ld_x, float* acc, int64_t ld_acc,
+                        int64_t M, int32_t init, void* stream) {
+  dc_status st;
+  if (rows < 1 || rows > 65535) return fail(DC_ERR_ARG, "rows=%d outside [1, 65535]", rows);
+  if (M < 0) return fail(DC_ERR_ARG, "M < 0");
+  if (init != 0 && init != 1) return fail(DC_ERR_ARG, "init=%d", init);
+  if ((st = check_slab("x", x, ld_x, M, DC_F32)) || (st = check_slab("acc", acc, ld_acc, M, DC_F32))) return st;
+  if (static_cast<const void*>(x) == static_cast<const void*>(acc)) {
+    if (ld_x != ld_acc) return fail(DC_ERR_ARG, "x == acc needs ld_x == ld_acc");
+  } else if (overlaps(x, rows * ld_x * 4, acc, rows * ld_acc * 4)) {
+    return fail(DC_ERR_ARG, "x and acc overlap");
+  }
+  return hip_status(dc::launch_accumulate(rows, x, ld_x, acc, ld_acc, M, init,
+                                          static_cast<hipStream_t>(stream)),
+                    "accumulate launch");
+}
+
+dc_status dc_deferred_reduce(int32_t W, const float* acc, int64_t ld_acc, float* out,
+                             int64_t ld_out, int64_t M, int32_t out_rows, void* stream) {
+  dc_status st;
+  if ((st = check_w(W))) return st;
+  if (out_rows != 1 && out_rows != W) return fail(DC_ERR_ARG, "out_rows=%d is neither 1 nor W", out_rows);
+  if (M < 0) return fail(DC_ERR_ARG, "M < 0");
+  if ((st = check_slab("acc", acc, ld_acc, M, DC_F32)) || (st = check_slab("out", out, ld_out, M, DC_F32))) return st;
+  if (static_cast<const void*>(acc) == static_cast<const void*>(out)) {
+    if (ld_acc != ld_out) return fail(DC_ERR_ARG, "acc == out needs ld_acc == ld_out");
+  } else if (overlaps(acc, W * ld_acc * 4, out, out_rows * ld_out * 4)) {
+    return fail(DC_ERR_ARG, "acc and out overlap");
+  }
+  return hip_status(dc::launch_deferred_reduce(W, acc, ld_acc, out, ld_out, M, out_rows,
+                                               static_cast<hipStream_t>(stream)),
+                    "deferred reduce launch");
+}
+
+dc_status dc_round_bf16(const float* in, uint16_t* out, int64_t n, void* stream) {
+  if (n < 0) return fail(DC_ERR_ARG, "n < 0");
+  if (n > 0 && (in == nullptr || out == nullptr)) return fail(DC_ERR_NULL, "in or out is NULL");
+  return hip_status(dc::launch_round_bf16(in, out, n, static_cast<hipStream_t>(stream)), "round launch");
+}
+
+dc_status dc_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0) return fail(DC_ERR_SHAPE, "bytes=%lld is not a multiple of 16", (long long)bytes);
+  if (bytes > 0 && (src == nullptr || dst == nullptr)) return fail(DC_ERR_NULL, "src or dst is NULL");
+  if (!aligned16(src) || !aligned16(dst)) return fail(DC_ERR_ALIGN, "src or dst not 16-byte aligned");
+  if (overlaps(src, bytes, dst, bytes)) return fail(DC_ERR_ARG, "src and dst overlap");
+  return hip_status(dc::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)), "copy launch");
+}
+
+}  // extern "C"

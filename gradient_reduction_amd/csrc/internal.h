@@ -1,0 +1,72 @@
+// Launchers of libdc's kernels.  Called by api.cpp after its host-side
+// argument checks; each returns the launch's hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dc.h"
+
+namespace dc {
+
+struct CommSpec {
+  int32_t size;
+  int32_t stride;
+};
+
+struct FlushLaunch {
+  int32_t W;
+  int32_t dtype;
+  int32_t pre_div;
+  const void* in;
+  void* out;
+  int64_t ld_in;
+  int64_t ld_out;
+  int64_t c0;  // first slab column of the bucket
+  int64_t c1;  // one past its last column
+  const dc_task* tasks;
+  int32_t ntasks;
+  const int32_t* owner;
+  int32_t nparams;
+  int32_t ncomms;
+  CommSpec comms[DC_MAX_COMMS];
+};
+
+hipError_t launch_flush(const FlushLaunch& a, hipStream_t stream);
+
+struct GroupTable {
+  int32_t num_groups;
+  int32_t begin[DC_MAX_GROUPS + 1];
+  int32_t parts[DC_MAX_GROUPS];
+  int32_t eligible[DC_MAX_GROUPS];
+};
+
+hipError_t launch_partition_ids(int32_t num_params, const int64_t* numel, const GroupTable& g,
+                                int64_t* flat_offset, int64_t* part_size, int32_t* pid_offsets,
+                                int32_t* pids, int64_t pids_capacity, hipStream_t stream);
+
+hipError_t launch_owner_map(int32_t W, int32_t num_params, const int32_t* pid_offsets,
+                            const int32_t* pids, int64_t pids_capacity, const GroupTable& g,
+                            int32_t* owner,
+                            int32_t* counts, hipStream_t stream);
+
+hipError_t launch_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
+                                 void* out, int64_t ld_out, int64_t M, int32_t pre_div,
+                                 hipStream_t stream);
+
+hipError_t launch_all_gather(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                             int64_t ld_out, int64_t L, int32_t order, int32_t step,
+                             hipStream_t stream);
+
+hipError_t launch_accumulate(int32_t rows, const float* x, int64_t ld_x, float* acc,
+                             int64_t ld_acc, int64_t M, int32_t init, hipStream_t stream);
+
+hipError_t launch_deferred_reduce(int32_t W, const float* acc, int64_t ld_acc, float* out,
+                                  int64_t ld_out, int64_t M, int32_t out_rows,
+                                  hipStream_t stream);
+
+hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
+
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
+}  // namespace dc

@@ -1,0 +1,395 @@
+// Reduce-scatter, all-gather, replica-local accumulation and the deferred
+// reduce (a8-a11) for gfx950, plus the bf16 rounding self-check and a plain
+// streaming copy used as the achievable-bandwidth reference.
+//
+// All are streaming kernels over 16-byte column vectors of [rows, ld] slabs:
+// every element is read once and written once per destination, nothing is
+// reused, so they are HBM bound.  Sizes whose shard boundaries are not
+// vector aligned run an element-wise variant.
+#include "device_common.h"
+#include "internal.h"
+
+namespace dc {
+namespace {
+
+constexpr int kU = 4;  // vectors (or elements) per thread per launch tile
+
+// ---------------------------------------------------------------------------
+// fold helpers
+// ---------------------------------------------------------------------------
+
+template <bool BF16, bool PRE>
+__device__ __forceinline__ void fold16(float* acc, u32x4 x, bool first, float inv, float c) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float a = bf16_lo(x[q]), b = bf16_hi(x[q]);
+      if constexpr (PRE) {
+        if (inv != 0.0f) { a *= inv; b *= inv; } else { a = a / c; b = b / c; }
+        bf16_round_pair(a, b);
+      }
+      acc[2 * q] = first ? a : acc[2 * q] + a;
+      acc[2 * q + 1] = first ? b : acc[2 * q + 1] + b;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float a = __uint_as_float(x[q]);
+      if constexpr (PRE) a = inv != 0.0f ? a * inv : a / c;
+      acc[q] = first ? a : acc[q] + a;
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ u32x4 pack16(const float* acc) {
+  u32x4 y;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] = bf16_pack_out(acc[2 * q], acc[2 * q + 1]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] = __float_as_uint(acc[q]);
+  }
+  return y;
+}
+
+// Fold the W rows of vector column `v` (rows `ldv` vectors apart).  With W
+// known at compile time every row load is issued before the first add.
+template <bool BF16, int WT, bool PRE>
+__device__ __forceinline__ u32x4 fold_rows(const u32x4* in, int64_t ldv, int64_t v, int32_t W,
+                                           float inv, float c) {
+  constexpr int E = BF16 ? 8 : 4;
+  float acc[E];
+  if constexpr (WT > 0) {
+    u32x4 x[WT];
+#pragma unroll
+    for (int r = 0; r < WT; ++r) x[r] = load16<true>(in + r * ldv + v);
+#pragma unroll
+    for (int r = 0; r < WT; ++r) fold16<BF16, PRE>(acc, x[r], r == 0, inv, c);
+  } else {
+#pragma unroll 4
+    for (int32_t r = 0; r < W; ++r) fold16<BF16, PRE>(acc, load16<true>(in + r * ldv + v), r == 0, inv, c);
+  }
+  return pack16<BF16>(acc);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* base, int64_t idx) {
+  if constexpr (BF16) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[idx] << 16);
+  else return reinterpret_cast<const float*>(base)[idx];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_elem(void* base, int64_t idx, float v) {
+  if constexpr (BF16) reinterpret_cast<uint16_t*>(base)[idx] = bf16_out(v);
+  else reinterpret_cast<float*>(base)[idx] = v;
+}
+
+template <bool BF16>
+__device__ __forceinline__ float pre_elem(float x, bool pre, float inv, float c) {
+  if (!pre) return x;
+  float v = inv != 0.0f ? x * inv : x / c;
+  if constexpr (BF16) v = bf16_lo(bf16_pack_rne(v, 0.0f));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// a8. reduce-scatter: out[s][k] = fold_r pre(in[r][s*L + k])
+// ---------------------------------------------------------------------------
+
+// Vector path (L a multiple of the vector width): blockIdx.y = shard.
+template <bool BF16, int WT, bool PRE>
+__global__ __launch_bounds__(kThreads) void k_rs_vec(int32_t W, const u32x4* __restrict__ in,
+                                                     int64_t ldv_in, u32x4* __restrict__ out,
+                                                     int64_t ldv_out, int64_t Lv, float inv,
+                                                     float c) {
+  const int64_t s = blockIdx.y;
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int64_t k = k0 + (int64_t)u * kThreads;
+    if (k < Lv) store16<false>(out + s * ldv_out + k, fold_rows<BF16, WT, PRE>(in, ldv_in, s * Lv + k, W, inv, c));
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_rs_elem(int32_t W, const void* __restrict__ in,
+                                                      int64_t ld_in, void* __restrict__ out,
+                                                      int64_t ld_out, int64_t L, int32_t pre,
+                                                      float inv, float c) {
+  const int64_t s = blockIdx.y;
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
+  for (int u = 0; u < kU; ++u) {
+    const int64_t k = k0 + (int64_t)u * kThreads;
+    if (k >= L) continue;
+    float acc = 0.0f;
+    for (int32_t r = 0; r < W; ++r) {
+      const float v = pre_elem<BF16>(load_elem<BF16>(in, r * ld_in + s * L + k), pre != 0, inv, c);
+      acc = r == 0 ? v : acc + v;
+    }
+    store_elem<BF16>(out, s * ld_out + k, acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// a9. all-gather
+// ---------------------------------------------------------------------------
+
+// Thread (s, k) reads chunk s's vector k once and writes it wherever node i
+// keeps chunk s: position s (rank order) or (i - s) mod W (ring order).  In
+// step mode only chunk `step` (rank) or position `step` (ring) is written.
+__global__ __launch_bounds__(kThreads) void k_ag_vec(int32_t W, const u32x4* __restrict__ in,
+                                                     int64_t ldv_in, u32x4* __restrict__ out,
+                                                     int64_t ldv_out, int64_t Lv, int32_t order,
+                                                     int32_t step) {
+  const int32_t s = blockIdx.y;
+  if (order == DC_ORDER_RANK && step >= 0 && s != step) return;
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int64_t k = k0 + (int64_t)u * kThreads;
+    if (k >= Lv) continue;
+    const u32x4 x = load16<true>(in + (int64_t)s * ldv_in + k);
+    for (int32_t i = 0; i < W; ++i) {
+      const int32_t p = order == DC_ORDER_RANK ? s : (i - s + W) % W;
+      if (order == DC_ORDER_RING && step >= 0 && p != step) continue;
+      store16<false>(out + (int64_t)i * ldv_out + (int64_t)p * Lv + k, x);
+    }
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void k_ag_elem(int32_t W, const E* __restrict__ in,
+                                                      int64_t ld_in, E* __restrict__ out,
+                                                      int64_t ld_out, int64_t L, int32_t order,
+                                                      int32_t step) {
+  const int32_t s = blockIdx.y;
+  if (order == DC_ORDER_RANK && step >= 0 && s != step) return;
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
+  for (int u = 0; u < kU; ++u) {
+    const int64_t k = k0 + (int64_t)u * kThreads;
+    if (k >= L) continue;
+    const E x = in[(int64_t)s * ld_in + k];
+    for (int32_t i = 0; i < W; ++i) {
+      const int32_t p = order == DC_ORDER_RANK ? s : (i - s + W) % W;
+      if (order == DC_ORDER_RING && step >= 0 && p != step) continue;
+      out[(int64_t)i * ld_out + (int64_t)p * L + k] = x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// a10. accumulate: acc = acc + x   (init: acc = +0 + x)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_accumulate(const float* __restrict__ x,
+                                                         int64_t ld_x, float* acc,
+                                                         int64_t ld_acc, int64_t M, int32_t init) {
+  const int64_t r = blockIdx.y;
+  const int64_t nvec = M / 4;
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x + r * ld_x);
+  u32x4* av = reinterpret_cast<u32x4*>(acc + r * ld_acc);
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int64_t k = k0 + (int64_t)u * kThreads;
+    if (k < nvec) {
+      const u32x4 xx = load16<true>(xv + k);
+      u32x4 aa;
+      if (init) {
+        aa = u32x4{0u, 0u, 0u, 0u};
+      } else {
+        aa = load16<true>(av + k);
+      }
+      u32x4 y;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y[q] = __float_as_uint(__uint_as_float(aa[q]) + __uint_as_float(xx[q]));
+      store16<false>(av + k, y);
+    } else if (k == nvec) {
+      for (int64_t j = nvec * 4; j < M; ++j) {
+        const float a = init ? 0.0f : acc[r * ld_acc + j];
+        acc[r * ld_acc + j] = a + x[r * ld_x + j];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// a11. deferred reduce: out[i][j] = fold_r acc[r][j], i < out_rows
+// ---------------------------------------------------------------------------
+template <int WT>
+__global__ __launch_bounds__(kThreads) void k_deferred(int32_t W, const float* acc, int64_t ld_acc,
+                                                       float* out, int64_t ld_out, int64_t M,
+                                                       int32_t out_rows) {
+  const int64_t nvec = M / 4;
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
+  const u32x4* in = reinterpret_cast<const u32x4*>(acc);
+  u32x4* ov = reinterpret_cast<u32x4*>(out);
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int64_t k = k0 + (int64_t)u * kThreads;
+    if (k < nvec) {
+      const u32x4 y = fold_rows<false, WT, false>(in, ld_acc / 4, k, W, 0.0f, 1.0f);
+      for (int32_t i = 0; i < out_rows; ++i) store16<false>(ov + i * (ld_out / 4) + k, y);
+    } else if (k == nvec) {
+      for (int64_t j = nvec * 4; j < M; ++j) {
+        float sum = 0.0f;
+        for (int32_t r = 0; r < W; ++r) sum = r == 0 ? acc[r * ld_acc + j] : sum + acc[r * ld_acc + j];
+        for (int32_t i = 0; i < out_rows; ++i) out[i * ld_out + j] = sum;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_round_bf16(const float* __restrict__ in,
+                                                         uint16_t* __restrict__ out, int64_t n) {
+  const int64_t step = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += step) out[i] = bf16_out(in[i]);
+}
+
+__global__ __launch_bounds__(kThreads) void k_copy(const u32x4* __restrict__ src,
+                                                   u32x4* __restrict__ dst, int64_t nvec) {
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int64_t k = k0 + (int64_t)u * kThreads;
+    if (k < nvec) store16<false>(dst + k, load16<true>(src + k));
+  }
+}
+
+inline unsigned blocks_for(int64_t n) {
+  return (unsigned)((n + kThreads * kU - 1) / (kThreads * kU));
+}
+
+inline void reciprocal(int32_t c, float* inv, float* cf) {
+  *cf = (float)c;
+  *inv = (c & (c - 1)) == 0 ? 1.0f / (float)c : 0.0f;  // exact for powers of two
+}
+
+template <bool BF16, bool PRE>
+hipError_t rs_vec_w(int32_t W, const void* in, int64_t ld_in, void* out, int64_t ld_out, int64_t L,
+                    float inv, float c, hipStream_t stream) {
+  constexpr int E = BF16 ? 8 : 4;
+  const int64_t Lv = L / E;
+  const dim3 grid(blocks_for(Lv), (unsigned)W);
+  const u32x4* i4 = reinterpret_cast<const u32x4*>(in);
+  u32x4* o4 = reinterpret_cast<u32x4*>(out);
+  switch (W) {
+#define DC_RS_W(w)                                                                           \
+  case w:                                                                                    \
+    hipLaunchKernelGGL((k_rs_vec<BF16, w, PRE>), grid, dim3(kThreads), 0, stream, W, i4,     \
+                       ld_in / E, o4, ld_out / E, Lv, inv, c);                               \
+    break;
+    DC_RS_W(1)
+    DC_RS_W(2)
+    DC_RS_W(4)
+    DC_RS_W(8)
+    DC_RS_W(16)
+#undef DC_RS_W
+    default:
+      hipLaunchKernelGGL((k_rs_vec<BF16, 0, PRE>), grid, dim3(kThreads), 0, stream, W, i4,
+                         ld_in / E, o4, ld_out / E, Lv, inv, c);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
+                                 void* out, int64_t ld_out, int64_t M, int32_t pre_div,
+                                 hipStream_t stream) {
+  const int64_t L = M / W;
+  if (L == 0) return hipSuccess;
+  float inv, c;
+  reciprocal(W, &inv, &c);
+  const bool bf = dtype == DC_BF16;
+  const int E = bf ? 8 : 4;
+  if (L % E == 0) {
+    if (bf) return pre_div ? rs_vec_w<true, true>(W, in, ld_in, out, ld_out, L, inv, c, stream)
+                           : rs_vec_w<true, false>(W, in, ld_in, out, ld_out, L, inv, c, stream);
+    return pre_div ? rs_vec_w<false, true>(W, in, ld_in, out, ld_out, L, inv, c, stream)
+                   : rs_vec_w<false, false>(W, in, ld_in, out, ld_out, L, inv, c, stream);
+  }
+  const dim3 grid(blocks_for(L), (unsigned)W);
+  if (bf)
+    hipLaunchKernelGGL(k_rs_elem<true>, grid, dim3(kThreads), 0, stream, W, in, ld_in, out, ld_out,
+                       L, pre_div, inv, c);
+  else
+    hipLaunchKernelGGL(k_rs_elem<false>, grid, dim3(kThreads), 0, stream, W, in, ld_in, out,
+                       ld_out, L, pre_div, inv, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_all_gather(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                             int64_t ld_out, int64_t L, int32_t order, int32_t step,
+                             hipStream_t stream) {
+  if (L == 0) return hipSuccess;
+  const bool bf = dtype == DC_BF16;
+  const int E = bf ? 8 : 4;
+  if (L % E == 0) {
+    const int64_t Lv = L / E;
+    hipLaunchKernelGGL(k_ag_vec, dim3(blocks_for(Lv), (unsigned)W), dim3(kThreads), 0, stream, W,
+                       reinterpret_cast<const u32x4*>(in), ld_in / E, reinterpret_cast<u32x4*>(out),
+                       ld_out / E, Lv, order, step);
+  } else if (bf) {
+    hipLaunchKernelGGL(k_ag_elem<uint16_t>, dim3(blocks_for(L), (unsigned)W), dim3(kThreads), 0,
+                       stream, W, reinterpret_cast<const uint16_t*>(in), ld_in,
+                       reinterpret_cast<uint16_t*>(out), ld_out, L, order, step);
+  } else {
+    hipLaunchKernelGGL(k_ag_elem<uint32_t>, dim3(blocks_for(L), (unsigned)W), dim3(kThreads), 0,
+                       stream, W, reinterpret_cast<const uint32_t*>(in), ld_in,
+                       reinterpret_cast<uint32_t*>(out), ld_out, L, order, step);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_accumulate(int32_t rows, const float* x, int64_t ld_x, float* acc,
+                             int64_t ld_acc, int64_t M, int32_t init, hipStream_t stream) {
+  if (M == 0 || rows == 0) return hipSuccess;
+  const int64_t nvec = M / 4;
+  hipLaunchKernelGGL(k_accumulate, dim3(blocks_for(nvec + 1), (unsigned)rows), dim3(kThreads), 0,
+                     stream, x, ld_x, acc, ld_acc, M, init);
+  return hipGetLastError();
+}
+
+hipError_t launch_deferred_reduce(int32_t W, const float* acc, int64_t ld_acc, float* out,
+                                  int64_t ld_out, int64_t M, int32_t out_rows,
+                                  hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const dim3 grid(blocks_for(M / 4 + 1));
+  switch (W) {
+#define DC_DR_W(w)                                                                            \
+  case w:                                                                                     \
+    hipLaunchKernelGGL(k_deferred<w>, grid, dim3(kThreads), 0, stream, W, acc, ld_acc, out,   \
+                       ld_out, M, out_rows);                                                  \
+    break;
+    DC_DR_W(1)
+    DC_DR_W(2)
+    DC_DR_W(4)
+    DC_DR_W(8)
+    DC_DR_W(16)
+#undef DC_DR_W
+    default:
+      hipLaunchKernelGGL(k_deferred<0>, grid, dim3(kThreads), 0, stream, W, acc, ld_acc, out,
+                         ld_out, M, out_rows);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + kThreads - 1) / kThreads;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_round_bf16, dim3((unsigned)blocks), dim3(kThreads), 0, stream, in, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  const int64_t nvec = bytes / 16;
+  if (nvec == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_copy, dim3(blocks_for(nvec)), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), nvec);
+  return hipGetLastError();
+}
+
+}  // namespace dc

@@ -1,0 +1,213 @@
+"""Thin ctypes binding of libdc.so: the functions of include/dc.h, same names,
+same arguments.
+
+Marshalling only.  Device pointers may be given as torch tensors (their
+data_ptr()) or ints; host arrays as numpy arrays or sequences; `stream` as a
+torch stream, a raw hipStream_t int, or None for torch's current stream on the
+current device.  Every function raises DCError when the library returns a
+non-zero status.  There is no fallback: without libdc.so nothing runs.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdc.so")
+
+DC_OK = 0
+DC_ERR_NULL, DC_ERR_ARG, DC_ERR_SHAPE, DC_ERR_ALIGN = 1, 2, 3, 4
+DC_ERR_DTYPE, DC_ERR_TASKS, DC_ERR_HIP, DC_ERR_UNSUPPORTED = 5, 6, 7, 8
+DC_BF16, DC_F32 = 0, 1
+DC_ORDER_RANK, DC_ORDER_RING = 0, 1
+DC_MAX_W, DC_MAX_GROUPS, DC_MAX_COMMS = 64, 64, 8
+
+TASK_DTYPE = np.dtype([("offset", "<i8"), ("numel", "<i8"), ("param", "<i4"),
+                       ("comm", "<i4"), ("reserved", "<i8")])
+COMM_DTYPE = np.dtype([("size", "<i4"), ("stride", "<i4")])
+
+
+class dc_probe(ctypes.Structure):
+    _fields_ = [("tasks", ctypes.c_int32), ("owner_tasks", ctypes.c_int32),
+                ("pre_div", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("reduced_elems", ctypes.c_int64), ("owner_elems", ctypes.c_int64),
+                ("written", ctypes.c_int64 * DC_MAX_W), ("kept", ctypes.c_int64 * DC_MAX_W),
+                ("discarded", ctypes.c_int64 * DC_MAX_W)]
+
+
+class DCError(RuntimeError):
+    def __init__(self, code, fn, msg):
+        super().__init__(f"{fn}: status {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+_i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+
+_SIGS = {
+    "dc_version": ([], ctypes.c_char_p),
+    "dc_strerror": ([_i32], ctypes.c_char_p),
+    "dc_last_error": ([], ctypes.c_char_p),
+    "dc_partition_ids": ([_i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp], _i32),
+    "dc_build_owner_map": ([_i32, _i32, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "dc_validate_tasks": ([_i32, _vp, _i32, _i64, _i32, _vp, _i32], _i32),
+    "dc_flush_bucket": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _vp,
+                         _i32, _i32, _vp], _i32),
+    "dc_probe_flush": ([_i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp], _i32),
+    "dc_reduce_scatter": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
+    "dc_all_gather": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _i32, _vp], _i32),
+    "dc_accumulate": ([_i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
+    "dc_deferred_reduce": ([_i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
+    "dc_round_bf16": ([_vp, _vp, _i64, _vp], _i32),
+    "dc_stream_copy": ([_vp, _vp, _i64, _vp], _i32),
+}
+
+
+def lib():
+    """The loaded libdc.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _dev(x):
+    """Device pointer of a tensor / int / None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _host(x, dtype):
+    """Host pointer of a numpy array (converted to `dtype`) or sequence."""
+    if x is None:
+        return None, None
+    a = np.ascontiguousarray(x, dtype=dtype)
+    return a.ctypes.data_as(_vp), a
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, rc):
+    if rc != DC_OK:
+        raise DCError(rc, fn, lib().dc_last_error().decode())
+
+
+def dc_version():
+    return lib().dc_version().decode()
+
+
+def dc_strerror(status):
+    return lib().dc_strerror(status).decode()
+
+
+def dc_last_error():
+    return lib().dc_last_error().decode()
+
+
+def dc_partition_ids(W, num_params, numel, num_groups, group_begin, group_parts, flat_offset,
+                     part_size, pid_offsets, pids, pids_capacity, stream=None):
+    gb, _a = _host(group_begin, np.int32)
+    gp, _b = _host(group_parts, np.int32)
+    _check("dc_partition_ids", lib().dc_partition_ids(
+        W, num_params, _dev(numel), num_groups, gb, gp, _dev(flat_offset), _dev(part_size),
+        _dev(pid_offsets), _dev(pids), pids_capacity, _stream(stream)))
+
+
+def dc_build_owner_map(W, num_params, pid_offsets, pids, pids_capacity, num_groups, group_begin,
+                       group_comm_size, group_rank_to_global, owner, counts, stream=None):
+    gb, _a = _host(group_begin, np.int32)
+    cs, _b = _host(group_comm_size, np.int32)
+    rg, _c = _host(np.asarray(group_rank_to_global, np.int32).reshape(-1), np.int32)
+    _check("dc_build_owner_map", lib().dc_build_owner_map(
+        W, num_params, _dev(pid_offsets), _dev(pids), pids_capacity, num_groups, gb, cs, rg,
+        _dev(owner), _dev(counts), _stream(stream)))
+
+
+def dc_validate_tasks(W, tasks, num_tasks, bucket_numel, num_params, comms, num_comms):
+    tp, _a = _host(tasks, TASK_DTYPE)
+    cp, _b = _host(comms, COMM_DTYPE)
+    _check("dc_validate_tasks", lib().dc_validate_tasks(W, tp, num_tasks, bucket_numel,
+                                                        num_params, cp, num_comms))
+
+
+def dc_flush_bucket(W, dtype, slab_in, ld_in, slab_out, ld_out, bucket_col, bucket_numel, tasks,
+                    num_tasks, owner, num_params, comms, num_comms, pre_div, stream=None):
+    cp, _a = _host(comms, COMM_DTYPE)
+    _check("dc_flush_bucket", lib().dc_flush_bucket(
+        W, dtype, _dev(slab_in), ld_in, _dev(slab_out), ld_out, bucket_col, bucket_numel,
+        _dev(tasks), num_tasks, _dev(owner), num_params, cp, num_comms, pre_div,
+        _stream(stream)))
+
+
+def dc_probe_flush(W, dtype, tasks, num_tasks, owner, num_params, pid_offsets, pids, comms,
+                   num_comms, pre_div):
+    """Host-only; returns a dc_probe."""
+    tp, _a = _host(tasks, TASK_DTYPE)
+    op, _b = _host(owner, np.int32)
+    po, _c = _host(pid_offsets, np.int32)
+    pp, _d = _host(pids, np.int32) if pids is not None and len(pids) else (None, None)
+    cp, _e = _host(comms, COMM_DTYPE)
+    out = dc_probe()
+    _check("dc_probe_flush", lib().dc_probe_flush(W, dtype, tp, num_tasks, op, num_params, po, pp,
+                                                  cp, num_comms, pre_div, ctypes.byref(out)))
+    return out
+
+
+def dc_reduce_scatter(W, dtype, in_, ld_in, out, ld_out, M, pre_div, stream=None):
+    _check("dc_reduce_scatter", lib().dc_reduce_scatter(W, dtype, _dev(in_), ld_in, _dev(out),
+                                                        ld_out, M, pre_div, _stream(stream)))
+
+
+def dc_all_gather(W, dtype, in_, ld_in, out, ld_out, shard_numel, order, step, stream=None):
+    _check("dc_all_gather", lib().dc_all_gather(W, dtype, _dev(in_), ld_in, _dev(out), ld_out,
+                                                shard_numel, order, step, _stream(stream)))
+
+
+def dc_accumulate(rows, x, ld_x, acc, ld_acc, M, init, stream=None):
+    _check("dc_accumulate", lib().dc_accumulate(rows, _dev(x), ld_x, _dev(acc), ld_acc, M, init,
+                                                _stream(stream)))
+
+
+def dc_deferred_reduce(W, acc, ld_acc, out, ld_out, M, out_rows, stream=None):
+    _check("dc_deferred_reduce", lib().dc_deferred_reduce(W, _dev(acc), ld_acc, _dev(out), ld_out,
+                                                          M, out_rows, _stream(stream)))
+
+
+def dc_round_bf16(in_, out, n, stream=None):
+    _check("dc_round_bf16", lib().dc_round_bf16(_dev(in_), _dev(out), n, _stream(stream)))
+
+
+def dc_stream_copy(src, dst, nbytes, stream=None):
+    _check("dc_stream_copy", lib().dc_stream_copy(_dev(src), _dev(dst), nbytes, _stream(stream)))
+
+
+def tasks_array(tasks):
+    """dc_task records from (offset, numel, param, comm) tuples."""
+    a = np.zeros(len(tasks), TASK_DTYPE)
+    for k, (off, n, p, c) in enumerate(tasks):
+        a[k] = (off, n, p, c, 0)
+    return a
+
+
+def comms_array(comms):
+    a = np.zeros(len(comms), COMM_DTYPE)
+    for k, (size, stride) in enumerate(comms):
+        a[k] = (size, stride)
+    return a

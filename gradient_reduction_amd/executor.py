@@ -1,0 +1,131 @@
+"""ZeRO-1 bucket-flush executor over one GPU's [W, M] gradient slab.
+
+DeepSpeed issue "[REQUEST] DeepCompile ZeRO-1: reduce-to-owner instead of
+AllReduce": at init the owner map is built from the partition lists and the
+qualifying ratio is reported; every bucket flush then reduces each task to its
+owner (reduce_to_owner on) or to every rank (off, the default), and the probe
+reports one line per flush for the first 20 flushes (reduce_probe).
+
+torch supplies device memory and the stream; every step runs in libdc.so.
+"""
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import dc
+
+PROBE_FLUSHES = 20
+
+
+@dataclass
+class BucketSpec:
+    col: int                                  # first slab column
+    numel: int
+    tasks: Sequence[Tuple[int, int, int, int]]  # (offset, numel, param, comm)
+
+
+class Zero1FlushExecutor:
+    def __init__(self, W: int, dtype: int, numel: Sequence[int], group_begin: Sequence[int],
+                 group_parts: Sequence[int], group_comm_size: Sequence[int],
+                 group_rank_to_global: Sequence[Sequence[int]], comms: Sequence[Tuple[int, int]],
+                 buckets: Sequence[BucketSpec], pre_div: int, reduce_to_owner: bool = False,
+                 reduce_probe: bool = False, device: str = "cuda", log=print):
+        import torch
+        self.torch = torch
+        self.W, self.dtype, self.pre_div = W, dtype, pre_div
+        self.reduce_to_owner, self.reduce_probe = reduce_to_owner, reduce_probe
+        self.log = log
+        self.P = len(numel)
+        self.G = len(group_parts)
+        self.group_begin = list(group_begin)
+        self.group_parts = list(group_parts)
+        self.group_comm_size = list(group_comm_size)
+        self.group_rank_to_global = np.asarray(group_rank_to_global, np.int32).reshape(self.G, W)
+        self.comms = dc.comms_array(comms)
+        self.buckets = list(buckets)
+        self.flushes = 0
+        dev = torch.device(device)
+        self.pids_capacity = self.P + sum(p - 1 for p in self.group_parts)
+        self.d_numel = torch.tensor(list(numel), dtype=torch.int64, device=dev)
+        self.d_flat = torch.empty(max(self.P, 1), dtype=torch.int64, device=dev)
+        self.d_part_size = torch.empty(self.G, dtype=torch.int64, device=dev)
+        self.d_pid_off = torch.empty(self.P + 1, dtype=torch.int32, device=dev)
+        self.d_pids = torch.empty(max(self.pids_capacity, 1), dtype=torch.int32, device=dev)
+        self.d_owner = torch.empty(max(self.P, 1), dtype=torch.int32, device=dev)
+        self.d_counts = torch.empty(2 * self.G, dtype=torch.int32, device=dev)
+        # one device task table for all buckets, bucket b at rows [t_begin[b], t_begin[b+1])
+        self.h_tasks = [dc.tasks_array(b.tasks) for b in self.buckets]
+        for b, t in zip(self.buckets, self.h_tasks):
+            dc.dc_validate_tasks(W, t, len(t), b.numel, self.P, self.comms, len(self.comms))
+        self.t_begin = np.concatenate([[0], np.cumsum([len(t) for t in self.h_tasks])]).astype(int)
+        allt = np.concatenate(self.h_tasks) if self.h_tasks else np.zeros(0, dc.TASK_DTYPE)
+        raw = torch.from_numpy(allt.view(np.uint8).copy())
+        self.d_tasks = raw.to(dev) if len(allt) else torch.empty(32, dtype=torch.uint8, device=dev)
+        self.h_owner: Optional[np.ndarray] = None
+
+    def build_owner_map(self, stream=None) -> None:
+        """a1 + a2 on the device (no host synchronization)."""
+        dc.dc_partition_ids(self.W, self.P, self.d_numel, self.G, self.group_begin,
+                            self.group_parts, self.d_flat, self.d_part_size, self.d_pid_off,
+                            self.d_pids, self.pids_capacity, stream)
+        dc.dc_build_owner_map(self.W, self.P, self.d_pid_off, self.d_pids, self.pids_capacity,
+                              self.G, self.group_begin, self.group_comm_size,
+                              self.group_rank_to_global, self.d_owner, self.d_counts, stream)
+
+    def fetch_metadata(self) -> None:
+        """Copy the owner map and partition lists to the host (synchronizes);
+        the probe and the ratio report use them."""
+        self.h_owner = self.d_owner[:self.P].cpu().numpy()
+        self.h_pid_off = self.d_pid_off.cpu().numpy()
+        self.h_pids = self.d_pids[:int(self.h_pid_off[-1])].cpu().numpy()
+        self.h_counts = self.d_counts.cpu().numpy()
+
+    def ratio_line(self) -> str:
+        owners = int(self.h_counts[0::2].sum())
+        return f"DeepCompile reduce_to_owner: {owners}/{self.P} gradients reduce to one rank"
+
+    def task_table(self, b: int) -> int:
+        return self.d_tasks.data_ptr() + 32 * int(self.t_begin[b])
+
+    def flush(self, b: int, slab_in, ld_in: int, slab_out, ld_out: int, stream=None) -> None:
+        bk = self.buckets[b]
+        owner = self.d_owner if self.reduce_to_owner else None
+        dc.dc_flush_bucket(self.W, self.dtype, slab_in, ld_in, slab_out, ld_out, bk.col, bk.numel,
+                           self.task_table(b), len(bk.tasks), owner, self.P, self.comms,
+                           len(self.comms), self.pre_div, stream)
+        if self.reduce_probe and self.flushes < PROBE_FLUSHES:
+            self.log(self.probe_line(b, self.flushes))
+        self.flushes += 1
+
+    def probe(self, b: int):
+        if self.h_owner is None:
+            self.fetch_metadata()
+        t = self.h_tasks[b]
+        owner = self.h_owner if self.reduce_to_owner else None
+        return dc.dc_probe_flush(self.W, self.dtype, t, len(t), owner, self.P, self.h_pid_off,
+                                 self.h_pids, self.comms, len(self.comms), self.pre_div)
+
+    def probe_line(self, b: int, flush_no: int, rank: int = 0) -> str:
+        pr = self.probe(b)
+        name = "BFloat16" if self.dtype == dc.DC_BF16 else "Float"
+        red = pr.reduced_elems
+        disc = 100.0 * pr.discarded[rank] / red if red else 0.0
+        oe = 100.0 * pr.owner_elems / red if red else 0.0
+        return (f"[dc-probe][r{rank}] flushReduceBucket #{flush_no} dtype={name} "
+                f"tasks={pr.tasks} reduced_elems={red} kept_elems={pr.kept[rank]} "
+                f"discarded={disc:.1f}% pre_div={self.pre_div} owner_tasks={pr.owner_tasks} "
+                f"owner_elems={pr.owner_elems} ({oe:.1f}%)")
+
+
+def from_workload(w, reduce_to_owner: bool, reduce_probe: bool = False, device: str = "cuda",
+                  log=print) -> Zero1FlushExecutor:
+    """Executor for a synthetic flush workload description (duck-typed: the
+    fields of synth.workloads.FlushWorkload)."""
+    buckets = [BucketSpec(b.col, b.numel, [(t.offset, t.numel, t.param, t.comm) for t in b.tasks])
+               for b in w.buckets]
+    comm_sizes = [w.comms[c].size for c in w.group_comm]
+    return Zero1FlushExecutor(
+        w.W, w.dtype, w.numel, w.group_begin, w.group_parts(), comm_sizes,
+        w.group_rank_to_global(), [(c.size, c.stride) for c in w.comms], buckets, w.pre_div,
+        reduce_to_owner=reduce_to_owner, reduce_probe=reduce_probe, device=device, log=log)

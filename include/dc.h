@@ -1,0 +1,282 @@
+/*
+ * dc.h - C ABI of libdc.so, a data-parallel gradient-reduction path for one
+ * MI355X (gfx950) GPU.
+ *
+ * W simulated data-parallel ranks are the rows of a [W, ld] gradient slab in
+ * device memory (row r = rank r's gradient; row-major; `ld` = row stride in
+ * elements).  Every device entry point enqueues work on the given HIP stream
+ * and returns at once; its results are valid once that stream reaches them.
+ *
+ * Pages cited (by title and section):
+ *   [DS] DeepSpeed issue "[REQUEST] DeepCompile ZeRO-1: reduce-to-owner
+ *        instead of AllReduce"
+ *   [MT] MaxText PR "Defer the data-parallel gradient all-reduce to update()
+ *        under gradient accumulation"
+ *   [AG] "AllGather" (collective-communication notes)
+ *
+ * Conventions shared by every function:
+ *   - Return value: DC_OK (0) or one of the DC_ERR_* codes below.  Argument
+ *     checks run on the host before anything is enqueued; a failed check
+ *     enqueues nothing.  dc_last_error() gives a message for the calling
+ *     thread's last failure.  No C++ exception crosses this boundary.
+ *   - "device" pointers are HIP device (or managed) memory; "host" pointers
+ *     are ordinary host memory read synchronously during the call.
+ *   - The caller owns every buffer.  The library allocates nothing, keeps no
+ *     pointer after the call returns (device pointers are used by the
+ *     enqueued kernels until they finish) and never synchronizes the stream.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *   - dtype: DC_BF16 (bfloat16 stored as uint16 bit patterns) or DC_F32.
+ *   - Slab base pointers must be 16-byte aligned and `ld` a multiple of 16
+ *     bytes (8 bf16 or 4 fp32 elements), else DC_ERR_ALIGN.
+ *   - Sums are folded in fp32 in ascending rank order (member order within a
+ *     communicator), starting from the first contribution, and rounded once
+ *     to the dtype (round to nearest even; NaN -> quiet NaN 0x7FC0|sign for
+ *     bf16).  fp32 arithmetic keeps subnormals and is never contracted.
+ */
+#ifndef DC_H
+#define DC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dc_status;
+
+#define DC_OK 0
+#define DC_ERR_NULL 1        /* a required pointer is NULL */
+#define DC_ERR_ARG 2         /* a scalar argument is out of range, or buffers overlap */
+#define DC_ERR_SHAPE 3       /* sizes or strides do not fit together */
+#define DC_ERR_ALIGN 4       /* a slab base or stride is not 16-byte aligned */
+#define DC_ERR_DTYPE 5       /* unknown dtype */
+#define DC_ERR_TASKS 6       /* a task table breaks its contract (dc_validate_tasks) */
+#define DC_ERR_HIP 7         /* a HIP launch or runtime call failed */
+#define DC_ERR_UNSUPPORTED 8 /* a valid request this build does not handle */
+
+#define DC_BF16 0
+#define DC_F32 1
+
+#define DC_ORDER_RANK 0
+#define DC_ORDER_RING 1
+
+#define DC_MAX_W 64          /* simulated ranks per slab */
+#define DC_MAX_GROUPS 64     /* parameter groups per owner map */
+#define DC_MAX_COMMS 8       /* communicators per flush */
+
+/* One bucket entry: a whole parameter's gradient ([DS] "Describe
+ * alternatives": buckets hold one full-parameter task each, in gradient
+ * arrival order).  32 bytes.
+ *   offset   first column of the task, relative to the bucket's first column
+ *   numel    columns of the task (>= 0)
+ *   param    index into the owner map
+ *   comm     index into the flush's communicator table
+ * A bucket's table is sorted and packed: offset[0] = 0,
+ * offset[t+1] = offset[t] + numel[t], and the numels sum to the bucket size. */
+typedef struct {
+  int64_t offset;
+  int64_t numel;
+  int32_t param;
+  int32_t comm;
+  int64_t reserved;
+} dc_task;
+
+/* A communicator over the W ranks ([DS] Design points, groups reduced over a
+ * different communicator, e.g. MoE experts): `size` c divides W and the ranks
+ * split into W/c blocks; block b's members are {b*c + i} when stride == 1,
+ * or {b + i*W/c} when stride == W/c (i = 0..c-1).  Entry 0 of every table is
+ * the data-parallel communicator {W, 1}. */
+typedef struct {
+  int32_t size;
+  int32_t stride;
+} dc_comm;
+
+/* Probe record of one flush ([DS] problem statement, the probe report, and
+ * "reduce_probe").  Per rank r: written[r] = elements the flush writes to row
+ * r, kept[r] = elements of tasks whose parameter rank r holds (its partition
+ * appears in the parameter's partition list), discarded[r] = written - kept. */
+typedef struct {
+  int32_t tasks;
+  int32_t owner_tasks;
+  int32_t pre_div;
+  int32_t dtype;
+  int64_t reduced_elems;
+  int64_t owner_elems;
+  int64_t written[DC_MAX_W];
+  int64_t kept[DC_MAX_W];
+  int64_t discarded[DC_MAX_W];
+} dc_probe;
+
+/* Library version string (static storage). */
+const char* dc_version(void);
+
+/* Static description of a status code. */
+const char* dc_strerror(dc_status status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* dc_last_error(void);
+
+/* a1. Partition lists ([DS] Design points, the owner map: the ZeRO
+ * optimizer's param_to_partition_ids lists every optimizer partition holding
+ * a piece of a parameter).  For each group g, the params
+ * group_begin[g] .. group_begin[g+1]-1 are laid end to end in declaration
+ * order (flat offset a_i = sum of earlier sizes in the group); the group's
+ * T_g elements split into group_parts[g] equal partitions of
+ * S_g = ceil(T_g / group_parts[g]) elements (the last one shorter); a
+ * non-empty param's list is floor(a_i/S_g) .. floor((a_i+n_i-1)/S_g), an
+ * empty param's list is empty.
+ *   numel         device int64[num_params], each in [0, 2^48)
+ *   group_begin   host int32[num_groups+1], non-decreasing, 0 .. num_params
+ *   group_parts   host int32[num_groups], each in [1, DC_MAX_W]
+ *   flat_offset   device int64[num_params] out: a_i
+ *   part_size     device int64[num_groups] out: S_g
+ *   pid_offsets   device int32[num_params+1] out: CSR row starts
+ *   pids          device int32[pids_capacity] out: CSR entries
+ * pids_capacity must be at least num_params + sum_g (group_parts[g] - 1),
+ * the largest count any sizes can produce, else DC_ERR_SHAPE.  Sizes outside
+ * [0, 2^48) are not checked on the host; the kernel treats a negative size
+ * as 0.  One workgroup scans all groups. */
+dc_status dc_partition_ids(int32_t W, int32_t num_params, const int64_t* numel,
+                           int32_t num_groups, const int32_t* group_begin,
+                           const int32_t* group_parts, int64_t* flat_offset, int64_t* part_size,
+                           int32_t* pid_offsets, int32_t* pids, int64_t pids_capacity,
+                           void* stream);
+
+/* a2. Owner map ([DS] Design points): a param with exactly one partition
+ * entry has exactly one owner, that entry's rank; a param with two or more
+ * entries (it straddles a partition boundary) or none gets -1, meaning
+ * AllReduce.  A group takes part only when its communicator is the
+ * data-parallel one: group_comm_size[g] == W and group rank i maps to global
+ * rank i for every i; every param of another group gets -1.
+ *   pid_offsets, pids      device CSR from dc_partition_ids; pids_capacity is
+ *                          the length of pids (entries beyond it are not read)
+ *   group_begin            host int32[num_groups+1] (as for dc_partition_ids)
+ *   group_comm_size        host int32[num_groups]
+ *   group_rank_to_global   host int32[num_groups * W], row g = group g's
+ *                          group rank -> global rank map (pad with -1)
+ *   owner                  device int32[num_params] out
+ *   counts                 device int32[2*num_groups] out: counts[2g] = params
+ *                          with an owner, counts[2g+1] = params with two or
+ *                          more entries (at most group_parts[g]-1)
+ * Entries of pids outside [0, W) are reported as no owner. */
+dc_status dc_build_owner_map(int32_t W, int32_t num_params, const int32_t* pid_offsets,
+                             const int32_t* pids, int64_t pids_capacity, int32_t num_groups,
+                             const int32_t* group_begin,
+                             const int32_t* group_comm_size, const int32_t* group_rank_to_global,
+                             int32_t* owner, int32_t* counts, void* stream);
+
+/* Host check of a bucket's task table (run once when the bucket layout is
+ * built): sorted and packed from offset 0, numel >= 0 summing to
+ * bucket_numel, param in [0, num_params), comm in [0, num_comms); comms[0] is
+ * {W, 1} and every comm's size divides W with stride 1 or W/size.
+ * tasks and comms are host arrays.  Returns DC_ERR_TASKS with a message
+ * naming the first broken entry. */
+dc_status dc_validate_tasks(int32_t W, const dc_task* tasks, int32_t num_tasks,
+                            int64_t bucket_numel, int32_t num_params, const dc_comm* comms,
+                            int32_t num_comms);
+
+/* a3-a6. Bucket flush ([DS] problem statement and "Describe the solution").
+ * For every task t, column j of the bucket inside t, and block of the task's
+ * communicator (c members m_0 < ... < m_{c-1}):
+ *   v_k = pre_div ? round_dtype(fp32(x[m_k][j]) / c) : x[m_k][j]
+ *   y   = round_dtype(((v_0 + v_1) + ...) + v_{c-1})      (fp32)
+ * A task on comm 0 whose param has owner o >= 0 writes y to row o only (the
+ * reduce-to-owner branch: same sum, same operand order, one destination);
+ * every other task writes y to every member of the block (AllReduce).
+ * owner == NULL is the empty map: every task AllReduces, bit for bit the path
+ * without owners ([DS] Design points, "No native flag").  Elements the flush
+ * does not write keep their contents.
+ *   slab_in, ld_in     device [W, ld_in] gradients (bf16 or fp32 per dtype)
+ *   slab_out, ld_out   device [W, ld_out] results; may equal slab_in (same
+ *                      ld) for an in-place flush; partial overlap is DC_ERR_ARG
+ *   bucket_col         first slab column of the bucket
+ *   bucket_numel       columns of the bucket; bucket_col + bucket_numel must
+ *                      not exceed ld_in or ld_out
+ *   tasks, num_tasks   device dc_task[num_tasks] (see dc_validate_tasks)
+ *   owner, num_params  device int32[num_params] from dc_build_owner_map, or NULL
+ *   comms, num_comms   host dc_comm[num_comms], 1 <= num_comms <= DC_MAX_COMMS
+ *   pre_div            0 or 1
+ * The task table is read on the device and is not checked here (validate it
+ * once with dc_validate_tasks).  A table that breaks the contract still
+ * never makes the kernel touch memory outside the bucket's columns of the
+ * two slabs: an out-of-range param or owner entry means AllReduce, an
+ * out-of-range comm means comm 0, and columns no task covers are not
+ * written. */
+dc_status dc_flush_bucket(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                          void* slab_out, int64_t ld_out, int64_t bucket_col,
+                          int64_t bucket_numel, const dc_task* tasks, int32_t num_tasks,
+                          const int32_t* owner, int32_t num_params, const dc_comm* comms,
+                          int32_t num_comms, int32_t pre_div, void* stream);
+
+/* a7. Probe counts of one flush ([DS] "reduce_probe"), on the host from
+ * metadata only (no device access, no synchronization).  tasks, owner (or
+ * NULL for the empty map), pid_offsets/pids (the CSR of dc_partition_ids)
+ * and comms are host arrays.  Holders of a param on a sub-communicator are,
+ * in every block, the members whose in-block index is in its list. */
+dc_status dc_probe_flush(int32_t W, int32_t dtype, const dc_task* tasks, int32_t num_tasks,
+                         const int32_t* owner, int32_t num_params, const int32_t* pid_offsets,
+                         const int32_t* pids, const dc_comm* comms, int32_t num_comms,
+                         int32_t pre_div, dc_probe* out);
+
+/* a8. ReduceScatter ([AG] duality with ReduceScatter: M elements in per node,
+ * M/N out, a reduction plus a split).  With L = M / W:
+ *   out[s][k] = round_dtype(fold over r of pre(in[r][s*L + k]))   k < L
+ * using the flush's fold and pre-division (by W).
+ *   in, ld_in     device [W, ld_in], ld_in >= M
+ *   out, ld_out   device [W, ld_out], ld_out >= L; must not overlap `in`
+ * M % W != 0 is DC_ERR_SHAPE (pad with zeros to a multiple of W). */
+dc_status dc_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                            int64_t ld_out, int64_t M, int32_t pre_div, void* stream);
+
+/* a9. AllGather ([AG] semantic definition and Ring AllGather).  Shard s is
+ * row s of `in` (L = shard_numel columns).
+ *   DC_ORDER_RANK: out[i][s*L + k] = in[s][k] - every node ends with
+ *                  [A_0, ..., A_{W-1}].
+ *   DC_ORDER_RING: out[i][p*L + k] = in[(i - p) mod W][k] - position p of
+ *                  node i holds the chunk a ring all-gather delivers at step
+ *                  p (own chunk first, then one chunk per step from the left
+ *                  neighbour).
+ * step = -1 writes every position; step = s in [0, W) writes chunk s (rank
+ * order) or position s (ring order) only, so a ring can be replayed step by
+ * step.
+ *   in, ld_in     device [W, ld_in], ld_in >= L
+ *   out, ld_out   device [W, ld_out], ld_out >= W*L; must not overlap `in` */
+dc_status dc_all_gather(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                        int64_t ld_out, int64_t shard_numel, int32_t order, int32_t step,
+                        void* stream);
+
+/* a10. Replica-local accumulation ([MT] What: unreduced per-replica partial
+ * sums accumulate locally across micro-batches).  fp32 only:
+ *   acc[r][j] = acc[r][j] + x[r][j]        r < rows, j < M
+ * and with init = 1 the accumulator starts from zero: acc = +0.0f + x.
+ *   x, ld_x       device [rows, ld_x] fp32
+ *   acc, ld_acc   device [rows, ld_acc] fp32, updated in place; may equal x */
+dc_status dc_accumulate(int32_t rows, const float* x, int64_t ld_x, float* acc, int64_t ld_acc,
+                        int64_t M, int32_t init, void* stream);
+
+/* a11. Deferred cross-replica reduce ([MT] What: the single all-reduce that
+ * update() emits).  fp32 only:
+ *   out[i][j] = fold over r = 0..W-1 of acc[r][j]        i < out_rows, j < M
+ * out_rows is 1 (one reduced copy) or W (every replica gets the sum).  With
+ * out_rows = 1 and W rows of one micro-batch this is also the
+ * per-micro-batch reduce of the status quo.
+ *   acc, ld_acc   device [W, ld_acc] fp32
+ *   out, ld_out   device [out_rows, ld_out] fp32; may equal acc (same ld) */
+dc_status dc_deferred_reduce(int32_t W, const float* acc, int64_t ld_acc, float* out,
+                             int64_t ld_out, int64_t M, int32_t out_rows, void* stream);
+
+/* fp32 -> bf16 with the rounding the flush uses (round to nearest even, NaN
+ * -> 0x7FC0|sign), n elements, device arrays; a self-check of the
+ * conversion on the GPU. */
+dc_status dc_round_bf16(const float* in, uint16_t* out, int64_t n, void* stream);
+
+/* Plain 16-byte streaming copy of `bytes` (a multiple of 16; both pointers
+ * 16-byte aligned, not overlapping): the achievable-bandwidth reference the
+ * measurements compare against. */
+dc_status dc_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DC_H */

@@ -9,7 +9,7 @@ DEV_SO = os.path.join(HERE, "libsynth_dev.so")
 
 def build(verbose: bool = False) -> None:
     cmds = [
-        ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", HOST_SO,
+        ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", HOST_SO,
          os.path.join(HERE, "gen_host.c")],
         ["hipcc", "--offload-arch=gfx950", "-O3", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -69,9 +69,11 @@ void synth_fill_host(int dtype, uint64_t seed, uint64_t stream, uint32_t C, uint
   uint64_t key = synth_key(seed, stream);
   if (dtype == 0) {
     uint16_t* o = (uint16_t*)out;
+#pragma omp parallel for schedule(static) if (n > 65536)
     for (int64_t k = 0; k < n; ++k) o[k] = (uint16_t)synth_bits(key, (uint64_t)(col0 + k), C, E, 1);
   } else {
     uint32_t* o = (uint32_t*)out;
+#pragma omp parallel for schedule(static) if (n > 65536)
     for (int64_t k = 0; k < n; ++k) o[k] = synth_bits(key, (uint64_t)(col0 + k), C, E, 0);
   }
 }

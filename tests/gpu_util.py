@@ -1,0 +1,141 @@
+"""Helpers for the GPU parity tests: device slabs, the oracle side of a
+workload, and sampled checks of full-size runs.
+
+Inputs on both sides come from synth (device generator for the GPU slab,
+host generator for the oracle), never from the GPU path's outputs.
+"""
+import sys
+
+import numpy as np
+
+import oracle
+import synth
+from synth import workloads as wl
+
+SENTINEL16 = 0x7E7E
+SENTINEL32 = 0x7E7E7E7E
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def empty_slab(dtype, rows, ld, sentinel=True):
+    t = torch()
+    if dtype == wl.DT_BF16:
+        x = t.empty((rows, ld), dtype=t.int16, device="cuda")
+        if sentinel:
+            x.fill_(SENTINEL16)
+    else:
+        x = t.empty((rows, ld), dtype=t.int32, device="cuda")
+        if sentinel:
+            x.fill_(SENTINEL32)
+    return x
+
+
+def gen_slab(dtype, rows, ld, ncols, seed, stream0, scale):
+    """Device slab filled by the device generator (columns >= ncols hold the
+    sentinel)."""
+    t = torch()
+    x = empty_slab(dtype, rows, ld)
+    synth.fill_slab_device(dtype, seed, stream0, scale, rows, ld, ncols, x.data_ptr(),
+                           t.cuda.current_stream().cuda_stream)
+    return x
+
+
+def host_slab(dtype, rows, ld, ncols, seed, stream0, scale):
+    x = np.zeros((rows, ld), synth.np_dtype(dtype))
+    x[:] = SENTINEL16 if dtype == wl.DT_BF16 else SENTINEL32
+    for r in range(rows):
+        x[r, :ncols] = synth.fill_row(dtype, seed, stream0 + r, scale, 0, ncols)
+    if dtype == wl.DT_F32:
+        return x.view(np.float32)
+    return x
+
+
+def to_host(x, dtype):
+    a = x.cpu().numpy()
+    return a.view(np.uint16) if dtype == wl.DT_BF16 else a.view(np.float32)
+
+
+def bits(a, dtype):
+    return a.view(np.uint16) if dtype == wl.DT_BF16 else a.view(np.uint32)
+
+
+def oracle_owner(w):
+    """Partition CSR and owner map of a flush workload, on the oracle."""
+    flat, ps, off, pids = oracle.partition_ids(w.numel, w.group_begin, w.group_parts())
+    comm_sizes = [w.comms[c].size for c in w.group_comm]
+    elig = oracle.group_eligible(w.W, comm_sizes, w.group_rank_to_global())
+    owner, counts = oracle.owner_map(off, pids, w.group_begin, elig)
+    return flat, ps, off, pids, owner, counts
+
+
+def oracle_flush_bucket(w, b, slab_in, slab_out, owner):
+    bk = w.buckets[b]
+    t_off = [t.offset for t in bk.tasks]
+    t_numel = [t.numel for t in bk.tasks]
+    t_param = [t.param for t in bk.tasks]
+    t_comm = [t.comm for t in bk.tasks]
+    oracle.flush(w.W, w.dtype, slab_in, slab_out, bk.col, t_off, t_numel, t_param, t_comm, owner,
+                 [c.size for c in w.comms], [c.stride for c in w.comms], w.pre_div)
+
+
+def sample_columns(w, per_bucket=64, seed=0):
+    """Columns to check in a full-size flush: both ends of every task in a
+    sample of tasks, the bucket edges, and random interior columns."""
+    rng = np.random.default_rng(seed)
+    cols = set()
+    for bk in w.buckets:
+        cols.update([bk.col, bk.col + bk.numel - 1])
+        idx = rng.choice(len(bk.tasks), size=min(per_bucket, len(bk.tasks)), replace=False)
+        for k in idx:
+            t = bk.tasks[k]
+            if t.numel == 0:
+                continue
+            a = bk.col + t.offset
+            cols.update([a, a + t.numel - 1, a + int(rng.integers(0, t.numel))])
+        cols.update((bk.col + rng.integers(0, bk.numel, per_bucket)).tolist())
+    return np.array(sorted(c for c in cols if 0 <= c < w.total), np.int64)
+
+
+def oracle_sampled_flush(w, cols, owner):
+    """Oracle outputs [W, len(cols)] of the flush at the given slab columns,
+    from host-generated inputs of just those columns (each column becomes a
+    one-column task of its parameter)."""
+    W = w.W
+    n = len(cols)
+    scale = w.scale
+    rows = np.stack([synth.gather(w.dtype, w.value_seed, r, scale, cols) for r in range(W)])
+    if w.dtype == wl.DT_F32:
+        rows = rows.view(np.float32)
+    ld = max(8, -(-n // 8) * 8)
+    slab = np.zeros((W, ld), rows.dtype)
+    slab[:, :n] = rows
+    out = np.zeros_like(slab)
+    if w.dtype == wl.DT_BF16:
+        out[:] = SENTINEL16
+    else:
+        out.view(np.uint32)[:] = SENTINEL32
+    # map every column to its task
+    t_param, t_comm = [], []
+    starts = [bk.col for bk in w.buckets]
+    for c in cols:
+        b = int(np.searchsorted(starts, c, side="right")) - 1
+        bk = w.buckets[b]
+        rel = c - bk.col
+        offs = [t.offset for t in bk.tasks]
+        k = int(np.searchsorted(offs, rel, side="right")) - 1
+        while bk.tasks[k].numel == 0 or not (bk.tasks[k].offset <= rel < bk.tasks[k].offset + bk.tasks[k].numel):
+            k -= 1
+        t_param.append(bk.tasks[k].param)
+        t_comm.append(bk.tasks[k].comm)
+    oracle.flush(W, w.dtype, slab, out, 0, np.arange(n), np.ones(n), t_param, t_comm, owner,
+                 [c.size for c in w.comms], [c.stride for c in w.comms], w.pre_div)
+    return out[:, :n]

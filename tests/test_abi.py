@@ -1,0 +1,142 @@
+"""The C ABI on the host (no GPU): every symbol of include/dc.h is exported,
+every argument check returns its documented code before any device work, and
+the host-only probe and task check agree with the oracle."""
+import ctypes
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from gradient_reduction_amd import dc
+from synth import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "dc.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dc_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert "dc_flush_bucket" in names and len(names) >= 14
+    lib = ctypes.CDLL(dc.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(names) == set(dc._SIGS), "binding and header disagree"
+
+
+def test_task_record_layout():
+    assert dc.TASK_DTYPE.itemsize == 32 and dc.COMM_DTYPE.itemsize == 8
+    assert ctypes.sizeof(dc.dc_probe) == 4 * 4 + 2 * 8 + 3 * 64 * 8
+
+
+def expect(code, fn, *args, **kw):
+    with pytest.raises(dc.DCError) as e:
+        fn(*args, **kw)
+    assert e.value.code == code, str(e.value)
+    assert dc.dc_last_error() != ""
+
+
+FAKE = 1 << 40          # an aligned address nothing dereferences: every call below fails its checks first
+TASK_PTR = FAKE + 4096
+
+
+def test_flush_argument_checks():
+    f = dc.dc_flush_bucket
+    ok = dict(W=8, dtype=0, slab_in=FAKE, ld_in=64, slab_out=FAKE, ld_out=64, bucket_col=0,
+              bucket_numel=64, tasks=TASK_PTR, num_tasks=1, owner=None, num_params=1,
+              comms=[(8, 1)], num_comms=1, pre_div=1, stream=0)
+
+    def call(**ch):
+        a = dict(ok)
+        a.update(ch)
+        return f(**a)
+
+    expect(dc.DC_ERR_ARG, call, W=0)
+    expect(dc.DC_ERR_ARG, call, W=65)
+    expect(dc.DC_ERR_DTYPE, call, dtype=2)
+    expect(dc.DC_ERR_NULL, call, slab_in=None)
+    expect(dc.DC_ERR_NULL, call, slab_out=None)
+    expect(dc.DC_ERR_NULL, call, tasks=None)
+    expect(dc.DC_ERR_ALIGN, call, slab_in=FAKE + 2, slab_out=FAKE + 4098)
+    expect(dc.DC_ERR_ALIGN, call, ld_in=60, ld_out=60, bucket_numel=60)
+    expect(dc.DC_ERR_SHAPE, call, bucket_col=10)
+    expect(dc.DC_ERR_ARG, call, bucket_numel=-1)
+    expect(dc.DC_ERR_ARG, call, pre_div=2)
+    expect(dc.DC_ERR_ARG, call, comms=[(4, 1)])
+    expect(dc.DC_ERR_ARG, call, comms=[(8, 1), (3, 1)], num_comms=2)
+    expect(dc.DC_ERR_ARG, call, comms=[(8, 1), (4, 3)], num_comms=2)
+    expect(dc.DC_ERR_ARG, call, comms=[(8, 1)] * 9, num_comms=9)
+    expect(dc.DC_ERR_ARG, call, ld_out=128)                        # in place with different ld
+    expect(dc.DC_ERR_ARG, call, slab_out=FAKE + 64)                # partial overlap
+
+
+def test_other_argument_checks():
+    expect(dc.DC_ERR_SHAPE, dc.dc_reduce_scatter, 8, 0, FAKE, 64, FAKE << 1, 64, 60, 0, stream=0)
+    expect(dc.DC_ERR_ARG, dc.dc_reduce_scatter, 8, 0, FAKE, 64, FAKE + 64, 64, 64, 0, stream=0)
+    expect(dc.DC_ERR_SHAPE, dc.dc_reduce_scatter, 8, 0, FAKE, 64, FAKE << 1, 0, 64, 0, stream=0)
+    expect(dc.DC_ERR_ARG, dc.dc_all_gather, 4, 1, FAKE, 64, FAKE << 1, 256, 64, 2, -1, stream=0)
+    expect(dc.DC_ERR_ARG, dc.dc_all_gather, 4, 1, FAKE, 64, FAKE << 1, 256, 64, 0, 4, stream=0)
+    expect(dc.DC_ERR_SHAPE, dc.dc_all_gather, 4, 1, FAKE, 64, FAKE << 1, 200, 64, 0, -1, stream=0)
+    expect(dc.DC_ERR_ARG, dc.dc_accumulate, 0, FAKE, 64, FAKE << 1, 64, 64, 0, stream=0)
+    expect(dc.DC_ERR_ARG, dc.dc_accumulate, 2, FAKE, 64, FAKE, 128, 64, 0, stream=0)
+    expect(dc.DC_ERR_ALIGN, dc.dc_accumulate, 2, FAKE, 66, FAKE << 1, 64, 64, 0, stream=0)
+    expect(dc.DC_ERR_ARG, dc.dc_deferred_reduce, 4, FAKE, 64, FAKE << 1, 64, 64, 2, stream=0)
+    expect(dc.DC_ERR_ARG, dc.dc_deferred_reduce, 4, FAKE, 64, FAKE + 128, 64, 64, 1, stream=0)
+    expect(dc.DC_ERR_SHAPE, dc.dc_stream_copy, FAKE, FAKE << 1, 100, stream=0)
+    expect(dc.DC_ERR_ARG, dc.dc_stream_copy, FAKE, FAKE + 16, 64, stream=0)
+    expect(dc.DC_ERR_SHAPE, dc.dc_partition_ids, 4, 3, FAKE, 1, [0, 2], [4], FAKE, FAKE, FAKE,
+           FAKE, 10, stream=0)
+    expect(dc.DC_ERR_SHAPE, dc.dc_partition_ids, 4, 3, FAKE, 1, [0, 3], [4], FAKE, FAKE, FAKE,
+           FAKE, 5, stream=0)
+    expect(dc.DC_ERR_ARG, dc.dc_partition_ids, 4, 3, FAKE, 1, [0, 3], [0], FAKE, FAKE, FAKE,
+           FAKE, 10, stream=0)
+    expect(dc.DC_ERR_ARG, dc.dc_build_owner_map, 4, 3, FAKE, FAKE, 10, 0, [0], [4], [0, 1, 2, 3],
+           FAKE, FAKE, stream=0)
+
+
+def test_validate_tasks():
+    comms = [(8, 1), (4, 1)]
+    good = dc.tasks_array([(0, 5, 0, 0), (5, 0, 1, 1), (5, 7, 2, 1)])
+    dc.dc_validate_tasks(8, good, 3, 12, 3, comms, 2)
+    for bad, n in ((dc.tasks_array([(1, 5, 0, 0)]), 6), (dc.tasks_array([(0, 5, 0, 0), (4, 1, 1, 0)]), 6),
+                   (dc.tasks_array([(0, 5, 3, 0)]), 5), (dc.tasks_array([(0, 5, 0, 2)]), 5),
+                   (dc.tasks_array([(0, -1, 0, 0)]), -1), (dc.tasks_array([(0, 5, 0, 0)]), 6)):
+        expect(dc.DC_ERR_TASKS, dc.dc_validate_tasks, 8, bad, len(bad), n, 3, comms, 2)
+
+
+def test_probe_matches_oracle_on_workloads():
+    """dc_probe_flush is host code: compare it with the oracle's probe on the
+    synthetic workloads and random ones (owner path on and off)."""
+    ws = [wl.tiny_flush(), wl.owner_flush_w8(), wl.mixed_flush_w16()]
+    rng = random.Random(3)
+    for k in range(5):
+        W = rng.choice([2, 4, 8, 16])
+        sizes = [rng.randint(0, 500) for _ in range(200)]
+        ws.append(wl.custom_flush(f"r{k}", W, 0, sizes, group_begin=[0, 120, 200],
+                                  group_comm=[0, 1], comms=[wl.Comm(W, 1), wl.Comm(W // 2, 2)],
+                                  capacity=3000))
+    for w in ws:
+        flat, ps, off, pids = oracle.partition_ids(w.numel, w.group_begin, w.group_parts())
+        comm_sizes = [w.comms[c].size for c in w.group_comm]
+        elig = oracle.group_eligible(w.W, comm_sizes, w.group_rank_to_global())
+        owner, _ = oracle.owner_map(off, pids, w.group_begin, elig)
+        comms = [(c.size, c.stride) for c in w.comms]
+        for own in (None, owner):
+            for bk in w.buckets:
+                t = dc.tasks_array([(x.offset, x.numel, x.param, x.comm) for x in bk.tasks])
+                pr = dc.dc_probe_flush(w.W, w.dtype, t, len(t), own, w.P, off, pids, comms,
+                                       len(comms), w.pre_div)
+                want = oracle.probe(w.W, t["numel"], t["param"], t["comm"], own, off, pids,
+                                    [c[0] for c in comms], [c[1] for c in comms])
+                assert pr.reduced_elems == want["reduced_elems"]
+                assert (pr.owner_tasks, pr.owner_elems) == (want["owner_tasks"], want["owner_elems"])
+                assert list(pr.kept)[:w.W] == list(want["kept"])
+                assert list(pr.written)[:w.W] == list(want["written"])
+                assert list(pr.discarded)[:w.W] == list(want["discarded"])

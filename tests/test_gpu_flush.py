@@ -1,0 +1,312 @@
+"""GPU parity: generator, bf16 rounding, partition lists / owner map and the
+bucket flush, all through the C ABI, against the CPU oracle.
+
+Bit-exact everywhere (integer metadata and fixed-order sums).
+"""
+import random
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gradient_reduction_amd import dc, executor
+from synth import workloads as wl
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dc.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def test_generator_device_matches_host():
+    for dtype, n in ((wl.DT_BF16, 100_003), (wl.DT_F32, 77_777)):
+        scale = wl.sigma_scale(1e-3)
+        U.say("generator", dtype, n)
+        d = U.to_host(U.gen_slab(dtype, 3, wl.round_up(n, 64), n, 9, 5, scale), dtype)
+        h = U.host_slab(dtype, 3, wl.round_up(n, 64), n, 9, 5, scale)
+        assert np.array_equal(U.bits(d, dtype), U.bits(h, dtype))
+
+
+def test_round_bf16_matches_oracle():
+    import torch
+    rng = np.random.default_rng(3)
+    highs = np.arange(65536, dtype=np.uint64)
+    lows = np.concatenate([[0, 1, 2, 0x7FFF, 0x8000, 0x8001, 0xFFFE, 0xFFFF],
+                           rng.integers(0, 65536, 24)]).astype(np.uint64)
+    u = ((highs[:, None] << 16) | lows[None, :]).ravel().astype(np.uint32)
+    U.say("round_bf16", len(u))
+    x = torch.from_numpy(u.view(np.int32).copy()).cuda()
+    y = torch.empty(len(u), dtype=torch.int16, device="cuda")
+    dc.dc_round_bf16(x, y, len(u))
+    got = y.cpu().numpy().view(np.uint16)
+    want = oracle.bf16_round(u.view(np.float32))
+    bad = np.nonzero(got != want)[0]
+    assert len(bad) == 0, f"{len(bad)} mismatches, e.g. {u[bad[:4]]}: {got[bad[:4]]} vs {want[bad[:4]]}"
+
+
+def run_owner_map(w):
+    import torch
+    ex = executor.from_workload(w, reduce_to_owner=True)
+    ex.build_owner_map()
+    ex.fetch_metadata()
+    torch.cuda.synchronize()
+    return ex, torch.cuda.current_stream()
+
+
+def owner_workloads():
+    out = [wl.tiny_flush(), wl.owner_flush_w8(), wl.mixed_flush_w16()]
+    rng = random.Random(5)
+    for k in range(6):
+        G = rng.randint(1, 4)
+        numel, gb, gcomm = [], [0], []
+        W = rng.choice([2, 4, 8, 16])
+        comms = [wl.Comm(W, 1), wl.Comm(max(1, W // 2), 1), wl.Comm(max(1, W // 2), 2)]
+        for g in range(G):
+            numel += [rng.choice([0, 1, 3, 7, 64, 1000, 5000]) for _ in range(rng.randint(1, 3000))]
+            gb.append(len(numel))
+            gcomm.append(rng.choice([0, 0, 1, 2]))
+        out.append(wl.custom_flush(f"rand{k}", W, wl.DT_BF16, numel, group_begin=gb,
+                                   group_comm=gcomm, comms=comms, capacity=10 ** 9))
+    return out
+
+
+@pytest.mark.parametrize("w", owner_workloads(), ids=lambda w: f"{w.name}-P{w.P}")
+def test_partition_ids_and_owner_map(w):
+    U.say("owner map", w.name, w.P)
+    ex, _ = run_owner_map(w)
+    flat, ps, off, pids, owner, counts = U.oracle_owner(w)
+    assert np.array_equal(ex.d_flat[:w.P].cpu().numpy(), flat)
+    assert np.array_equal(ex.d_part_size.cpu().numpy(), ps)
+    assert np.array_equal(ex.h_pid_off, off)
+    assert np.array_equal(ex.h_pids, pids)
+    assert np.array_equal(ex.h_owner, owner)
+    assert np.array_equal(ex.h_counts, counts)
+
+
+def flush_case(w, reduce_to_owner, in_place=False, probe=True):
+    """Run every bucket of w on the GPU and on the oracle; compare all of the
+    output slab bit for bit, and the probe records."""
+    import torch
+    U.say("flush", w.name, "owner" if reduce_to_owner else "allreduce", "in-place" if in_place else "")
+    scale = w.scale
+    ld = w.ld
+    x = U.gen_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, scale)
+    y = x if in_place else U.empty_slab(w.dtype, w.W, ld)
+    ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner)
+    ex.build_owner_map()
+    for b in range(len(w.buckets)):
+        ex.flush(b, x, ld, y, ld)
+    torch.cuda.synchronize()
+    got = U.to_host(y, w.dtype)
+    hin = U.host_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, scale)
+    hout = hin if in_place else np.zeros_like(hin)
+    if not in_place:
+        U.bits(hout, w.dtype)[:] = U.SENTINEL16 if w.dtype == wl.DT_BF16 else U.SENTINEL32
+    _, _, off, pids, owner, _ = U.oracle_owner(w)
+    for b in range(len(w.buckets)):
+        U.oracle_flush_bucket(w, b, hin, hout, owner if reduce_to_owner else None)
+    gb, hb = U.bits(got, w.dtype), U.bits(hout, w.dtype)
+    bad = np.argwhere(gb != hb)
+    assert len(bad) == 0, (f"{len(bad)} mismatches; first (row, col): {bad[:5].tolist()} "
+                           f"gpu {gb[tuple(bad[0])]:#x} oracle {hb[tuple(bad[0])]:#x}")
+    if probe:
+        ex.fetch_metadata()
+        for b, bk in enumerate(w.buckets):
+            pr = ex.probe(b)
+            want = oracle.probe(w.W, [t.numel for t in bk.tasks], [t.param for t in bk.tasks],
+                                [t.comm for t in bk.tasks], owner if reduce_to_owner else None,
+                                off, pids, [c.size for c in w.comms], [c.stride for c in w.comms])
+            assert (pr.tasks, pr.owner_tasks, pr.reduced_elems, pr.owner_elems) == (
+                want["tasks"], want["owner_tasks"], want["reduced_elems"], want["owner_elems"])
+            assert list(pr.written)[:w.W] == list(want["written"])
+            assert list(pr.kept)[:w.W] == list(want["kept"])
+            assert list(pr.discarded)[:w.W] == list(want["discarded"])
+
+
+@pytest.mark.parametrize("owner", [False, True], ids=["allreduce", "owner"])
+def test_flush_tiny_workload(owner):
+    flush_case(wl.tiny_flush(), owner)
+
+
+def small_flush_workloads():
+    """Edge cases at sizes the oracle finishes in seconds: every W the fast
+    kernels specialise and several they do not, both dtypes, pre-division on
+    and off, sub-communicators with both strides, tiny and empty tasks (task
+    edges inside 16-byte vectors), more tasks per tile than the LDS stage,
+    more tasks than one search round, and a bucket that starts mid-vector."""
+    rng = random.Random(17)
+    out = []
+    for W in (1, 2, 3, 4, 5, 7, 8, 16):
+        for dtype in (wl.DT_BF16, wl.DT_F32):
+            sizes = [rng.choice([0, 1, 2, 3, 5, 7, 9, 15, 16, 17, 100, 1000, 4096, 20_000])
+                     for _ in range(60)]
+            divs = [c for c in range(1, W + 1) if W % c == 0 and c < W]
+            comms = [wl.Comm(W, 1)]
+            gcomm = [0, 0]
+            if divs:
+                c = rng.choice(divs)
+                comms.append(wl.Comm(c, 1))
+                comms.append(wl.Comm(c, W // c))
+                gcomm = [0, rng.choice([1, 2])]
+            gb = [0, 40, 60]
+            out.append(wl.custom_flush(f"W{W}-{wl.DTYPE_NAME[dtype]}", W, dtype, sizes,
+                                       group_begin=gb, group_comm=gcomm, comms=comms,
+                                       capacity=30_000, pre_div=(W + dtype) % 2,
+                                       value_seed=W * 10 + dtype))
+    # many tiny tasks: > 256 tasks in one tile, and > 256 tasks in the table
+    tiny = [rng.randint(0, 5) for _ in range(70_000)]
+    out.append(wl.custom_flush("W8-bf16-70k-tiny", 8, wl.DT_BF16, tiny, capacity=10 ** 9,
+                               pre_div=1, value_seed=91))
+    out.append(wl.custom_flush("W16-f32-5k-tiny", 16, wl.DT_F32, tiny[:5000],
+                               capacity=10 ** 9, pre_div=0, value_seed=92))
+    return out
+
+
+@pytest.mark.parametrize("w", small_flush_workloads(), ids=lambda w: w.name)
+@pytest.mark.parametrize("owner", [False, True], ids=["allreduce", "owner"])
+def test_flush_small(w, owner):
+    flush_case(w, owner)
+
+
+@pytest.mark.parametrize("w", small_flush_workloads()[::5], ids=lambda w: w.name)
+def test_flush_in_place(w):
+    flush_case(w, True, in_place=True, probe=False)
+
+
+def test_flush_unaligned_bucket_start():
+    """A bucket whose first column is not on a 16-byte vector: columns before
+    it stay untouched."""
+    import torch
+    W, dtype = 8, wl.DT_BF16
+    sizes = [5, 3000, 1, 2, 999]
+    w = wl.custom_flush("unaligned", W, dtype, sizes, capacity=10 ** 9, pre_div=1)
+    col0 = 3
+    ld = wl.round_up(col0 + w.total, 64)
+    scale = w.scale
+    x = U.gen_slab(dtype, W, ld, ld, w.value_seed, 0, scale)
+    y = U.empty_slab(dtype, W, ld)
+    bk = w.buckets[0]
+    tasks = dc.tasks_array([(t.offset, t.numel, t.param, t.comm) for t in bk.tasks])
+    d_tasks = torch.from_numpy(tasks.view(np.uint8).copy()).cuda()
+    _, _, off, pids, owner, _ = U.oracle_owner(w)
+    d_owner = torch.from_numpy(owner).cuda()
+    dc.dc_flush_bucket(W, dtype, x, ld, y, ld, col0, bk.numel, d_tasks, len(tasks), d_owner,
+                       w.P, [(W, 1)], 1, 1)
+    torch.cuda.synchronize()
+    hin = U.host_slab(dtype, W, ld, ld, w.value_seed, 0, scale)
+    hout = np.full_like(hin, U.SENTINEL16)
+    oracle.flush(W, dtype, hin, hout, col0, [t.offset for t in bk.tasks], [t.numel for t in bk.tasks],
+                 [t.param for t in bk.tasks], [t.comm for t in bk.tasks], owner, [W], [1], 1)
+    assert np.array_equal(U.to_host(y, dtype), hout)
+
+
+def test_flush_empty_bucket_and_no_tasks():
+    import torch
+    W, dtype, ld = 4, wl.DT_F32, 64
+    x = U.gen_slab(dtype, W, ld, ld, 1, 0, wl.sigma_scale(1e-3))
+    y = U.empty_slab(dtype, W, ld)
+    d_tasks = torch.zeros(32, dtype=torch.uint8, device="cuda")
+    dc.dc_flush_bucket(W, dtype, x, ld, y, ld, 8, 0, d_tasks, 0, None, 0, [(W, 1)], 1, 0)
+    dc.dc_flush_bucket(W, dtype, x, ld, y, ld, 8, 16, d_tasks, 0, None, 0, [(W, 1)], 1, 0)
+    torch.cuda.synchronize()
+    assert np.all(U.to_host(y, dtype).view(np.uint32) == U.SENTINEL32)
+
+
+def _nan_mask(b, dtype):
+    if dtype == wl.DT_BF16:
+        return ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+    return ((b & 0x7F800000) == 0x7F800000) & ((b & 0x7FFFFF) != 0)
+
+
+def test_flush_nonfinite_and_subnormal_inputs():
+    """NaN, infinities, subnormals and signed zeros.  A NaN result must be a
+    NaN on both sides (its sign and payload are not part of the result: x86
+    and gfx950 pick different default NaNs); every other element is
+    bit-exact."""
+    import torch
+    rng = random.Random(8)
+    for W, dtype, pre in ((4, wl.DT_BF16, 1), (8, wl.DT_BF16, 0), (3, wl.DT_BF16, 1),
+                          (4, wl.DT_F32, 1), (5, wl.DT_F32, 1)):
+        n = 4000
+        ld = wl.round_up(n, 64)
+        if dtype == wl.DT_BF16:
+            pool = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F80, 0xFF80, 0x7FC0,
+                    0x7F7F, 0xFF7F, 0x3F80, 0x4B80, 0xCB80]
+            h = np.array([[rng.choice(pool) if rng.random() < 0.5 else rng.getrandbits(16)
+                           for _ in range(ld)] for _ in range(W)], np.uint16)
+            d = torch.from_numpy(h.view(np.int16).copy()).cuda()
+        else:
+            pool = [0, 0x80000000, 1, 0x80000001, 0x007FFFFF, 0x00800000, 0x7F800000, 0xFF800000,
+                    0x7FC00000, 0x7F7FFFFF, 0x3F800000]
+            h = np.array([[rng.choice(pool) if rng.random() < 0.5 else rng.getrandbits(32)
+                           for _ in range(ld)] for _ in range(W)], np.uint32)
+            d = torch.from_numpy(h.view(np.int32).copy()).cuda()
+            h = h.view(np.float32)
+        sizes = [1, 2, 3, 1000, 5, 2989]
+        w = wl.custom_flush("nonfinite", W, dtype, sizes, capacity=10 ** 9, pre_div=pre)
+        bk = w.buckets[0]
+        tasks = dc.tasks_array([(t.offset, t.numel, t.param, t.comm) for t in bk.tasks])
+        d_tasks = torch.from_numpy(tasks.view(np.uint8).copy()).cuda()
+        y = U.empty_slab(dtype, W, ld)
+        dc.dc_flush_bucket(W, dtype, d, ld, y, ld, 0, bk.numel, d_tasks, len(tasks), None, w.P,
+                           [(W, 1)], 1, pre)
+        torch.cuda.synchronize()
+        hout = np.zeros_like(h)
+        U.bits(hout, dtype)[:] = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
+        oracle.flush(W, dtype, h, hout, 0, [t.offset for t in bk.tasks], [t.numel for t in bk.tasks],
+                     [t.param for t in bk.tasks], [t.comm for t in bk.tasks], None, [W], [1], pre)
+        got = U.bits(U.to_host(y, dtype), dtype)
+        want = U.bits(hout, dtype)
+        gn, wn = _nan_mask(got, dtype), _nan_mask(want, dtype)
+        assert np.array_equal(gn, wn), (W, dtype, pre, "NaN positions differ")
+        bad = np.argwhere((got != want) & ~wn)
+        assert len(bad) == 0, (W, dtype, pre, bad[:4].tolist(), got[tuple(bad[0])], want[tuple(bad[0])])
+
+
+def full_size_flush(w, reduce_to_owner, in_place):
+    import torch
+    U.say("full-size flush", w.name, "owner" if reduce_to_owner else "allreduce",
+          f"W={w.W} cols={w.total} buckets={len(w.buckets)}")
+    ld = w.ld
+    x = U.gen_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, w.scale)
+    y = x if in_place else U.empty_slab(w.dtype, w.W, ld)
+    ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner)
+    ex.build_owner_map()
+    for b in range(len(w.buckets)):
+        ex.flush(b, x, ld, y, ld)
+    torch.cuda.synchronize()
+    cols = U.sample_columns(w)
+    U.say("  sampled columns", len(cols))
+    got = y[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    got = got.view(np.uint16) if w.dtype == wl.DT_BF16 else got.view(np.uint32)
+    _, _, _, _, owner, _ = U.oracle_owner(w)
+    want = U.oracle_sampled_flush(w, cols, owner if reduce_to_owner else None)
+    if in_place:
+        # rows the flush does not write keep the input
+        inp = np.stack([synth.gather(w.dtype, w.value_seed, r, w.scale, cols) for r in range(w.W)])
+        wb = U.bits(want, w.dtype)
+        sent = U.SENTINEL16 if w.dtype == wl.DT_BF16 else U.SENTINEL32
+        wb = np.where(wb == sent, inp.view(wb.dtype), wb)
+        want = wb
+    want = U.bits(want, w.dtype)
+    bad = np.argwhere(got != want)
+    del x, y
+    torch.cuda.empty_cache()
+    assert len(bad) == 0, f"{len(bad)} mismatches; first {bad[:5].tolist()} cols {cols[bad[:5, 1]]}"
+
+
+@pytest.mark.parametrize("owner", [True, False], ids=["owner", "allreduce"])
+def test_flush_w8_402m_full_size(owner):
+    full_size_flush(wl.owner_flush_w8(), owner, in_place=False)
+
+
+def test_flush_w16_mixed_1_2b_full_size_in_place():
+    full_size_flush(wl.mixed_flush_w16(), True, in_place=True)
