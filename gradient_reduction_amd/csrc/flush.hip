@@ -26,6 +26,26 @@ namespace {
 
 constexpr int kStage = 256;  // tasks staged in LDS per pass over a tile
 
+#ifndef DC_FLUSH_U
+#define DC_FLUSH_U 2      // vectors per thread per tile
+#endif
+#ifndef DC_FLUSH_NT
+#define DC_FLUSH_NT 1     // nontemporal row loads (each input is read once)
+#endif
+#ifndef DC_FLUSH_NTS
+#define DC_FLUSH_NTS 1    // nontemporal result stores
+#endif
+#ifndef DC_FLUSH_PIPE
+#define DC_FLUSH_PIPE 0   // software-pipeline the row loads across a thread's vectors
+#endif
+#ifndef DC_FLUSH_WPE
+#define DC_FLUSH_WPE 0    // minimum waves per SIMD requested from the register allocator
+#endif
+#ifndef DC_FLUSH_XCD
+#define DC_FLUSH_XCD 0    // give each XCD a contiguous run of tiles
+#endif
+constexpr int kXcds = 8;
+
 struct FlushParams {
   const void* in;
   void* out;
@@ -104,6 +124,24 @@ __device__ __forceinline__ int32_t staged_task(const int64_t* off, int32_t cnt, 
   return lo;
 }
 
+// Shape of communicator `comm`, selected with compile-time indices: a
+// run-time index into the kernel-argument arrays would make the compiler
+// copy them to per-lane private memory.
+__device__ __forceinline__ void comm_shape(const FlushParams& p, int32_t comm, int32_t& c,
+                                           int32_t& s, float& inv) {
+  c = p.csize[0];
+  s = p.cstride[0];
+  inv = p.cinv[0];
+#pragma unroll
+  for (int k = 1; k < DC_MAX_COMMS; ++k) {
+    if (comm == k) {
+      c = p.csize[k];
+      s = p.cstride[k];
+      inv = p.cinv[k];
+    }
+  }
+}
+
 __device__ __forceinline__ int32_t member(int32_t b, int32_t i, int32_t c, int32_t s) {
   return (s == 1 ? b * c : b) + i * s;
 }
@@ -151,76 +189,69 @@ __device__ __forceinline__ u32x4 pack_vec(const float* acc) {
   return y;
 }
 
-// W known at compile time and a communicator of C members with stride S
-// (C = W: the data-parallel comm): all W row loads are issued before the
-// fold, each block's members are folded in order, then one store (owner) or
-// one store per member.
-template <bool BF16, int WT, int C, int S, int PRE, bool NT>
-__device__ __forceinline__ void vec_static(const FlushParams& p, int64_t av, int32_t root,
-                                           float inv) {
+// W known at compile time: the W row vectors of column vector `av`.
+template <bool BF16, int WT, bool NT>
+__device__ __forceinline__ void load_rows(const FlushParams& p, int64_t av, u32x4 (&x)[WT]) {
   constexpr int E = BF16 ? 8 : 4;
-  const u32x4* in = reinterpret_cast<const u32x4*>(p.in);
-  u32x4* out = reinterpret_cast<u32x4*>(p.out);
-  const int64_t ldi = p.ld_in / E, ldo = p.ld_out / E;
-  u32x4 x[WT];
+  const u32x4* in = reinterpret_cast<const u32x4*>(p.in) + av;
+  const int64_t ldi = p.ld_in / E;
 #pragma unroll
-  for (int r = 0; r < WT; ++r) x[r] = load16<NT>(in + r * ldi + av);
+  for (int r = 0; r < WT; ++r) x[r] = load16<NT>(in + r * ldi);
+}
+
+// Fold the blocks of a communicator of C members with stride S (C = WT:
+// the data-parallel comm, one block) from the loaded rows, members in
+// order, then store: the owner row when there is one, else every member.
+// The pre-division reciprocal 1/C is a compile-time power of two.
+template <bool BF16, int WT, int C, int S, int PRE>
+__device__ __forceinline__ void fold_store(const FlushParams& p, const u32x4 (&x)[WT], int64_t av,
+                                           int32_t root) {
+  constexpr int E = BF16 ? 8 : 4;
+  constexpr float inv = 1.0f / (float)C;
+  u32x4* out = reinterpret_cast<u32x4*>(p.out) + av;
+  const int64_t ldo = p.ld_out / E;
 #pragma unroll
   for (int b = 0; b < WT / C; ++b) {
+    constexpr int step = S;
     const int base = S == 1 ? b * C : b;
     float acc[E];
 #pragma unroll
-    for (int i = 0; i < C; ++i) fold_vec<BF16, PRE>(acc, x[base + i * S], i == 0, inv, (float)C);
+    for (int i = 0; i < C; ++i) fold_vec<BF16, PRE>(acc, x[base + i * step], i == 0, inv, (float)C);
     const u32x4 y = pack_vec<BF16>(acc);
     if (C == WT && root >= 0) {
-      store16<false>(out + root * ldo + av, y);
+      store16<DC_FLUSH_NTS>(out + root * ldo, y);
     } else {
 #pragma unroll
-      for (int i = 0; i < C; ++i) store16<false>(out + (base + i * S) * ldo + av, y);
+      for (int i = 0; i < C; ++i) store16<DC_FLUSH_NTS>(out + (base + i * step) * ldo, y);
     }
   }
 }
 
-// Pick the compile-time shape of the task's communicator.  Every divisor c
-// of a power-of-two W is a power of two, so pre-division is always an exact
-// reciprocal multiply here.
-template <bool BF16, int WT, int PRE, bool NT, int C>
-__device__ __forceinline__ bool vec_static_try(const FlushParams& p, int64_t av, int32_t root,
-                                               int32_t c, int32_t s, float inv) {
-  if constexpr (C >= 1 && WT % C == 0) {
-    if (c == C) {
-      if (s == 1) vec_static<BF16, WT, C, 1, PRE, NT>(p, av, root, inv);
-      else vec_static<BF16, WT, C, WT / C, PRE, NT>(p, av, root, inv);
-      return true;
+// The fast kernel's two communicator shapes: the data-parallel comm (size
+// WT) or the one sub-communicator shape (C2, S2) the launch was made for.
+template <bool BF16, int WT, int C2, int S2, int PRE>
+__device__ __forceinline__ void fold_store_shape(const FlushParams& p, const u32x4 (&x)[WT],
+                                                 int64_t av, int32_t root, int32_t c) {
+  if constexpr (C2 > 0) {
+    if (c != WT) {
+      fold_store<BF16, WT, C2, S2, PRE>(p, x, av, -1);
+      return;
     }
   }
-  return false;
-}
-
-template <bool BF16, int WT, int PRE, bool NT>
-__device__ __forceinline__ void vec_static_dispatch(const FlushParams& p, int64_t av, int32_t root,
-                                                    int32_t comm) {
-  const int32_t c = p.csize[comm], s = p.cstride[comm];
-  const float inv = p.cinv[comm];
-  if (vec_static_try<BF16, WT, PRE, NT, WT>(p, av, root, c, s, inv)) return;
-  if (vec_static_try<BF16, WT, PRE, NT, WT / 2>(p, av, -1, c, s, inv)) return;
-  if (vec_static_try<BF16, WT, PRE, NT, WT / 4>(p, av, -1, c, s, inv)) return;
-  if (vec_static_try<BF16, WT, PRE, NT, WT / 8>(p, av, -1, c, s, inv)) return;
-  vec_static_try<BF16, WT, PRE, NT, WT / 16>(p, av, -1, c, s, inv);
+  fold_store<BF16, WT, WT, 1, PRE>(p, x, av, root);
 }
 
 // Any W and communicator, sizes known at run time: per block, load-and-fold
 // its members in order, then write the block (or the owner row).
 template <bool BF16, bool NT>
 __device__ __forceinline__ void vec_generic(const FlushParams& p, int64_t av, int32_t root,
-                                            int32_t comm) {
+                                            int32_t c, int32_t s, float inv) {
   constexpr int E = BF16 ? 8 : 4;
   const u32x4* in = reinterpret_cast<const u32x4*>(p.in);
   u32x4* out = reinterpret_cast<u32x4*>(p.out);
   const int64_t ldi = p.ld_in / E, ldo = p.ld_out / E;
-  const int32_t c = p.csize[comm], s = p.cstride[comm];
-  const int mode = !p.pre_div ? kPreNone : (p.cinv[comm] != 0.0f ? kPreMul : kPreDiv);
-  const float inv = p.cinv[comm], cf = (float)c;
+  const int mode = !p.pre_div ? kPreNone : (inv != 0.0f ? kPreMul : kPreDiv);
+  const float cf = (float)c;
   for (int32_t b = 0; b < p.W / c; ++b) {
     float acc[E];
     for (int32_t i = 0; i < c; ++i) {
@@ -243,10 +274,9 @@ __device__ __forceinline__ void vec_generic(const FlushParams& p, int64_t av, in
 // ---------------------------------------------------------------------------
 template <bool BF16>
 __device__ __forceinline__ void elem_flush(const FlushParams& p, int64_t col, int32_t root,
-                                           int32_t comm) {
-  const int32_t c = p.csize[comm], s = p.cstride[comm];
-  const int mode = !p.pre_div ? kPreNone : (p.cinv[comm] != 0.0f ? kPreMul : kPreDiv);
-  const float inv = p.cinv[comm], cf = (float)c;
+                                           int32_t c, int32_t s, float inv) {
+  const int mode = !p.pre_div ? kPreNone : (inv != 0.0f ? kPreMul : kPreDiv);
+  const float cf = (float)c;
   for (int32_t b = 0; b < p.W / c; ++b) {
     float acc = 0.0f;
     for (int32_t i = 0; i < c; ++i) {
@@ -277,16 +307,36 @@ __device__ __forceinline__ void elem_flush(const FlushParams& p, int64_t col, in
   }
 }
 
-template <bool BF16, int WT, int PRE, int U, bool NT>
-__global__ __launch_bounds__(kThreads) void k_flush(FlushParams p) {
+#if DC_FLUSH_WPE
+#define DC_FLUSH_ATTR __attribute__((amdgpu_waves_per_eu(DC_FLUSH_WPE)))
+#else
+#define DC_FLUSH_ATTR
+#endif
+
+// WT > 0: W known at compile time, every communicator of the launch is the
+// data-parallel one or the single shape (C2, S2) (C2 = 0: none).  WT = 0:
+// any W and any communicators, all at run time.
+template <bool BF16, int WT, int C2, int S2, int PRE, int U, bool NT>
+__global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p) {
   static_assert(U <= 32, "slow-vector mask is 32 bits");
   constexpr int E = BF16 ? 8 : 4;
   __shared__ int64_t s_off[kStage];
   __shared__ int64_t s_end[kStage];
   __shared__ int32_t s_root[kStage];
-  __shared__ int32_t s_comm[kStage];
+  __shared__ int32_t s_csz[kStage];
+  __shared__ int32_t s_cst[kStage];
+  __shared__ float s_cinv[kStage];
 
-  const int64_t t0 = (int64_t)blockIdx.x * (kThreads * U);
+  int64_t tile = blockIdx.x;
+  if (DC_FLUSH_XCD) {
+    // workgroups are dealt to the XCDs round-robin; renumber so that XCD x
+    // walks the x-th contiguous run of tiles
+    const int64_t nb = gridDim.x, per = (nb + kXcds - 1) / kXcds;
+    const int64_t x = tile % kXcds, k = tile / kXcds;
+    const int64_t full = nb - (per - 1) * kXcds;  // XCDs that get `per` tiles
+    tile = x < full ? x * per + k : full * per + (x - full) * (per - 1) + k;
+  }
+  const int64_t t0 = tile * (kThreads * U);
   const int64_t t1 = min(t0 + (int64_t)(kThreads * U), p.nv);
   // the tile's columns, relative to the bucket
   const int64_t lo = max((p.v0 + t0) * E, p.c0) - p.c0;
@@ -311,29 +361,73 @@ __global__ __launch_bounds__(kThreads) void k_flush(FlushParams p) {
       s_off[threadIdx.x] = t.offset;
       s_end[threadIdx.x] = t.offset + (t.numel > 0 ? t.numel : 0);
       s_root[threadIdx.x] = root < 0 ? -1 : root;
-      s_comm[threadIdx.x] = comm;
+      int32_t c, st;
+      float inv;
+      comm_shape(p, comm, c, st, inv);
+      s_csz[threadIdx.x] = c;
+      s_cst[threadIdx.x] = st;
+      s_cinv[threadIdx.x] = inv;
     }
     __syncthreads();
     const int64_t clo = max(lo, s_off[0]);
     const int64_t chi = min(hi, s_end[cnt - 1]);
     if (clo >= chi) continue;
 
-    // phase 1: vectors inside one task; phase 2: vectors cut by an edge
+    // phase 1: vectors inside one task; phase 2: vectors cut by an edge.
     uint32_t slow = 0;
+    if constexpr (WT > 0) {
+#if DC_FLUSH_PIPE
+      // software pipelined: the rows of the next vector are requested
+      // before the current one is folded
+      u32x4 cur[WT];
+      int64_t cav = -1;
+      int32_t croot = -1, cc = WT;
+#endif
 #pragma unroll 1
-    for (int u = 0; u < U; ++u) {
-      const int64_t tv = t0 + threadIdx.x + (int64_t)u * kThreads;
-      if (tv >= t1) break;
-      const int64_t av = p.v0 + tv;
-      const int64_t rc = av * E - p.c0;  // the vector's first column, relative
-      const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
-      if (e_lo >= e_hi) continue;
-      const int32_t k = staged_task(s_off, cnt, e_lo);
-      if (e_lo == rc && e_hi == rc + E && s_off[k] <= rc && s_end[k] >= rc + E) {
-        if constexpr (WT > 0) vec_static_dispatch<BF16, WT, PRE, NT>(p, av, s_root[k], s_comm[k]);
-        else vec_generic<BF16, NT>(p, av, s_root[k], s_comm[k]);
-      } else {
-        slow |= 1u << u;
+      for (int u = 0; u < U; ++u) {
+        const int64_t tv = t0 + threadIdx.x + (int64_t)u * kThreads;
+        if (tv >= t1) break;
+        const int64_t av = p.v0 + tv;
+        const int64_t rc = av * E - p.c0;  // the vector's first column, relative
+        const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
+        if (e_lo >= e_hi) continue;
+        const int32_t k = staged_task(s_off, cnt, e_lo);
+        if (e_lo == rc && e_hi == rc + E && s_off[k] <= rc && s_end[k] >= rc + E) {
+#if DC_FLUSH_PIPE
+          u32x4 nxt[WT];
+          load_rows<BF16, WT, NT>(p, av, nxt);
+          if (cav >= 0) fold_store_shape<BF16, WT, C2, S2, PRE>(p, cur, cav, croot, cc);
+#pragma unroll
+          for (int r = 0; r < WT; ++r) cur[r] = nxt[r];
+          cav = av;
+          croot = s_root[k];
+          cc = s_csz[k];
+#else
+          u32x4 x[WT];
+          load_rows<BF16, WT, NT>(p, av, x);
+          fold_store_shape<BF16, WT, C2, S2, PRE>(p, x, av, s_root[k], s_csz[k]);
+#endif
+        } else {
+          slow |= 1u << u;
+        }
+      }
+#if DC_FLUSH_PIPE
+      if (cav >= 0) fold_store_shape<BF16, WT, C2, S2, PRE>(p, cur, cav, croot, cc);
+#endif
+    } else {
+#pragma unroll 1
+      for (int u = 0; u < U; ++u) {
+        const int64_t tv = t0 + threadIdx.x + (int64_t)u * kThreads;
+        if (tv >= t1) break;
+        const int64_t av = p.v0 + tv;
+        const int64_t rc = av * E - p.c0;
+        const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
+        if (e_lo >= e_hi) continue;
+        const int32_t k = staged_task(s_off, cnt, e_lo);
+        if (e_lo == rc && e_hi == rc + E && s_off[k] <= rc && s_end[k] >= rc + E)
+          vec_generic<BF16, NT>(p, av, s_root[k], s_csz[k], s_cst[k], s_cinv[k]);
+        else
+          slow |= 1u << u;
       }
     }
 #pragma unroll 1
@@ -344,41 +438,79 @@ __global__ __launch_bounds__(kThreads) void k_flush(FlushParams p) {
       const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
       for (int64_t x = e_lo; x < e_hi; ++x) {
         const int32_t kk = staged_task(s_off, cnt, x);
-        if (s_off[kk] <= x && x < s_end[kk]) elem_flush<BF16>(p, p.c0 + x, s_root[kk], s_comm[kk]);
+        if (s_off[kk] <= x && x < s_end[kk])
+          elem_flush<BF16>(p, p.c0 + x, s_root[kk], s_csz[kk], s_cst[kk], s_cinv[kk]);
       }
     }
   }
 }
 
-template <bool BF16, int WT, int PRE>
-hipError_t launch_typed(const FlushParams& p, hipStream_t stream) {
-  constexpr int U = 4;
+template <bool BF16, int WT, int C2, int S2, int PRE>
+hipError_t launch_kernel(const FlushParams& p, hipStream_t stream) {
+  constexpr int U = DC_FLUSH_U;
   const int64_t blocks = (p.nv + kThreads * U - 1) / (kThreads * U);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_flush<BF16, WT, PRE, U, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     stream, p);
+  hipLaunchKernelGGL((k_flush<BF16, WT, C2, S2, PRE, U, DC_FLUSH_NT != 0>), dim3((unsigned)blocks),
+                     dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <bool BF16, int WT, int C2, int S2>
+hipError_t launch_pre(const FlushParams& p, hipStream_t stream) {
+  return p.pre_div ? launch_kernel<BF16, WT, C2, S2, kPreMul>(p, stream)
+                   : launch_kernel<BF16, WT, C2, S2, kPreNone>(p, stream);
+}
+
+// The one sub-communicator shape of a comm table, canonicalised (size 1 has
+// stride 1); 0 when there is none, -1 when there are several.
+int sub_shape(const FlushParams& p, int32_t* c2, int32_t* s2) {
+  *c2 = 0;
+  *s2 = 1;
+  for (int k = 1; k < p.ncomms; ++k) {
+    const int32_t c = p.csize[k], s = c == 1 ? 1 : p.cstride[k];
+    if (c == p.W) continue;
+    if (*c2 == 0) {
+      *c2 = c;
+      *s2 = s;
+    } else if (*c2 != c || *s2 != s) {
+      return -1;
+    }
+  }
+  return *c2 ? 1 : 0;
+}
+
+template <bool BF16, int WT>
+hipError_t launch_w(const FlushParams& p, int32_t c2, int32_t s2, hipStream_t stream) {
+  // every (C2, S2) a power-of-two W allows: C2 = WT/2, WT/4, ... with stride
+  // 1 (contiguous blocks) or WT/C2 (strided); size 1 has one shape
+  if (c2 == 0) return launch_pre<BF16, WT, 0, 1>(p, stream);
+#define DC_SUB(C)                                                                   \
+  if constexpr (WT > C && WT % C == 0) {                                            \
+    if (c2 == C) return s2 == 1 ? launch_pre<BF16, WT, C, 1>(p, stream)             \
+                                : launch_pre<BF16, WT, C, (C > 0 ? WT / C : 1)>(p, stream); \
+  }
+  DC_SUB(1)
+  DC_SUB(2)
+  DC_SUB(4)
+  DC_SUB(8)
+#undef DC_SUB
+  return launch_kernel<BF16, 0, 0, 1, kPreNone>(p, stream);
 }
 
 template <bool BF16>
 hipError_t launch_dtype(const FlushParams& p, hipStream_t stream) {
-  // W = 1, 2, 4, 8, 16 get a kernel with every row load issued up front on
-  // the data-parallel communicator; any other W runs the generic vector path.
-  const int pre = p.pre_div ? kPreMul : kPreNone;  // W is a power of two here
-  switch (p.W) {
-#define DC_FLUSH_W(w)                                                     \
-  case w:                                                                 \
-    return pre == kPreNone ? launch_typed<BF16, w, kPreNone>(p, stream)   \
-                           : launch_typed<BF16, w, kPreMul>(p, stream);
-    DC_FLUSH_W(1)
-    DC_FLUSH_W(2)
-    DC_FLUSH_W(4)
-    DC_FLUSH_W(8)
-    DC_FLUSH_W(16)
-#undef DC_FLUSH_W
-    default:
-      return launch_typed<BF16, 0, kPreNone>(p, stream);
+  int32_t c2, s2;
+  if (sub_shape(p, &c2, &s2) >= 0) {
+    switch (p.W) {
+      case 1: return launch_w<BF16, 1>(p, c2, s2, stream);
+      case 2: return launch_w<BF16, 2>(p, c2, s2, stream);
+      case 4: return launch_w<BF16, 4>(p, c2, s2, stream);
+      case 8: return launch_w<BF16, 8>(p, c2, s2, stream);
+      case 16: return launch_w<BF16, 16>(p, c2, s2, stream);
+      default: break;
+    }
   }
+  return launch_kernel<BF16, 0, 0, 1, kPreNone>(p, stream);
 }
 
 }  // namespace

@@ -12,7 +12,34 @@
 namespace dc {
 namespace {
 
-constexpr int kU = 4;  // vectors (or elements) per thread per launch tile
+// Vectors (or elements) per thread per launch tile, per kernel.
+#ifndef DC_RS_U
+#define DC_RS_U 1
+#endif
+#ifndef DC_AG_U
+#define DC_AG_U 1
+#endif
+#ifndef DC_ACC_U
+#define DC_ACC_U 1
+#endif
+#ifndef DC_DEF_U
+#define DC_DEF_U 1
+#endif
+#ifndef DC_COPY_U
+#define DC_COPY_U 1
+#endif
+#ifndef DC_SLAB_NT
+#define DC_SLAB_NT 1      // nontemporal loads (every input is read once)
+#endif
+#ifndef DC_SLAB_NTS
+#define DC_SLAB_NTS 1     // nontemporal stores (reduce-scatter, accumulate, reduce, copy)
+#endif
+#ifndef DC_AG_NTS
+#define DC_AG_NTS 0       // nontemporal stores in the all-gather
+#endif
+constexpr bool kNT = DC_SLAB_NT != 0;
+constexpr bool kNTS = DC_SLAB_NTS != 0;
+constexpr bool kAgNTS = DC_AG_NTS != 0;
 
 // ---------------------------------------------------------------------------
 // fold helpers
@@ -64,12 +91,12 @@ __device__ __forceinline__ u32x4 fold_rows(const u32x4* in, int64_t ldv, int64_t
   if constexpr (WT > 0) {
     u32x4 x[WT];
 #pragma unroll
-    for (int r = 0; r < WT; ++r) x[r] = load16<true>(in + r * ldv + v);
+    for (int r = 0; r < WT; ++r) x[r] = load16<kNT>(in + r * ldv + v);
 #pragma unroll
     for (int r = 0; r < WT; ++r) fold16<BF16, PRE>(acc, x[r], r == 0, inv, c);
   } else {
 #pragma unroll 4
-    for (int32_t r = 0; r < W; ++r) fold16<BF16, PRE>(acc, load16<true>(in + r * ldv + v), r == 0, inv, c);
+    for (int32_t r = 0; r < W; ++r) fold16<BF16, PRE>(acc, load16<kNT>(in + r * ldv + v), r == 0, inv, c);
   }
   return pack16<BF16>(acc);
 }
@@ -105,11 +132,11 @@ __global__ __launch_bounds__(kThreads) void k_rs_vec(int32_t W, const u32x4* __r
                                                      int64_t ldv_out, int64_t Lv, float inv,
                                                      float c) {
   const int64_t s = blockIdx.y;
-  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * DC_RS_U) + threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
+  for (int u = 0; u < DC_RS_U; ++u) {
     const int64_t k = k0 + (int64_t)u * kThreads;
-    if (k < Lv) store16<false>(out + s * ldv_out + k, fold_rows<BF16, WT, PRE>(in, ldv_in, s * Lv + k, W, inv, c));
+    if (k < Lv) store16<kNTS>(out + s * ldv_out + k, fold_rows<BF16, WT, PRE>(in, ldv_in, s * Lv + k, W, inv, c));
   }
 }
 
@@ -119,8 +146,8 @@ __global__ __launch_bounds__(kThreads) void k_rs_elem(int32_t W, const void* __r
                                                       int64_t ld_out, int64_t L, int32_t pre,
                                                       float inv, float c) {
   const int64_t s = blockIdx.y;
-  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
-  for (int u = 0; u < kU; ++u) {
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * DC_RS_U) + threadIdx.x;
+  for (int u = 0; u < DC_RS_U; ++u) {
     const int64_t k = k0 + (int64_t)u * kThreads;
     if (k >= L) continue;
     float acc = 0.0f;
@@ -145,16 +172,16 @@ __global__ __launch_bounds__(kThreads) void k_ag_vec(int32_t W, const u32x4* __r
                                                      int32_t step) {
   const int32_t s = blockIdx.y;
   if (order == DC_ORDER_RANK && step >= 0 && s != step) return;
-  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * DC_AG_U) + threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
+  for (int u = 0; u < DC_AG_U; ++u) {
     const int64_t k = k0 + (int64_t)u * kThreads;
     if (k >= Lv) continue;
-    const u32x4 x = load16<true>(in + (int64_t)s * ldv_in + k);
+    const u32x4 x = load16<kNT>(in + (int64_t)s * ldv_in + k);
     for (int32_t i = 0; i < W; ++i) {
       const int32_t p = order == DC_ORDER_RANK ? s : (i - s + W) % W;
       if (order == DC_ORDER_RING && step >= 0 && p != step) continue;
-      store16<false>(out + (int64_t)i * ldv_out + (int64_t)p * Lv + k, x);
+      store16<kAgNTS>(out + (int64_t)i * ldv_out + (int64_t)p * Lv + k, x);
     }
   }
 }
@@ -166,8 +193,8 @@ __global__ __launch_bounds__(kThreads) void k_ag_elem(int32_t W, const E* __rest
                                                       int32_t step) {
   const int32_t s = blockIdx.y;
   if (order == DC_ORDER_RANK && step >= 0 && s != step) return;
-  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
-  for (int u = 0; u < kU; ++u) {
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * DC_AG_U) + threadIdx.x;
+  for (int u = 0; u < DC_AG_U; ++u) {
     const int64_t k = k0 + (int64_t)u * kThreads;
     if (k >= L) continue;
     const E x = in[(int64_t)s * ld_in + k];
@@ -187,24 +214,24 @@ __global__ __launch_bounds__(kThreads) void k_accumulate(const float* __restrict
                                                          int64_t ld_acc, int64_t M, int32_t init) {
   const int64_t r = blockIdx.y;
   const int64_t nvec = M / 4;
-  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * DC_ACC_U) + threadIdx.x;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x + r * ld_x);
   u32x4* av = reinterpret_cast<u32x4*>(acc + r * ld_acc);
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
+  for (int u = 0; u < DC_ACC_U; ++u) {
     const int64_t k = k0 + (int64_t)u * kThreads;
     if (k < nvec) {
-      const u32x4 xx = load16<true>(xv + k);
+      const u32x4 xx = load16<kNT>(xv + k);
       u32x4 aa;
       if (init) {
         aa = u32x4{0u, 0u, 0u, 0u};
       } else {
-        aa = load16<true>(av + k);
+        aa = load16<kNT>(av + k);
       }
       u32x4 y;
 #pragma unroll
       for (int q = 0; q < 4; ++q) y[q] = __float_as_uint(__uint_as_float(aa[q]) + __uint_as_float(xx[q]));
-      store16<false>(av + k, y);
+      store16<kNTS>(av + k, y);
     } else if (k == nvec) {
       for (int64_t j = nvec * 4; j < M; ++j) {
         const float a = init ? 0.0f : acc[r * ld_acc + j];
@@ -222,15 +249,15 @@ __global__ __launch_bounds__(kThreads) void k_deferred(int32_t W, const float* a
                                                        float* out, int64_t ld_out, int64_t M,
                                                        int32_t out_rows) {
   const int64_t nvec = M / 4;
-  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * DC_DEF_U) + threadIdx.x;
   const u32x4* in = reinterpret_cast<const u32x4*>(acc);
   u32x4* ov = reinterpret_cast<u32x4*>(out);
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
+  for (int u = 0; u < DC_DEF_U; ++u) {
     const int64_t k = k0 + (int64_t)u * kThreads;
     if (k < nvec) {
       const u32x4 y = fold_rows<false, WT, false>(in, ld_acc / 4, k, W, 0.0f, 1.0f);
-      for (int32_t i = 0; i < out_rows; ++i) store16<false>(ov + i * (ld_out / 4) + k, y);
+      for (int32_t i = 0; i < out_rows; ++i) store16<kNTS>(ov + i * (ld_out / 4) + k, y);
     } else if (k == nvec) {
       for (int64_t j = nvec * 4; j < M; ++j) {
         float sum = 0.0f;
@@ -249,16 +276,16 @@ __global__ __launch_bounds__(kThreads) void k_round_bf16(const float* __restrict
 
 __global__ __launch_bounds__(kThreads) void k_copy(const u32x4* __restrict__ src,
                                                    u32x4* __restrict__ dst, int64_t nvec) {
-  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * kU) + threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * (kThreads * DC_COPY_U) + threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
+  for (int u = 0; u < DC_COPY_U; ++u) {
     const int64_t k = k0 + (int64_t)u * kThreads;
-    if (k < nvec) store16<false>(dst + k, load16<true>(src + k));
+    if (k < nvec) store16<kNTS>(dst + k, load16<kNT>(src + k));
   }
 }
 
-inline unsigned blocks_for(int64_t n) {
-  return (unsigned)((n + kThreads * kU - 1) / (kThreads * kU));
+inline unsigned blocks_for(int64_t n, int u) {
+  return (unsigned)((n + kThreads * u - 1) / (kThreads * u));
 }
 
 inline void reciprocal(int32_t c, float* inv, float* cf) {
@@ -271,7 +298,7 @@ hipError_t rs_vec_w(int32_t W, const void* in, int64_t ld_in, void* out, int64_t
                     float inv, float c, hipStream_t stream) {
   constexpr int E = BF16 ? 8 : 4;
   const int64_t Lv = L / E;
-  const dim3 grid(blocks_for(Lv), (unsigned)W);
+  const dim3 grid(blocks_for(Lv, DC_RS_U), (unsigned)W);
   const u32x4* i4 = reinterpret_cast<const u32x4*>(in);
   u32x4* o4 = reinterpret_cast<u32x4*>(out);
   switch (W) {
@@ -310,7 +337,7 @@ hipError_t launch_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64
     return pre_div ? rs_vec_w<false, true>(W, in, ld_in, out, ld_out, L, inv, c, stream)
                    : rs_vec_w<false, false>(W, in, ld_in, out, ld_out, L, inv, c, stream);
   }
-  const dim3 grid(blocks_for(L), (unsigned)W);
+  const dim3 grid(blocks_for(L, DC_RS_U), (unsigned)W);
   if (bf)
     hipLaunchKernelGGL(k_rs_elem<true>, grid, dim3(kThreads), 0, stream, W, in, ld_in, out, ld_out,
                        L, pre_div, inv, c);
@@ -328,15 +355,15 @@ hipError_t launch_all_gather(int32_t W, int32_t dtype, const void* in, int64_t l
   const int E = bf ? 8 : 4;
   if (L % E == 0) {
     const int64_t Lv = L / E;
-    hipLaunchKernelGGL(k_ag_vec, dim3(blocks_for(Lv), (unsigned)W), dim3(kThreads), 0, stream, W,
+    hipLaunchKernelGGL(k_ag_vec, dim3(blocks_for(Lv, DC_AG_U), (unsigned)W), dim3(kThreads), 0, stream, W,
                        reinterpret_cast<const u32x4*>(in), ld_in / E, reinterpret_cast<u32x4*>(out),
                        ld_out / E, Lv, order, step);
   } else if (bf) {
-    hipLaunchKernelGGL(k_ag_elem<uint16_t>, dim3(blocks_for(L), (unsigned)W), dim3(kThreads), 0,
+    hipLaunchKernelGGL(k_ag_elem<uint16_t>, dim3(blocks_for(L, DC_AG_U), (unsigned)W), dim3(kThreads), 0,
                        stream, W, reinterpret_cast<const uint16_t*>(in), ld_in,
                        reinterpret_cast<uint16_t*>(out), ld_out, L, order, step);
   } else {
-    hipLaunchKernelGGL(k_ag_elem<uint32_t>, dim3(blocks_for(L), (unsigned)W), dim3(kThreads), 0,
+    hipLaunchKernelGGL(k_ag_elem<uint32_t>, dim3(blocks_for(L, DC_AG_U), (unsigned)W), dim3(kThreads), 0,
                        stream, W, reinterpret_cast<const uint32_t*>(in), ld_in,
                        reinterpret_cast<uint32_t*>(out), ld_out, L, order, step);
   }
@@ -347,7 +374,7 @@ hipError_t launch_accumulate(int32_t rows, const float* x, int64_t ld_x, float* 
                              int64_t ld_acc, int64_t M, int32_t init, hipStream_t stream) {
   if (M == 0 || rows == 0) return hipSuccess;
   const int64_t nvec = M / 4;
-  hipLaunchKernelGGL(k_accumulate, dim3(blocks_for(nvec + 1), (unsigned)rows), dim3(kThreads), 0,
+  hipLaunchKernelGGL(k_accumulate, dim3(blocks_for(nvec + 1, DC_ACC_U), (unsigned)rows), dim3(kThreads), 0,
                      stream, x, ld_x, acc, ld_acc, M, init);
   return hipGetLastError();
 }
@@ -356,7 +383,7 @@ hipError_t launch_deferred_reduce(int32_t W, const float* acc, int64_t ld_acc, f
                                   int64_t ld_out, int64_t M, int32_t out_rows,
                                   hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  const dim3 grid(blocks_for(M / 4 + 1));
+  const dim3 grid(blocks_for(M / 4 + 1, DC_DEF_U));
   switch (W) {
 #define DC_DR_W(w)                                                                            \
   case w:                                                                                     \
@@ -387,7 +414,7 @@ hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStrea
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
   const int64_t nvec = bytes / 16;
   if (nvec == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_copy, dim3(blocks_for(nvec)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(k_copy, dim3(blocks_for(nvec, DC_COPY_U)), dim3(kThreads), 0, stream,
                      reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), nvec);
   return hipGetLastError();
 }
