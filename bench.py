@@ -120,15 +120,59 @@ def bench_flush(args, w, reduce_to_owner=True):
     value = step_bytes / (ms_step / 1e3) / 1e9
     log(f"[bench] step {ms_step:.3f} ms, {value:.1f} GB/s; flush kernels {kern.sum(axis=1).mean():.3f} ms "
         f"({flush_gbs:.1f} GB/s); per bucket ms {np.round(kern.mean(axis=0), 4).tolist()}")
+    ceiling = access_mix_ceiling(w, owner, x, y, ld)
     roofline = {"bound": "hbm", "achieved": round(flush_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(flush_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile(w, per_launch),
                 "kernel": "k_flush", "launch_ms_avg": round(avg_launch_ms, 4),
                 "bytes_per_launch_avg": int(np.mean(per_launch))}
+    if ceiling is not None:
+        roofline["access_mix_ceiling_gbs"] = round(ceiling, 1)
+        roofline["frac_of_access_mix_ceiling"] = round(flush_gbs / ceiling, 4)
     extra = {"per_bucket_gbs": [round(b / (m / 1e3) / 1e9, 1) for b, m in zip(per_launch, kern.mean(axis=0))]}
     del x, y
     torch.cuda.empty_cache()
     return ms_step, value, step_bytes, roofline, extra
+
+
+def access_mix_ceiling(w, owner, x, y, ld):
+    """Bandwidth the memory system gives the flush's own access mix: W rows
+    read and one row written (owned tasks) or W rows written (AllReduce
+    tasks), measured with dc_stream_rows (xor only) at the bucket size and
+    blended by the step's bytes.  None when W has no reference kernel."""
+    import torch
+    from gradient_reduction_amd import dc
+    if w.W not in (4, 8, 16):
+        return None
+    E = 16 // w.elem_bytes()
+    nvec = min(w.capacity, w.total) // E
+    ldv = ld // E
+    rates = {}
+    for nw in (1, w.W):
+        def run():
+            dc.dc_stream_rows(x, ldv, w.W, y, ldv, nw, nvec)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        rates[nw] = nvec * 16 * (w.W + nw) / (e0.elapsed_time(e1) / 10 / 1e3) / 1e9
+    b = w.elem_bytes()
+    own = ar = 0
+    for bk in w.buckets:
+        for t in bk.tasks:
+            if owner is not None and t.comm == 0 and owner[t.param] >= 0:
+                own += (w.W + 1) * t.numel * b
+            else:
+                ar += 2 * w.W * t.numel * b
+    ceiling = (own + ar) / (own / rates[1] + ar / rates[w.W])
+    log(f"[bench] access-mix reference: read {w.W} write 1 {rates[1]:.1f} GB/s, read {w.W} "
+        f"write {w.W} {rates[w.W]:.1f} GB/s; blended for this step {ceiling:.1f} GB/s")
+    return ceiling
 
 
 def traffic_from_profile(w, per_launch):

@@ -362,4 +362,22 @@ dc_status dc_stream_copy(const void* src, void* dst, int64_t bytes, void* stream
   return hip_status(dc::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)), "copy launch");
 }
 
+dc_status dc_stream_rows(const void* src, int64_t src_ld_vec, int32_t rows_read, void* dst,
+                         int64_t dst_ld_vec, int32_t rows_written, int64_t nvec, void* stream) {
+  if (!((rows_read == 4 || rows_read == 8 || rows_read == 16) &&
+        (rows_written == 1 || rows_written == rows_read)))
+    return fail(DC_ERR_UNSUPPORTED, "rows_read=%d rows_written=%d (need 4/8/16 and 1 or rows_read)",
+                rows_read, rows_written);
+  if (nvec < 0 || src_ld_vec < nvec || dst_ld_vec < nvec)
+    return fail(DC_ERR_SHAPE, "nvec=%lld with row strides %lld and %lld vectors", (long long)nvec,
+                (long long)src_ld_vec, (long long)dst_ld_vec);
+  if (nvec > 0 && (src == nullptr || dst == nullptr)) return fail(DC_ERR_NULL, "src or dst is NULL");
+  if (!aligned16(src) || !aligned16(dst)) return fail(DC_ERR_ALIGN, "src or dst not 16-byte aligned");
+  if (overlaps(src, rows_read * src_ld_vec * 16, dst, rows_written * dst_ld_vec * 16))
+    return fail(DC_ERR_ARG, "src and dst overlap");
+  return hip_status(dc::launch_stream_rows(src, src_ld_vec, rows_read, dst, dst_ld_vec, rows_written,
+                                           nvec, static_cast<hipStream_t>(stream)),
+                    "stream rows launch");
+}
+
 }  // extern "C"

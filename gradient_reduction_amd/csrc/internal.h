@@ -69,4 +69,8 @@ hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStrea
 
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
+hipError_t launch_stream_rows(const void* src, int64_t src_ld_vec, int32_t rows_read, void* dst,
+                              int64_t dst_ld_vec, int32_t rows_written, int64_t nvec,
+                              hipStream_t stream);
+
 }  // namespace dc

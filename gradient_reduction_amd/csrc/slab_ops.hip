@@ -284,6 +284,23 @@ __global__ __launch_bounds__(kThreads) void k_copy(const u32x4* __restrict__ src
   }
 }
 
+// Access-mix reference: R rows read, NW rows written, xor only.
+template <int R, int NW>
+__global__ __launch_bounds__(kThreads) void k_stream_rows(const u32x4* __restrict__ src,
+                                                          int64_t sld, u32x4* __restrict__ dst,
+                                                          int64_t dld, int64_t nvec) {
+  const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (k >= nvec) return;
+  u32x4 x[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = load16<kNT>(src + r * sld + k);
+  u32x4 y = x[0];
+#pragma unroll
+  for (int r = 1; r < R; ++r) y ^= x[r];
+#pragma unroll
+  for (int r = 0; r < NW; ++r) store16<kNTS>(dst + r * dld + k, y);
+}
+
 inline unsigned blocks_for(int64_t n, int u) {
   return (unsigned)((n + kThreads * u - 1) / (kThreads * u));
 }
@@ -409,6 +426,24 @@ hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStrea
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(k_round_bf16, dim3((unsigned)blocks), dim3(kThreads), 0, stream, in, out, n);
   return hipGetLastError();
+}
+
+hipError_t launch_stream_rows(const void* src, int64_t src_ld_vec, int32_t rows_read, void* dst,
+                              int64_t dst_ld_vec, int32_t rows_written, int64_t nvec,
+                              hipStream_t stream) {
+  if (nvec == 0) return hipSuccess;
+  const dim3 grid(blocks_for(nvec, 1));
+  const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+  u32x4* d4 = reinterpret_cast<u32x4*>(dst);
+#define DC_SR(R, NW)                                                                          \
+  if (rows_read == R && rows_written == NW) {                                                 \
+    hipLaunchKernelGGL((k_stream_rows<R, NW>), grid, dim3(kThreads), 0, stream, s4, src_ld_vec, \
+                       d4, dst_ld_vec, nvec);                                                 \
+    return hipGetLastError();                                                                 \
+  }
+  DC_SR(4, 1) DC_SR(4, 4) DC_SR(8, 1) DC_SR(8, 8) DC_SR(16, 1) DC_SR(16, 16)
+#undef DC_SR
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {

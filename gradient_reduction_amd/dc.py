@@ -60,6 +60,7 @@ _SIGS = {
     "dc_deferred_reduce": ([_i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
     "dc_round_bf16": ([_vp, _vp, _i64, _vp], _i32),
     "dc_stream_copy": ([_vp, _vp, _i64, _vp], _i32),
+    "dc_stream_rows": ([_vp, _i64, _i32, _vp, _i64, _i32, _i64, _vp], _i32),
 }
 
 
@@ -196,6 +197,11 @@ def dc_round_bf16(in_, out, n, stream=None):
 
 def dc_stream_copy(src, dst, nbytes, stream=None):
     _check("dc_stream_copy", lib().dc_stream_copy(_dev(src), _dev(dst), nbytes, _stream(stream)))
+
+
+def dc_stream_rows(src, src_ld_vec, rows_read, dst, dst_ld_vec, rows_written, nvec, stream=None):
+    _check("dc_stream_rows", lib().dc_stream_rows(_dev(src), src_ld_vec, rows_read, _dev(dst),
+                                                  dst_ld_vec, rows_written, nvec, _stream(stream)))
 
 
 def tasks_array(tasks):

@@ -275,6 +275,17 @@ dc_status dc_round_bf16(const float* in, uint16_t* out, int64_t n, void* stream)
  * measurements compare against. */
 dc_status dc_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/* Access-mix reference for measurements: for each of `nvec` 16-byte column
+ * vectors, read it from rows_read rows of `src` (rows src_ld_vec vectors
+ * apart), xor them, and store the result to rows_written rows of `dst`
+ * (rows dst_ld_vec vectors apart).  No other arithmetic, so its bandwidth is
+ * what the memory system gives the flush's access mix (W rows read, one row
+ * or W rows written).  rows_read is 4, 8 or 16 and rows_written 1 or
+ * rows_read (else DC_ERR_UNSUPPORTED); pointers 16-byte aligned; the two
+ * regions must not overlap. */
+dc_status dc_stream_rows(const void* src, int64_t src_ld_vec, int32_t rows_read, void* dst,
+                         int64_t dst_ld_vec, int32_t rows_written, int64_t nvec, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -90,6 +90,10 @@ def test_other_argument_checks():
     expect(dc.DC_ERR_ARG, dc.dc_deferred_reduce, 4, FAKE, 64, FAKE << 1, 64, 64, 2, stream=0)
     expect(dc.DC_ERR_ARG, dc.dc_deferred_reduce, 4, FAKE, 64, FAKE + 128, 64, 64, 1, stream=0)
     expect(dc.DC_ERR_SHAPE, dc.dc_stream_copy, FAKE, FAKE << 1, 100, stream=0)
+    expect(dc.DC_ERR_UNSUPPORTED, dc.dc_stream_rows, FAKE, 64, 3, FAKE << 1, 64, 1, 64, stream=0)
+    expect(dc.DC_ERR_UNSUPPORTED, dc.dc_stream_rows, FAKE, 64, 8, FAKE << 1, 64, 2, 64, stream=0)
+    expect(dc.DC_ERR_SHAPE, dc.dc_stream_rows, FAKE, 32, 8, FAKE << 1, 64, 1, 64, stream=0)
+    expect(dc.DC_ERR_ARG, dc.dc_stream_rows, FAKE, 64, 8, FAKE + 1024, 64, 1, 64, stream=0)
     expect(dc.DC_ERR_ARG, dc.dc_stream_copy, FAKE, FAKE + 16, 64, stream=0)
     expect(dc.DC_ERR_SHAPE, dc.dc_partition_ids, 4, 3, FAKE, 1, [0, 2], [4], FAKE, FAKE, FAKE,
            FAKE, 10, stream=0)

@@ -221,3 +221,21 @@ def test_deferred_ga_qwen3_full_size(K):
     tc = torch.from_numpy(cols).cuda()
     assert np.array_equal(D[0, tc].cpu().numpy().view(np.uint32), hD[0].view(np.uint32))
     assert np.array_equal(A[0, tc].cpu().numpy().view(np.uint32), hA[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("R,NW", [(4, 1), (8, 8), (16, 1)])
+def test_stream_rows_reference(R, NW):
+    """The access-mix reference kernel stores the xor of the R rows."""
+    import torch
+    nvec = 1000
+    ld = wl.round_up(nvec * 4, 64)
+    x = U.gen_slab(wl.DT_F32, R, ld, ld, 21, 0, wl.sigma_scale(1e-3))
+    y = U.empty_slab(wl.DT_F32, R, ld)
+    dc.dc_stream_rows(x, ld // 4, R, y, ld // 4, NW, nvec)
+    torch.cuda.synchronize()
+    hx = x.cpu().numpy().view(np.uint32)
+    want = np.bitwise_xor.reduce(hx[:, :nvec * 4], axis=0)
+    got = y.cpu().numpy().view(np.uint32)
+    for r in range(NW):
+        assert np.array_equal(got[r, :nvec * 4], want)
+    assert np.all(got[NW:, :] == U.SENTINEL32) and np.all(got[:, nvec * 4:] == U.SENTINEL32)
