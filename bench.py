@@ -33,15 +33,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def flush_bytes(w, owner):
-    """Algorithmic bytes of every flush launch of workload w."""
+def flush_bytes(w, owner, psize=None):
+    """Algorithmic bytes of every flush launch of workload w (ZeRO-2 when
+    psize, the per-param partition size, is given)."""
     b = w.elem_bytes()
     per = []
     for bk in w.buckets:
         tot = 0
         for t in bk.tasks:
-            own = owner is not None and t.comm == 0 and owner[t.param] >= 0
-            tot += w.W * t.numel * b + (1 if own else w.W) * t.numel * b + 32
+            if psize is not None:
+                one = t.comm == 0 and psize[t.param] > 0
+            else:
+                one = owner is not None and t.comm == 0 and owner[t.param] >= 0
+            tot += w.W * t.numel * b + (1 if one else w.W) * t.numel * b + 32
         per.append(tot)
     return per
 
@@ -65,7 +69,7 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.ev]
 
 
-def bench_flush(args, w, reduce_to_owner=True):
+def bench_flush(args, w, reduce_to_owner=True, zero2=False):
     import torch
     import synth
     from gradient_reduction_amd import executor
@@ -81,14 +85,15 @@ def bench_flush(args, w, reduce_to_owner=True):
     synth.fill_slab_device(w.dtype, w.value_seed, 0, w.scale, w.W, ld, w.total, x.data_ptr(),
                            stream.cuda_stream)
     y = torch.zeros((w.W, ld), dtype=dt, device=dev)
-    ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner, log=log)
+    ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner, log=log, zero2=zero2)
     ex.build_owner_map()
     ex.fetch_metadata()
     log("[bench] " + ex.ratio_line())
-    for b in range(min(len(w.buckets), 3)):
-        log("[bench] " + ex.probe_line(b, b))
+    if not zero2:
+        for b in range(min(len(w.buckets), 3)):
+            log("[bench] " + ex.probe_line(b, b))
     owner = ex.h_owner if reduce_to_owner else None
-    per_launch = flush_bytes(w, owner)
+    per_launch = flush_bytes(w, owner, ex.h_psize if zero2 else None)
     step_bytes = sum(per_launch) + owner_map_bytes(w)
     nb = len(w.buckets)
 
@@ -120,7 +125,7 @@ def bench_flush(args, w, reduce_to_owner=True):
     value = step_bytes / (ms_step / 1e3) / 1e9
     log(f"[bench] step {ms_step:.3f} ms, {value:.1f} GB/s; flush kernels {kern.sum(axis=1).mean():.3f} ms "
         f"({flush_gbs:.1f} GB/s); per bucket ms {np.round(kern.mean(axis=0), 4).tolist()}")
-    ceiling = access_mix_ceiling(w, owner, x, y, ld)
+    ceiling = access_mix_ceiling(w, owner, x, y, ld, ex.h_psize if zero2 else None)
     roofline = {"bound": "hbm", "achieved": round(flush_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(flush_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile(w, per_launch),
@@ -135,7 +140,7 @@ def bench_flush(args, w, reduce_to_owner=True):
     return ms_step, value, step_bytes, roofline, extra
 
 
-def access_mix_ceiling(w, owner, x, y, ld):
+def access_mix_ceiling(w, owner, x, y, ld, psize=None):
     """Bandwidth the memory system gives the flush's own access mix: W rows
     read and one row written (owned tasks) or W rows written (AllReduce
     tasks), measured with dc_stream_rows (xor only) at the bucket size and
@@ -165,7 +170,11 @@ def access_mix_ceiling(w, owner, x, y, ld):
     own = ar = 0
     for bk in w.buckets:
         for t in bk.tasks:
-            if owner is not None and t.comm == 0 and owner[t.param] >= 0:
+            if psize is not None:
+                one = t.comm == 0 and psize[t.param] > 0
+            else:
+                one = owner is not None and t.comm == 0 and owner[t.param] >= 0
+            if one:
                 own += (w.W + 1) * t.numel * b
             else:
                 ar += 2 * w.W * t.numel * b
@@ -245,19 +254,26 @@ def bench_deferred(args):
                                xs[k].data_ptr(), s)
     acc = torch.empty((W, ld), dtype=torch.float32, device=dev)
     out = torch.empty((W, ld), dtype=torch.float32, device=dev)
-    acc_b = [(2 if k else 1) * W * M * 4 + W * M * 4 for k in range(args.ga)]
-    red_b = W * M * 4 + W * M * 4
+    fused = args.fused
+    n_acc = args.ga - 1 if fused else args.ga
+    acc_b = [(2 if k else 1) * W * M * 4 + W * M * 4 for k in range(n_acc)]
+    # fused last step: x (and acc unless K = 1) read, W result rows written
+    red_b = ((W * M * 4 if args.ga > 1 else 0) + W * M * 4 + W * M * 4) if fused else W * M * 4 + W * M * 4
     step_bytes = sum(acc_b) + red_b
-    n = args.ga + 1
+    n = n_acc + 1
 
     def step(tm=None):
-        for k in range(args.ga):
+        for k in range(n_acc):
             if tm: tm.ev[k][0].record()
             dc.dc_accumulate(W, xs[k], ld, acc, ld, M, 1 if k == 0 else 0)
             if tm: tm.ev[k][1].record()
-        if tm: tm.ev[args.ga][0].record()
-        dc.dc_deferred_reduce(W, acc, ld, out, ld, M, W)
-        if tm: tm.ev[args.ga][1].record()
+        if tm: tm.ev[n_acc][0].record()
+        if fused:
+            dc.dc_accumulate_reduce(W, xs[args.ga - 1], ld, acc, ld, 1 if args.ga == 1 else 0, 0,
+                                    out, ld, W, M)
+        else:
+            dc.dc_deferred_reduce(W, acc, ld, out, ld, M, W)
+        if tm: tm.ev[n_acc][1].record()
 
     for _ in range(args.warmup):
         step()
@@ -272,12 +288,13 @@ def bench_deferred(args):
     ms_step = t0.elapsed_time(t1) / args.steps
     kern = np.array([tm.ms() for tm in timers]).mean(axis=0)
     red_gbs = red_b / (kern[-1] / 1e3) / 1e9
-    acc_gbs = sum(acc_b) / (kern[:-1].sum() / 1e3) / 1e9
+    acc_gbs = sum(acc_b) / (kern[:-1].sum() / 1e3) / 1e9 if n_acc else 0.0
     log(f"[bench] deferred K={args.ga}: step {ms_step:.3f} ms; accumulate {acc_gbs:.1f} GB/s; "
         f"reduce {red_gbs:.1f} GB/s ({kern[-1]:.3f} ms)")
     roofline = {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(red_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_deferred", "launch_ms_avg": round(float(kern[-1]), 4),
+                "kernel": "k_accum_reduce" if fused else "k_deferred",
+                "launch_ms_avg": round(float(kern[-1]), 4),
                 "bytes_per_launch_avg": red_b}
     extra = {"accumulate_gbs": round(acc_gbs, 1)}
     return w.name, ms_step, step_bytes / (ms_step / 1e3) / 1e9, roofline, extra, "f32"
@@ -355,8 +372,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="owner_w8",
-                    choices=["owner_w8", "allreduce_w8", "mixed", "deferred", "rs_ag", "tiny"])
+                    choices=["owner_w8", "allreduce_w8", "zero2_w8", "mixed", "zero2_mixed",
+                             "deferred", "rs_ag", "tiny"])
     ap.add_argument("--ga", type=int, default=8)
+    ap.add_argument("--fused", action="store_true",
+                    help="deferred workload: fuse the last accumulate into the reduce")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -374,22 +394,27 @@ def main():
     calib = copy_calibration()
     log(f"[bench] streaming copy reference: {calib} GB/s")
     cpu = None
-    if args.workload in ("owner_w8", "allreduce_w8", "mixed", "tiny"):
+    if args.workload in ("owner_w8", "allreduce_w8", "zero2_w8", "mixed", "zero2_mixed", "tiny"):
         w = {"owner_w8": wl.owner_flush_w8, "allreduce_w8": wl.owner_flush_w8,
-             "mixed": wl.mixed_flush_w16, "tiny": wl.tiny_flush}[args.workload]()
-        owner_mode = args.workload != "allreduce_w8"
-        ms, value, step_bytes, roof, extra = bench_flush(args, w, owner_mode)
+             "zero2_w8": wl.owner_flush_w8, "mixed": wl.mixed_flush_w16,
+             "zero2_mixed": wl.mixed_flush_w16, "tiny": wl.tiny_flush}[args.workload]()
+        zero2 = args.workload.startswith("zero2")
+        owner_mode = args.workload != "allreduce_w8" and not zero2
+        ms, value, step_bytes, roof, extra = bench_flush(args, w, owner_mode, zero2)
         name, dtype = w.name, wl.DTYPE_NAME[w.dtype]
         config = {"workload": name, "W": w.W, "elements": w.total, "buckets": len(w.buckets),
                   "tasks_per_bucket": [len(b.tasks) for b in w.buckets],
-                  "bucket_capacity": w.capacity, "mode": "reduce_to_owner" if owner_mode else "allreduce",
+                  "bucket_capacity": w.capacity,
+                  "mode": "zero2" if zero2 else ("reduce_to_owner" if owner_mode else "allreduce"),
                   "pre_div": w.pre_div, "step": "owner map + every bucket flush",
                   "step_bytes": step_bytes}
-        if not args.no_cpu_baseline:
+        if not args.no_cpu_baseline and not zero2:
             cpu = cpu_baseline_flush(w, owner_mode, max_buckets=2 if w.total > 1e8 else 1)
     elif args.workload == "deferred":
         name, ms, value, roof, extra, dtype = bench_deferred(args)
-        config = {"workload": name, "W": 4, "K": args.ga, "step": "K accumulates + deferred reduce"}
+        config = {"workload": name, "W": 4, "K": args.ga,
+                  "step": ("K-1 accumulates + fused accumulate-reduce" if args.fused
+                           else "K accumulates + deferred reduce")}
     else:
         name, ms, value, roof, extra, dtype = bench_rs_ag(args)
         config = {"workload": name, "W": 8, "step": "reduce-scatter + all-gather rank + all-gather ring"}

@@ -193,11 +193,15 @@ dc_status dc_validate_tasks(int32_t W, const dc_task* tasks, int32_t num_tasks,
   return ok();
 }
 
-dc_status dc_flush_bucket(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
-                          void* slab_out, int64_t ld_out, int64_t bucket_col,
-                          int64_t bucket_numel, const dc_task* tasks, int32_t num_tasks,
-                          const int32_t* owner, int32_t num_params, const dc_comm* comms,
-                          int32_t num_comms, int32_t pre_div, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dc_status flush_common(const char* fn, int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                       void* slab_out, int64_t ld_out, int64_t bucket_col, int64_t bucket_numel,
+                       const dc_task* tasks, int32_t num_tasks, const int32_t* owner,
+                       const int64_t* flat, const int64_t* psize, int32_t num_params,
+                       const dc_comm* comms, int32_t num_comms, int32_t pre_div, void* stream) {
   dc_status st;
   if ((st = check_w(W)) || (st = check_dtype(dtype)) || (st = check_comms(W, comms, num_comms))) return st;
   if (bucket_col < 0 || bucket_numel < 0)
@@ -228,10 +232,39 @@ dc_status dc_flush_bucket(int32_t W, int32_t dtype, const void* slab_in, int64_t
   a.tasks = tasks;
   a.ntasks = num_tasks;
   a.owner = owner;
+  a.flat = flat;
+  a.psize = psize;
   a.nparams = num_params;
   a.ncomms = num_comms;
   for (int k = 0; k < num_comms; ++k) a.comms[k] = {comms[k].size, comms[k].stride};
-  return hip_status(dc::launch_flush(a, static_cast<hipStream_t>(stream)), "flush launch");
+  return hip_status(dc::launch_flush(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+dc_status dc_flush_bucket(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                          void* slab_out, int64_t ld_out, int64_t bucket_col,
+                          int64_t bucket_numel, const dc_task* tasks, int32_t num_tasks,
+                          const int32_t* owner, int32_t num_params, const dc_comm* comms,
+                          int32_t num_comms, int32_t pre_div, void* stream) {
+  return flush_common("flush launch", W, dtype, slab_in, ld_in, slab_out, ld_out, bucket_col,
+                      bucket_numel, tasks, num_tasks, owner, nullptr, nullptr, num_params, comms,
+                      num_comms, pre_div, stream);
+}
+
+dc_status dc_flush_bucket_zero2(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                                void* slab_out, int64_t ld_out, int64_t bucket_col,
+                                int64_t bucket_numel, const dc_task* tasks, int32_t num_tasks,
+                                const int64_t* flat_offset, const int64_t* part_size,
+                                int32_t num_params, const dc_comm* comms, int32_t num_comms,
+                                int32_t pre_div, void* stream) {
+  if (num_tasks > 0 && (flat_offset == nullptr || part_size == nullptr))
+    return fail(DC_ERR_NULL, "flat_offset or part_size is NULL");
+  return flush_common("ZeRO-2 flush launch", W, dtype, slab_in, ld_in, slab_out, ld_out,
+                      bucket_col, bucket_numel, tasks, num_tasks, nullptr, flat_offset, part_size,
+                      num_params, comms, num_comms, pre_div, stream);
 }
 
 dc_status dc_probe_flush(int32_t W, int32_t dtype, const dc_task* tasks, int32_t num_tasks,
@@ -346,6 +379,35 @@ dc_status dc_deferred_reduce(int32_t W, const float* acc, int64_t ld_acc, float*
   return hip_status(dc::launch_deferred_reduce(W, acc, ld_acc, out, ld_out, M, out_rows,
                                                static_cast<hipStream_t>(stream)),
                     "deferred reduce launch");
+}
+
+dc_status dc_accumulate_reduce(int32_t W, const float* x, int64_t ld_x, float* acc, int64_t ld_acc,
+                               int32_t init, int32_t keep_acc, float* out, int64_t ld_out,
+                               int32_t out_rows, int64_t M, void* stream) {
+  dc_status st;
+  if ((st = check_w(W))) return st;
+  if (out_rows != 1 && out_rows != W) return fail(DC_ERR_ARG, "out_rows=%d is neither 1 nor W", out_rows);
+  if (M < 0) return fail(DC_ERR_ARG, "M < 0");
+  if ((init != 0 && init != 1) || (keep_acc != 0 && keep_acc != 1))
+    return fail(DC_ERR_ARG, "init=%d keep_acc=%d", init, keep_acc);
+  if ((st = check_slab("x", x, ld_x, M, DC_F32)) || (st = check_slab("acc", acc, ld_acc, M, DC_F32)) ||
+      (st = check_slab("out", out, ld_out, M, DC_F32)))
+    return st;
+  const void *xv = x, *av = acc, *ov = out;
+  if (xv == av) {
+    if (ld_x != ld_acc) return fail(DC_ERR_ARG, "x == acc needs ld_x == ld_acc");
+  } else if (overlaps(x, W * ld_x * 4, acc, W * ld_acc * 4)) {
+    return fail(DC_ERR_ARG, "x and acc overlap");
+  }
+  if (overlaps(x, W * ld_x * 4, out, out_rows * ld_out * 4)) return fail(DC_ERR_ARG, "x and out overlap");
+  if (av == ov) {
+    if (ld_acc != ld_out || keep_acc) return fail(DC_ERR_ARG, "out == acc needs ld_out == ld_acc and keep_acc = 0");
+  } else if (overlaps(acc, W * ld_acc * 4, out, out_rows * ld_out * 4)) {
+    return fail(DC_ERR_ARG, "acc and out overlap");
+  }
+  return hip_status(dc::launch_accumulate_reduce(W, x, ld_x, acc, ld_acc, init, keep_acc, out, ld_out,
+                                                 out_rows, M, static_cast<hipStream_t>(stream)),
+                    "accumulate-reduce launch");
 }
 
 dc_status dc_round_bf16(const float* in, uint16_t* out, int64_t n, void* stream) {

@@ -58,6 +58,8 @@ struct FlushParams {
   const dc_task* tasks;
   int32_t ntasks;
   const int32_t* owner;
+  const int64_t* flat;   // ZeRO-2: flat offset of each param in its group
+  const int64_t* psize;  // ZeRO-2: partition size of each param's group (0: AllReduce)
   int32_t nparams;
   int32_t W;
   int32_t ncomms;
@@ -316,7 +318,7 @@ __device__ __forceinline__ void elem_flush(const FlushParams& p, int64_t col, in
 // WT > 0: W known at compile time, every communicator of the launch is the
 // data-parallel one or the single shape (C2, S2) (C2 = 0: none).  WT = 0:
 // any W and any communicators, all at run time.
-template <bool BF16, int WT, int C2, int S2, int PRE, int U, bool NT>
+template <bool BF16, int WT, int C2, int S2, int PRE, int U, bool NT, bool Z2>
 __global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p) {
   static_assert(U <= 32, "slow-vector mask is 32 bits");
   constexpr int E = BF16 ? 8 : 4;
@@ -326,6 +328,9 @@ __global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p)
   __shared__ int32_t s_csz[kStage];
   __shared__ int32_t s_cst[kStage];
   __shared__ float s_cinv[kStage];
+  // ZeRO-2: flat offset of the task's first element and its partition size
+  __shared__ int64_t s_za[Z2 ? kStage : 1];
+  __shared__ int64_t s_zs[Z2 ? kStage : 1];
 
   int64_t tile = blockIdx.x;
   if (DC_FLUSH_XCD) {
@@ -367,6 +372,15 @@ __global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p)
       s_csz[threadIdx.x] = c;
       s_cst[threadIdx.x] = st;
       s_cinv[threadIdx.x] = inv;
+      if constexpr (Z2) {
+        int64_t a = 0, S = 0;
+        if (comm == 0 && t.param >= 0 && t.param < p.nparams) {
+          S = p.psize[t.param];
+          a = p.flat[t.param];
+        }
+        s_za[threadIdx.x] = a;
+        s_zs[threadIdx.x] = S > 0 ? S : 0;
+      }
     }
     __syncthreads();
     const int64_t clo = max(lo, s_off[0]);
@@ -392,7 +406,19 @@ __global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p)
         const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
         if (e_lo >= e_hi) continue;
         const int32_t k = staged_task(s_off, cnt, e_lo);
-        if (e_lo == rc && e_hi == rc + E && s_off[k] <= rc && s_end[k] >= rc + E) {
+        bool whole = e_lo == rc && e_hi == rc + E && s_off[k] <= rc && s_end[k] >= rc + E;
+        int32_t vroot = s_root[k];
+        if constexpr (Z2) {
+          // every element goes to the rank of its partition; a vector cut by
+          // a partition boundary takes the element path
+          if (whole && s_zs[k] > 0) {
+            const int64_t pos = s_za[k] + (rc - s_off[k]);
+            const int64_t q0 = pos / s_zs[k], q1 = (pos + E - 1) / s_zs[k];
+            if (q0 == q1 && q0 < WT) vroot = (int32_t)q0;
+            else whole = false;
+          }
+        }
+        if (whole) {
 #if DC_FLUSH_PIPE
           u32x4 nxt[WT];
           load_rows<BF16, WT, NT>(p, av, nxt);
@@ -400,12 +426,12 @@ __global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p)
 #pragma unroll
           for (int r = 0; r < WT; ++r) cur[r] = nxt[r];
           cav = av;
-          croot = s_root[k];
+          croot = vroot;
           cc = s_csz[k];
 #else
           u32x4 x[WT];
           load_rows<BF16, WT, NT>(p, av, x);
-          fold_store_shape<BF16, WT, C2, S2, PRE>(p, x, av, s_root[k], s_csz[k]);
+          fold_store_shape<BF16, WT, C2, S2, PRE>(p, x, av, vroot, s_csz[k]);
 #endif
         } else {
           slow |= 1u << u;
@@ -424,8 +450,18 @@ __global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p)
         const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
         if (e_lo >= e_hi) continue;
         const int32_t k = staged_task(s_off, cnt, e_lo);
-        if (e_lo == rc && e_hi == rc + E && s_off[k] <= rc && s_end[k] >= rc + E)
-          vec_generic<BF16, NT>(p, av, s_root[k], s_csz[k], s_cst[k], s_cinv[k]);
+        bool whole = e_lo == rc && e_hi == rc + E && s_off[k] <= rc && s_end[k] >= rc + E;
+        int32_t vroot = s_root[k];
+        if constexpr (Z2) {
+          if (whole && s_zs[k] > 0) {
+            const int64_t pos = s_za[k] + (rc - s_off[k]);
+            const int64_t q0 = pos / s_zs[k], q1 = (pos + E - 1) / s_zs[k];
+            if (q0 == q1 && q0 < p.W) vroot = (int32_t)q0;
+            else whole = false;
+          }
+        }
+        if (whole)
+          vec_generic<BF16, NT>(p, av, vroot, s_csz[k], s_cst[k], s_cinv[k]);
         else
           slow |= 1u << u;
       }
@@ -438,8 +474,16 @@ __global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p)
       const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
       for (int64_t x = e_lo; x < e_hi; ++x) {
         const int32_t kk = staged_task(s_off, cnt, x);
-        if (s_off[kk] <= x && x < s_end[kk])
-          elem_flush<BF16>(p, p.c0 + x, s_root[kk], s_csz[kk], s_cst[kk], s_cinv[kk]);
+        if (s_off[kk] <= x && x < s_end[kk]) {
+          int32_t eroot = s_root[kk];
+          if constexpr (Z2) {
+            if (s_zs[kk] > 0) {
+              const int64_t q = (s_za[kk] + (x - s_off[kk])) / s_zs[kk];
+              eroot = q < p.W ? (int32_t)q : -1;
+            }
+          }
+          elem_flush<BF16>(p, p.c0 + x, eroot, s_csz[kk], s_cst[kk], s_cinv[kk]);
+        }
       }
     }
   }
@@ -450,8 +494,12 @@ hipError_t launch_kernel(const FlushParams& p, hipStream_t stream) {
   constexpr int U = DC_FLUSH_U;
   const int64_t blocks = (p.nv + kThreads * U - 1) / (kThreads * U);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_flush<BF16, WT, C2, S2, PRE, U, DC_FLUSH_NT != 0>), dim3((unsigned)blocks),
-                     dim3(kThreads), 0, stream, p);
+  if (p.flat != nullptr)
+    hipLaunchKernelGGL((k_flush<BF16, WT, C2, S2, PRE, U, DC_FLUSH_NT != 0, true>),
+                       dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_flush<BF16, WT, C2, S2, PRE, U, DC_FLUSH_NT != 0, false>),
+                       dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -529,6 +577,8 @@ hipError_t launch_flush(const FlushLaunch& a, hipStream_t stream) {
   p.tasks = a.tasks;
   p.ntasks = a.ntasks;
   p.owner = a.owner;
+  p.flat = a.flat;
+  p.psize = a.psize;
   p.nparams = a.nparams;
   p.W = a.W;
   p.ncomms = a.ncomms;

@@ -27,6 +27,8 @@ struct FlushLaunch {
   const dc_task* tasks;
   int32_t ntasks;
   const int32_t* owner;
+  const int64_t* flat;   // ZeRO-2 mode when non-null (with psize)
+  const int64_t* psize;
   int32_t nparams;
   int32_t ncomms;
   CommSpec comms[DC_MAX_COMMS];
@@ -64,6 +66,11 @@ hipError_t launch_accumulate(int32_t rows, const float* x, int64_t ld_x, float* 
 hipError_t launch_deferred_reduce(int32_t W, const float* acc, int64_t ld_acc, float* out,
                                   int64_t ld_out, int64_t M, int32_t out_rows,
                                   hipStream_t stream);
+
+hipError_t launch_accumulate_reduce(int32_t W, const float* x, int64_t ld_x, float* acc,
+                                    int64_t ld_acc, int32_t init, int32_t keep_acc, float* out,
+                                    int64_t ld_out, int32_t out_rows, int64_t M,
+                                    hipStream_t stream);
 
 hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
 

@@ -268,6 +268,59 @@ __global__ __launch_bounds__(kThreads) void k_deferred(int32_t W, const float* a
   }
 }
 
+// a10 + a11 fused: a_r = acc_r + x_r (or +0 + x_r), optionally kept, then
+// folded in rank order.  W known at compile time loads every row first.
+template <int WT>
+__global__ __launch_bounds__(kThreads) void k_accum_reduce(int32_t W, const float* x, int64_t ld_x,
+                                                           float* acc, int64_t ld_acc, int32_t init,
+                                                           int32_t keep, float* out, int64_t ld_out,
+                                                           int32_t out_rows, int64_t M) {
+  const int64_t nvec = M / 4;
+  const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  u32x4* av = reinterpret_cast<u32x4*>(acc);
+  u32x4* ov = reinterpret_cast<u32x4*>(out);
+  const int64_t lx = ld_x / 4, la = ld_acc / 4, lo = ld_out / 4;
+  if (k < nvec) {
+    float sum[4];
+    constexpr int RB = WT > 0 ? WT : 4;  // rows per batch of loads
+    for (int32_t r0 = 0; r0 < W; r0 += RB) {
+      u32x4 xx[RB], aa[RB];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        if (WT == 0 && r0 + i >= W) break;
+        xx[i] = load16<kNT>(xv + (r0 + i) * lx + k);
+        aa[i] = init ? u32x4{0u, 0u, 0u, 0u} : load16<kNT>(av + (r0 + i) * la + k);
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        if (WT == 0 && r0 + i >= W) break;
+        u32x4 a;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float v = __uint_as_float(aa[i][q]) + __uint_as_float(xx[i][q]);
+          a[q] = __float_as_uint(v);
+          sum[q] = (r0 + i) == 0 ? v : sum[q] + v;
+        }
+        if (keep) store16<kNTS>(av + (r0 + i) * la + k, a);
+      }
+    }
+    const u32x4 y = u32x4{__float_as_uint(sum[0]), __float_as_uint(sum[1]), __float_as_uint(sum[2]),
+                          __float_as_uint(sum[3])};
+    for (int32_t i = 0; i < out_rows; ++i) store16<kNTS>(ov + i * lo + k, y);
+  } else if (k == nvec) {
+    for (int64_t j = nvec * 4; j < M; ++j) {
+      float s = 0.0f;
+      for (int32_t r = 0; r < W; ++r) {
+        const float a = (init ? 0.0f : acc[r * ld_acc + j]) + x[r * ld_x + j];
+        if (keep) acc[r * ld_acc + j] = a;
+        s = r == 0 ? a : s + a;
+      }
+      for (int32_t i = 0; i < out_rows; ++i) out[i * ld_out + j] = s;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void k_round_bf16(const float* __restrict__ in,
                                                          uint16_t* __restrict__ out, int64_t n) {
   const int64_t step = (int64_t)gridDim.x * kThreads;
@@ -416,6 +469,31 @@ hipError_t launch_deferred_reduce(int32_t W, const float* acc, int64_t ld_acc, f
     default:
       hipLaunchKernelGGL(k_deferred<0>, grid, dim3(kThreads), 0, stream, W, acc, ld_acc, out,
                          ld_out, M, out_rows);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_accumulate_reduce(int32_t W, const float* x, int64_t ld_x, float* acc,
+                                    int64_t ld_acc, int32_t init, int32_t keep_acc, float* out,
+                                    int64_t ld_out, int32_t out_rows, int64_t M,
+                                    hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const dim3 grid(blocks_for(M / 4 + 1, 1));
+  switch (W) {
+#define DC_AR_W(w)                                                                            \
+  case w:                                                                                     \
+    hipLaunchKernelGGL(k_accum_reduce<w>, grid, dim3(kThreads), 0, stream, W, x, ld_x, acc,   \
+                       ld_acc, init, keep_acc, out, ld_out, out_rows, M);                     \
+    break;
+    DC_AR_W(1)
+    DC_AR_W(2)
+    DC_AR_W(4)
+    DC_AR_W(8)
+    DC_AR_W(16)
+#undef DC_AR_W
+    default:
+      hipLaunchKernelGGL(k_accum_reduce<0>, grid, dim3(kThreads), 0, stream, W, x, ld_x, acc,
+                         ld_acc, init, keep_acc, out, ld_out, out_rows, M);
   }
   return hipGetLastError();
 }

@@ -53,11 +53,15 @@ _SIGS = {
     "dc_validate_tasks": ([_i32, _vp, _i32, _i64, _i32, _vp, _i32], _i32),
     "dc_flush_bucket": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _vp,
                          _i32, _i32, _vp], _i32),
+    "dc_flush_bucket_zero2": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
+                               _i32, _vp, _i32, _i32, _vp], _i32),
     "dc_probe_flush": ([_i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp], _i32),
     "dc_reduce_scatter": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
     "dc_all_gather": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _i32, _vp], _i32),
     "dc_accumulate": ([_i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
     "dc_deferred_reduce": ([_i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
+    "dc_accumulate_reduce": ([_i32, _vp, _i64, _vp, _i64, _i32, _i32, _vp, _i64, _i32, _i64, _vp],
+                             _i32),
     "dc_round_bf16": ([_vp, _vp, _i64, _vp], _i32),
     "dc_stream_copy": ([_vp, _vp, _i64, _vp], _i32),
     "dc_stream_rows": ([_vp, _i64, _i32, _vp, _i64, _i32, _i64, _vp], _i32),
@@ -157,6 +161,16 @@ def dc_flush_bucket(W, dtype, slab_in, ld_in, slab_out, ld_out, bucket_col, buck
         _stream(stream)))
 
 
+def dc_flush_bucket_zero2(W, dtype, slab_in, ld_in, slab_out, ld_out, bucket_col, bucket_numel,
+                          tasks, num_tasks, flat_offset, part_size, num_params, comms, num_comms,
+                          pre_div, stream=None):
+    cp, _a = _host(comms, COMM_DTYPE)
+    _check("dc_flush_bucket_zero2", lib().dc_flush_bucket_zero2(
+        W, dtype, _dev(slab_in), ld_in, _dev(slab_out), ld_out, bucket_col, bucket_numel,
+        _dev(tasks), num_tasks, _dev(flat_offset), _dev(part_size), num_params, cp, num_comms,
+        pre_div, _stream(stream)))
+
+
 def dc_probe_flush(W, dtype, tasks, num_tasks, owner, num_params, pid_offsets, pids, comms,
                    num_comms, pre_div):
     """Host-only; returns a dc_probe."""
@@ -189,6 +203,13 @@ def dc_accumulate(rows, x, ld_x, acc, ld_acc, M, init, stream=None):
 def dc_deferred_reduce(W, acc, ld_acc, out, ld_out, M, out_rows, stream=None):
     _check("dc_deferred_reduce", lib().dc_deferred_reduce(W, _dev(acc), ld_acc, _dev(out), ld_out,
                                                           M, out_rows, _stream(stream)))
+
+
+def dc_accumulate_reduce(W, x, ld_x, acc, ld_acc, init, keep_acc, out, ld_out, out_rows, M,
+                         stream=None):
+    _check("dc_accumulate_reduce", lib().dc_accumulate_reduce(
+        W, _dev(x), ld_x, _dev(acc), ld_acc, init, keep_acc, _dev(out), ld_out, out_rows, M,
+        _stream(stream)))
 
 
 def dc_round_bf16(in_, out, n, stream=None):

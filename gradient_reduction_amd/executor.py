@@ -1,10 +1,12 @@
-"""ZeRO-1 bucket-flush executor over one GPU's [W, M] gradient slab.
+"""ZeRO-1 (and ZeRO-2) bucket-flush executor over one GPU's [W, M] gradient slab.
 
 DeepSpeed issue "[REQUEST] DeepCompile ZeRO-1: reduce-to-owner instead of
 AllReduce": at init the owner map is built from the partition lists and the
 qualifying ratio is reported; every bucket flush then reduces each task to its
 owner (reduce_to_owner on) or to every rank (off, the default), and the probe
-reports one line per flush for the first 20 flushes (reduce_probe).
+reports one line per flush for the first 20 flushes (reduce_probe).  With
+zero2=True every element goes to the rank whose partition holds it (the
+issue's ZeRO-2 follow-up); the probe describes the ZeRO-1 paths only.
 
 torch supplies device memory and the stream; every step runs in libdc.so.
 """
@@ -30,11 +32,13 @@ class Zero1FlushExecutor:
                  group_parts: Sequence[int], group_comm_size: Sequence[int],
                  group_rank_to_global: Sequence[Sequence[int]], comms: Sequence[Tuple[int, int]],
                  buckets: Sequence[BucketSpec], pre_div: int, reduce_to_owner: bool = False,
-                 reduce_probe: bool = False, device: str = "cuda", log=print):
+                 reduce_probe: bool = False, device: str = "cuda", log=print,
+                 zero2: bool = False):
         import torch
         self.torch = torch
         self.W, self.dtype, self.pre_div = W, dtype, pre_div
         self.reduce_to_owner, self.reduce_probe = reduce_to_owner, reduce_probe
+        self.zero2 = zero2
         self.log = log
         self.P = len(numel)
         self.G = len(group_parts)
@@ -63,6 +67,18 @@ class Zero1FlushExecutor:
         raw = torch.from_numpy(allt.view(np.uint8).copy())
         self.d_tasks = raw.to(dev) if len(allt) else torch.empty(32, dtype=torch.uint8, device=dev)
         self.h_owner: Optional[np.ndarray] = None
+        # ZeRO-2: the partition size of each param's group, 0 for groups on
+        # another communicator (they keep AllReduce)
+        psize = np.zeros(max(self.P, 1), np.int64)
+        for g in range(self.G):
+            b, e = self.group_begin[g], self.group_begin[g + 1]
+            elig = (self.group_comm_size[g] == W and
+                    all(int(self.group_rank_to_global[g, i]) == i for i in range(W)))
+            if elig:
+                T = int(sum(int(n) for n in list(numel)[b:e]))
+                psize[b:e] = -(-T // self.group_parts[g])
+        self.h_psize = psize[:self.P]
+        self.d_psize = torch.from_numpy(psize).to(dev)
 
     def build_owner_map(self, stream=None) -> None:
         """a1 + a2 on the device (no host synchronization)."""
@@ -90,11 +106,17 @@ class Zero1FlushExecutor:
 
     def flush(self, b: int, slab_in, ld_in: int, slab_out, ld_out: int, stream=None) -> None:
         bk = self.buckets[b]
-        owner = self.d_owner if self.reduce_to_owner else None
-        dc.dc_flush_bucket(self.W, self.dtype, slab_in, ld_in, slab_out, ld_out, bk.col, bk.numel,
-                           self.task_table(b), len(bk.tasks), owner, self.P, self.comms,
-                           len(self.comms), self.pre_div, stream)
-        if self.reduce_probe and self.flushes < PROBE_FLUSHES:
+        if self.zero2:
+            dc.dc_flush_bucket_zero2(self.W, self.dtype, slab_in, ld_in, slab_out, ld_out, bk.col,
+                                     bk.numel, self.task_table(b), len(bk.tasks), self.d_flat,
+                                     self.d_psize, self.P, self.comms, len(self.comms),
+                                     self.pre_div, stream)
+        else:
+            owner = self.d_owner if self.reduce_to_owner else None
+            dc.dc_flush_bucket(self.W, self.dtype, slab_in, ld_in, slab_out, ld_out, bk.col,
+                               bk.numel, self.task_table(b), len(bk.tasks), owner, self.P,
+                               self.comms, len(self.comms), self.pre_div, stream)
+        if self.reduce_probe and not self.zero2 and self.flushes < PROBE_FLUSHES:
             self.log(self.probe_line(b, self.flushes))
         self.flushes += 1
 
@@ -119,7 +141,7 @@ class Zero1FlushExecutor:
 
 
 def from_workload(w, reduce_to_owner: bool, reduce_probe: bool = False, device: str = "cuda",
-                  log=print) -> Zero1FlushExecutor:
+                  log=print, zero2: bool = False) -> Zero1FlushExecutor:
     """Executor for a synthetic flush workload description (duck-typed: the
     fields of synth.workloads.FlushWorkload)."""
     buckets = [BucketSpec(b.col, b.numel, [(t.offset, t.numel, t.param, t.comm) for t in b.tasks])
@@ -128,4 +150,5 @@ def from_workload(w, reduce_to_owner: bool, reduce_probe: bool = False, device: 
     return Zero1FlushExecutor(
         w.W, w.dtype, w.numel, w.group_begin, w.group_parts(), comm_sizes,
         w.group_rank_to_global(), [(c.size, c.stride) for c in w.comms], buckets, w.pre_div,
-        reduce_to_owner=reduce_to_owner, reduce_probe=reduce_probe, device=device, log=log)
+        reduce_to_owner=reduce_to_owner, reduce_probe=reduce_probe, device=device, log=log,
+        zero2=zero2)

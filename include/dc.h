@@ -208,6 +208,26 @@ dc_status dc_flush_bucket(int32_t W, int32_t dtype, const void* slab_in, int64_t
                           const int32_t* owner, int32_t num_params, const dc_comm* comms,
                           int32_t num_comms, int32_t pre_div, void* stream);
 
+/* ZeRO-2 owner path ([DS] "Follow-up": ZeRO-2 keeps real per-rank buffers at
+ * offsets, so the reduce-to-owner optimization extends to every piece of a
+ * parameter).  Same fold as dc_flush_bucket, but on the data-parallel comm
+ * (comm 0) every element goes to the rank whose optimizer partition holds it:
+ * element e of a task of param i sits at flat position flat_offset[i] + e of
+ * its group and belongs to partition floor((flat_offset[i] + e) /
+ * part_size[i]); the sum is written to that row only.  A task whose param has
+ * part_size 0 (a group on another communicator), or any task on another
+ * comm, AllReduces within its blocks as in dc_flush_bucket.
+ *   flat_offset   device int64[num_params]: dc_partition_ids' flat offsets
+ *   part_size     device int64[num_params]: S of the param's group, or 0
+ * Other arguments, checks and guarantees as in dc_flush_bucket (a partition
+ * index outside [0, W) means AllReduce for that element). */
+dc_status dc_flush_bucket_zero2(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                                void* slab_out, int64_t ld_out, int64_t bucket_col,
+                                int64_t bucket_numel, const dc_task* tasks, int32_t num_tasks,
+                                const int64_t* flat_offset, const int64_t* part_size,
+                                int32_t num_params, const dc_comm* comms, int32_t num_comms,
+                                int32_t pre_div, void* stream);
+
 /* a7. Probe counts of one flush ([DS] "reduce_probe"), on the host from
  * metadata only (no device access, no synchronization).  tasks, owner (or
  * NULL for the empty map), pid_offsets/pids (the CSR of dc_partition_ids)
@@ -264,6 +284,25 @@ dc_status dc_accumulate(int32_t rows, const float* x, int64_t ld_x, float* acc, 
  *   out, ld_out   device [out_rows, ld_out] fp32; may equal acc (same ld) */
 dc_status dc_deferred_reduce(int32_t W, const float* acc, int64_t ld_acc, float* out,
                              int64_t ld_out, int64_t M, int32_t out_rows, void* stream);
+
+/* a10 + a11 fused for the last micro-batch of a step: the same fp32
+ * operations as dc_accumulate followed by dc_deferred_reduce, in one pass
+ * (bit-identical results), without writing the accumulator and reading it
+ * back ([MT] What: the accumulated partial sums feed the single reduce in
+ * update()).  For every j < M:
+ *   a_r = init ? +0.0f + x[r][j] : acc[r][j] + x[r][j]      r < W
+ *   acc[r][j] = a_r                      only when keep_acc = 1
+ *   out[i][j] = fold over r = 0..W-1 of a_r                  i < out_rows
+ *   x, ld_x       device [W, ld_x] fp32
+ *   acc, ld_acc   device [W, ld_acc] fp32 (not read when init = 1); may
+ *                 equal x (same ld)
+ *   out, ld_out   device [out_rows, ld_out] fp32, out_rows 1 or W; may equal
+ *                 acc (same ld) only when keep_acc = 0; must not overlap x
+ * Algorithmic bytes: W*M*4 read of x, W*M*4 read of acc unless init,
+ * W*M*4 written to acc if keep_acc, out_rows*M*4 written. */
+dc_status dc_accumulate_reduce(int32_t W, const float* x, int64_t ld_x, float* acc, int64_t ld_acc,
+                               int32_t init, int32_t keep_acc, float* out, int64_t ld_out,
+                               int32_t out_rows, int64_t M, void* stream);
 
 /* fp32 -> bf16 with the rounding the flush uses (round to nearest even, NaN
  * -> 0x7FC0|sign), n elements, device arrays; a self-check of the

@@ -45,6 +45,10 @@ def load_library(path):
                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp, _vp,
                                _vp, _vp, _vp, ctypes.c_int32]
     L.or_flush.restype = None
+    L.or_flush_zero2.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64, _vp,
+                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _vp, _vp, ctypes.c_int32]
+    L.or_flush_zero2.restype = None
     L.or_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _vp, _vp, _vp, _vp]
     L.or_probe.restype = None
@@ -162,6 +166,22 @@ def flush(W, dtype, slab_in, slab_out, bucket_col, t_off, t_numel, t_param, t_co
     lib().or_flush(W, dtype, _p(slab_in), slab_in.shape[1], _p(slab_out), slab_out.shape[1],
                    bucket_col, len(t_off), _p(t_off), _p(t_numel), _p(t_param), _p(t_comm),
                    _p(ow), _p(cs), _p(cst), pre_div)
+    return slab_out
+
+
+def flush_zero2(W, dtype, slab_in, slab_out, bucket_col, t_off, t_numel, t_param, t_comm,
+                flat_offset, part_size, comm_size, comm_stride, pre_div):
+    """ZeRO-2 flush, in place on slab_out.  part_size[p] = the partition size
+    of param p's group, 0 for params that keep AllReduce."""
+    slab_in = _slab(slab_in, dtype)
+    slab_out = _slab(slab_out, dtype)
+    t_off, t_numel = _c(t_off, np.int64), _c(t_numel, np.int64)
+    t_param, t_comm = _c(t_param, np.int32), _c(t_comm, np.int32)
+    fo, ps = _c(flat_offset, np.int64), _c(part_size, np.int64)
+    cs, cst = _c(comm_size, np.int32), _c(comm_stride, np.int32)
+    lib().or_flush_zero2(W, dtype, _p(slab_in), slab_in.shape[1], _p(slab_out), slab_out.shape[1],
+                         bucket_col, len(t_off), _p(t_off), _p(t_numel), _p(t_param), _p(t_comm),
+                         _p(fo), _p(ps), _p(cs), _p(cst), pre_div)
     return slab_out
 
 

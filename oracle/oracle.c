@@ -206,6 +206,42 @@ void or_flush(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out
   }
 }
 
+/* ZeRO-2 owner path ([DS] "Follow-up": ZeRO-2 keeps real per-rank buffers at
+ * offsets, so the same optimization applies to every piece of a parameter).
+ * Element e of a task on the data-parallel comm whose group is partitioned
+ * (part_size[param] = S > 0) lies at flat position a + e of its group, where
+ * a = flat_offset[param]; it belongs to partition floor((a + e) / S), and the
+ * sum is written to that rank only.  Tasks on other communicators, or with
+ * S = 0, AllReduce within their blocks exactly as in or_flush. */
+void or_flush_zero2(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                    int64_t ld_out, int64_t bucket_col, int32_t n_tasks, const int64_t* t_off,
+                    const int64_t* t_numel, const int32_t* t_param, const int32_t* t_comm,
+                    const int64_t* flat_offset, const int64_t* part_size,
+                    const int32_t* comm_size, const int32_t* comm_stride, int32_t pre_div) {
+  for (int32_t t = 0; t < n_tasks; ++t) {
+    int c = comm_size[t_comm[t]];
+    int s = comm_stride[t_comm[t]];
+    int nb = W / c;
+    int64_t S = t_comm[t] == 0 ? part_size[t_param[t]] : 0;
+    int64_t a = flat_offset[t_param[t]];
+    int64_t start = bucket_col + t_off[t];
+    for (int64_t j = start; j < start + t_numel[t]; ++j) {
+      for (int b = 0; b < nb; ++b) {
+        float acc = 0.0f;
+        for (int i = 0; i < c; ++i) {
+          float v = contribution(dtype, load_val(dtype, in, ld_in, member(b, i, c, s), j), pre_div, c);
+          acc = (i == 0) ? v : acc + v;
+        }
+        if (S > 0) {
+          store_val(dtype, out, ld_out, (a + (j - start)) / S, j, acc);
+        } else {
+          for (int i = 0; i < c; ++i) store_val(dtype, out, ld_out, member(b, i, c, s), j, acc);
+        }
+      }
+    }
+  }
+}
+
 /* a7. Probe ([DS] problem statement probe line; "reduce_probe").  Host-only
  * bookkeeping from metadata.  Holders of a parameter: the ranks whose
  * partition appears in its partition list (for a sub-communicator group,

@@ -87,6 +87,26 @@ def oracle_flush_bucket(w, b, slab_in, slab_out, owner):
                  [c.size for c in w.comms], [c.stride for c in w.comms], w.pre_div)
 
 
+def psize_per_param(w):
+    """ZeRO-2 partition size of each param's group (0 off the DP comm)."""
+    flat, ps, off, pids = oracle.partition_ids(w.numel, w.group_begin, w.group_parts())
+    comm_sizes = [w.comms[c].size for c in w.group_comm]
+    elig = oracle.group_eligible(w.W, comm_sizes, w.group_rank_to_global())
+    out = np.zeros(w.P, np.int64)
+    for g in range(w.G):
+        if elig[g]:
+            out[w.group_begin[g]:w.group_begin[g + 1]] = ps[g]
+    return flat, out
+
+
+def oracle_flush_bucket_zero2(w, b, slab_in, slab_out, flat, psize):
+    bk = w.buckets[b]
+    oracle.flush_zero2(w.W, w.dtype, slab_in, slab_out, bk.col, [t.offset for t in bk.tasks],
+                       [t.numel for t in bk.tasks], [t.param for t in bk.tasks],
+                       [t.comm for t in bk.tasks], flat, psize, [c.size for c in w.comms],
+                       [c.stride for c in w.comms], w.pre_div)
+
+
 def sample_columns(w, per_bucket=64, seed=0):
     """Columns to check in a full-size flush: both ends of every task in a
     sample of tasks, the bucket edges, and random interior columns."""
@@ -105,10 +125,11 @@ def sample_columns(w, per_bucket=64, seed=0):
     return np.array(sorted(c for c in cols if 0 <= c < w.total), np.int64)
 
 
-def oracle_sampled_flush(w, cols, owner):
+def oracle_sampled_flush(w, cols, owner, zero2=False):
     """Oracle outputs [W, len(cols)] of the flush at the given slab columns,
     from host-generated inputs of just those columns (each column becomes a
-    one-column task of its parameter)."""
+    one-column task of its parameter; under ZeRO-2 the task's flat offset is
+    moved to that column's position in the param)."""
     W = w.W
     n = len(cols)
     scale = w.scale
@@ -124,7 +145,7 @@ def oracle_sampled_flush(w, cols, owner):
     else:
         out.view(np.uint32)[:] = SENTINEL32
     # map every column to its task
-    t_param, t_comm = [], []
+    t_param, t_comm, t_pos = [], [], []
     starts = [bk.col for bk in w.buckets]
     for c in cols:
         b = int(np.searchsorted(starts, c, side="right")) - 1
@@ -136,6 +157,16 @@ def oracle_sampled_flush(w, cols, owner):
             k -= 1
         t_param.append(bk.tasks[k].param)
         t_comm.append(bk.tasks[k].comm)
-    oracle.flush(W, w.dtype, slab, out, 0, np.arange(n), np.ones(n), t_param, t_comm, owner,
-                 [c.size for c in w.comms], [c.stride for c in w.comms], w.pre_div)
+        t_pos.append(rel - bk.tasks[k].offset)
+    if zero2:
+        flat, psize = psize_per_param(w)
+        # one pseudo-param per sampled column, at its flat position
+        sflat = np.array([flat[p] + e for p, e in zip(t_param, t_pos)], np.int64)
+        spsize = np.array([psize[p] for p in t_param], np.int64)
+        oracle.flush_zero2(W, w.dtype, slab, out, 0, np.arange(n), np.ones(n), np.arange(n),
+                           t_comm, sflat, spsize, [c.size for c in w.comms],
+                           [c.stride for c in w.comms], w.pre_div)
+    else:
+        oracle.flush(W, w.dtype, slab, out, 0, np.arange(n), np.ones(n), t_param, t_comm, owner,
+                     [c.size for c in w.comms], [c.stride for c in w.comms], w.pre_div)
     return out[:, :n]

@@ -501,6 +501,71 @@ def pin_owner_path_equivalences():
         assert np.array_equal(out_bits(dtype, ar[:, T:]), out_bits(dtype, sentinel[:, T:]))
 
 
+def pin_zero2_routing():
+    """ZeRO-2 owner path ([DS] Follow-up): every element of a data-parallel
+    task is written to exactly one row, the rank whose partition holds that
+    element (brute force: cumulative sizes, partition = floor(position / S)),
+    with the AllReduce value; a param inside one partition matches the ZeRO-1
+    owner path; sub-communicator tasks match AllReduce."""
+    rng = random.Random(81)
+    for trial in range(30):
+        W = rng.choice([2, 4, 8])
+        dtype = rng.choice([BF16, F32])
+        g0 = [rng.choice([0, 1, 3, 7, 20, 33, 64]) for _ in range(rng.randint(2, 14))]
+        g1 = [rng.choice([0, 2, 5, 11]) for _ in range(rng.randint(0, 6))]
+        sizes = g0 + g1
+        P = len(sizes)
+        gb = [0, len(g0), P]
+        sub = W // 2
+        comm_size, comm_stride = [W, sub], [1, 1]
+        gcomm = [0, 1]
+        parts = [W, sub]
+        flat, ps, off, pids = oracle.partition_ids(sizes, gb, parts)
+        elig = oracle.group_eligible(W, [W, sub], [list(range(W)), list(range(sub)) + [-1] * (W - sub)])
+        owner, _ = oracle.owner_map(off, pids, gb, elig)
+        part_size = np.array([ps[0] if p < len(g0) else 0 for p in range(P)], np.int64)
+        arrival = list(range(P - 1, -1, -1))
+        t_numel = [sizes[p] for p in arrival]
+        t_off = np.concatenate([[0], np.cumsum(t_numel)[:-1]]).astype(np.int64) if P else []
+        t_comm = [0 if p < len(g0) else 1 for p in arrival]
+        T = sum(sizes)
+        ld = max(8, -(-T // 8) * 8)
+        rows = random_bits(rng, dtype, (W, ld), wide=False)
+        sentinel = 0x7E7E if dtype == BF16 else 0x7E7E7E7E
+        def blank():
+            o = np.zeros_like(rows)
+            out_bits(dtype, o)  # view check
+            if dtype == BF16:
+                o[:] = sentinel
+            else:
+                o.view(np.uint32)[:] = sentinel
+            return o
+        z2 = blank()
+        oracle.flush_zero2(W, dtype, rows, z2, 0, t_off, t_numel, arrival, t_comm, flat, part_size,
+                           comm_size, comm_stride, 1)
+        ar = blank()
+        oracle.flush(W, dtype, rows, ar, 0, t_off, t_numel, arrival, t_comm, None, comm_size,
+                     comm_stride, 1)
+        z1 = blank()
+        oracle.flush(W, dtype, rows, z1, 0, t_off, t_numel, arrival, t_comm, owner, comm_size,
+                     comm_stride, 1)
+        zb, ab, ob = out_bits(dtype, z2), out_bits(dtype, ar), out_bits(dtype, z1)
+        S = -(-sum(g0) // W) if sum(g0) else 0
+        pos0 = np.concatenate([[0], np.cumsum(g0)]) if g0 else [0]
+        for t, p in enumerate(arrival):
+            cols = range(int(t_off[t]), int(t_off[t]) + sizes[p])
+            if p < len(g0):
+                for e, j in enumerate(cols):
+                    q = (int(pos0[p]) + e) // S
+                    written = [r for r in range(W) if zb[r, j] != sentinel]
+                    assert written == [q], (trial, p, e, written, q)
+                    assert zb[q, j] == ab[q, j]
+                if len(pids[off[p]:off[p + 1]]) == 1:
+                    assert np.array_equal(zb[:, list(cols)], ob[:, list(cols)])
+            else:
+                assert np.array_equal(zb[:, list(cols)], ab[:, list(cols)])
+
+
 # ---------------------------------------------------------------------------
 # ring and recursive-doubling all-gather
 # ---------------------------------------------------------------------------
@@ -711,7 +776,7 @@ ALL_PINS = [
     pin_fold_identical_rows, pin_fold_brute_force, pin_fold_error_bound,
     pin_prediv_non_power_of_two, pin_reduce_scatter_all_gather, pin_partition_brute_force,
     pin_owner_rules, pin_group_eligibility, pin_probe_printed_example, pin_ratio_printed_example,
-    pin_probe_closed_forms, pin_owner_path_equivalences, pin_ring_table, pin_ring_closed_form,
+    pin_probe_closed_forms, pin_owner_path_equivalences, pin_zero2_routing, pin_ring_table, pin_ring_closed_form,
     pin_rd_table, pin_ring_step_replay, pin_deferred_ga1_identity,
     pin_accumulate_zero_start, pin_deferred_exact_reassociation, pin_deferred_tolerance, pin_deferred_restore,
     pin_deferred_round_trip,

@@ -90,6 +90,12 @@ def test_other_argument_checks():
     expect(dc.DC_ERR_ARG, dc.dc_deferred_reduce, 4, FAKE, 64, FAKE << 1, 64, 64, 2, stream=0)
     expect(dc.DC_ERR_ARG, dc.dc_deferred_reduce, 4, FAKE, 64, FAKE + 128, 64, 64, 1, stream=0)
     expect(dc.DC_ERR_SHAPE, dc.dc_stream_copy, FAKE, FAKE << 1, 100, stream=0)
+    ar = dc.dc_accumulate_reduce
+    expect(dc.DC_ERR_ARG, ar, 4, FAKE, 64, FAKE << 1, 64, 0, 0, FAKE << 2, 64, 2, 64, stream=0)
+    expect(dc.DC_ERR_ARG, ar, 4, FAKE, 64, FAKE << 1, 64, 2, 0, FAKE << 2, 64, 1, 64, stream=0)
+    expect(dc.DC_ERR_ARG, ar, 4, FAKE, 64, FAKE << 1, 64, 0, 1, FAKE << 1, 64, 4, 64, stream=0)
+    expect(dc.DC_ERR_ARG, ar, 4, FAKE, 64, FAKE << 1, 64, 0, 0, FAKE + 256, 64, 1, 64, stream=0)
+    expect(dc.DC_ERR_ALIGN, ar, 4, FAKE, 62, FAKE << 1, 64, 0, 0, FAKE << 2, 64, 1, 60, stream=0)
     expect(dc.DC_ERR_UNSUPPORTED, dc.dc_stream_rows, FAKE, 64, 3, FAKE << 1, 64, 1, 64, stream=0)
     expect(dc.DC_ERR_UNSUPPORTED, dc.dc_stream_rows, FAKE, 64, 8, FAKE << 1, 64, 2, 64, stream=0)
     expect(dc.DC_ERR_SHAPE, dc.dc_stream_rows, FAKE, 32, 8, FAKE << 1, 64, 1, 64, stream=0)

@@ -91,16 +91,17 @@ def test_partition_ids_and_owner_map(w):
     assert np.array_equal(ex.h_counts, counts)
 
 
-def flush_case(w, reduce_to_owner, in_place=False, probe=True):
+def flush_case(w, reduce_to_owner, in_place=False, probe=True, zero2=False):
     """Run every bucket of w on the GPU and on the oracle; compare all of the
     output slab bit for bit, and the probe records."""
     import torch
-    U.say("flush", w.name, "owner" if reduce_to_owner else "allreduce", "in-place" if in_place else "")
+    U.say("flush", w.name, "zero2" if zero2 else ("owner" if reduce_to_owner else "allreduce"),
+          "in-place" if in_place else "")
     scale = w.scale
     ld = w.ld
     x = U.gen_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, scale)
     y = x if in_place else U.empty_slab(w.dtype, w.W, ld)
-    ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner)
+    ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner, zero2=zero2)
     ex.build_owner_map()
     for b in range(len(w.buckets)):
         ex.flush(b, x, ld, y, ld)
@@ -111,8 +112,15 @@ def flush_case(w, reduce_to_owner, in_place=False, probe=True):
     if not in_place:
         U.bits(hout, w.dtype)[:] = U.SENTINEL16 if w.dtype == wl.DT_BF16 else U.SENTINEL32
     _, _, off, pids, owner, _ = U.oracle_owner(w)
-    for b in range(len(w.buckets)):
-        U.oracle_flush_bucket(w, b, hin, hout, owner if reduce_to_owner else None)
+    if zero2:
+        flat, psize = U.psize_per_param(w)
+        assert np.array_equal(ex.h_psize, psize)
+        for b in range(len(w.buckets)):
+            U.oracle_flush_bucket_zero2(w, b, hin, hout, flat, psize)
+        probe = False
+    else:
+        for b in range(len(w.buckets)):
+            U.oracle_flush_bucket(w, b, hin, hout, owner if reduce_to_owner else None)
     gb, hb = U.bits(got, w.dtype), U.bits(hout, w.dtype)
     bad = np.argwhere(gb != hb)
     assert len(bad) == 0, (f"{len(bad)} mismatches; first (row, col): {bad[:5].tolist()} "
@@ -179,6 +187,18 @@ def test_flush_small(w, owner):
 @pytest.mark.parametrize("w", small_flush_workloads()[::5], ids=lambda w: w.name)
 def test_flush_in_place(w):
     flush_case(w, True, in_place=True, probe=False)
+
+
+@pytest.mark.parametrize("w", small_flush_workloads() + [wl.tiny_flush()], ids=lambda w: w.name)
+def test_flush_zero2_small(w):
+    """ZeRO-2 owner path: every element of a data-parallel task goes to the
+    rank of its partition, bit-exact against the oracle."""
+    flush_case(w, False, zero2=True)
+
+
+@pytest.mark.parametrize("w", small_flush_workloads()[1::6], ids=lambda w: w.name)
+def test_flush_zero2_in_place(w):
+    flush_case(w, False, in_place=True, probe=False, zero2=True)
 
 
 def test_flush_unaligned_bucket_start():
@@ -271,24 +291,41 @@ def test_flush_nonfinite_and_subnormal_inputs():
         assert len(bad) == 0, (W, dtype, pre, bad[:4].tolist(), got[tuple(bad[0])], want[tuple(bad[0])])
 
 
-def full_size_flush(w, reduce_to_owner, in_place):
+def full_size_flush(w, reduce_to_owner, in_place, zero2=False):
     import torch
-    U.say("full-size flush", w.name, "owner" if reduce_to_owner else "allreduce",
+    U.say("full-size flush", w.name, "zero2" if zero2 else ("owner" if reduce_to_owner else "allreduce"),
           f"W={w.W} cols={w.total} buckets={len(w.buckets)}")
     ld = w.ld
     x = U.gen_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, w.scale)
     y = x if in_place else U.empty_slab(w.dtype, w.W, ld)
-    ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner)
+    ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner, zero2=zero2)
     ex.build_owner_map()
     for b in range(len(w.buckets)):
         ex.flush(b, x, ld, y, ld)
     torch.cuda.synchronize()
     cols = U.sample_columns(w)
+    if zero2:
+        # add the columns on both sides of every partition boundary
+        _, psize = U.psize_per_param(w)
+        flat, _ = U.psize_per_param(w)
+        extra = []
+        for bk in w.buckets:
+            for t in bk.tasks:
+                S = int(psize[t.param])
+                if S <= 0 or t.numel == 0:
+                    continue
+                a = int(flat[t.param])
+                q = a // S + 1
+                while q * S < a + t.numel:
+                    e = q * S - a
+                    extra += [bk.col + t.offset + e - 1, bk.col + t.offset + e]
+                    q += 1
+        cols = np.unique(np.concatenate([cols, np.array(extra, np.int64)]))
     U.say("  sampled columns", len(cols))
     got = y[:, torch.from_numpy(cols).cuda()].cpu().numpy()
     got = got.view(np.uint16) if w.dtype == wl.DT_BF16 else got.view(np.uint32)
     _, _, _, _, owner, _ = U.oracle_owner(w)
-    want = U.oracle_sampled_flush(w, cols, owner if reduce_to_owner else None)
+    want = U.oracle_sampled_flush(w, cols, owner if reduce_to_owner else None, zero2=zero2)
     if in_place:
         # rows the flush does not write keep the input
         inp = np.stack([synth.gather(w.dtype, w.value_seed, r, w.scale, cols) for r in range(w.W)])
@@ -310,3 +347,11 @@ def test_flush_w8_402m_full_size(owner):
 
 def test_flush_w16_mixed_1_2b_full_size_in_place():
     full_size_flush(wl.mixed_flush_w16(), True, in_place=True)
+
+
+def test_flush_zero2_w8_402m_full_size():
+    full_size_flush(wl.owner_flush_w8(), False, in_place=False, zero2=True)
+
+
+def test_flush_zero2_w16_mixed_1_2b_full_size_in_place():
+    full_size_flush(wl.mixed_flush_w16(), False, in_place=True, zero2=True)

@@ -239,3 +239,37 @@ def test_stream_rows_reference(R, NW):
     for r in range(NW):
         assert np.array_equal(got[r, :nvec * 4], want)
     assert np.all(got[NW:, :] == U.SENTINEL32) and np.all(got[:, nvec * 4:] == U.SENTINEL32)
+
+
+AR_CASES = [(4, 1003, 0, 1, 4, "none"), (4, 1003, 1, 0, 1, "none"), (3, 517, 0, 0, 3, "out=acc"),
+            (16, 4100, 0, 1, 1, "none"), (8, 2048, 1, 1, 8, "x=acc"), (5, 33, 0, 1, 5, "none"),
+            (4, 0, 0, 0, 1, "none")]
+
+
+@pytest.mark.parametrize("W,M,init,keep,out_rows,alias", AR_CASES, ids=lambda v: str(v))
+def test_accumulate_reduce_equals_two_steps(W, M, init, keep, out_rows, alias):
+    """The fused last-micro-batch kernel against the oracle's accumulate
+    followed by its deferred reduce: bit-exact outputs and accumulator."""
+    import torch
+    ld = wl.round_up(max(M, 1), 64)
+    scale = wl.sigma_scale(1e-3)
+    x = U.gen_slab(wl.DT_F32, W, ld, M, 31, 0, scale).view(torch.float32)
+    acc = U.gen_slab(wl.DT_F32, W, ld, M, 32, 0, scale).view(torch.float32)
+    hx = U.host_slab(wl.DT_F32, W, ld, M, 31, 0, scale)
+    hacc = U.host_slab(wl.DT_F32, W, ld, M, 32, 0, scale)
+    if alias == "x=acc":
+        x, hx = acc, hacc
+    out = acc if alias == "out=acc" else U.empty_slab(wl.DT_F32, out_rows, ld).view(torch.float32)
+    dc.dc_accumulate_reduce(W, x, ld, acc, ld, init, keep, out, ld, out_rows, M)
+    torch.cuda.synchronize()
+    a2 = hacc.copy()
+    oracle.accumulate(W, hx.copy() if alias == "x=acc" else hx, a2, M, init)
+    want = np.full((out_rows, ld), np.uint32(U.SENTINEL32)).view(np.float32)
+    oracle.deferred_reduce(W, a2, want, M, out_rows)
+    got = out.cpu().numpy()
+    if alias == "out=acc":
+        assert np.array_equal(got[:out_rows, :M].view(np.uint32), want[:, :M].view(np.uint32))
+    else:
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+        wacc = a2 if keep else hacc
+        assert np.array_equal(acc.cpu().numpy().view(np.uint32), wacc.view(np.uint32))
