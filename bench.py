@@ -347,6 +347,72 @@ def bench_rs_ag(args):
     return w.name, ms_step, (rs_b + 2 * ag_b) / (ms_step / 1e3) / 1e9, roofline, extra, "bf16"
 
 
+def bench_relayout_rs(args):
+    """Every bucket of the W=8 402.8M workload relaid by destination rank and
+    reduce-scattered with variable shards (the issue's reduce-scatter
+    alternative): one step = relayout + reduce-scatter-v of every bucket."""
+    import torch
+    import synth
+    from gradient_reduction_amd import dc, executor
+    from synth import workloads as wl
+    w = wl.owner_flush_w8()
+    W, ld, b = w.W, w.ld, w.elem_bytes()
+    dev = torch.device("cuda:0")
+    x = torch.empty((W, ld), dtype=torch.int16, device=dev)
+    synth.fill_slab_device(0, w.value_seed, 0, w.scale, W, ld, w.total, x.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream)
+    ex = executor.from_workload(w, reduce_to_owner=False, log=log, zero2=True)
+    ex.build_owner_map()
+    flat = ex.d_flat[:w.P].cpu().numpy()
+    plans = []
+    for bk in w.buckets:
+        t = dc.tasks_array([(k.offset, k.numel, k.param, k.comm) for k in bk.tasks])
+        pieces, seg = dc.dc_plan_relayout(W, t, len(t), flat, ex.h_psize, w.P)
+        plans.append((torch.from_numpy(pieces.view(np.uint8).copy()).to(dev), len(pieces), seg))
+    maxn = max(int(p[2][-1]) for p in plans)
+    maxseg = max(int(max(p[2][1:] - p[2][:-1])) for p in plans)
+    ld_r, ld_s = wl.round_up(maxn, 64), wl.round_up(maxseg, 64)
+    relaid = torch.empty((W, ld_r), dtype=torch.int16, device=dev)
+    shards = torch.empty((W, ld_s), dtype=torch.int16, device=dev)
+    nb = len(w.buckets)
+    rl_b = [2 * W * int(p[2][-1]) * b + 32 * p[1] for p in plans]
+    rs_b = [W * int(p[2][-1]) * b + int(p[2][-1]) * b for p in plans]
+
+    def step(tm=None):
+        for k, bk in enumerate(w.buckets):
+            d_pieces, npc, seg = plans[k]
+            if tm: tm.ev[2 * k][0].record()
+            dc.dc_relayout_bucket(W, 0, x, ld, relaid, ld_r, bk.col, bk.numel, d_pieces, npc,
+                                  int(seg[-1]))
+            if tm: tm.ev[2 * k][1].record(); tm.ev[2 * k + 1][0].record()
+            dc.dc_reduce_scatter_v(W, 0, relaid, ld_r, shards, ld_s, seg, w.pre_div)
+            if tm: tm.ev[2 * k + 1][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [Timer(torch, 2 * nb) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for k in range(args.steps):
+        step(timers[k])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    kern = np.array([tm.ms() for tm in timers]).mean(axis=0)
+    rl_gbs = sum(rl_b) / (kern[0::2].sum() / 1e3) / 1e9
+    rs_gbs = sum(rs_b) / (kern[1::2].sum() / 1e3) / 1e9
+    log(f"[bench] relayout + reduce-scatter-v: step {ms_step:.3f} ms; relayout {rl_gbs:.1f} GB/s "
+        f"({kern[0::2].sum():.3f} ms); reduce-scatter-v {rs_gbs:.1f} GB/s ({kern[1::2].sum():.3f} ms)")
+    roofline = {"bound": "hbm", "achieved": round(rs_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(rs_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_rs_v",
+                "launch_ms_avg": round(float(kern[1::2].mean()), 4),
+                "bytes_per_launch_avg": int(np.mean(rs_b))}
+    extra = {"relayout_gbs": round(rl_gbs, 1), "relayout_ms": round(float(kern[0::2].sum()), 4),
+             "reduce_scatter_v_ms": round(float(kern[1::2].sum()), 4)}
+    return w.name, ms_step, (sum(rl_b) + sum(rs_b)) / (ms_step / 1e3) / 1e9, roofline, extra, "bf16"
+
+
 def copy_calibration():
     """Achievable bandwidth of a plain 16-byte streaming copy (1 GiB)."""
     import torch
@@ -373,7 +439,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="owner_w8",
                     choices=["owner_w8", "allreduce_w8", "zero2_w8", "mixed", "zero2_mixed",
-                             "deferred", "rs_ag", "tiny"])
+                             "deferred", "rs_ag", "relayout_rs_w8", "tiny"])
     ap.add_argument("--ga", type=int, default=8)
     ap.add_argument("--fused", action="store_true",
                     help="deferred workload: fuse the last accumulate into the reduce")
@@ -415,6 +481,10 @@ def main():
         config = {"workload": name, "W": 4, "K": args.ga,
                   "step": ("K-1 accumulates + fused accumulate-reduce" if args.fused
                            else "K accumulates + deferred reduce")}
+    elif args.workload == "relayout_rs_w8":
+        name, ms, value, roof, extra, dtype = bench_relayout_rs(args)
+        config = {"workload": name, "W": 8,
+                  "step": "relayout by destination + reduce-scatter-v of every bucket"}
     else:
         name, ms, value, roof, extra, dtype = bench_rs_ag(args)
         config = {"workload": name, "W": 8, "step": "reduce-scatter + all-gather rank + all-gather ring"}

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -312,6 +313,104 @@ dc_status dc_probe_flush(int32_t W, int32_t dtype, const dc_task* tasks, int32_t
   }
   for (int r = 0; r < W; ++r) out->discarded[r] = out->written[r] - out->kept[r];
   return ok();
+}
+
+dc_status dc_plan_relayout(int32_t W, const dc_task* tasks, int32_t num_tasks,
+                           const int64_t* flat_offset, const int64_t* part_size,
+                           int32_t num_params, dc_piece* pieces, int32_t pieces_capacity,
+                           int32_t* num_pieces, int64_t* seg_start) {
+  dc_status st;
+  if ((st = check_w(W))) return st;
+  if (num_tasks < 0 || num_params < 0) return fail(DC_ERR_ARG, "num_tasks or num_params < 0");
+  if (seg_start == nullptr || num_pieces == nullptr) return fail(DC_ERR_NULL, "seg_start or num_pieces is NULL");
+  if (num_tasks > 0 && (tasks == nullptr || flat_offset == nullptr || part_size == nullptr))
+    return fail(DC_ERR_NULL, "tasks, flat_offset or part_size is NULL");
+  // pass 1: segment sizes and the piece count; pass 2: the pieces, each at
+  // its segment's cursor
+  std::vector<int64_t> count(W, 0), cur(W, 0);
+  int64_t total = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) {
+      seg_start[0] = 0;
+      for (int q = 0; q < W; ++q) seg_start[q + 1] = seg_start[q] + count[q];
+      *num_pieces = (int32_t)total;
+      if (pieces == nullptr) return ok();  // size query
+      if (total > pieces_capacity)
+        return fail(DC_ERR_SHAPE, "pieces_capacity=%d < %lld pieces", pieces_capacity, (long long)total);
+      for (int q = 0; q < W; ++q) cur[q] = seg_start[q];
+    }
+    int64_t np = 0;
+    for (int32_t t = 0; t < num_tasks; ++t) {
+      const dc_task& k = tasks[t];
+      if (k.param < 0 || k.param >= num_params || k.numel < 0)
+        return fail(DC_ERR_TASKS, "task %d has an out-of-range param or numel", t);
+      const int64_t S = k.comm == 0 ? part_size[k.param] : 0;
+      if (S <= 0 || k.numel == 0) continue;
+      const int64_t a = flat_offset[k.param];
+      const int64_t q0 = a / S, q1 = (a + k.numel - 1) / S;
+      if (a < 0 || q1 >= W)
+        return fail(DC_ERR_TASKS, "task %d: partitions %lld..%lld outside [0, %d)", t, (long long)q0,
+                    (long long)q1, W);
+      for (int64_t q = q0; q <= q1; ++q) {
+        const int64_t e0 = std::max<int64_t>(0, q * S - a);
+        const int64_t e1 = std::min<int64_t>(k.numel, (q + 1) * S - a);
+        if (pass == 0) {
+          count[q] += e1 - e0;
+        } else {
+          pieces[np] = dc_piece{k.offset + e0, cur[q], e1 - e0, 0};
+          cur[q] += e1 - e0;
+        }
+        ++np;
+      }
+    }
+    if (pass == 0) {
+      total = np;
+      if (total > INT32_MAX) return fail(DC_ERR_SHAPE, "too many pieces");
+    }
+  }
+  std::sort(pieces, pieces + total, [](const dc_piece& x, const dc_piece& y) { return x.dst < y.dst; });
+  return ok();
+}
+
+dc_status dc_relayout_bucket(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                             void* out, int64_t ld_out, int64_t bucket_col, int64_t bucket_numel,
+                             const dc_piece* pieces, int32_t num_pieces, int64_t out_numel,
+                             void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype))) return st;
+  if (bucket_col < 0 || bucket_numel < 0 || out_numel < 0 || num_pieces < 0)
+    return fail(DC_ERR_ARG, "negative bucket_col, bucket_numel, out_numel or num_pieces");
+  if ((st = check_slab("slab_in", slab_in, ld_in, bucket_col + bucket_numel, dtype)) ||
+      (st = check_slab("out", out, ld_out, out_numel, dtype)))
+    return st;
+  if (num_pieces > 0 && pieces == nullptr) return fail(DC_ERR_NULL, "pieces is NULL");
+  const int64_t b = elem_bytes(dtype);
+  if (overlaps(slab_in, W * ld_in * b, out, W * ld_out * b)) return fail(DC_ERR_ARG, "slab_in and out overlap");
+  return hip_status(dc::launch_relayout(W, dtype, slab_in, ld_in, out, ld_out, bucket_col, bucket_numel,
+                                        pieces, num_pieces, out_numel, static_cast<hipStream_t>(stream)),
+                    "relayout launch");
+}
+
+dc_status dc_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                              int64_t ld_out, const int64_t* seg_start, int32_t pre_div,
+                              void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype))) return st;
+  if (seg_start == nullptr) return fail(DC_ERR_NULL, "seg_start is NULL");
+  if (pre_div != 0 && pre_div != 1) return fail(DC_ERR_ARG, "pre_div=%d", pre_div);
+  if (seg_start[0] != 0) return fail(DC_ERR_SHAPE, "seg_start[0] must be 0");
+  int64_t maxlen = 0;
+  for (int q = 0; q < W; ++q) {
+    if (seg_start[q + 1] < seg_start[q]) return fail(DC_ERR_SHAPE, "seg_start decreases at %d", q);
+    maxlen = std::max<int64_t>(maxlen, seg_start[q + 1] - seg_start[q]);
+  }
+  if ((st = check_slab("in", in, ld_in, seg_start[W], dtype)) || (st = check_slab("out", out, ld_out, maxlen, dtype)))
+    return st;
+  const int64_t b = elem_bytes(dtype);
+  if (overlaps(in, W * ld_in * b, out, W * ld_out * b)) return fail(DC_ERR_ARG, "in and out overlap");
+  return hip_status(dc::launch_reduce_scatter_v(W, dtype, in, ld_in, out, ld_out, seg_start, pre_div,
+                                                static_cast<hipStream_t>(stream)),
+                    "reduce-scatter-v launch");
 }
 
 dc_status dc_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,

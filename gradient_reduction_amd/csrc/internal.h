@@ -56,6 +56,15 @@ hipError_t launch_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64
                                  void* out, int64_t ld_out, int64_t M, int32_t pre_div,
                                  hipStream_t stream);
 
+hipError_t launch_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
+                                   void* out, int64_t ld_out, const int64_t* seg_start,
+                                   int32_t pre_div, hipStream_t stream);
+
+hipError_t launch_relayout(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                           int64_t ld_out, int64_t bucket_col, int64_t bucket_numel,
+                           const dc_piece* pieces, int32_t npieces, int64_t out_numel,
+                           hipStream_t stream);
+
 hipError_t launch_all_gather(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
                              int64_t ld_out, int64_t L, int32_t order, int32_t step,
                              hipStream_t stream);

@@ -159,6 +159,40 @@ __global__ __launch_bounds__(kThreads) void k_rs_elem(int32_t W, const void* __r
   }
 }
 
+// Reduce-scatter with variable shards (after a relayout): shard q is
+// columns [seg[q], seg[q+1]) of the input; out[q][k] = fold_r pre(in[r][seg[q]+k]).
+// A shard that starts on a vector boundary takes 16-byte loads; the rest of
+// a shard, or a shard that does not, goes element by element.
+struct SegArgs {
+  int64_t seg[DC_MAX_W + 1];
+};
+
+template <bool BF16, int WT, bool PRE>
+__global__ __launch_bounds__(kThreads) void k_rs_v(int32_t W, const void* __restrict__ in,
+                                                   int64_t ld_in, void* __restrict__ out,
+                                                   int64_t ld_out, SegArgs sa, float inv, float c) {
+  constexpr int E = BF16 ? 8 : 4;
+  const int32_t q = blockIdx.y;
+  const int64_t s0 = sa.seg[q], len = sa.seg[q + 1] - s0;
+  const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (k * E >= len) return;
+  if (s0 % E == 0 && (k + 1) * E <= len) {
+    const u32x4 y = fold_rows<BF16, WT, PRE>(reinterpret_cast<const u32x4*>(in), ld_in / E,
+                                             s0 / E + k, W, inv, c);
+    store16<kNTS>(reinterpret_cast<u32x4*>(out) + q * (ld_out / E) + k, y);
+  } else {
+    const int64_t e1 = min((k + 1) * E, len);
+    for (int64_t e = k * E; e < e1; ++e) {
+      float acc = 0.0f;
+      for (int32_t r = 0; r < W; ++r) {
+        const float v = pre_elem<BF16>(load_elem<BF16>(in, r * ld_in + s0 + e), PRE, inv, c);
+        acc = r == 0 ? v : acc + v;
+      }
+      store_elem<BF16>(out, q * ld_out + e, acc);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // a9. all-gather
 // ---------------------------------------------------------------------------
@@ -415,6 +449,48 @@ hipError_t launch_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64
     hipLaunchKernelGGL(k_rs_elem<false>, grid, dim3(kThreads), 0, stream, W, in, ld_in, out,
                        ld_out, L, pre_div, inv, c);
   return hipGetLastError();
+}
+
+template <bool BF16, bool PRE>
+hipError_t rs_v_w(int32_t W, const void* in, int64_t ld_in, void* out, int64_t ld_out,
+                  const SegArgs& sa, int64_t maxlen, float inv, float c, hipStream_t stream) {
+  constexpr int E = BF16 ? 8 : 4;
+  const dim3 grid((unsigned)((maxlen + (int64_t)kThreads * E - 1) / ((int64_t)kThreads * E)),
+                  (unsigned)W);
+  switch (W) {
+#define DC_RSV_W(w)                                                                          \
+  case w:                                                                                    \
+    hipLaunchKernelGGL((k_rs_v<BF16, w, PRE>), grid, dim3(kThreads), 0, stream, W, in, ld_in, \
+                       out, ld_out, sa, inv, c);                                             \
+    break;
+    DC_RSV_W(1)
+    DC_RSV_W(2)
+    DC_RSV_W(4)
+    DC_RSV_W(8)
+    DC_RSV_W(16)
+#undef DC_RSV_W
+    default:
+      hipLaunchKernelGGL((k_rs_v<BF16, 0, PRE>), grid, dim3(kThreads), 0, stream, W, in, ld_in,
+                         out, ld_out, sa, inv, c);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
+                                   void* out, int64_t ld_out, const int64_t* seg_start,
+                                   int32_t pre_div, hipStream_t stream) {
+  SegArgs sa{};
+  int64_t maxlen = 0;
+  for (int q = 0; q <= W; ++q) sa.seg[q] = seg_start[q];
+  for (int q = 0; q < W; ++q) maxlen = max(maxlen, seg_start[q + 1] - seg_start[q]);
+  if (maxlen == 0) return hipSuccess;
+  float inv, c;
+  reciprocal(W, &inv, &c);
+  if (dtype == DC_BF16)
+    return pre_div ? rs_v_w<true, true>(W, in, ld_in, out, ld_out, sa, maxlen, inv, c, stream)
+                   : rs_v_w<true, false>(W, in, ld_in, out, ld_out, sa, maxlen, inv, c, stream);
+  return pre_div ? rs_v_w<false, true>(W, in, ld_in, out, ld_out, sa, maxlen, inv, c, stream)
+                 : rs_v_w<false, false>(W, in, ld_in, out, ld_out, sa, maxlen, inv, c, stream);
 }
 
 hipError_t launch_all_gather(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,

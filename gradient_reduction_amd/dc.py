@@ -25,6 +25,7 @@ DC_MAX_W, DC_MAX_GROUPS, DC_MAX_COMMS = 64, 64, 8
 TASK_DTYPE = np.dtype([("offset", "<i8"), ("numel", "<i8"), ("param", "<i4"),
                        ("comm", "<i4"), ("reserved", "<i8")])
 COMM_DTYPE = np.dtype([("size", "<i4"), ("stride", "<i4")])
+PIECE_DTYPE = np.dtype([("src", "<i8"), ("dst", "<i8"), ("len", "<i8"), ("reserved", "<i8")])
 
 
 class dc_probe(ctypes.Structure):
@@ -56,6 +57,10 @@ _SIGS = {
     "dc_flush_bucket_zero2": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
                                _i32, _vp, _i32, _i32, _vp], _i32),
     "dc_probe_flush": ([_i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp], _i32),
+    "dc_plan_relayout": ([_i32, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp], _i32),
+    "dc_relayout_bucket": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp],
+                           _i32),
+    "dc_reduce_scatter_v": ([_i32, _i32, _vp, _i64, _vp, _i64, _vp, _i32, _vp], _i32),
     "dc_reduce_scatter": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
     "dc_all_gather": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _i32, _vp], _i32),
     "dc_accumulate": ([_i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
@@ -183,6 +188,36 @@ def dc_probe_flush(W, dtype, tasks, num_tasks, owner, num_params, pid_offsets, p
     _check("dc_probe_flush", lib().dc_probe_flush(W, dtype, tp, num_tasks, op, num_params, po, pp,
                                                   cp, num_comms, pre_div, ctypes.byref(out)))
     return out
+
+
+def dc_plan_relayout(W, tasks, num_tasks, flat_offset, part_size, num_params):
+    """Host only; returns (pieces array, seg_start array).  Asks for the piece
+    count first, then fills an array of that size."""
+    tp, _a = _host(tasks, TASK_DTYPE)
+    fo, _b = _host(flat_offset, np.int64)
+    ps, _c = _host(part_size, np.int64)
+    seg = np.zeros(W + 1, np.int64)
+    n = ctypes.c_int32(0)
+    _check("dc_plan_relayout", lib().dc_plan_relayout(
+        W, tp, num_tasks, fo, ps, num_params, None, 0, ctypes.byref(n), seg.ctypes.data_as(_vp)))
+    pieces = np.zeros(max(n.value, 1), PIECE_DTYPE)
+    _check("dc_plan_relayout", lib().dc_plan_relayout(
+        W, tp, num_tasks, fo, ps, num_params, pieces.ctypes.data_as(_vp), n.value,
+        ctypes.byref(n), seg.ctypes.data_as(_vp)))
+    return pieces[:n.value].copy(), seg
+
+
+def dc_relayout_bucket(W, dtype, slab_in, ld_in, out, ld_out, bucket_col, bucket_numel, pieces,
+                       num_pieces, out_numel, stream=None):
+    _check("dc_relayout_bucket", lib().dc_relayout_bucket(
+        W, dtype, _dev(slab_in), ld_in, _dev(out), ld_out, bucket_col, bucket_numel, _dev(pieces),
+        num_pieces, out_numel, _stream(stream)))
+
+
+def dc_reduce_scatter_v(W, dtype, in_, ld_in, out, ld_out, seg_start, pre_div, stream=None):
+    sp, _a = _host(seg_start, np.int64)
+    _check("dc_reduce_scatter_v", lib().dc_reduce_scatter_v(W, dtype, _dev(in_), ld_in, _dev(out),
+                                                            ld_out, sp, pre_div, _stream(stream)))
 
 
 def dc_reduce_scatter(W, dtype, in_, ld_in, out, ld_out, M, pre_div, stream=None):

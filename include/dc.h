@@ -107,6 +107,15 @@ typedef struct {
   int64_t discarded[DC_MAX_W];
 } dc_probe;
 
+/* One piece of a bucket relayout: bucket columns [src, src+len) move to
+ * relaid columns [dst, dst+len).  32 bytes. */
+typedef struct {
+  int64_t src;
+  int64_t dst;
+  int64_t len;
+  int64_t reserved;
+} dc_piece;
+
 /* Library version string (static storage). */
 const char* dc_version(void);
 
@@ -237,6 +246,53 @@ dc_status dc_probe_flush(int32_t W, int32_t dtype, const dc_task* tasks, int32_t
                          const int32_t* owner, int32_t num_params, const int32_t* pid_offsets,
                          const int32_t* pids, const dc_comm* comms, int32_t num_comms,
                          int32_t pre_div, dc_probe* out);
+
+/* Relayout plan for a reduce-scatter over a bucket ([DS] "Describe
+ * alternatives": a reduce-scatter needs the bucket laid out contiguously by
+ * destination rank).  Every element of a task on the data-parallel comm whose
+ * param has part_size > 0 belongs to partition
+ * q = floor((flat_offset[param] + e) / part_size[param]); segment q of the
+ * relaid bucket holds those elements in bucket order, and the segments follow
+ * each other (q = 0..W-1).  Other tasks are not relaid.  Host only.
+ *   tasks, num_tasks         host dc_task[] of the bucket (as validated by
+ *                            dc_validate_tasks)
+ *   flat_offset, part_size   host int64[num_params] (as for
+ *                            dc_flush_bucket_zero2)
+ *   pieces                   host dc_piece[pieces_capacity] out, sorted by
+ *                            dst; NULL asks for the count only
+ *   num_pieces               out: the number of pieces (at most num_tasks +
+ *                            (W-1) per partitioned group in the bucket)
+ *   seg_start                host int64[W+1] out: segment boundaries
+ * Fewer than num_pieces slots is DC_ERR_SHAPE; a partition index outside
+ * [0, W) is DC_ERR_TASKS. */
+dc_status dc_plan_relayout(int32_t W, const dc_task* tasks, int32_t num_tasks,
+                           const int64_t* flat_offset, const int64_t* part_size,
+                           int32_t num_params, dc_piece* pieces, int32_t pieces_capacity,
+                           int32_t* num_pieces, int64_t* seg_start);
+
+/* Apply a relayout plan to every row: out[r][dst + i] = slab_in[r][bucket_col
+ * + src + i] for each piece and i < len (pure data movement).
+ *   slab_in, ld_in   device [W, ld_in]; the bucket is columns
+ *                    [bucket_col, bucket_col + bucket_numel)
+ *   out, ld_out      device [W, ld_out], ld_out >= out_numel; must not
+ *                    overlap slab_in
+ *   pieces           device dc_piece[num_pieces] sorted by dst
+ * Only columns [0, out_numel) of `out` are written; a piece reaching outside
+ * the bucket or outside [0, out_numel) is clipped, never followed. */
+dc_status dc_relayout_bucket(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                             void* out, int64_t ld_out, int64_t bucket_col, int64_t bucket_numel,
+                             const dc_piece* pieces, int32_t num_pieces, int64_t out_numel,
+                             void* stream);
+
+/* Reduce-scatter with variable shards: shard q is columns
+ * [seg_start[q], seg_start[q+1]) of `in`, and
+ *   out[q][k] = round_dtype(fold over r of pre(in[r][seg_start[q] + k]))
+ * with the flush's fold and pre-division by W.
+ *   seg_start     host int64[W+1], non-decreasing from 0, seg_start[W] <= ld_in
+ *   out, ld_out   device [W, ld_out], ld_out >= the longest shard; no overlap */
+dc_status dc_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                              int64_t ld_out, const int64_t* seg_start, int32_t pre_div,
+                              void* stream);
 
 /* a8. ReduceScatter ([AG] duality with ReduceScatter: M elements in per node,
  * M/N out, a reduction plus a split).  With L = M / W:

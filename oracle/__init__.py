@@ -49,6 +49,15 @@ def load_library(path):
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _vp, _vp, ctypes.c_int32]
     L.or_flush_zero2.restype = None
+    L.or_relayout_map.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  ctypes.c_int64, _vp, _vp]
+    L.or_relayout_map.restype = ctypes.c_int64
+    L.or_relayout_apply.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64, _vp,
+                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp]
+    L.or_relayout_apply.restype = None
+    L.or_reduce_scatter_v.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64, _vp,
+                                      ctypes.c_int64, _vp, ctypes.c_int32]
+    L.or_reduce_scatter_v.restype = None
     L.or_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _vp, _vp, _vp, _vp]
     L.or_probe.restype = None
@@ -183,6 +192,34 @@ def flush_zero2(W, dtype, slab_in, slab_out, bucket_col, t_off, t_numel, t_param
                          bucket_col, len(t_off), _p(t_off), _p(t_numel), _p(t_param), _p(t_comm),
                          _p(fo), _p(ps), _p(cs), _p(cst), pre_div)
     return slab_out
+
+
+def relayout_map(W, t_off, t_numel, t_param, t_comm, flat_offset, part_size, bucket_numel):
+    """(dest[bucket_numel], seg_start[W+1]) of the by-destination relayout."""
+    t_off, t_numel = _c(t_off, np.int64), _c(t_numel, np.int64)
+    t_param, t_comm = _c(t_param, np.int32), _c(t_comm, np.int32)
+    fo, ps = _c(flat_offset, np.int64), _c(part_size, np.int64)
+    dest = np.zeros(max(bucket_numel, 1), np.int64)
+    seg = np.zeros(W + 1, np.int64)
+    lib().or_relayout_map(W, len(t_off), _p(t_off), _p(t_numel), _p(t_param), _p(t_comm), _p(fo),
+                          _p(ps), bucket_numel, _p(dest), _p(seg))
+    return dest[:bucket_numel], seg
+
+
+def relayout_apply(W, dtype, slab_in, out, bucket_col, bucket_numel, dest):
+    slab_in, out = _slab(slab_in, dtype), _slab(out, dtype)
+    d = _c(dest, np.int64)
+    lib().or_relayout_apply(W, dtype, _p(slab_in), slab_in.shape[1], _p(out), out.shape[1],
+                            bucket_col, bucket_numel, _p(d))
+    return out
+
+
+def reduce_scatter_v(W, dtype, slab_in, out, seg_start, pre_div):
+    slab_in, out = _slab(slab_in, dtype), _slab(out, dtype)
+    seg = _c(seg_start, np.int64)
+    lib().or_reduce_scatter_v(W, dtype, _p(slab_in), slab_in.shape[1], _p(out), out.shape[1],
+                              _p(seg), pre_div)
+    return out
 
 
 def probe(W, t_numel, t_param, t_comm, owner, pid_offsets, pids, comm_size, comm_stride):

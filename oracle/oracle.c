@@ -242,6 +242,71 @@ void or_flush_zero2(int32_t W, int32_t dtype, const void* in, int64_t ld_in, voi
   }
 }
 
+/* Bucket relayout for a reduce-scatter ([DS] "Describe alternatives": a
+ * reduce-scatter over the bucket needs the payload contiguous by destination
+ * rank).  Every element of a data-parallel task with partition size S > 0
+ * goes to segment q = floor((flat_offset + e) / S); segment q holds its
+ * elements in arrival order (tasks in bucket order, elements in order), and
+ * the segments follow each other, q = 0..W-1.  dest[c] = the relaid column
+ * of bucket column c (-1 for an element of another task); seg_start[0..W]
+ * = segment boundaries.  Returns the relaid length. */
+int64_t or_relayout_map(int32_t W, int32_t n_tasks, const int64_t* t_off, const int64_t* t_numel,
+                        const int32_t* t_param, const int32_t* t_comm, const int64_t* flat_offset,
+                        const int64_t* part_size, int64_t bucket_numel, int64_t* dest,
+                        int64_t* seg_start) {
+  int64_t* count = (int64_t*)calloc((size_t)W, sizeof(int64_t));
+  for (int64_t c = 0; c < bucket_numel; ++c) dest[c] = -1;
+  /* pass 1: segment sizes */
+  for (int32_t t = 0; t < n_tasks; ++t) {
+    int64_t S = t_comm[t] == 0 ? part_size[t_param[t]] : 0;
+    if (S <= 0) continue;
+    for (int64_t e = 0; e < t_numel[t]; ++e) count[(flat_offset[t_param[t]] + e) / S] += 1;
+  }
+  seg_start[0] = 0;
+  for (int q = 0; q < W; ++q) seg_start[q + 1] = seg_start[q] + count[q];
+  /* pass 2: place elements in arrival order */
+  for (int q = 0; q < W; ++q) count[q] = seg_start[q];
+  for (int32_t t = 0; t < n_tasks; ++t) {
+    int64_t S = t_comm[t] == 0 ? part_size[t_param[t]] : 0;
+    if (S <= 0) continue;
+    for (int64_t e = 0; e < t_numel[t]; ++e) {
+      int64_t q = (flat_offset[t_param[t]] + e) / S;
+      dest[t_off[t] + e] = count[q]++;
+    }
+  }
+  free(count);
+  return seg_start[W];
+}
+
+/* Apply a relayout map to every row: out[r][dest[c]] = in[r][bucket_col + c]. */
+void or_relayout_apply(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                       int64_t ld_out, int64_t bucket_col, int64_t bucket_numel,
+                       const int64_t* dest) {
+  int64_t eb = dtype == OR_BF16 ? 2 : 4;
+  for (int r = 0; r < W; ++r)
+    for (int64_t c = 0; c < bucket_numel; ++c)
+      if (dest[c] >= 0)
+        memcpy((char*)out + ((int64_t)r * ld_out + dest[c]) * eb,
+               (const char*)in + ((int64_t)r * ld_in + bucket_col + c) * eb, (size_t)eb);
+}
+
+/* Reduce-scatter with variable shards: out[q][k] = round_dtype(fold over r
+ * of pre(in[r][seg_start[q] + k])) for k < seg_start[q+1] - seg_start[q];
+ * pre-division by W. */
+void or_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                         int64_t ld_out, const int64_t* seg_start, int32_t pre_div) {
+  for (int q = 0; q < W; ++q) {
+    for (int64_t k = 0; k < seg_start[q + 1] - seg_start[q]; ++k) {
+      float acc = 0.0f;
+      for (int r = 0; r < W; ++r) {
+        float v = contribution(dtype, load_val(dtype, in, ld_in, r, seg_start[q] + k), pre_div, W);
+        acc = (r == 0) ? v : acc + v;
+      }
+      store_val(dtype, out, ld_out, q, k, acc);
+    }
+  }
+}
+
 /* a7. Probe ([DS] problem statement probe line; "reduce_probe").  Host-only
  * bookkeeping from metadata.  Holders of a parameter: the ranks whose
  * partition appears in its partition list (for a sub-communicator group,

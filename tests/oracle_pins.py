@@ -566,6 +566,62 @@ def pin_zero2_routing():
                 assert np.array_equal(zb[:, list(cols)], ab[:, list(cols)])
 
 
+def pin_relayout_reduce_scatter():
+    """Relayout for a reduce-scatter over the bucket ([DS] alternatives): a
+    bijection from the data-parallel columns onto [0, n) whose segment q holds
+    exactly the columns of partition q (brute force), in bucket order; the
+    reduce-scatter of the relaid bucket gives each rank the ZeRO-2 flush's
+    values for its partition, bit for bit."""
+    rng = random.Random(91)
+    for trial in range(30):
+        W = rng.choice([2, 4, 8])
+        dtype = rng.choice([BF16, F32])
+        g0 = [rng.choice([0, 1, 3, 8, 21, 40, 64]) for _ in range(rng.randint(2, 14))]
+        g1 = [rng.choice([0, 2, 5]) for _ in range(rng.randint(0, 4))]
+        sizes = g0 + g1
+        P = len(sizes)
+        gb = [0, len(g0), P]
+        sub = W // 2
+        flat, ps, off, pids = oracle.partition_ids(sizes, gb, [W, sub])
+        part_size = np.array([ps[0] if p < len(g0) else 0 for p in range(P)], np.int64)
+        arrival = list(range(P - 1, -1, -1))
+        rng.shuffle(arrival) if trial % 3 == 0 else None
+        t_numel = [sizes[p] for p in arrival]
+        t_off = np.concatenate([[0], np.cumsum(t_numel)[:-1]]).astype(np.int64)
+        t_comm = [0 if p < len(g0) else 1 for p in arrival]
+        n = sum(sizes)
+        dest, seg = oracle.relayout_map(W, t_off, t_numel, arrival, t_comm, flat, part_size, n)
+        # brute force: partition of every data-parallel column, stable by column
+        S = -(-sum(g0) // W) if sum(g0) else 0
+        pos0 = np.concatenate([[0], np.cumsum(g0)]).astype(int)
+        part_of = {}
+        for t, p in enumerate(arrival):
+            if p < len(g0):
+                for e in range(sizes[p]):
+                    part_of[int(t_off[t]) + e] = (int(pos0[p]) + e) // S
+        order = sorted(part_of, key=lambda c: (part_of[c], c))
+        want = np.full(n, -1, np.int64)
+        for k, c in enumerate(order):
+            want[c] = k
+        assert np.array_equal(dest, want), trial
+        for q in range(W):
+            assert seg[q + 1] - seg[q] == sum(1 for c in part_of if part_of[c] == q)
+        # values
+        ld = max(8, -(-n // 8) * 8)
+        rows = random_bits(rng, dtype, (W, ld), wide=False)
+        relaid = np.zeros_like(rows)
+        oracle.relayout_apply(W, dtype, rows, relaid, 0, n, dest)
+        shard_ld = max(8, -(-int(max(seg[1:] - seg[:-1], default=0)) // 8) * 8)
+        shards = np.zeros((W, shard_ld), rows.dtype)
+        oracle.reduce_scatter_v(W, dtype, relaid, shards, seg, 1)
+        z2 = np.zeros_like(rows)
+        oracle.flush_zero2(W, dtype, rows, z2, 0, t_off, t_numel, arrival, t_comm, flat, part_size,
+                           [W, sub], [1, 1], 1)
+        sb, zb = out_bits(dtype, shards), out_bits(dtype, z2)
+        for c, q in part_of.items():
+            assert sb[q, dest[c] - seg[q]] == zb[q, c], (trial, c, q)
+
+
 # ---------------------------------------------------------------------------
 # ring and recursive-doubling all-gather
 # ---------------------------------------------------------------------------
@@ -776,7 +832,8 @@ ALL_PINS = [
     pin_fold_identical_rows, pin_fold_brute_force, pin_fold_error_bound,
     pin_prediv_non_power_of_two, pin_reduce_scatter_all_gather, pin_partition_brute_force,
     pin_owner_rules, pin_group_eligibility, pin_probe_printed_example, pin_ratio_printed_example,
-    pin_probe_closed_forms, pin_owner_path_equivalences, pin_zero2_routing, pin_ring_table, pin_ring_closed_form,
+    pin_probe_closed_forms, pin_owner_path_equivalences, pin_zero2_routing,
+    pin_relayout_reduce_scatter, pin_ring_table, pin_ring_closed_form,
     pin_rd_table, pin_ring_step_replay, pin_deferred_ga1_identity,
     pin_accumulate_zero_start, pin_deferred_exact_reassociation, pin_deferred_tolerance, pin_deferred_restore,
     pin_deferred_round_trip,

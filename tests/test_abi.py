@@ -150,3 +150,53 @@ def test_probe_matches_oracle_on_workloads():
                 assert list(pr.kept)[:w.W] == list(want["kept"])
                 assert list(pr.written)[:w.W] == list(want["written"])
                 assert list(pr.discarded)[:w.W] == list(want["discarded"])
+
+
+def _dest_from_pieces(pieces, n):
+    dest = np.full(n, -1, np.int64)
+    for pc in pieces:
+        dest[pc["src"]:pc["src"] + pc["len"]] = np.arange(pc["dst"], pc["dst"] + pc["len"])
+    return dest
+
+
+def test_plan_relayout_matches_oracle():
+    """The host relayout planner against the oracle's element-by-element
+    relayout map, on the synthetic workloads and random ones."""
+    ws = [wl.tiny_flush(), wl.owner_flush_w8(), wl.mixed_flush_w16()]
+    rng = random.Random(4)
+    for k in range(6):
+        W = rng.choice([2, 3, 4, 8])
+        sizes = [rng.randint(0, 300) for _ in range(150)]
+        ws.append(wl.custom_flush(f"r{k}", W, 0, sizes, group_begin=[0, 90, 150],
+                                  group_comm=[0, 0], comms=[wl.Comm(W, 1)], capacity=2500))
+    for w in ws:
+        flat, ps, off, pids = oracle.partition_ids(w.numel, w.group_begin, w.group_parts())
+        comm_sizes = [w.comms[c].size for c in w.group_comm]
+        elig = oracle.group_eligible(w.W, comm_sizes, w.group_rank_to_global())
+        psize = np.zeros(w.P, np.int64)
+        for g in range(w.G):
+            if elig[g]:
+                psize[w.group_begin[g]:w.group_begin[g + 1]] = ps[g]
+        for bk in w.buckets[:8]:
+            t = dc.tasks_array([(x.offset, x.numel, x.param, x.comm) for x in bk.tasks])
+            pieces, seg = dc.dc_plan_relayout(w.W, t, len(t), flat, psize, w.P)
+            assert np.all(np.diff(pieces["dst"]) > 0) if len(pieces) > 1 else True
+            dest, oseg = oracle.relayout_map(w.W, t["offset"], t["numel"], t["param"], t["comm"],
+                                             flat, psize, bk.numel)
+            assert np.array_equal(seg, oseg), w.name
+            assert np.array_equal(_dest_from_pieces(pieces, bk.numel), dest), w.name
+
+
+def test_plan_relayout_errors():
+    t = dc.tasks_array([(0, 10, 0, 0), (10, 10, 1, 0)])
+    # partition index past W
+    expect(dc.DC_ERR_TASKS, dc.dc_plan_relayout, 2, t, 2, [0, 10], [4, 4], 2)
+    # too few slots
+    seg = np.zeros(3, np.int64)
+    n = ctypes.c_int32(0)
+    rc = dc.lib().dc_plan_relayout(2, t.ctypes.data_as(ctypes.c_void_p), 2,
+                                   np.array([0, 10], np.int64).ctypes.data_as(ctypes.c_void_p),
+                                   np.array([10, 10], np.int64).ctypes.data_as(ctypes.c_void_p), 2,
+                                   np.zeros(1, dc.PIECE_DTYPE).ctypes.data_as(ctypes.c_void_p), 1,
+                                   ctypes.byref(n), seg.ctypes.data_as(ctypes.c_void_p))
+    assert rc == dc.DC_ERR_SHAPE and n.value == 2

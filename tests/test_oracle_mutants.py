@@ -67,6 +67,15 @@ MUTANTS = {
     "zero2_straddler_allreduce": (
         "int64_t S = t_comm[t] == 0 ? part_size[t_param[t]] : 0;",
         "int64_t S = 0;"),
+    "relayout_segment_by_task_order": (
+        "dest[t_off[t] + e] = count[q]++;",
+        "dest[t_off[t] + e] = seg_start[q] + (seg_start[q + 1] - 1 - (count[q]++ - seg_start[q]));"),
+    "relayout_segment_off_by_one": (
+        "for (int q = 0; q < W; ++q) seg_start[q + 1] = seg_start[q] + count[q];",
+        "for (int q = 0; q < W; ++q) seg_start[q + 1] = seg_start[q] + count[q] + (q == 0);"),
+    "rsv_wrong_destination_row": (
+        "      store_val(dtype, out, ld_out, q, k, acc);",
+        "      store_val(dtype, out, ld_out, (q + 1) % W, k, acc);"),
     "rd_partner_plus": (
         "int q = i ^ d;",
         "int q = (i + d) % N;"),
