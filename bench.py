@@ -11,9 +11,13 @@ per step / step time (GB/s), and the flush kernel against MI355X's 8 TB/s HBM
 peak.  Algorithmic bytes of a task of n elements over W ranks, b bytes each:
 W*n*b read + (owner ? 1 : W)*n*b written + its 32-byte task record.
 
-Other workloads (--workload): mixed (W=16 fp32 1.2B-element flush), deferred
-(qwen3-0.6b W=4 fp32 gradient accumulation), rs_ag (7B layer reduce-scatter +
-all-gather), tiny (W=4 flush).
+Other workloads (--workload): allreduce_w8 and zero2_w8 (the same gradient
+through the AllReduce and ZeRO-2 paths), mixed and zero2_mixed (W=16 fp32
+1.2B-element flush), deferred (qwen3-0.6b W=4 fp32 gradient accumulation),
+rs_ag (7B layer reduce-scatter + all-gather), schedules_w8 (7B layer, ring-
+order reduce-scatter and the ring / bidirectional-ring / recursive-doubling
+all-gather step executors), relayout_rs_w8 (relayout by destination +
+reduce-scatter-v), tiny (W=4 flush).
 """
 import argparse
 import json
@@ -347,6 +351,83 @@ def bench_rs_ag(args):
     return w.name, ms_step, (rs_b + 2 * ag_b) / (ms_step / 1e3) / 1e9, roofline, extra, "bf16"
 
 
+def bench_schedules(args):
+    """The 7B-layer slab through the schedule-faithful collectives: reduce-
+    scatter in rank order and in ring order, then all-gather by the ring,
+    bidirectional-ring and recursive-doubling step executors (one launch per
+    step, chunks at their own index)."""
+    import torch
+    import synth
+    from gradient_reduction_amd import dc
+    from synth import workloads as wl
+    w = wl.rs_ag_w8()
+    W, M, L = w.W, w.M, w.M // w.W
+    dev = torch.device("cuda:0")
+    x = torch.empty((W, w.ld), dtype=torch.int16, device=dev)
+    synth.fill_slab_device(0, w.value_seed, 0, w.scale, W, w.ld, M, x.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream)
+    ld_sh = wl.round_up(L, 64)
+    sh = torch.empty((W, ld_sh), dtype=torch.int16, device=dev)
+    out = torch.empty((W, w.ld), dtype=torch.int16, device=dev)
+    scheds = [("ring", dc.DC_SCHED_RING, W - 1), ("bidir", dc.DC_SCHED_BIDIR, W // 2),
+              ("rd", dc.DC_SCHED_RD, W.bit_length() - 1)]
+    rs_b = W * M * 2 + M * 2
+    # step 0 reads the W shards and writes them in place; every later chunk
+    # moved is read from one node's row and written to another's: W*(W-1)
+    # chunks of L in all, whatever the schedule.
+    ag_b = 2 * (M + (W - 1) * M) * 2
+    names = ["rs_rank", "rs_ring"] + [f"ag_{n}" for n, _, _ in scheds]
+
+    def step(tm=None):
+        if tm: tm.ev[0][0].record()
+        dc.dc_reduce_scatter(W, 0, x, w.ld, sh, ld_sh, M, 1)
+        if tm: tm.ev[0][1].record(); tm.ev[1][0].record()
+        dc.dc_reduce_scatter_ring(W, 0, x, w.ld, sh, ld_sh, M, 1)
+        if tm: tm.ev[1][1].record()
+        for k, (_, algo, S) in enumerate(scheds):
+            if tm: tm.ev[2 + k][0].record()
+            for s in range(S + 1):
+                dc.dc_all_gather_step(W, 0, sh, ld_sh, out, w.ld, L, algo, s)
+            if tm: tm.ev[2 + k][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [Timer(torch, len(names)) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for k in range(args.steps):
+        step(timers[k])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    kern = np.array([tm.ms() for tm in timers]).mean(axis=0)
+    byts = [rs_b, rs_b] + [ag_b] * len(scheds)
+    gbs = {n: b / (t / 1e3) / 1e9 for n, b, t in zip(names, byts, kern)}
+    log("[bench] " + ", ".join(f"{n} {kern[i]:.3f} ms {gbs[n]:.1f} GB/s" for i, n in enumerate(names)))
+    roofline = {"bound": "hbm", "achieved": round(gbs["rs_ring"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs["rs_ring"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_rs_ring", "launch_ms_avg": round(float(kern[1]), 4),
+                "bytes_per_launch_avg": rs_b}
+    extra = {n: {"ms": round(float(kern[i]), 4), "gbs": round(gbs[n], 1)} for i, n in enumerate(names)}
+    extra["ag_launches"] = {n: S + 1 for n, _, S in scheds}
+    # rank-order against ring-order shards: both are correct sums, in
+    # different orders; how far apart they land in bf16
+    rk = torch.empty_like(sh)
+    dc.dc_reduce_scatter(W, 0, x, w.ld, rk, ld_sh, M, 1)
+    dc.dc_reduce_scatter_ring(W, 0, x, w.ld, sh, ld_sh, M, 1)
+    a = rk[:, :L].view(torch.bfloat16).float()
+    r = sh[:, :L].view(torch.bfloat16).float()
+    diff = (a - r).abs()
+    extra["ring_vs_rank"] = {
+        "elements_differing_frac": round(float((diff > 0).float().mean()), 5),
+        "max_abs_diff_over_max_abs": float(diff.max() / a.abs().max()),
+        "max_rel_diff_where_abs_ge_1pct_of_max": float(
+            (diff / a.abs().clamp_min(1e-30))[a.abs() >= 0.01 * a.abs().max()].max())}
+    log(f"[bench] ring vs rank order: {extra['ring_vs_rank']}")
+    return w.name, ms_step, sum(byts) / (ms_step / 1e3) / 1e9, roofline, extra, "bf16"
+
+
 def bench_relayout_rs(args):
     """Every bucket of the W=8 402.8M workload relaid by destination rank and
     reduce-scattered with variable shards (the issue's reduce-scatter
@@ -439,7 +520,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="owner_w8",
                     choices=["owner_w8", "allreduce_w8", "zero2_w8", "mixed", "zero2_mixed",
-                             "deferred", "rs_ag", "relayout_rs_w8", "tiny"])
+                             "deferred", "rs_ag", "schedules_w8", "relayout_rs_w8", "tiny"])
     ap.add_argument("--ga", type=int, default=8)
     ap.add_argument("--fused", action="store_true",
                     help="deferred workload: fuse the last accumulate into the reduce")
@@ -485,6 +566,10 @@ def main():
         name, ms, value, roof, extra, dtype = bench_relayout_rs(args)
         config = {"workload": name, "W": 8,
                   "step": "relayout by destination + reduce-scatter-v of every bucket"}
+    elif args.workload == "schedules_w8":
+        name, ms, value, roof, extra, dtype = bench_schedules(args)
+        config = {"workload": name, "W": 8,
+                  "step": "reduce-scatter rank + ring order, all-gather ring/bidir/rd step executors"}
     else:
         name, ms, value, roof, extra, dtype = bench_rs_ag(args)
         config = {"workload": name, "W": 8, "step": "reduce-scatter + all-gather rank + all-gather ring"}

@@ -446,6 +446,51 @@ dc_status dc_all_gather(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
                     "all-gather launch");
 }
 
+dc_status dc_reduce_scatter_ring(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
+                                 void* out, int64_t ld_out, int64_t M, int32_t pre_div,
+                                 void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype))) return st;
+  if (M < 0) return fail(DC_ERR_ARG, "M=%lld < 0", (long long)M);
+  if (M % W != 0) return fail(DC_ERR_SHAPE, "M=%lld is not a multiple of W=%d (pad with zeros)", (long long)M, W);
+  if (pre_div != 0 && pre_div != 1) return fail(DC_ERR_ARG, "pre_div=%d", pre_div);
+  if ((st = check_slab("in", in, ld_in, M, dtype)) || (st = check_slab("out", out, ld_out, M / W, dtype))) return st;
+  const int64_t b = elem_bytes(dtype);
+  if (overlaps(in, W * ld_in * b, out, W * ld_out * b)) return fail(DC_ERR_ARG, "in and out overlap");
+  return hip_status(dc::launch_reduce_scatter_ring(W, dtype, in, ld_in, out, ld_out, M, pre_div,
+                                                   static_cast<hipStream_t>(stream)),
+                    "ring reduce-scatter launch");
+}
+
+dc_status dc_all_gather_step(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                             int64_t ld_out, int64_t shard_numel, int32_t algo, int32_t step,
+                             void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype))) return st;
+  if (shard_numel < 0) return fail(DC_ERR_ARG, "shard_numel < 0");
+  int32_t steps;
+  if (algo == DC_SCHED_RING) {
+    steps = W - 1;
+  } else if (algo == DC_SCHED_BIDIR) {
+    steps = W / 2;  // ceil((W-1)/2)
+  } else if (algo == DC_SCHED_RD) {
+    if ((W & (W - 1)) != 0) return fail(DC_ERR_ARG, "recursive doubling needs W a power of two, got %d", W);
+    steps = 0;
+    for (int d = 1; d < W; d <<= 1) ++steps;
+  } else {
+    return fail(DC_ERR_ARG, "algo=%d", algo);
+  }
+  if (step < 0 || step > steps) return fail(DC_ERR_ARG, "step=%d outside [0, %d]", step, steps);
+  if ((st = check_slab("in", in, ld_in, shard_numel, dtype)) ||
+      (st = check_slab("out", out, ld_out, W * shard_numel, dtype)))
+    return st;
+  const int64_t b = elem_bytes(dtype);
+  if (overlaps(in, W * ld_in * b, out, W * ld_out * b)) return fail(DC_ERR_ARG, "in and out overlap");
+  return hip_status(dc::launch_all_gather_step(W, dtype, in, ld_in, out, ld_out, shard_numel, algo, step,
+                                               static_cast<hipStream_t>(stream)),
+                    "all-gather step launch");
+}
+
 dc_status dc_accumulate(int32_t rows, const float* x, int64_t ld_x, float* acc, int64_t ld_acc,
                         int64_t M, int32_t init, void* stream) {
   dc_status st;

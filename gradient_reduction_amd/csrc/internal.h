@@ -65,6 +65,14 @@ hipError_t launch_relayout(int32_t W, int32_t dtype, const void* in, int64_t ld_
                            const dc_piece* pieces, int32_t npieces, int64_t out_numel,
                            hipStream_t stream);
 
+hipError_t launch_reduce_scatter_ring(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
+                                      void* out, int64_t ld_out, int64_t M, int32_t pre_div,
+                                      hipStream_t stream);
+
+hipError_t launch_all_gather_step(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
+                                  void* out, int64_t ld_out, int64_t L, int32_t algo,
+                                  int32_t step, hipStream_t stream);
+
 hipError_t launch_all_gather(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
                              int64_t ld_out, int64_t L, int32_t order, int32_t step,
                              hipStream_t stream);

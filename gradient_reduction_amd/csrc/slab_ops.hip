@@ -193,9 +193,116 @@ __global__ __launch_bounds__(kThreads) void k_rs_v(int32_t W, const void* __rest
   }
 }
 
+// Ring-order reduce-scatter: shard s folded in rank order s, s+1, ..., s-1
+// (mod W), the order in which a ring passes the partial sums along.  The
+// rows are loaded in that order, so the register array is indexed
+// statically.
+template <bool BF16, int WT, bool PRE>
+__global__ __launch_bounds__(kThreads) void k_rs_ring(int32_t W, const u32x4* __restrict__ in,
+                                                      int64_t ldv_in, u32x4* __restrict__ out,
+                                                      int64_t ldv_out, int64_t Lv, float inv,
+                                                      float c) {
+  constexpr int E = BF16 ? 8 : 4;
+  const int32_t s = blockIdx.y;
+  const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (k >= Lv) return;
+  const int64_t v = (int64_t)s * Lv + k;
+  float acc[E];
+  if constexpr (WT > 0) {
+    u32x4 x[WT];
+#pragma unroll
+    for (int j = 0; j < WT; ++j) x[j] = load16<kNT>(in + (int64_t)((s + j) % WT) * ldv_in + v);
+#pragma unroll
+    for (int j = 0; j < WT; ++j) fold16<BF16, PRE>(acc, x[j], j == 0, inv, c);
+  } else {
+    for (int32_t j = 0; j < W; ++j)
+      fold16<BF16, PRE>(acc, load16<kNT>(in + (int64_t)((s + j) % W) * ldv_in + v), j == 0, inv, c);
+  }
+  store16<kNTS>(out + (int64_t)s * ldv_out + k, pack16<BF16>(acc));
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_rs_ring_elem(int32_t W, const void* __restrict__ in,
+                                                           int64_t ld_in, void* __restrict__ out,
+                                                           int64_t ld_out, int64_t L, int32_t pre,
+                                                           float inv, float c) {
+  const int32_t s = blockIdx.y;
+  const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (k >= L) return;
+  float acc = 0.0f;
+  for (int32_t j = 0; j < W; ++j) {
+    const float v = pre_elem<BF16>(load_elem<BF16>(in, (int64_t)((s + j) % W) * ld_in + (int64_t)s * L + k),
+                                   pre != 0, inv, c);
+    acc = j == 0 ? v : acc + v;
+  }
+  store_elem<BF16>(out, (int64_t)s * ld_out + k, acc);
+}
+
 // ---------------------------------------------------------------------------
 // a9. all-gather
 // ---------------------------------------------------------------------------
+
+// One step of an all-gather schedule on the [W, W*L] buffer, every chunk at
+// its own index.  Transfer t of node i at step `step`:
+//   step 0: node i places its own shard (from `in`);
+//   ring: chunk (i - step) mod W from node i-1;
+//   bidirectional ring: t = 0 chunk (i - step) mod W from node i-1, t = 1
+//     chunk (i + step) mod W from node i+1 (not when the two coincide);
+//   recursive doubling: the 2^(step-1) chunks of node i XOR 2^(step-1).
+// Every chunk a step reads was placed by an earlier step, and every chunk it
+// writes is new, so one launch per step is race free.
+__device__ __forceinline__ bool ag_transfer(int32_t W, int32_t algo, int32_t step, int32_t i,
+                                            int32_t t, int32_t* src, int32_t* chunk) {
+  if (step == 0) {
+    *src = -1;
+    *chunk = i;
+    return t == 0;
+  }
+  if (algo == 0) {
+    *src = (i - 1 + W) % W;
+    *chunk = ((i - step) % W + W) % W;
+    return t == 0;
+  }
+  if (algo == 1) {
+    if (t == 0) {
+      *src = (i - 1 + W) % W;
+      *chunk = ((i - step) % W + W) % W;
+      return true;
+    }
+    *src = (i + 1) % W;
+    *chunk = (i + step) % W;
+    return t == 1 && (2 * step) % W != 0;
+  }
+  const int32_t d = 1 << (step - 1);
+  *src = i ^ d;
+  *chunk = (*src & ~(d - 1)) + t;
+  return t < d;
+}
+
+template <int EB>
+__global__ __launch_bounds__(kThreads) void k_ag_step(int32_t W, const char* __restrict__ in,
+                                                      int64_t ld_in, char* out, int64_t ld_out,
+                                                      int64_t L, int32_t algo, int32_t step) {
+  constexpr int E = 16 / EB;
+  const int32_t i = blockIdx.y, t = blockIdx.z;
+  int32_t src, chunk;
+  if (!ag_transfer(W, algo, step, i, t, &src, &chunk)) return;
+  const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const char* from = src < 0 ? in + (int64_t)i * ld_in * EB
+                             : out + ((int64_t)src * ld_out + (int64_t)chunk * L) * EB;
+  char* to = out + ((int64_t)i * ld_out + (int64_t)chunk * L) * EB;
+  if (L % E == 0) {
+    if (k < L / E)
+      store16<kAgNTS>(reinterpret_cast<u32x4*>(to) + k, load16<kNT>(reinterpret_cast<const u32x4*>(from) + k));
+  } else {
+    for (int64_t e = k * E; e < min((k + 1) * E, L); ++e) {
+      if constexpr (EB == 2)
+        reinterpret_cast<uint16_t*>(to)[e] = reinterpret_cast<const uint16_t*>(from)[e];
+      else
+        reinterpret_cast<uint32_t*>(to)[e] = reinterpret_cast<const uint32_t*>(from)[e];
+    }
+  }
+}
 
 // Thread (s, k) reads chunk s's vector k once and writes it wherever node i
 // keeps chunk s: position s (rank order) or (i - s) mod W (ring order).  In
@@ -491,6 +598,76 @@ hipError_t launch_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int
                    : rs_v_w<true, false>(W, in, ld_in, out, ld_out, sa, maxlen, inv, c, stream);
   return pre_div ? rs_v_w<false, true>(W, in, ld_in, out, ld_out, sa, maxlen, inv, c, stream)
                  : rs_v_w<false, false>(W, in, ld_in, out, ld_out, sa, maxlen, inv, c, stream);
+}
+
+template <bool BF16, bool PRE>
+hipError_t rs_ring_w(int32_t W, const void* in, int64_t ld_in, void* out, int64_t ld_out, int64_t L,
+                     float inv, float c, hipStream_t stream) {
+  constexpr int E = BF16 ? 8 : 4;
+  const int64_t Lv = L / E;
+  const dim3 grid(blocks_for(Lv, 1), (unsigned)W);
+  const u32x4* i4 = reinterpret_cast<const u32x4*>(in);
+  u32x4* o4 = reinterpret_cast<u32x4*>(out);
+  switch (W) {
+#define DC_RR_W(w)                                                                                \
+  case w:                                                                                         \
+    hipLaunchKernelGGL((k_rs_ring<BF16, w, PRE>), grid, dim3(kThreads), 0, stream, W, i4, ld_in / E, \
+                       o4, ld_out / E, Lv, inv, c);                                               \
+    break;
+    DC_RR_W(1)
+    DC_RR_W(2)
+    DC_RR_W(4)
+    DC_RR_W(8)
+    DC_RR_W(16)
+#undef DC_RR_W
+    default:
+      hipLaunchKernelGGL((k_rs_ring<BF16, 0, PRE>), grid, dim3(kThreads), 0, stream, W, i4,
+                         ld_in / E, o4, ld_out / E, Lv, inv, c);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_scatter_ring(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
+                                      void* out, int64_t ld_out, int64_t M, int32_t pre_div,
+                                      hipStream_t stream) {
+  const int64_t L = M / W;
+  if (L == 0) return hipSuccess;
+  float inv, c;
+  reciprocal(W, &inv, &c);
+  const bool bf = dtype == DC_BF16;
+  const int E = bf ? 8 : 4;
+  if (L % E == 0) {
+    if (bf) return pre_div ? rs_ring_w<true, true>(W, in, ld_in, out, ld_out, L, inv, c, stream)
+                           : rs_ring_w<true, false>(W, in, ld_in, out, ld_out, L, inv, c, stream);
+    return pre_div ? rs_ring_w<false, true>(W, in, ld_in, out, ld_out, L, inv, c, stream)
+                   : rs_ring_w<false, false>(W, in, ld_in, out, ld_out, L, inv, c, stream);
+  }
+  const dim3 grid(blocks_for(L, 1), (unsigned)W);
+  if (bf)
+    hipLaunchKernelGGL(k_rs_ring_elem<true>, grid, dim3(kThreads), 0, stream, W, in, ld_in, out,
+                       ld_out, L, pre_div, inv, c);
+  else
+    hipLaunchKernelGGL(k_rs_ring_elem<false>, grid, dim3(kThreads), 0, stream, W, in, ld_in, out,
+                       ld_out, L, pre_div, inv, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_all_gather_step(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
+                                  void* out, int64_t ld_out, int64_t L, int32_t algo,
+                                  int32_t step, hipStream_t stream) {
+  if (L == 0) return hipSuccess;
+  const int E = dtype == DC_BF16 ? 8 : 4;
+  const int32_t tmax = step == 0 ? 1 : algo == 0 ? 1 : algo == 1 ? 2 : 1 << (step - 1);
+  const dim3 grid(blocks_for((L + E - 1) / E, 1), (unsigned)W, (unsigned)tmax);
+  if (dtype == DC_BF16)
+    hipLaunchKernelGGL(k_ag_step<2>, grid, dim3(kThreads), 0, stream, W,
+                       reinterpret_cast<const char*>(in), ld_in, reinterpret_cast<char*>(out), ld_out,
+                       L, algo, step);
+  else
+    hipLaunchKernelGGL(k_ag_step<4>, grid, dim3(kThreads), 0, stream, W,
+                       reinterpret_cast<const char*>(in), ld_in, reinterpret_cast<char*>(out), ld_out,
+                       L, algo, step);
+  return hipGetLastError();
 }
 
 hipError_t launch_all_gather(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,

@@ -20,6 +20,7 @@ DC_ERR_NULL, DC_ERR_ARG, DC_ERR_SHAPE, DC_ERR_ALIGN = 1, 2, 3, 4
 DC_ERR_DTYPE, DC_ERR_TASKS, DC_ERR_HIP, DC_ERR_UNSUPPORTED = 5, 6, 7, 8
 DC_BF16, DC_F32 = 0, 1
 DC_ORDER_RANK, DC_ORDER_RING = 0, 1
+DC_SCHED_RING, DC_SCHED_BIDIR, DC_SCHED_RD = 0, 1, 2
 DC_MAX_W, DC_MAX_GROUPS, DC_MAX_COMMS = 64, 64, 8
 
 TASK_DTYPE = np.dtype([("offset", "<i8"), ("numel", "<i8"), ("param", "<i4"),
@@ -62,6 +63,8 @@ _SIGS = {
                            _i32),
     "dc_reduce_scatter_v": ([_i32, _i32, _vp, _i64, _vp, _i64, _vp, _i32, _vp], _i32),
     "dc_reduce_scatter": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
+    "dc_reduce_scatter_ring": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
+    "dc_all_gather_step": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _i32, _vp], _i32),
     "dc_all_gather": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _i32, _vp], _i32),
     "dc_accumulate": ([_i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
     "dc_deferred_reduce": ([_i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
@@ -223,6 +226,16 @@ def dc_reduce_scatter_v(W, dtype, in_, ld_in, out, ld_out, seg_start, pre_div, s
 def dc_reduce_scatter(W, dtype, in_, ld_in, out, ld_out, M, pre_div, stream=None):
     _check("dc_reduce_scatter", lib().dc_reduce_scatter(W, dtype, _dev(in_), ld_in, _dev(out),
                                                         ld_out, M, pre_div, _stream(stream)))
+
+
+def dc_reduce_scatter_ring(W, dtype, in_, ld_in, out, ld_out, M, pre_div, stream=None):
+    _check("dc_reduce_scatter_ring", lib().dc_reduce_scatter_ring(
+        W, dtype, _dev(in_), ld_in, _dev(out), ld_out, M, pre_div, _stream(stream)))
+
+
+def dc_all_gather_step(W, dtype, in_, ld_in, out, ld_out, shard_numel, algo, step, stream=None):
+    _check("dc_all_gather_step", lib().dc_all_gather_step(
+        W, dtype, _dev(in_), ld_in, _dev(out), ld_out, shard_numel, algo, step, _stream(stream)))
 
 
 def dc_all_gather(W, dtype, in_, ld_in, out, ld_out, shard_numel, order, step, stream=None):

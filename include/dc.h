@@ -60,6 +60,10 @@ typedef int32_t dc_status;
 #define DC_ORDER_RANK 0
 #define DC_ORDER_RING 1
 
+#define DC_SCHED_RING 0      /* all-gather step schedules (dc_all_gather_step) */
+#define DC_SCHED_BIDIR 1
+#define DC_SCHED_RD 2
+
 #define DC_MAX_W 64          /* simulated ranks per slab */
 #define DC_MAX_GROUPS 64     /* parameter groups per owner map */
 #define DC_MAX_COMMS 8       /* communicators per flush */
@@ -320,6 +324,35 @@ dc_status dc_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64_t ld
 dc_status dc_all_gather(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
                         int64_t ld_out, int64_t shard_numel, int32_t order, int32_t step,
                         void* stream);
+
+/* Ring-order ReduceScatter: the sum a ring reduce-scatter produces.  A ring
+ * passes partial sums to the right, each node adding its own contribution,
+ * so chunk s is folded in rank order s, s+1, ..., s-1 (mod W) instead of
+ * 0..W-1 ([DS] Numerics: the summation order changes with the algorithm,
+ * which is why owner and AllReduce results need not be bit-identical):
+ *   out[s][k] = round_dtype(fold over j = 0..W-1 of pre(in[(s+j) mod W][s*L + k]))
+ * Arguments, layout and checks as in dc_reduce_scatter. */
+dc_status dc_reduce_scatter_ring(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
+                                 void* out, int64_t ld_out, int64_t M, int32_t pre_div,
+                                 void* stream);
+
+/* One step of an AllGather schedule ([AG] Ring AllGather, bidirectional
+ * ring, Recursive Doubling AllGather) executed on one GPU: row i of `out`
+ * ([W, W*L]) is node i's buffer, and every chunk is stored at its own index,
+ * so after the last step every row is the rank-order concatenation.
+ *   step 0            node i places its own shard: out[i][i*L + k] = in[i][k]
+ *   DC_SCHED_RING     steps 1..W-1: node i receives chunk (i - step) mod W
+ *                     from node i-1
+ *   DC_SCHED_BIDIR    steps 1..ceil((W-1)/2): node i receives chunk
+ *                     (i - step) mod W from node i-1 and chunk (i + step)
+ *                     mod W from node i+1 (once when they coincide)
+ *   DC_SCHED_RD       steps 1..log2 W (W a power of two): node i receives
+ *                     the 2^(step-1) chunks held by node i XOR 2^(step-1)
+ * Steps must run in order on the same buffers.  Other arguments as in
+ * dc_all_gather; a step outside the schedule is DC_ERR_ARG. */
+dc_status dc_all_gather_step(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                             int64_t ld_out, int64_t shard_numel, int32_t algo, int32_t step,
+                             void* stream);
 
 /* a10. Replica-local accumulation ([MT] What: unreduced per-replica partial
  * sums accumulate locally across micro-batches).  fp32 only:

@@ -64,6 +64,14 @@ def load_library(path):
     L.or_reduce_scatter.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64, _vp,
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
     L.or_reduce_scatter.restype = None
+    L.or_reduce_scatter_ring.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64, _vp,
+                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+    L.or_reduce_scatter_ring.restype = None
+    L.or_ag_step_transfers.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp]
+    L.or_ag_step_transfers.restype = ctypes.c_int32
+    L.or_all_gather_step.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64, _vp,
+                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    L.or_all_gather_step.restype = ctypes.c_int32
     L.or_ring_ag_schedule.argtypes = [ctypes.c_int32, _vp, _vp]
     L.or_ring_ag_schedule.restype = None
     L.or_rd_ag_schedule.argtypes = [ctypes.c_int32, _vp, _vp, _vp]
@@ -263,6 +271,29 @@ def reduce_scatter(W, dtype, slab_in, out, M, pre_div):
     lib().or_reduce_scatter(W, dtype, _p(slab_in), slab_in.shape[1], _p(out), out.shape[1], M,
                             pre_div)
     return out
+
+
+def reduce_scatter_ring(W, dtype, slab_in, out, M, pre_div):
+    slab_in, out = _slab(slab_in, dtype), _slab(out, dtype)
+    lib().or_reduce_scatter_ring(W, dtype, _p(slab_in), slab_in.shape[1], _p(out), out.shape[1],
+                                 M, pre_div)
+    return out
+
+
+AG_RING, AG_BIDIR, AG_RD = 0, 1, 2
+
+
+def ag_step_transfers(N, algo, step):
+    """[(dst, src, chunk)] of one step, or None if the step does not exist."""
+    rec = np.zeros((N * N, 3), np.int32)
+    n = lib().or_ag_step_transfers(N, algo, step, _p(rec))
+    return None if n < 0 else [tuple(int(v) for v in r) for r in rec[:n]]
+
+
+def all_gather_step(W, dtype, shards, out, L, algo, step):
+    shards, out = _slab(shards, dtype), _slab(out, dtype)
+    return lib().or_all_gather_step(W, dtype, _p(shards), shards.shape[1], _p(out), out.shape[1],
+                                    L, algo, step)
 
 
 def ring_ag_schedule(N):

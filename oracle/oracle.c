@@ -370,6 +370,47 @@ void or_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64_t ld_in, 
   }
 }
 
+/* Ring reduce-scatter, simulated as a ring passes partial sums ([AG] the
+ * ring all-reduce is reduce-scatter followed by all-gather; the ring
+ * reduce-scatter is the all-gather's data flow reversed with a reduction,
+ * per the duality table).  W-1 steps; at step s (s = 0..W-2) node i sends
+ * its partial sum of chunk (i - s) mod W to node i+1, which adds its own
+ * contribution (pre-divided as in the flush) and keeps the result as its
+ * partial of that chunk.  Chunk c starts at node c, so its sum is folded in
+ * rank order c, c+1, ..., c-1 (mod W); it is complete at node c-1 after the
+ * last step.  out[c][k] = the completed chunk c (rank-order shard layout). */
+void or_reduce_scatter_ring(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                            int64_t ld_out, int64_t M, int32_t pre_div) {
+  int64_t L = M / W;
+  /* partial[i][c*L + k]: node i's running sum of chunk c */
+  float* partial = (float*)malloc(sizeof(float) * (size_t)(W * (M > 0 ? M : 1)));
+  float* msg = (float*)malloc(sizeof(float) * (size_t)(W * (L > 0 ? L : 1)));
+  for (int i = 0; i < W; ++i)
+    for (int64_t j = 0; j < M; ++j)
+      partial[(int64_t)i * M + j] = contribution(dtype, load_val(dtype, in, ld_in, i, j), pre_div, W);
+  for (int step = 0; step < W - 1; ++step) {
+    /* every node sends first (messages), then every node adds */
+    for (int i = 0; i < W; ++i) {
+      int c = ((i - step) % W + W) % W;
+      for (int64_t k = 0; k < L; ++k) msg[(int64_t)i * L + k] = partial[(int64_t)i * M + c * L + k];
+    }
+    for (int i = 0; i < W; ++i) {
+      int src = (i - 1 + W) % W;
+      int c = ((src - step) % W + W) % W;
+      for (int64_t k = 0; k < L; ++k) {
+        float own = contribution(dtype, load_val(dtype, in, ld_in, i, c * L + k), pre_div, W);
+        partial[(int64_t)i * M + c * L + k] = msg[(int64_t)src * L + k] + own;
+      }
+    }
+  }
+  for (int c = 0; c < W; ++c) {
+    int holder = (c - 1 + W) % W;
+    for (int64_t k = 0; k < L; ++k) store_val(dtype, out, ld_out, c, k, partial[(int64_t)holder * M + c * L + k]);
+  }
+  free(partial);
+  free(msg);
+}
+
 /* ------------------------------------------------------------------------ */
 /* a9. AllGather ([AG] semantic definition; Ring AllGather steps).           */
 /* ------------------------------------------------------------------------ */
@@ -446,6 +487,107 @@ int32_t or_rd_ag_schedule(int32_t N, int32_t* partner, int64_t* recv_chunks, int
   free(held);
   free(next);
   return steps;
+}
+
+/* Step-by-step AllGather schedules ([AG] Ring AllGather, bidirectional ring,
+ * Recursive Doubling AllGather), with every received chunk stored at its own
+ * index (so the finished buffer is the rank-order concatenation).  Derives,
+ * by simulating the schedule from the start, the transfers of step `step`
+ * (1-based) as records {dst node, src node, chunk}; returns their count, or -1
+ * when the step does not exist.  algo 0: ring (N-1 steps; every node forwards
+ * to its right neighbour the chunk it received last), 1: bidirectional ring
+ * (ceil((N-1)/2) steps; the same in both directions at once, a chunk
+ * arriving from both sides at the last step taken once), 2: recursive
+ * doubling (N a power of two, log2 N steps; node i swaps everything it holds
+ * with node i XOR 2^(j-1)). */
+int32_t or_ag_step_transfers(int32_t N, int32_t algo, int32_t step, int32_t* rec) {
+  int32_t steps = algo == 0 ? N - 1 : algo == 1 ? N / 2 : 0;
+  if (algo == 2) {
+    if (N < 1 || (N & (N - 1)) != 0) return -1;
+    for (int d = 1; d < N; d <<= 1) ++steps;
+  }
+  if (step < 1 || step > steps) return -1;
+  char* held = (char*)calloc((size_t)N * N, 1);
+  int32_t* from_left = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+  int32_t* from_right = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+  int32_t* nl = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+  int32_t* nr = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+  for (int i = 0; i < N; ++i) {
+    held[(int64_t)i * N + i] = 1;
+    from_left[i] = from_right[i] = i;
+  }
+  int32_t n = 0;
+  for (int s = 1; s <= step; ++s) {
+    n = 0;
+    if (algo == 2) {
+      int d = 1 << (s - 1);
+      char* next = (char*)malloc((size_t)N * N);
+      memcpy(next, held, (size_t)N * N);
+      for (int i = 0; i < N; ++i) {
+        int q = i ^ d;
+        for (int c = 0; c < N; ++c)
+          if (held[(int64_t)q * N + c] && !held[(int64_t)i * N + c]) {
+            next[(int64_t)i * N + c] = 1;
+            if (s == step) { rec[n * 3] = i; rec[n * 3 + 1] = q; rec[n * 3 + 2] = c; }
+            ++n;
+          }
+      }
+      memcpy(held, next, (size_t)N * N);
+      free(next);
+    } else {
+      for (int i = 0; i < N; ++i) {
+        int left = (i - 1 + N) % N, right = (i + 1) % N;
+        nl[i] = from_left[left];   /* what the left neighbour forwards right */
+        nr[i] = from_right[right]; /* what the right neighbour forwards left */
+      }
+      for (int i = 0; i < N; ++i) {
+        int left = (i - 1 + N) % N, right = (i + 1) % N;
+        if (!held[(int64_t)i * N + nl[i]]) {
+          held[(int64_t)i * N + nl[i]] = 2;
+          if (s == step) { rec[n * 3] = i; rec[n * 3 + 1] = left; rec[n * 3 + 2] = nl[i]; }
+          ++n;
+        }
+        if (algo == 1 && !held[(int64_t)i * N + nr[i]]) {
+          held[(int64_t)i * N + nr[i]] = 2;
+          if (s == step) { rec[n * 3] = i; rec[n * 3 + 1] = right; rec[n * 3 + 2] = nr[i]; }
+          ++n;
+        }
+      }
+      for (int i = 0; i < N; ++i) {
+        from_left[i] = nl[i];
+        from_right[i] = nr[i];
+      }
+    }
+  }
+  free(held);
+  free(from_left);
+  free(from_right);
+  free(nl);
+  free(nr);
+  return n;
+}
+
+/* Apply step `step` of a schedule to an all-gather buffer out[i][c*L + k]:
+ * step 0 places every node's own shard (out[i][i*L + k] = in[i][k]); a later
+ * step copies each transfer's chunk from the source node's row. */
+int32_t or_all_gather_step(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
+                           int64_t ld_out, int64_t L, int32_t algo, int32_t step) {
+  int64_t eb = dtype == OR_BF16 ? 2 : 4;
+  if (step == 0) {
+    for (int i = 0; i < W; ++i)
+      memcpy((char*)out + ((int64_t)i * ld_out + (int64_t)i * L) * eb,
+             (const char*)in + ((int64_t)i * ld_in) * eb, (size_t)(L * eb));
+    return 0;
+  }
+  int32_t* rec = (int32_t*)malloc(sizeof(int32_t) * 3 * (size_t)W * W);
+  int32_t n = or_ag_step_transfers(W, algo, step, rec);
+  for (int32_t t = 0; t < n; ++t) {
+    int dst = rec[t * 3], src = rec[t * 3 + 1], c = rec[t * 3 + 2];
+    memcpy((char*)out + ((int64_t)dst * ld_out + (int64_t)c * L) * eb,
+           (const char*)out + ((int64_t)src * ld_out + (int64_t)c * L) * eb, (size_t)(L * eb));
+  }
+  free(rec);
+  return n;
 }
 
 /* order 0 (rank order): out[i][s*L + k] = in[s][k], the concatenation

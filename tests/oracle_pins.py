@@ -285,6 +285,58 @@ def pin_reduce_scatter_all_gather():
                 assert int(out_bits(dtype, shards)[s, k]) == bits_of(dtype, y)
 
 
+def pin_ring_reduce_scatter():
+    """Ring reduce-scatter: chunk c's sum is folded in rank order c, c+1, ...
+    (mod W).  Hand-derived: W=4, chunk 1 column (1, 2^24, 1, -2^24) gives 0 in
+    rank order (2^24+1 rounds to 2^24) but 1 in ring order 1,2,3,0; exact-sum
+    inputs give the exact sum; W <= 2 equals rank order; tiny inputs match
+    the exact-rational model of the rotated fold."""
+    for dtype in (F32, BF16):
+        W, L = 4, 1
+        if dtype == F32:
+            col0 = [2.0 ** 24, 1.0, -(2.0 ** 24), 1.0]
+            col1 = [1.0, 2.0 ** 24, 1.0, -(2.0 ** 24)]
+            rows = np.array([[a, b, 0, 0] for a, b in zip(col0, col1)], np.float32)
+        else:
+            enc = {1.0: 0x3F80, 2.0 ** 24: 0x4B80, -(2.0 ** 24): 0xCB80}
+            rows = np.array([[enc[a], enc[b], 0, 0] for a, b in zip(
+                [2.0 ** 24, 1.0, -(2.0 ** 24), 1.0], [1.0, 2.0 ** 24, 1.0, -(2.0 ** 24)])], np.uint16)
+        ring = np.zeros((W, 8), rows.dtype)
+        oracle.reduce_scatter_ring(W, dtype, rows, ring, W * L, 0)
+        rank = np.zeros((W, 8), rows.dtype)
+        oracle.reduce_scatter(W, dtype, rows, rank, W * L, 0)
+        one = 0x3F800000 if dtype == F32 else 0x3F80
+        assert out_bits(dtype, ring)[0, 0] == one and out_bits(dtype, rank)[0, 0] == one
+        assert out_bits(dtype, ring)[1, 0] == one and out_bits(dtype, rank)[1, 0] == 0
+    rng = random.Random(101)
+    for trial in range(40):
+        dtype = (BF16, F32)[trial % 2]
+        W = (1, 2, 3, 4, 5, 8)[trial % 6]
+        L = rng.randint(1, 5)
+        pre = trial % 3 == 0
+        rows = random_bits(rng, dtype, (W, W * L + 3))
+        ring = np.zeros((W, max(8, L)), rows.dtype)
+        oracle.reduce_scatter_ring(W, dtype, rows, ring, W * L, int(pre))
+        vals = [to_floats(dtype, rows[r]) for r in range(W)]
+        for c in range(W):
+            for k in range(L):
+                order = [(c + j) % W for j in range(W)]
+                y = X.fold([vals[r][c * L + k] for r in order], dtype == BF16, pre, W)
+                assert int(out_bits(dtype, ring)[c, k]) == bits_of(dtype, y), (trial, W, c, k)
+        if W <= 2:
+            rank = np.zeros_like(ring)
+            oracle.reduce_scatter(W, dtype, rows, rank, W * L, int(pre))
+            assert np.array_equal(out_bits(dtype, ring), out_bits(dtype, rank))
+    for W in (3, 8):
+        ks = [[rng.randint(-255, 255) for _ in range(W * 3)] for _ in range(W)]
+        rows = (np.array(ks, np.float64) * 2.0 ** -20).astype(np.float32)
+        ring = np.zeros((W, 8), np.float32)
+        oracle.reduce_scatter_ring(W, F32, rows, ring, W * 3, 0)
+        for c in range(W):
+            for k in range(3):
+                assert ring[c, k] == np.float32(sum(ks[r][c * 3 + k] for r in range(W)) * 2.0 ** -20)
+
+
 # ---------------------------------------------------------------------------
 # partitions and the owner map
 # ---------------------------------------------------------------------------
@@ -712,6 +764,78 @@ def pin_ring_step_replay():
     assert np.array_equal(part, full)
 
 
+def _ag_steps(N, algo):
+    """Step count of each schedule: eq:ring-ag (N-1), eq:ag-bidir-ring
+    (ceil((N-1)/2)), eq:rd-ag (log2 N)."""
+    if algo == oracle.AG_RING:
+        return N - 1
+    if algo == oracle.AG_BIDIR:
+        return math.ceil((N - 1) / 2)
+    return int(round(math.log2(N)))
+
+
+def pin_ag_step_executors():
+    """Replaying steps 0..last of every schedule, chunks at their own index,
+    gives the rank-order gather on every node, for N up to 16 (recursive
+    doubling at powers of two); the step counts are those of eq:ring-ag,
+    eq:ag-bidir-ring and eq:rd-ag; every (node, chunk) arrives exactly once
+    (the (N-1)M/N receive volume of the bandwidth lower bound); a step reads
+    only chunks held before it and never one it writes; ring and bidirectional
+    transfers come from a neighbour only; per-step volumes are one chunk
+    (ring), at most one per direction (bidirectional) and 2^(j-1) chunks
+    (recursive doubling, the printed N = 8 table); ring step s delivers
+    position s of the printed N = 4 table."""
+    ring4 = _ring_table()
+    rd8 = {1: 1, 2: 2, 3: 4}
+    rng = np.random.default_rng(67)
+    for N in range(1, 17):
+        algos = [oracle.AG_RING, oracle.AG_BIDIR]
+        if N & (N - 1) == 0:
+            algos.append(oracle.AG_RD)
+        L = 3
+        shards = rng.standard_normal((N, L)).astype(np.float32)
+        want = np.zeros((N, N * L), np.float32)
+        oracle.all_gather(N, F32, shards, want, L, 0)
+        for algo in algos:
+            S = _ag_steps(N, algo)
+            assert oracle.ag_step_transfers(N, algo, S + 1) is None, (N, algo)
+            assert oracle.ag_step_transfers(N, algo, 0) is None, (N, algo)
+            held = {(i, i) for i in range(N)}
+            got = np.full((N, N * L), np.nan, np.float32)
+            oracle.all_gather_step(N, F32, shards, got, L, algo, 0)
+            for s in range(1, S + 1):
+                tr = oracle.ag_step_transfers(N, algo, s)
+                assert tr is not None and len(tr) > 0, (N, algo, s)
+                writes = {(d, c) for d, _, c in tr}
+                assert len(writes) == len(tr), (N, algo, s, "chunk delivered twice")
+                for d, src, c in tr:
+                    assert (src, c) in held and (d, c) not in held, (N, algo, s, d, src, c)
+                    assert (src, c) not in writes, (N, algo, s, "reads a chunk written in the step")
+                    if algo != oracle.AG_RD:
+                        assert (d - src) % N in (1, N - 1), (N, algo, s)
+                per_node = np.bincount([d for d, _, _ in tr], minlength=N)
+                if algo == oracle.AG_RING:
+                    assert np.all(per_node == 1), (N, s)
+                    for d, src, c in tr:
+                        assert src == (d - 1) % N
+                        if N == 4:
+                            assert c == ring4[s][d][s], (s, d, c)
+                elif algo == oracle.AG_BIDIR:
+                    assert np.all((per_node >= 1) & (per_node <= 2)), (N, s)
+                    for d in range(N):
+                        srcs = [src for dd, src, _ in tr if dd == d]
+                        assert len(set(srcs)) == len(srcs), (N, s, d)
+                else:
+                    assert np.all(per_node == 1 << (s - 1)), (N, s)
+                    if N == 8:
+                        assert per_node[0] == rd8[s]
+                held |= writes
+                n = oracle.all_gather_step(N, F32, shards, got, L, algo, s)
+                assert n == len(tr)
+            assert held == {(i, c) for i in range(N) for c in range(N)}, (N, algo)
+            assert np.array_equal(got, want), (N, algo)
+
+
 # ---------------------------------------------------------------------------
 # deferred reduction under gradient accumulation
 # ---------------------------------------------------------------------------
@@ -830,11 +954,11 @@ def pin_deferred_round_trip():
 ALL_PINS = [
     pin_bf16_rounding, pin_bf16_rounding_matches_torch, pin_fold_rank_order, pin_fold_exact_sums,
     pin_fold_identical_rows, pin_fold_brute_force, pin_fold_error_bound,
-    pin_prediv_non_power_of_two, pin_reduce_scatter_all_gather, pin_partition_brute_force,
+    pin_prediv_non_power_of_two, pin_reduce_scatter_all_gather, pin_ring_reduce_scatter, pin_partition_brute_force,
     pin_owner_rules, pin_group_eligibility, pin_probe_printed_example, pin_ratio_printed_example,
     pin_probe_closed_forms, pin_owner_path_equivalences, pin_zero2_routing,
     pin_relayout_reduce_scatter, pin_ring_table, pin_ring_closed_form,
-    pin_rd_table, pin_ring_step_replay, pin_deferred_ga1_identity,
+    pin_rd_table, pin_ring_step_replay, pin_ag_step_executors, pin_deferred_ga1_identity,
     pin_accumulate_zero_start, pin_deferred_exact_reassociation, pin_deferred_tolerance, pin_deferred_restore,
     pin_deferred_round_trip,
 ]

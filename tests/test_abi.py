@@ -84,6 +84,19 @@ def test_other_argument_checks():
     expect(dc.DC_ERR_ARG, dc.dc_all_gather, 4, 1, FAKE, 64, FAKE << 1, 256, 64, 2, -1, stream=0)
     expect(dc.DC_ERR_ARG, dc.dc_all_gather, 4, 1, FAKE, 64, FAKE << 1, 256, 64, 0, 4, stream=0)
     expect(dc.DC_ERR_SHAPE, dc.dc_all_gather, 4, 1, FAKE, 64, FAKE << 1, 200, 64, 0, -1, stream=0)
+    rr = dc.dc_reduce_scatter_ring
+    expect(dc.DC_ERR_SHAPE, rr, 8, 0, FAKE, 64, FAKE << 1, 64, 60, 0, stream=0)
+    expect(dc.DC_ERR_ARG, rr, 8, 0, FAKE, 64, FAKE + 64, 64, 64, 0, stream=0)
+    expect(dc.DC_ERR_ARG, rr, 8, 0, FAKE, 64, FAKE << 1, 64, 64, 2, stream=0)
+    st = dc.dc_all_gather_step
+    expect(dc.DC_ERR_ARG, st, 4, 1, FAKE, 64, FAKE << 1, 256, 64, 3, 1, stream=0)
+    expect(dc.DC_ERR_ARG, st, 4, 1, FAKE, 64, FAKE << 1, 256, 64, dc.DC_SCHED_RING, 4, stream=0)
+    expect(dc.DC_ERR_ARG, st, 4, 1, FAKE, 64, FAKE << 1, 256, 64, dc.DC_SCHED_BIDIR, 3, stream=0)
+    expect(dc.DC_ERR_ARG, st, 5, 1, FAKE, 64, FAKE << 1, 320, 64, dc.DC_SCHED_BIDIR, 3, stream=0)
+    expect(dc.DC_ERR_ARG, st, 6, 1, FAKE, 64, FAKE << 1, 384, 64, dc.DC_SCHED_RD, 1, stream=0)
+    expect(dc.DC_ERR_ARG, st, 8, 1, FAKE, 64, FAKE << 1, 512, 64, dc.DC_SCHED_RD, 4, stream=0)
+    expect(dc.DC_ERR_ARG, st, 4, 1, FAKE, 64, FAKE << 1, 256, 64, dc.DC_SCHED_RING, -1, stream=0)
+    expect(dc.DC_ERR_SHAPE, st, 4, 1, FAKE, 64, FAKE << 1, 200, 64, dc.DC_SCHED_RING, 0, stream=0)
     expect(dc.DC_ERR_ARG, dc.dc_accumulate, 0, FAKE, 64, FAKE << 1, 64, 64, 0, stream=0)
     expect(dc.DC_ERR_ARG, dc.dc_accumulate, 2, FAKE, 64, FAKE, 128, 64, 0, stream=0)
     expect(dc.DC_ERR_ALIGN, dc.dc_accumulate, 2, FAKE, 66, FAKE << 1, 64, 64, 0, stream=0)

@@ -89,6 +89,108 @@ def test_all_gather_ring_step_replay(W, dtype, L):
     assert torch.equal(rk, full_rank)
 
 
+def _as_f64(a, dtype):
+    if dtype == wl.DT_BF16:
+        return oracle.bf16_to_f32(a.view(np.uint16)).astype(np.float64)
+    return a.astype(np.float64)
+
+
+RING_CASES = RS_CASES + [(8, wl.DT_BF16, 8 * 1001, 1), (4, wl.DT_F32, 4 * 1001, 0),
+                         (7, wl.DT_F32, 7 * 4096, 1), (64, wl.DT_BF16, 64 * 64, 1)]
+
+
+@pytest.mark.parametrize("W,dtype,M,pre", RING_CASES, ids=lambda v: str(v))
+def test_reduce_scatter_ring(W, dtype, M, pre):
+    """Ring-order reduce-scatter bit-exact against the oracle's simulated
+    ring; the distance to the rank-order shards is reported, not bounded
+    beyond the fold error bound (both are correct sums in different orders)."""
+    import torch
+    U.say("ring rs", W, dtype, M, pre)
+    L = M // W
+    ld_in = max(64, wl.round_up(M, 64))
+    ld_sh = max(64, wl.round_up(L, 64))
+    scale = wl.sigma_scale(1e-2)
+    x = U.gen_slab(dtype, W, ld_in, M, 14, 0, scale)
+    sh = U.empty_slab(dtype, W, ld_sh)
+    dc.dc_reduce_scatter_ring(W, dtype, x, ld_in, sh, ld_sh, M, pre)
+    rk = U.empty_slab(dtype, W, ld_sh)
+    dc.dc_reduce_scatter(W, dtype, x, ld_in, rk, ld_sh, M, pre)
+    torch.cuda.synchronize()
+    hx = U.host_slab(dtype, W, ld_in, M, 14, 0, scale)
+    hsh = np.zeros((W, ld_sh), hx.dtype)
+    U.bits(hsh, dtype)[:] = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
+    oracle.reduce_scatter_ring(W, dtype, hx, hsh, M, pre)
+    got = U.to_host(sh, dtype)
+    assert np.array_equal(U.bits(got, dtype), U.bits(hsh, dtype))
+    if L:
+        a = _as_f64(got[:, :L], dtype)
+        b = _as_f64(U.to_host(rk, dtype)[:, :L], dtype)
+        U.say("  ring vs rank order: max |diff| / max |x| =",
+              float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30)))
+
+
+def test_reduce_scatter_ring_7b_layer_full_size():
+    """The 7B-layer workload at full size, ring order, on sampled columns:
+    the sampled columns of every shard are gathered into a small slab whose
+    chunk s holds shard s's samples, so the oracle's ring folds them starting
+    at the same rank."""
+    import torch
+    w = wl.rs_ag_w8()
+    W, M, dtype = w.W, w.M, w.dtype
+    L = M // W
+    U.say("ring rs full size", M)
+    x = U.gen_slab(dtype, W, w.ld, M, w.value_seed, 0, w.scale)
+    ld_sh = wl.round_up(L, 64)
+    sh = U.empty_slab(dtype, W, ld_sh)
+    dc.dc_reduce_scatter_ring(W, dtype, x, w.ld, sh, ld_sh, M, 1)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    ks = np.unique(np.concatenate([[0, 7, 8, L - 1], rng.integers(0, L, 2000)]))
+    n = len(ks)
+    got = sh[:, torch.from_numpy(ks).cuda()].cpu().numpy().view(np.uint16)
+    cols = np.concatenate([s * L + ks for s in range(W)])
+    slab = np.stack([synth.gather(dtype, w.value_seed, r, w.scale, cols) for r in range(W)])
+    out = np.zeros((W, n), np.uint16)
+    oracle.reduce_scatter_ring(W, dtype, slab, out, W * n, 1)
+    assert np.array_equal(got, out)
+
+
+AGS_CASES = [(W, dtype, L, algo) for (W, dtype, L) in
+             [(4, wl.DT_BF16, 1000), (8, wl.DT_F32, 333), (5, wl.DT_BF16, 77), (16, wl.DT_BF16, 2048),
+              (1, wl.DT_F32, 64), (2, wl.DT_BF16, 9), (3, wl.DT_F32, 0)]
+             for algo in (dc.DC_SCHED_RING, dc.DC_SCHED_BIDIR, dc.DC_SCHED_RD)
+             if algo != dc.DC_SCHED_RD or W & (W - 1) == 0]
+
+
+@pytest.mark.parametrize("W,dtype,L,algo", AGS_CASES, ids=lambda v: str(v))
+def test_all_gather_step_schedules(W, dtype, L, algo):
+    """Every step of the ring, bidirectional-ring and recursive-doubling
+    schedules against the oracle's step executor (bit-exact, including the
+    chunks not yet delivered, which keep the sentinel); the finished buffer
+    is the rank-order gather."""
+    import torch
+    U.say("ag step", W, dtype, L, algo)
+    ld_sh = max(64, wl.round_up(L, 64))
+    ld = max(64, wl.round_up(W * L, 64))
+    scale = wl.sigma_scale(1e-2)
+    sh = U.gen_slab(dtype, W, ld_sh, L, 16, 0, scale)
+    hsh = U.host_slab(dtype, W, ld_sh, L, 16, 0, scale)
+    out = U.empty_slab(dtype, W, ld)
+    ho = np.zeros((W, ld), hsh.dtype)
+    U.bits(ho, dtype)[:] = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
+    steps = {dc.DC_SCHED_RING: W - 1, dc.DC_SCHED_BIDIR: W // 2,
+             dc.DC_SCHED_RD: W.bit_length() - 1}[algo]
+    for s in range(steps + 1):
+        dc.dc_all_gather_step(W, dtype, sh, ld_sh, out, ld, L, algo, s)
+        oracle.all_gather_step(W, dtype, hsh, ho, L, algo, s)
+        torch.cuda.synchronize()
+        assert np.array_equal(U.bits(U.to_host(out, dtype), dtype), U.bits(ho, dtype)), s
+    rank = U.empty_slab(dtype, W, ld)
+    dc.dc_all_gather(W, dtype, sh, ld_sh, rank, ld, L, dc.DC_ORDER_RANK, -1)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :W * L], rank[:, :W * L])
+
+
 def test_reduce_scatter_all_gather_7b_layer_full_size():
     """The 7B-layer workload at full size (M = 202,383,360, W = 8): shards on
     sampled columns against the oracle, then AllReduce = ReduceScatter +

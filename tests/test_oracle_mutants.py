@@ -76,6 +76,24 @@ MUTANTS = {
     "rsv_wrong_destination_row": (
         "      store_val(dtype, out, ld_out, q, k, acc);",
         "      store_val(dtype, out, ld_out, (q + 1) % W, k, acc);"),
+    "ring_rs_wrong_holder": (
+        "int holder = (c - 1 + W) % W;",
+        "int holder = (c - 2 + 2 * W) % W;"),
+    "ring_rs_sends_left": (
+        "int src = (i - 1 + W) % W;",
+        "int src = (i + 1) % W;"),
+    "bidir_floor_step_count": (
+        "int32_t steps = algo == 0 ? N - 1 : algo == 1 ? N / 2 : 0;",
+        "int32_t steps = algo == 0 ? N - 1 : algo == 1 ? (N - 1) / 2 : 0;"),
+    "bidir_chunk_taken_twice": (
+        "if (algo == 1 && !held[(int64_t)i * N + nr[i]]) {",
+        "if (algo == 1) {"),
+    "ag_step_forwards_own_chunk": (
+        "        from_left[i] = nl[i];\n",
+        "        from_left[i] = from_left[i];\n"),
+    "ag_step0_wrong_position": (
+        "memcpy((char*)out + ((int64_t)i * ld_out + (int64_t)i * L) * eb,",
+        "memcpy((char*)out + ((int64_t)i * ld_out + (int64_t)((i + 1) % W) * L) * eb,"),
     "rd_partner_plus": (
         "int q = i ^ d;",
         "int q = (i + d) % N;"),
