@@ -49,6 +49,9 @@ def load_library(path):
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _vp, _vp, ctypes.c_int32]
     L.or_flush_zero2.restype = None
+    L.or_flush_buffers.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                   _vp, _vp, _vp, _vp, ctypes.c_int32]
+    L.or_flush_buffers.restype = None
     L.or_relayout_map.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp,
                                   ctypes.c_int64, _vp, _vp]
     L.or_relayout_map.restype = ctypes.c_int64
@@ -200,6 +203,28 @@ def flush_zero2(W, dtype, slab_in, slab_out, bucket_col, t_off, t_numel, t_param
                          bucket_col, len(t_off), _p(t_off), _p(t_numel), _p(t_param), _p(t_comm),
                          _p(fo), _p(ps), _p(cs), _p(cst), pre_div)
     return slab_out
+
+
+def flush_buffers(W, dtype, in_arena, in_off, out_arena, out_off, t_numel, t_comm, comm_size,
+                  comm_stride, pre_div):
+    """Flush straight from per-rank gradient buffers into per-rank grad
+    buffers: in_off / out_off are [n_tasks, W] element offsets into the flat
+    arenas (out_off -1: that rank's buffer is empty)."""
+    arr = np.uint16 if dtype == BF16 else np.float32
+    assert in_arena.dtype == arr and out_arena.dtype == arr
+    assert in_arena.flags.c_contiguous and out_arena.flags.c_contiguous
+    n = len(t_numel)
+    in_off = _c(np.asarray(in_off).reshape(n * W), np.int64)
+    out_off = _c(np.asarray(out_off).reshape(n * W), np.int64)
+    for t in range(n):
+        for r in range(W):
+            assert 0 <= in_off[t * W + r] and in_off[t * W + r] + t_numel[t] <= in_arena.size
+            o = out_off[t * W + r]
+            assert o == -1 or (0 <= o and o + t_numel[t] <= out_arena.size)
+    lib().or_flush_buffers(W, dtype, _p(in_arena), _p(in_off), _p(out_arena), _p(out_off), n,
+                           _p(_c(t_numel, np.int64)), _p(_c(t_comm, np.int32)),
+                           _p(_c(comm_size, np.int32)), _p(_c(comm_stride, np.int32)), pre_div)
+    return out_arena
 
 
 def relayout_map(W, t_off, t_numel, t_param, t_comm, flat_offset, part_size, bucket_numel):

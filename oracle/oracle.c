@@ -242,6 +242,42 @@ void or_flush_zero2(int32_t W, int32_t dtype, const void* in, int64_t ld_in, voi
   }
 }
 
+/* Bucket flush with copy-in and copy-out done in place of the bucket
+ * ([DS] problem statement: gradients reach the bucket from the ranks, and the
+ * copy-out after the reduction skips every rank whose gradient buffer is
+ * empty; "Describe the solution": copy-out is unchanged and still correct).
+ * Rank r's gradient of task t lives at in[in_off[t*W + r] + e], e < numel;
+ * rank r's gradient buffer for it at out[out_off[t*W + r] + e], or nowhere
+ * when out_off is -1 (an empty buffer).  Every block of the task's
+ * communicator folds its members in ascending order, exactly as the bucket
+ * flush does, and the sum is copied into the buffer of every member that has
+ * one; nothing else is written.  in and out are flat arrays of the dtype. */
+void or_flush_buffers(int32_t W, int32_t dtype, const void* in, const int64_t* in_off, void* out,
+                      const int64_t* out_off, int32_t n_tasks, const int64_t* t_numel,
+                      const int32_t* t_comm, const int32_t* comm_size, const int32_t* comm_stride,
+                      int32_t pre_div) {
+  for (int32_t t = 0; t < n_tasks; ++t) {
+    int c = comm_size[t_comm[t]];
+    int s = comm_stride[t_comm[t]];
+    int nb = W / c;
+    for (int64_t e = 0; e < t_numel[t]; ++e) {
+      for (int b = 0; b < nb; ++b) {
+        float sum = 0.0f;
+        for (int i = 0; i < c; ++i) {
+          int r = member(b, i, c, s);
+          float v = contribution(dtype, load_val(dtype, in, 0, 0, in_off[(int64_t)t * W + r] + e), pre_div, c);
+          sum = (i == 0) ? v : sum + v;
+        }
+        for (int i = 0; i < c; ++i) {
+          int r = member(b, i, c, s);
+          int64_t o = out_off[(int64_t)t * W + r];
+          if (o >= 0) store_val(dtype, out, 0, 0, o + e, sum);
+        }
+      }
+    }
+  }
+}
+
 /* Bucket relayout for a reduce-scatter ([DS] "Describe alternatives": a
  * reduce-scatter over the bucket needs the payload contiguous by destination
  * rank).  Every element of a data-parallel task with partition size S > 0

@@ -674,6 +674,82 @@ def pin_relayout_reduce_scatter():
             assert sb[q, dest[c] - seg[q]] == zb[q, c], (trial, c, q)
 
 
+def _scatter_layout(rng, sizes, gap=3):
+    """Disjoint offsets for buffers of the given sizes, in shuffled order with
+    random gaps; returns (offsets, arena size)."""
+    order = list(range(len(sizes)))
+    rng.shuffle(order)
+    off = [0] * len(sizes)
+    pos = rng.randint(0, gap)
+    for k in order:
+        off[k] = pos
+        pos += sizes[k] + rng.randint(0, gap)
+    return off, pos + 1
+
+
+def pin_flush_buffers():
+    """Flush straight from per-rank gradient buffers into per-rank grad
+    buffers equals copy-in to a bucket, the bucket flush, then copy-out into
+    the non-empty buffers ([DS] problem statement), bit for bit, with every
+    other element untouched; with one holder per data-parallel task it also
+    equals the reduce-to-owner flush followed by the same copy-out ([DS]:
+    copy-out unchanged and still correct); in place, holders get the sum and
+    every other buffer keeps its gradient."""
+    rng = random.Random(83)
+    cases = [(4, BF16, 1, [(4, 1), (2, 1), (2, 2)]), (4, F32, 0, [(4, 1), (2, 1), (2, 2)]),
+             (8, BF16, 0, [(8, 1), (4, 1), (2, 4)]), (6, F32, 1, [(6, 1), (3, 1), (2, 3)])]
+    for W, dtype, pre, comms in cases:
+        cs, cst = [c for c, _ in comms], [s for _, s in comms]
+        numel = [0, 1, 13, 8, 5, 9, 16, 3]
+        n = len(numel)
+        t_comm = [rng.randrange(len(comms)) for _ in range(n)]
+        t_comm[2], t_comm[3] = 0, 0
+        hold = [[rng.random() < 0.4 for _ in range(W)] for _ in range(n)]
+        hold[2] = [r == 1 for r in range(W)]          # one owner
+        hold[3] = [True] * W                          # every rank
+        hold[4] = [False] * W                         # nobody keeps it
+        in_off, in_size = _scatter_layout(rng, [numel[t] for t in range(n) for _ in range(W)])
+        held = [(t, r) for t in range(n) for r in range(W) if hold[t][r]]
+        o_off, out_size = _scatter_layout(rng, [numel[t] for t, _ in held])
+        out_off = np.full((n, W), -1, np.int64)
+        for (t, r), o in zip(held, o_off):
+            out_off[t, r] = o
+        in_off = np.array(in_off, np.int64).reshape(n, W)
+        arena = random_bits(rng, dtype, (in_size,))
+        sent = np.zeros(out_size, arena.dtype)
+        if dtype == BF16:
+            sent[:] = 0x7E7E
+        else:
+            sent.view(np.uint32)[:] = 0x7E7E7E7E
+        got = oracle.flush_buffers(W, dtype, arena, in_off, sent.copy(), out_off, numel, t_comm, cs,
+                                   cst, pre)
+        # copy-in, bucket flush, copy-out
+        t_off = np.concatenate([[0], np.cumsum(numel)[:-1]]).astype(np.int64)
+        M = int(sum(numel))
+        slab = np.zeros((W, M), arena.dtype)
+        for t in range(n):
+            for r in range(W):
+                slab[r, t_off[t]:t_off[t] + numel[t]] = arena[in_off[t, r]:in_off[t, r] + numel[t]]
+        for owner in (None, [1 if t == 2 else -1 for t in range(n)]):
+            bo = np.zeros_like(slab)
+            ow = None if owner is None else np.array(owner, np.int32)
+            oracle.flush(W, dtype, slab, bo, 0, t_off, numel, list(range(n)), t_comm, ow, cs, cst, pre)
+            want = sent.copy()
+            for t, r in held:
+                o = out_off[t, r]
+                want[o:o + numel[t]] = bo[r, t_off[t]:t_off[t] + numel[t]]
+            assert np.array_equal(out_bits(dtype, got), out_bits(dtype, want)), (W, dtype, owner)
+        # in place: the output buffers are the holders' own gradient buffers
+        inplace = arena.copy()
+        ip_off = np.where(out_off >= 0, in_off, -1)
+        oracle.flush_buffers(W, dtype, inplace, in_off, inplace, ip_off, numel, t_comm, cs, cst, pre)
+        want = arena.copy()
+        for t, r in held:
+            o = in_off[t, r]
+            want[o:o + numel[t]] = got[out_off[t, r]:out_off[t, r] + numel[t]]
+        assert np.array_equal(out_bits(dtype, inplace), out_bits(dtype, want)), (W, dtype, "in place")
+
+
 # ---------------------------------------------------------------------------
 # ring and recursive-doubling all-gather
 # ---------------------------------------------------------------------------
@@ -957,7 +1033,7 @@ ALL_PINS = [
     pin_prediv_non_power_of_two, pin_reduce_scatter_all_gather, pin_ring_reduce_scatter, pin_partition_brute_force,
     pin_owner_rules, pin_group_eligibility, pin_probe_printed_example, pin_ratio_printed_example,
     pin_probe_closed_forms, pin_owner_path_equivalences, pin_zero2_routing,
-    pin_relayout_reduce_scatter, pin_ring_table, pin_ring_closed_form,
+    pin_relayout_reduce_scatter, pin_flush_buffers, pin_ring_table, pin_ring_closed_form,
     pin_rd_table, pin_ring_step_replay, pin_ag_step_executors, pin_deferred_ga1_identity,
     pin_accumulate_zero_start, pin_deferred_exact_reassociation, pin_deferred_tolerance, pin_deferred_restore,
     pin_deferred_round_trip,

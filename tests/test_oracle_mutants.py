@@ -76,6 +76,15 @@ MUTANTS = {
     "rsv_wrong_destination_row": (
         "      store_val(dtype, out, ld_out, q, k, acc);",
         "      store_val(dtype, out, ld_out, (q + 1) % W, k, acc);"),
+    "buffers_first_holder_only": (
+        "if (o >= 0) store_val(dtype, out, 0, 0, o + e, sum);",
+        "if (o >= 0) { store_val(dtype, out, 0, 0, o + e, sum); break; }"),
+    "buffers_neighbour_gradient": (
+        "load_val(dtype, in, 0, 0, in_off[(int64_t)t * W + r] + e)",
+        "load_val(dtype, in, 0, 0, in_off[(int64_t)t * W + (r + 1) % W] + e)"),
+    "buffers_element_shift": (
+        "store_val(dtype, out, 0, 0, o + e, sum);",
+        "store_val(dtype, out, 0, 0, o + (e + 1) % t_numel[t], sum);"),
     "ring_rs_wrong_holder": (
         "int holder = (c - 1 + W) % W;",
         "int holder = (c - 2 + 2 * W) % W;"),
