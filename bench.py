@@ -17,7 +17,9 @@ through the AllReduce and ZeRO-2 paths), mixed and zero2_mixed (W=16 fp32
 rs_ag (7B layer reduce-scatter + all-gather), schedules_w8 (7B layer, ring-
 order reduce-scatter and the ring / bidirectional-ring / recursive-doubling
 all-gather step executors), relayout_rs_w8 (relayout by destination +
-reduce-scatter-v), tiny (W=4 flush).
+reduce-scatter-v), fused_w8 and fused_mixed (the flush with copy-in and
+copy-out fused in, from per-rank gradient buffers into per-rank grad
+buffers), tiny (W=4 flush).
 """
 import argparse
 import json
@@ -144,11 +146,12 @@ def bench_flush(args, w, reduce_to_owner=True, zero2=False):
     return ms_step, value, step_bytes, roofline, extra
 
 
-def access_mix_ceiling(w, owner, x, y, ld, psize=None):
+def access_mix_ceiling(w, owner, x, y, ld, psize=None, split=None):
     """Bandwidth the memory system gives the flush's own access mix: W rows
     read and one row written (owned tasks) or W rows written (AllReduce
     tasks), measured with dc_stream_rows (xor only) at the bucket size and
-    blended by the step's bytes.  None when W has no reference kernel."""
+    blended by the step's bytes (split = (one-row bytes, W-row bytes) when
+    given).  None when W has no reference kernel."""
     import torch
     from gradient_reduction_amd import dc
     if w.W not in (4, 8, 16):
@@ -174,6 +177,8 @@ def access_mix_ceiling(w, owner, x, y, ld, psize=None):
     own = ar = 0
     for bk in w.buckets:
         for t in bk.tasks:
+            if split is not None:
+                break
             if psize is not None:
                 one = t.comm == 0 and psize[t.param] > 0
             else:
@@ -182,10 +187,117 @@ def access_mix_ceiling(w, owner, x, y, ld, psize=None):
                 own += (w.W + 1) * t.numel * b
             else:
                 ar += 2 * w.W * t.numel * b
+    if split is not None:
+        own, ar = split
     ceiling = (own + ar) / (own / rates[1] + ar / rates[w.W])
     log(f"[bench] access-mix reference: read {w.W} write 1 {rates[1]:.1f} GB/s, read {w.W} "
         f"write {w.W} {rates[w.W]:.1f} GB/s; blended for this step {ceiling:.1f} GB/s")
     return ceiling
+
+
+def bench_flush_buffers(args, w):
+    """The flush with copy-in and copy-out fused in: each rank's gradient of
+    every param in a per-rank arena (params at 128-byte aligned positions, as
+    separate allocations would be), grad buffers of the same layout for the
+    ranks that keep one, one dc_flush_bucket_buffers launch per bucket."""
+    import torch
+    import synth
+    from gradient_reduction_amd import executor
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    eb = w.elem_bytes()
+    dt = torch.int16 if w.dtype == 0 else torch.int32
+    ex = executor.from_workload(w, reduce_to_owner=True, log=log)
+    ex.build_owner_map()
+    ex.fetch_metadata()
+    # every param is one task here, so its slab columns are contiguous
+    pcol = np.full(w.P, -1, np.int64)
+    for bk in w.buckets:
+        for t in bk.tasks:
+            assert pcol[t.param] < 0, "a param split over tasks"
+            pcol[t.param] = bk.col + t.offset
+    pad = 128 // eb
+    poff = np.zeros(w.P, np.int64)
+    pos = 0
+    for p in range(w.P):
+        poff[p] = pos
+        pos = -(-(pos + w.numel[p]) // pad) * pad
+    ld = -(-max(pos, 1) // 64) * 64
+    log(f"[bench] {w.name}: fused copy-in/out flush, arenas [{w.W}, {ld}] "
+        f"({2 * w.W * ld * eb / 1e9:.2f} GB in + out)")
+    x = torch.empty((w.W, ld), dtype=dt, device=dev)
+    for p in range(w.P):
+        if w.numel[p]:
+            synth.fill_slab_device(w.dtype, w.value_seed, 0, w.scale, w.W, ld, w.numel[p],
+                                   x.data_ptr() + int(poff[p]) * eb, stream.cuda_stream,
+                                   col0=int(pcol[p]))
+    y = torch.zeros((w.W, ld), dtype=dt, device=dev)
+    hold = np.zeros((w.W, w.P), bool)
+    nb = len(w.buckets)
+    per_launch, one_b, many_b, unfused = [], 0, 0, 0
+    for b, bk in enumerate(w.buckets):
+        h = ex.holders(b)
+        tot = 0
+        for k, t in enumerate(bk.tasks):
+            hold[:, t.param] |= h[k]
+            nh = int(h[k].sum())
+            tot += w.W * t.numel * eb + nh * t.numel * eb + 32 + 16 * w.W
+            if nh <= 1:
+                one_b += (w.W + 1) * t.numel * eb
+            else:
+                many_b += (w.W + nh) * t.numel * eb
+            rows = 1 if (t.comm == 0 and ex.h_owner[t.param] >= 0) else w.W
+            # copy-in (read + write W rows), flush (read W, write `rows`), copy-out (holders)
+            unfused += (2 * w.W + w.W + rows + 2 * nh) * t.numel * eb + 32
+        per_launch.append(tot)
+    rows_i = np.arange(w.W, dtype=np.int64)[:, None] * ld
+    in_addr = (x.data_ptr() + (rows_i + poff[None, :]) * eb).astype(np.uint64)
+    out_addr = np.where(hold, y.data_ptr() + (rows_i + poff[None, :]) * eb, 0).astype(np.uint64)
+    ex.register_buffers(in_addr, out_addr)
+    step_bytes = sum(per_launch) + owner_map_bytes(w)
+
+    def step(timer=None):
+        ex.build_owner_map()
+        for b in range(nb):
+            if timer is not None:
+                timer.ev[b][0].record()
+            ex.flush_buffers(b)
+            if timer is not None:
+                timer.ev[b][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [Timer(torch, nb) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for k in range(args.steps):
+        step(timers[k])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    kern = np.array([tm.ms() for tm in timers])
+    gbs = sum(per_launch) / (kern.sum(axis=1).mean() / 1e3) / 1e9
+    value = step_bytes / (ms_step / 1e3) / 1e9
+    log(f"[bench] step {ms_step:.3f} ms, {value:.1f} GB/s; fused flush kernels "
+        f"{kern.sum(axis=1).mean():.3f} ms ({gbs:.1f} GB/s); per bucket ms "
+        f"{np.round(kern.mean(axis=0), 4).tolist()}")
+    ceiling = access_mix_ceiling(w, None, x, y, ld, split=(one_b, many_b))
+    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_flush_buffers", "launch_ms_avg": round(float(kern.mean()), 4),
+                "bytes_per_launch_avg": int(np.mean(per_launch))}
+    if ceiling is not None:
+        roofline["access_mix_ceiling_gbs"] = round(ceiling, 1)
+        roofline["frac_of_access_mix_ceiling"] = round(gbs / ceiling, 4)
+    extra = {"per_bucket_gbs": [round(b / (m / 1e3) / 1e9, 1) for b, m in zip(per_launch, kern.mean(axis=0))],
+             "fused_bytes_per_step": int(sum(per_launch)),
+             "unfused_bytes_per_step": int(unfused),
+             "bytes_saved_frac": round(1 - sum(per_launch) / unfused, 4)}
+    del x, y
+    torch.cuda.empty_cache()
+    return ms_step, value, step_bytes, roofline, extra
 
 
 def traffic_from_profile(w, per_launch):
@@ -520,7 +632,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="owner_w8",
                     choices=["owner_w8", "allreduce_w8", "zero2_w8", "mixed", "zero2_mixed",
-                             "deferred", "rs_ag", "schedules_w8", "relayout_rs_w8", "tiny"])
+                             "deferred", "rs_ag", "schedules_w8", "relayout_rs_w8", "fused_w8",
+                             "fused_mixed", "tiny"])
     ap.add_argument("--ga", type=int, default=8)
     ap.add_argument("--fused", action="store_true",
                     help="deferred workload: fuse the last accumulate into the reduce")
@@ -557,6 +670,14 @@ def main():
                   "step_bytes": step_bytes}
         if not args.no_cpu_baseline and not zero2:
             cpu = cpu_baseline_flush(w, owner_mode, max_buckets=2 if w.total > 1e8 else 1)
+    elif args.workload in ("fused_w8", "fused_mixed"):
+        w = wl.owner_flush_w8() if args.workload == "fused_w8" else wl.mixed_flush_w16()
+        ms, value, step_bytes, roof, extra = bench_flush_buffers(args, w)
+        name, dtype = w.name, wl.DTYPE_NAME[w.dtype]
+        config = {"workload": name, "W": w.W, "elements": w.total, "buckets": len(w.buckets),
+                  "mode": "copy-in/copy-out fused flush into per-rank grad buffers",
+                  "pre_div": w.pre_div, "step": "owner map + every bucket flush",
+                  "step_bytes": step_bytes}
     elif args.workload == "deferred":
         name, ms, value, roof, extra, dtype = bench_deferred(args)
         config = {"workload": name, "W": 4, "K": args.ga,

@@ -268,6 +268,69 @@ dc_status dc_flush_bucket_zero2(int32_t W, int32_t dtype, const void* slab_in, i
                       num_params, comms, num_comms, pre_div, stream);
 }
 
+dc_status dc_flush_bucket_buffers(int32_t W, int32_t dtype, int64_t bucket_numel,
+                                  const dc_task* tasks, int32_t num_tasks,
+                                  const void* const* in_ptrs, void* const* out_ptrs,
+                                  const dc_comm* comms, int32_t num_comms, int32_t pre_div,
+                                  void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype)) || (st = check_comms(W, comms, num_comms))) return st;
+  if (bucket_numel < 0 || num_tasks < 0)
+    return fail(DC_ERR_ARG, "bucket_numel=%lld, num_tasks=%d", (long long)bucket_numel, num_tasks);
+  if (num_tasks > 0 && (tasks == nullptr || in_ptrs == nullptr || out_ptrs == nullptr))
+    return fail(DC_ERR_NULL, "tasks, in_ptrs or out_ptrs is NULL");
+  if (pre_div != 0 && pre_div != 1) return fail(DC_ERR_ARG, "pre_div=%d", pre_div);
+  return hip_status(dc::launch_flush_buffers(W, dtype, bucket_numel, tasks, num_tasks, in_ptrs, out_ptrs,
+                                             comms, num_comms, pre_div, static_cast<hipStream_t>(stream)),
+                    "buffer flush launch");
+}
+
+dc_status dc_validate_buffer_tasks(int32_t W, int32_t dtype, const dc_task* tasks, int32_t num_tasks,
+                                   int64_t bucket_numel, const dc_comm* comms, int32_t num_comms,
+                                   const void* const* in_ptrs, void* const* out_ptrs) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype)) || (st = check_comms(W, comms, num_comms))) return st;
+  if (num_tasks < 0 || bucket_numel < 0) return fail(DC_ERR_ARG, "num_tasks or bucket_numel < 0");
+  if (num_tasks > 0 && (tasks == nullptr || in_ptrs == nullptr || out_ptrs == nullptr))
+    return fail(DC_ERR_NULL, "tasks, in_ptrs or out_ptrs is NULL");
+  int64_t pos = 0;
+  for (int32_t t = 0; t < num_tasks; ++t) {
+    const dc_task& k = tasks[t];
+    if (k.numel < 0) return fail(DC_ERR_TASKS, "task %d: numel %lld < 0", t, (long long)k.numel);
+    if (k.offset < pos) return fail(DC_ERR_TASKS, "task %d: offset %lld overlaps the previous task (ends at %lld)", t, (long long)k.offset, (long long)pos);
+    if (k.offset + k.numel > bucket_numel) return fail(DC_ERR_TASKS, "task %d ends past bucket_numel=%lld", t, (long long)bucket_numel);
+    if (k.comm < 0 || k.comm >= num_comms) return fail(DC_ERR_TASKS, "task %d: comm %d outside [0, %d)", t, k.comm, num_comms);
+    pos = k.offset + k.numel;
+  }
+  // byte intervals; an input identical to its own output is the in-place pair
+  struct Iv { uintptr_t a, b; int out; int32_t t, r; };
+  std::vector<Iv> iv;
+  const uintptr_t eb = (uintptr_t)elem_bytes(dtype);
+  for (int32_t t = 0; t < num_tasks; ++t) {
+    if (tasks[t].numel == 0) continue;
+    const uintptr_t len = (uintptr_t)tasks[t].numel * eb;
+    for (int32_t r = 0; r < W; ++r) {
+      const uintptr_t in = reinterpret_cast<uintptr_t>(in_ptrs[(int64_t)t * W + r]);
+      const uintptr_t out = reinterpret_cast<uintptr_t>(out_ptrs[(int64_t)t * W + r]);
+      if (in == 0) return fail(DC_ERR_TASKS, "task %d rank %d: input pointer is NULL", t, r);
+      if (out != 0) iv.push_back({out, out + len, 1, t, r});
+      if (out != in) iv.push_back({in, in + len, 0, t, r});
+    }
+  }
+  std::sort(iv.begin(), iv.end(), [](const Iv& x, const Iv& y) { return x.a < y.a || (x.a == y.a && x.out > y.out); });
+  uintptr_t end_all = 0, end_out = 0;
+  int32_t who_all = -1, who_out = -1, rank_all = -1, rank_out = -1;
+  for (const Iv& x : iv) {
+    if (x.out && x.a < end_all)
+      return fail(DC_ERR_TASKS, "output of task %d rank %d overlaps a buffer of task %d rank %d", x.t, x.r, who_all, rank_all);
+    if (!x.out && x.a < end_out)
+      return fail(DC_ERR_TASKS, "input of task %d rank %d overlaps the output of task %d rank %d", x.t, x.r, who_out, rank_out);
+    if (x.b > end_all) { end_all = x.b; who_all = x.t; rank_all = x.r; }
+    if (x.out && x.b > end_out) { end_out = x.b; who_out = x.t; rank_out = x.r; }
+  }
+  return ok();
+}
+
 dc_status dc_probe_flush(int32_t W, int32_t dtype, const dc_task* tasks, int32_t num_tasks,
                          const int32_t* owner, int32_t num_params, const int32_t* pid_offsets,
                          const int32_t* pids, const dc_comm* comms, int32_t num_comms,

@@ -60,4 +60,112 @@ __device__ __forceinline__ void store16(u32x4* p, u32x4 v) {
   else *p = v;
 }
 
+// ---------------------------------------------------------------------------
+// Folding helpers shared by the streaming kernels.  A contribution is
+// pre-divided by the communicator size c when PRE is set: a multiply by the
+// exact reciprocal inv when c is a power of two (bit-identical to the
+// division), a true division otherwise (inv == 0), then rounded to the dtype.
+// ---------------------------------------------------------------------------
+
+template <bool BF16, bool PRE>
+__device__ __forceinline__ void fold16(float* acc, u32x4 x, bool first, float inv, float c) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float a = bf16_lo(x[q]), b = bf16_hi(x[q]);
+      if constexpr (PRE) {
+        if (inv != 0.0f) { a *= inv; b *= inv; } else { a = a / c; b = b / c; }
+        bf16_round_pair(a, b);
+      }
+      acc[2 * q] = first ? a : acc[2 * q] + a;
+      acc[2 * q + 1] = first ? b : acc[2 * q + 1] + b;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float a = __uint_as_float(x[q]);
+      if constexpr (PRE) a = inv != 0.0f ? a * inv : a / c;
+      acc[q] = first ? a : acc[q] + a;
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ u32x4 pack16(const float* acc) {
+  u32x4 y;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] = bf16_pack_out(acc[2 * q], acc[2 * q + 1]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] = __float_as_uint(acc[q]);
+  }
+  return y;
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* base, int64_t idx) {
+  if constexpr (BF16) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[idx] << 16);
+  else return reinterpret_cast<const float*>(base)[idx];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_elem(void* base, int64_t idx, float v) {
+  if constexpr (BF16) reinterpret_cast<uint16_t*>(base)[idx] = bf16_out(v);
+  else reinterpret_cast<float*>(base)[idx] = v;
+}
+
+template <bool BF16>
+__device__ __forceinline__ float pre_elem(float x, bool pre, float inv, float c) {
+  if (!pre) return x;
+  float v = inv != 0.0f ? x * inv : x / c;
+  if constexpr (BF16) v = bf16_lo(bf16_pack_rne(v, 0.0f));
+  return v;
+}
+
+// Block-wide k-ary search over n sorted keys: r1 = #{i : key(i) <= x1},
+// r2 = #{i : key(i) < x2}.  Each round the block probes kThreads evenly spaced
+// keys of both ranges and keeps the bracket the counts point to.  Every thread
+// of the block must call it (it synchronizes).
+template <class Key>
+__device__ void kary_bounds(int32_t n, Key key, int64_t x1, int64_t x2, int32_t& r1, int32_t& r2) {
+  int32_t lo1 = 0, hi1 = n, lo2 = 0, hi2 = n;
+  while (lo1 < hi1 || lo2 < hi2) {
+    const int32_t st1 = (hi1 - lo1 + kThreads - 1) / kThreads;
+    const int32_t st2 = (hi2 - lo2 + kThreads - 1) / kThreads;
+    const int32_t q1 = lo1 + (int32_t)threadIdx.x * st1;
+    const int32_t q2 = lo2 + (int32_t)threadIdx.x * st2;
+    const bool p1 = lo1 < hi1 && q1 < hi1 && key(q1) <= x1;
+    const bool p2 = lo2 < hi2 && q2 < hi2 && key(q2) < x2;
+    const int32_t n1 = __syncthreads_count(p1);
+    const int32_t n2 = __syncthreads_count(p2);
+    if (lo1 < hi1) {
+      const int32_t k1 = (hi1 - lo1 + st1 - 1) / st1;
+      const int32_t nlo = n1 >= 1 ? lo1 + (n1 - 1) * st1 + 1 : lo1;
+      const int32_t nhi = n1 < k1 ? lo1 + n1 * st1 : hi1;
+      lo1 = nlo;
+      hi1 = nhi;
+    }
+    if (lo2 < hi2) {
+      const int32_t k2 = (hi2 - lo2 + st2 - 1) / st2;
+      const int32_t nlo = n2 >= 1 ? lo2 + (n2 - 1) * st2 + 1 : lo2;
+      const int32_t nhi = n2 < k2 ? lo2 + n2 * st2 : hi2;
+      lo2 = nlo;
+      hi2 = nhi;
+    }
+  }
+  r1 = lo1;
+  r2 = lo2;
+}
+
+// Index of the last of cnt sorted keys (in LDS) that is <= x, or 0.
+__device__ __forceinline__ int32_t last_le(const int64_t* key, int32_t cnt, int64_t x) {
+  int32_t lo = 0, hi = cnt;
+  while (hi - lo > 1) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (key[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 }  // namespace dc

@@ -65,6 +65,11 @@ hipError_t launch_relayout(int32_t W, int32_t dtype, const void* in, int64_t ld_
                            const dc_piece* pieces, int32_t npieces, int64_t out_numel,
                            hipStream_t stream);
 
+hipError_t launch_flush_buffers(int32_t W, int32_t dtype, int64_t bucket_numel, const dc_task* tasks,
+                                int32_t num_tasks, const void* const* in_ptrs, void* const* out_ptrs,
+                                const dc_comm* comms, int32_t num_comms, int32_t pre_div,
+                                hipStream_t stream);
+
 hipError_t launch_reduce_scatter_ring(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
                                       void* out, int64_t ld_out, int64_t M, int32_t pre_div,
                                       hipStream_t stream);

@@ -27,48 +27,6 @@ struct RelayoutParams {
   int64_t bucket_numel;
 };
 
-// Number of pieces with dst <= x1 and with dst < x2 (pieces sorted by dst);
-// a k-ary search over 256 probes per round, as in the flush.
-__device__ void find_pieces(const dc_piece* t, int32_t n, int64_t x1, int64_t x2, int32_t& r1,
-                            int32_t& r2) {
-  int32_t lo1 = 0, hi1 = n, lo2 = 0, hi2 = n;
-  while (lo1 < hi1 || lo2 < hi2) {
-    const int32_t st1 = (hi1 - lo1 + kThreads - 1) / kThreads;
-    const int32_t st2 = (hi2 - lo2 + kThreads - 1) / kThreads;
-    const int32_t q1 = lo1 + (int32_t)threadIdx.x * st1;
-    const int32_t q2 = lo2 + (int32_t)threadIdx.x * st2;
-    const bool p1 = lo1 < hi1 && q1 < hi1 && t[q1].dst <= x1;
-    const bool p2 = lo2 < hi2 && q2 < hi2 && t[q2].dst < x2;
-    const int32_t n1 = __syncthreads_count(p1);
-    const int32_t n2 = __syncthreads_count(p2);
-    if (lo1 < hi1) {
-      const int32_t k1 = (hi1 - lo1 + st1 - 1) / st1;
-      const int32_t nlo = n1 >= 1 ? lo1 + (n1 - 1) * st1 + 1 : lo1;
-      const int32_t nhi = n1 < k1 ? lo1 + n1 * st1 : hi1;
-      lo1 = nlo;
-      hi1 = nhi;
-    }
-    if (lo2 < hi2) {
-      const int32_t k2 = (hi2 - lo2 + st2 - 1) / st2;
-      const int32_t nlo = n2 >= 1 ? lo2 + (n2 - 1) * st2 + 1 : lo2;
-      const int32_t nhi = n2 < k2 ? lo2 + n2 * st2 : hi2;
-      lo2 = nlo;
-      hi2 = nhi;
-    }
-  }
-  r1 = lo1;
-  r2 = lo2;
-}
-
-__device__ __forceinline__ int32_t staged_piece(const int64_t* dst, int32_t cnt, int64_t x) {
-  int32_t lo = 0, hi = cnt;
-  while (hi - lo > 1) {
-    const int32_t mid = (lo + hi) >> 1;
-    if (dst[mid] <= x) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 // One workgroup per tile of 256*U destination vectors (16 bytes of every
 // row).  A vector inside one piece whose source is vector aligned moves as W
 // 16-byte loads and stores; any other vector moves element by element.
@@ -86,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void k_relayout(RelayoutParams p) {
   const int64_t t1 = min(t0 + (int64_t)(kThreads * kRelayoutU), nvec);
   const int64_t lo = t0 * E, hi = min(t1 * E, p.out_numel);
   int32_t first, last;
-  find_pieces(p.pieces, p.npieces, lo, hi, first, last);
+  kary_bounds(p.npieces, [&](int32_t i) { return p.pieces[i].dst; }, lo, hi, first, last);
   first = max(first - 1, 0);
   last = last - 1;
   const char* in = reinterpret_cast<const char*>(p.in);
@@ -108,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void k_relayout(RelayoutParams p) {
       if (v >= t1) break;
       const int64_t d0 = v * E;
       const int64_t d1 = min(d0 + E, p.out_numel);
-      const int32_t k = staged_piece(s_dst, cnt, d0);
+      const int32_t k = last_le(s_dst, cnt, d0);
       const int64_t src0 = s_src[k] + (d0 - s_dst[k]);
       const bool whole = d1 == d0 + E && s_dst[k] <= d0 && s_end[k] >= d1 &&
                          (p.bucket_col + src0) % E == 0 && src0 >= 0 && src0 + E <= p.bucket_numel;
@@ -127,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void k_relayout(RelayoutParams p) {
         }
       } else {
         for (int64_t d = d0; d < d1; ++d) {
-          const int32_t kk = staged_piece(s_dst, cnt, d);
+          const int32_t kk = last_le(s_dst, cnt, d);
           if (!(s_dst[kk] <= d && d < s_end[kk])) continue;
           const int64_t sc = s_src[kk] + (d - s_dst[kk]);
           if (sc < 0 || sc >= p.bucket_numel) continue;

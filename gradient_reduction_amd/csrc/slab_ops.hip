@@ -41,46 +41,6 @@ constexpr bool kNT = DC_SLAB_NT != 0;
 constexpr bool kNTS = DC_SLAB_NTS != 0;
 constexpr bool kAgNTS = DC_AG_NTS != 0;
 
-// ---------------------------------------------------------------------------
-// fold helpers
-// ---------------------------------------------------------------------------
-
-template <bool BF16, bool PRE>
-__device__ __forceinline__ void fold16(float* acc, u32x4 x, bool first, float inv, float c) {
-  if constexpr (BF16) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float a = bf16_lo(x[q]), b = bf16_hi(x[q]);
-      if constexpr (PRE) {
-        if (inv != 0.0f) { a *= inv; b *= inv; } else { a = a / c; b = b / c; }
-        bf16_round_pair(a, b);
-      }
-      acc[2 * q] = first ? a : acc[2 * q] + a;
-      acc[2 * q + 1] = first ? b : acc[2 * q + 1] + b;
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float a = __uint_as_float(x[q]);
-      if constexpr (PRE) a = inv != 0.0f ? a * inv : a / c;
-      acc[q] = first ? a : acc[q] + a;
-    }
-  }
-}
-
-template <bool BF16>
-__device__ __forceinline__ u32x4 pack16(const float* acc) {
-  u32x4 y;
-  if constexpr (BF16) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) y[q] = bf16_pack_out(acc[2 * q], acc[2 * q + 1]);
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) y[q] = __float_as_uint(acc[q]);
-  }
-  return y;
-}
-
 // Fold the W rows of vector column `v` (rows `ldv` vectors apart).  With W
 // known at compile time every row load is issued before the first add.
 template <bool BF16, int WT, bool PRE>
@@ -99,26 +59,6 @@ __device__ __forceinline__ u32x4 fold_rows(const u32x4* in, int64_t ldv, int64_t
     for (int32_t r = 0; r < W; ++r) fold16<BF16, PRE>(acc, load16<kNT>(in + r * ldv + v), r == 0, inv, c);
   }
   return pack16<BF16>(acc);
-}
-
-template <bool BF16>
-__device__ __forceinline__ float load_elem(const void* base, int64_t idx) {
-  if constexpr (BF16) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[idx] << 16);
-  else return reinterpret_cast<const float*>(base)[idx];
-}
-
-template <bool BF16>
-__device__ __forceinline__ void store_elem(void* base, int64_t idx, float v) {
-  if constexpr (BF16) reinterpret_cast<uint16_t*>(base)[idx] = bf16_out(v);
-  else reinterpret_cast<float*>(base)[idx] = v;
-}
-
-template <bool BF16>
-__device__ __forceinline__ float pre_elem(float x, bool pre, float inv, float c) {
-  if (!pre) return x;
-  float v = inv != 0.0f ? x * inv : x / c;
-  if constexpr (BF16) v = bf16_lo(bf16_pack_rne(v, 0.0f));
-  return v;
 }
 
 // ---------------------------------------------------------------------------

@@ -55,6 +55,8 @@ _SIGS = {
     "dc_validate_tasks": ([_i32, _vp, _i32, _i64, _i32, _vp, _i32], _i32),
     "dc_flush_bucket": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _vp,
                          _i32, _i32, _vp], _i32),
+    "dc_flush_bucket_buffers": ([_i32, _i32, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp], _i32),
+    "dc_validate_buffer_tasks": ([_i32, _i32, _vp, _i32, _i64, _vp, _i32, _vp, _vp], _i32),
     "dc_flush_bucket_zero2": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
                                _i32, _vp, _i32, _i32, _vp], _i32),
     "dc_probe_flush": ([_i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp], _i32),
@@ -82,6 +84,11 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        # torch ships its own HIP runtime under the same soname as the system
+        # one libdc is linked against; whichever is loaded first serves the
+        # whole process, so load torch's first: the streams and memory handed
+        # to libdc are torch's.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         for name, (args, res) in _SIGS.items():
             fn = getattr(L, name)
@@ -167,6 +174,28 @@ def dc_flush_bucket(W, dtype, slab_in, ld_in, slab_out, ld_out, bucket_col, buck
         W, dtype, _dev(slab_in), ld_in, _dev(slab_out), ld_out, bucket_col, bucket_numel,
         _dev(tasks), num_tasks, _dev(owner), num_params, cp, num_comms, pre_div,
         _stream(stream)))
+
+
+def dc_flush_bucket_buffers(W, dtype, bucket_numel, tasks, num_tasks, in_ptrs, out_ptrs, comms,
+                            num_comms, pre_div, stream=None):
+    """tasks, in_ptrs, out_ptrs: device tensors (in_ptrs / out_ptrs int64
+    [num_tasks * W] holding device addresses, 0 for an empty buffer)."""
+    cp, _a = _host(comms, COMM_DTYPE)
+    _check("dc_flush_bucket_buffers", lib().dc_flush_bucket_buffers(
+        W, dtype, bucket_numel, _dev(tasks), num_tasks, _dev(in_ptrs), _dev(out_ptrs), cp, num_comms,
+        pre_div, _stream(stream)))
+
+
+def dc_validate_buffer_tasks(W, dtype, tasks, num_tasks, bucket_numel, comms, num_comms, in_ptrs,
+                             out_ptrs):
+    """Host arrays: tasks (TASK_DTYPE), comms, in_ptrs / out_ptrs (uint64
+    addresses, 0 = empty buffer)."""
+    tp, _a = _host(tasks, TASK_DTYPE)
+    cp, _b = _host(comms, COMM_DTYPE)
+    ip, _c = _host(in_ptrs, np.uint64)
+    op, _d = _host(out_ptrs, np.uint64)
+    _check("dc_validate_buffer_tasks", lib().dc_validate_buffer_tasks(
+        W, dtype, tp, num_tasks, bucket_numel, cp, num_comms, ip, op))
 
 
 def dc_flush_bucket_zero2(W, dtype, slab_in, ld_in, slab_out, ld_out, bucket_col, bucket_numel,

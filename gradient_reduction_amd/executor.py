@@ -8,6 +8,10 @@ reports one line per flush for the first 20 flushes (reduce_probe).  With
 zero2=True every element goes to the rank whose partition holds it (the
 issue's ZeRO-2 follow-up); the probe describes the ZeRO-1 paths only.
 
+register_buffers + flush_buffers run the flush with copy-in and copy-out
+fused in: each rank's gradient is read from its own buffer and the sum lands
+in the grad buffers of the ranks that keep one, with no bucket in between.
+
 torch supplies device memory and the stream; every step runs in libdc.so.
 """
 from dataclasses import dataclass
@@ -118,6 +122,78 @@ class Zero1FlushExecutor:
                                self.comms, len(self.comms), self.pre_div, stream)
         if self.reduce_probe and not self.zero2 and self.flushes < PROBE_FLUSHES:
             self.log(self.probe_line(b, self.flushes))
+        self.flushes += 1
+
+    # -- copy-in and copy-out fused into the flush ------------------------------
+
+    def holders(self, b: int) -> np.ndarray:
+        """[n_tasks, W] bool for bucket b: rank r keeps a gradient buffer for
+        the task's param, i.e. its partition holds part of it (in every block
+        of a sub-communicator).  These are the ranks the copy-out writes and
+        the probe's `kept` counts."""
+        if self.h_owner is None:
+            self.fetch_metadata()
+        W = self.W
+        bk = self.buckets[b]
+        out = np.zeros((len(bk.tasks), W), bool)
+        for k, (_, _, param, comm) in enumerate(bk.tasks):
+            c, st = int(self.comms[comm]["size"]), int(self.comms[comm]["stride"])
+            for q in self.h_pids[self.h_pid_off[param]:self.h_pid_off[param + 1]]:
+                for blk in range(W // c):
+                    out[k, (blk * c if st == 1 else blk) + int(q) * st] = True
+        return out
+
+    def register_buffers(self, in_addr: np.ndarray, out_addr: np.ndarray) -> None:
+        """in_addr, out_addr: [W, P] device addresses of rank r's gradient of
+        param p and of its grad buffer (0 = empty buffer).  A task's slice
+        starts at its position within its param (the params' tasks in bucket
+        order).  Task coordinates are re-laid at 16-byte steps so aligned
+        buffers move as whole vectors.  Tables are validated on the host and
+        kept on the device."""
+        torch = self.torch
+        W, E = self.W, 8 if self.dtype == dc.DC_BF16 else 4
+        eb = 2 if self.dtype == dc.DC_BF16 else 4
+        in_addr = np.asarray(in_addr, np.uint64).reshape(W, self.P)
+        out_addr = np.asarray(out_addr, np.uint64).reshape(W, self.P)
+        seen = np.zeros(self.P, np.int64)
+        tasks, ins, outs, self.buf_extent, self.buf_begin = [], [], [], [], [0]
+        for b, bk in enumerate(self.buckets):
+            pos = 0
+            rows = []
+            tin = np.zeros((len(bk.tasks), W), np.uint64)
+            tout = np.zeros((len(bk.tasks), W), np.uint64)
+            for k, (_, numel, param, comm) in enumerate(bk.tasks):
+                rows.append((pos, numel, param, comm))
+                skip = np.uint64(int(seen[param]) * eb)
+                tin[k] = in_addr[:, param] + skip
+                tout[k] = np.where(out_addr[:, param] != 0, out_addr[:, param] + skip, 0)
+                seen[param] += numel
+                pos = -(-(pos + numel) // E) * E
+            t = dc.tasks_array(rows)
+            extent = int(rows[-1][0] + rows[-1][1]) if rows else 0
+            dc.dc_validate_buffer_tasks(W, self.dtype, t, len(t), extent, self.comms,
+                                        len(self.comms), tin.ravel(), tout.ravel())
+            tasks.append(t)
+            ins.append(tin.ravel())
+            outs.append(tout.ravel())
+            self.buf_extent.append(extent)
+            self.buf_begin.append(self.buf_begin[-1] + len(t))
+        dev = self.d_tasks.device
+        allt = np.concatenate(tasks) if tasks else np.zeros(0, dc.TASK_DTYPE)
+        self.d_btasks = torch.from_numpy(allt.view(np.uint8).copy()).to(dev) if len(allt) else None
+        self.d_bin = torch.from_numpy(np.concatenate(ins).view(np.int64)).to(dev)
+        self.d_bout = torch.from_numpy(np.concatenate(outs).view(np.int64)).to(dev)
+
+    def flush_buffers(self, b: int, stream=None) -> None:
+        n = len(self.buckets[b].tasks)
+        if n == 0:
+            return
+        t0 = self.buf_begin[b]
+        dc.dc_flush_bucket_buffers(self.W, self.dtype, self.buf_extent[b],
+                                   self.d_btasks.data_ptr() + 32 * t0, n,
+                                   self.d_bin.data_ptr() + 8 * t0 * self.W,
+                                   self.d_bout.data_ptr() + 8 * t0 * self.W,
+                                   self.comms, len(self.comms), self.pre_div, stream)
         self.flushes += 1
 
     def probe(self, b: int):

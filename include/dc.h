@@ -241,6 +241,54 @@ dc_status dc_flush_bucket_zero2(int32_t W, int32_t dtype, const void* slab_in, i
                                 int32_t num_params, const dc_comm* comms, int32_t num_comms,
                                 int32_t pre_div, void* stream);
 
+/* Bucket flush with copy-in and copy-out fused in ([DS] problem statement:
+ * gradients enter the bucket from every rank and, after the reduction, the
+ * copy-out moves the result into each rank's gradient buffer, skipping the
+ * ranks whose buffer is empty; "Describe the solution": copy-out unchanged
+ * and still correct).  No bucket is staged: rank r's gradient of task t is
+ * read from in_ptrs[t*W + r] and the sum is written to out_ptrs[t*W + r]
+ * for every member r of the block whose pointer is not NULL (a NULL pointer
+ * is an empty buffer and is never written).  For every task t, element
+ * e < numel and block of the task's communicator (members m_0 < ... < m_{c-1}):
+ *   v_k = pre_div ? round_dtype(fp32(in_ptrs[t*W + m_k][e]) / c) : in_ptrs[t*W + m_k][e]
+ *   y   = round_dtype(((v_0 + v_1) + ...) + v_{c-1})      (fp32)
+ * the same values, in the same order, as dc_flush_bucket on a bucket filled
+ * from those buffers; with exactly one non-NULL output (the owner) it is the
+ * reduce-to-owner flush followed by the copy-out.
+ *   bucket_numel       extent of the task coordinates: offsets and numel of
+ *                      the tasks place them in [0, bucket_numel)
+ *   tasks, num_tasks   device dc_task[num_tasks] sorted by offset, disjoint
+ *                      (gaps allowed); param is not used; an out-of-range
+ *                      comm means comm 0
+ *   in_ptrs            device array [num_tasks * W] of device pointers, each
+ *                      to numel elements of the dtype (rank r's gradient)
+ *   out_ptrs           device array [num_tasks * W] of device pointers or NULL
+ *   comms, num_comms   host dc_comm[num_comms] as in dc_flush_bucket
+ *   pre_div            0 or 1
+ * An output may be the same buffer as its own input (in place); otherwise
+ * outputs must not overlap each other or any input (check the tables once
+ * with dc_validate_buffer_tasks).  A task whose offset is a multiple of 16
+ * bytes' worth of elements and whose pointers are all 16-byte aligned runs on
+ * 16-byte vectors; any other element runs one at a time. */
+dc_status dc_flush_bucket_buffers(int32_t W, int32_t dtype, int64_t bucket_numel,
+                                  const dc_task* tasks, int32_t num_tasks,
+                                  const void* const* in_ptrs, void* const* out_ptrs,
+                                  const dc_comm* comms, int32_t num_comms, int32_t pre_div,
+                                  void* stream);
+
+/* Host check of the tables of dc_flush_bucket_buffers (run once when the
+ * buffers are registered): tasks sorted by offset, disjoint, numel >= 0,
+ * inside [0, bucket_numel), comm in [0, num_comms); comms as in
+ * dc_validate_tasks; a non-NULL input for every rank of every non-empty task;
+ * no output overlapping another output or any input other than its own (an
+ * output equal to its own input is the in-place case).  tasks, comms and the
+ * two pointer tables are host copies (the pointer values are compared, never
+ * dereferenced).  Returns DC_ERR_TASKS with a message naming the first
+ * problem. */
+dc_status dc_validate_buffer_tasks(int32_t W, int32_t dtype, const dc_task* tasks, int32_t num_tasks,
+                                   int64_t bucket_numel, const dc_comm* comms, int32_t num_comms,
+                                   const void* const* in_ptrs, void* const* out_ptrs);
+
 /* a7. Probe counts of one flush ([DS] "reduce_probe"), on the host from
  * metadata only (no device access, no synchronization).  tasks, owner (or
  * NULL for the empty map), pid_offsets/pids (the CSR of dc_partition_ids)

@@ -42,12 +42,18 @@ def _load_dev():
         path = os.path.join(_HERE, "libsynth_dev.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        import torch  # noqa: F401  (torch's HIP runtime first, as for libdc)
         lib = ctypes.CDLL(path)
         lib.synth_fill_slab_device.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
                                                ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int32,
                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                                ctypes.c_void_p]
         lib.synth_fill_slab_device.restype = ctypes.c_int
+        lib.synth_fill_slab_device_at.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
+                                                  ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int32,
+                                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                  ctypes.c_void_p, ctypes.c_void_p]
+        lib.synth_fill_slab_device_at.restype = ctypes.c_int
         _dev = lib
     return _dev
 
@@ -87,10 +93,11 @@ def gather(dtype: int, seed: int, stream: int, scale, cols: np.ndarray) -> np.nd
 
 
 def fill_slab_device(dtype: int, seed: int, stream0: int, scale, rows: int, ld: int,
-                     ncols: int, ptr: int, hip_stream: int) -> None:
-    """Fill a device [rows, ld] slab at `ptr` on `hip_stream` (raw handle)."""
+                     ncols: int, ptr: int, hip_stream: int, col0: int = 0) -> None:
+    """Fill a device [rows, ld] slab at `ptr` on `hip_stream` (raw handle):
+    position j of row r holds column col0 + j of stream stream0 + r."""
     C, E = scale
-    rc = _load_dev().synth_fill_slab_device(dtype, seed, stream0, C, E, rows, ld, ncols,
-                                            ctypes.c_void_p(ptr), ctypes.c_void_p(hip_stream))
+    rc = _load_dev().synth_fill_slab_device_at(dtype, seed, stream0, C, E, rows, ld, ncols, col0,
+                                               ctypes.c_void_p(ptr), ctypes.c_void_p(hip_stream))
     if rc != 0:
         raise RuntimeError(f"synth_fill_slab_device failed with code {rc}")

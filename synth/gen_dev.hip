@@ -40,14 +40,15 @@ __device__ inline uint32_t value_bits(uint64_t key, uint64_t i, uint32_t C, uint
   return (neg << 31) | (bexp << 23) | (uint32_t)(sig & 0x7FFFFF);
 }
 
-// Row r of a [rows, ld] slab gets stream stream0 + r, columns [0, ncols).
+// Row r of a [rows, ld] slab gets stream stream0 + r: position j of the row
+// holds the value of column col0 + j, for j in [0, ncols).
 __global__ void fill_slab(int bf16, uint64_t seed, uint64_t stream0, uint32_t C, uint32_t E,
-                          int64_t ld, int64_t ncols, void* base) {
+                          int64_t ld, int64_t ncols, int64_t col0, void* base) {
   const int64_t r = blockIdx.y;
   const uint64_t key = mix(mix(seed + kG) + (stream0 + (uint64_t)r + 1) * kG);
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
   for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < ncols; j += step) {
-    uint32_t v = value_bits(key, (uint64_t)j, C, E, bf16 != 0);
+    uint32_t v = value_bits(key, (uint64_t)(col0 + j), C, E, bf16 != 0);
     if (bf16)
       reinterpret_cast<uint16_t*>(base)[r * ld + j] = (uint16_t)v;
     else
@@ -57,17 +58,25 @@ __global__ void fill_slab(int bf16, uint64_t seed, uint64_t stream0, uint32_t C,
 
 }  // namespace
 
-// Fill a [rows, ld] slab (dtype 0 = bf16, 1 = fp32) on `stream`.  Returns 0 on
-// success, -1 on a bad argument, or the HIP error code of the launch.
-extern "C" int synth_fill_slab_device(int dtype, uint64_t seed, uint64_t stream0, uint32_t C,
-                                      uint32_t E, int32_t rows, int64_t ld, int64_t ncols,
-                                      void* base, hipStream_t stream) {
-  if (base == nullptr || rows <= 0 || rows > 65535 || ncols < 0 || ld < ncols || (dtype != 0 && dtype != 1))
+// Fill a [rows, ld] slab (dtype 0 = bf16, 1 = fp32) on `stream` with columns
+// [col0, col0 + ncols) of every row's stream.  Returns 0 on success, -1 on a
+// bad argument, or the HIP error code of the launch.
+extern "C" int synth_fill_slab_device_at(int dtype, uint64_t seed, uint64_t stream0, uint32_t C,
+                                         uint32_t E, int32_t rows, int64_t ld, int64_t ncols,
+                                         int64_t col0, void* base, hipStream_t stream) {
+  if (base == nullptr || rows <= 0 || rows > 65535 || ncols < 0 || ld < ncols || col0 < 0 ||
+      (dtype != 0 && dtype != 1))
     return -1;
   if (ncols == 0) return 0;
   int64_t blocks = (ncols + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(fill_slab, dim3((unsigned)blocks, (unsigned)rows), dim3(256), 0, stream,
-                     dtype == 0 ? 1 : 0, seed, stream0, C, E, ld, ncols, base);
+                     dtype == 0 ? 1 : 0, seed, stream0, C, E, ld, ncols, col0, base);
   return (int)hipGetLastError();
+}
+
+extern "C" int synth_fill_slab_device(int dtype, uint64_t seed, uint64_t stream0, uint32_t C,
+                                      uint32_t E, int32_t rows, int64_t ld, int64_t ncols,
+                                      void* base, hipStream_t stream) {
+  return synth_fill_slab_device_at(dtype, seed, stream0, C, E, rows, ld, ncols, 0, base, stream);
 }

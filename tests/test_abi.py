@@ -213,3 +213,98 @@ def test_plan_relayout_errors():
                                    np.zeros(1, dc.PIECE_DTYPE).ctypes.data_as(ctypes.c_void_p), 1,
                                    ctypes.byref(n), seg.ctypes.data_as(ctypes.c_void_p))
     assert rc == dc.DC_ERR_SHAPE and n.value == 2
+
+
+def test_flush_buffers_argument_checks():
+    f = dc.dc_flush_bucket_buffers
+    expect(dc.DC_ERR_NULL, f, 4, 0, 64, None, 1, FAKE, FAKE, [(4, 1)], 1, 0, stream=0)
+    expect(dc.DC_ERR_NULL, f, 4, 0, 64, TASK_PTR, 1, None, FAKE, [(4, 1)], 1, 0, stream=0)
+    expect(dc.DC_ERR_ARG, f, 4, 0, -1, TASK_PTR, 1, FAKE, FAKE, [(4, 1)], 1, 0, stream=0)
+    expect(dc.DC_ERR_ARG, f, 4, 0, 64, TASK_PTR, 1, FAKE, FAKE, [(4, 1)], 1, 3, stream=0)
+    expect(dc.DC_ERR_ARG, f, 4, 0, 64, TASK_PTR, 1, FAKE, FAKE, [(2, 1)], 1, 0, stream=0)
+    expect(dc.DC_ERR_DTYPE, f, 4, 7, 64, TASK_PTR, 1, FAKE, FAKE, [(4, 1)], 1, 0, stream=0)
+
+
+def _buffer_tables(W, numel, gap_in=64, gap_out=64):
+    """Disjoint fake addresses: in buffers then out buffers, 16-byte aligned."""
+    n = len(numel)
+    tin = np.zeros((n, W), np.uint64)
+    tout = np.zeros((n, W), np.uint64)
+    pos = FAKE
+    for t in range(n):
+        for r in range(W):
+            tin[t, r] = pos
+            pos += numel[t] * 2 + gap_in
+    for t in range(n):
+        for r in range(W):
+            tout[t, r] = pos
+            pos += numel[t] * 2 + gap_out
+    return tin, tout
+
+
+def test_validate_buffer_tasks():
+    W = 4
+    numel = [10, 0, 7]
+    tasks = dc.tasks_array([(0, 10, 0, 0), (10, 0, 1, 0), (16, 7, 2, 1)])
+    comms = [(4, 1), (2, 1)]
+    tin, tout = _buffer_tables(W, numel)
+    v = dc.dc_validate_buffer_tasks
+    v(W, 0, tasks, 3, 23, comms, 2, tin.ravel(), tout.ravel())
+    # empty buffers and the in-place pair are fine
+    t2 = tout.copy()
+    t2[0, 1:] = 0
+    t2[2] = tin[2]
+    v(W, 0, tasks, 3, 23, comms, 2, tin.ravel(), t2.ravel())
+    # ranks may share one input buffer (identical gradients on every rank)
+    ti = tin.copy()
+    ti[0, :] = tin[0, 0]
+    v(W, 0, tasks, 3, 23, comms, 2, ti.ravel(), tout.ravel())
+    # failures
+    bad = dc.tasks_array([(0, 10, 0, 0), (10, 0, 1, 0), (9, 7, 2, 1)])
+    expect(dc.DC_ERR_TASKS, v, W, 0, bad, 3, 23, comms, 2, tin.ravel(), tout.ravel())
+    expect(dc.DC_ERR_TASKS, v, W, 0, tasks, 3, 22, comms, 2, tin.ravel(), tout.ravel())
+    bad = dc.tasks_array([(0, 10, 0, 0), (10, 0, 1, 0), (16, 7, 2, 2)])
+    expect(dc.DC_ERR_TASKS, v, W, 0, bad, 3, 23, comms, 2, tin.ravel(), tout.ravel())
+    t3 = tin.copy()
+    t3[2, 3] = 0
+    expect(dc.DC_ERR_TASKS, v, W, 0, tasks, 3, 23, comms, 2, t3.ravel(), tout.ravel())
+    t4 = tout.copy()
+    t4[2, 1] = tout[2, 0] + 2        # two outputs overlap
+    expect(dc.DC_ERR_TASKS, v, W, 0, tasks, 3, 23, comms, 2, tin.ravel(), t4.ravel())
+    t5 = tout.copy()
+    t5[0, 2] = tin[0, 3] + 4         # an output inside another rank's input
+    expect(dc.DC_ERR_TASKS, v, W, 0, tasks, 3, 23, comms, 2, tin.ravel(), t5.ravel())
+    t6 = tout.copy()
+    t6[0, 2] = tin[0, 2] + 2         # shifted in place: overlaps its own input
+    expect(dc.DC_ERR_TASKS, v, W, 0, tasks, 3, 23, comms, 2, tin.ravel(), t6.ravel())
+    # packed back to back for 2-byte elements: fine in bf16, overlapping in fp32
+    pin, pout = _buffer_tables(W, numel, 0, 0)
+    v(W, 0, tasks, 3, 23, comms, 2, pin.ravel(), pout.ravel())
+    expect(dc.DC_ERR_TASKS, v, W, 1, tasks, 3, 23, comms, 2, pin.ravel(), pout.ravel())
+
+
+def _host_executor(w):
+    """An executor built on the CPU, its partition lists set from the oracle
+    (the device kernels that build them need a GPU)."""
+    from gradient_reduction_amd import executor
+    ex = executor.from_workload(w, reduce_to_owner=True, device="cpu")
+    flat, ps, off, pids = oracle.partition_ids(w.numel, w.group_begin, w.group_parts())
+    comm_sizes = [w.comms[c].size for c in w.group_comm]
+    elig = oracle.group_eligible(w.W, comm_sizes, w.group_rank_to_global())
+    owner, _ = oracle.owner_map(off, pids, w.group_begin, elig)
+    ex.h_owner, ex.h_pid_off, ex.h_pids = owner, off, pids
+    return ex
+
+
+def test_executor_holders_match_probe():
+    """The ranks the fused copy-out writes are the probe's kept set."""
+    ws = [wl.tiny_flush(), wl.mixed_flush_w16(),
+          wl.custom_flush("h", 8, 0, [1000, 3, 77, 4096, 5000, 12, 900, 64], group_begin=[0, 5, 8],
+                          group_comm=[0, 1], comms=[wl.Comm(8, 1), wl.Comm(4, 2)], capacity=3000)]
+    for w in ws:
+        ex = _host_executor(w)
+        for b in range(len(w.buckets)):
+            h = ex.holders(b)
+            pr = ex.probe(b)
+            kept = (h * np.array([t.numel for t in w.buckets[b].tasks])[:, None]).sum(axis=0)
+            assert list(kept) == [pr.kept[r] for r in range(w.W)], (w.name, b)
