@@ -70,9 +70,41 @@ class Timer:
     def __init__(self, torch, n):
         self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(n)]
+        # torch creates the HIP event at its first record(); do that now, not
+        # inside the timed loop, where creating it can stall the host
+        for a, b in self.ev:
+            a.record()
+            b.record()
 
     def ms(self):
         return [a.elapsed_time(b) for a, b in self.ev]
+
+
+def run_timed(torch, args, step, n_events):
+    """args.warmup untimed steps, then args.steps timed ones bracketed by a
+    synchronize on both sides; HIP events around every launch.  Python's
+    garbage collector is off in the timed loop so a collection cannot stall
+    the host mid-step.  Returns (ms per step, [steps, n_events] launch ms)."""
+    import gc
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [Timer(torch, n_events) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    t1.record()
+    torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
+    try:
+        t0.record()
+        for k in range(args.steps):
+            step(timers[k])
+        t1.record()
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
+    return t0.elapsed_time(t1) / args.steps, np.array([tm.ms() for tm in timers])
 
 
 def bench_flush(args, w, reduce_to_owner=True, zero2=False):
@@ -112,22 +144,10 @@ def bench_flush(args, w, reduce_to_owner=True, zero2=False):
             if timer is not None:
                 timer.ev[b][1].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    timers = [Timer(torch, nb) for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for k in range(args.steps):
-        step(timers[k])
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    kern = np.array([tm.ms() for tm in timers])          # [steps, buckets]
+    ms_step, kern = run_timed(torch, args, step, nb)          # [steps, buckets]
     avg_launch_ms = float(kern.mean())
     flush_gbs = sum(per_launch) / (kern.sum(axis=1).mean() / 1e3) / 1e9
+    flush_gbs_median = sum(per_launch) / (np.median(kern.sum(axis=1)) / 1e3) / 1e9
     value = step_bytes / (ms_step / 1e3) / 1e9
     log(f"[bench] step {ms_step:.3f} ms, {value:.1f} GB/s; flush kernels {kern.sum(axis=1).mean():.3f} ms "
         f"({flush_gbs:.1f} GB/s); per bucket ms {np.round(kern.mean(axis=0), 4).tolist()}")
@@ -140,7 +160,8 @@ def bench_flush(args, w, reduce_to_owner=True, zero2=False):
     if ceiling is not None:
         roofline["access_mix_ceiling_gbs"] = round(ceiling, 1)
         roofline["frac_of_access_mix_ceiling"] = round(flush_gbs / ceiling, 4)
-    extra = {"per_bucket_gbs": [round(b / (m / 1e3) / 1e9, 1) for b, m in zip(per_launch, kern.mean(axis=0))]}
+    extra = {"per_bucket_gbs": [round(b / (m / 1e3) / 1e9, 1) for b, m in zip(per_launch, kern.mean(axis=0))],
+             "flush_gbs_median_step": round(flush_gbs_median, 1)}
     del x, y
     torch.cuda.empty_cache()
     return ms_step, value, step_bytes, roofline, extra
@@ -266,19 +287,9 @@ def bench_flush_buffers(args, w):
             if timer is not None:
                 timer.ev[b][1].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    timers = [Timer(torch, nb) for _ in range(args.steps)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for k in range(args.steps):
-        step(timers[k])
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    kern = np.array([tm.ms() for tm in timers])
+    ms_step, kern = run_timed(torch, args, step, nb)
     gbs = sum(per_launch) / (kern.sum(axis=1).mean() / 1e3) / 1e9
+    gbs_median = sum(per_launch) / (np.median(kern.sum(axis=1)) / 1e3) / 1e9
     value = step_bytes / (ms_step / 1e3) / 1e9
     log(f"[bench] step {ms_step:.3f} ms, {value:.1f} GB/s; fused flush kernels "
         f"{kern.sum(axis=1).mean():.3f} ms ({gbs:.1f} GB/s); per bucket ms "
@@ -292,6 +303,7 @@ def bench_flush_buffers(args, w):
         roofline["access_mix_ceiling_gbs"] = round(ceiling, 1)
         roofline["frac_of_access_mix_ceiling"] = round(gbs / ceiling, 4)
     extra = {"per_bucket_gbs": [round(b / (m / 1e3) / 1e9, 1) for b, m in zip(per_launch, kern.mean(axis=0))],
+             "flush_gbs_median_step": round(gbs_median, 1),
              "fused_bytes_per_step": int(sum(per_launch)),
              "unfused_bytes_per_step": int(unfused),
              "bytes_saved_frac": round(1 - sum(per_launch) / unfused, 4)}
@@ -391,18 +403,8 @@ def bench_deferred(args):
             dc.dc_deferred_reduce(W, acc, ld, out, ld, M, W)
         if tm: tm.ev[n_acc][1].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    timers = [Timer(torch, n) for _ in range(args.steps)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for k in range(args.steps):
-        step(timers[k])
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    kern = np.array([tm.ms() for tm in timers]).mean(axis=0)
+    ms_step, kern_all = run_timed(torch, args, step, n)
+    kern = kern_all.mean(axis=0)
     red_gbs = red_b / (kern[-1] / 1e3) / 1e9
     acc_gbs = sum(acc_b) / (kern[:-1].sum() / 1e3) / 1e9 if n_acc else 0.0
     log(f"[bench] deferred K={args.ga}: step {ms_step:.3f} ms; accumulate {acc_gbs:.1f} GB/s; "
@@ -442,18 +444,8 @@ def bench_rs_ag(args):
         dc.dc_all_gather(W, 0, sh, ld_sh, out, w.ld, L, dc.DC_ORDER_RING, -1)
         if tm: tm.ev[2][1].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    timers = [Timer(torch, 3) for _ in range(args.steps)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for k in range(args.steps):
-        step(timers[k])
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    kern = np.array([tm.ms() for tm in timers]).mean(axis=0)
+    ms_step, kern_all = run_timed(torch, args, step, 3)
+    kern = kern_all.mean(axis=0)
     gbs = [rs_b / (kern[0] / 1e3) / 1e9, ag_b / (kern[1] / 1e3) / 1e9, ag_b / (kern[2] / 1e3) / 1e9]
     log(f"[bench] rs {gbs[0]:.1f} GB/s, ag rank {gbs[1]:.1f} GB/s, ag ring {gbs[2]:.1f} GB/s")
     roofline = {"bound": "hbm", "achieved": round(gbs[0], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -502,18 +494,8 @@ def bench_schedules(args):
                 dc.dc_all_gather_step(W, 0, sh, ld_sh, out, w.ld, L, algo, s)
             if tm: tm.ev[2 + k][1].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    timers = [Timer(torch, len(names)) for _ in range(args.steps)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for k in range(args.steps):
-        step(timers[k])
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    kern = np.array([tm.ms() for tm in timers]).mean(axis=0)
+    ms_step, kern_all = run_timed(torch, args, step, len(names))
+    kern = kern_all.mean(axis=0)
     byts = [rs_b, rs_b] + [ag_b] * len(scheds)
     gbs = {n: b / (t / 1e3) / 1e9 for n, b, t in zip(names, byts, kern)}
     log("[bench] " + ", ".join(f"{n} {kern[i]:.3f} ms {gbs[n]:.1f} GB/s" for i, n in enumerate(names)))
@@ -532,7 +514,8 @@ def bench_schedules(args):
     r = sh[:, :L].view(torch.bfloat16).float()
     diff = (a - r).abs()
     extra["ring_vs_rank"] = {
-        "elements_differing_frac": round(float((diff > 0).float().mean()), 5),
+        "elements_differing": int((diff > 0).sum()),
+        "elements": int(diff.numel()),
         "max_abs_diff_over_max_abs": float(diff.max() / a.abs().max()),
         "max_rel_diff_where_abs_ge_1pct_of_max": float(
             (diff / a.abs().clamp_min(1e-30))[a.abs() >= 0.01 * a.abs().max()].max())}
@@ -581,18 +564,8 @@ def bench_relayout_rs(args):
             dc.dc_reduce_scatter_v(W, 0, relaid, ld_r, shards, ld_s, seg, w.pre_div)
             if tm: tm.ev[2 * k + 1][1].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    timers = [Timer(torch, 2 * nb) for _ in range(args.steps)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for k in range(args.steps):
-        step(timers[k])
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    kern = np.array([tm.ms() for tm in timers]).mean(axis=0)
+    ms_step, kern_all = run_timed(torch, args, step, 2 * nb)
+    kern = kern_all.mean(axis=0)
     rl_gbs = sum(rl_b) / (kern[0::2].sum() / 1e3) / 1e9
     rs_gbs = sum(rs_b) / (kern[1::2].sum() / 1e3) / 1e9
     log(f"[bench] relayout + reduce-scatter-v: step {ms_step:.3f} ms; relayout {rl_gbs:.1f} GB/s "
