@@ -124,15 +124,17 @@ __device__ __forceinline__ float pre_elem(float x, bool pre, float inv, float c)
 }
 
 // Block-wide k-ary search over n sorted keys: r1 = #{i : key(i) <= x1},
-// r2 = #{i : key(i) < x2}.  Each round the block probes kThreads evenly spaced
-// keys of both ranges and keeps the bracket the counts point to.  Every thread
-// of the block must call it (it synchronizes).
-template <class Key>
+// r2 = #{i : key(i) < x2}.  Each round the TPB threads of the block probe TPB
+// evenly spaced keys of both ranges and keep the bracket the counts point to,
+// so n keys take ceil(log_TPB n) rounds.  Every bound is block-uniform and the
+// interval shrinks every round, so the loop ends for any key contents.  Every
+// thread of the block must call it (it synchronizes).
+template <int TPB, class Key>
 __device__ void kary_bounds(int32_t n, Key key, int64_t x1, int64_t x2, int32_t& r1, int32_t& r2) {
   int32_t lo1 = 0, hi1 = n, lo2 = 0, hi2 = n;
   while (lo1 < hi1 || lo2 < hi2) {
-    const int32_t st1 = (hi1 - lo1 + kThreads - 1) / kThreads;
-    const int32_t st2 = (hi2 - lo2 + kThreads - 1) / kThreads;
+    const int32_t st1 = (hi1 - lo1 + TPB - 1) / TPB;
+    const int32_t st2 = (hi2 - lo2 + TPB - 1) / TPB;
     const int32_t q1 = lo1 + (int32_t)threadIdx.x * st1;
     const int32_t q2 = lo2 + (int32_t)threadIdx.x * st2;
     const bool p1 = lo1 < hi1 && q1 < hi1 && key(q1) <= x1;

@@ -11,7 +11,7 @@
 // offset never breaks alignment; a vector can still straddle a task or
 // bucket boundary, and those vectors take an element-wise path.
 //
-// A workgroup of 256 threads owns a tile of 256*U consecutive vectors.  It
+// A workgroup of 256 threads (DC_FLUSH_TPB) owns a tile of 256*U consecutive vectors.  It
 // finds the tasks overlapping its tile with a block-wide k-ary search over
 // the sorted task table, stages them in LDS with their roots already
 // resolved through the owner map ("roots precomputed for the whole bucket"),
@@ -24,7 +24,11 @@
 namespace dc {
 namespace {
 
-constexpr int kStage = 256;  // tasks staged in LDS per pass over a tile
+#ifndef DC_FLUSH_TPB
+#define DC_FLUSH_TPB 256  // threads per workgroup
+#endif
+constexpr int kFT = DC_FLUSH_TPB;
+constexpr int kStage = kFT;  // tasks staged in LDS per pass over a tile (one per thread)
 
 #ifndef DC_FLUSH_U
 #define DC_FLUSH_U 2      // vectors per thread per tile
@@ -77,53 +81,6 @@ __device__ __forceinline__ float pre_scale(float x, int mode, float inv, float c
   if (mode == kPreMul) return x * inv;
   if (mode == kPreDiv) return x / c;
   return x;
-}
-
-// Block-wide search over a table sorted by offset: r1 = number of tasks with
-// offset <= x1, r2 = number with offset < x2.  Each round probes 256 evenly
-// spaced entries and keeps the gap between the last true and the first false
-// probe, so a table of n tasks takes ceil(log_256 n) rounds.  Every bound is
-// block-uniform; the loop ends for any table contents because the interval
-// shrinks every round.
-__device__ void find_tasks(const dc_task* t, int32_t n, int64_t x1, int64_t x2, int32_t& r1,
-                           int32_t& r2) {
-  int32_t lo1 = 0, hi1 = n, lo2 = 0, hi2 = n;
-  while (lo1 < hi1 || lo2 < hi2) {
-    const int32_t st1 = (hi1 - lo1 + kThreads - 1) / kThreads;
-    const int32_t st2 = (hi2 - lo2 + kThreads - 1) / kThreads;
-    const int32_t q1 = lo1 + (int32_t)threadIdx.x * st1;
-    const int32_t q2 = lo2 + (int32_t)threadIdx.x * st2;
-    const bool p1 = lo1 < hi1 && q1 < hi1 && t[q1].offset <= x1;
-    const bool p2 = lo2 < hi2 && q2 < hi2 && t[q2].offset < x2;
-    const int32_t n1 = __syncthreads_count(p1);
-    const int32_t n2 = __syncthreads_count(p2);
-    if (lo1 < hi1) {
-      const int32_t k1 = (hi1 - lo1 + st1 - 1) / st1;
-      const int32_t nlo = n1 >= 1 ? lo1 + (n1 - 1) * st1 + 1 : lo1;
-      const int32_t nhi = n1 < k1 ? lo1 + n1 * st1 : hi1;
-      lo1 = nlo;
-      hi1 = nhi;
-    }
-    if (lo2 < hi2) {
-      const int32_t k2 = (hi2 - lo2 + st2 - 1) / st2;
-      const int32_t nlo = n2 >= 1 ? lo2 + (n2 - 1) * st2 + 1 : lo2;
-      const int32_t nhi = n2 < k2 ? lo2 + n2 * st2 : hi2;
-      lo2 = nlo;
-      hi2 = nhi;
-    }
-  }
-  r1 = lo1;
-  r2 = lo2;
-}
-
-// Largest staged index k with off[k] <= x (0 if none).
-__device__ __forceinline__ int32_t staged_task(const int64_t* off, int32_t cnt, int64_t x) {
-  int32_t lo = 0, hi = cnt;  // answer + 1 in (lo, hi]
-  while (hi - lo > 1) {
-    const int32_t mid = (lo + hi) >> 1;
-    if (off[mid] <= x) lo = mid; else hi = mid;
-  }
-  return lo;
 }
 
 // Shape of communicator `comm`, selected with compile-time indices: a
@@ -319,7 +276,7 @@ __device__ __forceinline__ void elem_flush(const FlushParams& p, int64_t col, in
 // data-parallel one or the single shape (C2, S2) (C2 = 0: none).  WT = 0:
 // any W and any communicators, all at run time.
 template <bool BF16, int WT, int C2, int S2, int PRE, int U, bool NT, bool Z2>
-__global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p) {
+__global__ __launch_bounds__(kFT) DC_FLUSH_ATTR void k_flush(FlushParams p) {
   static_assert(U <= 32, "slow-vector mask is 32 bits");
   constexpr int E = BF16 ? 8 : 4;
   __shared__ int64_t s_off[kStage];
@@ -341,14 +298,14 @@ __global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p)
     const int64_t full = nb - (per - 1) * kXcds;  // XCDs that get `per` tiles
     tile = x < full ? x * per + k : full * per + (x - full) * (per - 1) + k;
   }
-  const int64_t t0 = tile * (kThreads * U);
-  const int64_t t1 = min(t0 + (int64_t)(kThreads * U), p.nv);
+  const int64_t t0 = tile * (kFT * U);
+  const int64_t t1 = min(t0 + (int64_t)(kFT * U), p.nv);
   // the tile's columns, relative to the bucket
   const int64_t lo = max((p.v0 + t0) * E, p.c0) - p.c0;
   const int64_t hi = min((p.v0 + t1) * E, p.c1) - p.c0;
 
   int32_t first, last;
-  find_tasks(p.tasks, p.ntasks, lo, hi, first, last);
+  kary_bounds<kFT>(p.ntasks, [&](int32_t i) { return p.tasks[i].offset; }, lo, hi, first, last);
   first = max(first - 1, 0);  // the task holding column lo
   last = last - 1;            // the last task starting before hi
 
@@ -399,13 +356,13 @@ __global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p)
 #endif
 #pragma unroll 1
       for (int u = 0; u < U; ++u) {
-        const int64_t tv = t0 + threadIdx.x + (int64_t)u * kThreads;
+        const int64_t tv = t0 + threadIdx.x + (int64_t)u * kFT;
         if (tv >= t1) break;
         const int64_t av = p.v0 + tv;
         const int64_t rc = av * E - p.c0;  // the vector's first column, relative
         const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
         if (e_lo >= e_hi) continue;
-        const int32_t k = staged_task(s_off, cnt, e_lo);
+        const int32_t k = last_le(s_off, cnt, e_lo);
         bool whole = e_lo == rc && e_hi == rc + E && s_off[k] <= rc && s_end[k] >= rc + E;
         int32_t vroot = s_root[k];
         if constexpr (Z2) {
@@ -443,13 +400,13 @@ __global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p)
     } else {
 #pragma unroll 1
       for (int u = 0; u < U; ++u) {
-        const int64_t tv = t0 + threadIdx.x + (int64_t)u * kThreads;
+        const int64_t tv = t0 + threadIdx.x + (int64_t)u * kFT;
         if (tv >= t1) break;
         const int64_t av = p.v0 + tv;
         const int64_t rc = av * E - p.c0;
         const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
         if (e_lo >= e_hi) continue;
-        const int32_t k = staged_task(s_off, cnt, e_lo);
+        const int32_t k = last_le(s_off, cnt, e_lo);
         bool whole = e_lo == rc && e_hi == rc + E && s_off[k] <= rc && s_end[k] >= rc + E;
         int32_t vroot = s_root[k];
         if constexpr (Z2) {
@@ -469,11 +426,11 @@ __global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p)
 #pragma unroll 1
     for (int u = 0; u < U; ++u) {
       if (!((slow >> u) & 1u)) continue;
-      const int64_t av = p.v0 + t0 + threadIdx.x + (int64_t)u * kThreads;
+      const int64_t av = p.v0 + t0 + threadIdx.x + (int64_t)u * kFT;
       const int64_t rc = av * E - p.c0;
       const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
       for (int64_t x = e_lo; x < e_hi; ++x) {
-        const int32_t kk = staged_task(s_off, cnt, x);
+        const int32_t kk = last_le(s_off, cnt, x);
         if (s_off[kk] <= x && x < s_end[kk]) {
           int32_t eroot = s_root[kk];
           if constexpr (Z2) {
@@ -492,14 +449,14 @@ __global__ __launch_bounds__(kThreads) DC_FLUSH_ATTR void k_flush(FlushParams p)
 template <bool BF16, int WT, int C2, int S2, int PRE>
 hipError_t launch_kernel(const FlushParams& p, hipStream_t stream) {
   constexpr int U = DC_FLUSH_U;
-  const int64_t blocks = (p.nv + kThreads * U - 1) / (kThreads * U);
+  const int64_t blocks = (p.nv + kFT * U - 1) / (kFT * U);
   if (blocks == 0) return hipSuccess;
   if (p.flat != nullptr)
     hipLaunchKernelGGL((k_flush<BF16, WT, C2, S2, PRE, U, DC_FLUSH_NT != 0, true>),
-                       dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+                       dim3((unsigned)blocks), dim3(kFT), 0, stream, p);
   else
     hipLaunchKernelGGL((k_flush<BF16, WT, C2, S2, PRE, U, DC_FLUSH_NT != 0, false>),
-                       dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+                       dim3((unsigned)blocks), dim3(kFT), 0, stream, p);
   return hipGetLastError();
 }
 

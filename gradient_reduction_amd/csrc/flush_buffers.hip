@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void k_flush_buffers(BufParams p) {
   const int64_t t1 = min(t0 + (int64_t)(kThreads * kBufU), p.nslots);
   const int64_t lo = t0 * E, hi = min(t1 * E, p.bucket_numel);
   int32_t first, last;
-  kary_bounds(p.ntasks, [&](int32_t i) { return p.tasks[i].offset; }, lo, hi, first, last);
+  kary_bounds<kThreads>(p.ntasks, [&](int32_t i) { return p.tasks[i].offset; }, lo, hi, first, last);
   first = max(first - 1, 0);
   last = last - 1;
   for (int32_t base = first; base <= last; base += S) {

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void k_relayout(RelayoutParams p) {
   const int64_t t1 = min(t0 + (int64_t)(kThreads * kRelayoutU), nvec);
   const int64_t lo = t0 * E, hi = min(t1 * E, p.out_numel);
   int32_t first, last;
-  kary_bounds(p.npieces, [&](int32_t i) { return p.pieces[i].dst; }, lo, hi, first, last);
+  kary_bounds<kThreads>(p.npieces, [&](int32_t i) { return p.pieces[i].dst; }, lo, hi, first, last);
   first = max(first - 1, 0);
   last = last - 1;
   const char* in = reinterpret_cast<const char*>(p.in);

@@ -101,24 +101,86 @@ __global__ __launch_bounds__(kThreads) void k_rs_elem(int32_t W, const void* __r
 
 // Reduce-scatter with variable shards (after a relayout): shard q is
 // columns [seg[q], seg[q+1]) of the input; out[q][k] = fold_r pre(in[r][seg[q]+k]).
-// A shard that starts on a vector boundary takes 16-byte loads; the rest of
-// a shard, or a shard that does not, goes element by element.
+// Shards start wherever the relayout's packed segments do, so a shard's
+// input is usually not vector aligned while its output row is: each full
+// output vector is cut out of the two aligned input vectors around it
+// (funnel16, with the block-uniform offset of the shard), folded and stored
+// aligned.  The partial last vector of a shard goes element by element.
 struct SegArgs {
   int64_t seg[DC_MAX_W + 1];
+  int64_t bpre[DC_MAX_W + 1];   // first workgroup of each shard (shards' vectors / kThreads, prefix)
 };
+
+// The 16 bytes that start `wo` words + `bs` bytes (wo in 0..3, bs in {0, 2})
+// into the 32 bytes a:b; wo and bs are the same for the whole block.
+__device__ __forceinline__ u32x4 funnel16(u32x4 a, u32x4 b, int wo, int bs) {
+  const uint32_t c[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  uint32_t w[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const uint32_t x01 = (wo & 1) ? c[j + 1] : c[j];
+    const uint32_t x23 = (wo & 1) ? c[j + 3] : c[j + 2];
+    w[j] = (wo & 2) ? x23 : x01;
+  }
+  u32x4 y;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) y[j] = __builtin_amdgcn_alignbyte(w[j + 1], w[j], bs);
+  return y;
+}
 
 template <bool BF16, int WT, bool PRE>
 __global__ __launch_bounds__(kThreads) void k_rs_v(int32_t W, const void* __restrict__ in,
                                                    int64_t ld_in, void* __restrict__ out,
                                                    int64_t ld_out, SegArgs sa, float inv, float c) {
   constexpr int E = BF16 ? 8 : 4;
-  const int32_t q = blockIdx.y;
-  const int64_t s0 = sa.seg[q], len = sa.seg[q + 1] - s0;
-  const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int QMAX = WT > 0 ? WT : DC_MAX_W;
+  // the shard of this workgroup: the grid covers exactly the shards' vectors,
+  // shard after shard (compile-time indices into the argument arrays)
+  const int64_t blk = blockIdx.x;
+  int32_t q = 0;
+  int64_t s0 = sa.seg[0], s1 = sa.seg[1], b0 = 0;
+#pragma unroll
+  for (int i = 1; i < QMAX; ++i) {
+    if (i < W && blk >= sa.bpre[i]) {
+      q = i;
+      s0 = sa.seg[i];
+      s1 = sa.seg[i + 1];
+      b0 = sa.bpre[i];
+    }
+  }
+  const int64_t len = s1 - s0;
+  const int64_t k = (blk - b0) * kThreads + threadIdx.x;
   if (k * E >= len) return;
-  if (s0 % E == 0 && (k + 1) * E <= len) {
-    const u32x4 y = fold_rows<BF16, WT, PRE>(reinterpret_cast<const u32x4*>(in), ld_in / E,
-                                             s0 / E + k, W, inv, c);
+  const int64_t ldv = ld_in / E;
+  const int32_t o = (int32_t)(s0 % E);
+  if ((k + 1) * E <= len) {
+    u32x4 y;
+    if (o == 0) {
+      y = fold_rows<BF16, WT, PRE>(reinterpret_cast<const u32x4*>(in), ldv, s0 / E + k, W, inv, c);
+    } else {
+      // input vectors v and v+1 hold the window; v+1 ends inside the row
+      // because the window does and rows are whole vectors long
+      const u32x4* in4 = reinterpret_cast<const u32x4*>(in);
+      const int64_t v = s0 / E + k;
+      const int wo = (o * EB) >> 2, bs = (o * EB) & 3;
+      float acc[E];
+      if constexpr (WT > 0) {
+        u32x4 a[WT], b[WT];
+#pragma unroll
+        for (int r = 0; r < WT; ++r) {
+          a[r] = load16<kNT>(in4 + r * ldv + v);
+          b[r] = load16<kNT>(in4 + r * ldv + v + 1);
+        }
+#pragma unroll
+        for (int r = 0; r < WT; ++r) fold16<BF16, PRE>(acc, funnel16(a[r], b[r], wo, bs), r == 0, inv, c);
+      } else {
+        for (int32_t r = 0; r < W; ++r)
+          fold16<BF16, PRE>(acc, funnel16(load16<kNT>(in4 + r * ldv + v), load16<kNT>(in4 + r * ldv + v + 1), wo, bs),
+                            r == 0, inv, c);
+      }
+      y = pack16<BF16>(acc);
+    }
     store16<kNTS>(reinterpret_cast<u32x4*>(out) + q * (ld_out / E) + k, y);
   } else {
     const int64_t e1 = min((k + 1) * E, len);
@@ -501,9 +563,8 @@ hipError_t launch_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64
 template <bool BF16, bool PRE>
 hipError_t rs_v_w(int32_t W, const void* in, int64_t ld_in, void* out, int64_t ld_out,
                   const SegArgs& sa, int64_t maxlen, float inv, float c, hipStream_t stream) {
-  constexpr int E = BF16 ? 8 : 4;
-  const dim3 grid((unsigned)((maxlen + (int64_t)kThreads * E - 1) / ((int64_t)kThreads * E)),
-                  (unsigned)W);
+  const dim3 grid((unsigned)sa.bpre[W]);
+  (void)maxlen;
   switch (W) {
 #define DC_RSV_W(w)                                                                          \
   case w:                                                                                    \
@@ -528,8 +589,15 @@ hipError_t launch_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int
                                    int32_t pre_div, hipStream_t stream) {
   SegArgs sa{};
   int64_t maxlen = 0;
+  const int64_t E = dtype == DC_BF16 ? 8 : 4;
   for (int q = 0; q <= W; ++q) sa.seg[q] = seg_start[q];
-  for (int q = 0; q < W; ++q) maxlen = max(maxlen, seg_start[q + 1] - seg_start[q]);
+  sa.bpre[0] = 0;
+  for (int q = 0; q < W; ++q) {
+    const int64_t len = seg_start[q + 1] - seg_start[q];
+    maxlen = max(maxlen, len);
+    sa.bpre[q + 1] = sa.bpre[q] + ((len + E - 1) / E + kThreads - 1) / kThreads;
+  }
+  for (int q = W + 1; q <= DC_MAX_W; ++q) sa.bpre[q] = sa.bpre[W];
   if (maxlen == 0) return hipSuccess;
   float inv, c;
   reciprocal(W, &inv, &c);

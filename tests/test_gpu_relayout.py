@@ -132,3 +132,68 @@ def test_relayout_reduce_scatter_w8_402m_full_size():
         assert np.array_equal(U.bits(got, w.dtype), wb[q, np.arange(len(picks))]), b
     del x
     torch.cuda.empty_cache()
+
+
+RSV_CASES = [(W, dtype, pre) for W in (1, 2, 3, 4, 8, 16) for dtype in (wl.DT_BF16, wl.DT_F32)
+             for pre in (0, 1) if (W + pre) % 2 == 0 or W in (8, 16)]
+
+
+@pytest.mark.parametrize("W,dtype,pre", RSV_CASES, ids=lambda v: str(v))
+def test_reduce_scatter_v_every_offset(W, dtype, pre):
+    """Segments starting at every offset inside a 16-byte vector, with
+    lengths below, at and above a vector and spanning several tiles: the
+    shifted-vector path and the element tail, bit-exact."""
+    import torch
+    rng = random.Random(500 + W + 10 * dtype)
+    E = 8 if dtype == wl.DT_BF16 else 4
+    lens = []
+    for q in range(W):
+        k = q % 6
+        lens.append([0, 1, E - 1, E, E + 3, 3000 + rng.randint(0, 2 * E)][k] if W <= 6 else
+                    rng.choice([0, 1, E, 2 * E + 1, 777, 5000 + rng.randint(0, E)]))
+    # shift every segment start so starts cover all residues mod E
+    seg = [0]
+    for q in range(W):
+        seg.append(seg[-1] + lens[q])
+    pad = rng.randint(0, E - 1)
+    seg = [s + pad for s in seg]
+    seg[0] = 0   # the first shard runs from 0: it absorbs the pad
+    n = seg[-1]
+    ld = max(64, wl.round_up(n, 64))
+    scale = wl.sigma_scale(1e-2)
+    x = U.gen_slab(dtype, W, ld, n, 61 + W, 0, scale)
+    hx = U.host_slab(dtype, W, ld, n, 61 + W, 0, scale)
+    maxlen = max(seg[q + 1] - seg[q] for q in range(W))
+    ld_s = max(64, wl.round_up(maxlen, 64))
+    sh = U.empty_slab(dtype, W, ld_s)
+    U.say("rs-v offsets", W, dtype, pre, [s % E for s in seg[:-1]])
+    dc.dc_reduce_scatter_v(W, dtype, x, ld, sh, ld_s, seg, pre)
+    torch.cuda.synchronize()
+    hs = np.zeros((W, ld_s), hx.dtype)
+    U.bits(hs, dtype)[:] = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
+    oracle.reduce_scatter_v(W, dtype, hx, hs, seg, pre)
+    assert np.array_equal(U.bits(U.to_host(sh, dtype), dtype), U.bits(hs, dtype))
+
+
+def test_reduce_scatter_v_all_residues():
+    """W=8 bf16 with segment q starting at residue q mod 8, several tiles long."""
+    import torch
+    W, dtype, E = 8, wl.DT_BF16, 8
+    seg = [0]
+    for q in range(W):
+        seg.append(seg[-1] + 4099 * 8 + 1)   # each start advances the residue by one
+    n = seg[-1]
+    assert sorted(s % E for s in seg[:-1]) == list(range(E))
+    ld = wl.round_up(n, 64)
+    scale = wl.sigma_scale(1e-2)
+    x = U.gen_slab(dtype, W, ld, n, 77, 0, scale)
+    hx = U.host_slab(dtype, W, ld, n, 77, 0, scale)
+    ld_s = wl.round_up(4099 * 8 + 1, 64)
+    for pre in (0, 1):
+        sh = U.empty_slab(dtype, W, ld_s)
+        dc.dc_reduce_scatter_v(W, dtype, x, ld, sh, ld_s, seg, pre)
+        torch.cuda.synchronize()
+        hs = np.zeros((W, ld_s), np.uint16)
+        hs[:] = U.SENTINEL16
+        oracle.reduce_scatter_v(W, dtype, hx, hs, seg, pre)
+        assert np.array_equal(U.to_host(sh, dtype), hs), pre
