@@ -449,14 +449,23 @@ __global__ __launch_bounds__(kFT) DC_FLUSH_ATTR void k_flush(FlushParams p) {
 template <bool BF16, int WT, int C2, int S2, int PRE>
 hipError_t launch_kernel(const FlushParams& p, hipStream_t stream) {
   constexpr int U = DC_FLUSH_U;
-  const int64_t blocks = (p.nv + kFT * U - 1) / (kFT * U);
+  // Tiles sit on absolute multiples of the tile size, not at the bucket's
+  // first vector: a bucket that starts inside a cache line would otherwise
+  // have every wave's 1 KB straddle lines, sharing partial lines between
+  // neighbouring tiles (measured 15% slower on such buckets).  Vectors in
+  // front of the bucket fall outside its columns and are skipped.
+  FlushParams q = p;
+  const int64_t shift = p.v0 % (kFT * U);
+  q.v0 = p.v0 - shift;
+  q.nv = p.nv + shift;
+  const int64_t blocks = (q.nv + kFT * U - 1) / (kFT * U);
   if (blocks == 0) return hipSuccess;
-  if (p.flat != nullptr)
+  if (q.flat != nullptr)
     hipLaunchKernelGGL((k_flush<BF16, WT, C2, S2, PRE, U, DC_FLUSH_NT != 0, true>),
-                       dim3((unsigned)blocks), dim3(kFT), 0, stream, p);
+                       dim3((unsigned)blocks), dim3(kFT), 0, stream, q);
   else
     hipLaunchKernelGGL((k_flush<BF16, WT, C2, S2, PRE, U, DC_FLUSH_NT != 0, false>),
-                       dim3((unsigned)blocks), dim3(kFT), 0, stream, p);
+                       dim3((unsigned)blocks), dim3(kFT), 0, stream, q);
   return hipGetLastError();
 }
 

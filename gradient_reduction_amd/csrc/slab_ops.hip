@@ -108,8 +108,12 @@ __global__ __launch_bounds__(kThreads) void k_rs_elem(int32_t W, const void* __r
 // aligned.  The partial last vector of a shard goes element by element.
 struct SegArgs {
   int64_t seg[DC_MAX_W + 1];
-  int64_t bpre[DC_MAX_W + 1];   // first workgroup of each shard (shards' vectors / kThreads, prefix)
+  int64_t bpre[DC_MAX_W + 1];   // first workgroup of each shard (prefix of its workgroup counts)
 };
+
+// A shard's workgroups start kRsvAlign-aligned in absolute input vectors:
+// lanes in front of the shard idle, and every wave reads whole cache lines.
+constexpr int64_t kRsvAlign = 64;
 
 // The 16 bytes that start `wo` words + `bs` bytes (wo in 0..3, bs in {0, 2})
 // into the 32 bytes a:b; wo and bs are the same for the whole block.
@@ -150,8 +154,8 @@ __global__ __launch_bounds__(kThreads) void k_rs_v(int32_t W, const void* __rest
     }
   }
   const int64_t len = s1 - s0;
-  const int64_t k = (blk - b0) * kThreads + threadIdx.x;
-  if (k * E >= len) return;
+  const int64_t k = (blk - b0) * kThreads + threadIdx.x - (s0 / E) % kRsvAlign;
+  if (k < 0 || k * E >= len) return;
   const int64_t ldv = ld_in / E;
   const int32_t o = (int32_t)(s0 % E);
   if ((k + 1) * E <= len) {
@@ -595,7 +599,8 @@ hipError_t launch_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int
   for (int q = 0; q < W; ++q) {
     const int64_t len = seg_start[q + 1] - seg_start[q];
     maxlen = max(maxlen, len);
-    sa.bpre[q + 1] = sa.bpre[q] + ((len + E - 1) / E + kThreads - 1) / kThreads;
+    const int64_t lead = (seg_start[q] / E) % kRsvAlign;
+    sa.bpre[q + 1] = sa.bpre[q] + (lead + (len + E - 1) / E + kThreads - 1) / kThreads;
   }
   for (int q = W + 1; q <= DC_MAX_W; ++q) sa.bpre[q] = sa.bpre[W];
   if (maxlen == 0) return hipSuccess;

@@ -147,12 +147,14 @@ class Zero1FlushExecutor:
         """in_addr, out_addr: [W, P] device addresses of rank r's gradient of
         param p and of its grad buffer (0 = empty buffer).  A task's slice
         starts at its position within its param (the params' tasks in bucket
-        order).  Task coordinates are re-laid at 16-byte steps so aligned
-        buffers move as whole vectors.  Tables are validated on the host and
-        kept on the device."""
+        order).  Task coordinates are re-laid at 128-byte steps: buffers that
+        start on a 128-byte boundary then move as whole vectors with every
+        wave's accesses on whole cache lines.  Tables are validated on the
+        host and kept on the device."""
         torch = self.torch
-        W, E = self.W, 8 if self.dtype == dc.DC_BF16 else 4
+        W = self.W
         eb = 2 if self.dtype == dc.DC_BF16 else 4
+        step = 128 // eb
         in_addr = np.asarray(in_addr, np.uint64).reshape(W, self.P)
         out_addr = np.asarray(out_addr, np.uint64).reshape(W, self.P)
         seen = np.zeros(self.P, np.int64)
@@ -168,7 +170,7 @@ class Zero1FlushExecutor:
                 tin[k] = in_addr[:, param] + skip
                 tout[k] = np.where(out_addr[:, param] != 0, out_addr[:, param] + skip, 0)
                 seen[param] += numel
-                pos = -(-(pos + numel) // E) * E
+                pos = -(-(pos + numel) // step) * step
             t = dc.tasks_array(rows)
             extent = int(rows[-1][0] + rows[-1][1]) if rows else 0
             dc.dc_validate_buffer_tasks(W, self.dtype, t, len(t), extent, self.comms,
