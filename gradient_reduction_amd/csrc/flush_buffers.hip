@@ -21,7 +21,11 @@ namespace {
 #ifndef DC_BUF_U
 #define DC_BUF_U 2                  // vector slots per thread per tile
 #endif
+#ifndef DC_BUF_TPB
+#define DC_BUF_TPB 256              // threads per workgroup
+#endif
 constexpr int kBufU = DC_BUF_U;
+constexpr int kBT = DC_BUF_TPB;
 constexpr int kPtrStage = 1024;     // staged pointers per table (LDS)
 
 struct BufParams {
@@ -47,7 +51,7 @@ __device__ __forceinline__ void comm_recip(int32_t c, float* inv, float* cf) {
 }
 
 template <bool BF16, int WT, bool PRE>
-__global__ __launch_bounds__(kThreads) void k_flush_buffers(BufParams p) {
+__global__ __launch_bounds__(kBT) void k_flush_buffers(BufParams p) {
   constexpr int E = BF16 ? 8 : 4;
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int WS = WT > 0 ? WT : DC_MAX_W;                    // pointer stride per task
@@ -68,32 +72,32 @@ __global__ __launch_bounds__(kThreads) void k_flush_buffers(BufParams p) {
       s_cst[q] = p.cstride[q];
     }
   }
-  const int64_t t0 = (int64_t)blockIdx.x * (kThreads * kBufU);
-  const int64_t t1 = min(t0 + (int64_t)(kThreads * kBufU), p.nslots);
+  const int64_t t0 = (int64_t)blockIdx.x * (kBT * kBufU);
+  const int64_t t1 = min(t0 + (int64_t)(kBT * kBufU), p.nslots);
   const int64_t lo = t0 * E, hi = min(t1 * E, p.bucket_numel);
   int32_t first, last;
-  kary_bounds<kThreads>(p.ntasks, [&](int32_t i) { return p.tasks[i].offset; }, lo, hi, first, last);
+  kary_bounds<kBT>(p.ntasks, [&](int32_t i) { return p.tasks[i].offset; }, lo, hi, first, last);
   first = max(first - 1, 0);
   last = last - 1;
   for (int32_t base = first; base <= last; base += S) {
     const int32_t cnt = min(S, last - base + 1);
     __syncthreads();
-    for (int32_t x = threadIdx.x; x < cnt; x += kThreads) {
+    for (int32_t x = threadIdx.x; x < cnt; x += kBT) {
       const dc_task t = p.tasks[base + x];
       s_off[x] = t.offset;
       s_end[x] = t.offset + (t.numel > 0 ? t.numel : 0);
       s_comm[x] = (t.comm >= 0 && t.comm < p.num_comms) ? t.comm : 0;
     }
-    for (int32_t x = threadIdx.x; x < cnt * W; x += kThreads) {
+    for (int32_t x = threadIdx.x; x < cnt * W; x += kBT) {
       const int32_t k = x / W, r = x - k * W;
       const int64_t g = (int64_t)(base + k) * W + r;
       s_in[k * WS + r] = reinterpret_cast<const char*>(p.in_ptrs[g]);
       s_out[k * WS + r] = reinterpret_cast<char*>(p.out_ptrs[g]);
     }
     __syncthreads();
-    for (int32_t x = threadIdx.x; x < cnt; x += kThreads) s_vec[x] = s_off[x] % E == 0;
+    for (int32_t x = threadIdx.x; x < cnt; x += kBT) s_vec[x] = s_off[x] % E == 0;
     __syncthreads();
-    for (int32_t x = threadIdx.x; x < cnt * W; x += kThreads) {
+    for (int32_t x = threadIdx.x; x < cnt * W; x += kBT) {
       const int32_t k = x / W, r = x - k * W;
       if (((reinterpret_cast<uintptr_t>(s_in[k * WS + r]) | reinterpret_cast<uintptr_t>(s_out[k * WS + r])) & 15) != 0)
         s_vec[k] = 0;
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void k_flush_buffers(BufParams p) {
     __syncthreads();
 #pragma unroll 1
     for (int u = 0; u < kBufU; ++u) {
-      const int64_t v = t0 + threadIdx.x + (int64_t)u * kThreads;
+      const int64_t v = t0 + threadIdx.x + (int64_t)u * kBT;
       if (v >= t1) break;
       const int64_t d0 = v * E;
       const int32_t k = last_le(s_off, cnt, d0);
@@ -173,11 +177,11 @@ __global__ __launch_bounds__(kThreads) void k_flush_buffers(BufParams p) {
 
 template <bool BF16, bool PRE>
 hipError_t launch_w(const BufParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.nslots + kThreads * kBufU - 1) / (kThreads * kBufU)));
+  const dim3 grid((unsigned)((p.nslots + kBT * kBufU - 1) / (kBT * kBufU)));
   switch (p.W) {
 #define DC_FB_W(w)                                                                        \
   case w:                                                                                 \
-    hipLaunchKernelGGL((k_flush_buffers<BF16, w, PRE>), grid, dim3(kThreads), 0, stream, p); \
+    hipLaunchKernelGGL((k_flush_buffers<BF16, w, PRE>), grid, dim3(kBT), 0, stream, p); \
     break;
     DC_FB_W(2)
     DC_FB_W(4)
@@ -185,7 +189,7 @@ hipError_t launch_w(const BufParams& p, hipStream_t stream) {
     DC_FB_W(16)
 #undef DC_FB_W
     default:
-      hipLaunchKernelGGL((k_flush_buffers<BF16, 0, PRE>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((k_flush_buffers<BF16, 0, PRE>), grid, dim3(kBT), 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -11,7 +11,11 @@
 namespace dc {
 namespace {
 
-constexpr int kPieceStage = 256;
+#ifndef DC_RL_TPB
+#define DC_RL_TPB 64            // one wave per workgroup (5% faster than 256)
+#endif
+constexpr int kRT = DC_RL_TPB;          // threads per workgroup
+constexpr int kPieceStage = kRT;        // pieces staged per pass (one per thread)
 constexpr int kRelayoutU = 2;
 
 struct RelayoutParams {
@@ -33,18 +37,18 @@ struct RelayoutParams {
 // Source columns are checked against the bucket, so a bad plan never reads
 // or writes outside the bucket of the input or [0, out_numel) of the output.
 template <int EB, int WT>
-__global__ __launch_bounds__(kThreads) void k_relayout(RelayoutParams p) {
+__global__ __launch_bounds__(kRT) void k_relayout(RelayoutParams p) {
   constexpr int E = 16 / EB;
   __shared__ int64_t s_dst[kPieceStage];
   __shared__ int64_t s_src[kPieceStage];
   __shared__ int64_t s_end[kPieceStage];
   const int W = WT > 0 ? WT : p.W;
   const int64_t nvec = (p.out_numel + E - 1) / E;
-  const int64_t t0 = (int64_t)blockIdx.x * (kThreads * kRelayoutU);
-  const int64_t t1 = min(t0 + (int64_t)(kThreads * kRelayoutU), nvec);
+  const int64_t t0 = (int64_t)blockIdx.x * (kRT * kRelayoutU);
+  const int64_t t1 = min(t0 + (int64_t)(kRT * kRelayoutU), nvec);
   const int64_t lo = t0 * E, hi = min(t1 * E, p.out_numel);
   int32_t first, last;
-  kary_bounds<kThreads>(p.npieces, [&](int32_t i) { return p.pieces[i].dst; }, lo, hi, first, last);
+  kary_bounds<kRT>(p.npieces, [&](int32_t i) { return p.pieces[i].dst; }, lo, hi, first, last);
   first = max(first - 1, 0);
   last = last - 1;
   const char* in = reinterpret_cast<const char*>(p.in);
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void k_relayout(RelayoutParams p) {
     __syncthreads();
 #pragma unroll 1
     for (int u = 0; u < kRelayoutU; ++u) {
-      const int64_t v = t0 + threadIdx.x + (int64_t)u * kThreads;
+      const int64_t v = t0 + threadIdx.x + (int64_t)u * kRT;
       if (v >= t1) break;
       const int64_t d0 = v * E;
       const int64_t d1 = min(d0 + E, p.out_numel);
@@ -107,18 +111,18 @@ template <int EB>
 hipError_t launch_eb(const RelayoutParams& p, hipStream_t stream) {
   constexpr int E = 16 / EB;
   const int64_t nvec = (p.out_numel + E - 1) / E;
-  const dim3 grid((unsigned)((nvec + kThreads * kRelayoutU - 1) / (kThreads * kRelayoutU)));
+  const dim3 grid((unsigned)((nvec + kRT * kRelayoutU - 1) / (kRT * kRelayoutU)));
   switch (p.W) {
 #define DC_RL_W(w)                                                                      \
   case w:                                                                               \
-    hipLaunchKernelGGL((k_relayout<EB, w>), grid, dim3(kThreads), 0, stream, p);        \
+    hipLaunchKernelGGL((k_relayout<EB, w>), grid, dim3(kRT), 0, stream, p);        \
     break;
     DC_RL_W(4)
     DC_RL_W(8)
     DC_RL_W(16)
 #undef DC_RL_W
     default:
-      hipLaunchKernelGGL((k_relayout<EB, 0>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((k_relayout<EB, 0>), grid, dim3(kRT), 0, stream, p);
   }
   return hipGetLastError();
 }
