@@ -355,3 +355,91 @@ def test_flush_zero2_w8_402m_full_size():
 
 def test_flush_zero2_w16_mixed_1_2b_full_size_in_place():
     full_size_flush(wl.mixed_flush_w16(), False, in_place=True, zero2=True)
+
+
+def test_flush_robust_to_bad_tables():
+    """The documented contract for a task table that breaks the rules: an
+    out-of-range param or owner entry means AllReduce, an out-of-range comm
+    means comm 0, a task running past the bucket is cut at its end, and no
+    column outside the bucket is written.  The oracle runs the same table
+    with those readings applied by hand."""
+    import torch
+    W, dtype = 8, wl.DT_BF16
+    P = 6
+    owner = np.array([3, 9, -7, -1, 0, 7], np.int32)      # 9 and -7 are out of range
+    col0, bucket_numel = 40, 5000
+    tasks = [(0, 700, 0, 0), (700, 900, 1, 0), (1600, 333, 2, 0), (1933, 1000, P + 5, 0),
+             (2933, 400, 4, 5), (3333, 2000, 5, 0)]             # param P+5, comm 5, past the end
+    ld = wl.round_up(col0 + bucket_numel + 3000, 64)
+    scale = wl.sigma_scale(1e-2)
+    x = U.gen_slab(dtype, W, ld, ld, 123, 0, scale)
+    y = U.empty_slab(dtype, W, ld)
+    t = dc.tasks_array(tasks)
+    d_tasks = torch.from_numpy(t.view(np.uint8).copy()).cuda()
+    d_owner = torch.from_numpy(owner).cuda()
+    dc.dc_flush_bucket(W, dtype, x, ld, y, ld, col0, bucket_numel, d_tasks, len(tasks), d_owner, P,
+                       [(W, 1)], 1, 1)
+    torch.cuda.synchronize()
+    # the readings, applied by hand for the oracle
+    own_fixed = np.where((owner >= 0) & (owner < W), owner, -1).astype(np.int32)
+    own_fixed = np.concatenate([own_fixed, [-1]]).astype(np.int32)   # param P: the bad one
+    fixed = []
+    for off, n, p, c in tasks:
+        p = p if 0 <= p < P else P
+        c = c if c == 0 else 0
+        n = min(n, bucket_numel - off)
+        fixed.append((off, n, p, c))
+    hin = U.host_slab(dtype, W, ld, ld, 123, 0, scale)
+    hout = np.full_like(hin, U.SENTINEL16)
+    oracle.flush(W, dtype, hin, hout, col0, [f[0] for f in fixed], [f[1] for f in fixed],
+                 [f[2] for f in fixed], [f[3] for f in fixed], own_fixed, [W], [1], 1)
+    assert np.array_equal(U.to_host(y, dtype), hout)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_flush_random_abi_cases(seed):
+    """Seeded random flushes straight through the ABI: random W, dtype,
+    communicators, owners, pre-division, bucket start column (any residue),
+    task sizes from 0 to several tiles, in and out of place."""
+    import torch
+    rng = random.Random(1000 + seed)
+    W = rng.choice([1, 2, 3, 4, 6, 8, 12, 16])
+    dtype = rng.choice([wl.DT_BF16, wl.DT_F32])
+    divs = [c for c in range(1, W) if W % c == 0]
+    comms = [(W, 1)]
+    if divs and rng.random() < 0.7:
+        c = rng.choice(divs)
+        comms.append((c, rng.choice([1, W // c])))
+    n_tasks = rng.randint(1, 40)
+    sizes = [rng.choice([0, 1, 2, 7, 8, 9, 63, 64, 65, 511, 513, 1024, 3000, 9000]) for _ in range(n_tasks)]
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int).tolist()
+    bucket_numel = int(sum(sizes))
+    P = n_tasks
+    owner = np.array([rng.choice([-1, rng.randrange(W)]) for _ in range(P)], np.int32)
+    t_comm = [rng.randrange(len(comms)) for _ in range(n_tasks)]
+    tasks = [(offs[k], sizes[k], k, t_comm[k]) for k in range(n_tasks)]
+    col0 = rng.randint(0, 17)
+    pre = rng.randint(0, 1)
+    in_place = rng.random() < 0.3
+    ld = max(64, wl.round_up(col0 + bucket_numel + rng.randint(0, 100), 64))
+    scale = wl.sigma_scale(1e-2)
+    U.say("random flush", seed, W, dtype, comms, n_tasks, bucket_numel, col0, pre, in_place)
+    x = U.gen_slab(dtype, W, ld, ld, 300 + seed, 0, scale)
+    y = x if in_place else U.empty_slab(dtype, W, ld)
+    t = dc.tasks_array(tasks)
+    dc.dc_validate_tasks(W, t, len(t), bucket_numel, P, comms, len(comms))
+    d_tasks = torch.from_numpy(t.view(np.uint8).copy()).cuda()
+    use_owner = rng.random() < 0.7
+    d_owner = torch.from_numpy(owner).cuda() if use_owner else None
+    dc.dc_flush_bucket(W, dtype, x, ld, y, ld, col0, bucket_numel, d_tasks, len(tasks), d_owner, P,
+                       comms, len(comms), pre)
+    torch.cuda.synchronize()
+    hin = U.host_slab(dtype, W, ld, ld, 300 + seed, 0, scale)
+    if in_place:
+        hout = hin
+    else:
+        hout = np.zeros_like(hin)
+        U.bits(hout, dtype)[:] = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
+    oracle.flush(W, dtype, hin, hout, col0, offs, sizes, list(range(n_tasks)), t_comm,
+                 owner if use_owner else None, [c for c, _ in comms], [s for _, s in comms], pre)
+    assert np.array_equal(U.bits(U.to_host(y, dtype), dtype), U.bits(hout, dtype))
