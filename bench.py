@@ -161,10 +161,27 @@ def bench_flush(args, w, reduce_to_owner=True, zero2=False):
         roofline["access_mix_ceiling_gbs"] = round(ceiling, 1)
         roofline["frac_of_access_mix_ceiling"] = round(flush_gbs / ceiling, 4)
     extra = {"per_bucket_gbs": [round(b / (m / 1e3) / 1e9, 1) for b, m in zip(per_launch, kern.mean(axis=0))],
-             "flush_gbs_median_step": round(flush_gbs_median, 1)}
+             "flush_gbs_median_step": round(flush_gbs_median, 1),
+             "graph_ms_per_step": round(graph_step_ms(torch, args, ex.capture_step(x, ld, y, ld)), 4)}
+    log(f"[bench] the same step replayed as one HIP graph: {extra['graph_ms_per_step']:.4f} ms")
     del x, y
     torch.cuda.empty_cache()
     return ms_step, value, step_bytes, roofline, extra
+
+
+def graph_step_ms(torch, args, g):
+    """Average time of one replay of a captured step (same warm-up and step
+    counts as the eager timing)."""
+    for _ in range(max(args.warmup, 1)):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / args.steps
 
 
 def access_mix_ceiling(w, owner, x, y, ld, psize=None, split=None):

@@ -198,6 +198,33 @@ class Zero1FlushExecutor:
                                    self.comms, len(self.comms), self.pre_div, stream)
         self.flushes += 1
 
+    # -- one step as a HIP graph --------------------------------------------------
+
+    def capture_step(self, slab_in=None, ld_in: int = 0, slab_out=None, ld_out: int = 0,
+                     fused: bool = False):
+        """Record one step (owner map + every bucket flush, or every fused
+        flush) as a HIP graph; `graph.replay()` re-issues it with one launch.
+        The graph keeps the pointers, sizes and tables given here, so replay
+        it on the same buffers.  No call in the step allocates, synchronizes
+        or clears memory, so every kernel records as a plain kernel node.
+        The probe is not printed from a graph."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        probe, self.reduce_probe = self.reduce_probe, False
+        flushes = self.flushes
+        try:
+            with torch.cuda.graph(g):
+                self.build_owner_map()
+                for b in range(len(self.buckets)):
+                    if fused:
+                        self.flush_buffers(b)
+                    else:
+                        self.flush(b, slab_in, ld_in, slab_out, ld_out)
+        finally:
+            self.reduce_probe = probe
+            self.flushes = flushes
+        return g
+
     def probe(self, b: int):
         if self.h_owner is None:
             self.fetch_metadata()

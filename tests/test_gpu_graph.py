@@ -1,0 +1,69 @@
+"""A flush step recorded as a HIP graph: every replay, with eager work and
+synchronizations between replays, matches the eager step bit for bit."""
+import numpy as np
+import pytest
+
+from gradient_reduction_amd import dc, executor
+from synth import workloads as wl
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dc.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _workloads():
+    rng_sizes = [7, 0, 3000, 65, 12000, 1, 9, 40000, 513, 2048]
+    return [
+        (wl.tiny_flush(), True, False),
+        (wl.custom_flush("g-w8-f32", 8, wl.DT_F32, rng_sizes * 4, capacity=30_000, pre_div=1,
+                         value_seed=5), False, False),
+        (wl.custom_flush("g-w16-bf16-sub", 16, wl.DT_BF16, rng_sizes * 3, group_begin=[0, 15, 30],
+                         group_comm=[0, 1], comms=[wl.Comm(16, 1), wl.Comm(4, 4)], capacity=25_000,
+                         pre_div=1, value_seed=6), True, False),
+        (wl.tiny_flush(), False, True),
+    ]
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_graph_replays_match_eager(case):
+    import torch
+    w, owner, zero2 = _workloads()[case]
+    U.say("graph", w.name, owner, zero2)
+    ld = w.ld
+    x = U.gen_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, w.scale)
+    sent = U.SENTINEL16 if w.dtype == wl.DT_BF16 else U.SENTINEL32
+    ex = executor.from_workload(w, reduce_to_owner=owner, zero2=zero2)
+    # eager
+    y_eager = U.empty_slab(w.dtype, w.W, ld)
+    ex.build_owner_map()
+    for b in range(len(w.buckets)):
+        ex.flush(b, x, ld, y_eager, ld)
+    torch.cuda.synchronize()
+    want = y_eager.cpu()
+    # graph on its own output slab
+    y = U.empty_slab(w.dtype, w.W, ld)
+    g = ex.capture_step(x, ld, y, ld)
+    for rep in range(4):
+        y.fill_(sent)                       # eager work between replays
+        torch.cuda.synchronize()
+        assert bool((y == sent).all())
+        g.replay()
+        if rep % 2:
+            torch.cuda.synchronize()
+        got = y.cpu()
+        assert torch.equal(got, want), f"replay {rep}"
+    # the eager path still works after capture
+    y2 = U.empty_slab(w.dtype, w.W, ld)
+    ex.build_owner_map()
+    for b in range(len(w.buckets)):
+        ex.flush(b, x, ld, y2, ld)
+    torch.cuda.synchronize()
+    assert torch.equal(y2.cpu(), want)

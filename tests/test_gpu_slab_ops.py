@@ -375,3 +375,40 @@ def test_accumulate_reduce_equals_two_steps(W, M, init, keep, out_rows, alias):
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
         wacc = a2 if keep else hacc
         assert np.array_equal(acc.cpu().numpy().view(np.uint32), wacc.view(np.uint32))
+
+
+def test_all_gather_schedules_7b_layer_full_size():
+    """The 7B-layer slab (W = 8, L = 25,297,920 bf16): every schedule's
+    finished buffer equals the one-shot rank-order gather bit for bit, and
+    after step 1 of the ring exactly two chunks per node are placed (the
+    rest keep the sentinel)."""
+    import torch
+    w = wl.rs_ag_w8()
+    W, M, dtype = w.W, w.M, w.dtype
+    L = M // W
+    U.say("ag schedules full size", M)
+    x = U.gen_slab(dtype, W, w.ld, M, w.value_seed, 0, w.scale)
+    ld_sh = wl.round_up(L, 64)
+    sh = U.empty_slab(dtype, W, ld_sh)
+    dc.dc_reduce_scatter(W, dtype, x, w.ld, sh, ld_sh, M, 1)
+    del x
+    want = U.empty_slab(dtype, W, w.ld)
+    dc.dc_all_gather(W, dtype, sh, ld_sh, want, w.ld, L, dc.DC_ORDER_RANK, -1)
+    steps = {dc.DC_SCHED_RING: W - 1, dc.DC_SCHED_BIDIR: W // 2, dc.DC_SCHED_RD: 3}
+    for algo, S in steps.items():
+        out = U.empty_slab(dtype, W, w.ld)
+        for s in range(S + 1):
+            dc.dc_all_gather_step(W, dtype, sh, ld_sh, out, w.ld, L, algo, s)
+            if algo == dc.DC_SCHED_RING and s == 1:
+                torch.cuda.synchronize()
+                for i in range(W):
+                    for c in range(W):
+                        blk = out[i, c * L:(c + 1) * L]
+                        placed = c in (i, (i - 1) % W)
+                        if placed:
+                            assert torch.equal(blk, want[i, c * L:(c + 1) * L]), (i, c)
+                        else:
+                            assert bool((blk == U.SENTINEL16).all()), (i, c)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:, :M], want[:, :M]), algo
+        del out
