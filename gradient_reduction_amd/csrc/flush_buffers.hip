@@ -22,11 +22,15 @@ namespace {
 #define DC_BUF_U 2                  // vector slots per thread per tile
 #endif
 #ifndef DC_BUF_TPB
-#define DC_BUF_TPB 256              // threads per workgroup
+#define DC_BUF_TPB 64               // threads per workgroup (one wave)
 #endif
 constexpr int kBufU = DC_BUF_U;
 constexpr int kBT = DC_BUF_TPB;
-constexpr int kPtrStage = 1024;     // staged pointers per table (LDS)
+#ifndef DC_BUF_PTRS
+#define DC_BUF_PTRS 256             // staged pointers per table (LDS): small enough
+                                    // that one-wave workgroups are not LDS bound
+#endif
+constexpr int kPtrStage = DC_BUF_PTRS;
 
 struct BufParams {
   const dc_task* tasks;
