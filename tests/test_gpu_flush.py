@@ -75,6 +75,17 @@ def owner_workloads():
             gcomm.append(rng.choice([0, 0, 1, 2]))
         out.append(wl.custom_flush(f"rand{k}", W, wl.DT_BF16, numel, group_begin=gb,
                                    group_comm=gcomm, comms=comms, capacity=10 ** 9))
+    # the limits: W = 64, 64 groups, 8 communicators (contiguous and strided)
+    numel, gb, gcomm = [], [0], []
+    comms64 = [wl.Comm(64, 1), wl.Comm(32, 1), wl.Comm(16, 4), wl.Comm(8, 8), wl.Comm(4, 1),
+               wl.Comm(2, 32), wl.Comm(1, 1), wl.Comm(32, 2)]
+    for g in range(64):
+        numel += [rng.choice([0, 1, 5, 63, 64, 65, 700, 4099]) for _ in range(rng.randint(1, 40))]
+        gb.append(len(numel))
+        gcomm.append(rng.choice(range(8)) if g % 3 else 0)
+    out.append(wl.custom_flush("W64-G64-C8", 64, wl.DT_BF16, numel, group_begin=gb,
+                               group_comm=gcomm, comms=comms64, capacity=25_000, pre_div=1,
+                               value_seed=64))
     return out
 
 
@@ -175,6 +186,15 @@ def small_flush_workloads():
                                pre_div=1, value_seed=91))
     out.append(wl.custom_flush("W16-f32-5k-tiny", 16, wl.DT_F32, tiny[:5000],
                                capacity=10 ** 9, pre_div=0, value_seed=92))
+    # the limits: W = 64 (the ABI's maximum) with all 8 communicators, both dtypes
+    comms64 = [wl.Comm(64, 1), wl.Comm(32, 1), wl.Comm(16, 4), wl.Comm(8, 8), wl.Comm(4, 1),
+               wl.Comm(2, 32), wl.Comm(1, 1), wl.Comm(32, 2)]
+    for dtype in (wl.DT_BF16, wl.DT_F32):
+        sizes = [rng.choice([0, 1, 7, 9, 64, 333, 2000, 9000]) for _ in range(40)]
+        out.append(wl.custom_flush(f"W64-C8-{wl.DTYPE_NAME[dtype]}", 64, dtype, sizes,
+                                   group_begin=[0, 10, 20, 30, 40], group_comm=[0, 1, 3, 5],
+                                   comms=comms64, capacity=25_000, pre_div=1 - dtype,
+                                   value_seed=640 + dtype))
     return out
 
 

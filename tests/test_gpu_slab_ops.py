@@ -26,7 +26,8 @@ def _gpu():
 
 RS_CASES = [(8, wl.DT_BF16, 8 * 5000, 0), (8, wl.DT_BF16, 8 * 4097, 1), (4, wl.DT_F32, 4 * 9999, 1),
             (3, wl.DT_BF16, 3 * 2001, 1), (16, wl.DT_F32, 16 * 1024, 0), (5, wl.DT_F32, 5 * 333, 0),
-            (1, wl.DT_BF16, 800, 1), (2, wl.DT_BF16, 0, 0)]
+            (1, wl.DT_BF16, 800, 1), (2, wl.DT_BF16, 0, 0), (64, wl.DT_BF16, 64 * 1001, 1),
+            (64, wl.DT_F32, 64 * 512, 0)]
 
 
 @pytest.mark.parametrize("W,dtype,M,pre", RS_CASES, ids=lambda v: str(v))
@@ -157,7 +158,8 @@ def test_reduce_scatter_ring_7b_layer_full_size():
 
 AGS_CASES = [(W, dtype, L, algo) for (W, dtype, L) in
              [(4, wl.DT_BF16, 1000), (8, wl.DT_F32, 333), (5, wl.DT_BF16, 77), (16, wl.DT_BF16, 2048),
-              (1, wl.DT_F32, 64), (2, wl.DT_BF16, 9), (3, wl.DT_F32, 0)]
+              (1, wl.DT_F32, 64), (2, wl.DT_BF16, 9), (3, wl.DT_F32, 0), (64, wl.DT_BF16, 100),
+              (32, wl.DT_F32, 33)]
              for algo in (dc.DC_SCHED_RING, dc.DC_SCHED_BIDIR, dc.DC_SCHED_RD)
              if algo != dc.DC_SCHED_RD or W & (W - 1) == 0]
 
@@ -180,11 +182,13 @@ def test_all_gather_step_schedules(W, dtype, L, algo):
     U.bits(ho, dtype)[:] = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
     steps = {dc.DC_SCHED_RING: W - 1, dc.DC_SCHED_BIDIR: W // 2,
              dc.DC_SCHED_RD: W.bit_length() - 1}[algo]
+    compare_every = W <= 16
     for s in range(steps + 1):
         dc.dc_all_gather_step(W, dtype, sh, ld_sh, out, ld, L, algo, s)
         oracle.all_gather_step(W, dtype, hsh, ho, L, algo, s)
-        torch.cuda.synchronize()
-        assert np.array_equal(U.bits(U.to_host(out, dtype), dtype), U.bits(ho, dtype)), s
+        if compare_every or s == steps:
+            torch.cuda.synchronize()
+            assert np.array_equal(U.bits(U.to_host(out, dtype), dtype), U.bits(ho, dtype)), s
     rank = U.empty_slab(dtype, W, ld)
     dc.dc_all_gather(W, dtype, sh, ld_sh, rank, ld, L, dc.DC_ORDER_RANK, -1)
     torch.cuda.synchronize()
@@ -255,7 +259,8 @@ def test_accumulate(rows, M, init, alias):
 
 @pytest.mark.parametrize("W,M,out_rows,alias", [(4, 1003, 1, False), (4, 1003, 4, False),
                                                 (3, 500, 3, False), (16, 4096, 1, False),
-                                                (4, 2048, 4, True), (8, 5, 1, False)])
+                                                (4, 2048, 4, True), (8, 5, 1, False),
+                                                (64, 999, 1, False), (64, 256, 64, False)])
 def test_deferred_reduce(W, M, out_rows, alias):
     import torch
     ld = wl.round_up(M, 64)
