@@ -110,7 +110,7 @@ const char* dc_strerror(dc_status status) {
     case DC_ERR_DTYPE: return "unknown dtype";
     case DC_ERR_TASKS: return "the task table breaks its contract";
     case DC_ERR_HIP: return "a HIP call failed";
-    case DC_ERR_UNSUPPORTED: return "not supported by this build";
+    case DC_ERR_UNSUPPORTED: return "not supported by this library";
     default: return "unknown status";
   }
 }

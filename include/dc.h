@@ -52,7 +52,7 @@ typedef int32_t dc_status;
 #define DC_ERR_DTYPE 5       /* unknown dtype */
 #define DC_ERR_TASKS 6       /* a task table breaks its contract (dc_validate_tasks) */
 #define DC_ERR_HIP 7         /* a HIP launch or runtime call failed */
-#define DC_ERR_UNSUPPORTED 8 /* a valid request this build does not handle */
+#define DC_ERR_UNSUPPORTED 8 /* a valid request this library does not handle */
 
 #define DC_BF16 0
 #define DC_F32 1
