@@ -41,16 +41,6 @@ constexpr int kStage = kFT;  // tasks staged in LDS per pass over a tile (one pe
 #ifndef DC_FLUSH_NTS
 #define DC_FLUSH_NTS 1    // nontemporal result stores
 #endif
-#ifndef DC_FLUSH_PIPE
-#define DC_FLUSH_PIPE 0   // software-pipeline the row loads across a thread's vectors
-#endif
-#ifndef DC_FLUSH_WPE
-#define DC_FLUSH_WPE 0    // minimum waves per SIMD requested from the register allocator
-#endif
-#ifndef DC_FLUSH_XCD
-#define DC_FLUSH_XCD 0    // give each XCD a contiguous run of tiles
-#endif
-constexpr int kXcds = 8;
 
 struct FlushParams {
   const void* in;
@@ -268,17 +258,12 @@ __device__ __forceinline__ void elem_flush(const FlushParams& p, int64_t col, in
   }
 }
 
-#if DC_FLUSH_WPE
-#define DC_FLUSH_ATTR __attribute__((amdgpu_waves_per_eu(DC_FLUSH_WPE)))
-#else
-#define DC_FLUSH_ATTR
-#endif
 
 // WT > 0: W known at compile time, every communicator of the launch is the
 // data-parallel one or the single shape (C2, S2) (C2 = 0: none).  WT = 0:
 // any W and any communicators, all at run time.
 template <bool BF16, int WT, int C2, int S2, int PRE, int U, bool NT, bool Z2>
-__global__ __launch_bounds__(kFT) DC_FLUSH_ATTR void k_flush(FlushParams p) {
+__global__ __launch_bounds__(kFT) void k_flush(FlushParams p) {
   static_assert(U <= 32, "slow-vector mask is 32 bits");
   constexpr int E = BF16 ? 8 : 4;
   __shared__ int64_t s_off[kStage];
@@ -291,15 +276,7 @@ __global__ __launch_bounds__(kFT) DC_FLUSH_ATTR void k_flush(FlushParams p) {
   __shared__ int64_t s_za[Z2 ? kStage : 1];
   __shared__ int64_t s_zs[Z2 ? kStage : 1];
 
-  int64_t tile = blockIdx.x;
-  if (DC_FLUSH_XCD) {
-    // workgroups are dealt to the XCDs round-robin; renumber so that XCD x
-    // walks the x-th contiguous run of tiles
-    const int64_t nb = gridDim.x, per = (nb + kXcds - 1) / kXcds;
-    const int64_t x = tile % kXcds, k = tile / kXcds;
-    const int64_t full = nb - (per - 1) * kXcds;  // XCDs that get `per` tiles
-    tile = x < full ? x * per + k : full * per + (x - full) * (per - 1) + k;
-  }
+  const int64_t tile = blockIdx.x;
   const int64_t t0 = tile * (kFT * U);
   const int64_t t1 = min(t0 + (int64_t)(kFT * U), p.nv);
   // the tile's columns, relative to the bucket
@@ -349,13 +326,6 @@ __global__ __launch_bounds__(kFT) DC_FLUSH_ATTR void k_flush(FlushParams p) {
     // phase 1: vectors inside one task; phase 2: vectors cut by an edge.
     uint32_t slow = 0;
     if constexpr (WT > 0) {
-#if DC_FLUSH_PIPE
-      // software pipelined: the rows of the next vector are requested
-      // before the current one is folded
-      u32x4 cur[WT];
-      int64_t cav = -1;
-      int32_t croot = -1, cc = WT;
-#endif
 #pragma unroll 1
       for (int u = 0; u < U; ++u) {
         const int64_t tv = t0 + threadIdx.x + (int64_t)u * kFT;
@@ -378,27 +348,13 @@ __global__ __launch_bounds__(kFT) DC_FLUSH_ATTR void k_flush(FlushParams p) {
           }
         }
         if (whole) {
-#if DC_FLUSH_PIPE
-          u32x4 nxt[WT];
-          load_rows<BF16, WT, NT>(p, av, nxt);
-          if (cav >= 0) fold_store_shape<BF16, WT, C2, S2, PRE>(p, cur, cav, croot, cc);
-#pragma unroll
-          for (int r = 0; r < WT; ++r) cur[r] = nxt[r];
-          cav = av;
-          croot = vroot;
-          cc = s_csz[k];
-#else
           u32x4 x[WT];
           load_rows<BF16, WT, NT>(p, av, x);
           fold_store_shape<BF16, WT, C2, S2, PRE>(p, x, av, vroot, s_csz[k]);
-#endif
         } else {
           slow |= 1u << u;
         }
       }
-#if DC_FLUSH_PIPE
-      if (cav >= 0) fold_store_shape<BF16, WT, C2, S2, PRE>(p, cur, cav, croot, cc);
-#endif
     } else {
 #pragma unroll 1
       for (int u = 0; u < U; ++u) {
