@@ -1,4 +1,4 @@
-// Bucket flush (a3-a6) for gfx950.
+// Bucket flush for gfx950.
 //
 // DeepSpeed issue "[REQUEST] DeepCompile ZeRO-1: reduce-to-owner instead of
 // AllReduce", problem statement and "Describe the solution": every bucket

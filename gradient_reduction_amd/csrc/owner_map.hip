@@ -1,4 +1,4 @@
-// Partition lists and owner map (a1, a2) for gfx950.
+// Partition lists and owner map for gfx950.
 //
 // DeepSpeed issue "[REQUEST] DeepCompile ZeRO-1: reduce-to-owner instead of
 // AllReduce", Design points: the owner map costs nothing to build; a param

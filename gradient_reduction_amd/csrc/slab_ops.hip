@@ -1,5 +1,5 @@
 // Reduce-scatter, all-gather, replica-local accumulation and the deferred
-// reduce (a8-a11) for gfx950, plus the bf16 rounding self-check and a plain
+// reduce for gfx950, plus the bf16 rounding self-check and a plain
 // streaming copy used as the achievable-bandwidth reference.
 //
 // All are streaming kernels over 16-byte column vectors of [rows, ld] slabs:
@@ -67,7 +67,7 @@ __device__ __forceinline__ u32x4 fold_rows(const u32x4* in, int64_t ldv, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// a8. reduce-scatter: out[s][k] = fold_r pre(in[r][s*L + k])
+// Reduce-scatter: out[s][k] = fold_r pre(in[r][s*L + k])
 // ---------------------------------------------------------------------------
 
 // Vector path (L a multiple of the vector width): blockIdx.y = shard.
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kST) void k_rs_ring_elem(int32_t W, const void* __r
 }
 
 // ---------------------------------------------------------------------------
-// a9. all-gather
+// All-gather
 // ---------------------------------------------------------------------------
 
 // One step of an all-gather schedule on the [W, W*L] buffer, every chunk at
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(kST) void k_ag_elem(int32_t W, const E* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// a10. accumulate: acc = acc + x   (init: acc = +0 + x)
+// Accumulate: acc = acc + x   (init: acc = +0 + x)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kST) void k_accumulate(const float* __restrict__ x,
                                                          int64_t ld_x, float* acc,
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(kST) void k_accumulate(const float* __restrict__ x,
 }
 
 // ---------------------------------------------------------------------------
-// a11. deferred reduce: out[i][j] = fold_r acc[r][j], i < out_rows
+// Deferred reduce: out[i][j] = fold_r acc[r][j], i < out_rows
 // ---------------------------------------------------------------------------
 template <int WT>
 __global__ __launch_bounds__(kST) void k_deferred(int32_t W, const float* acc, int64_t ld_acc,
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(kST) void k_deferred(int32_t W, const float* acc, i
   }
 }
 
-// a10 + a11 fused: a_r = acc_r + x_r (or +0 + x_r), optionally kept, then
+// Accumulate and deferred reduce fused: a_r = acc_r + x_r (or +0 + x_r), optionally kept, then
 // folded in rank order.  W known at compile time loads every row first.
 template <int WT>
 __global__ __launch_bounds__(kST) void k_accum_reduce(int32_t W, const float* x, int64_t ld_x,

@@ -85,7 +85,7 @@ class Zero1FlushExecutor:
         self.d_psize = torch.from_numpy(psize).to(dev)
 
     def build_owner_map(self, stream=None) -> None:
-        """a1 + a2 on the device (no host synchronization)."""
+        """Partition lists and owner map on the device (no host synchronization)."""
         dc.dc_partition_ids(self.W, self.P, self.d_numel, self.G, self.group_begin,
                             self.group_parts, self.d_flat, self.d_part_size, self.d_pid_off,
                             self.d_pids, self.pids_capacity, stream)

@@ -129,7 +129,7 @@ const char* dc_strerror(dc_status status);
 /* Message of the calling thread's last failed call ("" if none). */
 const char* dc_last_error(void);
 
-/* a1. Partition lists ([DS] Design points, the owner map: the ZeRO
+/* Partition lists ([DS] Design points, the owner map: the ZeRO
  * optimizer's param_to_partition_ids lists every optimizer partition holding
  * a piece of a parameter).  For each group g, the params
  * group_begin[g] .. group_begin[g+1]-1 are laid end to end in declaration
@@ -155,7 +155,7 @@ dc_status dc_partition_ids(int32_t W, int32_t num_params, const int64_t* numel,
                            int32_t* pid_offsets, int32_t* pids, int64_t pids_capacity,
                            void* stream);
 
-/* a2. Owner map ([DS] Design points): a param with exactly one partition
+/* Owner map ([DS] Design points): a param with exactly one partition
  * entry has exactly one owner, that entry's rank; a param with two or more
  * entries (it straddles a partition boundary) or none gets -1, meaning
  * AllReduce.  A group takes part only when its communicator is the
@@ -188,7 +188,7 @@ dc_status dc_validate_tasks(int32_t W, const dc_task* tasks, int32_t num_tasks,
                             int64_t bucket_numel, int32_t num_params, const dc_comm* comms,
                             int32_t num_comms);
 
-/* a3-a6. Bucket flush ([DS] problem statement and "Describe the solution").
+/* Bucket flush ([DS] problem statement and "Describe the solution").
  * For every task t, column j of the bucket inside t, and block of the task's
  * communicator (c members m_0 < ... < m_{c-1}):
  *   v_k = pre_div ? round_dtype(fp32(x[m_k][j]) / c) : x[m_k][j]
@@ -289,7 +289,7 @@ dc_status dc_validate_buffer_tasks(int32_t W, int32_t dtype, const dc_task* task
                                    int64_t bucket_numel, const dc_comm* comms, int32_t num_comms,
                                    const void* const* in_ptrs, void* const* out_ptrs);
 
-/* a7. Probe counts of one flush ([DS] "reduce_probe"), on the host from
+/* Probe counts of one flush ([DS] "reduce_probe"), on the host from
  * metadata only (no device access, no synchronization).  tasks, owner (or
  * NULL for the empty map), pid_offsets/pids (the CSR of dc_partition_ids)
  * and comms are host arrays.  Holders of a param on a sub-communicator are,
@@ -346,7 +346,7 @@ dc_status dc_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int64_t 
                               int64_t ld_out, const int64_t* seg_start, int32_t pre_div,
                               void* stream);
 
-/* a8. ReduceScatter ([AG] duality with ReduceScatter: M elements in per node,
+/* ReduceScatter ([AG] duality with ReduceScatter: M elements in per node,
  * M/N out, a reduction plus a split).  With L = M / W:
  *   out[s][k] = round_dtype(fold over r of pre(in[r][s*L + k]))   k < L
  * using the flush's fold and pre-division (by W).
@@ -356,7 +356,7 @@ dc_status dc_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int64_t 
 dc_status dc_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
                             int64_t ld_out, int64_t M, int32_t pre_div, void* stream);
 
-/* a9. AllGather ([AG] semantic definition and Ring AllGather).  Shard s is
+/* AllGather ([AG] semantic definition and Ring AllGather).  Shard s is
  * row s of `in` (L = shard_numel columns).
  *   DC_ORDER_RANK: out[i][s*L + k] = in[s][k] - every node ends with
  *                  [A_0, ..., A_{W-1}].
@@ -402,7 +402,7 @@ dc_status dc_all_gather_step(int32_t W, int32_t dtype, const void* in, int64_t l
                              int64_t ld_out, int64_t shard_numel, int32_t algo, int32_t step,
                              void* stream);
 
-/* a10. Replica-local accumulation ([MT] What: unreduced per-replica partial
+/* Replica-local accumulation ([MT] What: unreduced per-replica partial
  * sums accumulate locally across micro-batches).  fp32 only:
  *   acc[r][j] = acc[r][j] + x[r][j]        r < rows, j < M
  * and with init = 1 the accumulator starts from zero: acc = +0.0f + x.
@@ -411,7 +411,7 @@ dc_status dc_all_gather_step(int32_t W, int32_t dtype, const void* in, int64_t l
 dc_status dc_accumulate(int32_t rows, const float* x, int64_t ld_x, float* acc, int64_t ld_acc,
                         int64_t M, int32_t init, void* stream);
 
-/* a11. Deferred cross-replica reduce ([MT] What: the single all-reduce that
+/* Deferred cross-replica reduce ([MT] What: the single all-reduce that
  * update() emits).  fp32 only:
  *   out[i][j] = fold over r = 0..W-1 of acc[r][j]        i < out_rows, j < M
  * out_rows is 1 (one reduced copy) or W (every replica gets the sum).  With
@@ -422,7 +422,7 @@ dc_status dc_accumulate(int32_t rows, const float* x, int64_t ld_x, float* acc, 
 dc_status dc_deferred_reduce(int32_t W, const float* acc, int64_t ld_acc, float* out,
                              int64_t ld_out, int64_t M, int32_t out_rows, void* stream);
 
-/* a10 + a11 fused for the last micro-batch of a step: the same fp32
+/* Accumulation and the deferred reduce fused for the last micro-batch of a step: the same fp32
  * operations as dc_accumulate followed by dc_deferred_reduce, in one pass
  * (bit-identical results), without writing the accumulator and reading it
  * back ([MT] What: the accumulated partial sums feed the single reduce in

@@ -130,7 +130,7 @@ def bf16_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-# -- a1 / a2 ---------------------------------------------------------------
+# -- partition lists and owner map -----------------------------------------
 
 def partition_ids(numel, group_begin, group_parts):
     numel = _c(numel, np.int64)
@@ -172,7 +172,7 @@ def owner_map(pid_offsets, pids, group_begin, eligible):
     return owner, counts
 
 
-# -- a3..a7 ----------------------------------------------------------------
+# -- bucket flushes and the probe ------------------------------------------
 
 def flush(W, dtype, slab_in, slab_out, bucket_col, t_off, t_numel, t_param, t_comm, owner,
           comm_size, comm_stride, pre_div):
@@ -289,7 +289,7 @@ def ratio_line(owners, P):
     return f"DeepCompile reduce_to_owner: {owners}/{P} gradients reduce to one rank"
 
 
-# -- a8 / a9 ---------------------------------------------------------------
+# -- reduce-scatter and all-gather -----------------------------------------
 
 def reduce_scatter(W, dtype, slab_in, out, M, pre_div):
     slab_in, out = _slab(slab_in, dtype), _slab(out, dtype)
@@ -346,7 +346,7 @@ def all_gather(W, dtype, shards, out, L, order, step=-1):
     return out
 
 
-# -- a10 / a11 -------------------------------------------------------------
+# -- accumulation and the deferred reduce ----------------------------------
 
 def accumulate(rows, x, acc, M, init):
     x, acc = _slab(x, F32), _slab(acc, F32)

@@ -96,7 +96,7 @@ static float contribution(int dtype, float x, int pre_div, int c) {
 static int member(int b, int i, int c, int s) { return (s == 1 ? b * c : b) + i * s; }
 
 /* ------------------------------------------------------------------------ */
-/* a1. Partition ids ([DS] Design points, owner map: param_to_partition_ids   */
+/* Partition ids ([DS] Design points, owner map: param_to_partition_ids   */
 /* lists every optimizer partition holding a piece of each parameter).       */
 /* ------------------------------------------------------------------------ */
 
@@ -146,7 +146,7 @@ void or_group_eligible(int32_t W, int32_t G, const int32_t* comm_size,
   }
 }
 
-/* a2. Owner map ([DS] Design points): exactly one partition entry means
+/* Owner map ([DS] Design points): exactly one partition entry means
  * exactly one owner, and that entry is the owner's rank; two or more entries
  * (a straddler) or none, or an excluded group, mean no owner (-1), which the
  * flush treats as AllReduce.  counts[2g] = owners, counts[2g+1] = straddlers
@@ -168,7 +168,7 @@ void or_owner_map(int32_t P, const int32_t* pid_offsets, const int32_t* pids, in
 }
 
 /* ------------------------------------------------------------------------ */
-/* a3-a6. Bucket flush ([DS] problem statement and "Describe the solution"). */
+/* Bucket flush ([DS] problem statement and "Describe the solution").       */
 /* ------------------------------------------------------------------------ */
 
 /* For every task t and every column j of it, for every block of the task's
@@ -343,7 +343,7 @@ void or_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int64_t ld_in
   }
 }
 
-/* a7. Probe ([DS] problem statement probe line; "reduce_probe").  Host-only
+/* Probe ([DS] problem statement probe line; "reduce_probe").  Host-only
  * bookkeeping from metadata.  Holders of a parameter: the ranks whose
  * partition appears in its partition list (for a sub-communicator group,
  * in every block the member whose in-block index appears).  Written rows:
@@ -388,7 +388,7 @@ void or_probe(int32_t W, int32_t n_tasks, const int64_t* t_numel, const int32_t*
 }
 
 /* ------------------------------------------------------------------------ */
-/* a8. ReduceScatter ([AG] duality with ReduceScatter: M in, M/N out, a       */
+/* ReduceScatter ([AG] duality with ReduceScatter: M in, M/N out, a       */
 /* reduction plus a split).  Shard s is columns [s*L, (s+1)*L), L = M/W.     */
 /* ------------------------------------------------------------------------ */
 void or_reduce_scatter(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
@@ -448,7 +448,7 @@ void or_reduce_scatter_ring(int32_t W, int32_t dtype, const void* in, int64_t ld
 }
 
 /* ------------------------------------------------------------------------ */
-/* a9. AllGather ([AG] semantic definition; Ring AllGather steps).           */
+/* AllGather ([AG] semantic definition; Ring AllGather steps).               */
 /* ------------------------------------------------------------------------ */
 
 /* Ring schedule, simulated as the page describes it: node i starts with its
@@ -649,7 +649,7 @@ int32_t or_all_gather(int32_t W, int32_t dtype, const void* in, int64_t ld_in, v
 }
 
 /* ------------------------------------------------------------------------ */
-/* a10-a11. Deferred reduction ([MT] What): replica-local accumulation of    */
+/* Deferred reduction ([MT] What): replica-local accumulation of    */
 /* the unreduced per-micro-batch gradients, then one cross-replica sum.      */
 /* ------------------------------------------------------------------------ */
 
