@@ -231,3 +231,59 @@ def test_flush_buffers_mixed_w16_full_size():
         pytest.skip(f"needs {need / 1e9:.0f} GB of device memory, {free / 1e9:.0f} GB free")
     ex, d_out, ld, poff, pcol, hold = _full_size(w)
     _check_sampled(w, d_out, ld, poff, pcol, hold)
+
+
+def test_flush_buffers_split_params_via_executor():
+    """Params split over buckets through the executor: each task's slice
+    continues where the param's previous task ended, in the input buffers and
+    in the holders' grad buffers; the whole output arena matches the oracle
+    (sentinel wherever no holder keeps a buffer)."""
+    import torch
+    W, dtype, pre = 4, wl.DT_BF16, 1
+    numel = [100, 5000, 37, 777, 4096]
+    buckets = [executor.BucketSpec(0, 3100, [(0, 100, 0, 0), (100, 3000, 1, 0)]),
+               executor.BucketSpec(3100, 2814, [(0, 2000, 1, 0), (2000, 37, 2, 0), (2037, 777, 3, 0)]),
+               executor.BucketSpec(5914, 1000, [(0, 1000, 4, 0)]),
+               executor.BucketSpec(6914, 3096, [(0, 3096, 4, 0)])]
+    ex = executor.Zero1FlushExecutor(W, dtype, numel, [0, 5], [W], [W], [list(range(W))], [(W, 1)],
+                                     buckets, pre, reduce_to_owner=True)
+    ex.build_owner_map()
+    ex.fetch_metadata()
+    eb = 2
+    pad = 64
+    poff, pos = [], 0
+    for n in numel:
+        poff.append(pos)
+        pos = wl.round_up(pos + n, pad)
+    ld = wl.round_up(pos, 64)
+    scale = wl.sigma_scale(1e-2)
+    x = U.gen_slab(dtype, W, ld, ld, 71, 0, scale)
+    hx = U.host_slab(dtype, W, ld, ld, 71, 0, scale)
+    y = U.empty_slab(dtype, W, ld)
+    hold = np.zeros((W, len(numel)), bool)
+    for b, bk in enumerate(buckets):
+        h = ex.holders(b)
+        for k, t in enumerate(bk.tasks):
+            hold[:, t[2]] |= h[k]
+    rows = np.arange(W, dtype=np.int64)[:, None] * ld
+    po = np.array(poff, np.int64)[None, :]
+    in_addr = (x.data_ptr() + (rows + po) * eb).astype(np.uint64)
+    out_addr = np.where(hold, y.data_ptr() + (rows + po) * eb, 0).astype(np.uint64)
+    ex.register_buffers(in_addr, out_addr)
+    for b in range(len(buckets)):
+        ex.flush_buffers(b)
+    torch.cuda.synchronize()
+    # the oracle on the same offsets
+    seen = [0] * len(numel)
+    in_off, out_off, t_numel = [], [], []
+    for bk in buckets:
+        for (_, n, p, _) in bk.tasks:
+            in_off.append([r * ld + poff[p] + seen[p] for r in range(W)])
+            out_off.append([r * ld + poff[p] + seen[p] if hold[r, p] else -1 for r in range(W)])
+            t_numel.append(n)
+            seen[p] += n
+    hin = np.ascontiguousarray(hx).ravel()
+    hout = np.full(W * ld, U.SENTINEL16, np.uint16)
+    oracle.flush_buffers(W, dtype, hin, np.array(in_off), hout, np.array(out_off), t_numel,
+                         [0] * len(t_numel), [W], [1], pre)
+    assert np.array_equal(U.to_host(y, dtype).ravel(), hout)
