@@ -432,6 +432,45 @@ def bench_deferred(args):
                 "launch_ms_avg": round(float(kern[-1]), 4),
                 "bytes_per_launch_avg": red_b}
     extra = {"accumulate_gbs": round(acc_gbs, 1)}
+
+    # The pages' status quo beside it: every micro-batch reduced across the
+    # replicas, the reduced gradients accumulated (one row).  Timed on its own.
+    g = torch.empty((1, ld), dtype=torch.float32, device=dev)
+    A = torch.empty((1, ld), dtype=torch.float32, device=dev)
+
+    def quo():
+        for k in range(args.ga):
+            dc.dc_deferred_reduce(W, xs[k], ld, g, ld, M, 1)
+            dc.dc_accumulate(1, g, ld, A, ld, M, 1 if k == 0 else 0)
+
+    quo()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        quo()
+    e1.record()
+    torch.cuda.synchronize()
+    extra["status_quo_ms_per_step"] = round(e0.elapsed_time(e1) / args.steps, 4)
+    # numerics of the deferred sum D against the per-micro-batch sum A: the
+    # 5e-5 * sum|x| gate, the normwise difference and the largest relative
+    # difference where |A| > 1e-3 max|A|
+    step()
+    torch.cuda.synchronize()
+    d, a = out[0, :M].double(), A[0, :M].double()
+    diff = (d - a).abs()
+    sabs = torch.zeros(M, dtype=torch.float64, device=dev)
+    for k in range(args.ga):
+        sabs += xs[k, :, :M].abs().sum(dim=0).double()
+    big = a.abs() > 1e-3 * a.abs().max()
+    extra["deferred_vs_per_microbatch"] = {
+        "max_diff_over_gate": float((diff / (5e-5 * sabs).clamp_min(1e-300)).max()),
+        "normwise": float(diff.norm() / a.norm()),
+        "max_rel_where_abs_gt_1e-3_max": float((diff[big] / a.abs()[big]).max()),
+        "bit_identical_frac": round(float((diff == 0).double().mean()), 6)}
+    log(f"[bench] status quo (reduce every micro-batch, then accumulate): "
+        f"{extra['status_quo_ms_per_step']:.3f} ms; D vs A: {extra['deferred_vs_per_microbatch']}")
+    del d, a, diff, sabs, big
     return w.name, ms_step, step_bytes / (ms_step / 1e3) / 1e9, roofline, extra, "f32"
 
 
@@ -615,6 +654,34 @@ def copy_calibration():
     return round(2 * n / (ms / 1e3) / 1e9, 1)
 
 
+def system_info():
+    """Host and GPU state next to the figures: CPU model, cores, memory, and
+    rocm-smi's clocks and power (when the tool answers)."""
+    import subprocess
+    info = {"cpu_threads": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            lines = f.read().splitlines()
+        names = [ln.split(":", 1)[1].strip() for ln in lines if ln.startswith("model name")]
+        phys = {ln.split(":", 1)[1].strip() for ln in lines if ln.startswith("physical id")}
+        info["cpu_model"] = names[0] if names else None
+        info["sockets"] = len(phys) or None
+        with open("/proc/meminfo") as f:
+            info["mem_total_gb"] = round(int(f.readline().split()[1]) / 2 ** 20, 1)
+    except OSError:
+        pass
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        if r.returncode == 0 and r.stdout.strip().startswith("{"):
+            card = next(iter(json.loads(r.stdout).values()))
+            info["gpu"] = {k: v for k, v in card.items()
+                           if any(t in k.lower() for t in ("sclk", "mclk", "fclk", "power"))}
+    except (OSError, subprocess.SubprocessError, ValueError, StopIteration, AttributeError):
+        pass
+    return info
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -690,7 +757,8 @@ def main():
             "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": dtype,
             "data": "synthetic (seeded SplitMix64 Irwin-Hall gradients, random-init shapes)",
-            "config": config, "roofline": roof, "cpu_baseline": cpu, "detail": extra}
+            "config": config, "roofline": roof, "cpu_baseline": cpu, "detail": extra,
+            "system": system_info()}
     print(json.dumps(line), flush=True)
 
 
