@@ -75,8 +75,11 @@ typedef int32_t dc_status;
  *   numel    columns of the task (>= 0)
  *   param    index into the owner map
  *   comm     index into the flush's communicator table
- * A bucket's table is sorted and packed: offset[0] = 0,
- * offset[t+1] = offset[t] + numel[t], and the numels sum to the bucket size. */
+ * For the slab flushes a bucket's table is sorted and packed: offset[0] = 0,
+ * offset[t+1] = offset[t] + numel[t], and the numels sum to the bucket size.
+ * dc_flush_bucket_buffers takes sorted, disjoint tasks with gaps allowed (its
+ * offsets are coordinates only) and does not read `param`.  `reserved` is
+ * not read by any entry point. */
 typedef struct {
   int64_t offset;
   int64_t numel;
