@@ -417,3 +417,59 @@ def test_all_gather_schedules_7b_layer_full_size():
         torch.cuda.synchronize()
         assert torch.equal(out[:, :M], want[:, :M]), algo
         del out
+
+
+def test_accumulator_lifetime_restore_and_round_trip():
+    """MaxText PR, accumulator lifetime, on the GPU kernels: a reduced total
+    restored onto replica 0 (zeros elsewhere) reduces back to itself; a
+    mid-step save / restore / continue sequence matches the oracle's same
+    sequence bit for bit and stays within the 5e-5 * sum|x| gate of the
+    uninterrupted step."""
+    import torch
+    W, K, M = 4, 8, 5001
+    ld = wl.round_up(M, 64)
+    scale = wl.sigma_scale(1e-3)
+    xs = [U.gen_slab(wl.DT_F32, W, ld, M, 81, wl.microbatch_stream(k, W, 0), scale).view(torch.float32)
+          for k in range(K)]
+    hxs = [U.host_slab(wl.DT_F32, W, ld, M, 81, wl.microbatch_stream(k, W, 0), scale) for k in range(K)]
+
+    def gpu_deferred(chunks, acc=None):
+        acc = torch.zeros((W, ld), dtype=torch.float32, device="cuda") if acc is None else acc
+        for x in chunks:
+            dc.dc_accumulate(W, x, ld, acc, ld, M, 0)
+        D = torch.empty((1, ld), dtype=torch.float32, device="cuda")
+        dc.dc_deferred_reduce(W, acc, ld, D, ld, M, 1)
+        return D, acc
+
+    def host_deferred(chunks, acc=None):
+        acc = np.zeros((W, ld), np.float32) if acc is None else acc
+        for x in chunks:
+            oracle.accumulate(W, x, acc, M, 0)
+        D = np.zeros((1, ld), np.float32)
+        oracle.deferred_reduce(W, acc, D, M, 1)
+        return D, acc
+
+    D_full, _ = gpu_deferred(xs)
+    D_save, _ = gpu_deferred(xs[:3])
+    acc = torch.zeros((W, ld), dtype=torch.float32, device="cuda")
+    acc[0, :M] = D_save[0, :M]
+    D_rt, _ = gpu_deferred(xs[3:], acc)
+    # restore alone: the saved total reduces back to itself
+    acc2 = torch.zeros((W, ld), dtype=torch.float32, device="cuda")
+    acc2[0, :M] = D_save[0, :M]
+    D_back = torch.empty((1, ld), dtype=torch.float32, device="cuda")
+    dc.dc_deferred_reduce(W, acc2, ld, D_back, ld, M, 1)
+    torch.cuda.synchronize()
+    h_full, _ = host_deferred(hxs)
+    h_save, _ = host_deferred(hxs[:3])
+    hacc = np.zeros((W, ld), np.float32)
+    hacc[0, :M] = h_save[0, :M]
+    h_rt, _ = host_deferred(hxs[3:], hacc)
+    assert np.array_equal(D_full[0, :M].cpu().numpy().view(np.uint32), h_full[0, :M].view(np.uint32))
+    assert np.array_equal(D_rt[0, :M].cpu().numpy().view(np.uint32), h_rt[0, :M].view(np.uint32))
+    saved = D_save[0, :M].cpu().numpy()
+    want_back = np.where(saved == 0, np.float32(0.0), saved)
+    assert np.array_equal(D_back[0, :M].cpu().numpy().view(np.uint32), want_back.view(np.uint32))
+    S = sum(np.abs(x[:, :M].astype(np.float64)).sum(axis=0) for x in hxs)
+    err = np.abs(D_rt[0, :M].cpu().numpy().astype(np.float64) - D_full[0, :M].cpu().numpy())
+    assert np.all(err <= 5e-5 * S)
