@@ -31,7 +31,7 @@ struct RelayoutParams {
   int64_t bucket_numel;
 };
 
-// One workgroup per tile of 256*U destination vectors (16 bytes of every
+// One workgroup per tile of kRT*U destination vectors (16 bytes of every
 // row).  A vector inside one piece whose source is vector aligned moves as W
 // 16-byte loads and stores; any other vector moves element by element.
 // Source columns are checked against the bucket, so a bad plan never reads
