@@ -726,7 +726,11 @@ def main():
                   "pre_div": w.pre_div, "step": "owner map + every bucket flush",
                   "step_bytes": step_bytes}
         if not args.no_cpu_baseline and not zero2:
-            cpu = cpu_baseline_flush(w, owner_mode, max_buckets=2 if w.total > 1e8 else 1)
+            # the whole step when its slab fits a few GB of host memory (about 20 s
+            # of single-threaded oracle work for the W=8 402.8M workload), else
+            # the first two buckets
+            whole = w.W * w.total * w.elem_bytes() < 8e9
+            cpu = cpu_baseline_flush(w, owner_mode, max_buckets=len(w.buckets) if whole else 2)
     elif args.workload in ("fused_w8", "fused_mixed"):
         w = wl.owner_flush_w8() if args.workload == "fused_w8" else wl.mixed_flush_w16()
         ms, value, step_bytes, roof, extra = bench_flush_buffers(args, w)
