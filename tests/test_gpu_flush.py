@@ -33,6 +33,17 @@ def test_generator_device_matches_host():
         d = U.to_host(U.gen_slab(dtype, 3, wl.round_up(n, 64), n, 9, 5, scale), dtype)
         h = U.host_slab(dtype, 3, wl.round_up(n, 64), n, 9, 5, scale)
         assert np.array_equal(U.bits(d, dtype), U.bits(h, dtype))
+    # a column origin: position j of row r holds column col0 + j
+    import torch
+    for dtype in (wl.DT_BF16, wl.DT_F32):
+        col0, n, ld = 123_457, 5_003, 5_056
+        x = U.empty_slab(dtype, 2, ld)
+        synth.fill_slab_device(dtype, 9, 7, wl.sigma_scale(1e-2), 2, ld, n, x.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream, col0=col0)
+        got = U.bits(U.to_host(x, dtype), dtype)
+        for r in range(2):
+            want = synth.fill_row(dtype, 9, 7 + r, wl.sigma_scale(1e-2), col0, n)
+            assert np.array_equal(got[r, :n], want.view(got.dtype)), (dtype, r)
 
 
 def test_round_bf16_matches_oracle():
