@@ -345,9 +345,40 @@ def traffic_from_profile(w, per_launch):
     return rec.get("hbm_bytes_per_launch_avg")
 
 
+def host_threads():
+    """Threads for the all-cores oracle run: the CPUs this process may run on,
+    at most 16 (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def column_blocks(bk, nthreads, block=1 << 18):
+    """Split a bucket's tasks into column blocks of the same param and comm,
+    dealt to nthreads lists round-robin (a static schedule).  Every column of
+    the oracle's flush is folded on its own, so the split changes no output."""
+    lists = [([], [], [], []) for _ in range(nthreads)]
+    k = 0
+    for t in bk.tasks:
+        for o in range(0, t.numel, block):
+            dst = lists[k % nthreads]
+            dst[0].append(t.offset + o)
+            dst[1].append(min(block, t.numel - o))
+            dst[2].append(t.param)
+            dst[3].append(t.comm)
+            k += 1
+    return [x for x in lists if x[0]]
+
+
 def cpu_baseline_flush(w, reduce_to_owner=True, max_buckets=2):
-    """The oracle, single-threaded, on the first buckets of the same workload
-    (host inputs from the same generator; generation untimed)."""
+    """The oracle on the first buckets of the same workload (host inputs from
+    the same generator; generation untimed), timed twice: on one thread (the
+    reported baseline), and on all of the host's threads with each bucket's
+    columns split into blocks (the oracle's C calls release the GIL).  The two
+    outputs must be identical."""
+    import concurrent.futures
     import oracle
     import synth
     flat, ps, off, pids = oracle.partition_ids(w.numel, w.group_begin, w.group_parts())
@@ -356,32 +387,52 @@ def cpu_baseline_flush(w, reduce_to_owner=True, max_buckets=2):
     owner, _ = oracle.owner_map(off, pids, w.group_begin, elig)
     own = owner if reduce_to_owner else None
     per = flush_bytes(w, own)
-    secs = 0.0
-    nbytes = 0
-    used = []
-    for b, bk in enumerate(w.buckets[:max_buckets]):
-        n = bk.numel
-        ld = -(-n // 8) * 8
-        rows = np.zeros((w.W, ld), synth.np_dtype(w.dtype))
-        for r in range(w.W):
-            rows[r, :n] = synth.fill_row(w.dtype, w.value_seed, r, w.scale, bk.col, n)
-        if w.dtype == 1:
-            rows = rows.view(np.float32)
-        out = np.zeros_like(rows)
-        t = time.perf_counter()
-        oracle.flush(w.W, w.dtype, rows, out, 0, [t_.offset for t_ in bk.tasks],
-                     [t_.numel for t_ in bk.tasks], [t_.param for t_ in bk.tasks],
-                     [t_.comm for t_ in bk.tasks], own, [c.size for c in w.comms],
-                     [c.stride for c in w.comms], w.pre_div)
-        secs += time.perf_counter() - t
-        nbytes += per[b]
-        used.append(b)
-        del rows, out
-    log(f"[bench] cpu oracle: {nbytes / 1e9:.2f} GB in {secs:.2f} s")
-    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"buckets {used} of {len(w.buckets)} ({sum(w.buckets[b].numel for b in used)} "
-                      f"columns, {sum(len(w.buckets[b].tasks) for b in used)} tasks), oracle.c "
-                      f"single thread, {nbytes} algorithmic bytes, {secs:.2f} s"}
+    csize = [c.size for c in w.comms]
+    cstride = [c.stride for c in w.comms]
+    nthreads = host_threads()
+    used = list(range(min(max_buckets, len(w.buckets))))
+    nbytes = sum(per[b] for b in used)
+
+    def run(rows, out, tasks):
+        oracle.flush(w.W, w.dtype, rows, out, 0, tasks[0], tasks[1], tasks[2], tasks[3], own,
+                     csize, cstride, w.pre_div)
+
+    secs = psecs = 0.0
+    same = True
+    with concurrent.futures.ThreadPoolExecutor(nthreads) as pool:
+        for b in used:
+            bk = w.buckets[b]
+            n = bk.numel
+            ld = -(-n // 8) * 8
+            rows = np.zeros((w.W, ld), synth.np_dtype(w.dtype))
+            for r in range(w.W):
+                rows[r, :n] = synth.fill_row(w.dtype, w.value_seed, r, w.scale, bk.col, n)
+            if w.dtype == 1:
+                rows = rows.view(np.float32)
+            whole = ([t_.offset for t_ in bk.tasks], [t_.numel for t_ in bk.tasks],
+                     [t_.param for t_ in bk.tasks], [t_.comm for t_ in bk.tasks])
+            out1 = np.zeros_like(rows)
+            t = time.perf_counter()
+            run(rows, out1, whole)
+            secs += time.perf_counter() - t
+            outn = np.zeros_like(rows)
+            parts = column_blocks(bk, nthreads)
+            t = time.perf_counter()
+            list(pool.map(lambda tl: run(rows, outn, tl), parts))
+            psecs += time.perf_counter() - t
+            same = same and np.array_equal(out1.view(np.uint8), outn.view(np.uint8))
+            del rows, out1, outn
+    log(f"[bench] cpu oracle: {nbytes / 1e9:.2f} GB in {secs:.2f} s on 1 thread, {psecs:.2f} s "
+        f"on {nthreads} threads (outputs identical: {same})")
+    sample = (f"buckets {used} of {len(w.buckets)} ({sum(w.buckets[b].numel for b in used)} columns, "
+              f"{sum(len(w.buckets[b].tasks) for b in used)} tasks), oracle.c single thread, "
+              f"{nbytes} algorithmic bytes, {secs:.2f} s")
+    base = {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": sample}
+    allc = {"value": round(nbytes / psecs / 1e9, 4), "unit": "GB/s", "threads": nthreads,
+            "host_cpus": os.cpu_count(), "seconds": round(psecs, 3),
+            "outputs_identical_to_one_thread": bool(same)}
+    return base, allc
 
 
 def bench_deferred(args):
@@ -730,7 +781,9 @@ def main():
             # of single-threaded oracle work for the W=8 402.8M workload), else
             # the first two buckets
             whole = w.W * w.total * w.elem_bytes() < 8e9
-            cpu = cpu_baseline_flush(w, owner_mode, max_buckets=len(w.buckets) if whole else 2)
+            cpu, cpu_par = cpu_baseline_flush(w, owner_mode,
+                                              max_buckets=len(w.buckets) if whole else 2)
+            extra["cpu_oracle_all_threads"] = cpu_par
     elif args.workload in ("fused_w8", "fused_mixed"):
         w = wl.owner_flush_w8() if args.workload == "fused_w8" else wl.mixed_flush_w16()
         ms, value, step_bytes, roof, extra = bench_flush_buffers(args, w)
