@@ -195,6 +195,60 @@ def test_all_gather_step_schedules(W, dtype, L, algo):
     assert torch.equal(out[:, :W * L], rank[:, :W * L])
 
 
+RING_AR_CASES = [(8, wl.DT_BF16, 1000, 0), (8, wl.DT_BF16, 1000, 1), (4, wl.DT_F32, 333, 0),
+                 (5, wl.DT_BF16, 77, 1), (16, wl.DT_F32, 2048, 0), (2, wl.DT_BF16, 9, 0),
+                 (1, wl.DT_F32, 64, 1), (64, wl.DT_BF16, 100, 0)]
+
+
+@pytest.mark.parametrize("W,dtype,L,pre", RING_AR_CASES, ids=lambda v: str(v))
+def test_ring_allreduce_composition(W, dtype, L, pre):
+    """A ring AllReduce on one GPU: the ring-order reduce-scatter followed by
+    every step of the ring all-gather schedule.  Bit-exact against the
+    oracle's ring reduce-scatter and step executor; every row of the result
+    holds the same vector; against the rank-order AllReduce of the flush it
+    differs only within the error bound of two fp32 summation orders (plus
+    one bf16 rounding of each side)."""
+    import torch
+    U.say("ring allreduce", W, dtype, L, pre)
+    M = W * L
+    ld = max(64, wl.round_up(M, 64))
+    ld_sh = max(64, wl.round_up(L, 64))
+    scale = wl.sigma_scale(1e-2)
+    x = U.gen_slab(dtype, W, ld, M, 21, 0, scale)
+    hx = U.host_slab(dtype, W, ld, M, 21, 0, scale)
+    sh = U.empty_slab(dtype, W, ld_sh)
+    out = U.empty_slab(dtype, W, ld)
+    dc.dc_reduce_scatter_ring(W, dtype, x, ld, sh, ld_sh, M, pre)
+    for s in range(W):
+        dc.dc_all_gather_step(W, dtype, sh, ld_sh, out, ld, L, dc.DC_SCHED_RING, s)
+    ar = U.empty_slab(dtype, W, ld)
+    if M:
+        tasks = dc.tasks_array([(0, M, 0, 0)])
+        d_tasks = torch.from_numpy(tasks.view(np.uint8).copy()).cuda()
+        dc.dc_flush_bucket(W, dtype, x, ld, ar, ld, 0, M, d_tasks, 1, None, 1, [(W, 1)], 1, pre)
+    torch.cuda.synchronize()
+
+    hsh = np.zeros((W, ld_sh), hx.dtype)
+    oracle.reduce_scatter_ring(W, dtype, hx, hsh, M, pre)
+    ho = np.zeros((W, ld), hx.dtype)
+    U.bits(ho, dtype)[:] = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
+    for s in range(W):
+        oracle.all_gather_step(W, dtype, hsh, ho, L, oracle.AG_RING, s)
+    got = U.to_host(out, dtype)
+    assert np.array_equal(U.bits(got, dtype)[:, :M], U.bits(ho, dtype)[:, :M])
+    for i in range(1, W):
+        assert np.array_equal(U.bits(got, dtype)[i, :M], U.bits(got, dtype)[0, :M]), i
+    if M and not pre:
+        a = _as_f64(got[0, :M], dtype)
+        b = _as_f64(U.to_host(ar, dtype)[0, :M], dtype)
+        mag = np.sum(np.abs(_as_f64(hx[:, :M], dtype)), axis=0)
+        tol = 2.0 * (W - 1) * 2.0 ** -24 * mag * 1.01
+        if dtype == wl.DT_BF16:
+            tol = tol + 2.0 ** -8 * (np.abs(a) + np.abs(b)) * 1.01
+        assert np.all(np.abs(a - b) <= tol)
+        U.say("  ring vs rank order: elements that differ", int(np.count_nonzero(a != b)), "of", M)
+
+
 def test_reduce_scatter_all_gather_7b_layer_full_size():
     """The 7B-layer workload at full size (M = 202,383,360, W = 8): shards on
     sampled columns against the oracle, then AllReduce = ReduceScatter +
