@@ -154,9 +154,10 @@ def bench_flush(args, w, reduce_to_owner=True, zero2=False):
     ceiling = access_mix_ceiling(w, owner, x, y, ld, ex.h_psize if zero2 else None)
     roofline = {"bound": "hbm", "achieved": round(flush_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(flush_gbs / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profile(w, per_launch),
+                "traffic": traffic_from_profile(args.workload, w.name),
                 "kernel": "k_flush", "launch_ms_avg": round(avg_launch_ms, 4),
-                "bytes_per_launch_avg": int(np.mean(per_launch))}
+                "bytes_per_launch_avg": int(np.mean(per_launch)),
+                "bytes_per_launch": [int(b) for b in per_launch]}
     if ceiling is not None:
         roofline["access_mix_ceiling_gbs"] = round(ceiling, 1)
         roofline["frac_of_access_mix_ceiling"] = round(flush_gbs / ceiling, 4)
@@ -313,9 +314,11 @@ def bench_flush_buffers(args, w):
         f"{np.round(kern.mean(axis=0), 4).tolist()}")
     ceiling = access_mix_ceiling(w, None, x, y, ld, split=(one_b, many_b))
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile(args.workload, w.name),
                 "kernel": "k_flush_buffers", "launch_ms_avg": round(float(kern.mean()), 4),
-                "bytes_per_launch_avg": int(np.mean(per_launch))}
+                "bytes_per_launch_avg": int(np.mean(per_launch)),
+                "bytes_per_launch": [int(b) for b in per_launch]}
     if ceiling is not None:
         roofline["access_mix_ceiling_gbs"] = round(ceiling, 1)
         roofline["frac_of_access_mix_ceiling"] = round(gbs / ceiling, 4)
@@ -329,18 +332,49 @@ def bench_flush_buffers(args, w):
     return ms_step, value, step_bytes, roofline, extra
 
 
-def traffic_from_profile(w, per_launch):
-    """Measured HBM bytes per flush launch from the committed counter summary,
-    if it was taken on the current flush source; else None."""
-    path = os.path.join(ROOT, "profiles", "flush_w8_402m_traffic.json")
+# Counter summaries behind `traffic`: bench workload -> (profile stem, source
+# file of its dominant kernel).  A summary counts only while the kernel's
+# source and the shared device header still hash to what they were when the
+# counters were taken.
+TRAFFIC_PROFILES = {
+    "owner_w8": ("flush_w8_402m", "flush.hip"),
+    "allreduce_w8": ("flush_allreduce_w8_402m", "flush.hip"),
+    "zero2_w8": ("flush_zero2_w8_402m", "flush.hip"),
+    "mixed": ("flush_w16_1200m", "flush.hip"),
+    "zero2_mixed": ("flush_zero2_w16_1200m", "flush.hip"),
+    "fused_w8": ("flush_buffers_w8_402m", "flush_buffers.hip"),
+    "fused_mixed": ("flush_buffers_w16_1200m", "flush_buffers.hip"),
+    "relayout_rs_w8": ("relayout_rs_w8_402m", "slab_ops.hip"),
+    "deferred": ("deferred_qwen3_k8", "slab_ops.hip"),
+    "deferred_fused": ("deferred_qwen3_k8_fused", "slab_ops.hip"),
+    "rs_ag": ("rs_ag_w8_202m", "slab_ops.hip"),
+    "schedules_w8": ("schedules_w8_202m", "slab_ops.hip"),
+}
+
+
+def kernel_source_sha256(source):
+    import hashlib
+    h = hashlib.sha256()
+    for name in (source, "device_common.h"):
+        with open(os.path.join(ROOT, "gradient_reduction_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from_profile(key, workload, config=None):
+    """Measured HBM bytes per launch of the dominant kernel from the committed
+    counter summary of bench workload `key`, if it was taken on the current
+    kernel source, for the same workload (and config); else None."""
+    if key not in TRAFFIC_PROFILES:
+        return None
+    stem, source = TRAFFIC_PROFILES[key]
+    path = os.path.join(ROOT, "profiles", stem + "_traffic.json")
     if not os.path.exists(path):
         return None
-    import hashlib
-    src = open(os.path.join(ROOT, "gradient_reduction_amd", "csrc", "flush.hip"), "rb").read()
     rec = json.load(open(path))
-    if rec.get("flush_source_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("source_sha256") != kernel_source_sha256(source):
         return None
-    if rec.get("workload") != w.name:
+    if rec.get("workload") != workload or rec.get("config", {}) != (config or {}):
         return None
     return rec.get("hbm_bytes_per_launch_avg")
 
@@ -478,10 +512,12 @@ def bench_deferred(args):
     log(f"[bench] deferred K={args.ga}: step {ms_step:.3f} ms; accumulate {acc_gbs:.1f} GB/s; "
         f"reduce {red_gbs:.1f} GB/s ({kern[-1]:.3f} ms)")
     roofline = {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(red_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(red_gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile("deferred_fused" if fused else "deferred", w.name,
+                                                {"ga": args.ga}),
                 "kernel": "k_accum_reduce" if fused else "k_deferred",
                 "launch_ms_avg": round(float(kern[-1]), 4),
-                "bytes_per_launch_avg": red_b}
+                "bytes_per_launch_avg": red_b, "bytes_per_launch": [red_b]}
     extra = {"accumulate_gbs": round(acc_gbs, 1)}
 
     # The pages' status quo beside it: every micro-batch reduced across the
@@ -556,8 +592,10 @@ def bench_rs_ag(args):
     gbs = [rs_b / (kern[0] / 1e3) / 1e9, ag_b / (kern[1] / 1e3) / 1e9, ag_b / (kern[2] / 1e3) / 1e9]
     log(f"[bench] rs {gbs[0]:.1f} GB/s, ag rank {gbs[1]:.1f} GB/s, ag ring {gbs[2]:.1f} GB/s")
     roofline = {"bound": "hbm", "achieved": round(gbs[0], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs[0] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_rs_vec",
-                "launch_ms_avg": round(float(kern[0]), 4), "bytes_per_launch_avg": rs_b}
+                "frac": round(gbs[0] / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile("rs_ag", w.name), "kernel": "k_rs_vec",
+                "launch_ms_avg": round(float(kern[0]), 4), "bytes_per_launch_avg": rs_b,
+                "bytes_per_launch": [rs_b]}
     extra = {"all_gather_rank_gbs": round(gbs[1], 1), "all_gather_ring_gbs": round(gbs[2], 1)}
     return w.name, ms_step, (rs_b + 2 * ag_b) / (ms_step / 1e3) / 1e9, roofline, extra, "bf16"
 
@@ -607,9 +645,10 @@ def bench_schedules(args):
     gbs = {n: b / (t / 1e3) / 1e9 for n, b, t in zip(names, byts, kern)}
     log("[bench] " + ", ".join(f"{n} {kern[i]:.3f} ms {gbs[n]:.1f} GB/s" for i, n in enumerate(names)))
     roofline = {"bound": "hbm", "achieved": round(gbs["rs_ring"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(gbs["rs_ring"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(gbs["rs_ring"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile("schedules_w8", w.name),
                 "kernel": "k_rs_ring", "launch_ms_avg": round(float(kern[1]), 4),
-                "bytes_per_launch_avg": rs_b}
+                "bytes_per_launch_avg": rs_b, "bytes_per_launch": [rs_b]}
     extra = {n: {"ms": round(float(kern[i]), 4), "gbs": round(gbs[n], 1)} for i, n in enumerate(names)}
     extra["ag_launches"] = {n: S + 1 for n, _, S in scheds}
     # rank-order against ring-order shards: both are correct sums, in
@@ -678,9 +717,11 @@ def bench_relayout_rs(args):
     log(f"[bench] relayout + reduce-scatter-v: step {ms_step:.3f} ms; relayout {rl_gbs:.1f} GB/s "
         f"({kern[0::2].sum():.3f} ms); reduce-scatter-v {rs_gbs:.1f} GB/s ({kern[1::2].sum():.3f} ms)")
     roofline = {"bound": "hbm", "achieved": round(rs_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(rs_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_rs_v",
+                "frac": round(rs_gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile("relayout_rs_w8", w.name), "kernel": "k_rs_v",
                 "launch_ms_avg": round(float(kern[1::2].mean()), 4),
-                "bytes_per_launch_avg": int(np.mean(rs_b))}
+                "bytes_per_launch_avg": int(np.mean(rs_b)),
+                "bytes_per_launch": [int(b) for b in rs_b]}
     extra = {"relayout_gbs": round(rl_gbs, 1), "relayout_ms": round(float(kern[0::2].sum()), 4),
              "reduce_scatter_v_ms": round(float(kern[1::2].sum()), 4)}
     return w.name, ms_step, (sum(rl_b) + sum(rs_b)) / (ms_step / 1e3) / 1e9, roofline, extra, "bf16"
