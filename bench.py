@@ -185,6 +185,34 @@ def graph_step_ms(torch, args, g):
     return a.elapsed_time(b) / args.steps
 
 
+def stream_rows_gbs(src, src_ldv, rows_read, dst, dst_ldv, rows_written, nvec):
+    """GB/s of dc_stream_rows (xor only) reading rows_read rows and writing
+    rows_written rows of nvec 16-byte vectors: 3 untimed launches, then the
+    average of 10."""
+    import torch
+    from gradient_reduction_amd import dc
+
+    def run():
+        dc.dc_stream_rows(src, src_ldv, rows_read, dst, dst_ldv, rows_written, nvec)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return nvec * 16 * (rows_read + rows_written) / (e0.elapsed_time(e1) / 10 / 1e3) / 1e9
+
+
+def add_mix_ceiling(roofline, ceiling, what):
+    roofline["access_mix_ceiling_gbs"] = round(ceiling, 1)
+    roofline["frac_of_access_mix_ceiling"] = round(roofline["achieved"] / ceiling, 4)
+    log(f"[bench] access-mix reference ({what}): {ceiling:.1f} GB/s; the kernel reaches "
+        f"{roofline['frac_of_access_mix_ceiling']:.3f} of it")
+
+
 def access_mix_ceiling(w, owner, x, y, ld, psize=None, split=None):
     """Bandwidth the memory system gives the flush's own access mix: W rows
     read and one row written (owned tasks) or W rows written (AllReduce
@@ -198,20 +226,7 @@ def access_mix_ceiling(w, owner, x, y, ld, psize=None, split=None):
     E = 16 // w.elem_bytes()
     nvec = min(w.capacity, w.total) // E
     ldv = ld // E
-    rates = {}
-    for nw in (1, w.W):
-        def run():
-            dc.dc_stream_rows(x, ldv, w.W, y, ldv, nw, nvec)
-        for _ in range(3):
-            run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
-            run()
-        e1.record()
-        torch.cuda.synchronize()
-        rates[nw] = nvec * 16 * (w.W + nw) / (e0.elapsed_time(e1) / 10 / 1e3) / 1e9
+    rates = {nw: stream_rows_gbs(x, ldv, w.W, y, ldv, nw, nvec) for nw in (1, w.W)}
     b = w.elem_bytes()
     own = ar = 0
     for bk in w.buckets:
@@ -518,6 +533,9 @@ def bench_deferred(args):
                 "kernel": "k_accum_reduce" if fused else "k_deferred",
                 "launch_ms_avg": round(float(kern[-1]), 4),
                 "bytes_per_launch_avg": red_b, "bytes_per_launch": [red_b]}
+    if not fused and W in (4, 8, 16):
+        add_mix_ceiling(roofline, stream_rows_gbs(acc, ld // 4, W, out, ld // 4, W, M // 4),
+                        f"read {W} rows, write {W}")
     extra = {"accumulate_gbs": round(acc_gbs, 1)}
 
     # The pages' status quo beside it: every micro-batch reduced across the
@@ -596,6 +614,8 @@ def bench_rs_ag(args):
                 "traffic": traffic_from_profile("rs_ag", w.name), "kernel": "k_rs_vec",
                 "launch_ms_avg": round(float(kern[0]), 4), "bytes_per_launch_avg": rs_b,
                 "bytes_per_launch": [rs_b]}
+    add_mix_ceiling(roofline, stream_rows_gbs(x, w.ld // 8, W, out, w.ld // 8, 1, M // 8),
+                    f"read {W} rows, write 1")
     extra = {"all_gather_rank_gbs": round(gbs[1], 1), "all_gather_ring_gbs": round(gbs[2], 1)}
     return w.name, ms_step, (rs_b + 2 * ag_b) / (ms_step / 1e3) / 1e9, roofline, extra, "bf16"
 
@@ -649,6 +669,8 @@ def bench_schedules(args):
                 "traffic": traffic_from_profile("schedules_w8", w.name),
                 "kernel": "k_rs_ring", "launch_ms_avg": round(float(kern[1]), 4),
                 "bytes_per_launch_avg": rs_b, "bytes_per_launch": [rs_b]}
+    add_mix_ceiling(roofline, stream_rows_gbs(x, w.ld // 8, W, out, w.ld // 8, 1, M // 8),
+                    f"read {W} rows, write 1")
     extra = {n: {"ms": round(float(kern[i]), 4), "gbs": round(gbs[n], 1)} for i, n in enumerate(names)}
     extra["ag_launches"] = {n: S + 1 for n, _, S in scheds}
     # rank-order against ring-order shards: both are correct sums, in
@@ -724,6 +746,15 @@ def bench_relayout_rs(args):
                 "bytes_per_launch": [int(b) for b in rs_b]}
     extra = {"relayout_gbs": round(rl_gbs, 1), "relayout_ms": round(float(kern[0::2].sum()), 4),
              "reduce_scatter_v_ms": round(float(kern[1::2].sum()), 4)}
+    # references at the largest relaid bucket: reduce-scatter-v reads W rows and
+    # writes one row's worth; the relayout reads and writes all W rows (the
+    # input slab is not used after the timed steps)
+    nvec = maxn // 8
+    add_mix_ceiling(roofline, stream_rows_gbs(relaid, ld_r // 8, W, x, ld // 8, 1, nvec),
+                    f"read {W} rows, write 1")
+    rl_ref = stream_rows_gbs(x, ld // 8, W, relaid, ld_r // 8, W, nvec)
+    extra["relayout_access_mix_ceiling_gbs"] = round(rl_ref, 1)
+    extra["relayout_frac_of_access_mix_ceiling"] = round(rl_gbs / rl_ref, 4)
     return w.name, ms_step, (sum(rl_b) + sum(rs_b)) / (ms_step / 1e3) / 1e9, roofline, extra, "bf16"
 
 
