@@ -308,3 +308,20 @@ def test_executor_holders_match_probe():
             pr = ex.probe(b)
             kept = (h * np.array([t.numel for t in w.buckets[b].tasks])[:, None]).sum(axis=0)
             assert list(kept) == [pr.kept[r] for r in range(w.W)], (w.name, b)
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/dc.h is a C header: a C99 translation unit that includes it and
+    names its types and constants compiles with -pedantic -Werror."""
+    import subprocess
+    src = tmp_path / "h.c"
+    src.write_text('#include "dc.h"\n'
+                   "int f(void) {\n"
+                   "  dc_task t = {0, 0, 0, 0, 0}; dc_comm c = {1, 1}; dc_probe p; dc_piece q;\n"
+                   "  (void)t; (void)c; (void)p; (void)q;\n"
+                   "  return DC_OK + DC_BF16 + DC_F32 + DC_MAX_W + DC_SCHED_RD;\n"
+                   "}\n")
+    r = subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-c",
+                        "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                        str(tmp_path / "h.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
