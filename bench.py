@@ -12,7 +12,9 @@ peak.  Algorithmic bytes of a task of n elements over W ranks, b bytes each:
 W*n*b read + (owner ? 1 : W)*n*b written + its 32-byte task record.
 
 Other workloads (--workload): allreduce_w8 and zero2_w8 (the same gradient
-through the AllReduce and ZeRO-2 paths), mixed and zero2_mixed (W=16 fp32
+through the AllReduce and ZeRO-2 paths), layered_w8 and layered_allreduce_w8
+(the same 402.8M gradient declared as whole layers: about 33 tasks per
+bucket instead of 118, 5 straddlers), mixed and zero2_mixed (W=16 fp32
 1.2B-element flush), deferred (qwen3-0.6b W=4 fp32 gradient accumulation),
 rs_ag (7B layer reduce-scatter + all-gather), schedules_w8 (7B layer, ring-
 order reduce-scatter and the ring / bidirectional-ring / recursive-doubling
@@ -355,6 +357,8 @@ TRAFFIC_PROFILES = {
     "owner_w8": ("flush_w8_402m", "flush.hip"),
     "allreduce_w8": ("flush_allreduce_w8_402m", "flush.hip"),
     "zero2_w8": ("flush_zero2_w8_402m", "flush.hip"),
+    "layered_w8": ("flush_w8_402m_layered", "flush.hip"),
+    "layered_allreduce_w8": ("flush_allreduce_w8_402m_layered", "flush.hip"),
     "mixed": ("flush_w16_1200m", "flush.hip"),
     "zero2_mixed": ("flush_zero2_w16_1200m", "flush.hip"),
     "fused_w8": ("flush_buffers_w8_402m", "flush_buffers.hip"),
@@ -811,7 +815,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="owner_w8",
-                    choices=["owner_w8", "allreduce_w8", "zero2_w8", "mixed", "zero2_mixed",
+                    choices=["owner_w8", "allreduce_w8", "zero2_w8", "layered_w8",
+                             "layered_allreduce_w8", "mixed", "zero2_mixed",
                              "deferred", "rs_ag", "schedules_w8", "relayout_rs_w8", "fused_w8",
                              "fused_mixed", "tiny"])
     ap.add_argument("--ga", type=int, default=8)
@@ -834,12 +839,15 @@ def main():
     calib = copy_calibration()
     log(f"[bench] streaming copy reference: {calib} GB/s")
     cpu = None
-    if args.workload in ("owner_w8", "allreduce_w8", "zero2_w8", "mixed", "zero2_mixed", "tiny"):
-        w = {"owner_w8": wl.owner_flush_w8, "allreduce_w8": wl.owner_flush_w8,
-             "zero2_w8": wl.owner_flush_w8, "mixed": wl.mixed_flush_w16,
-             "zero2_mixed": wl.mixed_flush_w16, "tiny": wl.tiny_flush}[args.workload]()
+    flush_workloads = {"owner_w8": wl.owner_flush_w8, "allreduce_w8": wl.owner_flush_w8,
+                       "zero2_w8": wl.owner_flush_w8, "layered_w8": wl.owner_flush_w8_layered,
+                       "layered_allreduce_w8": wl.owner_flush_w8_layered,
+                       "mixed": wl.mixed_flush_w16, "zero2_mixed": wl.mixed_flush_w16,
+                       "tiny": wl.tiny_flush}
+    if args.workload in flush_workloads:
+        w = flush_workloads[args.workload]()
         zero2 = args.workload.startswith("zero2")
-        owner_mode = args.workload != "allreduce_w8" and not zero2
+        owner_mode = "allreduce" not in args.workload and not zero2
         ms, value, step_bytes, roof, extra = bench_flush(args, w, owner_mode, zero2)
         name, dtype = w.name, wl.DTYPE_NAME[w.dtype]
         config = {"workload": name, "W": w.W, "elements": w.total, "buckets": len(w.buckets),

@@ -243,6 +243,38 @@ def owner_flush_w8(seed_sizes: int = 102, value_seed: int = 2, target: int = 402
     return finish(w)
 
 
+def owner_flush_w8_layered(value_seed: int = 2, target: int = 402_800_000,
+                           capacity: int = 52_428_800) -> FlushWorkload:
+    """W=8 bf16 flush of the same 402.8M-element gradient laid out as layers.
+
+    The embedding (151936 x 1024) is declared first, then decoder layers of
+    hidden 1024 in declaration order -- input norm (1024), q, k, v, o
+    (1024 x 1024 each), post norm (1024), up (1024 x 4096), down
+    (4096 x 1024) -- stopping at the first parameter that brings the total to
+    `target`, then a final norm (1024).  That is 19 whole layers and a 20th
+    cut after its up projection: 161 params, 403,088,384 elements, buckets of
+    33/32/32/32/31 tasks plus the embedding alone.  Only 5 params straddle a
+    partition boundary (the embedding and four 1024 x 4096 matrices), so
+    about 33 tasks per bucket instead of the ~118 of the shuffled mix.  Same
+    group, partitions, values and pre-division as the shuffled mix.
+    """
+    layer = [HIDDEN, HIDDEN * HIDDEN, HIDDEN * HIDDEN, HIDDEN * HIDDEN, HIDDEN * HIDDEN, HIDDEN,
+             HIDDEN * 4 * HIDDEN, 4 * HIDDEN * HIDDEN]
+    numel = [EMBED]
+    total = EMBED
+    while total < target:
+        for n in layer:
+            numel.append(n)
+            total += n
+            if total >= target:
+                break
+    numel.append(HIDDEN)
+    w = FlushWorkload(name="owner_flush_w8_bf16_402.8M_layered", W=8, dtype=DT_BF16, sigma=1e-3,
+                      value_seed=value_seed, numel=numel, group_begin=[0, len(numel)],
+                      group_comm=[0], comms=[Comm(8, 1)], capacity=capacity, pre_div=1)
+    return finish(w)
+
+
 def mixed_flush_w16(seed_sizes: int = 105, value_seed: int = 5, target: int = 1_200_000_000,
                     capacity: int = 52_428_800, moe_stride: int = 1) -> FlushWorkload:
     """W=16 fp32, lognormal sizes (median 64k, sigma_ln 2, clipped to

@@ -137,7 +137,7 @@ def test_validate_tasks():
 def test_probe_matches_oracle_on_workloads():
     """dc_probe_flush is host code: compare it with the oracle's probe on the
     synthetic workloads and random ones (owner path on and off)."""
-    ws = [wl.tiny_flush(), wl.owner_flush_w8(), wl.mixed_flush_w16()]
+    ws = [wl.tiny_flush(), wl.owner_flush_w8(), wl.owner_flush_w8_layered(), wl.mixed_flush_w16()]
     rng = random.Random(3)
     for k in range(5):
         W = rng.choice([2, 4, 8, 16])
@@ -175,7 +175,7 @@ def _dest_from_pieces(pieces, n):
 def test_plan_relayout_matches_oracle():
     """The host relayout planner against the oracle's element-by-element
     relayout map, on the synthetic workloads and random ones."""
-    ws = [wl.tiny_flush(), wl.owner_flush_w8(), wl.mixed_flush_w16()]
+    ws = [wl.tiny_flush(), wl.owner_flush_w8(), wl.owner_flush_w8_layered(), wl.mixed_flush_w16()]
     rng = random.Random(4)
     for k in range(6):
         W = rng.choice([2, 3, 4, 8])

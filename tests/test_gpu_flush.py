@@ -73,7 +73,7 @@ def run_owner_map(w):
 
 
 def owner_workloads():
-    out = [wl.tiny_flush(), wl.owner_flush_w8(), wl.mixed_flush_w16()]
+    out = [wl.tiny_flush(), wl.owner_flush_w8(), wl.owner_flush_w8_layered(), wl.mixed_flush_w16()]
     rng = random.Random(5)
     for k in range(6):
         G = rng.randint(1, 4)
@@ -374,6 +374,11 @@ def full_size_flush(w, reduce_to_owner, in_place, zero2=False):
 @pytest.mark.parametrize("owner", [True, False], ids=["owner", "allreduce"])
 def test_flush_w8_402m_full_size(owner):
     full_size_flush(wl.owner_flush_w8(), owner, in_place=False)
+
+
+@pytest.mark.parametrize("owner", [True, False], ids=["owner", "allreduce"])
+def test_flush_w8_402m_layered_full_size(owner):
+    full_size_flush(wl.owner_flush_w8_layered(), owner, in_place=False)
 
 
 def test_flush_w16_mixed_1_2b_full_size_in_place():
