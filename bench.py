@@ -84,9 +84,12 @@ class Timer:
 
 def run_timed(torch, args, step, n_events):
     """args.warmup untimed steps, then args.steps timed ones bracketed by a
-    synchronize on both sides; HIP events around every launch.  Python's
-    garbage collector is off in the timed loop so a collection cannot stall
-    the host mid-step.  Returns (ms per step, [steps, n_events] launch ms)."""
+    synchronize on both sides: the step time.  Then args.steps more with HIP
+    events around every launch, for the per-launch kernel times (an event
+    record is a packet of its own on the stream, so these steps run a little
+    longer and are not the step time).  Python's garbage collector is off in
+    both loops so a collection cannot stall the host mid-step.  Returns
+    (ms per step, [steps, n_events] launch ms)."""
     import gc
     for _ in range(args.warmup):
         step()
@@ -100,9 +103,12 @@ def run_timed(torch, args, step, n_events):
     gc.disable()
     try:
         t0.record()
+        for _ in range(args.steps):
+            step()
+        t1.record()
+        torch.cuda.synchronize()
         for k in range(args.steps):
             step(timers[k])
-        t1.record()
         torch.cuda.synchronize()
     finally:
         gc.enable()
