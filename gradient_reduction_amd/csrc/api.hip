@@ -49,6 +49,16 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
 }
 
+// Largest row stride, column count or byte count accepted: rows * ld * 4
+// bytes (rows up to 65535) and W * ld * 16 then stay inside int64, so no size
+// arithmetic below can wrap.
+constexpr int64_t kMaxExtent = (int64_t)1 << 44;
+
+dc_status check_extent(const char* name, int64_t n) {
+  if (n > kMaxExtent) return fail(DC_ERR_SHAPE, "%s=%lld exceeds 2^44", name, (long long)n);
+  return DC_OK;
+}
+
 dc_status check_w(int32_t W) {
   if (W < 1 || W > DC_MAX_W) return fail(DC_ERR_ARG, "W=%d outside [1, %d]", W, DC_MAX_W);
   return DC_OK;
@@ -62,6 +72,8 @@ dc_status check_dtype(int32_t dtype) {
 // A [rows, ld] slab: non-NULL, 16-byte aligned base and stride, ld >= cols.
 dc_status check_slab(const char* name, const void* p, int64_t ld, int64_t cols, int32_t dtype) {
   if (p == nullptr) return fail(DC_ERR_NULL, "%s is NULL", name);
+  if (ld > kMaxExtent || cols > kMaxExtent)
+    return fail(DC_ERR_SHAPE, "%s: ld=%lld or %lld columns exceeds 2^44", name, (long long)ld, (long long)cols);
   if (ld < 1 || ld < cols) return fail(DC_ERR_SHAPE, "%s: ld=%lld < %lld columns", name, (long long)ld, (long long)cols);
   if (!aligned16(p) || (ld * elem_bytes(dtype)) % 16 != 0)
     return fail(DC_ERR_ALIGN, "%s: base or row stride (ld=%lld) not 16-byte aligned", name, (long long)ld);
@@ -207,6 +219,7 @@ dc_status flush_common(const char* fn, int32_t W, int32_t dtype, const void* sla
   if ((st = check_w(W)) || (st = check_dtype(dtype)) || (st = check_comms(W, comms, num_comms))) return st;
   if (bucket_col < 0 || bucket_numel < 0)
     return fail(DC_ERR_ARG, "bucket_col=%lld, bucket_numel=%lld", (long long)bucket_col, (long long)bucket_numel);
+  if ((st = check_extent("bucket_col", bucket_col)) || (st = check_extent("bucket_numel", bucket_numel))) return st;
   const int64_t end = bucket_col + bucket_numel;
   if ((st = check_slab("slab_in", slab_in, ld_in, end, dtype)) ||
       (st = check_slab("slab_out", slab_out, ld_out, end, dtype)))
@@ -443,6 +456,8 @@ dc_status dc_relayout_bucket(int32_t W, int32_t dtype, const void* slab_in, int6
   if ((st = check_w(W)) || (st = check_dtype(dtype))) return st;
   if (bucket_col < 0 || bucket_numel < 0 || out_numel < 0 || num_pieces < 0)
     return fail(DC_ERR_ARG, "negative bucket_col, bucket_numel, out_numel or num_pieces");
+  if ((st = check_extent("bucket_col", bucket_col)) || (st = check_extent("bucket_numel", bucket_numel)))
+    return st;
   if ((st = check_slab("slab_in", slab_in, ld_in, bucket_col + bucket_numel, dtype)) ||
       (st = check_slab("out", out, ld_out, out_numel, dtype)))
     return st;
@@ -497,6 +512,7 @@ dc_status dc_all_gather(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
   dc_status st;
   if ((st = check_w(W)) || (st = check_dtype(dtype))) return st;
   if (shard_numel < 0) return fail(DC_ERR_ARG, "shard_numel < 0");
+  if ((st = check_extent("shard_numel", shard_numel))) return st;
   if (order != DC_ORDER_RANK && order != DC_ORDER_RING) return fail(DC_ERR_ARG, "order=%d", order);
   if (step < -1 || step >= W) return fail(DC_ERR_ARG, "step=%d outside [-1, W)", step);
   if ((st = check_slab("in", in, ld_in, shard_numel, dtype)) ||
@@ -531,6 +547,7 @@ dc_status dc_all_gather_step(int32_t W, int32_t dtype, const void* in, int64_t l
   dc_status st;
   if ((st = check_w(W)) || (st = check_dtype(dtype))) return st;
   if (shard_numel < 0) return fail(DC_ERR_ARG, "shard_numel < 0");
+  if ((st = check_extent("shard_numel", shard_numel))) return st;
   int32_t steps;
   if (algo == DC_SCHED_RING) {
     steps = W - 1;
@@ -625,6 +642,7 @@ dc_status dc_round_bf16(const float* in, uint16_t* out, int64_t n, void* stream)
 
 dc_status dc_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   if (bytes < 0 || bytes % 16 != 0) return fail(DC_ERR_SHAPE, "bytes=%lld is not a multiple of 16", (long long)bytes);
+  if (check_extent("bytes", bytes)) return DC_ERR_SHAPE;
   if (bytes > 0 && (src == nullptr || dst == nullptr)) return fail(DC_ERR_NULL, "src or dst is NULL");
   if (!aligned16(src) || !aligned16(dst)) return fail(DC_ERR_ALIGN, "src or dst not 16-byte aligned");
   if (overlaps(src, bytes, dst, bytes)) return fail(DC_ERR_ARG, "src and dst overlap");
@@ -637,6 +655,7 @@ dc_status dc_stream_rows(const void* src, int64_t src_ld_vec, int32_t rows_read,
         (rows_written == 1 || rows_written == rows_read)))
     return fail(DC_ERR_UNSUPPORTED, "rows_read=%d rows_written=%d (need 4/8/16 and 1 or rows_read)",
                 rows_read, rows_written);
+  if (check_extent("src_ld_vec", src_ld_vec) || check_extent("dst_ld_vec", dst_ld_vec)) return DC_ERR_SHAPE;
   if (nvec < 0 || src_ld_vec < nvec || dst_ld_vec < nvec)
     return fail(DC_ERR_SHAPE, "nvec=%lld with row strides %lld and %lld vectors", (long long)nvec,
                 (long long)src_ld_vec, (long long)dst_ld_vec);

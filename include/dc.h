@@ -28,6 +28,8 @@
  *   - dtype: DC_BF16 (bfloat16 stored as uint16 bit patterns) or DC_F32.
  *   - Slab base pointers must be 16-byte aligned and `ld` a multiple of 16
  *     bytes (8 bf16 or 4 fp32 elements), else DC_ERR_ALIGN.
+ *   - Row strides, column counts and byte counts above 2^44 are DC_ERR_SHAPE,
+ *     so that no size computed from them can overflow int64.
  *   - Sums are folded in fp32 in ascending rank order (member order within a
  *     communicator), starting from the first contribution, and rounded once
  *     to the dtype (round to nearest even; NaN -> quiet NaN 0x7FC0|sign for

@@ -75,6 +75,11 @@ def test_flush_argument_checks():
     expect(dc.DC_ERR_ARG, call, comms=[(8, 1)] * 9, num_comms=9)
     expect(dc.DC_ERR_ARG, call, ld_out=128)                        # in place with different ld
     expect(dc.DC_ERR_ARG, call, slab_out=FAKE + 64)                # partial overlap
+    # sizes whose products would overflow int64 are refused before any arithmetic
+    big = (1 << 62) + 64
+    expect(dc.DC_ERR_SHAPE, call, ld_in=big, ld_out=big, slab_out=FAKE << 1)
+    expect(dc.DC_ERR_SHAPE, call, bucket_col=(1 << 63) - 8)
+    expect(dc.DC_ERR_SHAPE, call, bucket_numel=(1 << 44) + 8)
 
 
 def test_other_argument_checks():
@@ -114,6 +119,14 @@ def test_other_argument_checks():
     expect(dc.DC_ERR_SHAPE, dc.dc_stream_rows, FAKE, 32, 8, FAKE << 1, 64, 1, 64, stream=0)
     expect(dc.DC_ERR_ARG, dc.dc_stream_rows, FAKE, 64, 8, FAKE + 1024, 64, 1, 64, stream=0)
     expect(dc.DC_ERR_ARG, dc.dc_stream_copy, FAKE, FAKE + 16, 64, stream=0)
+    huge = 1 << 60
+    expect(dc.DC_ERR_SHAPE, dc.dc_all_gather, 8, 0, FAKE, huge, FAKE << 1, huge, huge, 0, -1, stream=0)
+    expect(dc.DC_ERR_SHAPE, dc.dc_all_gather_step, 8, 0, FAKE, huge, FAKE << 1, huge, huge,
+           dc.DC_SCHED_RING, 1, stream=0)
+    expect(dc.DC_ERR_SHAPE, dc.dc_accumulate, 65535, FAKE, huge, FAKE << 1, huge, 64, 0, stream=0)
+    expect(dc.DC_ERR_SHAPE, dc.dc_reduce_scatter, 8, 0, FAKE, huge, FAKE << 1, huge, huge, 0, stream=0)
+    expect(dc.DC_ERR_SHAPE, dc.dc_stream_copy, FAKE, FAKE << 1, huge, stream=0)
+    expect(dc.DC_ERR_SHAPE, dc.dc_stream_rows, FAKE, huge, 8, FAKE << 1, 64, 1, 64, stream=0)
     expect(dc.DC_ERR_SHAPE, dc.dc_partition_ids, 4, 3, FAKE, 1, [0, 2], [4], FAKE, FAKE, FAKE,
            FAKE, 10, stream=0)
     expect(dc.DC_ERR_SHAPE, dc.dc_partition_ids, 4, 3, FAKE, 1, [0, 3], [4], FAKE, FAKE, FAKE,
