@@ -144,7 +144,11 @@ def bench_flush(args, w, reduce_to_owner=True, zero2=False):
     nb = len(w.buckets)
 
     def step(timer=None):
+        if timer is not None:
+            timer.ev[nb][0].record()
         ex.build_owner_map()
+        if timer is not None:
+            timer.ev[nb][1].record()
         for b in range(nb):
             if timer is not None:
                 timer.ev[b][0].record()
@@ -152,7 +156,8 @@ def bench_flush(args, w, reduce_to_owner=True, zero2=False):
             if timer is not None:
                 timer.ev[b][1].record()
 
-    ms_step, kern = run_timed(torch, args, step, nb)          # [steps, buckets]
+    ms_step, kern_all = run_timed(torch, args, step, nb + 1)
+    kern, owner_map_ms = kern_all[:, :nb], kern_all[:, nb]    # [steps, buckets], [steps]
     avg_launch_ms = float(kern.mean())
     flush_gbs = sum(per_launch) / (kern.sum(axis=1).mean() / 1e3) / 1e9
     flush_gbs_median = sum(per_launch) / (np.median(kern.sum(axis=1)) / 1e3) / 1e9
@@ -171,6 +176,7 @@ def bench_flush(args, w, reduce_to_owner=True, zero2=False):
         roofline["frac_of_access_mix_ceiling"] = round(flush_gbs / ceiling, 4)
     extra = {"per_bucket_gbs": [round(b / (m / 1e3) / 1e9, 1) for b, m in zip(per_launch, kern.mean(axis=0))],
              "flush_gbs_median_step": round(flush_gbs_median, 1),
+             "owner_map_us": round(float(owner_map_ms.mean()) * 1e3, 2),
              "graph_ms_per_step": round(graph_step_ms(torch, args, ex.capture_step(x, ld, y, ld)), 4)}
     log(f"[bench] the same step replayed as one HIP graph: {extra['graph_ms_per_step']:.4f} ms")
     del x, y
@@ -320,7 +326,11 @@ def bench_flush_buffers(args, w):
     step_bytes = sum(per_launch) + owner_map_bytes(w)
 
     def step(timer=None):
+        if timer is not None:
+            timer.ev[nb][0].record()
         ex.build_owner_map()
+        if timer is not None:
+            timer.ev[nb][1].record()
         for b in range(nb):
             if timer is not None:
                 timer.ev[b][0].record()
@@ -328,7 +338,8 @@ def bench_flush_buffers(args, w):
             if timer is not None:
                 timer.ev[b][1].record()
 
-    ms_step, kern = run_timed(torch, args, step, nb)
+    ms_step, kern_all = run_timed(torch, args, step, nb + 1)
+    kern, owner_map_ms = kern_all[:, :nb], kern_all[:, nb]
     gbs = sum(per_launch) / (kern.sum(axis=1).mean() / 1e3) / 1e9
     gbs_median = sum(per_launch) / (np.median(kern.sum(axis=1)) / 1e3) / 1e9
     value = step_bytes / (ms_step / 1e3) / 1e9
@@ -347,6 +358,7 @@ def bench_flush_buffers(args, w):
         roofline["frac_of_access_mix_ceiling"] = round(gbs / ceiling, 4)
     extra = {"per_bucket_gbs": [round(b / (m / 1e3) / 1e9, 1) for b, m in zip(per_launch, kern.mean(axis=0))],
              "flush_gbs_median_step": round(gbs_median, 1),
+             "owner_map_us": round(float(owner_map_ms.mean()) * 1e3, 2),
              "fused_bytes_per_step": int(sum(per_launch)),
              "unfused_bytes_per_step": int(unfused),
              "bytes_saved_frac": round(1 - sum(per_launch) / unfused, 4)}
