@@ -553,6 +553,34 @@ def pin_owner_path_equivalences():
         assert np.array_equal(out_bits(dtype, ar[:, T:]), out_bits(dtype, sentinel[:, T:]))
 
 
+def pin_owner_only_on_dp_comm():
+    """DeepSpeed issue, design points (MoE groups): reduce-to-owner applies
+    to the data-parallel communicator only.  A task on a sub-communicator
+    keeps AllReduce inside each of its blocks even when the owner array has
+    an entry for its param, while a data-parallel task with the same entry
+    writes that rank's row alone.  Integer-valued inputs keep every sum
+    exact, so the expected rows are the brute-force block sums."""
+    rng = random.Random(57)
+    for W, c, stride in ((4, 2, 1), (4, 2, 2), (8, 4, 2), (8, 2, 1)):
+        n = 5
+        vals = [[rng.randint(-40, 40) for _ in range(2 * n)] for _ in range(W)]
+        rows = np.array(vals, np.float32)
+        sent = np.full((W, 2 * n), 999.0, np.float32)
+        out = sent.copy()
+        owner = np.array([1, 1], np.int32)            # both params name rank 1
+        # task 0: param 0 on the data-parallel comm; task 1: param 1 on comm 1
+        oracle.flush(W, F32, rows, out, 0, [0, n], [n, n], [0, 1], [0, 1], owner, [W, c],
+                     [1, stride], 0)
+        for r in range(W):
+            want0 = [float(sum(vals[q][j] for q in range(W))) if r == 1 else 999.0
+                     for j in range(n)]
+            assert list(out[r, :n]) == want0, ("data-parallel task", W, r)
+            blk = [r - (r % c) + i for i in range(c)] if stride == 1 else \
+                  [r % stride + i * stride for i in range(c)]
+            want1 = [float(sum(vals[q][j] for q in blk)) for j in range(n, 2 * n)]
+            assert list(out[r, n:]) == want1, ("sub-communicator task", W, c, stride, r)
+
+
 def pin_zero2_routing():
     """ZeRO-2 owner path ([DS] Follow-up): every element of a data-parallel
     task is written to exactly one row, the rank whose partition holds that
@@ -961,6 +989,19 @@ def pin_accumulate_zero_start():
     assert list(acc[0].view(np.uint32)) == [0, 0x3FC00000, 0, 0]
 
 
+def pin_deferred_rank_order():
+    """MaxText PR, What: the deferred reduce is one cross-replica sum, read
+    here as a fold in replica order 0..W-1 in fp32.  Hand-derived, as for the
+    flush: replicas (2^24, 1, -2^24, 1) give 2^24 + 1 -> 2^24 (a tie, to
+    even), then 0, then 1; the reverse order gives 2.  Every output row holds
+    the same sum."""
+    acc = np.array([[2.0 ** 24, 3.0], [1.0, 5.0], [-(2.0 ** 24), -8.0], [1.0, 0.5]], np.float32)
+    for out_rows in (1, 4):
+        out = np.full((out_rows, 2), 7.0, np.float32)
+        oracle.deferred_reduce(4, acc, out, 2, out_rows)
+        assert np.array_equal(out, np.tile(np.array([1.0, 0.5], np.float32), (out_rows, 1))), out
+
+
 def pin_deferred_exact_reassociation():
     """MaxText PR, Results: where the reassociation is exact the two orders
     agree bit for bit.  Values k*2^-20 (|k| < 2^10) keep every partial sum
@@ -1032,9 +1073,10 @@ ALL_PINS = [
     pin_fold_identical_rows, pin_fold_brute_force, pin_fold_error_bound,
     pin_prediv_non_power_of_two, pin_reduce_scatter_all_gather, pin_ring_reduce_scatter, pin_partition_brute_force,
     pin_owner_rules, pin_group_eligibility, pin_probe_printed_example, pin_ratio_printed_example,
-    pin_probe_closed_forms, pin_owner_path_equivalences, pin_zero2_routing,
+    pin_probe_closed_forms, pin_owner_path_equivalences, pin_owner_only_on_dp_comm,
+    pin_zero2_routing,
     pin_relayout_reduce_scatter, pin_flush_buffers, pin_ring_table, pin_ring_closed_form,
     pin_rd_table, pin_ring_step_replay, pin_ag_step_executors, pin_deferred_ga1_identity,
-    pin_accumulate_zero_start, pin_deferred_exact_reassociation, pin_deferred_tolerance, pin_deferred_restore,
+    pin_accumulate_zero_start, pin_deferred_rank_order, pin_deferred_exact_reassociation, pin_deferred_tolerance, pin_deferred_restore,
     pin_deferred_round_trip,
 ]

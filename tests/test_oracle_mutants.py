@@ -103,6 +103,12 @@ MUTANTS = {
     "ag_step0_wrong_position": (
         "memcpy((char*)out + ((int64_t)i * ld_out + (int64_t)i * L) * eb,",
         "memcpy((char*)out + ((int64_t)i * ld_out + (int64_t)((i + 1) % W) * L) * eb,"),
+    "deferred_reverse_rank_order": (
+        "s = (r == 0) ? acc[r * ld_acc + j] : s + acc[r * ld_acc + j];",
+        "s = (r == 0) ? acc[(W - 1 - r) * ld_acc + j] : s + acc[(W - 1 - r) * ld_acc + j];"),
+    "owner_honoured_on_sub_comm": (
+        "int root = (t_comm[t] == 0 && owner != NULL) ? owner[t_param[t]] : -1;",
+        "int root = (owner != NULL) ? owner[t_param[t]] : -1;"),
     "rd_partner_plus": (
         "int q = i ^ d;",
         "int q = (i + d) % N;"),
