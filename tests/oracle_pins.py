@@ -506,6 +506,36 @@ def pin_probe_closed_forms():
         assert int(on_pr["discarded"].sum()) == stra
 
 
+def pin_probe_sub_comm_holders():
+    """DeepSpeed issue, problem statement (kept and discarded counts) and
+    design points (MoE groups): a param of a group on a size-c
+    sub-communicator is held, in every block, by the member whose in-block
+    index is one of its partitions.  Brute force over the ranks: contiguous
+    blocks put rank r at index r mod c, strided blocks (stride W/c) at
+    index r div (W/c).  Such tasks are AllReduced, so every rank is written
+    every element."""
+    rng = random.Random(43)
+    for W, c in ((4, 2), (8, 4), (8, 2), (16, 4), (6, 3)):
+        for stride in (1, W // c):
+            sizes = [rng.randint(0, 50) for _ in range(rng.randint(1, 12))]
+            P = len(sizes)
+            flat, ps, off, pids = oracle.partition_ids(sizes, [0, P], [c])
+            arrival = list(range(P - 1, -1, -1))
+            t_numel = [sizes[p] for p in arrival]
+            pr = oracle.probe(W, t_numel, arrival, [1] * P, None, off, pids, [W, c], [1, stride])
+            kept = [0] * W
+            for p, n in zip(arrival, t_numel):
+                parts = set(int(q) for q in pids[off[p]:off[p + 1]])
+                for r in range(W):
+                    idx = r % c if stride == 1 else r // stride
+                    if idx in parts:
+                        kept[r] += n
+            tot = sum(t_numel)
+            assert list(pr["kept"]) == kept, (W, c, stride)
+            assert list(pr["written"]) == [tot] * W
+            assert list(pr["discarded"]) == [tot - k for k in kept]
+
+
 # ---------------------------------------------------------------------------
 # the owner path and the AllReduce path
 # ---------------------------------------------------------------------------
@@ -686,20 +716,21 @@ def pin_relayout_reduce_scatter():
         assert np.array_equal(dest, want), trial
         for q in range(W):
             assert seg[q + 1] - seg[q] == sum(1 for c in part_of if part_of[c] == q)
-        # values
-        ld = max(8, -(-n // 8) * 8)
+        # values, with the bucket starting at a column other than 0
+        col0 = rng.randint(0, 9)
+        ld = max(8, -(-(col0 + n) // 8) * 8)
         rows = random_bits(rng, dtype, (W, ld), wide=False)
         relaid = np.zeros_like(rows)
-        oracle.relayout_apply(W, dtype, rows, relaid, 0, n, dest)
+        oracle.relayout_apply(W, dtype, rows, relaid, col0, n, dest)
         shard_ld = max(8, -(-int(max(seg[1:] - seg[:-1], default=0)) // 8) * 8)
         shards = np.zeros((W, shard_ld), rows.dtype)
         oracle.reduce_scatter_v(W, dtype, relaid, shards, seg, 1)
         z2 = np.zeros_like(rows)
-        oracle.flush_zero2(W, dtype, rows, z2, 0, t_off, t_numel, arrival, t_comm, flat, part_size,
-                           [W, sub], [1, 1], 1)
+        oracle.flush_zero2(W, dtype, rows, z2, col0, t_off, t_numel, arrival, t_comm, flat,
+                           part_size, [W, sub], [1, 1], 1)
         sb, zb = out_bits(dtype, shards), out_bits(dtype, z2)
         for c, q in part_of.items():
-            assert sb[q, dest[c] - seg[q]] == zb[q, c], (trial, c, q)
+            assert sb[q, dest[c] - seg[q]] == zb[q, col0 + c], (trial, c, q)
 
 
 def _scatter_layout(rng, sizes, gap=3):
@@ -991,15 +1022,19 @@ def pin_accumulate_zero_start():
 
 def pin_deferred_rank_order():
     """MaxText PR, What: the deferred reduce is one cross-replica sum, read
-    here as a fold in replica order 0..W-1 in fp32.  Hand-derived, as for the
-    flush: replicas (2^24, 1, -2^24, 1) give 2^24 + 1 -> 2^24 (a tie, to
-    even), then 0, then 1; the reverse order gives 2.  Every output row holds
-    the same sum."""
-    acc = np.array([[2.0 ** 24, 3.0], [1.0, 5.0], [-(2.0 ** 24), -8.0], [1.0, 0.5]], np.float32)
+    here as a fold in replica order 0..W-1 in fp32 that starts from replica
+    0's value.  Hand-derived, as for the flush: replicas (2^24, 1, -2^24, 1)
+    give 2^24 + 1 -> 2^24 (a tie, to even), then 0, then 1; the reverse
+    order gives 2.  Replicas that are all -0 sum to -0 (a start from +0 would
+    give +0).  Every output row holds the same sum."""
+    acc = np.array([[2.0 ** 24, 3.0, -0.0], [1.0, 5.0, -0.0], [-(2.0 ** 24), -8.0, -0.0],
+                    [1.0, 0.5, -0.0]], np.float32)
     for out_rows in (1, 4):
-        out = np.full((out_rows, 2), 7.0, np.float32)
-        oracle.deferred_reduce(4, acc, out, 2, out_rows)
-        assert np.array_equal(out, np.tile(np.array([1.0, 0.5], np.float32), (out_rows, 1))), out
+        out = np.full((out_rows, 3), 7.0, np.float32)
+        oracle.deferred_reduce(4, acc, out, 3, out_rows)
+        # the fold starts from replica 0's value, so replicas all -0 sum to -0
+        want = np.tile(np.array([1.0, 0.5, -0.0], np.float32), (out_rows, 1))
+        assert np.array_equal(out.view(np.uint32), want.view(np.uint32)), out
 
 
 def pin_deferred_exact_reassociation():
@@ -1073,7 +1108,8 @@ ALL_PINS = [
     pin_fold_identical_rows, pin_fold_brute_force, pin_fold_error_bound,
     pin_prediv_non_power_of_two, pin_reduce_scatter_all_gather, pin_ring_reduce_scatter, pin_partition_brute_force,
     pin_owner_rules, pin_group_eligibility, pin_probe_printed_example, pin_ratio_printed_example,
-    pin_probe_closed_forms, pin_owner_path_equivalences, pin_owner_only_on_dp_comm,
+    pin_probe_closed_forms, pin_probe_sub_comm_holders, pin_owner_path_equivalences,
+    pin_owner_only_on_dp_comm,
     pin_zero2_routing,
     pin_relayout_reduce_scatter, pin_flush_buffers, pin_ring_table, pin_ring_closed_form,
     pin_rd_table, pin_ring_step_replay, pin_ag_step_executors, pin_deferred_ga1_identity,

@@ -109,6 +109,15 @@ MUTANTS = {
     "owner_honoured_on_sub_comm": (
         "int root = (t_comm[t] == 0 && owner != NULL) ? owner[t_param[t]] : -1;",
         "int root = (owner != NULL) ? owner[t_param[t]] : -1;"),
+    "deferred_starts_from_zero": (
+        "s = (r == 0) ? acc[r * ld_acc + j] : s + acc[r * ld_acc + j];",
+        "s = s + acc[r * ld_acc + j];"),
+    "relayout_ignores_bucket_column": (
+        "(const char*)in + ((int64_t)r * ld_in + bucket_col + c) * eb",
+        "(const char*)in + ((int64_t)r * ld_in + c) * eb"),
+    "probe_strided_holders_as_contiguous": (
+        "for (int b = 0; b < W / c; ++b) hd[member(b, pids[k], c, s)] = 1;",
+        "for (int b = 0; b < W / c; ++b) hd[b * c + pids[k]] = 1;"),
     "rd_partner_plus": (
         "int q = i ^ d;",
         "int q = (i + d) % N;"),
