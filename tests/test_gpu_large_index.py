@@ -1,0 +1,158 @@
+"""GPU parity at column indices past 2^31 (through the C ABI).
+
+The full-size workloads reach 1.2e9 columns, under 2^31.  Here a bucket is
+flushed across column 2^31 (fast W = 4 bf16 path, both modes, and the
+run-time-W path at W = 3 fp32), the accumulate and deferred reduce run over
+M = 2^31 + 1003 fp32 columns (a ragged tail included), and a reduce-scatter
+and all-gather run with shards of 2^31 + 64 bf16 columns, so that any 32-bit
+column or vector index would land somewhere else.  Outputs are compared with
+the oracle bit for bit on sampled columns; in the flush every column of a
+margin around the bucket is compared, sentinels included.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gradient_reduction_amd import dc
+from synth import workloads as wl
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+BIG = 1 << 31
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dc.lib()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _fill_columns(x, dtype, seed, rows, ld, c0, n, scale):
+    """Device columns [c0, c0+n) of every row from the generator (the rest of
+    the slab is left as allocated)."""
+    eb = 2 if dtype == wl.DT_BF16 else 4
+    synth.fill_slab_device(dtype, seed, 0, scale, rows, ld, n, x.data_ptr() + c0 * eb, _stream(),
+                           col0=c0)
+
+
+def _host_columns(dtype, seed, rows, cols, scale):
+    a = np.stack([synth.gather(dtype, seed, r, scale, cols) for r in range(rows)])
+    return a.view(np.float32) if dtype == wl.DT_F32 else a
+
+
+@pytest.mark.parametrize("W,dtype,owner", [(4, wl.DT_BF16, True), (4, wl.DT_BF16, False),
+                                           (3, wl.DT_F32, True)], ids=lambda v: str(v))
+def test_flush_across_column_2_31(W, dtype, owner):
+    import torch
+    sizes = [3000, 1, 2995, 4104, 17, 905]          # the fourth task holds column 2^31
+    c0 = BIG - 6000
+    numel = sum(sizes)
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int).tolist()
+    assert c0 + offs[3] < BIG < c0 + offs[3] + sizes[3]
+    ld = wl.round_up(c0 + numel + 1024, 64)
+    U.say("flush past 2^31", W, dtype, owner, "ld", ld)
+    scale = wl.sigma_scale(1e-2)
+    tdt = torch.int16 if dtype == wl.DT_BF16 else torch.int32
+    sent = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
+    x = torch.empty((W, ld), dtype=tdt, device="cuda")
+    _fill_columns(x, dtype, 601, W, ld, c0, numel, scale)
+    y = torch.full((W, ld), sent if dtype == wl.DT_BF16 else np.int32(np.uint32(sent)).item(),
+                   dtype=tdt, device="cuda")
+    P = len(sizes)
+    own = np.array([1, -1, 2, 0, -1, W - 1], np.int32)
+    tasks = dc.tasks_array([(offs[k], sizes[k], k, 0) for k in range(P)])
+    d_tasks = torch.from_numpy(tasks.view(np.uint8).copy()).cuda()
+    d_own = torch.from_numpy(own).cuda() if owner else None
+    dc.dc_flush_bucket(W, dtype, x, ld, y, ld, c0, numel, d_tasks, P, d_own, P, [(W, 1)], 1, 1)
+    torch.cuda.synchronize()
+    lo, hi = c0 - 64, c0 + numel + 64
+    got = U.bits(y[:, lo:hi].cpu().numpy().view(np.uint16 if dtype == wl.DT_BF16 else np.float32), dtype)
+    del x, y
+    torch.cuda.empty_cache()
+    hin = _host_columns(dtype, 601, W, np.arange(lo, hi, dtype=np.int64), scale)
+    hout = np.zeros_like(hin)
+    U.bits(hout, dtype)[:] = sent
+    oracle.flush(W, dtype, hin, hout, c0 - lo, offs, sizes, list(range(P)), [0] * P,
+                 own if owner else None, [W], [1], 1)
+    bad = np.argwhere(got != U.bits(hout, dtype))
+    assert len(bad) == 0, f"{len(bad)} mismatches, first (row, column) {[(r, lo + c) for r, c in bad[:4]]}"
+
+
+def _sample(n_total, around, rng, extra=48):
+    cols = set([0, 1, n_total - 1, n_total - 2, n_total - 3])
+    for a in around:
+        cols.update(range(max(0, a - 5), min(n_total, a + 6)))
+    cols.update(int(c) for c in rng.integers(0, n_total, extra))
+    return np.array(sorted(cols), np.int64)
+
+
+def test_accumulate_and_deferred_past_2_31_columns():
+    import torch
+    W, M = 2, BIG + 1003
+    ld = wl.round_up(M, 64)
+    U.say("accumulate + deferred past 2^31", W, M)
+    scale = wl.sigma_scale(1e-3)
+    x = torch.empty((W, ld), dtype=torch.float32, device="cuda")
+    acc = torch.empty((W, ld), dtype=torch.float32, device="cuda")
+    _fill_columns(x, wl.DT_F32, 611, W, ld, 0, M, scale)
+    _fill_columns(acc, wl.DT_F32, 612, W, ld, 0, M, scale)
+    out = torch.empty((W, ld), dtype=torch.float32, device="cuda")
+    dc.dc_accumulate(W, x, ld, acc, ld, M, 0)
+    dc.dc_deferred_reduce(W, acc, ld, out, ld, M, W)
+    torch.cuda.synchronize()
+    cols = _sample(M, [BIG, 4 * (M // 4)], np.random.default_rng(5))   # 2^31 and the ragged tail
+    idx = torch.from_numpy(cols).cuda()
+    got_acc = acc[:, idx].cpu().numpy()
+    got_out = out[:, idx].cpu().numpy()
+    del x, acc, out
+    torch.cuda.empty_cache()
+    hx = _host_columns(wl.DT_F32, 611, W, cols, scale)
+    ha = _host_columns(wl.DT_F32, 612, W, cols, scale)
+    n = len(cols)
+    oracle.accumulate(W, hx, ha, n, 0)
+    hout = np.zeros((W, n), np.float32)
+    oracle.deferred_reduce(W, ha, hout, n, W)
+    assert np.array_equal(got_acc.view(np.uint32), ha.view(np.uint32))
+    assert np.array_equal(got_out.view(np.uint32), hout.view(np.uint32))
+
+
+def test_reduce_scatter_all_gather_past_2_31_columns():
+    import torch
+    W, L = 2, BIG + 64
+    M = W * L
+    U.say("reduce-scatter + all-gather past 2^31", W, L)
+    scale = wl.sigma_scale(1e-2)
+    x = torch.empty((W, M), dtype=torch.int16, device="cuda")
+    _fill_columns(x, wl.DT_BF16, 621, W, M, 0, M, scale)
+    sh = torch.empty((W, L), dtype=torch.int16, device="cuda")
+    dc.dc_reduce_scatter(W, wl.DT_BF16, x, M, sh, L, M, 1)
+    del x
+    out = torch.empty((W, M), dtype=torch.int16, device="cuda")
+    dc.dc_all_gather(W, wl.DT_BF16, sh, L, out, M, L, dc.DC_ORDER_RANK, -1)
+    torch.cuda.synchronize()
+    ks = _sample(L, [BIG - 64, BIG], np.random.default_rng(6))
+    kidx = torch.from_numpy(ks).cuda()
+    got_sh = sh[:, kidx].cpu().numpy().view(np.uint16)
+    # all-gather: node i holds shard s at columns s*L + k
+    for i in range(W):
+        for s in range(W):
+            assert torch.equal(out[i, s * L + kidx], sh[s, kidx]), (i, s)
+    del sh, out
+    torch.cuda.empty_cache()
+    # oracle: a small slab whose shard s column j holds column s*L + ks[j]
+    n = len(ks)
+    small = np.concatenate([_host_columns(wl.DT_BF16, 621, W, s * L + ks, scale) for s in range(W)], axis=1)
+    want = np.zeros((W, n), np.uint16)
+    oracle.reduce_scatter(W, wl.DT_BF16, small, want, W * n, 1)
+    assert np.array_equal(got_sh, want)
