@@ -156,3 +156,134 @@ def test_reduce_scatter_all_gather_past_2_31_columns():
     want = np.zeros((W, n), np.uint16)
     oracle.reduce_scatter(W, wl.DT_BF16, small, want, W * n, 1)
     assert np.array_equal(got_sh, want)
+
+
+def test_zero2_flush_and_relayout_across_column_2_31():
+    """ZeRO-2 routing and the relayout + reduce-scatter-v at flat positions
+    past 2^31: W = 8 bf16, params at flat positions equal to their columns,
+    partition size S = floor(2^31 / 7) + 1, so the boundary between
+    partitions 6 and 7 sits at 7 S = 2^31 + 5, inside the bucket."""
+    import torch
+    W, dtype = 8, wl.DT_BF16
+    sizes = [3000, 1, 2995, 4104, 17, 905]
+    c0 = BIG - 6000
+    numel = sum(sizes)
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int).tolist()
+    P = len(sizes)
+    S = BIG // 7 + 1
+    assert c0 < 7 * S < c0 + numel and 7 * S > BIG
+    flat = np.array([c0 + o for o in offs], np.int64)
+    psize = np.full(P, S, np.int64)
+    ld = wl.round_up(c0 + numel + 1024, 64)
+    U.say("zero2 + relayout past 2^31", W, "S", S)
+    scale = wl.sigma_scale(1e-2)
+    x = torch.empty((W, ld), dtype=torch.int16, device="cuda")
+    _fill_columns(x, dtype, 631, W, ld, c0, numel, scale)
+    y = torch.full((W, ld), U.SENTINEL16, dtype=torch.int16, device="cuda")
+    tasks = dc.tasks_array([(offs[k], sizes[k], k, 0) for k in range(P)])
+    d_tasks = torch.from_numpy(tasks.view(np.uint8).copy()).cuda()
+    dc.dc_flush_bucket_zero2(W, dtype, x, ld, y, ld, c0, numel, d_tasks, P,
+                             torch.from_numpy(flat).cuda(), torch.from_numpy(psize).cuda(), P,
+                             [(W, 1)], 1, 1)
+    pieces, seg = dc.dc_plan_relayout(W, tasks, P, flat, psize, P)
+    n = int(seg[-1])
+    ld_r = wl.round_up(n, 64)
+    relaid = torch.empty((W, ld_r), dtype=torch.int16, device="cuda")
+    d_pieces = torch.from_numpy(pieces.view(np.uint8).copy()).cuda()
+    dc.dc_relayout_bucket(W, dtype, x, ld, relaid, ld_r, c0, numel, d_pieces, len(pieces), n)
+    maxseg = int(max(seg[1:] - seg[:-1]))
+    ld_s = wl.round_up(max(maxseg, 1), 64)
+    shards = torch.full((W, ld_s), U.SENTINEL16, dtype=torch.int16, device="cuda")
+    dc.dc_reduce_scatter_v(W, dtype, relaid, ld_r, shards, ld_s, seg, 1)
+    torch.cuda.synchronize()
+    lo, hi = c0 - 64, c0 + numel + 64
+    got = y[:, lo:hi].cpu().numpy().view(np.uint16)
+    got_sh = shards.cpu().numpy().view(np.uint16)
+    del x, y, relaid, shards
+    torch.cuda.empty_cache()
+    hin = _host_columns(dtype, 631, W, np.arange(lo, hi, dtype=np.int64), scale)
+    hout = np.full_like(hin, U.SENTINEL16)
+    oracle.flush_zero2(W, dtype, hin, hout, c0 - lo, offs, sizes, list(range(P)), [0] * P, flat, psize,
+                       [W], [1], 1)
+    assert np.array_equal(got, hout)
+    # the partitions the bucket spans, and a boundary inside it
+    parts = sorted({int(p) // S for k in range(P) for p in (flat[k], flat[k] + sizes[k] - 1)})
+    assert len(parts) >= 2 and parts[-1] * S > BIG
+    # relayout + reduce-scatter-v: each segment's shard equals the ZeRO-2 flush
+    # at the columns of that partition, in bucket order
+    cols = [(k, e) for k in range(P) for e in range(sizes[k])]
+    by_part = {}
+    for k, e in cols:
+        by_part.setdefault(int(flat[k] + e) // S, []).append(offs[k] + e)
+    for q in range(W):
+        cq = by_part.get(q, [])
+        assert int(seg[q + 1] - seg[q]) == len(cq), q
+        for j, c in enumerate(cq):
+            assert got_sh[q, j] == hout[q, c0 - lo + c], (q, j)
+
+
+def test_ring_reduce_scatter_and_gather_steps_past_2_31_columns():
+    """Ring-order reduce-scatter and the ring and recursive-doubling gather
+    step executors with shards of 2^31 + 64 bf16 columns (W = 2: the ring
+    order folds rank s then s+1, equal to rank order since fp32 addition is
+    commutative)."""
+    import torch
+    W, L = 2, BIG + 64
+    M = W * L
+    U.say("ring reduce-scatter + gather steps past 2^31", W, L)
+    scale = wl.sigma_scale(1e-2)
+    x = torch.empty((W, M), dtype=torch.int16, device="cuda")
+    _fill_columns(x, wl.DT_BF16, 641, W, M, 0, M, scale)
+    sh = torch.empty((W, L), dtype=torch.int16, device="cuda")
+    dc.dc_reduce_scatter_ring(W, wl.DT_BF16, x, M, sh, L, M, 1)
+    torch.cuda.synchronize()
+    ks = _sample(L, [BIG - 64, BIG], np.random.default_rng(7))
+    kidx = torch.from_numpy(ks).cuda()
+    got_sh = sh[:, kidx].cpu().numpy().view(np.uint16)
+    del x
+    torch.cuda.empty_cache()
+    out = torch.full((W, M), U.SENTINEL16, dtype=torch.int16, device="cuda")
+    for algo in (dc.DC_SCHED_RING, dc.DC_SCHED_RD):
+        out.fill_(U.SENTINEL16)
+        for step in range(2):
+            dc.dc_all_gather_step(W, wl.DT_BF16, sh, L, out, M, L, algo, step)
+        torch.cuda.synchronize()
+        for i in range(W):
+            for s in range(W):
+                assert torch.equal(out[i, s * L + kidx], sh[s, kidx]), (algo, i, s)
+    del sh, out
+    torch.cuda.empty_cache()
+    n = len(ks)
+    small = np.concatenate([_host_columns(wl.DT_BF16, 641, W, s * L + ks, scale) for s in range(W)], axis=1)
+    want = np.zeros((W, n), np.uint16)
+    oracle.reduce_scatter_ring(W, wl.DT_BF16, small, want, W * n, 1)
+    assert np.array_equal(got_sh, want)
+
+
+def test_accumulate_reduce_past_2_31_columns():
+    import torch
+    W, M = 2, BIG + 1003
+    ld = wl.round_up(M, 64)
+    U.say("accumulate-reduce past 2^31", W, M)
+    scale = wl.sigma_scale(1e-3)
+    x = torch.empty((W, ld), dtype=torch.float32, device="cuda")
+    acc = torch.empty((W, ld), dtype=torch.float32, device="cuda")
+    _fill_columns(x, wl.DT_F32, 651, W, ld, 0, M, scale)
+    _fill_columns(acc, wl.DT_F32, 652, W, ld, 0, M, scale)
+    out = torch.empty((1, ld), dtype=torch.float32, device="cuda")
+    dc.dc_accumulate_reduce(W, x, ld, acc, ld, 0, 1, out, ld, 1, M)
+    torch.cuda.synchronize()
+    cols = _sample(M, [BIG, 4 * (M // 4)], np.random.default_rng(8))
+    idx = torch.from_numpy(cols).cuda()
+    got_acc = acc[:, idx].cpu().numpy()
+    got_out = out[:, idx].cpu().numpy()
+    del x, acc, out
+    torch.cuda.empty_cache()
+    hx = _host_columns(wl.DT_F32, 651, W, cols, scale)
+    ha = _host_columns(wl.DT_F32, 652, W, cols, scale)
+    n = len(cols)
+    oracle.accumulate(W, hx, ha, n, 0)
+    hout = np.zeros((1, n), np.float32)
+    oracle.deferred_reduce(W, ha, hout, n, 1)
+    assert np.array_equal(got_acc.view(np.uint32), ha.view(np.uint32))
+    assert np.array_equal(got_out.view(np.uint32), hout.view(np.uint32))
