@@ -97,6 +97,16 @@ def owner_workloads():
     out.append(wl.custom_flush("W64-G64-C8", 64, wl.DT_BF16, numel, group_begin=gb,
                                group_comm=gcomm, comms=comms64, capacity=25_000, pre_div=1,
                                value_seed=64))
+    # parameter sizes up to 2^40, group totals far past 2^32: 64-bit offsets,
+    # partition sizes and partition indices (no slab is allocated)
+    numel, gb = [], [0]
+    for g in range(3):
+        numel += [rng.choice([0, 1, 1 << 20, (1 << 40) - 1, 1 << 40, rng.randrange(1 << 40)])
+                  for _ in range(rng.randint(50, 400))]
+        gb.append(len(numel))
+    out.append(wl.custom_flush("W8-sizes-to-2^40", 8, wl.DT_BF16, numel, group_begin=gb,
+                               group_comm=[0, 1, 0], comms=[wl.Comm(8, 1), wl.Comm(4, 2)],
+                               capacity=1 << 46))
     return out
 
 
