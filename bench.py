@@ -131,7 +131,8 @@ def bench_flush(args, w, reduce_to_owner=True, zero2=False):
     synth.fill_slab_device(w.dtype, w.value_seed, 0, w.scale, w.W, ld, w.total, x.data_ptr(),
                            stream.cuda_stream)
     y = torch.zeros((w.W, ld), dtype=dt, device=dev)
-    ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner, log=log, zero2=zero2)
+    ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner, log=log, zero2=zero2,
+                                reduce_probe=args.probe)
     ex.build_owner_map()
     ex.fetch_metadata()
     log("[bench] " + ex.ratio_line())
@@ -841,6 +842,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="deferred workload: fuse the last accumulate into the reduce")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", action="store_true",
+                    help="flush workloads: print the probe line of each of the first 20 flushes "
+                         "(the executor's reduce_probe), as they are issued")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path simulates W data-parallel ranks as rows "
