@@ -41,13 +41,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def flush_bytes(w, owner, psize=None):
+def flush_bytes(w, owner, psize=None, tiles=None):
     """Algorithmic bytes of every flush launch of workload w (ZeRO-2 when
-    psize, the per-param partition size, is given)."""
+    psize, the per-param partition size, is given): every row read, the rows
+    written, 32 bytes per task record and, for a planned flush (tiles: the
+    tile count of each bucket), 16 bytes per tile record."""
     b = w.elem_bytes()
     per = []
-    for bk in w.buckets:
-        tot = 0
+    for i, bk in enumerate(w.buckets):
+        tot = 16 * int(tiles[i]) if tiles is not None else 0
         for t in bk.tasks:
             if psize is not None:
                 one = t.comm == 0 and psize[t.param] > 0
@@ -140,7 +142,12 @@ def bench_flush(args, w, reduce_to_owner=True, zero2=False):
         for b in range(min(len(w.buckets), 3)):
             log("[bench] " + ex.probe_line(b, b))
     owner = ex.h_owner if reduce_to_owner else None
-    per_launch = flush_bytes(w, owner, ex.h_psize if zero2 else None)
+    tiles = None
+    if not args.searched:
+        ex.plan()
+        tiles = np.diff(ex.tile_begin)
+        log(f"[bench] flush plans: {tiles.tolist()} tiles per bucket")
+    per_launch = flush_bytes(w, owner, ex.h_psize if zero2 else None, tiles)
     step_bytes = sum(per_launch) + owner_map_bytes(w)
     nb = len(w.buckets)
 
@@ -842,6 +849,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="deferred workload: fuse the last accumulate into the reduce")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--searched", action="store_true",
+                    help="flush workloads: flush without plans (each tile searches the task "
+                         "table) instead of with the per-bucket tile plans")
     ap.add_argument("--probe", action="store_true",
                     help="flush workloads: print the probe line of each of the first 20 flushes "
                          "(the executor's reduce_probe), as they are issued")
@@ -877,6 +887,8 @@ def main():
                   "bucket_capacity": w.capacity,
                   "mode": "zero2" if zero2 else ("reduce_to_owner" if owner_mode else "allreduce"),
                   "pre_div": w.pre_div, "step": "owner map + every bucket flush",
+                  "flush": ("searched: each tile looks up its tasks" if args.searched else
+                            "planned: per-bucket tile plans built once at init on the host"),
                   "step_bytes": step_bytes}
         if not args.no_cpu_baseline and not zero2:
             # the whole step when its slab fits a few GB of host memory (about 20 s

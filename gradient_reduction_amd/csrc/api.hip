@@ -214,7 +214,9 @@ dc_status flush_common(const char* fn, int32_t W, int32_t dtype, const void* sla
                        void* slab_out, int64_t ld_out, int64_t bucket_col, int64_t bucket_numel,
                        const dc_task* tasks, int32_t num_tasks, const int32_t* owner,
                        const int64_t* flat, const int64_t* psize, int32_t num_params,
-                       const dc_comm* comms, int32_t num_comms, int32_t pre_div, void* stream) {
+                       const dc_comm* comms, int32_t num_comms, int32_t pre_div, void* stream,
+                       const dc_tile* tiles = nullptr, int64_t num_tiles = -1,
+                       int64_t root_tiles = 0) {
   dc_status st;
   if ((st = check_w(W)) || (st = check_dtype(dtype)) || (st = check_comms(W, comms, num_comms))) return st;
   if (bucket_col < 0 || bucket_numel < 0)
@@ -232,6 +234,13 @@ dc_status flush_common(const char* fn, int32_t W, int32_t dtype, const void* sla
     if (ld_in != ld_out) return fail(DC_ERR_ARG, "in-place flush needs ld_in == ld_out");
   } else if (overlaps(slab_in, W * ld_in * b, slab_out, W * ld_out * b)) {
     return fail(DC_ERR_ARG, "slab_in and slab_out overlap without being the same slab");
+  }
+  if (num_tiles >= 0) {  // planned
+    const int64_t want = dc::flush_tiles(dtype, bucket_col, end).count;
+    if (tiles == nullptr && want > 0) return fail(DC_ERR_NULL, "tiles is NULL");
+    if (num_tiles != want)
+      return fail(DC_ERR_SHAPE, "num_tiles=%lld, the bucket has %lld tiles", (long long)num_tiles,
+                  (long long)want);
   }
   dc::FlushLaunch a{};
   a.W = W;
@@ -251,6 +260,9 @@ dc_status flush_common(const char* fn, int32_t W, int32_t dtype, const void* sla
   a.nparams = num_params;
   a.ncomms = num_comms;
   for (int k = 0; k < num_comms; ++k) a.comms[k] = {comms[k].size, comms[k].stride};
+  a.tiles = num_tiles >= 0 ? tiles : nullptr;
+  a.ntiles = num_tiles >= 0 ? num_tiles : 0;
+  a.root_tiles = num_tiles >= 0 ? root_tiles : 0;
   return hip_status(dc::launch_flush(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -279,6 +291,101 @@ dc_status dc_flush_bucket_zero2(int32_t W, int32_t dtype, const void* slab_in, i
   return flush_common("ZeRO-2 flush launch", W, dtype, slab_in, ld_in, slab_out, ld_out,
                       bucket_col, bucket_numel, tasks, num_tasks, nullptr, flat_offset, part_size,
                       num_params, comms, num_comms, pre_div, stream);
+}
+
+dc_status dc_flush_bucket_planned(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                                  void* slab_out, int64_t ld_out, int64_t bucket_col,
+                                  int64_t bucket_numel, const dc_task* tasks, int32_t num_tasks,
+                                  const int32_t* owner, const int64_t* flat_offset,
+                                  const int64_t* part_size, int32_t num_params,
+                                  const dc_comm* comms, int32_t num_comms, int32_t pre_div,
+                                  const dc_tile* tiles, int64_t num_tiles, int64_t root_tiles,
+                                  void* stream) {
+  if ((flat_offset == nullptr) != (part_size == nullptr))
+    return fail(DC_ERR_NULL, "flat_offset and part_size go together");
+  if (flat_offset != nullptr && owner != nullptr)
+    return fail(DC_ERR_ARG, "ZeRO-2 mode (flat_offset given) takes no owner map");
+  dc_status st;
+  if ((st = check_extent("num_tiles", num_tiles))) return st;
+  if (num_tiles < 0) return fail(DC_ERR_ARG, "num_tiles < 0");
+  if (root_tiles < 0 || root_tiles > num_tiles)
+    return fail(DC_ERR_ARG, "root_tiles=%lld outside [0, num_tiles=%lld]", (long long)root_tiles,
+                (long long)num_tiles);
+  return flush_common("planned flush launch", W, dtype, slab_in, ld_in, slab_out, ld_out,
+                      bucket_col, bucket_numel, tasks, num_tasks, owner, flat_offset, part_size,
+                      num_params, comms, num_comms, pre_div, stream, tiles, num_tiles, root_tiles);
+}
+
+dc_status dc_plan_flush(int32_t W, int32_t dtype, int64_t bucket_col, int64_t bucket_numel,
+                        const dc_task* tasks, int32_t num_tasks, const int32_t* owner,
+                        const int64_t* flat_offset, const int64_t* part_size, int32_t num_params,
+                        const dc_comm* comms, int32_t num_comms, dc_tile* tiles,
+                        int64_t capacity, int64_t* num_tiles, int64_t* root_tiles) {
+  dc_status st;
+  if ((st = check_dtype(dtype))) return st;
+  if (num_tiles == nullptr) return fail(DC_ERR_NULL, "num_tiles is NULL");
+  if (bucket_col < 0 || bucket_numel < 0)
+    return fail(DC_ERR_ARG, "bucket_col=%lld, bucket_numel=%lld", (long long)bucket_col, (long long)bucket_numel);
+  if ((st = check_extent("bucket_col", bucket_col)) || (st = check_extent("bucket_numel", bucket_numel)))
+    return st;
+  if ((flat_offset == nullptr) != (part_size == nullptr))
+    return fail(DC_ERR_NULL, "flat_offset and part_size go together");
+  if (flat_offset != nullptr && owner != nullptr)
+    return fail(DC_ERR_ARG, "ZeRO-2 mode (flat_offset given) takes no owner map");
+  if ((st = dc_validate_tasks(W, tasks, num_tasks, bucket_numel, num_params, comms, num_comms)))
+    return st;
+  const int64_t c0 = bucket_col, c1 = bucket_col + bucket_numel;
+  const dc::FlushTiles g = dc::flush_tiles(dtype, c0, c1);
+  *num_tiles = g.count;
+  if (tiles == nullptr) return ok();  // size query
+  int64_t roots = 0;
+  if (capacity < g.count)
+    return fail(DC_ERR_SHAPE, "capacity=%lld < %lld tiles", (long long)capacity, (long long)g.count);
+  if (g.count > 0 && num_tasks == 0) {
+    for (int64_t b = 0; b < g.count; ++b) tiles[b] = dc_tile{0, -1, -1, 0};
+    if (root_tiles != nullptr) *root_tiles = 0;
+    return ok();
+  }
+  const int64_t E = dtype == DC_BF16 ? 8 : 4;
+  // tasks are sorted and packed: walk them alongside the tiles
+  int32_t k = 0;
+  for (int64_t b = 0; b < g.count; ++b) {
+    const int64_t t0 = b * g.tile, t1 = std::min(t0 + g.tile, g.nv);
+    const int64_t f_lo = (g.v0 + t0) * E - c0, f_hi = (g.v0 + t1) * E - c0;
+    const int64_t lo = std::max(f_lo, (int64_t)0), hi = std::min(f_hi, bucket_numel);
+    // first: the last task starting at or before lo; last: the last starting before hi
+    while (k + 1 < num_tasks && tasks[k + 1].offset <= lo) ++k;
+    int32_t last = k;
+    while (last + 1 < num_tasks && tasks[last + 1].offset < hi) ++last;
+    if (tasks[0].offset >= hi) last = -1;
+    dc_tile rec{k, last, -1, 0};
+    const dc_task& t = tasks[k];
+    if (last == k && f_lo >= 0 && f_hi <= bucket_numel && t.offset <= f_lo && f_hi <= t.offset + t.numel) {
+      int32_t root = -1;
+      bool whole = true;
+      if (t.comm == 0) {
+        if (flat_offset != nullptr) {
+          const int64_t S = part_size[t.param];
+          if (S > 0) {
+            const int64_t a = flat_offset[t.param];
+            const int64_t q0 = (a + (f_lo - t.offset)) / S, q1 = (a + (f_hi - 1 - t.offset)) / S;
+            if (q0 == q1 && q0 >= 0 && q0 < W) root = (int32_t)q0;
+            else whole = false;
+          }
+        } else if (owner != nullptr && owner[t.param] >= 0 && owner[t.param] < W) {
+          root = owner[t.param];
+        }
+      }
+      if (whole) {
+        rec.root = root;
+        rec.flags = 1 | (t.comm << 8);
+        roots += root >= 0;
+      }
+    }
+    tiles[b] = rec;
+  }
+  if (root_tiles != nullptr) *root_tiles = roots;
+  return ok();
 }
 
 dc_status dc_flush_bucket_buffers(int32_t W, int32_t dtype, int64_t bucket_numel,

@@ -20,6 +20,8 @@
 // then streams its vectors: W 16-byte row loads, an fp32 fold in rank order,
 // one 16-byte store to the owner row or W stores (AllReduce).  This is a
 // streaming reduction with no reuse: no MFMA, HBM bound.
+#include <atomic>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -63,6 +65,8 @@ struct FlushParams {
   int32_t csize[DC_MAX_COMMS];
   int32_t cstride[DC_MAX_COMMS];
   float cinv[DC_MAX_COMMS];  // 1/c when c is a power of two, else 0
+  const dc_tile* tiles;      // planned flush: one record per tile, else NULL
+  int64_t root_tiles;        // planned: tiles that write one row (host side: the launch shape)
 };
 
 // Pre-division modes: none, multiply by an exact power-of-two reciprocal
@@ -284,9 +288,39 @@ __global__ __launch_bounds__(kFT) void k_flush(FlushParams p) {
   const int64_t hi = min((p.v0 + t1) * E, p.c1) - p.c0;
 
   int32_t first, last;
-  kary_bounds<kFT>(p.ntasks, [&](int32_t i) { return p.tasks[i].offset; }, lo, hi, first, last);
-  first = max(first - 1, 0);  // the task holding column lo
-  last = last - 1;            // the last task starting before hi
+  if (p.tiles != nullptr) {
+    // planned: the tile's record replaces the search; a tile inside one task
+    // streams straight away (record fields clamped to their ranges)
+    const dc_tile rec = p.tiles[tile];
+    if (rec.flags & 1) {
+      int32_t comm = (rec.flags >> 8) & 0xFF;
+      comm = comm < p.ncomms ? comm : 0;
+      const int32_t root = (comm == 0 && rec.root >= 0 && rec.root < p.W) ? rec.root : -1;
+      int32_t fc, fs;
+      float finv;
+      comm_shape(p, comm, fc, fs, finv);
+#pragma unroll 1
+      for (int u = 0; u < U; ++u) {
+        const int64_t tv = t0 + threadIdx.x + (int64_t)u * kFT;
+        if (tv >= t1) break;
+        const int64_t av = p.v0 + tv;
+        if constexpr (WT > 0) {
+          u32x4 x[WT];
+          load_rows<BF16, WT, NT>(p, av, x);
+          fold_store_shape<BF16, WT, C2, S2, PRE>(p, x, av, root, fc);
+        } else {
+          vec_generic<BF16, NT>(p, av, root, fc, fs, finv);
+        }
+      }
+      return;
+    }
+    first = max(rec.first, 0);
+    last = min(rec.last, p.ntasks - 1);
+  } else {
+    kary_bounds<kFT>(p.ntasks, [&](int32_t i) { return p.tasks[i].offset; }, lo, hi, first, last);
+    first = max(first - 1, 0);  // the task holding column lo
+    last = last - 1;            // the last task starting before hi
+  }
 
   for (int32_t base = first; base <= last; base += kStage) {
     const int32_t cnt = min(kStage, last - base + 1);
@@ -404,6 +438,55 @@ __global__ __launch_bounds__(kFT) void k_flush(FlushParams p) {
   }
 }
 
+// Workgroups kept resident per compute unit by a planned launch (0: no cap).
+// The one-wave workgroups of a planned tile stream with no search in front,
+// and fewer of them in flight at once measured faster than a full compute
+// unit: at W = 8, about 64 KB of row loads per compute unit (8 workgroups)
+// for tiles that write one row, and 32 KB (4) for tiles that write all eight,
+// whose stores take their own share of the memory system; at W = 16 (fp32
+// measured), 6 and 3.
+int planned_cap(int32_t W, bool one_row) {
+  if (W >= 16) return one_row ? 6 : 3;
+  if (W >= 8) return one_row ? 8 : 4;
+  if (W >= 4) return one_row ? 16 : 12;
+  return 0;
+}
+
+// Dynamic LDS a launch of one k_flush instantiation reserves, unused, so
+// that at most `cap` of its workgroups fit in one compute unit's LDS.  Cached
+// per device and cap (one cache per instantiation; filled once, read after).
+struct PadCache {
+  std::atomic<int32_t> v[16][17];
+  PadCache() {
+    for (auto& row : v)
+      for (auto& x : row) x.store(-1, std::memory_order_relaxed);
+  }
+};
+
+template <bool BF16, int WT, int C2, int S2, int PRE, bool Z2>
+size_t flush_pad(int cap) {
+  static PadCache cache;
+  if (cap <= 0 || cap > 16) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
+  const int32_t hit = cache.v[dev][cap].load(std::memory_order_relaxed);
+  if (hit >= 0) return (size_t)hit;
+  int lds_cu = 0;
+  hipFuncAttributes fa;
+  auto kern = k_flush<BF16, WT, C2, S2, PRE, DC_FLUSH_U, DC_FLUSH_NT != 0, Z2>;
+  if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+          hipSuccess ||
+      hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern)) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int64_t per_wg = (int64_t)(lds_cu / cap) / 256 * 256;
+  const int64_t pad = per_wg - (int64_t)fa.sharedSizeBytes;
+  const int32_t v = pad > 0 ? (int32_t)pad : 0;
+  cache.v[dev][cap].store(v, std::memory_order_relaxed);
+  return (size_t)v;
+}
+
 template <bool BF16, int WT, int C2, int S2, int PRE>
 hipError_t launch_kernel(const FlushParams& p, hipStream_t stream) {
   constexpr int U = DC_FLUSH_U;
@@ -412,18 +495,21 @@ hipError_t launch_kernel(const FlushParams& p, hipStream_t stream) {
   // have every wave's 1 KB straddle lines, sharing partial lines between
   // neighbouring tiles (measured 15% slower on such buckets).  Vectors in
   // front of the bucket fall outside its columns and are skipped.
+  const FlushTiles g = flush_tiles(BF16 ? DC_BF16 : DC_F32, p.c0, p.c1);
+  if (g.count == 0) return hipSuccess;
   FlushParams q = p;
-  const int64_t shift = p.v0 % (kFT * U);
-  q.v0 = p.v0 - shift;
-  q.nv = p.nv + shift;
-  const int64_t blocks = (q.nv + kFT * U - 1) / (kFT * U);
-  if (blocks == 0) return hipSuccess;
-  if (q.flat != nullptr)
+  q.v0 = g.v0;
+  q.nv = g.nv;
+  const int cap = p.tiles != nullptr ? planned_cap(p.W, 2 * p.root_tiles >= g.count) : 0;
+  if (q.flat != nullptr) {
+    const size_t pad = flush_pad<BF16, WT, C2, S2, PRE, true>(cap);
     hipLaunchKernelGGL((k_flush<BF16, WT, C2, S2, PRE, U, DC_FLUSH_NT != 0, true>),
-                       dim3((unsigned)blocks), dim3(kFT), 0, stream, q);
-  else
+                       dim3((unsigned)g.count), dim3(kFT), pad, stream, q);
+  } else {
+    const size_t pad = flush_pad<BF16, WT, C2, S2, PRE, false>(cap);
     hipLaunchKernelGGL((k_flush<BF16, WT, C2, S2, PRE, U, DC_FLUSH_NT != 0, false>),
-                       dim3((unsigned)blocks), dim3(kFT), 0, stream, q);
+                       dim3((unsigned)g.count), dim3(kFT), pad, stream, q);
+  }
   return hipGetLastError();
 }
 
@@ -513,8 +599,23 @@ hipError_t launch_flush(const FlushLaunch& a, hipStream_t stream) {
     p.cstride[k] = k < a.ncomms ? a.comms[k].stride : 1;
     p.cinv[k] = (c & (c - 1)) == 0 ? 1.0f / (float)c : 0.0f;  // exact for powers of two
   }
+  p.tiles = a.tiles;
+  p.root_tiles = a.root_tiles;
   if (p.nv == 0 || a.ntasks == 0) return hipSuccess;
   return a.dtype == DC_BF16 ? launch_dtype<true>(p, stream) : launch_dtype<false>(p, stream);
+}
+
+FlushTiles flush_tiles(int32_t dtype, int64_t c0, int64_t c1) {
+  static_assert(kFT * DC_FLUSH_U == 128, "the public tile record documents 128-vector tiles");
+  const int64_t E = dtype == DC_BF16 ? 8 : 4;
+  FlushTiles g;
+  g.tile = (int64_t)kFT * DC_FLUSH_U;
+  const int64_t first = c0 / E;
+  const int64_t shift = first % g.tile;
+  g.v0 = first - shift;
+  g.nv = c1 > c0 ? (c1 + E - 1) / E - first + shift : 0;
+  g.count = (g.nv + g.tile - 1) / g.tile;
+  return g;
 }
 
 }  // namespace dc

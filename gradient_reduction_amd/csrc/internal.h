@@ -32,9 +32,23 @@ struct FlushLaunch {
   int32_t nparams;
   int32_t ncomms;
   CommSpec comms[DC_MAX_COMMS];
+  const dc_tile* tiles;  // planned flush when non-null (ntiles records)
+  int64_t ntiles;
+  int64_t root_tiles;    // planned: tiles that write one row (picks the occupancy)
 };
 
 hipError_t launch_flush(const FlushLaunch& a, hipStream_t stream);
+
+// The flush kernel's tile grid over bucket columns [c0, c1) of a dtype: tile
+// b covers vectors [v0 + b*tile, v0 + min((b+1)*tile, nv)) in absolute
+// 16-byte column vectors.  Returns the tile count (0 for an empty bucket).
+struct FlushTiles {
+  int64_t v0;    // first vector of tile 0 (a multiple of the tile size)
+  int64_t nv;    // vectors from v0 to the bucket's last one
+  int64_t tile;  // vectors per tile
+  int64_t count;
+};
+FlushTiles flush_tiles(int32_t dtype, int64_t c0, int64_t c1);
 
 struct GroupTable {
   int32_t num_groups;

@@ -27,6 +27,7 @@ TASK_DTYPE = np.dtype([("offset", "<i8"), ("numel", "<i8"), ("param", "<i4"),
                        ("comm", "<i4"), ("reserved", "<i8")])
 COMM_DTYPE = np.dtype([("size", "<i4"), ("stride", "<i4")])
 PIECE_DTYPE = np.dtype([("src", "<i8"), ("dst", "<i8"), ("len", "<i8"), ("reserved", "<i8")])
+TILE_DTYPE = np.dtype([("first", "<i4"), ("last", "<i4"), ("root", "<i4"), ("flags", "<i4")])
 
 
 class dc_probe(ctypes.Structure):
@@ -59,6 +60,10 @@ _SIGS = {
     "dc_validate_buffer_tasks": ([_i32, _i32, _vp, _i32, _i64, _vp, _i32, _vp, _vp], _i32),
     "dc_flush_bucket_zero2": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
                                _i32, _vp, _i32, _i32, _vp], _i32),
+    "dc_plan_flush": ([_i32, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i64,
+                       _vp, _vp], _i32),
+    "dc_flush_bucket_planned": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
+                                 _vp, _i32, _vp, _i32, _i32, _vp, _i64, _i64, _vp], _i32),
     "dc_probe_flush": ([_i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp], _i32),
     "dc_plan_relayout": ([_i32, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp], _i32),
     "dc_relayout_bucket": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp],
@@ -220,6 +225,36 @@ def dc_probe_flush(W, dtype, tasks, num_tasks, owner, num_params, pid_offsets, p
     _check("dc_probe_flush", lib().dc_probe_flush(W, dtype, tp, num_tasks, op, num_params, po, pp,
                                                   cp, num_comms, pre_div, ctypes.byref(out)))
     return out
+
+
+def dc_plan_flush(W, dtype, bucket_col, bucket_numel, tasks, num_tasks, owner, flat_offset,
+                  part_size, num_params, comms, num_comms):
+    """Host only; returns (dc_tile records as TILE_DTYPE, root tile count).
+    Asks for the tile count first, then fills an array of that size."""
+    tp, _a = _host(tasks, TASK_DTYPE)
+    op, _b = _host(owner, np.int32)
+    fo, _c = _host(flat_offset, np.int64)
+    ps, _d = _host(part_size, np.int64)
+    cp, _e = _host(comms, COMM_DTYPE)
+    n, r = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check("dc_plan_flush", lib().dc_plan_flush(
+        W, dtype, bucket_col, bucket_numel, tp, num_tasks, op, fo, ps, num_params, cp, num_comms,
+        None, 0, ctypes.byref(n), None))
+    tiles = np.zeros(max(n.value, 1), TILE_DTYPE)
+    _check("dc_plan_flush", lib().dc_plan_flush(
+        W, dtype, bucket_col, bucket_numel, tp, num_tasks, op, fo, ps, num_params, cp, num_comms,
+        tiles.ctypes.data_as(_vp), n.value, ctypes.byref(n), ctypes.byref(r)))
+    return tiles[:n.value].copy(), r.value
+
+
+def dc_flush_bucket_planned(W, dtype, slab_in, ld_in, slab_out, ld_out, bucket_col, bucket_numel,
+                            tasks, num_tasks, owner, flat_offset, part_size, num_params, comms,
+                            num_comms, pre_div, tiles, num_tiles, root_tiles, stream=None):
+    cp, _a = _host(comms, COMM_DTYPE)
+    _check("dc_flush_bucket_planned", lib().dc_flush_bucket_planned(
+        W, dtype, _dev(slab_in), ld_in, _dev(slab_out), ld_out, bucket_col, bucket_numel,
+        _dev(tasks), num_tasks, _dev(owner), _dev(flat_offset), _dev(part_size), num_params, cp,
+        num_comms, pre_div, _dev(tiles), num_tiles, root_tiles, _stream(stream)))
 
 
 def dc_plan_relayout(W, tasks, num_tasks, flat_offset, part_size, num_params):

@@ -71,6 +71,9 @@ class Zero1FlushExecutor:
         raw = torch.from_numpy(allt.view(np.uint8).copy())
         self.d_tasks = raw.to(dev) if len(allt) else torch.empty(32, dtype=torch.uint8, device=dev)
         self.h_owner: Optional[np.ndarray] = None
+        self.d_tiles = None        # flush plans (plan()), one table for all buckets
+        self.tile_begin = None
+        self.root_tiles = None
         # ZeRO-2: the partition size of each param's group, 0 for groups on
         # another communicator (they keep AllReduce)
         psize = np.zeros(max(self.P, 1), np.int64)
@@ -108,9 +111,53 @@ class Zero1FlushExecutor:
     def task_table(self, b: int) -> int:
         return self.d_tasks.data_ptr() + 32 * int(self.t_begin[b])
 
+    def plan(self) -> None:
+        """Plan every bucket's flush on the host (dc_plan_flush: per tile, the
+        tasks it overlaps and, for a tile inside one task, its rows), from
+        the owner map (or the ZeRO-2 partition sizes), and keep the plans on
+        the device; flush() then takes the planned path.  Synchronizes: call
+        it at init, after build_owner_map, not while a graph is captured."""
+        torch = self.torch
+        if self.h_owner is None:
+            self.fetch_metadata()
+        flat = self.d_flat[:self.P].cpu().numpy() if self.zero2 else None
+        recs, self.root_tiles = [], []
+        for b, bk in enumerate(self.buckets):
+            t = self.h_tasks[b]
+            if self.zero2:
+                tiles, roots = dc.dc_plan_flush(self.W, self.dtype, bk.col, bk.numel, t, len(t), None,
+                                                flat, self.h_psize, self.P, self.comms,
+                                                len(self.comms))
+            else:
+                owner = self.h_owner if self.reduce_to_owner else None
+                tiles, roots = dc.dc_plan_flush(self.W, self.dtype, bk.col, bk.numel, t, len(t),
+                                                owner, None, None, self.P, self.comms,
+                                                len(self.comms))
+            recs.append(tiles)
+            self.root_tiles.append(roots)
+        self.tile_begin = np.concatenate([[0], np.cumsum([len(r) for r in recs])]).astype(int)
+        allr = np.concatenate(recs) if recs else np.zeros(0, dc.TILE_DTYPE)
+        raw = torch.from_numpy(allr.view(np.uint8).copy()) if len(allr) else torch.zeros(16, dtype=torch.uint8)
+        self.d_tiles = raw.to(self.d_tasks.device)
+
     def flush(self, b: int, slab_in, ld_in: int, slab_out, ld_out: int, stream=None) -> None:
         bk = self.buckets[b]
-        if self.zero2:
+        if self.d_tiles is not None:
+            nt = int(self.tile_begin[b + 1] - self.tile_begin[b])
+            tp = self.d_tiles.data_ptr() + 16 * int(self.tile_begin[b])
+            if self.zero2:
+                dc.dc_flush_bucket_planned(self.W, self.dtype, slab_in, ld_in, slab_out, ld_out,
+                                           bk.col, bk.numel, self.task_table(b), len(bk.tasks), None,
+                                           self.d_flat, self.d_psize, self.P, self.comms,
+                                           len(self.comms), self.pre_div, tp, nt,
+                                           self.root_tiles[b], stream)
+            else:
+                owner = self.d_owner if self.reduce_to_owner else None
+                dc.dc_flush_bucket_planned(self.W, self.dtype, slab_in, ld_in, slab_out, ld_out,
+                                           bk.col, bk.numel, self.task_table(b), len(bk.tasks), owner,
+                                           None, None, self.P, self.comms, len(self.comms),
+                                           self.pre_div, tp, nt, self.root_tiles[b], stream)
+        elif self.zero2:
             dc.dc_flush_bucket_zero2(self.W, self.dtype, slab_in, ld_in, slab_out, ld_out, bk.col,
                                      bk.numel, self.task_table(b), len(bk.tasks), self.d_flat,
                                      self.d_psize, self.P, self.comms, len(self.comms),

@@ -125,6 +125,27 @@ typedef struct {
   int64_t reserved;
 } dc_piece;
 
+/* One tile of a planned bucket flush (dc_plan_flush): the flush kernel cuts
+ * a bucket into tiles of 128 consecutive 16-byte column vectors (2 KiB of
+ * each row; tile b of a bucket starting at column c covers the row's vectors
+ * [v0 + 128 b, v0 + 128 (b + 1)), v0 = floor(c / E / 128) * 128 with E
+ * elements per vector, clipped to the bucket's last vector), and this record
+ * says which tasks a tile overlaps and, when the whole tile lies inside one
+ * task and the bucket, which rows receive its sums.  16 bytes.
+ *   first, last   indices of the first and last task overlapping the tile
+ *                 (last < first: none)
+ *   root          whole tile inside one task: the row that alone receives
+ *                 the sums (the owner, or under ZeRO-2 the partition's rank),
+ *                 or -1 for every member of each block (AllReduce)
+ *   flags         bit 0: the whole tile lies inside task `first` and the
+ *                 bucket; bits 8..15: that task's communicator */
+typedef struct {
+  int32_t first;
+  int32_t last;
+  int32_t root;
+  int32_t flags;
+} dc_tile;
+
 /* Library version string (static storage). */
 const char* dc_version(void);
 
@@ -245,6 +266,65 @@ dc_status dc_flush_bucket_zero2(int32_t W, int32_t dtype, const void* slab_in, i
                                 const int64_t* flat_offset, const int64_t* part_size,
                                 int32_t num_params, const dc_comm* comms, int32_t num_comms,
                                 int32_t pre_div, void* stream);
+
+/* Plan of a bucket flush ([DS] Design points: the roots of a bucket's
+ * collectives are computed for the whole bucket before any reduction).
+ * Host only, once per bucket layout: for every tile of the flush kernel's
+ * grid over columns [bucket_col, bucket_col + bucket_numel), the tasks it
+ * overlaps and, for a tile inside one task, the rows its sums go to:
+ *   owner-map mode (flat_offset == NULL): the owner owner[param] of a task on
+ *   comm 0 when owner is given and the entry lies in [0, W), else -1;
+ *   ZeRO-2 mode (flat_offset and part_size given, owner NULL): for a task on
+ *   comm 0 whose param has part_size S > 0, the partition
+ *   floor((flat_offset[param] + e) / S) when every element e of the tile
+ *   lies in the same one inside [0, W) (otherwise the tile is not whole),
+ *   else -1.
+ *   tasks, num_tasks      host dc_task[num_tasks]; must pass dc_validate_tasks
+ *                         (else DC_ERR_TASKS)
+ *   owner                 host int32[num_params] or NULL
+ *   flat_offset, part_size host int64[num_params] or NULL (ZeRO-2)
+ *   comms, num_comms      host, as for dc_flush_bucket
+ *   tiles, capacity       host dc_tile[capacity] out; NULL asks for the count
+ *   num_tiles             out: the tile count, a function of dtype,
+ *                         bucket_col and bucket_numel only
+ *   root_tiles            out (may be NULL): tiles whose sums go to one row
+ *                         (whole tiles with root >= 0), set with the tiles
+ * Fewer than *num_tiles slots is DC_ERR_SHAPE.  The plan stays valid while
+ * the layout, owner map (or partition sizes) and dtype stay the same. */
+dc_status dc_plan_flush(int32_t W, int32_t dtype, int64_t bucket_col, int64_t bucket_numel,
+                        const dc_task* tasks, int32_t num_tasks, const int32_t* owner,
+                        const int64_t* flat_offset, const int64_t* part_size, int32_t num_params,
+                        const dc_comm* comms, int32_t num_comms, dc_tile* tiles,
+                        int64_t capacity, int64_t* num_tiles, int64_t* root_tiles);
+
+/* Bucket flush with a plan (dc_plan_flush): the same results, bit for bit,
+ * as dc_flush_bucket (flat_offset == NULL) or dc_flush_bucket_zero2
+ * (flat_offset and part_size given, owner NULL) with the same arguments.  A
+ * tile the plan marks whole streams its vectors with no per-tile search of
+ * the task table; the launch also keeps fewer workgroups resident per
+ * compute unit (it reserves LDS it does not use), which fewer, longer
+ * streams of loads in flight at once measured faster for this access mix.
+ *   tiles, num_tiles   device dc_tile[num_tiles] from dc_plan_flush for this
+ *                      bucket, dtype, layout and map; num_tiles must equal
+ *                      the planned count (else DC_ERR_SHAPE)
+ *   root_tiles         the count dc_plan_flush reported, in [0, num_tiles]
+ *                      (else DC_ERR_ARG); it only picks the launch shape:
+ *                      buckets whose tiles mostly write one row keep more
+ *                      workgroups per compute unit than those that write
+ *                      every row, and any value gives the same results
+ * Other arguments and checks as in dc_flush_bucket.  The plan is read on
+ * the device and not checked: a stale or altered plan can give wrong sums,
+ * and write columns of slab_out's rows outside the bucket, but never makes
+ * the kernel touch memory outside the two slabs' W rows of ld columns (task
+ * indices, roots and communicators are clamped to their ranges). */
+dc_status dc_flush_bucket_planned(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                                  void* slab_out, int64_t ld_out, int64_t bucket_col,
+                                  int64_t bucket_numel, const dc_task* tasks, int32_t num_tasks,
+                                  const int32_t* owner, const int64_t* flat_offset,
+                                  const int64_t* part_size, int32_t num_params,
+                                  const dc_comm* comms, int32_t num_comms, int32_t pre_div,
+                                  const dc_tile* tiles, int64_t num_tiles, int64_t root_tiles,
+                                  void* stream);
 
 /* Bucket flush with copy-in and copy-out fused in ([DS] problem statement:
  * gradients enter the bucket from every rank and, after the reduction, the

@@ -338,3 +338,143 @@ def test_header_is_plain_c(tmp_path):
                         "-I", os.path.join(ROOT, "include"), str(src), "-o",
                         str(tmp_path / "h.o")], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def _brute_plan(W, dtype, col0, numel, tasks, owner, flat, psize):
+    """The tile records as the header defines them, from a per-column task
+    index: tile b covers vectors [v0 + 128 b, v0 + 128 (b + 1)) clipped to
+    the bucket's last vector."""
+    E = 8 if dtype == wl.DT_BF16 else 4
+    first_v = col0 // E
+    v0 = first_v - first_v % 128
+    v_end = -(-(col0 + numel) // E)
+    count = -(-(v_end - v0) // 128) if numel > 0 else 0
+    tid = np.repeat(np.arange(len(tasks)), tasks["numel"])          # task of each bucket column
+    out = np.zeros(count, dc.TILE_DTYPE)
+    for b in range(count):
+        f_lo = (v0 + 128 * b) * E - col0
+        f_hi = (v0 + min(128 * (b + 1), v_end - v0)) * E - col0
+        ids = tid[max(f_lo, 0):min(f_hi, numel)]
+        first, last = int(ids.min()), int(ids.max())
+        root, flags = -1, 0
+        whole = first == last and f_lo >= 0 and f_hi <= numel
+        if whole:
+            k = first
+            p, c = int(tasks["param"][k]), int(tasks["comm"][k])
+            if c == 0 and flat is not None and psize[p] > 0:
+                a = int(flat[p]) - int(tasks["offset"][k])
+                q0, q1 = (a + f_lo) // int(psize[p]), (a + f_hi - 1) // int(psize[p])
+                if q0 == q1 and 0 <= q0 < W:
+                    root = q0
+                else:
+                    whole = False
+            elif c == 0 and owner is not None and 0 <= owner[p] < W:
+                root = int(owner[p])
+            flags = 1 | (c << 8) if whole else 0
+            root = root if whole else -1
+        out[b] = (first, last, root, flags)
+    return out
+
+
+def test_plan_flush_matches_definition():
+    """dc_plan_flush (host code) against the tile records the header
+    defines, built from a per-column task index: small and random workloads
+    with every bucket-start residue, owner map on and off, and ZeRO-2."""
+    ws = [wl.tiny_flush()]
+    rng = random.Random(8)
+    for k in range(8):
+        W = rng.choice([1, 2, 3, 4, 8, 16])
+        dtype = rng.choice([wl.DT_BF16, wl.DT_F32])
+        sizes = [rng.choice([0, 1, 7, 8, 9, 500, 1023, 1024, 1025, 4000, 9000]) for _ in range(120)]
+        ws.append(wl.custom_flush(f"r{k}", W, dtype, sizes, group_begin=[0, 70, 120],
+                                  group_comm=[0, 1 if W > 1 else 0],
+                                  comms=[wl.Comm(W, 1), wl.Comm(1, W) if W > 1 else wl.Comm(1, 1)],
+                                  capacity=rng.choice([3000, 20_000, 10 ** 6])))
+    for w in ws:
+        flat, ps, off, pids = oracle.partition_ids(w.numel, w.group_begin, w.group_parts())
+        comm_sizes = [w.comms[c].size for c in w.group_comm]
+        elig = oracle.group_eligible(w.W, comm_sizes, w.group_rank_to_global())
+        owner, _ = oracle.owner_map(off, pids, w.group_begin, elig)
+        psize = np.zeros(w.P, np.int64)
+        for g in range(w.G):
+            if elig[g]:
+                psize[w.group_begin[g]:w.group_begin[g + 1]] = ps[g]
+        comms = [(c.size, c.stride) for c in w.comms]
+        for bk in w.buckets[:10]:
+            t = dc.tasks_array([(x.offset, x.numel, x.param, x.comm) for x in bk.tasks])
+            for col0 in (bk.col, bk.col + rng.randint(1, 15)):
+                for own, fl, pz in ((None, None, None), (owner, None, None), (None, flat, psize)):
+                    got, roots = dc.dc_plan_flush(w.W, w.dtype, col0, bk.numel, t, len(t), own, fl,
+                                                  pz, w.P, comms, len(comms))
+                    want = _brute_plan(w.W, w.dtype, col0, bk.numel, t, own, fl, pz)
+                    assert np.array_equal(got, want), (w.name, col0, own is None, fl is None)
+                    assert roots == int(np.sum(want["root"] >= 0))
+
+
+def test_plan_flush_headline_tiles_all_whole():
+    """On the 402.8M-parameter W=8 bf16 layout every tile lies inside one task
+    (tensors and buckets fall on 1024-element steps), and the roots are the
+    owners the oracle's owner map names."""
+    w = wl.owner_flush_w8()
+    _, _, off, pids = oracle.partition_ids(w.numel, w.group_begin, w.group_parts())
+    elig = oracle.group_eligible(w.W, [w.comms[c].size for c in w.group_comm], w.group_rank_to_global())
+    owner, _ = oracle.owner_map(off, pids, w.group_begin, elig)
+    comms = [(c.size, c.stride) for c in w.comms]
+    total = 0
+    for bk in w.buckets:
+        t = dc.tasks_array([(x.offset, x.numel, x.param, x.comm) for x in bk.tasks])
+        got, roots = dc.dc_plan_flush(w.W, w.dtype, bk.col, bk.numel, t, len(t), owner, None, None,
+                                      w.P, comms, len(comms))
+        assert roots == int(np.sum(got["root"] >= 0))
+        total += len(got)
+        assert np.all(got["flags"] == 1) and np.all(got["first"] == got["last"])
+        assert np.array_equal(got["root"], owner[t["param"][got["first"]]])
+    assert total * 128 * 8 == sum(bk.numel for bk in w.buckets)
+
+
+def test_plan_flush_argument_checks():
+    t = dc.tasks_array([(0, 10, 0, 0), (10, 10, 1, 0)])
+    comms = [(8, 1)]
+    expect(dc.DC_ERR_DTYPE, dc.dc_plan_flush, 8, 3, 0, 20, t, 2, None, None, None, 2, comms, 1)
+    expect(dc.DC_ERR_TASKS, dc.dc_plan_flush, 8, 0, 0, 21, t, 2, None, None, None, 2, comms, 1)
+    expect(dc.DC_ERR_ARG, dc.dc_plan_flush, 8, 0, -1, 20, t, 2, None, None, None, 2, comms, 1)
+    expect(dc.DC_ERR_NULL, dc.dc_plan_flush, 8, 0, 0, 20, t, 2, None, [0, 10], None, 2, comms, 1)
+    expect(dc.DC_ERR_ARG, dc.dc_plan_flush, 8, 0, 0, 20, t, 2, [0, 1], [0, 10], [3, 3], 2, comms, 1)
+    expect(dc.DC_ERR_SHAPE, dc.dc_plan_flush, 8, 0, (1 << 44) + 8, 20, t, 2, None, None, None, 2, comms, 1)
+    # too few slots, and the size query
+    n = ctypes.c_int64(0)
+    big = dc.tasks_array([(0, 5000, 0, 0)])
+    args = (8, 0, 0, 5000, big.ctypes.data_as(ctypes.c_void_p), 1, None, None, None, 1,
+            dc.comms_array(comms).ctypes.data_as(ctypes.c_void_p), 1)
+    assert dc.lib().dc_plan_flush(*args, None, 0, ctypes.byref(n), None) == dc.DC_OK and n.value == 5
+    rc = dc.lib().dc_plan_flush(*args, np.zeros(4, dc.TILE_DTYPE).ctypes.data_as(ctypes.c_void_p), 4,
+                                ctypes.byref(n), None)
+    assert rc == dc.DC_ERR_SHAPE
+    assert dc.TILE_DTYPE.itemsize == 16
+
+
+def test_flush_planned_argument_checks():
+    f = dc.dc_flush_bucket_planned
+    ok = dict(W=8, dtype=0, slab_in=FAKE, ld_in=2048, slab_out=FAKE, ld_out=2048, bucket_col=0,
+              bucket_numel=2048, tasks=TASK_PTR, num_tasks=1, owner=None, flat_offset=None,
+              part_size=None, num_params=1, comms=[(8, 1)], num_comms=1, pre_div=1,
+              tiles=TASK_PTR + 4096, num_tiles=2, root_tiles=0, stream=0)
+
+    def call(**ch):
+        a = dict(ok)
+        a.update(ch)
+        return f(**a)
+
+    expect(dc.DC_ERR_SHAPE, call, num_tiles=3)                     # 2048 bf16 columns: 2 tiles
+    expect(dc.DC_ERR_SHAPE, call, num_tiles=0)
+    expect(dc.DC_ERR_SHAPE, call, bucket_col=8, ld_in=4096, ld_out=4096)   # starts mid-tile: 3 tiles
+    expect(dc.DC_ERR_NULL, call, tiles=None)
+    expect(dc.DC_ERR_NULL, call, tiles=None, num_tiles=0)             # a bucket with tiles needs a plan
+    expect(dc.DC_ERR_ARG, call, num_tiles=-1)
+    expect(dc.DC_ERR_ARG, call, root_tiles=3)
+    expect(dc.DC_ERR_ARG, call, root_tiles=-1)
+    expect(dc.DC_ERR_NULL, call, flat_offset=FAKE)
+    expect(dc.DC_ERR_ARG, call, flat_offset=FAKE, part_size=FAKE, owner=FAKE)
+    expect(dc.DC_ERR_ARG, call, W=0)
+    expect(dc.DC_ERR_NULL, call, slab_in=None)
+    expect(dc.DC_ERR_ARG, call, pre_div=2)

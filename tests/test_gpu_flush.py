@@ -123,18 +123,21 @@ def test_partition_ids_and_owner_map(w):
     assert np.array_equal(ex.h_counts, counts)
 
 
-def flush_case(w, reduce_to_owner, in_place=False, probe=True, zero2=False):
+def flush_case(w, reduce_to_owner, in_place=False, probe=True, zero2=False, planned=False):
     """Run every bucket of w on the GPU and on the oracle; compare all of the
-    output slab bit for bit, and the probe records."""
+    output slab bit for bit, and the probe records.  planned: the executor
+    plans every bucket first and flushes with the plans."""
     import torch
     U.say("flush", w.name, "zero2" if zero2 else ("owner" if reduce_to_owner else "allreduce"),
-          "in-place" if in_place else "")
+          "in-place" if in_place else "", "planned" if planned else "")
     scale = w.scale
     ld = w.ld
     x = U.gen_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, scale)
     y = x if in_place else U.empty_slab(w.dtype, w.W, ld)
     ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner, zero2=zero2)
     ex.build_owner_map()
+    if planned:
+        ex.plan()
     for b in range(len(w.buckets)):
         ex.flush(b, x, ld, y, ld)
     torch.cuda.synchronize()
@@ -332,15 +335,17 @@ def test_flush_nonfinite_and_subnormal_inputs():
         assert len(bad) == 0, (W, dtype, pre, bad[:4].tolist(), got[tuple(bad[0])], want[tuple(bad[0])])
 
 
-def full_size_flush(w, reduce_to_owner, in_place, zero2=False):
+def full_size_flush(w, reduce_to_owner, in_place, zero2=False, planned=False):
     import torch
     U.say("full-size flush", w.name, "zero2" if zero2 else ("owner" if reduce_to_owner else "allreduce"),
-          f"W={w.W} cols={w.total} buckets={len(w.buckets)}")
+          f"W={w.W} cols={w.total} buckets={len(w.buckets)}", "planned" if planned else "")
     ld = w.ld
     x = U.gen_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, w.scale)
     y = x if in_place else U.empty_slab(w.dtype, w.W, ld)
     ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner, zero2=zero2)
     ex.build_owner_map()
+    if planned:
+        ex.plan()
     for b in range(len(w.buckets)):
         ex.flush(b, x, ld, y, ld)
     torch.cuda.synchronize()

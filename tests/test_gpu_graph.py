@@ -32,11 +32,12 @@ def _workloads():
     ]
 
 
+@pytest.mark.parametrize("planned", [False, True], ids=["searched", "planned"])
 @pytest.mark.parametrize("case", range(4))
-def test_graph_replays_match_eager(case):
+def test_graph_replays_match_eager(case, planned):
     import torch
     w, owner, zero2 = _workloads()[case]
-    U.say("graph", w.name, owner, zero2)
+    U.say("graph", w.name, owner, zero2, "planned" if planned else "")
     ld = w.ld
     x = U.gen_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, w.scale)
     sent = U.SENTINEL16 if w.dtype == wl.DT_BF16 else U.SENTINEL32
@@ -44,6 +45,8 @@ def test_graph_replays_match_eager(case):
     # eager
     y_eager = U.empty_slab(w.dtype, w.W, ld)
     ex.build_owner_map()
+    if planned:
+        ex.plan()
     for b in range(len(w.buckets)):
         ex.flush(b, x, ld, y_eager, ld)
     torch.cuda.synchronize()
