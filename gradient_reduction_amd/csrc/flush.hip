@@ -20,7 +20,6 @@
 // then streams its vectors: W 16-byte row loads, an fp32 fold in rank order,
 // one 16-byte store to the owner row or W stores (AllReduce).  This is a
 // streaming reduction with no reuse: no MFMA, HBM bound.
-#include <atomic>
 
 #include "device_common.h"
 #include "internal.h"
@@ -453,38 +452,11 @@ int planned_cap(int32_t W, bool one_row) {
 }
 
 // Dynamic LDS a launch of one k_flush instantiation reserves, unused, so
-// that at most `cap` of its workgroups fit in one compute unit's LDS.  Cached
-// per device and cap (one cache per instantiation; filled once, read after).
-struct PadCache {
-  std::atomic<int32_t> v[16][17];
-  PadCache() {
-    for (auto& row : v)
-      for (auto& x : row) x.store(-1, std::memory_order_relaxed);
-  }
-};
-
+// that at most `cap` of its workgroups fit in one compute unit's LDS.
 template <bool BF16, int WT, int C2, int S2, int PRE, bool Z2>
 size_t flush_pad(int cap) {
-  static PadCache cache;
-  if (cap <= 0 || cap > 16) return 0;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
-  const int32_t hit = cache.v[dev][cap].load(std::memory_order_relaxed);
-  if (hit >= 0) return (size_t)hit;
-  int lds_cu = 0;
-  hipFuncAttributes fa;
   auto kern = k_flush<BF16, WT, C2, S2, PRE, DC_FLUSH_U, DC_FLUSH_NT != 0, Z2>;
-  if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
-          hipSuccess ||
-      hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern)) != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  const int64_t per_wg = (int64_t)(lds_cu / cap) / 256 * 256;
-  const int64_t pad = per_wg - (int64_t)fa.sharedSizeBytes;
-  const int32_t v = pad > 0 ? (int32_t)pad : 0;
-  cache.v[dev][cap].store(v, std::memory_order_relaxed);
-  return (size_t)v;
+  return occupancy_pad(reinterpret_cast<const void*>(kern), cap);
 }
 
 template <bool BF16, int WT, int C2, int S2, int PRE>

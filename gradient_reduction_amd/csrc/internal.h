@@ -39,6 +39,15 @@ struct FlushLaunch {
 
 hipError_t launch_flush(const FlushLaunch& a, hipStream_t stream);
 
+// Dynamic LDS a launch of `kernel` reserves, unused, so that at most `cap` of
+// its workgroups fit in one compute unit (0 when cap <= 0 or unreachable).
+size_t occupancy_pad(const void* kernel, int cap);
+
+// Workgroup cap for a 64-thread streaming launch whose threads each keep
+// `rows` row accesses of `u` 16-byte vectors in flight, so that about `kb`
+// KB of row accesses are in flight per compute unit (0 = no cap).
+int stream_cap(int rows, int u, int kb);
+
 // The flush kernel's tile grid over bucket columns [c0, c1) of a dtype: tile
 // b covers vectors [v0 + b*tile, v0 + min((b+1)*tile, nv)) in absolute
 // 16-byte column vectors.  Returns the tile count (0 for an empty bucket).

@@ -506,6 +506,19 @@ __global__ __launch_bounds__(kST) void k_stream_rows(const u32x4* __restrict__ s
   for (int r = 0; r < NW; ++r) store16<kNTS>(dst + r * dld + k, y);
 }
 
+// Row accesses in flight per compute unit (KB) at which each kernel below
+// measured fastest on the 7B-layer reduce-scatter / all-gather (W = 8) and
+// the W = 4 deferred reduce, 5-8% over a full compute unit (within 2% for
+// the ring-order reduce-scatter); other W keep the same budget.  The
+// variable-shard reduce-scatter measured no gain and keeps no cap.
+constexpr int kKbRs = 96, kKbRsRing = 144, kKbAg = 144, kKbDeferred = 96, kKbAccRed = 120;
+
+// The dynamic LDS that caps a launch of `kern` at `cap` workgroups per compute unit.
+template <typename K>
+size_t pad_for(K* kern, int cap) {
+  return occupancy_pad(reinterpret_cast<const void*>(kern), cap);
+}
+
 inline unsigned blocks_for(int64_t n, int u) {
   return (unsigned)((n + kST * u - 1) / (kST * u));
 }
@@ -521,12 +534,14 @@ hipError_t rs_vec_w(int32_t W, const void* in, int64_t ld_in, void* out, int64_t
   constexpr int E = BF16 ? 8 : 4;
   const int64_t Lv = L / E;
   const dim3 grid(blocks_for(Lv, DC_RS_U), (unsigned)W);
+  const int cap = stream_cap(W + 1, DC_RS_U, kKbRs);
   const u32x4* i4 = reinterpret_cast<const u32x4*>(in);
   u32x4* o4 = reinterpret_cast<u32x4*>(out);
   switch (W) {
 #define DC_RS_W(w)                                                                           \
   case w:                                                                                    \
-    hipLaunchKernelGGL((k_rs_vec<BF16, w, PRE>), grid, dim3(kST), 0, stream, W, i4,     \
+    hipLaunchKernelGGL((k_rs_vec<BF16, w, PRE>), grid, dim3(kST),                            \
+                       pad_for(k_rs_vec<BF16, w, PRE>, cap), stream, W, i4,                  \
                        ld_in / E, o4, ld_out / E, Lv, inv, c);                               \
     break;
     DC_RS_W(1)
@@ -536,7 +551,8 @@ hipError_t rs_vec_w(int32_t W, const void* in, int64_t ld_in, void* out, int64_t
     DC_RS_W(16)
 #undef DC_RS_W
     default:
-      hipLaunchKernelGGL((k_rs_vec<BF16, 0, PRE>), grid, dim3(kST), 0, stream, W, i4,
+      hipLaunchKernelGGL((k_rs_vec<BF16, 0, PRE>), grid, dim3(kST),
+                         pad_for(k_rs_vec<BF16, 0, PRE>, cap), stream, W, i4,
                          ld_in / E, o4, ld_out / E, Lv, inv, c);
   }
   return hipGetLastError();
@@ -624,12 +640,14 @@ hipError_t rs_ring_w(int32_t W, const void* in, int64_t ld_in, void* out, int64_
   constexpr int E = BF16 ? 8 : 4;
   const int64_t Lv = L / E;
   const dim3 grid(blocks_for(Lv, 1), (unsigned)W);
+  const int cap = stream_cap(W + 1, 1, kKbRsRing);
   const u32x4* i4 = reinterpret_cast<const u32x4*>(in);
   u32x4* o4 = reinterpret_cast<u32x4*>(out);
   switch (W) {
 #define DC_RR_W(w)                                                                                \
   case w:                                                                                         \
-    hipLaunchKernelGGL((k_rs_ring<BF16, w, PRE>), grid, dim3(kST), 0, stream, W, i4, ld_in / E, \
+    hipLaunchKernelGGL((k_rs_ring<BF16, w, PRE>), grid, dim3(kST),                                \
+                       pad_for(k_rs_ring<BF16, w, PRE>, cap), stream, W, i4, ld_in / E,           \
                        o4, ld_out / E, Lv, inv, c);                                               \
     break;
     DC_RR_W(1)
@@ -639,7 +657,8 @@ hipError_t rs_ring_w(int32_t W, const void* in, int64_t ld_in, void* out, int64_
     DC_RR_W(16)
 #undef DC_RR_W
     default:
-      hipLaunchKernelGGL((k_rs_ring<BF16, 0, PRE>), grid, dim3(kST), 0, stream, W, i4,
+      hipLaunchKernelGGL((k_rs_ring<BF16, 0, PRE>), grid, dim3(kST),
+                         pad_for(k_rs_ring<BF16, 0, PRE>, cap), stream, W, i4,
                          ld_in / E, o4, ld_out / E, Lv, inv, c);
   }
   return hipGetLastError();
@@ -696,7 +715,9 @@ hipError_t launch_all_gather(int32_t W, int32_t dtype, const void* in, int64_t l
   const int E = bf ? 8 : 4;
   if (L % E == 0) {
     const int64_t Lv = L / E;
-    hipLaunchKernelGGL(k_ag_vec, dim3(blocks_for(Lv, DC_AG_U), (unsigned)W), dim3(kST), 0, stream, W,
+    const int cap = stream_cap(1 + W, DC_AG_U, kKbAg);
+    hipLaunchKernelGGL(k_ag_vec, dim3(blocks_for(Lv, DC_AG_U), (unsigned)W), dim3(kST),
+                       pad_for(k_ag_vec, cap), stream, W,
                        reinterpret_cast<const u32x4*>(in), ld_in / E, reinterpret_cast<u32x4*>(out),
                        ld_out / E, Lv, order, step);
   } else if (bf) {
@@ -725,10 +746,12 @@ hipError_t launch_deferred_reduce(int32_t W, const float* acc, int64_t ld_acc, f
                                   hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const dim3 grid(blocks_for(M / 4 + 1, DC_DEF_U));
+  const int cap = stream_cap(W + out_rows, DC_DEF_U, kKbDeferred);
   switch (W) {
 #define DC_DR_W(w)                                                                            \
   case w:                                                                                     \
-    hipLaunchKernelGGL(k_deferred<w>, grid, dim3(kST), 0, stream, W, acc, ld_acc, out,   \
+    hipLaunchKernelGGL(k_deferred<w>, grid, dim3(kST),                                        \
+                       pad_for(k_deferred<w>, cap), stream, W, acc, ld_acc, out,              \
                        ld_out, M, out_rows);                                                  \
     break;
     DC_DR_W(1)
@@ -738,7 +761,8 @@ hipError_t launch_deferred_reduce(int32_t W, const float* acc, int64_t ld_acc, f
     DC_DR_W(16)
 #undef DC_DR_W
     default:
-      hipLaunchKernelGGL(k_deferred<0>, grid, dim3(kST), 0, stream, W, acc, ld_acc, out,
+      hipLaunchKernelGGL(k_deferred<0>, grid, dim3(kST),
+                         pad_for(k_deferred<0>, cap), stream, W, acc, ld_acc, out,
                          ld_out, M, out_rows);
   }
   return hipGetLastError();
@@ -750,10 +774,12 @@ hipError_t launch_accumulate_reduce(int32_t W, const float* x, int64_t ld_x, flo
                                     hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const dim3 grid(blocks_for(M / 4 + 1, 1));
+  const int cap = stream_cap(W + (init ? 0 : W) + (keep_acc ? W : 0) + out_rows, 1, kKbAccRed);
   switch (W) {
 #define DC_AR_W(w)                                                                            \
   case w:                                                                                     \
-    hipLaunchKernelGGL(k_accum_reduce<w>, grid, dim3(kST), 0, stream, W, x, ld_x, acc,   \
+    hipLaunchKernelGGL(k_accum_reduce<w>, grid, dim3(kST),                                    \
+                       pad_for(k_accum_reduce<w>, cap), stream, W, x, ld_x, acc,              \
                        ld_acc, init, keep_acc, out, ld_out, out_rows, M);                     \
     break;
     DC_AR_W(1)
@@ -763,7 +789,8 @@ hipError_t launch_accumulate_reduce(int32_t W, const float* x, int64_t ld_x, flo
     DC_AR_W(16)
 #undef DC_AR_W
     default:
-      hipLaunchKernelGGL(k_accum_reduce<0>, grid, dim3(kST), 0, stream, W, x, ld_x, acc,
+      hipLaunchKernelGGL(k_accum_reduce<0>, grid, dim3(kST),
+                         pad_for(k_accum_reduce<0>, cap), stream, W, x, ld_x, acc,
                          ld_acc, init, keep_acc, out, ld_out, out_rows, M);
   }
   return hipGetLastError();
