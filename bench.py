@@ -400,7 +400,7 @@ TRAFFIC_PROFILES = {
 def kernel_source_sha256(source):
     import hashlib
     h = hashlib.sha256()
-    for name in (source, "device_common.h"):
+    for name in (source, "device_common.h", "internal.h"):
         with open(os.path.join(ROOT, "gradient_reduction_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()

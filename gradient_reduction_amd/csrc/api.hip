@@ -382,7 +382,7 @@ dc_status dc_plan_flush(int32_t W, int32_t dtype, int64_t bucket_col, int64_t bu
         roots += root >= 0;
       }
     }
-    tiles[b] = rec;
+    tiles[dc::tile_slot(b, g.count)] = rec;
   }
   if (root_tiles != nullptr) *root_tiles = roots;
   return ok();

@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kFT) void k_flush(FlushParams p) {
   if (p.tiles != nullptr) {
     // planned: the tile's record replaces the search; a tile inside one task
     // streams straight away (record fields clamped to their ranges)
-    const dc_tile rec = p.tiles[tile];
+    const dc_tile rec = p.tiles[tile_slot(tile, (int64_t)gridDim.x)];
     if (rec.flags & 1) {
       int32_t comm = (rec.flags >> 8) & 0xFF;
       comm = comm < p.ncomms ? comm : 0;

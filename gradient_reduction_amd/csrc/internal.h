@@ -59,6 +59,16 @@ struct FlushTiles {
 };
 FlushTiles flush_tiles(int32_t dtype, int64_t c0, int64_t c1);
 
+// Where tile b's plan record sits in a plan of n records: XCD-major.  The
+// hardware deals workgroups to the 8 XCDs in turn, so tile b runs on XCD
+// b mod 8; keeping each XCD's records together lets one 128-byte line serve
+// eight of its tiles from that XCD's L2, where tile order would have every
+// XCD fetch every line for one record in eight.
+__host__ __device__ inline int64_t tile_slot(int64_t b, int64_t n) {
+  const int64_t r = b % 8, q = n / 8, rem = n % 8;
+  return r * q + (r < rem ? r : rem) + b / 8;
+}
+
 struct GroupTable {
   int32_t num_groups;
   int32_t begin[DC_MAX_GROUPS + 1];

@@ -131,7 +131,10 @@ typedef struct {
  * [v0 + 128 b, v0 + 128 (b + 1)), v0 = floor(c / E / 128) * 128 with E
  * elements per vector, clipped to the bucket's last vector), and this record
  * says which tasks a tile overlaps and, when the whole tile lies inside one
- * task and the bucket, which rows receive its sums.  16 bytes.
+ * task and the bucket, which rows receive its sums.  16 bytes.  A plan of n
+ * records keeps them XCD-major, in the order the 8 XCDs run the tiles: the
+ * record of tile b sits at index (b mod 8) floor(n/8) + min(b mod 8, n mod 8)
+ * + floor(b/8).
  *   first, last   indices of the first and last task overlapping the tile
  *                 (last < first: none)
  *   root          whole tile inside one task: the row that alone receives

@@ -373,7 +373,14 @@ def _brute_plan(W, dtype, col0, numel, tasks, owner, flat, psize):
             flags = 1 | (c << 8) if whole else 0
             root = root if whole else -1
         out[b] = (first, last, root, flags)
-    return out
+    # XCD-major: tile b's record at (b mod 8) floor(n/8) + min(b mod 8, n mod 8) + floor(b/8)
+    b = np.arange(count)
+    r, q, rem = b % 8, count // 8, count % 8
+    slot = r * q + np.minimum(r, rem) + b // 8
+    assert np.array_equal(np.sort(slot), b)
+    placed = np.zeros_like(out)
+    placed[slot] = out
+    return placed
 
 
 def test_plan_flush_matches_definition():
