@@ -12,6 +12,11 @@ register_buffers + flush_buffers run the flush with copy-in and copy-out
 fused in: each rank's gradient is read from its own buffer and the sum lands
 in the grad buffers of the ranks that keep one, with no bucket in between.
 
+plan() builds each bucket's flush plan once on the host (dc_plan_flush: the
+tasks each tile of the flush grid overlaps and, for a tile inside one task,
+the rows its sums go to); flush() then launches dc_flush_bucket_planned, the
+same sums with no per-tile search.
+
 torch supplies device memory and the stream; every step runs in libdc.so.
 """
 from dataclasses import dataclass

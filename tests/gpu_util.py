@@ -9,6 +9,7 @@ import sys
 import numpy as np
 
 import oracle
+from gradient_reduction_amd import dc
 import synth
 from synth import workloads as wl
 
@@ -170,3 +171,21 @@ def oracle_sampled_flush(w, cols, owner, zero2=False):
         oracle.flush(W, w.dtype, slab, out, 0, np.arange(n), np.ones(n), t_param, t_comm, owner,
                      [c.size for c in w.comms], [c.stride for c in w.comms], w.pre_div)
     return out[:, :n]
+
+
+def planned_flush(W, dtype, x, ld_in, y, ld_out, col0, numel, tasks, d_tasks, P, comms, pre,
+                  owner=None, flat=None, psize=None):
+    """Plan a bucket on the host (dc_plan_flush) and flush it with the plan
+    (dc_flush_bucket_planned).  owner / flat / psize are host arrays; their
+    device copies are made here.  Returns the device tensors the launch reads."""
+    import torch
+    tiles, roots = dc.dc_plan_flush(W, dtype, col0, numel, tasks, len(tasks), owner, flat, psize, P,
+                                    comms, len(comms))
+    keep = [torch.from_numpy(tiles.view(np.uint8).copy()).cuda() if len(tiles) else None]
+    d_own = torch.from_numpy(np.asarray(owner, np.int32)).cuda() if owner is not None else None
+    d_flat = torch.from_numpy(np.asarray(flat, np.int64)).cuda() if flat is not None else None
+    d_ps = torch.from_numpy(np.asarray(psize, np.int64)).cuda() if psize is not None else None
+    keep += [d_own, d_flat, d_ps]
+    dc.dc_flush_bucket_planned(W, dtype, x, ld_in, y, ld_out, col0, numel, d_tasks, len(tasks), d_own,
+                               d_flat, d_ps, P, comms, len(comms), pre, keep[0], len(tiles), roots)
+    return keep

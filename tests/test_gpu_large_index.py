@@ -51,9 +51,10 @@ def _host_columns(dtype, seed, rows, cols, scale):
     return a.view(np.float32) if dtype == wl.DT_F32 else a
 
 
+@pytest.mark.parametrize("planned", [False, True], ids=["searched", "planned"])
 @pytest.mark.parametrize("W,dtype,owner", [(4, wl.DT_BF16, True), (4, wl.DT_BF16, False),
                                            (3, wl.DT_F32, True)], ids=lambda v: str(v))
-def test_flush_across_column_2_31(W, dtype, owner):
+def test_flush_across_column_2_31(W, dtype, owner, planned):
     import torch
     sizes = [3000, 1, 2995, 4104, 17, 905]          # the fourth task holds column 2^31
     c0 = BIG - 6000
@@ -61,7 +62,7 @@ def test_flush_across_column_2_31(W, dtype, owner):
     offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int).tolist()
     assert c0 + offs[3] < BIG < c0 + offs[3] + sizes[3]
     ld = wl.round_up(c0 + numel + 1024, 64)
-    U.say("flush past 2^31", W, dtype, owner, "ld", ld)
+    U.say("flush past 2^31", W, dtype, owner, "ld", ld, "planned" if planned else "")
     scale = wl.sigma_scale(1e-2)
     tdt = torch.int16 if dtype == wl.DT_BF16 else torch.int32
     sent = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
@@ -74,7 +75,11 @@ def test_flush_across_column_2_31(W, dtype, owner):
     tasks = dc.tasks_array([(offs[k], sizes[k], k, 0) for k in range(P)])
     d_tasks = torch.from_numpy(tasks.view(np.uint8).copy()).cuda()
     d_own = torch.from_numpy(own).cuda() if owner else None
-    dc.dc_flush_bucket(W, dtype, x, ld, y, ld, c0, numel, d_tasks, P, d_own, P, [(W, 1)], 1, 1)
+    if planned:
+        keep = U.planned_flush(W, dtype, x, ld, y, ld, c0, numel, tasks, d_tasks, P, [(W, 1)], 1,
+                               owner=own if owner else None)
+    else:
+        dc.dc_flush_bucket(W, dtype, x, ld, y, ld, c0, numel, d_tasks, P, d_own, P, [(W, 1)], 1, 1)
     torch.cuda.synchronize()
     lo, hi = c0 - 64, c0 + numel + 64
     got = U.bits(y[:, lo:hi].cpu().numpy().view(np.uint16 if dtype == wl.DT_BF16 else np.float32), dtype)
@@ -185,6 +190,10 @@ def test_zero2_flush_and_relayout_across_column_2_31():
     dc.dc_flush_bucket_zero2(W, dtype, x, ld, y, ld, c0, numel, d_tasks, P,
                              torch.from_numpy(flat).cuda(), torch.from_numpy(psize).cuda(), P,
                              [(W, 1)], 1, 1)
+    # the planned ZeRO-2 flush of the same bucket into a second slab
+    y2 = torch.full((W, ld), U.SENTINEL16, dtype=torch.int16, device="cuda")
+    keep = U.planned_flush(W, dtype, x, ld, y2, ld, c0, numel, tasks, d_tasks, P, [(W, 1)], 1,
+                           flat=flat, psize=psize)
     pieces, seg = dc.dc_plan_relayout(W, tasks, P, flat, psize, P)
     n = int(seg[-1])
     ld_r = wl.round_up(n, 64)
@@ -198,14 +207,16 @@ def test_zero2_flush_and_relayout_across_column_2_31():
     torch.cuda.synchronize()
     lo, hi = c0 - 64, c0 + numel + 64
     got = y[:, lo:hi].cpu().numpy().view(np.uint16)
+    got2 = y2[:, lo:hi].cpu().numpy().view(np.uint16)
     got_sh = shards.cpu().numpy().view(np.uint16)
-    del x, y, relaid, shards
+    del x, y, y2, relaid, shards, keep
     torch.cuda.empty_cache()
     hin = _host_columns(dtype, 631, W, np.arange(lo, hi, dtype=np.int64), scale)
     hout = np.full_like(hin, U.SENTINEL16)
     oracle.flush_zero2(W, dtype, hin, hout, c0 - lo, offs, sizes, list(range(P)), [0] * P, flat, psize,
                        [W], [1], 1)
     assert np.array_equal(got, hout)
+    assert np.array_equal(got2, hout)
     # the partitions the bucket spans, and a boundary inside it
     parts = sorted({int(p) // S for k in range(P) for p in (flat[k], flat[k] + sizes[k] - 1)})
     assert len(parts) >= 2 and parts[-1] * S > BIG

@@ -38,9 +38,10 @@ FLUSH_CASES = [(8, wl.DT_BF16, True, 1, 64), (8, wl.DT_BF16, False, 1, 128),
                (5, wl.DT_F32, False, 0, 256), (16, wl.DT_F32, True, 0, 64)]
 
 
+@pytest.mark.parametrize("planned", [False, True], ids=["searched", "planned"])
 @pytest.mark.parametrize("W,dtype,owner,pre,extra", FLUSH_CASES, ids=lambda v: str(v))
 @pytest.mark.parametrize("out_wider", [True, False], ids=["out-wider", "in-wider"])
-def test_flush_distinct_strides(W, dtype, owner, pre, extra, out_wider):
+def test_flush_distinct_strides(W, dtype, owner, pre, extra, out_wider, planned):
     import torch
     sizes = [3000, 1, 17, 8191, 0, 640, 4097, 9]
     offs, col0, numel = _bucket(W, sizes, 13)
@@ -55,8 +56,12 @@ def test_flush_distinct_strides(W, dtype, owner, pre, extra, out_wider):
     tasks = dc.tasks_array([(offs[k], sizes[k], k, 0) for k in range(P)])
     d_tasks = torch.from_numpy(tasks.view(np.uint8).copy()).cuda()
     d_own = torch.from_numpy(own).cuda() if owner else None
-    dc.dc_flush_bucket(W, dtype, x, ld_in, y, ld_out, col0, numel, d_tasks, P, d_own, P,
-                       [(W, 1)], 1, pre)
+    if planned:
+        keep = U.planned_flush(W, dtype, x, ld_in, y, ld_out, col0, numel, tasks, d_tasks, P,
+                               [(W, 1)], pre, owner=own if owner else None)
+    else:
+        dc.dc_flush_bucket(W, dtype, x, ld_in, y, ld_out, col0, numel, d_tasks, P, d_own, P,
+                           [(W, 1)], 1, pre)
     torch.cuda.synchronize()
     hin = U.host_slab(dtype, W, ld_in, ld_in, 501, 0, scale)
     hout = np.zeros((W, ld_out), hin.dtype)
@@ -66,8 +71,9 @@ def test_flush_distinct_strides(W, dtype, owner, pre, extra, out_wider):
     assert np.array_equal(U.bits(U.to_host(y, dtype), dtype), U.bits(hout, dtype))
 
 
+@pytest.mark.parametrize("planned", [False, True], ids=["searched", "planned"])
 @pytest.mark.parametrize("W,dtype", [(8, wl.DT_BF16), (4, wl.DT_F32), (6, wl.DT_BF16)])
-def test_flush_zero2_distinct_strides(W, dtype):
+def test_flush_zero2_distinct_strides(W, dtype, planned):
     import torch
     sizes = [5000, 77, 12001, 3, 2500]
     offs, col0, numel = _bucket(W, sizes, 5)
@@ -83,9 +89,13 @@ def test_flush_zero2_distinct_strides(W, dtype):
     y = U.empty_slab(dtype, W, ld_out)
     tasks = dc.tasks_array([(offs[k], sizes[k], k, 0) for k in range(P)])
     d_tasks = torch.from_numpy(tasks.view(np.uint8).copy()).cuda()
-    dc.dc_flush_bucket_zero2(W, dtype, x, ld_in, y, ld_out, col0, numel, d_tasks, P,
-                             torch.from_numpy(flat).cuda(), torch.from_numpy(psize).cuda(), P,
-                             [(W, 1)], 1, 1)
+    if planned:
+        keep = U.planned_flush(W, dtype, x, ld_in, y, ld_out, col0, numel, tasks, d_tasks, P,
+                               [(W, 1)], 1, flat=flat, psize=psize)
+    else:
+        dc.dc_flush_bucket_zero2(W, dtype, x, ld_in, y, ld_out, col0, numel, d_tasks, P,
+                                 torch.from_numpy(flat).cuda(), torch.from_numpy(psize).cuda(), P,
+                                 [(W, 1)], 1, 1)
     torch.cuda.synchronize()
     hin = U.host_slab(dtype, W, ld_in, ld_in, 502, 0, scale)
     hout = np.zeros((W, ld_out), hin.dtype)
