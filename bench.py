@@ -330,7 +330,11 @@ def bench_flush_buffers(args, w):
     rows_i = np.arange(w.W, dtype=np.int64)[:, None] * ld
     in_addr = (x.data_ptr() + (rows_i + poff[None, :]) * eb).astype(np.uint64)
     out_addr = np.where(hold, y.data_ptr() + (rows_i + poff[None, :]) * eb, 0).astype(np.uint64)
-    ex.register_buffers(in_addr, out_addr)
+    ex.register_buffers(in_addr, out_addr, planned=not args.searched)
+    if not args.searched:
+        # 16 bytes per tile record read
+        per_launch = [pl + 16 * int(ex.buf_tile_begin[i + 1] - ex.buf_tile_begin[i])
+                      for i, pl in enumerate(per_launch)]
     step_bytes = sum(per_launch) + owner_map_bytes(w)
 
     def step(timer=None):
@@ -850,8 +854,8 @@ def main():
                     help="deferred workload: fuse the last accumulate into the reduce")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--searched", action="store_true",
-                    help="flush workloads: flush without plans (each tile searches the task "
-                         "table) instead of with the per-bucket tile plans")
+                    help="flush and fused workloads: flush without plans (each tile searches "
+                         "the task table) instead of with the per-bucket tile plans")
     ap.add_argument("--probe", action="store_true",
                     help="flush workloads: print the probe line of each of the first 20 flushes "
                          "(the executor's reduce_probe), as they are issued")
@@ -904,6 +908,8 @@ def main():
         name, dtype = w.name, wl.DTYPE_NAME[w.dtype]
         config = {"workload": name, "W": w.W, "elements": w.total, "buckets": len(w.buckets),
                   "mode": "copy-in/copy-out fused flush into per-rank grad buffers",
+                  "flush": ("searched: each tile looks up its tasks" if args.searched else
+                            "planned: per-bucket tile plans built once at registration"),
                   "pre_div": w.pre_div, "step": "owner map + every bucket flush",
                   "step_bytes": step_bytes}
     elif args.workload == "deferred":

@@ -405,6 +405,71 @@ dc_status dc_flush_bucket_buffers(int32_t W, int32_t dtype, int64_t bucket_numel
                     "buffer flush launch");
 }
 
+dc_status dc_plan_flush_buffers(int32_t W, int32_t dtype, int64_t bucket_numel, const dc_task* tasks,
+                                int32_t num_tasks, const dc_comm* comms, int32_t num_comms,
+                                dc_tile* tiles, int64_t capacity, int64_t* num_tiles) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype)) || (st = check_comms(W, comms, num_comms))) return st;
+  if (num_tiles == nullptr) return fail(DC_ERR_NULL, "num_tiles is NULL");
+  if (bucket_numel < 0 || num_tasks < 0) return fail(DC_ERR_ARG, "bucket_numel or num_tasks < 0");
+  if ((st = check_extent("bucket_numel", bucket_numel))) return st;
+  if (num_tasks > 0 && tasks == nullptr) return fail(DC_ERR_NULL, "tasks is NULL");
+  int64_t end = 0;
+  for (int32_t t = 0; t < num_tasks; ++t) {
+    const dc_task& k = tasks[t];
+    if (k.numel < 0 || k.offset < end || k.offset + k.numel > bucket_numel)
+      return fail(DC_ERR_TASKS, "task %d: offset %lld numel %lld (sorted, disjoint, inside %lld)", t,
+                  (long long)k.offset, (long long)k.numel, (long long)bucket_numel);
+    if (k.comm < 0 || k.comm >= num_comms) return fail(DC_ERR_TASKS, "task %d: comm %d", t, k.comm);
+    end = k.offset + k.numel;
+  }
+  const int64_t count = num_tasks > 0 ? dc::buffer_tiles(dtype, bucket_numel) : 0;
+  *num_tiles = count;
+  if (tiles == nullptr) return ok();  // size query
+  if (capacity < count)
+    return fail(DC_ERR_SHAPE, "capacity=%lld < %lld tiles", (long long)capacity, (long long)count);
+  const int64_t E = dtype == DC_BF16 ? 8 : 4;
+  const int64_t nslots = (bucket_numel + E - 1) / E;
+  int32_t k = 0;
+  for (int64_t b = 0; b < count; ++b) {
+    const int64_t s0 = b * 128, s1 = std::min(s0 + 128, nslots);
+    const int64_t lo = s0 * E, hi = std::min(s1 * E, bucket_numel);
+    // first: the last task starting at or before lo; last: the last starting before hi
+    while (k + 1 < num_tasks && tasks[k + 1].offset <= lo) ++k;
+    int32_t last = k;
+    while (last + 1 < num_tasks && tasks[last + 1].offset < hi) ++last;
+    if (tasks[0].offset >= hi) last = -1;
+    const dc_task& t = tasks[k];
+    const bool whole = last == k && t.comm == 0 && t.offset % E == 0 && t.offset <= lo &&
+                       s1 * E <= t.offset + t.numel;
+    tiles[dc::tile_slot(b, count)] = dc_tile{k, last, -1, whole ? 1 : 0};
+  }
+  return ok();
+}
+
+dc_status dc_flush_bucket_buffers_planned(int32_t W, int32_t dtype, int64_t bucket_numel,
+                                          const dc_task* tasks, int32_t num_tasks,
+                                          const void* const* in_ptrs, void* const* out_ptrs,
+                                          const dc_comm* comms, int32_t num_comms, int32_t pre_div,
+                                          const dc_tile* tiles, int64_t num_tiles, void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype)) || (st = check_comms(W, comms, num_comms))) return st;
+  if (bucket_numel < 0 || num_tasks < 0)
+    return fail(DC_ERR_ARG, "bucket_numel=%lld, num_tasks=%d", (long long)bucket_numel, num_tasks);
+  if ((st = check_extent("bucket_numel", bucket_numel)) || (st = check_extent("num_tiles", num_tiles))) return st;
+  if (num_tasks > 0 && (tasks == nullptr || in_ptrs == nullptr || out_ptrs == nullptr))
+    return fail(DC_ERR_NULL, "tasks, in_ptrs or out_ptrs is NULL");
+  if (pre_div != 0 && pre_div != 1) return fail(DC_ERR_ARG, "pre_div=%d", pre_div);
+  const int64_t want = num_tasks > 0 ? dc::buffer_tiles(dtype, bucket_numel) : 0;
+  if (num_tiles != want)
+    return fail(DC_ERR_SHAPE, "num_tiles=%lld, the bucket has %lld tiles", (long long)num_tiles, (long long)want);
+  if (want > 0 && tiles == nullptr) return fail(DC_ERR_NULL, "tiles is NULL");
+  return hip_status(dc::launch_flush_buffers(W, dtype, bucket_numel, tasks, num_tasks, in_ptrs, out_ptrs,
+                                             comms, num_comms, pre_div, static_cast<hipStream_t>(stream),
+                                             tiles),
+                    "planned buffer flush launch");
+}
+
 dc_status dc_validate_buffer_tasks(int32_t W, int32_t dtype, const dc_task* tasks, int32_t num_tasks,
                                    int64_t bucket_numel, const dc_comm* comms, int32_t num_comms,
                                    const void* const* in_ptrs, void* const* out_ptrs) {

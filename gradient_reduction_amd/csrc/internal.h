@@ -101,7 +101,14 @@ hipError_t launch_relayout(int32_t W, int32_t dtype, const void* in, int64_t ld_
 hipError_t launch_flush_buffers(int32_t W, int32_t dtype, int64_t bucket_numel, const dc_task* tasks,
                                 int32_t num_tasks, const void* const* in_ptrs, void* const* out_ptrs,
                                 const dc_comm* comms, int32_t num_comms, int32_t pre_div,
-                                hipStream_t stream);
+                                hipStream_t stream, const dc_tile* tiles = nullptr);
+
+// Tiles of the fused flush over a bucket of n coordinates: 128 slots of E
+// elements each, from coordinate 0.
+inline int64_t buffer_tiles(int32_t dtype, int64_t n) {
+  const int64_t E = dtype == DC_BF16 ? 8 : 4;
+  return ((n + E - 1) / E + 127) / 128;
+}
 
 hipError_t launch_reduce_scatter_ring(int32_t W, int32_t dtype, const void* in, int64_t ld_in,
                                       void* out, int64_t ld_out, int64_t M, int32_t pre_div,

@@ -58,6 +58,9 @@ _SIGS = {
                          _i32, _i32, _vp], _i32),
     "dc_flush_bucket_buffers": ([_i32, _i32, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp], _i32),
     "dc_validate_buffer_tasks": ([_i32, _i32, _vp, _i32, _i64, _vp, _i32, _vp, _vp], _i32),
+    "dc_plan_flush_buffers": ([_i32, _i32, _i64, _vp, _i32, _vp, _i32, _vp, _i64, _vp], _i32),
+    "dc_flush_bucket_buffers_planned": ([_i32, _i32, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp,
+                                         _i64, _vp], _i32),
     "dc_flush_bucket_zero2": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
                                _i32, _vp, _i32, _i32, _vp], _i32),
     "dc_plan_flush": ([_i32, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i64,
@@ -189,6 +192,28 @@ def dc_flush_bucket_buffers(W, dtype, bucket_numel, tasks, num_tasks, in_ptrs, o
     _check("dc_flush_bucket_buffers", lib().dc_flush_bucket_buffers(
         W, dtype, bucket_numel, _dev(tasks), num_tasks, _dev(in_ptrs), _dev(out_ptrs), cp, num_comms,
         pre_div, _stream(stream)))
+
+
+def dc_plan_flush_buffers(W, dtype, bucket_numel, tasks, num_tasks, comms, num_comms):
+    """Host only; returns the fused flush's dc_tile records (TILE_DTYPE)."""
+    tp, _a = _host(tasks, TASK_DTYPE)
+    cp, _b = _host(comms, COMM_DTYPE)
+    n = ctypes.c_int64(0)
+    _check("dc_plan_flush_buffers", lib().dc_plan_flush_buffers(
+        W, dtype, bucket_numel, tp, num_tasks, cp, num_comms, None, 0, ctypes.byref(n)))
+    tiles = np.zeros(max(n.value, 1), TILE_DTYPE)
+    _check("dc_plan_flush_buffers", lib().dc_plan_flush_buffers(
+        W, dtype, bucket_numel, tp, num_tasks, cp, num_comms, tiles.ctypes.data_as(_vp), n.value,
+        ctypes.byref(n)))
+    return tiles[:n.value].copy()
+
+
+def dc_flush_bucket_buffers_planned(W, dtype, bucket_numel, tasks, num_tasks, in_ptrs, out_ptrs,
+                                    comms, num_comms, pre_div, tiles, num_tiles, stream=None):
+    cp, _a = _host(comms, COMM_DTYPE)
+    _check("dc_flush_bucket_buffers_planned", lib().dc_flush_bucket_buffers_planned(
+        W, dtype, bucket_numel, _dev(tasks), num_tasks, _dev(in_ptrs), _dev(out_ptrs), cp, num_comms,
+        pre_div, _dev(tiles), num_tiles, _stream(stream)))
 
 
 def dc_validate_buffer_tasks(W, dtype, tasks, num_tasks, bucket_numel, comms, num_comms, in_ptrs,

@@ -195,14 +195,16 @@ class Zero1FlushExecutor:
                     out[k, (blk * c if st == 1 else blk) + int(q) * st] = True
         return out
 
-    def register_buffers(self, in_addr: np.ndarray, out_addr: np.ndarray) -> None:
+    def register_buffers(self, in_addr: np.ndarray, out_addr: np.ndarray, planned: bool = True) -> None:
         """in_addr, out_addr: [W, P] device addresses of rank r's gradient of
         param p and of its grad buffer (0 = empty buffer).  A task's slice
         starts at its position within its param (the params' tasks in bucket
         order).  Task coordinates are re-laid at 128-byte steps: buffers that
         start on a 128-byte boundary then move as whole vectors with every
         wave's accesses on whole cache lines.  Tables are validated on the
-        host and kept on the device."""
+        host and kept on the device; with planned (the default) each bucket's
+        tile plan (dc_plan_flush_buffers) is built here too, and flush_buffers
+        launches the planned kernel."""
         torch = self.torch
         W = self.W
         eb = 2 if self.dtype == dc.DC_BF16 else 4
@@ -211,6 +213,7 @@ class Zero1FlushExecutor:
         out_addr = np.asarray(out_addr, np.uint64).reshape(W, self.P)
         seen = np.zeros(self.P, np.int64)
         tasks, ins, outs, self.buf_extent, self.buf_begin = [], [], [], [], [0]
+        plans, self.buf_tile_begin = [], [0]
         for b, bk in enumerate(self.buckets):
             pos = 0
             rows = []
@@ -232,22 +235,40 @@ class Zero1FlushExecutor:
             outs.append(tout.ravel())
             self.buf_extent.append(extent)
             self.buf_begin.append(self.buf_begin[-1] + len(t))
+            if planned:
+                pl = dc.dc_plan_flush_buffers(W, self.dtype, extent, t, len(t), self.comms,
+                                              len(self.comms))
+                plans.append(pl)
+                self.buf_tile_begin.append(self.buf_tile_begin[-1] + len(pl))
         dev = self.d_tasks.device
         allt = np.concatenate(tasks) if tasks else np.zeros(0, dc.TASK_DTYPE)
         self.d_btasks = torch.from_numpy(allt.view(np.uint8).copy()).to(dev) if len(allt) else None
         self.d_bin = torch.from_numpy(np.concatenate(ins).view(np.int64)).to(dev)
         self.d_bout = torch.from_numpy(np.concatenate(outs).view(np.int64)).to(dev)
+        self.d_btiles = None
+        if planned:
+            allp = np.concatenate(plans) if plans else np.zeros(0, dc.TILE_DTYPE)
+            raw = allp.view(np.uint8).copy() if len(allp) else np.zeros(16, np.uint8)
+            self.d_btiles = torch.from_numpy(raw).to(dev)
 
     def flush_buffers(self, b: int, stream=None) -> None:
         n = len(self.buckets[b].tasks)
         if n == 0:
             return
         t0 = self.buf_begin[b]
-        dc.dc_flush_bucket_buffers(self.W, self.dtype, self.buf_extent[b],
-                                   self.d_btasks.data_ptr() + 32 * t0, n,
-                                   self.d_bin.data_ptr() + 8 * t0 * self.W,
-                                   self.d_bout.data_ptr() + 8 * t0 * self.W,
-                                   self.comms, len(self.comms), self.pre_div, stream)
+        if self.d_btiles is not None:
+            p0 = self.buf_tile_begin[b]
+            dc.dc_flush_bucket_buffers_planned(
+                self.W, self.dtype, self.buf_extent[b], self.d_btasks.data_ptr() + 32 * t0, n,
+                self.d_bin.data_ptr() + 8 * t0 * self.W, self.d_bout.data_ptr() + 8 * t0 * self.W,
+                self.comms, len(self.comms), self.pre_div, self.d_btiles.data_ptr() + 16 * p0,
+                self.buf_tile_begin[b + 1] - p0, stream)
+        else:
+            dc.dc_flush_bucket_buffers(self.W, self.dtype, self.buf_extent[b],
+                                       self.d_btasks.data_ptr() + 32 * t0, n,
+                                       self.d_bin.data_ptr() + 8 * t0 * self.W,
+                                       self.d_bout.data_ptr() + 8 * t0 * self.W,
+                                       self.comms, len(self.comms), self.pre_div, stream)
         self.flushes += 1
 
     # -- one step as a HIP graph --------------------------------------------------

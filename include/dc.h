@@ -364,6 +364,41 @@ dc_status dc_flush_bucket_buffers(int32_t W, int32_t dtype, int64_t bucket_numel
                                   const dc_comm* comms, int32_t num_comms, int32_t pre_div,
                                   void* stream);
 
+/* Plan of a fused flush (dc_flush_bucket_buffers' tables), host only, once
+ * per registration: the fused kernel cuts the bucket's coordinates
+ * [0, bucket_numel) into tiles of 128 slots of 16 bytes (slot v covers
+ * coordinates [v E, v E + E), E elements per 16 bytes), and tile b's record
+ * names the first task starting at or before the tile and the last starting
+ * inside it (last < first: none), and sets flags bit 0 when the tile's slots
+ * all lie inside that one task, the task is on the data-parallel comm and its
+ * offset is a multiple of E; root is -1.  Records are XCD-major as in
+ * dc_tile.
+ *   tasks, comms        host copies: tasks sorted, disjoint, inside the
+ *                       bucket, comm in range (else DC_ERR_TASKS)
+ *   tiles, capacity     host dc_tile[capacity] out; NULL asks for the count
+ *   num_tiles           out: ceil(ceil(bucket_numel / E) / 128), 0 with no
+ *                       tasks; fewer slots than that is DC_ERR_SHAPE */
+dc_status dc_plan_flush_buffers(int32_t W, int32_t dtype, int64_t bucket_numel, const dc_task* tasks,
+                                int32_t num_tasks, const dc_comm* comms, int32_t num_comms,
+                                dc_tile* tiles, int64_t capacity, int64_t* num_tiles);
+
+/* dc_flush_bucket_buffers with a plan from dc_plan_flush_buffers: the same
+ * results, bit for bit.  A tile the plan marks whole, whose task the kernel
+ * finds covering the tile and whose W input and output pointers are 16-byte
+ * aligned, streams from the task's pointer row with no search and no staging;
+ * every other tile takes the staged path over the record's task range.
+ *   tiles, num_tiles   device dc_tile[num_tiles]; num_tiles must equal the
+ *                      planned count (else DC_ERR_SHAPE)
+ * Other arguments as in dc_flush_bucket_buffers.  The plan is read on the
+ * device and not checked: a stale plan can leave columns unwritten or give
+ * wrong sums, but the kernel checks a whole tile's task before using its
+ * pointers, so it never addresses memory outside the registered buffers. */
+dc_status dc_flush_bucket_buffers_planned(int32_t W, int32_t dtype, int64_t bucket_numel,
+                                          const dc_task* tasks, int32_t num_tasks,
+                                          const void* const* in_ptrs, void* const* out_ptrs,
+                                          const dc_comm* comms, int32_t num_comms, int32_t pre_div,
+                                          const dc_tile* tiles, int64_t num_tiles, void* stream);
+
 /* Host check of the tables of dc_flush_bucket_buffers (run once when the
  * buffers are registered): tasks sorted by offset, disjoint, numel >= 0,
  * inside [0, bucket_numel), comm in [0, num_comms); comms as in

@@ -485,3 +485,75 @@ def test_flush_planned_argument_checks():
     expect(dc.DC_ERR_ARG, call, W=0)
     expect(dc.DC_ERR_NULL, call, slab_in=None)
     expect(dc.DC_ERR_ARG, call, pre_div=2)
+
+
+def _brute_plan_buffers(dtype, numel, tasks):
+    """The fused flush's tile records as the header defines them, from each
+    tile's coordinate range, XCD-major."""
+    E = 8 if dtype == wl.DT_BF16 else 4
+    nslots = -(-numel // E)
+    count = -(-nslots // 128) if len(tasks) else 0
+    off = tasks["offset"].astype(np.int64)
+    out = np.zeros(count, dc.TILE_DTYPE)
+    for b in range(count):
+        lo, s1 = 128 * b * E, min(128 * (b + 1), nslots)
+        hi = min(s1 * E, numel)
+        first = max(int(np.searchsorted(off, lo, side="right")) - 1, 0)
+        last = int(np.searchsorted(off, hi, side="left")) - 1
+        t = tasks[first]
+        whole = (last == first and t["comm"] == 0 and t["offset"] % E == 0 and t["offset"] <= lo
+                 and s1 * E <= t["offset"] + t["numel"])
+        out[b] = (first, last, -1, 1 if whole else 0)
+    b = np.arange(count)
+    slot = (b % 8) * (count // 8) + np.minimum(b % 8, count % 8) + b // 8
+    placed = np.zeros_like(out)
+    placed[slot] = out
+    return placed
+
+
+def test_plan_flush_buffers_matches_definition():
+    rng = random.Random(12)
+    for k in range(30):
+        W = rng.choice([2, 4, 6, 8, 16])
+        dtype = rng.choice([wl.DT_BF16, wl.DT_F32])
+        E = 8 if dtype == wl.DT_BF16 else 4
+        comms = [(W, 1), (W // 2, 2)]
+        rows, pos = [], rng.randint(0, 20)
+        for i in range(rng.randint(1, 60)):
+            n = rng.choice([0, 1, 7, 8, 63, 64, 500, 1024, 1025, 3000, 20_000])
+            rows.append((pos, n, i, rng.choice([0, 0, 0, 1])))
+            pos += n + rng.choice([0, 0, 1, 5, 64, 3000])
+            if rng.random() < 0.5:
+                pos = -(-pos // (4 * E)) * 4 * E
+        numel = rows[-1][0] + rows[-1][1] + rng.choice([0, 3, 100])
+        t = dc.tasks_array(rows)
+        got = dc.dc_plan_flush_buffers(W, dtype, numel, t, len(t), comms, len(comms))
+        want = _brute_plan_buffers(dtype, numel, t)
+        assert np.array_equal(got, want), k
+
+
+def test_plan_flush_buffers_argument_checks():
+    comms = [(8, 1)]
+    bad = dc.tasks_array([(0, 10, 0, 0), (5, 10, 1, 0)])           # overlapping
+    expect(dc.DC_ERR_TASKS, dc.dc_plan_flush_buffers, 8, 0, 20, bad, 2, comms, 1)
+    expect(dc.DC_ERR_TASKS, dc.dc_plan_flush_buffers, 8, 0, 12, dc.tasks_array([(0, 13, 0, 0)]), 1,
+           comms, 1)
+    expect(dc.DC_ERR_TASKS, dc.dc_plan_flush_buffers, 8, 0, 20, dc.tasks_array([(0, 10, 0, 3)]), 1,
+           comms, 1)
+    expect(dc.DC_ERR_DTYPE, dc.dc_plan_flush_buffers, 8, 5, 20, dc.tasks_array([(0, 10, 0, 0)]), 1,
+           comms, 1)
+    f = dc.dc_flush_bucket_buffers_planned
+    ok = dict(W=8, dtype=0, bucket_numel=2048, tasks=TASK_PTR, num_tasks=1, in_ptrs=FAKE,
+              out_ptrs=FAKE, comms=comms, num_comms=1, pre_div=1, tiles=TASK_PTR + 4096,
+              num_tiles=2, stream=0)
+
+    def call(**ch):
+        a = dict(ok)
+        a.update(ch)
+        return f(**a)
+
+    expect(dc.DC_ERR_SHAPE, call, num_tiles=3)
+    expect(dc.DC_ERR_NULL, call, tiles=None)
+    expect(dc.DC_ERR_NULL, call, in_ptrs=None)
+    expect(dc.DC_ERR_ARG, call, pre_div=3)
+    expect(dc.DC_ERR_ARG, call, W=0)

@@ -67,7 +67,7 @@ CASES = [
 NUMEL = [0, 1, 7, 8, 9, 64, 1000, 4099, 5000, 3, 8197, 16]
 
 
-def run_case(W, dtype, pre, comms, numel, seed, aligned, padded, inplace):
+def run_case(W, dtype, pre, comms, numel, seed, aligned, padded, inplace, planned=False):
     import torch
     rng = random.Random(seed)
     n = len(numel)
@@ -115,8 +115,14 @@ def run_case(W, dtype, pre, comms, numel, seed, aligned, padded, inplace):
     dc.dc_validate_buffer_tasks(W, dtype, tasks, n, extent, comms, len(comms),
                                 p_in.cpu().numpy().view(np.uint64), p_out.cpu().numpy().view(np.uint64))
     U.say("flush buffers", W, dtype, pre, n, "aligned" if aligned else "unaligned",
-          "padded" if padded else "packed", "in place" if inplace else "")
-    dc.dc_flush_bucket_buffers(W, dtype, extent, d_tasks, n, p_in, p_out, comms, len(comms), pre)
+          "padded" if padded else "packed", "in place" if inplace else "", "planned" if planned else "")
+    if planned:
+        tiles = dc.dc_plan_flush_buffers(W, dtype, extent, tasks, n, comms, len(comms))
+        d_tiles = torch.from_numpy(tiles.view(np.uint8).copy()).cuda() if len(tiles) else None
+        dc.dc_flush_bucket_buffers_planned(W, dtype, extent, d_tasks, n, p_in, p_out, comms, len(comms),
+                                           pre, d_tiles, len(tiles))
+    else:
+        dc.dc_flush_bucket_buffers(W, dtype, extent, d_tasks, n, p_in, p_out, comms, len(comms), pre)
     torch.cuda.synchronize()
     oracle.flush_buffers(W, dtype, h_in, in_off, h_out, out_off, numel, t_comm, cs, cst, pre)
     got = U.to_host(d_out, dtype)[0]
@@ -126,13 +132,15 @@ def run_case(W, dtype, pre, comms, numel, seed, aligned, padded, inplace):
 @pytest.mark.parametrize("W,dtype,pre,comms", CASES, ids=lambda v: str(v))
 @pytest.mark.parametrize("aligned,padded", [(True, True), (True, False), (False, True)],
                          ids=["aligned-padded", "aligned-packed", "unaligned"])
-def test_flush_buffers_small(W, dtype, pre, comms, aligned, padded):
-    run_case(W, dtype, pre, comms, NUMEL, 100 + W, aligned, padded, inplace=False)
+@pytest.mark.parametrize("planned", [False, True], ids=["searched", "planned"])
+def test_flush_buffers_small(W, dtype, pre, comms, aligned, padded, planned):
+    run_case(W, dtype, pre, comms, NUMEL, 100 + W, aligned, padded, inplace=False, planned=planned)
 
 
 @pytest.mark.parametrize("W,dtype,pre,comms", CASES[:4], ids=lambda v: str(v))
-def test_flush_buffers_in_place(W, dtype, pre, comms):
-    run_case(W, dtype, pre, comms, NUMEL, 200 + W, True, True, inplace=True)
+@pytest.mark.parametrize("planned", [False, True], ids=["searched", "planned"])
+def test_flush_buffers_in_place(W, dtype, pre, comms, planned):
+    run_case(W, dtype, pre, comms, NUMEL, 200 + W, True, True, inplace=True, planned=planned)
 
 
 def test_flush_buffers_many_tiny_tasks():
@@ -140,8 +148,11 @@ def test_flush_buffers_many_tiny_tasks():
     runs several rounds."""
     rng = random.Random(5)
     numel = [rng.randint(0, 9) for _ in range(700)]
-    run_case(8, wl.DT_BF16, 1, [(8, 1), (4, 1)], numel, 301, True, True, inplace=False)
-    run_case(6, wl.DT_F32, 0, [(6, 1), (2, 3)], numel, 302, False, False, inplace=False)
+    for planned in (False, True):
+        run_case(8, wl.DT_BF16, 1, [(8, 1), (4, 1)], numel, 301, True, True, inplace=False,
+                 planned=planned)
+        run_case(6, wl.DT_F32, 0, [(6, 1), (2, 3)], numel, 302, False, False, inplace=False,
+                 planned=planned)
 
 
 def test_flush_buffers_empty():
@@ -153,7 +164,7 @@ def test_flush_buffers_empty():
     torch.cuda.synchronize()
 
 
-def _full_size(w):
+def _full_size(w, planned=True):
     """Per-rank gradient arenas [W, ld] holding each param at a 128-byte
     aligned position with the slab's values, grad-buffer arenas of the same
     layout for the holders, the executor's tables, and every bucket flushed."""
@@ -189,7 +200,7 @@ def _full_size(w):
     rows = np.arange(w.W, dtype=np.int64)[:, None] * ld
     in_addr = (d_in.data_ptr() + (rows + poff[None, :]) * eb).astype(np.uint64)
     out_addr = np.where(hold, d_out.data_ptr() + (rows + poff[None, :]) * eb, 0).astype(np.uint64)
-    ex.register_buffers(in_addr, out_addr)
+    ex.register_buffers(in_addr, out_addr, planned=planned)
     for b in range(len(w.buckets)):
         ex.flush_buffers(b)
     torch.cuda.synchronize()
@@ -216,9 +227,10 @@ def _check_sampled(w, d_out, ld, poff, pcol, hold):
     U.say("  checked", int(H.sum()), "holder elements,", int((~H).sum()), "untouched")
 
 
-def test_flush_buffers_owner_w8_full_size():
+@pytest.mark.parametrize("planned", [True, False], ids=["planned", "searched"])
+def test_flush_buffers_owner_w8_full_size(planned):
     w = wl.owner_flush_w8()
-    ex, d_out, ld, poff, pcol, hold = _full_size(w)
+    ex, d_out, ld, poff, pcol, hold = _full_size(w, planned)
     _check_sampled(w, d_out, ld, poff, pcol, hold)
 
 
