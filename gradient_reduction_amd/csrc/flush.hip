@@ -443,11 +443,11 @@ __global__ __launch_bounds__(kFT) void k_flush(FlushParams p) {
 // unit: at W = 8, about 64 KB of row loads per compute unit (8 workgroups)
 // for tiles that write one row, and 32 KB (4) for tiles that write all eight,
 // whose stores take their own share of the memory system; at W = 16 (fp32
-// measured), 6 and 3.
+// measured), 6 and 3; at W = 4 (bf16 measured), 12 and 8.
 int planned_cap(int32_t W, bool one_row) {
   if (W >= 16) return one_row ? 6 : 3;
   if (W >= 8) return one_row ? 8 : 4;
-  if (W >= 4) return one_row ? 16 : 12;
+  if (W >= 4) return one_row ? 12 : 8;
   return 0;
 }
 
