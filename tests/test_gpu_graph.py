@@ -70,3 +70,52 @@ def test_graph_replays_match_eager(case, planned):
         ex.flush(b, x, ld, y2, ld)
     torch.cuda.synchronize()
     assert torch.equal(y2.cpu(), want)
+
+
+@pytest.mark.parametrize("planned", [False, True], ids=["searched", "planned"])
+def test_graph_replays_fused_flush(planned):
+    """The fused copy-in/copy-out flush recorded as a graph (capture_step with
+    fused=True): every replay, with eager fills between, matches the eager
+    flush bit for bit."""
+    import torch
+    W, dtype, pre = 4, wl.DT_BF16, 1
+    numel = [100, 5000, 37, 777, 4096, 20_000]
+    buckets = [executor.BucketSpec(0, 3100, [(0, 100, 0, 0), (100, 3000, 1, 0)]),
+               executor.BucketSpec(3100, 2814, [(0, 2000, 1, 0), (2000, 37, 2, 0), (2037, 777, 3, 0)]),
+               executor.BucketSpec(5914, 4096, [(0, 4096, 4, 0)]),
+               executor.BucketSpec(10010, 20_000, [(0, 20_000, 5, 0)])]
+    ex = executor.Zero1FlushExecutor(W, dtype, numel, [0, 6], [W], [W], [list(range(W))], [(W, 1)],
+                                     buckets, pre, reduce_to_owner=True)
+    ex.build_owner_map()
+    ex.fetch_metadata()
+    poff, pos = [], 0
+    for n in numel:
+        poff.append(pos)
+        pos = wl.round_up(pos + n, 64)
+    ld = wl.round_up(pos, 64)
+    U.say("graph fused", "planned" if planned else "searched", "ld", ld)
+    x = U.gen_slab(dtype, W, ld, ld, 81, 0, wl.sigma_scale(1e-2))
+    y = U.empty_slab(dtype, W, ld)
+    hold = np.zeros((W, len(numel)), bool)
+    for b, bk in enumerate(buckets):
+        h = ex.holders(b)
+        for k, t in enumerate(bk.tasks):
+            hold[:, t[2]] |= h[k]
+    rows = np.arange(W, dtype=np.int64)[:, None] * ld
+    po = np.array(poff, np.int64)[None, :]
+    in_addr = (x.data_ptr() + (rows + po) * 2).astype(np.uint64)
+    out_addr = np.where(hold, y.data_ptr() + (rows + po) * 2, 0).astype(np.uint64)
+    ex.register_buffers(in_addr, out_addr, planned=planned)
+    for b in range(len(buckets)):
+        ex.flush_buffers(b)
+    torch.cuda.synchronize()
+    want = y.cpu()
+    assert not bool((want == U.SENTINEL16).all())
+    g = ex.capture_step(fused=True)
+    for rep in range(4):
+        y.fill_(U.SENTINEL16)
+        torch.cuda.synchronize()
+        g.replay()
+        if rep % 2:
+            torch.cuda.synchronize()
+        assert torch.equal(y.cpu(), want), f"replay {rep}"
