@@ -1,0 +1,219 @@
+"""Full-size workloads against the oracle on every output element.
+
+The GPU runs each workload at its full size; the oracle computes the whole
+output from host-generated inputs of the same seeds, split into column blocks
+over host threads (oracle/columns.py, itself checked against one whole
+oracle call by tests/test_oracle_columns.py), and the two are compared bit
+for bit over every column of every row:
+
+  * the W = 8 bf16 402.8M-element flush (shuffled and layered parameter
+    lists), reduce-to-owner and AllReduce, searched and planned, and the
+    shuffled list under ZeRO-2 (DeepSpeed issue "[REQUEST] DeepCompile
+    ZeRO-1: reduce-to-owner instead of AllReduce", "Describe the solution":
+    the same reduction in the same operand order, one destination);
+  * the W = 16 fp32 1.2B-element mixed flush in place, owner map and
+    ZeRO-2, in chunks of buckets (rows a flush does not write keep the input);
+  * the qwen3-0.6b W = 4 fp32 gradient accumulation at K = 8: the replica
+    accumulators, the deferred reduce, the status quo (every micro-batch
+    reduced, the reduced gradients accumulated) and the fused last
+    accumulate, in column chunks (MaxText PR "Defer the data-parallel
+    gradient all-reduce to update() under gradient accumulation", What);
+  * the 7B-layer W = 8 bf16 reduce-scatter and the all-gather in rank and
+    in ring order ("AllGather", semantic definition and Ring AllGather).
+"""
+import numpy as np
+import pytest
+
+from oracle import columns as OC
+from gradient_reduction_amd import dc, executor
+import synth
+from synth import workloads as wl
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def _host_cols(y, c0, n, dtype):
+    """Columns [c0, c0 + n) of every row of device slab y, as host bits."""
+    a = y[:, c0:c0 + n].contiguous().cpu().numpy()
+    return a.view(np.uint16) if dtype == wl.DT_BF16 else a.view(np.uint32)
+
+
+def _bits(a, dtype):
+    return a.view(np.uint16) if dtype == wl.DT_BF16 else a.view(np.uint32)
+
+
+def _check(got, want, what):
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got != want)
+        raise AssertionError(f"{what}: {len(bad)} of {got.size} elements differ from the oracle; "
+                             f"first [row, col] {bad[:4].tolist()}")
+
+
+def _flush_all(w, ex, x, y, planned):
+    import torch
+    if planned:
+        ex.plan()
+    else:
+        ex.d_tiles = None
+    for b in range(len(w.buckets)):
+        ex.flush(b, x, w.ld, y, w.ld)
+    torch.cuda.synchronize()
+
+
+def full_flush_every_column(w, mode):
+    """Out-of-place flush of every bucket, searched and planned, against the
+    oracle on every column."""
+    import torch
+    U.say("whole-output flush", w.name, mode, f"W={w.W} columns={w.total}")
+    x = U.gen_slab(w.dtype, w.W, w.ld, w.total, w.value_seed, 0, w.scale)
+    outs = {}
+    for planned in (False, True):
+        y = U.empty_slab(w.dtype, w.W, w.ld)
+        ex = executor.from_workload(w, reduce_to_owner=(mode == "owner"), zero2=(mode == "zero2"))
+        ex.build_owner_map()
+        _flush_all(w, ex, x, y, planned)
+        outs["planned" if planned else "searched"] = y
+    del x
+    owner = OC.owner_of(w) if mode == "owner" else None
+    zero2 = OC.zero2_tables(w) if mode == "zero2" else None
+    sent = U.SENTINEL16 if w.dtype == wl.DT_BF16 else U.SENTINEL32
+    checked = 0
+    for b, bk in enumerate(w.buckets):
+        want = _bits(OC.flush_bucket(w, b, owner=owner, zero2=zero2, init=sent), w.dtype)
+        for name, y in outs.items():
+            _check(_host_cols(y, bk.col, bk.numel, w.dtype), want, f"{mode} {name} bucket {b}")
+        checked += bk.numel
+        U.say(f"  bucket {b}: {bk.numel} columns x {w.W} rows equal the oracle (searched, planned)")
+    assert checked == w.total
+    del outs
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", ["owner", "allreduce", "zero2"])
+def test_flush_w8_402m_every_column(mode):
+    full_flush_every_column(wl.owner_flush_w8(), mode)
+
+
+@pytest.mark.parametrize("mode", ["owner", "allreduce"])
+def test_flush_w8_402m_layered_every_column(mode):
+    full_flush_every_column(wl.owner_flush_w8_layered(), mode)
+
+
+MIXED_CHUNKS = 5
+
+
+@pytest.mark.parametrize("chunk", range(MIXED_CHUNKS))
+@pytest.mark.parametrize("mode", ["owner", "zero2"])
+def test_flush_w16_mixed_1_2b_in_place_every_column(mode, chunk):
+    """The 76.8 GB mixed slab flushed in place, bucket by bucket; chunk k
+    checks every column of its share of the buckets (planned launch for the
+    owner map, searched for ZeRO-2, so both kernels see the full size)."""
+    import torch
+    w = wl.mixed_flush_w16()
+    nb = len(w.buckets)
+    mine = [b for b in range(nb) if b * MIXED_CHUNKS // nb == chunk]
+    U.say("mixed in place", mode, "buckets", mine)
+    x = U.gen_slab(w.dtype, w.W, w.ld, w.total, w.value_seed, 0, w.scale)
+    ex = executor.from_workload(w, reduce_to_owner=(mode == "owner"), zero2=(mode == "zero2"))
+    ex.build_owner_map()
+    if mode == "owner":
+        ex.plan()
+    for b in mine:
+        ex.flush(b, x, w.ld, x, w.ld)
+    torch.cuda.synchronize()
+    owner = OC.owner_of(w) if mode == "owner" else None
+    zero2 = OC.zero2_tables(w) if mode == "zero2" else None
+    for b in mine:
+        bk = w.buckets[b]
+        want = _bits(OC.flush_bucket(w, b, owner=owner, zero2=zero2, init="input"), w.dtype)
+        _check(_host_cols(x, bk.col, bk.numel, w.dtype), want, f"mixed {mode} bucket {b}")
+        U.say(f"  bucket {b}: {bk.numel} columns x {w.W} rows equal the oracle")
+    del x
+    torch.cuda.empty_cache()
+
+
+DEFERRED_CHUNKS = 4
+
+
+@pytest.mark.parametrize("chunk", range(DEFERRED_CHUNKS))
+def test_deferred_ga_qwen3_k8_every_column(chunk):
+    """K = 8 micro-batches of the qwen3-0.6b tree over W = 4 replicas, on
+    the device: the accumulators after K accumulates, the deferred reduce to
+    every replica, the status quo (reduce each micro-batch to one row, then
+    accumulate) and the fused last accumulate (K - 1 accumulates, then the
+    accumulate-reduce keeping the accumulator).  Chunk k of the columns is
+    compared with the oracle element by element."""
+    import torch
+    K = 8
+    w = wl.deferred_ga_w4(K)
+    W, M, ld = w.W, w.M, w.ld
+    c0 = chunk * M // DEFERRED_CHUNKS
+    c1 = (chunk + 1) * M // DEFERRED_CHUNKS
+    U.say("deferred K=8 every column, chunk", chunk, c0, c1)
+    f32 = torch.float32
+    acc = torch.empty((W, ld), dtype=f32, device="cuda")
+    acc2 = torch.empty((W, ld), dtype=f32, device="cuda")
+    A = torch.empty((1, ld), dtype=f32, device="cuda")
+    g = torch.empty((1, ld), dtype=f32, device="cuda")
+    x = torch.empty((W, ld), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    D = torch.empty((W, ld), dtype=f32, device="cuda")
+    D2 = torch.empty((W, ld), dtype=f32, device="cuda")
+    for k in range(K):
+        synth.fill_slab_device(wl.DT_F32, w.value_seed, wl.microbatch_stream(k, W, 0), w.scale, W,
+                               ld, M, x.data_ptr(), stream)
+        xf = x.view(f32)
+        dc.dc_accumulate(W, xf, ld, acc, ld, M, 1 if k == 0 else 0)
+        dc.dc_deferred_reduce(W, xf, ld, g, ld, M, 1)
+        dc.dc_accumulate(1, g, ld, A, ld, M, 1 if k == 0 else 0)
+        if k < K - 1:
+            dc.dc_accumulate(W, xf, ld, acc2, ld, M, 1 if k == 0 else 0)
+        else:
+            dc.dc_accumulate_reduce(W, xf, ld, acc2, ld, 0, 1, D2, ld, W, M)
+    dc.dc_deferred_reduce(W, acc, ld, D, ld, M, W)
+    torch.cuda.synchronize()
+    del x
+    h_acc, h_D, h_A = OC.deferred_columns(W, w.value_seed, w.scale, K,
+                                          lambda k, r: wl.microbatch_stream(k, W, r), c0, c1 - c0)
+    n = c1 - c0
+    _check(_host_cols(acc, c0, n, wl.DT_F32), h_acc.view(np.uint32), "accumulators")
+    _check(_host_cols(acc2, c0, n, wl.DT_F32), h_acc.view(np.uint32), "fused path's accumulators")
+    want_D = np.broadcast_to(h_D.view(np.uint32), (W, n))
+    _check(_host_cols(D, c0, n, wl.DT_F32), want_D, "deferred reduce, every replica")
+    _check(_host_cols(D2, c0, n, wl.DT_F32), want_D, "fused accumulate-reduce, every replica")
+    _check(_host_cols(A, c0, n, wl.DT_F32)[0], h_A.view(np.uint32), "status quo")
+    U.say(f"  columns [{c0}, {c1}): accumulators, D (both paths) and A equal the oracle")
+    del acc, acc2, A, g, D, D2
+    torch.cuda.empty_cache()
+
+
+def test_reduce_scatter_all_gather_7b_layer_every_column():
+    """Reduce-scatter of the 7B-layer slab (W = 8 bf16, M = 202,383,360)
+    into 8 shards, then all-gather in rank and in ring order: every shard
+    element and every gathered element against the oracle."""
+    import torch
+    w = wl.rs_ag_w8()
+    W, M, dtype = w.W, w.M, w.dtype
+    L = M // W
+    U.say("rs/ag every column", M)
+    x = U.gen_slab(dtype, W, w.ld, M, w.value_seed, 0, w.scale)
+    ld_sh = wl.round_up(L, 64)
+    sh = U.empty_slab(dtype, W, ld_sh)
+    dc.dc_reduce_scatter(W, dtype, x, w.ld, sh, ld_sh, M, 0)
+    rank = U.empty_slab(dtype, W, w.ld)
+    ring = U.empty_slab(dtype, W, w.ld)
+    dc.dc_all_gather(W, dtype, sh, ld_sh, rank, w.ld, L, dc.DC_ORDER_RANK, -1)
+    dc.dc_all_gather(W, dtype, sh, ld_sh, ring, w.ld, L, dc.DC_ORDER_RING, -1)
+    torch.cuda.synchronize()
+    del x
+    hin = OC.host_rows(dtype, w.value_seed, 0, w.scale, W, 0, M)
+    want_sh = OC.reduce_scatter_columns(W, dtype, np.ascontiguousarray(hin[:, :M]), M, 0)
+    del hin
+    _check(_host_cols(sh, 0, L, dtype), want_sh, "reduce-scatter shards")
+    U.say("  shards equal the oracle")
+    for order, y, name in ((dc.DC_ORDER_RANK, rank, "rank"), (dc.DC_ORDER_RING, ring, "ring")):
+        want = OC.all_gather_rows(W, dtype, want_sh, L, order)
+        _check(_host_cols(y, 0, M, dtype), want, f"all-gather, {name} order")
+        U.say(f"  all-gather in {name} order equals the oracle")
+    torch.cuda.empty_cache()
