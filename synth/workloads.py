@@ -214,29 +214,30 @@ HIDDEN = 1024
 EMBED = 151936 * 1024
 
 
-def owner_flush_w8(seed_sizes: int = 102, value_seed: int = 2, target: int = 402_800_000,
-                   capacity: int = 52_428_800, embedding: bool = True) -> FlushWorkload:
+def param_list(name: str) -> List[int]:
+    """A committed parameter-size list (synth/param_lists/<name>.json,
+    written once by synth/param_lists/generate.py)."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "param_lists", name + ".json")
+    with open(path) as f:
+        rec = json.load(f)
+    numel = [int(n) for n in rec["numel"]]
+    assert len(numel) == rec["params"] and sum(numel) == rec["total"], path
+    return numel
+
+
+def owner_flush_w8(value_seed: int = 2, capacity: int = 52_428_800) -> FlushWorkload:
     """W=8 bf16 flush of a 402.8M-element transformer-shaped gradient.
 
-    The embedding (151936 x 1024) is declared first, then a seeded shuffle of
-    a stratified mix of 1024-vectors (78.0%), 1024x1024 (15.2%) and 1024x4096
-    / 4096x1024 (6.8%) matrices, the smallest such mix whose total reaches
-    `target`.  The mix's mean size, 445,395, gives about 118 tasks per
-    52,428,800-element bucket.  One group, 8 equal partitions, pre-division on.
+    The committed list owner_flush_w8_402.8M (size seed 102): the embedding
+    (151936 x 1024) declared first, then a seeded shuffle of a stratified mix
+    of 1024-vectors (78.0%), 1024x1024 (15.2%) and 1024x4096 / 4096x1024
+    (6.8%) matrices, the smallest such mix whose total reaches 402.8M.  The
+    mix's mean size, 445,395, gives about 118 tasks per 52,428,800-element
+    bucket.  One group, 8 equal partitions, pre-division on.
     """
-    rng = random.Random(seed_sizes)
-    head = [EMBED] if embedding else []
-    N = 0
-    while True:
-        N += 1
-        n_vec = round(0.780 * N)
-        n_sq = round(0.152 * N)
-        n_wide = N - n_vec - n_sq
-        mix = [HIDDEN] * n_vec + [HIDDEN * HIDDEN] * n_sq + [4 * HIDDEN * HIDDEN] * n_wide
-        if sum(head) + sum(mix) >= target:
-            break
-    rng.shuffle(mix)
-    numel = head + mix
+    numel = param_list("owner_flush_w8_402.8M")
     w = FlushWorkload(name="owner_flush_w8_bf16_402.8M", W=8, dtype=DT_BF16, sigma=1e-3,
                       value_seed=value_seed, numel=numel, group_begin=[0, len(numel)],
                       group_comm=[0], comms=[Comm(8, 1)], capacity=capacity, pre_div=1)
@@ -275,25 +276,15 @@ def owner_flush_w8_layered(value_seed: int = 2, target: int = 402_800_000,
     return finish(w)
 
 
-def mixed_flush_w16(seed_sizes: int = 105, value_seed: int = 5, target: int = 1_200_000_000,
-                    capacity: int = 52_428_800, moe_stride: int = 1) -> FlushWorkload:
-    """W=16 fp32, lognormal sizes (median 64k, sigma_ln 2, clipped to
-    [1, 2^25]), 2% tiny params (uniform 1..64), total exactly `target`.
-    Three groups (contiguous thirds by count); group 2 is an MoE expert group
-    reduced over four 4-rank sub-communicators and so never gets an owner.
-    Pre-division off."""
-    rng = random.Random(seed_sizes)
-    numel: List[int] = []
-    total = 0
-    while total < target:
-        if rng.random() < 0.02:
-            n = rng.randint(1, 64)
-        else:
-            n = int(round(rng.lognormvariate(math.log(65536.0), 2.0)))
-            n = min(max(n, 1), 1 << 25)
-        n = min(n, target - total)
-        numel.append(n)
-        total += n
+def mixed_flush_w16(value_seed: int = 5, capacity: int = 52_428_800,
+                    moe_stride: int = 1) -> FlushWorkload:
+    """W=16 fp32, the committed list mixed_flush_w16_1.2B (size seed 105):
+    lognormal sizes (median 64k, sigma_ln 2, clipped to [1, 2^25]), 2% tiny
+    params (uniform 1..64), total exactly 1.2B.  Three groups (contiguous
+    thirds by count); group 2 is an MoE expert group reduced over four 4-rank
+    sub-communicators (contiguous blocks, or strided with moe_stride != 1)
+    and so never gets an owner.  Pre-division off."""
+    numel = param_list("mixed_flush_w16_1.2B")
     P = len(numel)
     gb = [0, P // 3, 2 * P // 3, P]
     sub = Comm(4, 1) if moe_stride == 1 else Comm(4, 16 // 4)

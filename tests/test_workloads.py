@@ -85,3 +85,17 @@ def test_flat_trees():
     q = wl.qwen3_0_6b_tree()
     assert len(q) == 310 and sum(q) == 596_049_920
     assert sum(wl.layer_7b_tree()) == 202_383_360
+
+
+def test_committed_param_lists_match_their_recipe():
+    """The committed size lists are what synth/param_lists/generate.py
+    writes from their seeds (the workloads read the files, not the
+    generator), and hold what the workloads above pin."""
+    from synth.param_lists import generate
+    assert generate.main(check=True)
+    a = wl.param_list("owner_flush_w8_402.8M")
+    b = wl.param_list("mixed_flush_w16_1.2B")
+    assert (len(a), sum(a), a[0]) == (554, 403_487_744, 151936 * 1024)
+    assert set(a[1:]) == {1024, 1024 * 1024, 4 * 1024 * 1024}
+    assert (len(b), sum(b)) == (2487, 1_200_000_000)
+    assert 1 <= min(b) and max(b) <= 1 << 25
