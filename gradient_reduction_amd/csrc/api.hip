@@ -106,6 +106,37 @@ dc_status check_comms(int32_t W, const dc_comm* comms, int32_t num_comms) {
   return DC_OK;
 }
 
+// The data-parallel group: the same world size, and group rank i is global
+// rank i for every i ([DS] Design points: groups reduced over another
+// communicator take no part in the owner map).
+bool dp_group(int32_t W, int32_t g, const int32_t* group_comm_size,
+              const int32_t* group_rank_to_global) {
+  if (group_comm_size[g] != W) return false;
+  for (int i = 0; i < W; ++i)
+    if (group_rank_to_global[(int64_t)g * W + i] != i) return false;
+  return true;
+}
+
+// The ranks holding task t's param: every rank whose optimizer partition
+// (group rank, in every block of a sub-communicator) is in the param's
+// partition list.  hd gets W flags.  The probe's `kept` and the copy-out
+// targets of the fused flush both come from here.
+dc_status task_holders(int32_t W, const dc_task& k, int32_t t, const int32_t* pid_offsets,
+                       const int32_t* pids, const dc_comm* comms, char* hd) {
+  const int32_t c = comms[k.comm].size, s = comms[k.comm].stride;
+  std::fill(hd, hd + W, 0);
+  const int32_t o0 = pid_offsets[k.param], o1 = pid_offsets[k.param + 1];
+  if (o1 > o0 && pids == nullptr) return fail(DC_ERR_NULL, "pids is NULL");
+  for (int32_t e = o0; e < o1; ++e) {
+    const int32_t q = pids[e];
+    if (q < 0 || q >= c)
+      return fail(DC_ERR_TASKS, "task %d: param %d: partition %d outside its comm of %d", t,
+                  k.param, q, c);
+    for (int32_t blk = 0; blk < W / c; ++blk) hd[(s == 1 ? blk * c : blk) + q * s] = 1;
+  }
+  return DC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -175,10 +206,7 @@ dc_status dc_build_owner_map(int32_t W, int32_t num_params, const int32_t* pid_o
   g.num_groups = num_groups;
   for (int k = 0; k <= num_groups; ++k) g.begin[k] = group_begin[k];
   for (int k = 0; k < num_groups; ++k) {
-    // the data-parallel group: same world size, group rank i is global rank i
-    int elig = group_comm_size[k] == W;
-    for (int i = 0; elig && i < W; ++i) elig = group_rank_to_global[(int64_t)k * W + i] == i;
-    g.eligible[k] = elig;
+    g.eligible[k] = dp_group(W, k, group_comm_size, group_rank_to_global);
     g.parts[k] = group_comm_size[k];
   }
   return hip_status(dc::launch_owner_map(W, num_params, pid_offsets, pids, pids_capacity, g, owner,
@@ -236,7 +264,7 @@ dc_status flush_common(const char* fn, int32_t W, int32_t dtype, const void* sla
     return fail(DC_ERR_ARG, "slab_in and slab_out overlap without being the same slab");
   }
   if (num_tiles >= 0) {  // planned
-    const int64_t want = dc::flush_tiles(dtype, bucket_col, end).count;
+    const int64_t want = dc::plan_tiles(dtype, bucket_col, end).count;
     if (tiles == nullptr && want > 0) return fail(DC_ERR_NULL, "tiles is NULL");
     if (num_tiles != want)
       return fail(DC_ERR_SHAPE, "num_tiles=%lld, the bucket has %lld tiles", (long long)num_tiles,
@@ -335,12 +363,12 @@ dc_status dc_plan_flush(int32_t W, int32_t dtype, int64_t bucket_col, int64_t bu
   if ((st = dc_validate_tasks(W, tasks, num_tasks, bucket_numel, num_params, comms, num_comms)))
     return st;
   const int64_t c0 = bucket_col, c1 = bucket_col + bucket_numel;
-  const dc::FlushTiles g = dc::flush_tiles(dtype, c0, c1);
+  const dc::FlushTiles g = dc::plan_tiles(dtype, c0, c1);
   *num_tiles = g.count;
   if (tiles == nullptr) return ok();  // size query
-  int64_t roots = 0;
   if (capacity < g.count)
     return fail(DC_ERR_SHAPE, "capacity=%lld < %lld tiles", (long long)capacity, (long long)g.count);
+  int64_t roots = 0;
   if (g.count > 0 && num_tasks == 0) {
     for (int64_t b = 0; b < g.count; ++b) tiles[b] = dc_tile{0, -1, -1, 0};
     if (root_tiles != nullptr) *root_tiles = 0;
@@ -360,7 +388,8 @@ dc_status dc_plan_flush(int32_t W, int32_t dtype, int64_t bucket_col, int64_t bu
     if (tasks[0].offset >= hi) last = -1;
     dc_tile rec{k, last, -1, 0};
     const dc_task& t = tasks[k];
-    if (last == k && f_lo >= 0 && f_hi <= bucket_numel && t.offset <= f_lo && f_hi <= t.offset + t.numel) {
+    if (last == k && f_lo >= 0 && f_hi <= bucket_numel && t.offset <= f_lo &&
+        f_hi <= t.offset + t.numel) {
       int32_t root = -1;
       bool whole = true;
       if (t.comm == 0) {
@@ -535,7 +564,6 @@ dc_status dc_probe_flush(int32_t W, int32_t dtype, const dc_task* tasks, int32_t
     const dc_task& k = tasks[t];
     if (k.param < 0 || k.param >= num_params || k.comm < 0 || k.comm >= num_comms || k.numel < 0)
       return fail(DC_ERR_TASKS, "task %d has an out-of-range param, comm or numel", t);
-    const int32_t c = comms[k.comm].size, s = comms[k.comm].stride;
     int32_t root = (k.comm == 0 && owner != nullptr) ? owner[k.param] : -1;
     if (root >= W) root = -1;
     out->reduced_elems += k.numel;
@@ -544,16 +572,9 @@ dc_status dc_probe_flush(int32_t W, int32_t dtype, const dc_task* tasks, int32_t
       out->owner_elems += k.numel;
     }
     std::fill(wr.begin(), wr.end(), 0);
-    std::fill(hd.begin(), hd.end(), 0);
     if (root >= 0) wr[root] = 1;
     else std::fill(wr.begin(), wr.end(), 1);
-    const int32_t o0 = pid_offsets[k.param], o1 = pid_offsets[k.param + 1];
-    if (o1 > o0 && pids == nullptr) return fail(DC_ERR_NULL, "pids is NULL");
-    for (int32_t e = o0; e < o1; ++e) {
-      const int32_t q = pids[e];
-      if (q < 0 || q >= c) return fail(DC_ERR_TASKS, "param %d: partition %d outside its comm of %d", k.param, q, c);
-      for (int32_t blk = 0; blk < W / c; ++blk) hd[(s == 1 ? blk * c : blk) + q * s] = 1;
-    }
+    if ((st = task_holders(W, k, t, pid_offsets, pids, comms, hd.data()))) return st;
     for (int r = 0; r < W; ++r) {
       if (wr[r]) out->written[r] += k.numel;
       if (hd[r]) out->kept[r] += k.numel;
@@ -561,6 +582,46 @@ dc_status dc_probe_flush(int32_t W, int32_t dtype, const dc_task* tasks, int32_t
   }
   for (int r = 0; r < W; ++r) out->discarded[r] = out->written[r] - out->kept[r];
   return ok();
+}
+
+dc_status dc_holders(int32_t W, const dc_task* tasks, int32_t num_tasks, int32_t num_params,
+                     const int32_t* pid_offsets, const int32_t* pids, const dc_comm* comms,
+                     int32_t num_comms, uint8_t* holders) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_comms(W, comms, num_comms))) return st;
+  if (num_tasks < 0 || num_params < 0) return fail(DC_ERR_ARG, "num_tasks or num_params < 0");
+  if (num_tasks > 0 && (tasks == nullptr || pid_offsets == nullptr || holders == nullptr))
+    return fail(DC_ERR_NULL, "tasks, pid_offsets or holders is NULL");
+  std::vector<char> hd(W);
+  for (int32_t t = 0; t < num_tasks; ++t) {
+    const dc_task& k = tasks[t];
+    if (k.param < 0 || k.param >= num_params || k.comm < 0 || k.comm >= num_comms)
+      return fail(DC_ERR_TASKS, "task %d has an out-of-range param or comm", t);
+    if ((st = task_holders(W, k, t, pid_offsets, pids, comms, hd.data()))) return st;
+    for (int r = 0; r < W; ++r) holders[(int64_t)t * W + r] = (uint8_t)hd[r];
+  }
+  return ok();
+}
+
+dc_status dc_param_part_size(int32_t W, int32_t num_params, int32_t num_groups,
+                             const int32_t* group_begin, const int32_t* group_comm_size,
+                             const int32_t* group_rank_to_global, const int64_t* part_size,
+                             int64_t* param_part_size, void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_groups(num_params, num_groups, group_begin))) return st;
+  if (group_comm_size == nullptr || group_rank_to_global == nullptr || part_size == nullptr)
+    return fail(DC_ERR_NULL, "group_comm_size, group_rank_to_global or part_size is NULL");
+  if (num_params > 0 && param_part_size == nullptr) return fail(DC_ERR_NULL, "param_part_size is NULL");
+  dc::GroupTable g{};
+  g.num_groups = num_groups;
+  for (int k = 0; k <= num_groups; ++k) g.begin[k] = group_begin[k];
+  for (int k = 0; k < num_groups; ++k) {
+    g.eligible[k] = dp_group(W, k, group_comm_size, group_rank_to_global);
+    g.parts[k] = group_comm_size[k];
+  }
+  return hip_status(dc::launch_param_part_size(num_params, g, part_size, param_part_size,
+                                               static_cast<hipStream_t>(stream)),
+                    "param part size launch");
 }
 
 dc_status dc_plan_relayout(int32_t W, const dc_task* tasks, int32_t num_tasks,
@@ -838,6 +899,29 @@ dc_status dc_stream_rows(const void* src, int64_t src_ld_vec, int32_t rows_read,
   return hip_status(dc::launch_stream_rows(src, src_ld_vec, rows_read, dst, dst_ld_vec, rows_written,
                                            nvec, static_cast<hipStream_t>(stream)),
                     "stream rows launch");
+}
+
+dc_status dc_stream_rows_shaped(const void* src, int64_t src_ld_vec, int32_t rows_read, void* dst,
+                                int64_t dst_ld_vec, int32_t rows_written, int64_t nvec,
+                                int32_t group, int32_t cap, void* stream) {
+  if (group != 1 && group != 2 && group != 4) return fail(DC_ERR_UNSUPPORTED, "group=%d (1, 2 or 4)", group);
+  if (cap < 0 || cap > 64) return fail(DC_ERR_ARG, "cap=%d outside [0, 64]", cap);
+  if (!((rows_read == 4 || rows_read == 8 || rows_read == 16) &&
+        (rows_written == 1 || rows_written == rows_read)))
+    return fail(DC_ERR_UNSUPPORTED, "rows_read=%d rows_written=%d (need 4/8/16 and 1 or rows_read)",
+                rows_read, rows_written);
+  if (check_extent("src_ld_vec", src_ld_vec) || check_extent("dst_ld_vec", dst_ld_vec)) return DC_ERR_SHAPE;
+  if (nvec < 0 || src_ld_vec < nvec || dst_ld_vec < nvec)
+    return fail(DC_ERR_SHAPE, "nvec=%lld with row strides %lld and %lld vectors", (long long)nvec,
+                (long long)src_ld_vec, (long long)dst_ld_vec);
+  if (nvec > 0 && (src == nullptr || dst == nullptr)) return fail(DC_ERR_NULL, "src or dst is NULL");
+  if (!aligned16(src) || !aligned16(dst)) return fail(DC_ERR_ALIGN, "src or dst not 16-byte aligned");
+  if (overlaps(src, rows_read * src_ld_vec * 16, dst, rows_written * dst_ld_vec * 16))
+    return fail(DC_ERR_ARG, "src and dst overlap");
+  return hip_status(dc::launch_stream_rows_shaped(src, src_ld_vec, rows_read, dst, dst_ld_vec,
+                                                  rows_written, nvec, group, cap,
+                                                  static_cast<hipStream_t>(stream)),
+                    "shaped stream rows launch");
 }
 
 }  // extern "C"

@@ -60,6 +60,27 @@ __device__ __forceinline__ void store16(u32x4* p, u32x4 v) {
   else *p = v;
 }
 
+// Buffer resource word 3 for raw (untyped) buffer accesses on gfx9-class
+// GPUs: 32-bit data format, everything else zero.
+constexpr int32_t kBufferFlags = 0x00020000;
+
+// One 16-byte store through a buffer resource over `bytes` bytes from
+// `row_base`, with cache-policy bits AUX (gfx950: bit 0 sc0, bit 1 nt, bit 4
+// sc1).  Offsets at or past `bytes` are dropped by the hardware.
+template <int AUX>
+__device__ __forceinline__ void store_buf(u32x4* row_base, int32_t bytes, int32_t off, u32x4 v) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(row_base, (short)0, bytes, kBufferFlags);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, AUX);
+}
+
+// Cache policies of the planned flush's streams (and of the access-mix
+// reference that runs at the same shapes), from an interleaved sweep on the
+// 402.8M-element W = 8 flush: stores of tiles that write every row ran 3-4%
+// faster with sc0 sc1 nt than with nt alone; one-row tiles 0.5% with nt sc1.
+constexpr int kStoreOneRow = 18;   // nt sc1
+constexpr int kStoreAllRows = 19;  // sc0 sc1 nt
+
 // ---------------------------------------------------------------------------
 // Folding helpers shared by the streaming kernels.  A contribution is
 // pre-divided by the communicator size c when PRE is set: a multiply by the

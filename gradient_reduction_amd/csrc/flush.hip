@@ -11,15 +11,22 @@
 // offset never breaks alignment; a vector can still straddle a task or
 // bucket boundary, and those vectors take an element-wise path.
 //
-// A workgroup of one wave (64 threads) owns a tile of 64*U consecutive
-// vectors; tiles of about 128 vectors measured 2-4% faster than 512 on every
-// flush path (more, smaller tiles spread each bucket more evenly).  It
-// finds the tasks overlapping its tile with a block-wide k-ary search over
-// the sorted task table, stages them in LDS with their roots already
-// resolved through the owner map ("roots precomputed for the whole bucket"),
-// then streams its vectors: W 16-byte row loads, an fp32 fold in rank order,
-// one 16-byte store to the owner row or W stores (AllReduce).  This is a
-// streaming reduction with no reuse: no MFMA, HBM bound.
+// Searched flush: a workgroup of one wave (64 threads) owns a tile of 64*U
+// consecutive vectors; tiles of about 128 vectors measured 2-4% faster than
+// 512 on every flush path (more, smaller tiles spread each bucket more
+// evenly).  It finds the tasks overlapping its tile with a block-wide k-ary
+// search over the sorted task table, stages them in LDS with their roots
+// resolved through the owner map before any row is read (the issue's design
+// points resolve a bucket's roots ahead of its reduction), then streams its
+// vectors: W 16-byte row loads, an fp32 fold in rank order, one 16-byte
+// store to the owner row or W stores (AllReduce).
+//
+// Planned flush: a plan built once per bucket layout on the host gives every
+// tile of 64 vectors its task range and, for a tile inside one task, its
+// root.  A one-wave workgroup takes one plan tile; a tile inside one task
+// streams with no search and no staging.
+//
+// This is a streaming reduction with no reuse: no MFMA, HBM bound.
 
 #include "device_common.h"
 #include "internal.h"
@@ -43,6 +50,7 @@ constexpr int kStage = kFT;  // tasks staged in LDS per pass over a tile (one pe
 #define DC_FLUSH_NTS 1    // nontemporal result stores
 #endif
 
+
 struct FlushParams {
   const void* in;
   void* out;
@@ -64,8 +72,8 @@ struct FlushParams {
   int32_t csize[DC_MAX_COMMS];
   int32_t cstride[DC_MAX_COMMS];
   float cinv[DC_MAX_COMMS];  // 1/c when c is a power of two, else 0
-  const dc_tile* tiles;      // planned flush: one record per tile, else NULL
-  int64_t root_tiles;        // planned: tiles that write one row (host side: the launch shape)
+  const dc_tile* tiles;      // planned flush: one record per plan tile, else NULL
+  int64_t root_tiles;        // planned: tiles that write one row (host side: the residency cap)
 };
 
 // Pre-division modes: none, multiply by an exact power-of-two reciprocal
@@ -262,11 +270,14 @@ __device__ __forceinline__ void elem_flush(const FlushParams& p, int64_t col, in
 }
 
 
-// WT > 0: W known at compile time, every communicator of the launch is the
-// data-parallel one or the single shape (C2, S2) (C2 = 0: none).  WT = 0:
-// any W and any communicators, all at run time.
+// The vectors [t0, t1) of the bucket's grid (relative to v0, at most kFT*U
+// of them, thread i taking t0 + i + u*kFT) whose tasks are first..last of the
+// task table: staged in LDS in chunks of kStage, roots resolved; vectors
+// inside one task stream, vectors cut by an edge go element by element.
+// Every thread of the workgroup must call it (it synchronizes).
 template <bool BF16, int WT, int C2, int S2, int PRE, int U, bool NT, bool Z2>
-__global__ __launch_bounds__(kFT) void k_flush(FlushParams p) {
+__device__ void flush_staged(const FlushParams& p, int64_t t0, int64_t t1, int32_t first,
+                             int32_t last) {
   static_assert(U <= 32, "slow-vector mask is 32 bits");
   constexpr int E = BF16 ? 8 : 4;
   __shared__ int64_t s_off[kStage];
@@ -279,47 +290,9 @@ __global__ __launch_bounds__(kFT) void k_flush(FlushParams p) {
   __shared__ int64_t s_za[Z2 ? kStage : 1];
   __shared__ int64_t s_zs[Z2 ? kStage : 1];
 
-  const int64_t tile = blockIdx.x;
-  const int64_t t0 = tile * (kFT * U);
-  const int64_t t1 = min(t0 + (int64_t)(kFT * U), p.nv);
-  // the tile's columns, relative to the bucket
+  // the range's columns, relative to the bucket
   const int64_t lo = max((p.v0 + t0) * E, p.c0) - p.c0;
   const int64_t hi = min((p.v0 + t1) * E, p.c1) - p.c0;
-
-  int32_t first, last;
-  if (p.tiles != nullptr) {
-    // planned: the tile's record replaces the search; a tile inside one task
-    // streams straight away (record fields clamped to their ranges)
-    const dc_tile rec = p.tiles[tile_slot(tile, (int64_t)gridDim.x)];
-    if (rec.flags & 1) {
-      int32_t comm = (rec.flags >> 8) & 0xFF;
-      comm = comm < p.ncomms ? comm : 0;
-      const int32_t root = (comm == 0 && rec.root >= 0 && rec.root < p.W) ? rec.root : -1;
-      int32_t fc, fs;
-      float finv;
-      comm_shape(p, comm, fc, fs, finv);
-#pragma unroll 1
-      for (int u = 0; u < U; ++u) {
-        const int64_t tv = t0 + threadIdx.x + (int64_t)u * kFT;
-        if (tv >= t1) break;
-        const int64_t av = p.v0 + tv;
-        if constexpr (WT > 0) {
-          u32x4 x[WT];
-          load_rows<BF16, WT, NT>(p, av, x);
-          fold_store_shape<BF16, WT, C2, S2, PRE>(p, x, av, root, fc);
-        } else {
-          vec_generic<BF16, NT>(p, av, root, fc, fs, finv);
-        }
-      }
-      return;
-    }
-    first = max(rec.first, 0);
-    last = min(rec.last, p.ntasks - 1);
-  } else {
-    kary_bounds<kFT>(p.ntasks, [&](int32_t i) { return p.tasks[i].offset; }, lo, hi, first, last);
-    first = max(first - 1, 0);  // the task holding column lo
-    last = last - 1;            // the last task starting before hi
-  }
 
   for (int32_t base = first; base <= last; base += kStage) {
     const int32_t cnt = min(kStage, last - base + 1);
@@ -358,60 +331,37 @@ __global__ __launch_bounds__(kFT) void k_flush(FlushParams p) {
 
     // phase 1: vectors inside one task; phase 2: vectors cut by an edge.
     uint32_t slow = 0;
-    if constexpr (WT > 0) {
 #pragma unroll 1
-      for (int u = 0; u < U; ++u) {
-        const int64_t tv = t0 + threadIdx.x + (int64_t)u * kFT;
-        if (tv >= t1) break;
-        const int64_t av = p.v0 + tv;
-        const int64_t rc = av * E - p.c0;  // the vector's first column, relative
-        const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
-        if (e_lo >= e_hi) continue;
-        const int32_t k = last_le(s_off, cnt, e_lo);
-        bool whole = e_lo == rc && e_hi == rc + E && s_off[k] <= rc && s_end[k] >= rc + E;
-        int32_t vroot = s_root[k];
-        if constexpr (Z2) {
-          // every element goes to the rank of its partition; a vector cut by
-          // a partition boundary takes the element path
-          if (whole && s_zs[k] > 0) {
-            const int64_t pos = s_za[k] + (rc - s_off[k]);
-            const int64_t q0 = pos / s_zs[k], q1 = (pos + E - 1) / s_zs[k];
-            if (q0 == q1 && q0 < WT) vroot = (int32_t)q0;
-            else whole = false;
-          }
+    for (int u = 0; u < U; ++u) {
+      const int64_t tv = t0 + threadIdx.x + (int64_t)u * kFT;
+      if (tv >= t1) break;
+      const int64_t av = p.v0 + tv;
+      const int64_t rc = av * E - p.c0;  // the vector's first column, relative
+      const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
+      if (e_lo >= e_hi) continue;
+      const int32_t k = last_le(s_off, cnt, e_lo);
+      bool whole = e_lo == rc && e_hi == rc + E && s_off[k] <= rc && s_end[k] >= rc + E;
+      int32_t vroot = s_root[k];
+      if constexpr (Z2) {
+        // every element goes to the rank of its partition; a vector cut by
+        // a partition boundary takes the element path
+        if (whole && s_zs[k] > 0) {
+          const int64_t pos = s_za[k] + (rc - s_off[k]);
+          const int64_t q0 = pos / s_zs[k], q1 = (pos + E - 1) / s_zs[k];
+          if (q0 == q1 && q0 < (WT > 0 ? WT : p.W)) vroot = (int32_t)q0;
+          else whole = false;
         }
-        if (whole) {
+      }
+      if (whole) {
+        if constexpr (WT > 0) {
           u32x4 x[WT];
           load_rows<BF16, WT, NT>(p, av, x);
           fold_store_shape<BF16, WT, C2, S2, PRE>(p, x, av, vroot, s_csz[k]);
         } else {
-          slow |= 1u << u;
-        }
-      }
-    } else {
-#pragma unroll 1
-      for (int u = 0; u < U; ++u) {
-        const int64_t tv = t0 + threadIdx.x + (int64_t)u * kFT;
-        if (tv >= t1) break;
-        const int64_t av = p.v0 + tv;
-        const int64_t rc = av * E - p.c0;
-        const int64_t e_lo = max(rc, clo), e_hi = min(rc + E, chi);
-        if (e_lo >= e_hi) continue;
-        const int32_t k = last_le(s_off, cnt, e_lo);
-        bool whole = e_lo == rc && e_hi == rc + E && s_off[k] <= rc && s_end[k] >= rc + E;
-        int32_t vroot = s_root[k];
-        if constexpr (Z2) {
-          if (whole && s_zs[k] > 0) {
-            const int64_t pos = s_za[k] + (rc - s_off[k]);
-            const int64_t q0 = pos / s_zs[k], q1 = (pos + E - 1) / s_zs[k];
-            if (q0 == q1 && q0 < p.W) vroot = (int32_t)q0;
-            else whole = false;
-          }
-        }
-        if (whole)
           vec_generic<BF16, NT>(p, av, vroot, s_csz[k], s_cst[k], s_cinv[k]);
-        else
-          slow |= 1u << u;
+        }
+      } else {
+        slow |= 1u << u;
       }
     }
 #pragma unroll 1
@@ -437,30 +387,173 @@ __global__ __launch_bounds__(kFT) void k_flush(FlushParams p) {
   }
 }
 
-// Workgroups kept resident per compute unit by a planned launch (0: no cap).
-// The one-wave workgroups of a planned tile stream with no search in front,
-// and fewer of them in flight at once measured faster than a full compute
-// unit: at W = 8, about 64 KB of row loads per compute unit (8 workgroups)
-// for tiles that write one row, and 32 KB (4) for tiles that write all eight,
-// whose stores take their own share of the memory system; at W = 16 (fp32
-// measured), 6 and 3; at W = 4 (bf16 measured), 12 and 8.
-int planned_cap(int32_t W, bool one_row) {
-  if (W >= 16) return one_row ? 6 : 3;
-  if (W >= 8) return one_row ? 8 : 4;
-  if (W >= 4) return one_row ? 12 : 8;
+// The task range of vectors [t0, t1) by a block-wide k-ary search of the
+// sorted task table: the task holding the first column through the last
+// task starting before the range's end.  Every thread must call it.
+template <int E>
+__device__ __forceinline__ void search_range(const FlushParams& p, int64_t t0, int64_t t1,
+                                             int32_t& first, int32_t& last) {
+  const int64_t lo = max((p.v0 + t0) * E, p.c0) - p.c0;
+  const int64_t hi = min((p.v0 + t1) * E, p.c1) - p.c0;
+  kary_bounds<kFT>(p.ntasks, [&](int32_t i) { return p.tasks[i].offset; }, lo, hi, first, last);
+  first = max(first - 1, 0);  // the task holding column lo
+  last = last - 1;            // the last task starting before hi
+}
+
+// Searched flush.  WT > 0: W known at compile time, every communicator of
+// the launch is the data-parallel one or the single shape (C2, S2) (C2 = 0:
+// none).  WT = 0: any W and any communicators, all at run time.
+template <bool BF16, int WT, int C2, int S2, int PRE, int U, bool NT, bool Z2>
+__global__ __launch_bounds__(kFT) void k_flush(FlushParams p) {
+  constexpr int E = BF16 ? 8 : 4;
+  const int64_t t0 = (int64_t)blockIdx.x * (kFT * U);
+  const int64_t t1 = min(t0 + (int64_t)(kFT * U), p.nv);
+  int32_t first, last;
+  search_range<E>(p, t0, t1, first, last);
+  flush_staged<BF16, WT, C2, S2, PRE, U, NT, Z2>(p, t0, t1, first, last);
+}
+
+// Planned flush: workgroup b takes plan tile b, kPlanTile vectors (thread i:
+// vector i).  With PF, a full tile issues its W row loads together with the
+// load of its plan record (the row addresses do not depend on the plan), so
+// the record arrives under the rows' latency.  A tile the record marks
+// whole (inside one task and the bucket) folds and stores straight away, to
+// its root row or to every member; any other tile takes the staged path over
+// the record's task range.
+template <bool BF16, int WT, int C2, int S2, int PRE, bool NT, bool Z2, bool PF>
+__global__ __launch_bounds__(kFT) void k_flush_planned(FlushParams p) {
+  constexpr int E = BF16 ? 8 : 4;
+  const int64_t tile = blockIdx.x;
+  const int64_t t0 = tile * kPlanTile, t1 = min(t0 + kPlanTile, p.nv);
+  const int64_t slot = tile_slot(tile, (int64_t)gridDim.x);
+  if constexpr (WT > 0) {
+    if (t1 - t0 == kPlanTile) {
+      const int64_t av = p.v0 + t0 + threadIdx.x;
+      u32x4 x[WT];
+      if constexpr (PF) load_rows<BF16, WT, NT>(p, av, x);
+      const dc_tile rec = p.tiles[slot];
+      if (rec.flags & 1) {
+        int32_t comm = (rec.flags >> 8) & 0xFF;
+        comm = comm < p.ncomms ? comm : 0;
+        const int32_t root = (comm == 0 && rec.root >= 0 && rec.root < p.W) ? rec.root : -1;
+        int32_t fc, fs;
+        float finv;
+        comm_shape(p, comm, fc, fs, finv);
+        if constexpr (!PF) load_rows<BF16, WT, NT>(p, av, x);
+        if (C2 == 0 || fc == WT) {
+          constexpr float inv = 1.0f / (float)WT;
+          float acc[E];
+#pragma unroll
+          for (int i = 0; i < WT; ++i) fold_vec<BF16, PRE>(acc, x[i], i == 0, inv, (float)WT);
+          const u32x4 y = pack_vec<BF16>(acc);
+          u32x4* out = reinterpret_cast<u32x4*>(p.out) + (p.v0 + t0);
+          const int64_t ldo = p.ld_out / E;
+          constexpr int32_t bytes = kPlanTile * 16;
+          if (root >= 0) {
+            store_buf<kStoreOneRow>(out + root * ldo, bytes, threadIdx.x * 16, y);
+          } else {
+#pragma unroll
+            for (int r = 0; r < WT; ++r) store_buf<kStoreAllRows>(out + r * ldo, bytes, threadIdx.x * 16, y);
+          }
+        } else {
+          // the launch's one sub-communicator shape: block by block
+          fold_store_shape<BF16, WT, C2, S2, PRE>(p, x, av, root, fc);
+        }
+        return;
+      }
+      if constexpr (PF) {
+        // the rows are used on this path too, so the compiler keeps their
+        // loads ahead of the record test (here it only waits for them)
+#pragma unroll
+        for (int i = 0; i < WT; ++i) asm volatile("" ::"v"(x[i]));
+      }
+    }
+  }
+  const dc_tile rec = p.tiles[slot];
+  if (WT == 0 && (rec.flags & 1) && t1 - t0 == kPlanTile) {
+    int32_t comm = (rec.flags >> 8) & 0xFF;
+    comm = comm < p.ncomms ? comm : 0;
+    const int32_t root = (comm == 0 && rec.root >= 0 && rec.root < p.W) ? rec.root : -1;
+    int32_t fc, fs;
+    float finv;
+    comm_shape(p, comm, fc, fs, finv);
+    vec_generic<BF16, NT>(p, p.v0 + t0 + threadIdx.x, root, fc, fs, finv);
+    return;
+  }
+  const int32_t first = max(rec.first, 0), last = min(rec.last, p.ntasks - 1);
+  flush_staged<BF16, WT, C2, S2, PRE, 1, NT, Z2>(p, t0, t1, first, last);
+}
+
+// Planned launch shapes (one-wave workgroups, one plan tile each, LDS
+// reserved to cap residency), from interleaved sweeps on the 402.8M-element
+// W = 8 bf16 and the 1.2B-element W = 16 fp32 flushes: W = 8 buckets whose
+// tiles mostly write one row ran fastest at 8 workgroups per compute unit,
+// buckets whose tiles write every row at 5; W = 16 at 6 and 3.  W = 4 keeps
+// the caps measured there with two-vector tiles.  Other W take the caps of
+// the nearest measured W below them.  A searched launch keeps full
+// occupancy: its per-tile search needs the other resident workgroups to
+// hide it.
+#ifndef DC_PLAN_CAP_W8
+#define DC_PLAN_CAP_W8 8, 5     // W = 8: one-row buckets, every-row buckets
+#endif
+#ifndef DC_PLAN_CAP_W16
+#define DC_PLAN_CAP_W16 6, 3
+#endif
+#ifndef DC_PLAN_CAP_W4
+#define DC_PLAN_CAP_W4 12, 8
+#endif
+// Whether a planned workgroup loads its tile's rows together with its plan
+// record (before it knows the tile's root): faster at W = 8 (6.49 against
+// 6.27 TB/s on the 402.8M-element flush), much slower at W = 16 fp32 (4.8
+// against 6.0 TB/s per bucket).
+#ifndef DC_PLAN_PF_W8
+#define DC_PLAN_PF_W8 1
+#endif
+#ifndef DC_PLAN_PF_W16
+#define DC_PLAN_PF_W16 0
+#endif
+#ifndef DC_PLAN_PF_W4
+#define DC_PLAN_PF_W4 1
+#endif
+constexpr bool plan_prefetch(int WT) {
+  return WT == 8 ? DC_PLAN_PF_W8 != 0 : WT == 16 ? DC_PLAN_PF_W16 != 0 : WT == 4 ? DC_PLAN_PF_W4 != 0 : false;
+}
+
+int cap_pick(int one, int all, bool one_row) { return one_row ? one : all; }
+
+int plan_cap(int32_t W, bool one_row) {
+  if (W >= 16) return cap_pick(DC_PLAN_CAP_W16, one_row);
+  if (W >= 8) return cap_pick(DC_PLAN_CAP_W8, one_row);
+  if (W >= 4) return cap_pick(DC_PLAN_CAP_W4, one_row);
   return 0;
 }
 
-// Dynamic LDS a launch of one k_flush instantiation reserves, unused, so
-// that at most `cap` of its workgroups fit in one compute unit's LDS.
-template <bool BF16, int WT, int C2, int S2, int PRE, bool Z2>
-size_t flush_pad(int cap) {
-  auto kern = k_flush<BF16, WT, C2, S2, PRE, DC_FLUSH_U, DC_FLUSH_NT != 0, Z2>;
+// Dynamic LDS a launch of one kernel reserves, unused, so that at most `cap`
+// of its workgroups fit in one compute unit's LDS.
+template <typename K>
+size_t kernel_pad(K* kern, int cap) {
   return occupancy_pad(reinterpret_cast<const void*>(kern), cap);
+}
+
+template <bool BF16, int WT, int C2, int S2, int PRE, bool Z2>
+hipError_t launch_planned(const FlushParams& p, hipStream_t stream) {
+  const FlushTiles g = plan_tiles(BF16 ? DC_BF16 : DC_F32, p.c0, p.c1);
+  if (g.count == 0) return hipSuccess;
+  FlushParams q = p;
+  q.v0 = g.v0;
+  q.nv = g.nv;
+  const int cap = plan_cap(p.W, 2 * p.root_tiles >= g.count);
+  auto kern = k_flush_planned<BF16, WT, C2, S2, PRE, DC_FLUSH_NT != 0, Z2, plan_prefetch(WT)>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)g.count), dim3(kFT), kernel_pad(kern, cap), stream, q);
+  return hipGetLastError();
 }
 
 template <bool BF16, int WT, int C2, int S2, int PRE>
 hipError_t launch_kernel(const FlushParams& p, hipStream_t stream) {
+  if (p.tiles != nullptr) {
+    return p.flat != nullptr ? launch_planned<BF16, WT, C2, S2, PRE, true>(p, stream)
+                             : launch_planned<BF16, WT, C2, S2, PRE, false>(p, stream);
+  }
   constexpr int U = DC_FLUSH_U;
   // Tiles sit on absolute multiples of the tile size, not at the bucket's
   // first vector: a bucket that starts inside a cache line would otherwise
@@ -472,15 +565,12 @@ hipError_t launch_kernel(const FlushParams& p, hipStream_t stream) {
   FlushParams q = p;
   q.v0 = g.v0;
   q.nv = g.nv;
-  const int cap = p.tiles != nullptr ? planned_cap(p.W, 2 * p.root_tiles >= g.count) : 0;
   if (q.flat != nullptr) {
-    const size_t pad = flush_pad<BF16, WT, C2, S2, PRE, true>(cap);
     hipLaunchKernelGGL((k_flush<BF16, WT, C2, S2, PRE, U, DC_FLUSH_NT != 0, true>),
-                       dim3((unsigned)g.count), dim3(kFT), pad, stream, q);
+                       dim3((unsigned)g.count), dim3(kFT), 0, stream, q);
   } else {
-    const size_t pad = flush_pad<BF16, WT, C2, S2, PRE, false>(cap);
     hipLaunchKernelGGL((k_flush<BF16, WT, C2, S2, PRE, U, DC_FLUSH_NT != 0, false>),
-                       dim3((unsigned)g.count), dim3(kFT), pad, stream, q);
+                       dim3((unsigned)g.count), dim3(kFT), 0, stream, q);
   }
   return hipGetLastError();
 }
@@ -577,11 +667,11 @@ hipError_t launch_flush(const FlushLaunch& a, hipStream_t stream) {
   return a.dtype == DC_BF16 ? launch_dtype<true>(p, stream) : launch_dtype<false>(p, stream);
 }
 
-FlushTiles flush_tiles(int32_t dtype, int64_t c0, int64_t c1) {
-  static_assert(kFT * DC_FLUSH_U == 128, "the public tile record documents 128-vector tiles");
+namespace {
+FlushTiles tiles_of(int32_t dtype, int64_t c0, int64_t c1, int64_t tile) {
   const int64_t E = dtype == DC_BF16 ? 8 : 4;
   FlushTiles g;
-  g.tile = (int64_t)kFT * DC_FLUSH_U;
+  g.tile = tile;
   const int64_t first = c0 / E;
   const int64_t shift = first % g.tile;
   g.v0 = first - shift;
@@ -589,5 +679,16 @@ FlushTiles flush_tiles(int32_t dtype, int64_t c0, int64_t c1) {
   g.count = (g.nv + g.tile - 1) / g.tile;
   return g;
 }
+}  // namespace
+
+FlushTiles flush_tiles(int32_t dtype, int64_t c0, int64_t c1) {
+  return tiles_of(dtype, c0, c1, (int64_t)kFT * DC_FLUSH_U);
+}
+
+FlushTiles plan_tiles(int32_t dtype, int64_t c0, int64_t c1) {
+  static_assert(kPlanTile == kFT, "a plan tile is one vector per thread of a workgroup");
+  return tiles_of(dtype, c0, c1, kPlanTile);
+}
+
 
 }  // namespace dc

@@ -34,7 +34,7 @@ struct FlushLaunch {
   CommSpec comms[DC_MAX_COMMS];
   const dc_tile* tiles;  // planned flush when non-null (ntiles records)
   int64_t ntiles;
-  int64_t root_tiles;    // planned: tiles that write one row (picks the occupancy)
+  int64_t root_tiles;    // planned: tiles that write one row (picks the residency cap)
 };
 
 hipError_t launch_flush(const FlushLaunch& a, hipStream_t stream);
@@ -48,22 +48,28 @@ size_t occupancy_pad(const void* kernel, int cap);
 // KB of row accesses are in flight per compute unit (0 = no cap).
 int stream_cap(int rows, int u, int kb);
 
-// The flush kernel's tile grid over bucket columns [c0, c1) of a dtype: tile
-// b covers vectors [v0 + b*tile, v0 + min((b+1)*tile, nv)) in absolute
-// 16-byte column vectors.  Returns the tile count (0 for an empty bucket).
+// A tile grid over bucket columns [c0, c1) of a dtype: tile b covers
+// vectors [v0 + b*tile, v0 + min((b+1)*tile, nv)) in absolute 16-byte column
+// vectors.  `count` is the tile count (0 for an empty bucket).
 struct FlushTiles {
   int64_t v0;    // first vector of tile 0 (a multiple of the tile size)
   int64_t nv;    // vectors from v0 to the bucket's last one
   int64_t tile;  // vectors per tile
   int64_t count;
 };
+// The searched flush's grid: tiles of 128 vectors (2 per thread of a wave).
 FlushTiles flush_tiles(int32_t dtype, int64_t c0, int64_t c1);
 
-// Where tile b's plan record sits in a plan of n records: XCD-major.  The
-// hardware deals workgroups to the 8 XCDs in turn, so tile b runs on XCD
-// b mod 8; keeping each XCD's records together lets one 128-byte line serve
-// eight of its tiles from that XCD's L2, where tile order would have every
-// XCD fetch every line for one record in eight.
+// The planned flush's grid: plan tiles of kPlanTile vectors (one per thread
+// of a wave, one tile per workgroup).
+constexpr int64_t kPlanTile = 64;
+FlushTiles plan_tiles(int32_t dtype, int64_t c0, int64_t c1);
+
+// Where tile b's record sits among n records: XCD-major.  The hardware deals
+// workgroups to the 8 XCDs in turn, so workgroup b runs on XCD b mod 8;
+// keeping each XCD's records together lets one 128-byte line serve eight of
+// its workgroups from that XCD's L2, where tile order would have every XCD
+// fetch every line for one record in eight.
 __host__ __device__ inline int64_t tile_slot(int64_t b, int64_t n) {
   const int64_t r = b % 8, q = n / 8, rem = n % 8;
   return r * q + (r < rem ? r : rem) + b / 8;
@@ -79,6 +85,9 @@ struct GroupTable {
 hipError_t launch_partition_ids(int32_t num_params, const int64_t* numel, const GroupTable& g,
                                 int64_t* flat_offset, int64_t* part_size, int32_t* pid_offsets,
                                 int32_t* pids, int64_t pids_capacity, hipStream_t stream);
+
+hipError_t launch_param_part_size(int32_t num_params, const GroupTable& g, const int64_t* part_size,
+                                  int64_t* out, hipStream_t stream);
 
 hipError_t launch_owner_map(int32_t W, int32_t num_params, const int32_t* pid_offsets,
                             const int32_t* pids, int64_t pids_capacity, const GroupTable& g,
@@ -141,5 +150,9 @@ hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStre
 hipError_t launch_stream_rows(const void* src, int64_t src_ld_vec, int32_t rows_read, void* dst,
                               int64_t dst_ld_vec, int32_t rows_written, int64_t nvec,
                               hipStream_t stream);
+
+hipError_t launch_stream_rows_shaped(const void* src, int64_t src_ld_vec, int32_t rows_read,
+                                     void* dst, int64_t dst_ld_vec, int32_t rows_written,
+                                     int64_t nvec, int32_t group, int32_t cap, hipStream_t stream);
 
 }  // namespace dc

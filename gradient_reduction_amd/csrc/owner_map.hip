@@ -147,7 +147,31 @@ __global__ __launch_bounds__(kScanThreads) void k_owner_map(
   (void)P;
 }
 
+// ZeRO-2 partition size of every param: its group's S when the group is on
+// the data-parallel comm, else 0.  One thread per param; the group is found
+// by a scan of the (at most DC_MAX_GROUPS) group starts.
+__global__ __launch_bounds__(256) void k_param_part_size(int32_t P, GroupArgs ga,
+                                                         const int64_t* __restrict__ part_size,
+                                                         int64_t* __restrict__ out) {
+  const int32_t i = (int32_t)(blockIdx.x * 256 + threadIdx.x);
+  if (i >= P) return;
+  const GroupTable& g = ga.g;
+  int32_t grp = 0;
+  for (int32_t k = 1; k < g.num_groups; ++k)
+    if (g.begin[k] <= i) grp = k;
+  out[i] = g.eligible[grp] ? part_size[grp] : 0;
+}
+
 }  // namespace
+
+hipError_t launch_param_part_size(int32_t num_params, const GroupTable& g, const int64_t* part_size,
+                                  int64_t* out, hipStream_t stream) {
+  if (num_params <= 0) return hipSuccess;
+  GroupArgs ga{g};
+  hipLaunchKernelGGL(k_param_part_size, dim3((unsigned)((num_params + 255) / 256)), dim3(256), 0,
+                     stream, num_params, ga, part_size, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_partition_ids(int32_t num_params, const int64_t* numel, const GroupTable& g,
                                 int64_t* flat_offset, int64_t* part_size, int32_t* pid_offsets,

@@ -506,6 +506,66 @@ __global__ __launch_bounds__(kST) void k_stream_rows(const u32x4* __restrict__ s
   for (int r = 0; r < NW; ++r) store16<kNTS>(dst + r * dld + k, y);
 }
 
+// The same mix at a launch shape of the planned flush: each one-wave
+// workgroup takes G runs of 64 vectors; with one row written the G results
+// are stored together after the last load, with every row written each
+// vector's rows are stored as soon as it is folded; stores use the planned
+// flush's cache policies.  A workgroup short of G full runs (the tail) goes
+// vector by vector.
+template <int R, int NW, int G>
+__global__ __launch_bounds__(kST) void k_stream_rows_g(const u32x4* __restrict__ src,
+                                                       int64_t sld, u32x4* __restrict__ dst,
+                                                       int64_t dld, int64_t nvec) {
+  static_assert(kST == 64, "runs of one vector per thread of a wave");
+  const int64_t v0 = (int64_t)blockIdx.x * (kST * G);
+  if (v0 + kST * G <= nvec) {
+    constexpr int32_t bytes = G * kST * 16;
+    if constexpr (NW == 1) {
+      u32x4 y[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int64_t k = v0 + j * kST + threadIdx.x;
+        u32x4 x[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r] = load16<kNT>(src + r * sld + k);
+        y[j] = x[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) y[j] ^= x[r];
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) store_buf<kStoreOneRow>(dst + v0, bytes, (j * kST + threadIdx.x) * 16, y[j]);
+    } else {
+#pragma unroll 1
+      for (int j = 0; j < G; ++j) {
+        const int64_t k = v0 + j * kST + threadIdx.x;
+        u32x4 x[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r] = load16<kNT>(src + r * sld + k);
+        u32x4 y = x[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) y ^= x[r];
+#pragma unroll
+        for (int r = 0; r < NW; ++r)
+          store_buf<kStoreAllRows>(dst + r * dld + v0, bytes, (j * kST + threadIdx.x) * 16, y);
+      }
+    }
+    return;
+  }
+#pragma unroll 1
+  for (int j = 0; j < G; ++j) {
+    const int64_t k = v0 + j * kST + threadIdx.x;
+    if (k >= nvec) break;
+    u32x4 x[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[r] = load16<kNT>(src + r * sld + k);
+    u32x4 y = x[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) y ^= x[r];
+#pragma unroll
+    for (int r = 0; r < NW; ++r) store16<kNTS>(dst + r * dld + k, y);
+  }
+}
+
 // Row accesses in flight per compute unit (KB) at which each kernel below
 // measured fastest on the 7B-layer reduce-scatter / all-gather (W = 8) and
 // the W = 4 deferred reduce, 5-8% over a full compute unit (within 2% for
@@ -819,6 +879,26 @@ hipError_t launch_stream_rows(const void* src, int64_t src_ld_vec, int32_t rows_
   }
   DC_SR(4, 1) DC_SR(4, 4) DC_SR(8, 1) DC_SR(8, 8) DC_SR(16, 1) DC_SR(16, 16)
 #undef DC_SR
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_stream_rows_shaped(const void* src, int64_t src_ld_vec, int32_t rows_read,
+                                     void* dst, int64_t dst_ld_vec, int32_t rows_written,
+                                     int64_t nvec, int32_t group, int32_t cap, hipStream_t stream) {
+  if (nvec == 0) return hipSuccess;
+  const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+  u32x4* d4 = reinterpret_cast<u32x4*>(dst);
+#define DC_SRG(R, NW, G)                                                                       \
+  if (rows_read == R && rows_written == NW && group == G) {                                    \
+    auto kern = k_stream_rows_g<R, NW, G>;                                                     \
+    hipLaunchKernelGGL(kern, dim3(blocks_for(nvec, G)), dim3(kST), pad_for(kern, cap), stream, \
+                       s4, src_ld_vec, d4, dst_ld_vec, nvec);                                  \
+    return hipGetLastError();                                                                  \
+  }
+#define DC_SRG3(R, NW) DC_SRG(R, NW, 1) DC_SRG(R, NW, 2) DC_SRG(R, NW, 4)
+  DC_SRG3(4, 1) DC_SRG3(4, 4) DC_SRG3(8, 1) DC_SRG3(8, 8) DC_SRG3(16, 1) DC_SRG3(16, 16)
+#undef DC_SRG3
+#undef DC_SRG
   return hipErrorInvalidValue;
 }
 

@@ -68,6 +68,8 @@ _SIGS = {
     "dc_flush_bucket_planned": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
                                  _vp, _i32, _vp, _i32, _i32, _vp, _i64, _i64, _vp], _i32),
     "dc_probe_flush": ([_i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp], _i32),
+    "dc_holders": ([_i32, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _vp], _i32),
+    "dc_param_part_size": ([_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "dc_plan_relayout": ([_i32, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp], _i32),
     "dc_relayout_bucket": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp],
                            _i32),
@@ -83,6 +85,7 @@ _SIGS = {
     "dc_round_bf16": ([_vp, _vp, _i64, _vp], _i32),
     "dc_stream_copy": ([_vp, _vp, _i64, _vp], _i32),
     "dc_stream_rows": ([_vp, _i64, _i32, _vp, _i64, _i32, _i64, _vp], _i32),
+    "dc_stream_rows_shaped": ([_vp, _i64, _i32, _vp, _i64, _i32, _i64, _i32, _i32, _vp], _i32),
 }
 
 
@@ -252,6 +255,28 @@ def dc_probe_flush(W, dtype, tasks, num_tasks, owner, num_params, pid_offsets, p
     return out
 
 
+def dc_holders(W, tasks, num_tasks, num_params, pid_offsets, pids, comms, num_comms):
+    """Host only; returns a [num_tasks, W] bool array."""
+    tp, _a = _host(tasks, TASK_DTYPE)
+    po, _b = _host(pid_offsets, np.int32)
+    pp, _c = _host(pids, np.int32) if pids is not None and len(pids) else (None, None)
+    cp, _d = _host(comms, COMM_DTYPE)
+    out = np.zeros((max(num_tasks, 0), W), np.uint8)
+    _check("dc_holders", lib().dc_holders(W, tp, num_tasks, num_params, po, pp, cp, num_comms,
+                                          out.ctypes.data_as(_vp)))
+    return out.astype(bool)
+
+
+def dc_param_part_size(W, num_params, num_groups, group_begin, group_comm_size,
+                       group_rank_to_global, part_size, param_part_size, stream=None):
+    gb, _a = _host(group_begin, np.int32)
+    cs, _b = _host(group_comm_size, np.int32)
+    rg, _c = _host(np.asarray(group_rank_to_global, np.int32).reshape(-1), np.int32)
+    _check("dc_param_part_size", lib().dc_param_part_size(
+        W, num_params, num_groups, gb, cs, rg, _dev(part_size), _dev(param_part_size),
+        _stream(stream)))
+
+
 def dc_plan_flush(W, dtype, bucket_col, bucket_numel, tasks, num_tasks, owner, flat_offset,
                   part_size, num_params, comms, num_comms):
     """Host only; returns (dc_tile records as TILE_DTYPE, root tile count).
@@ -360,6 +385,13 @@ def dc_stream_copy(src, dst, nbytes, stream=None):
 def dc_stream_rows(src, src_ld_vec, rows_read, dst, dst_ld_vec, rows_written, nvec, stream=None):
     _check("dc_stream_rows", lib().dc_stream_rows(_dev(src), src_ld_vec, rows_read, _dev(dst),
                                                   dst_ld_vec, rows_written, nvec, _stream(stream)))
+
+
+def dc_stream_rows_shaped(src, src_ld_vec, rows_read, dst, dst_ld_vec, rows_written, nvec, group,
+                          cap, stream=None):
+    _check("dc_stream_rows_shaped", lib().dc_stream_rows_shaped(
+        _dev(src), src_ld_vec, rows_read, _dev(dst), dst_ld_vec, rows_written, nvec, group, cap,
+        _stream(stream)))
 
 
 def tasks_array(tasks):

@@ -80,26 +80,23 @@ class Zero1FlushExecutor:
         self.tile_begin = None
         self.root_tiles = None
         # ZeRO-2: the partition size of each param's group, 0 for groups on
-        # another communicator (they keep AllReduce)
-        psize = np.zeros(max(self.P, 1), np.int64)
-        for g in range(self.G):
-            b, e = self.group_begin[g], self.group_begin[g + 1]
-            elig = (self.group_comm_size[g] == W and
-                    all(int(self.group_rank_to_global[g, i]) == i for i in range(W)))
-            if elig:
-                T = int(sum(int(n) for n in list(numel)[b:e]))
-                psize[b:e] = -(-T // self.group_parts[g])
-        self.h_psize = psize[:self.P]
-        self.d_psize = torch.from_numpy(psize).to(dev)
+        # another communicator (they keep AllReduce), from dc_param_part_size
+        self.d_psize = torch.zeros(max(self.P, 1), dtype=torch.int64, device=dev)
+        self._h_psize: Optional[np.ndarray] = None
 
     def build_owner_map(self, stream=None) -> None:
-        """Partition lists and owner map on the device (no host synchronization)."""
+        """Partition lists and owner map on the device (no host
+        synchronization); in ZeRO-2 mode also every param's partition size."""
         dc.dc_partition_ids(self.W, self.P, self.d_numel, self.G, self.group_begin,
                             self.group_parts, self.d_flat, self.d_part_size, self.d_pid_off,
                             self.d_pids, self.pids_capacity, stream)
         dc.dc_build_owner_map(self.W, self.P, self.d_pid_off, self.d_pids, self.pids_capacity,
                               self.G, self.group_begin, self.group_comm_size,
                               self.group_rank_to_global, self.d_owner, self.d_counts, stream)
+        if self.zero2:
+            dc.dc_param_part_size(self.W, self.P, self.G, self.group_begin, self.group_comm_size,
+                                  self.group_rank_to_global, self.d_part_size, self.d_psize,
+                                  stream)
 
     def fetch_metadata(self) -> None:
         """Copy the owner map and partition lists to the host (synchronizes);
@@ -108,6 +105,15 @@ class Zero1FlushExecutor:
         self.h_pid_off = self.d_pid_off.cpu().numpy()
         self.h_pids = self.d_pids[:int(self.h_pid_off[-1])].cpu().numpy()
         self.h_counts = self.d_counts.cpu().numpy()
+        self._h_psize = self.d_psize[:self.P].cpu().numpy()
+
+    @property
+    def h_psize(self) -> np.ndarray:
+        """Host copy of every param's ZeRO-2 partition size (fetched, with a
+        synchronization, on first use after build_owner_map)."""
+        if self._h_psize is None:
+            self._h_psize = self.d_psize[:self.P].cpu().numpy()
+        return self._h_psize
 
     def ratio_line(self) -> str:
         owners = int(self.h_counts[0::2].sum())
@@ -180,20 +186,14 @@ class Zero1FlushExecutor:
 
     def holders(self, b: int) -> np.ndarray:
         """[n_tasks, W] bool for bucket b: rank r keeps a gradient buffer for
-        the task's param, i.e. its partition holds part of it (in every block
-        of a sub-communicator).  These are the ranks the copy-out writes and
-        the probe's `kept` counts."""
+        the task's param (dc_holders: its partition holds part of it, in
+        every block of a sub-communicator).  These are the ranks the copy-out
+        writes and the probe's `kept` counts."""
         if self.h_owner is None:
             self.fetch_metadata()
-        W = self.W
-        bk = self.buckets[b]
-        out = np.zeros((len(bk.tasks), W), bool)
-        for k, (_, _, param, comm) in enumerate(bk.tasks):
-            c, st = int(self.comms[comm]["size"]), int(self.comms[comm]["stride"])
-            for q in self.h_pids[self.h_pid_off[param]:self.h_pid_off[param + 1]]:
-                for blk in range(W // c):
-                    out[k, (blk * c if st == 1 else blk) + int(q) * st] = True
-        return out
+        t = self.h_tasks[b]
+        return dc.dc_holders(self.W, t, len(t), self.P, self.h_pid_off, self.h_pids, self.comms,
+                             len(self.comms))
 
     def register_buffers(self, in_addr: np.ndarray, out_addr: np.ndarray, planned: bool = True) -> None:
         """in_addr, out_addr: [W, P] device addresses of rank r's gradient of

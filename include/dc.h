@@ -125,16 +125,16 @@ typedef struct {
   int64_t reserved;
 } dc_piece;
 
-/* One tile of a planned bucket flush (dc_plan_flush): the flush kernel cuts
- * a bucket into tiles of 128 consecutive 16-byte column vectors (2 KiB of
- * each row; tile b of a bucket starting at column c covers the row's vectors
- * [v0 + 128 b, v0 + 128 (b + 1)), v0 = floor(c / E / 128) * 128 with E
- * elements per vector, clipped to the bucket's last vector), and this record
- * says which tasks a tile overlaps and, when the whole tile lies inside one
- * task and the bucket, which rows receive its sums.  16 bytes.  A plan of n
- * records keeps them XCD-major, in the order the 8 XCDs run the tiles: the
- * record of tile b sits at index (b mod 8) floor(n/8) + min(b mod 8, n mod 8)
- * + floor(b/8).
+/* One tile record of a planned bucket flush (dc_plan_flush).  The planned
+ * flush cuts a bucket into plan tiles of 64 consecutive 16-byte column
+ * vectors (1 KiB of each row; tile b of a bucket starting at column c covers
+ * the row's vectors [v0 + 64 b, v0 + 64 (b + 1)), v0 = floor(c / E / 64) * 64
+ * with E elements per vector, clipped to the bucket's last vector), one
+ * workgroup per tile, and this record says which tasks a tile overlaps and,
+ * when the whole tile lies inside one task and the bucket, which rows
+ * receive its sums.  16 bytes.  A plan of n records keeps them XCD-major, in
+ * the order the 8 XCDs run the tiles: the record of tile b sits at index
+ * (b mod 8) floor(n/8) + min(b mod 8, n mod 8) + floor(b/8).
  *   first, last   indices of the first and last task overlapping the tile
  *                 (last < first: none)
  *   root          whole tile inside one task: the row that alone receives
@@ -184,10 +184,10 @@ dc_status dc_partition_ids(int32_t W, int32_t num_params, const int64_t* numel,
                            int32_t* pid_offsets, int32_t* pids, int64_t pids_capacity,
                            void* stream);
 
-/* Owner map ([DS] Design points): a param with exactly one partition
- * entry has exactly one owner, that entry's rank; a param with two or more
- * entries (it straddles a partition boundary) or none gets -1, meaning
- * AllReduce.  A group takes part only when its communicator is the
+/* Owner map ([DS] Design points): a param whose partition list has a
+ * single element is held by one rank only and gets that rank as its owner; a
+ * param listed in two or more partitions (it straddles a partition
+ * boundary) or in none gets -1, meaning AllReduce.  A group takes part only when its communicator is the
  * data-parallel one: group_comm_size[g] == W and group rank i maps to global
  * rank i for every i; every param of another group gets -1.
  *   pid_offsets, pids      device CSR from dc_partition_ids; pids_capacity is
@@ -272,9 +272,9 @@ dc_status dc_flush_bucket_zero2(int32_t W, int32_t dtype, const void* slab_in, i
 
 /* Plan of a bucket flush ([DS] Design points: the roots of a bucket's
  * collectives are computed for the whole bucket before any reduction).
- * Host only, once per bucket layout: for every tile of the flush kernel's
- * grid over columns [bucket_col, bucket_col + bucket_numel), the tasks it
- * overlaps and, for a tile inside one task, the rows its sums go to:
+ * Host only, once per bucket layout: for every plan tile (see dc_tile) over
+ * columns [bucket_col, bucket_col + bucket_numel), the tasks it overlaps
+ * and, for a tile inside one task, the rows its sums go to:
  *   owner-map mode (flat_offset == NULL): the owner owner[param] of a task on
  *   comm 0 when owner is given and the entry lies in [0, W), else -1;
  *   ZeRO-2 mode (flat_offset and part_size given, owner NULL): for a task on
@@ -303,15 +303,16 @@ dc_status dc_plan_flush(int32_t W, int32_t dtype, int64_t bucket_col, int64_t bu
 /* Bucket flush with a plan (dc_plan_flush): the same results, bit for bit,
  * as dc_flush_bucket (flat_offset == NULL) or dc_flush_bucket_zero2
  * (flat_offset and part_size given, owner NULL) with the same arguments.  A
- * tile the plan marks whole streams its vectors with no per-tile search of
- * the task table; the launch also keeps fewer workgroups resident per
- * compute unit (it reserves LDS it does not use), which fewer, longer
- * streams of loads in flight at once measured faster for this access mix.
+ * tile the plan marks whole streams its vectors with no search of the task
+ * table and no staging; other tiles use the record's task range.  The
+ * launch also keeps fewer workgroups resident per compute unit (it reserves
+ * LDS it does not use): fewer, longer streams of loads in flight at once
+ * measured faster for this access mix.
  *   tiles, num_tiles   device dc_tile[num_tiles] from dc_plan_flush for this
  *                      bucket, dtype, layout and map; num_tiles must equal
  *                      the planned count (else DC_ERR_SHAPE)
  *   root_tiles         the count dc_plan_flush reported, in [0, num_tiles]
- *                      (else DC_ERR_ARG); it only picks the launch shape:
+ *                      (else DC_ERR_ARG); it only picks the residency cap:
  *                      buckets whose tiles mostly write one row keep more
  *                      workgroups per compute unit than those that write
  *                      every row, and any value gives the same results
@@ -421,6 +422,41 @@ dc_status dc_probe_flush(int32_t W, int32_t dtype, const dc_task* tasks, int32_t
                          const int32_t* owner, int32_t num_params, const int32_t* pid_offsets,
                          const int32_t* pids, const dc_comm* comms, int32_t num_comms,
                          int32_t pre_div, dc_probe* out);
+
+/* Holders of every task's param ([DS] problem statement: the copy-out after
+ * the reduction writes each rank's gradient buffer and skips the ranks
+ * whose buffer is empty; a rank keeps a buffer for a param when its
+ * optimizer partition holds part of it, [DS] Design points).  Host only:
+ * holders[t*W + r] = 1 when rank r's partition (its group rank, in every
+ * block of a sub-communicator) is in the partition list of task t's param,
+ * else 0 -- the ranks whose elements dc_probe_flush counts as kept, and the
+ * outputs a fused flush (dc_flush_bucket_buffers) writes.
+ *   tasks, num_tasks        host dc_task[num_tasks]; param in [0, num_params)
+ *                           and comm in [0, num_comms) (else DC_ERR_TASKS)
+ *   pid_offsets, pids       host CSR from dc_partition_ids
+ *   comms, num_comms        host, as for dc_flush_bucket
+ *   holders                 host uint8[num_tasks * W] out
+ * A partition id outside its communicator is DC_ERR_TASKS. */
+dc_status dc_holders(int32_t W, const dc_task* tasks, int32_t num_tasks, int32_t num_params,
+                     const int32_t* pid_offsets, const int32_t* pids, const dc_comm* comms,
+                     int32_t num_comms, uint8_t* holders);
+
+/* Per-param ZeRO-2 partition sizes ([DS] "Follow-up": the ZeRO-2 owner path
+ * sends every element to the rank whose partition holds it): for every
+ * param of group g, param_part_size = part_size[g] (dc_partition_ids' S_g)
+ * when g is on the data-parallel communicator -- the rule of
+ * dc_build_owner_map: group_comm_size[g] == W and group rank i is global
+ * rank i -- and 0 otherwise (such params keep AllReduce within their
+ * blocks).  This is the part_size argument of dc_flush_bucket_zero2,
+ * dc_plan_flush and dc_plan_relayout.
+ *   group_begin, group_comm_size, group_rank_to_global  host, as for
+ *                                                       dc_build_owner_map
+ *   part_size          device int64[num_groups] from dc_partition_ids
+ *   param_part_size    device int64[num_params] out */
+dc_status dc_param_part_size(int32_t W, int32_t num_params, int32_t num_groups,
+                             const int32_t* group_begin, const int32_t* group_comm_size,
+                             const int32_t* group_rank_to_global, const int64_t* part_size,
+                             int64_t* param_part_size, void* stream);
 
 /* Relayout plan for a reduce-scatter over a bucket ([DS] "Describe
  * alternatives": a reduce-scatter needs the bucket laid out contiguously by
@@ -584,6 +620,19 @@ dc_status dc_stream_copy(const void* src, void* dst, int64_t bytes, void* stream
  * regions must not overlap. */
 dc_status dc_stream_rows(const void* src, int64_t src_ld_vec, int32_t rows_read, void* dst,
                          int64_t dst_ld_vec, int32_t rows_written, int64_t nvec, void* stream);
+
+/* The access-mix reference at a launch shape of the planned flush: the same
+ * xor stream as dc_stream_rows, but each one-wave workgroup takes `group`
+ * (1, 2 or 4) runs of 64 vectors -- with one row written their results are
+ * stored together after the last load -- at most `cap` workgroups stay
+ * resident per compute unit (0: no cap, at most 64), and the stores use the
+ * planned flush's cache policies.  A sweep over shapes that includes a
+ * kernel's own gives a reference its access mix cannot beat with xor for
+ * arithmetic.  Other arguments and checks as in dc_stream_rows; a group
+ * outside {1, 2, 4} is DC_ERR_UNSUPPORTED. */
+dc_status dc_stream_rows_shaped(const void* src, int64_t src_ld_vec, int32_t rows_read, void* dst,
+                                int64_t dst_ld_vec, int32_t rows_written, int64_t nvec,
+                                int32_t group, int32_t cap, void* stream);
 
 #ifdef __cplusplus
 }

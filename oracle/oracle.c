@@ -146,11 +146,12 @@ void or_group_eligible(int32_t W, int32_t G, const int32_t* comm_size,
   }
 }
 
-/* Owner map ([DS] Design points): exactly one partition entry means
- * exactly one owner, and that entry is the owner's rank; two or more entries
- * (a straddler) or none, or an excluded group, mean no owner (-1), which the
- * flush treats as AllReduce.  counts[2g] = owners, counts[2g+1] = straddlers
- * (params with two or more entries) in group g. */
+/* Owner map ([DS] Design points, the owner map): a param whose partition
+ * list has a single element is held by one rank only, the rank that element
+ * names, and gets that rank as its owner; a param listed in two or more
+ * partitions (a straddler), in none, or in an excluded group gets -1, which
+ * the flush treats as AllReduce.  counts[2g] = owners, counts[2g+1] =
+ * straddlers (params with two or more entries) in group g. */
 void or_owner_map(int32_t P, const int32_t* pid_offsets, const int32_t* pids, int32_t G,
                   const int32_t* group_begin, const int32_t* eligible, int32_t* owner,
                   int32_t* counts) {

@@ -367,7 +367,7 @@ def pin_partition_brute_force():
 
 
 def pin_owner_rules():
-    """DeepSpeed issue, Design points: exactly one entry means that entry is
+    """DeepSpeed issue, Design points: a single-element partition list names
     the owner; straddlers (2+ entries) and empty params keep AllReduce (-1);
     at most p-1 straddlers per group; an excluded group has no owners."""
     rng = random.Random(31)

@@ -309,18 +309,49 @@ def _host_executor(w):
     return ex
 
 
-def test_executor_holders_match_probe():
-    """The ranks the fused copy-out writes are the probe's kept set."""
+def test_holders_match_oracle():
+    """dc_holders against the holder sets written out from the oracle's
+    partition lists (rank r holds a param when its partition -- its group
+    rank in every block of a sub-communicator -- is in the param's list),
+    and the kept counts they give against the oracle's probe; the executor
+    hands the same mask to the fused flush."""
     ws = [wl.tiny_flush(), wl.mixed_flush_w16(),
           wl.custom_flush("h", 8, 0, [1000, 3, 77, 4096, 5000, 12, 900, 64], group_begin=[0, 5, 8],
                           group_comm=[0, 1], comms=[wl.Comm(8, 1), wl.Comm(4, 2)], capacity=3000)]
     for w in ws:
+        flat, ps, off, pids = oracle.partition_ids(w.numel, w.group_begin, w.group_parts())
+        comm_sizes = [w.comms[c].size for c in w.group_comm]
+        elig = oracle.group_eligible(w.W, comm_sizes, w.group_rank_to_global())
+        owner, _ = oracle.owner_map(off, pids, w.group_begin, elig)
+        comms = [(c.size, c.stride) for c in w.comms]
         ex = _host_executor(w)
-        for b in range(len(w.buckets)):
-            h = ex.holders(b)
-            pr = ex.probe(b)
-            kept = (h * np.array([t.numel for t in w.buckets[b].tasks])[:, None]).sum(axis=0)
-            assert list(kept) == [pr.kept[r] for r in range(w.W)], (w.name, b)
+        for b, bk in enumerate(w.buckets):
+            t = dc.tasks_array([(x.offset, x.numel, x.param, x.comm) for x in bk.tasks])
+            got = dc.dc_holders(w.W, t, len(t), w.P, off, pids, comms, len(comms))
+            want = np.zeros((len(t), w.W), bool)
+            for k, x in enumerate(bk.tasks):
+                c, st = w.comms[x.comm].size, w.comms[x.comm].stride
+                for q in pids[off[x.param]:off[x.param + 1]]:
+                    for blk in w.comms[x.comm].blocks(w.W):
+                        want[k, blk[int(q)]] = True
+            assert np.array_equal(got, want), (w.name, b)
+            assert np.array_equal(ex.holders(b), want)
+            pr = oracle.probe(w.W, t["numel"], t["param"], t["comm"], owner, off, pids,
+                              [c for c, _ in comms], [s for _, s in comms])
+            kept = (got * t["numel"][:, None]).sum(axis=0)
+            assert list(kept) == list(pr["kept"]), (w.name, b)
+
+
+def test_holders_argument_checks():
+    t = dc.tasks_array([(0, 10, 0, 0), (10, 10, 1, 0)])
+    off = np.array([0, 1, 3], np.int32)
+    pids = np.array([0, 1, 2], np.int32)
+    expect(dc.DC_ERR_TASKS, dc.dc_holders, 4, t, 2, 1, off, pids, [(4, 1)], 1)      # param 1 >= 1
+    bad = np.array([0, 1, 2, 9], np.int32)
+    expect(dc.DC_ERR_TASKS, dc.dc_holders, 4, t, 2, 2, off, bad[[0, 3, 1]], [(4, 1)], 1)  # pid 9
+    expect(dc.DC_ERR_ARG, dc.dc_holders, 4, t, 2, 2, off, pids, [(3, 1)], 1)        # comm 0 != W
+    assert dc.dc_holders(4, t, 2, 2, off, pids, [(4, 1)], 1).tolist() == [
+        [True, False, False, False], [False, True, True, False]]
 
 
 def test_header_is_plain_c(tmp_path):
@@ -342,20 +373,20 @@ def test_header_is_plain_c(tmp_path):
 
 def _brute_plan(W, dtype, col0, numel, tasks, owner, flat, psize):
     """The tile records as the header defines them, from a per-column task
-    index: tile b covers vectors [v0 + 128 b, v0 + 128 (b + 1)) clipped to
-    the bucket's last vector."""
+    index: tile b covers vectors [v0 + 64 b, v0 + 64 (b + 1)) clipped to the
+    bucket's last vector; records XCD-major."""
     E = 8 if dtype == wl.DT_BF16 else 4
     first_v = col0 // E
-    v0 = first_v - first_v % 128
+    v0 = first_v - first_v % 64
     v_end = -(-(col0 + numel) // E)
-    count = -(-(v_end - v0) // 128) if numel > 0 else 0
+    count = -(-(v_end - v0) // 64) if numel > 0 else 0
     tid = np.repeat(np.arange(len(tasks)), tasks["numel"])          # task of each bucket column
     out = np.zeros(count, dc.TILE_DTYPE)
     for b in range(count):
-        f_lo = (v0 + 128 * b) * E - col0
-        f_hi = (v0 + min(128 * (b + 1), v_end - v0)) * E - col0
+        f_lo = (v0 + 64 * b) * E - col0
+        f_hi = (v0 + min(64 * (b + 1), v_end - v0)) * E - col0
         ids = tid[max(f_lo, 0):min(f_hi, numel)]
-        first, last = int(ids.min()), int(ids.max())
+        first, last = (int(ids.min()), int(ids.max())) if len(ids) else (0, -1)
         root, flags = -1, 0
         whole = first == last and f_lo >= 0 and f_hi <= numel
         if whole:
@@ -436,7 +467,7 @@ def test_plan_flush_headline_tiles_all_whole():
         total += len(got)
         assert np.all(got["flags"] == 1) and np.all(got["first"] == got["last"])
         assert np.array_equal(got["root"], owner[t["param"][got["first"]]])
-    assert total * 128 * 8 == sum(bk.numel for bk in w.buckets)
+    assert total * 64 * 8 == sum(bk.numel for bk in w.buckets)
 
 
 def test_plan_flush_argument_checks():
@@ -453,7 +484,8 @@ def test_plan_flush_argument_checks():
     big = dc.tasks_array([(0, 5000, 0, 0)])
     args = (8, 0, 0, 5000, big.ctypes.data_as(ctypes.c_void_p), 1, None, None, None, 1,
             dc.comms_array(comms).ctypes.data_as(ctypes.c_void_p), 1)
-    assert dc.lib().dc_plan_flush(*args, None, 0, ctypes.byref(n), None) == dc.DC_OK and n.value == 5
+    # 625 vectors: 10 tiles of 64
+    assert dc.lib().dc_plan_flush(*args, None, 0, ctypes.byref(n), None) == dc.DC_OK and n.value == 10
     rc = dc.lib().dc_plan_flush(*args, np.zeros(4, dc.TILE_DTYPE).ctypes.data_as(ctypes.c_void_p), 4,
                                 ctypes.byref(n), None)
     assert rc == dc.DC_ERR_SHAPE
@@ -465,20 +497,20 @@ def test_flush_planned_argument_checks():
     ok = dict(W=8, dtype=0, slab_in=FAKE, ld_in=2048, slab_out=FAKE, ld_out=2048, bucket_col=0,
               bucket_numel=2048, tasks=TASK_PTR, num_tasks=1, owner=None, flat_offset=None,
               part_size=None, num_params=1, comms=[(8, 1)], num_comms=1, pre_div=1,
-              tiles=TASK_PTR + 4096, num_tiles=2, root_tiles=0, stream=0)
+              tiles=TASK_PTR + 4096, num_tiles=4, root_tiles=0, stream=0)
 
     def call(**ch):
         a = dict(ok)
         a.update(ch)
         return f(**a)
 
-    expect(dc.DC_ERR_SHAPE, call, num_tiles=3)                     # 2048 bf16 columns: 2 tiles
+    expect(dc.DC_ERR_SHAPE, call, num_tiles=3)                     # 2048 bf16 columns: 4 tiles
     expect(dc.DC_ERR_SHAPE, call, num_tiles=0)
-    expect(dc.DC_ERR_SHAPE, call, bucket_col=8, ld_in=4096, ld_out=4096)   # starts mid-tile: 3 tiles
+    expect(dc.DC_ERR_SHAPE, call, bucket_col=8, ld_in=4096, ld_out=4096)   # starts mid-tile: 5 tiles
     expect(dc.DC_ERR_NULL, call, tiles=None)
     expect(dc.DC_ERR_NULL, call, tiles=None, num_tiles=0)             # a bucket with tiles needs a plan
     expect(dc.DC_ERR_ARG, call, num_tiles=-1)
-    expect(dc.DC_ERR_ARG, call, root_tiles=3)
+    expect(dc.DC_ERR_ARG, call, root_tiles=5)
     expect(dc.DC_ERR_ARG, call, root_tiles=-1)
     expect(dc.DC_ERR_NULL, call, flat_offset=FAKE)
     expect(dc.DC_ERR_ARG, call, flat_offset=FAKE, part_size=FAKE, owner=FAKE)

@@ -1,6 +1,7 @@
 """Host logic of the executor, on the CPU: the fused flush's pointer tables
-(per-rank addresses, split params, empty buffers, coordinates), the ZeRO-2
-partition sizes, and the holder sets (the device kernels are not run)."""
+(per-rank addresses, split params, empty buffers, coordinates); the device
+kernels are not run (the holder sets come from dc_holders, tested in
+test_abi.py; the ZeRO-2 partition sizes from a kernel, tested on the GPU)."""
 import numpy as np
 import pytest
 
@@ -73,9 +74,3 @@ def test_register_buffers_rejects_overlap():
     assert e.value.code == dc.DC_ERR_TASKS
 
 
-@pytest.mark.parametrize("w", [wl.tiny_flush(), wl.owner_flush_w8(), wl.mixed_flush_w16()],
-                         ids=lambda w: w.name)
-def test_zero2_partition_sizes_match_oracle(w):
-    ex = executor.from_workload(w, reduce_to_owner=False, device="cpu", zero2=True)
-    _, psize = U.psize_per_param(w)
-    assert np.array_equal(ex.h_psize, psize)
