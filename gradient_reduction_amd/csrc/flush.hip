@@ -487,14 +487,16 @@ __global__ __launch_bounds__(kFT) void k_flush_planned(FlushParams p) {
 // Planned launch shapes (one-wave workgroups, one plan tile each, LDS
 // reserved to cap residency), from interleaved sweeps on the 402.8M-element
 // W = 8 bf16 and the 1.2B-element W = 16 fp32 flushes: W = 8 buckets whose
-// tiles mostly write one row ran fastest at 8 workgroups per compute unit,
-// buckets whose tiles write every row at 5; W = 16 at 6 and 3.  W = 4 keeps
+// tiles mostly write one row ran fastest at 8 workgroups per compute unit
+// (6.40 TB/s, against 6.35 at 10, 6.24 at 7 and 5.88 at 6), buckets whose
+// tiles write every row at 6 (6.48-6.55, against 6.34-6.36 at 4, 5 and 7);
+// W = 16 at 6 and 3.  W = 4 keeps
 // the caps measured there with two-vector tiles.  Other W take the caps of
 // the nearest measured W below them.  A searched launch keeps full
 // occupancy: its per-tile search needs the other resident workgroups to
 // hide it.
 #ifndef DC_PLAN_CAP_W8
-#define DC_PLAN_CAP_W8 8, 5     // W = 8: one-row buckets, every-row buckets
+#define DC_PLAN_CAP_W8 8, 6     // W = 8: one-row buckets, every-row buckets
 #endif
 #ifndef DC_PLAN_CAP_W16
 #define DC_PLAN_CAP_W16 6, 3

@@ -318,22 +318,36 @@ __global__ __launch_bounds__(kST) void k_ag_step(int32_t W, const char* __restri
 // Thread (s, k) reads chunk s's vector k once and writes it wherever node i
 // keeps chunk s: position s (rank order) or (i - s) mod W (ring order).  In
 // step mode only chunk `step` (rank) or position `step` (ring) is written.
+// Each workgroup covers U runs of 64 vectors of one chunk; a full one stores
+// through buffer resources with cache-policy bits SP (SP < 0: plain stores),
+// a partial one with plain stores.
+template <int U, int SP>
 __global__ __launch_bounds__(kST) void k_ag_vec(int32_t W, const u32x4* __restrict__ in,
-                                                     int64_t ldv_in, u32x4* __restrict__ out,
-                                                     int64_t ldv_out, int64_t Lv, int32_t order,
-                                                     int32_t step) {
+                                                int64_t ldv_in, u32x4* __restrict__ out,
+                                                int64_t ldv_out, int64_t Lv, int32_t order,
+                                                int32_t step) {
   const int32_t s = blockIdx.y;
   if (order == DC_ORDER_RANK && step >= 0 && s != step) return;
-  const int64_t k0 = (int64_t)blockIdx.x * (kST * DC_AG_U) + threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * (kST * U);
+  const bool full = t0 + kST * U <= Lv;
+  u32x4 x[U];
 #pragma unroll
-  for (int u = 0; u < DC_AG_U; ++u) {
-    const int64_t k = k0 + (int64_t)u * kST;
-    if (k >= Lv) continue;
-    const u32x4 x = load16<kNT>(in + (int64_t)s * ldv_in + k);
-    for (int32_t i = 0; i < W; ++i) {
-      const int32_t p = order == DC_ORDER_RANK ? s : (i - s + W) % W;
-      if (order == DC_ORDER_RING && step >= 0 && p != step) continue;
-      store16<kAgNTS>(out + (int64_t)i * ldv_out + (int64_t)p * Lv + k, x);
+  for (int u = 0; u < U; ++u) {
+    const int64_t k = t0 + threadIdx.x + (int64_t)u * kST;
+    if (k < Lv) x[u] = load16<kNT>(in + (int64_t)s * ldv_in + k);
+  }
+  for (int32_t i = 0; i < W; ++i) {
+    const int32_t p = order == DC_ORDER_RANK ? s : (i - s + W) % W;
+    if (order == DC_ORDER_RING && step >= 0 && p != step) continue;
+    u32x4* base = out + (int64_t)i * ldv_out + (int64_t)p * Lv + t0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t j = (int32_t)threadIdx.x + u * kST;
+      if (SP >= 0 && full) {
+        store_buf<(SP >= 0 ? SP : 0)>(base, kST * U * 16, j * 16, x[u]);
+      } else if (t0 + j < Lv) {
+        store16<kAgNTS>(base + j, x[u]);
+      }
     }
   }
 }
@@ -571,7 +585,27 @@ __global__ __launch_bounds__(kST) void k_stream_rows_g(const u32x4* __restrict__
 // the W = 4 deferred reduce, 5-8% over a full compute unit (within 2% for
 // the ring-order reduce-scatter); other W keep the same budget.  The
 // variable-shard reduce-scatter measured no gain and keeps no cap.
-constexpr int kKbRs = 96, kKbRsRing = 144, kKbAg = 144, kKbDeferred = 96, kKbAccRed = 120;
+constexpr int kKbRs = 96, kKbRsRing = 144, kKbDeferred = 96, kKbAccRed = 120;
+
+// All-gather launch shapes (vectors per thread, store policy; workgroups per
+// compute unit), from interleaved sweeps on the 7B-layer all-gather (W = 8
+// bf16, 25.3M-element shards): one vector per thread with sc0 sc1 nt stores
+// ran at 6.07 TB/s in rank order at 12 workgroups per compute unit and 6.20
+// in ring order at 12 (6.12 at 16), against 5.62-5.69 for two vectors per
+// thread with plain stores at 8.
+#ifndef DC_AG_RANK_SHAPE
+#define DC_AG_RANK_SHAPE 1, 19
+#endif
+#ifndef DC_AG_RANK_CAP
+#define DC_AG_RANK_CAP 12
+#endif
+#ifndef DC_AG_RING_SHAPE
+#define DC_AG_RING_SHAPE 1, 19
+#endif
+#ifndef DC_AG_RING_CAP
+#define DC_AG_RING_CAP 12
+#endif
+
 
 // The dynamic LDS that caps a launch of `kern` at `cap` workgroups per compute unit.
 template <typename K>
@@ -582,6 +616,14 @@ size_t pad_for(K* kern, int cap) {
 inline unsigned blocks_for(int64_t n, int u) {
   return (unsigned)((n + kST * u - 1) / (kST * u));
 }
+template <int U, int SP>
+void launch_ag_vec(int32_t W, const u32x4* in, int64_t ldv_in, u32x4* out, int64_t ldv_out,
+                   int64_t Lv, int32_t order, int32_t step, int cap, hipStream_t stream) {
+  hipLaunchKernelGGL((k_ag_vec<U, SP>), dim3(blocks_for(Lv, U), (unsigned)W), dim3(kST),
+                     pad_for(k_ag_vec<U, SP>, cap), stream, W, in, ldv_in, out, ldv_out, Lv, order,
+                     step);
+}
+
 
 inline void reciprocal(int32_t c, float* inv, float* cf) {
   *cf = (float)c;
@@ -775,11 +817,14 @@ hipError_t launch_all_gather(int32_t W, int32_t dtype, const void* in, int64_t l
   const int E = bf ? 8 : 4;
   if (L % E == 0) {
     const int64_t Lv = L / E;
-    const int cap = stream_cap(1 + W, DC_AG_U, kKbAg);
-    hipLaunchKernelGGL(k_ag_vec, dim3(blocks_for(Lv, DC_AG_U), (unsigned)W), dim3(kST),
-                       pad_for(k_ag_vec, cap), stream, W,
-                       reinterpret_cast<const u32x4*>(in), ld_in / E, reinterpret_cast<u32x4*>(out),
-                       ld_out / E, Lv, order, step);
+    const u32x4* i4 = reinterpret_cast<const u32x4*>(in);
+    u32x4* o4 = reinterpret_cast<u32x4*>(out);
+    if (order == DC_ORDER_RANK)
+      launch_ag_vec<DC_AG_RANK_SHAPE>(W, i4, ld_in / E, o4, ld_out / E, Lv, order, step,
+                                      DC_AG_RANK_CAP, stream);
+    else
+      launch_ag_vec<DC_AG_RING_SHAPE>(W, i4, ld_in / E, o4, ld_out / E, Lv, order, step,
+                                      DC_AG_RING_CAP, stream);
   } else if (bf) {
     hipLaunchKernelGGL(k_ag_elem<uint16_t>, dim3(blocks_for(L, DC_AG_U), (unsigned)W), dim3(kST), 0,
                        stream, W, reinterpret_cast<const uint16_t*>(in), ld_in,
