@@ -46,6 +46,35 @@ constexpr bool kNT = DC_SLAB_NT != 0;
 constexpr bool kNTS = DC_SLAB_NTS != 0;
 constexpr bool kAgNTS = DC_AG_NTS != 0;
 
+// Cache policy of the result stores (gfx950 bits: 0 sc0, 1 nt, 4 sc1; < 0:
+// nontemporal global stores), from an interleaved sweep at the bench shapes:
+// the reduce-scatters (one row written per vector folded) ran the same with
+// every policy tried and keep nontemporal stores; the accumulate ran about
+// 1% faster with nt sc1, and the kernels that write several rows (the
+// deferred reduce, 6.64 against 6.41-6.55 TB/s, and the fused
+// accumulate-reduce, 6.14-6.36 against 6.00-6.25) with nt sc1 as well.
+#ifndef DC_SLAB_SP1
+#define DC_SLAB_SP1 -1
+#endif
+#ifndef DC_SLAB_SPACC
+#define DC_SLAB_SPACC 18
+#endif
+#ifndef DC_SLAB_SPN
+#define DC_SLAB_SPN 18
+#endif
+
+// Store vector k of a row whose workgroup covers the run of vectors
+// [t0, t0 + n) (t0 and n the same for the whole workgroup): through a buffer
+// resource over the run with cache bits SP, or a nontemporal global store.
+template <int SP>
+__device__ __forceinline__ void store_run(u32x4* row, int64_t t0, int64_t n, int64_t k, u32x4 v) {
+  if constexpr (SP < 0) {
+    store16<kNTS>(row + k, v);
+  } else {
+    store_buf<SP>(row + t0, (int32_t)(n * 16), (int32_t)((k - t0) * 16), v);
+  }
+}
+
 // Fold the W rows of vector column `v` (rows `ldv` vectors apart).  With W
 // known at compile time every row load is issued before the first add.
 template <bool BF16, int WT, bool PRE>
@@ -77,11 +106,14 @@ __global__ __launch_bounds__(kST) void k_rs_vec(int32_t W, const u32x4* __restri
                                                      int64_t ldv_out, int64_t Lv, float inv,
                                                      float c) {
   const int64_t s = blockIdx.y;
-  const int64_t k0 = (int64_t)blockIdx.x * (kST * DC_RS_U) + threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * (kST * DC_RS_U);
+  const int64_t n = min((int64_t)(kST * DC_RS_U), Lv - t0);
 #pragma unroll
   for (int u = 0; u < DC_RS_U; ++u) {
-    const int64_t k = k0 + (int64_t)u * kST;
-    if (k < Lv) store16<kNTS>(out + s * ldv_out + k, fold_rows<BF16, WT, PRE>(in, ldv_in, s * Lv + k, W, inv, c));
+    const int64_t k = t0 + threadIdx.x + (int64_t)u * kST;
+    if (k < Lv)
+      store_run<DC_SLAB_SP1>(out + s * ldv_out, t0, n, k,
+                             fold_rows<BF16, WT, PRE>(in, ldv_in, s * Lv + k, W, inv, c));
   }
 }
 
@@ -229,7 +261,9 @@ __global__ __launch_bounds__(kST) void k_rs_ring(int32_t W, const u32x4* __restr
     for (int32_t j = 0; j < W; ++j)
       fold16<BF16, PRE>(acc, load16<kNT>(in + (int64_t)((s + j) % W) * ldv_in + v), j == 0, inv, c);
   }
-  store16<kNTS>(out + (int64_t)s * ldv_out + k, pack16<BF16>(acc));
+  const int64_t t0 = (int64_t)blockIdx.x * kST;
+  store_run<DC_SLAB_SP1>(out + (int64_t)s * ldv_out, t0, min((int64_t)kST, Lv - t0), k,
+                         pack16<BF16>(acc));
 }
 
 template <bool BF16>
@@ -397,7 +431,8 @@ __global__ __launch_bounds__(kST) void k_accumulate(const float* __restrict__ x,
       u32x4 y;
 #pragma unroll
       for (int q = 0; q < 4; ++q) y[q] = __float_as_uint(__uint_as_float(aa[q]) + __uint_as_float(xx[q]));
-      store16<kNTS>(av + k, y);
+      const int64_t t0 = (int64_t)blockIdx.x * (kST * DC_ACC_U);
+      store_run<DC_SLAB_SPACC>(av, t0, min((int64_t)(kST * DC_ACC_U), nvec - t0), k, y);
     } else if (k == nvec) {
       for (int64_t j = nvec * 4; j < M; ++j) {
         const float a = init ? 0.0f : acc[r * ld_acc + j];
@@ -423,7 +458,9 @@ __global__ __launch_bounds__(kST) void k_deferred(int32_t W, const float* acc, i
     const int64_t k = k0 + (int64_t)u * kST;
     if (k < nvec) {
       const u32x4 y = fold_rows<false, WT, false>(in, ld_acc / 4, k, W, 0.0f, 1.0f);
-      for (int32_t i = 0; i < out_rows; ++i) store16<kNTS>(ov + i * (ld_out / 4) + k, y);
+      const int64_t t0 = (int64_t)blockIdx.x * (kST * DC_DEF_U);
+      const int64_t n = min((int64_t)(kST * DC_DEF_U), nvec - t0);
+      for (int32_t i = 0; i < out_rows; ++i) store_run<DC_SLAB_SPN>(ov + i * (ld_out / 4), t0, n, k, y);
     } else if (k == nvec) {
       for (int64_t j = nvec * 4; j < M; ++j) {
         float sum = 0.0f;
@@ -447,6 +484,7 @@ __global__ __launch_bounds__(kST) void k_accum_reduce(int32_t W, const float* x,
   u32x4* av = reinterpret_cast<u32x4*>(acc);
   u32x4* ov = reinterpret_cast<u32x4*>(out);
   const int64_t lx = ld_x / 4, la = ld_acc / 4, lo = ld_out / 4;
+  const int64_t t0 = (int64_t)blockIdx.x * kST, n = min((int64_t)kST, nvec - t0);
   if (k < nvec) {
     float sum[4];
     constexpr int RB = WT > 0 ? WT : 4;  // rows per batch of loads
@@ -468,12 +506,12 @@ __global__ __launch_bounds__(kST) void k_accum_reduce(int32_t W, const float* x,
           a[q] = __float_as_uint(v);
           sum[q] = (r0 + i) == 0 ? v : sum[q] + v;
         }
-        if (keep) store16<kNTS>(av + (r0 + i) * la + k, a);
+        if (keep) store_run<DC_SLAB_SPN>(av + (r0 + i) * la, t0, n, k, a);
       }
     }
     const u32x4 y = u32x4{__float_as_uint(sum[0]), __float_as_uint(sum[1]), __float_as_uint(sum[2]),
                           __float_as_uint(sum[3])};
-    for (int32_t i = 0; i < out_rows; ++i) store16<kNTS>(ov + i * lo + k, y);
+    for (int32_t i = 0; i < out_rows; ++i) store_run<DC_SLAB_SPN>(ov + i * lo, t0, n, k, y);
   } else if (k == nvec) {
     for (int64_t j = nvec * 4; j < M; ++j) {
       float s = 0.0f;
