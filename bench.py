@@ -543,7 +543,8 @@ def bench_flush(args, w, mode):
     extra["graph_ms_per_step"] = round(graph_step_ms(torch, args, ex.capture_step(x, ld, y, ld)), 4)
     log(f"[bench] owner map once: {once_ms:.4f} ms per step; the step replayed as one HIP graph: "
         f"{extra['graph_ms_per_step']:.4f} ms")
-    extra["gpu_during_steps"] = gpu_state_under_load(torch, step)
+    if args.load_sample_s > 0:
+        extra["gpu_during_steps"] = gpu_state_under_load(torch, step, args.load_sample_s)
     # the reference runs above wrote into y: clear it and run the step once
     # more, so y holds exactly one step's result over zeros
     y.zero_()
@@ -1227,6 +1228,9 @@ def main():
     ap.add_argument("--searched", action="store_true",
                     help="flush and fused workloads: flush without plans (each tile searches "
                          "the task table) instead of with the per-bucket tile plans")
+    ap.add_argument("--load-sample-s", type=float, default=1.5,
+                    help="flush workloads: seconds of steps run while rocm-smi samples the GPU's "
+                         "clocks and power (0: no sample, e.g. under a profiler)")
     ap.add_argument("--probe", action="store_true",
                     help="flush workloads: print the probe line of each of the first 20 flushes "
                          "(the executor's reduce_probe), as they are issued")
