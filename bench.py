@@ -158,6 +158,26 @@ def time_steps(torch, args, step):
     return a.elapsed_time(b) / args.steps
 
 
+def region_launch_ms(torch, args, launches, n):
+    """Average duration of one launch of a kernel, timed as a region:
+    `launches` issues n launches of it back to back with nothing else on the
+    stream, and one HIP event pair brackets args.steps rounds of that (after
+    warm-up).  The gaps between the launches count against the kernel.  The
+    events run_timed records around every launch add a packet of their own to
+    each launch, which the kernel trace does not see (about 2% on a
+    quarter-millisecond launch), so roofline figures use this timing."""
+    return time_steps(torch, args, launches) / n
+
+
+REGION_TIMING = ("one HIP event pair around args.steps rounds of the kernel's launches issued back to "
+                 "back on its stream, no other work between; launch_ms_avg = that time / launches")
+
+
+def per_launch_events(gbs, ms):
+    return {"gbs": round(gbs, 1), "launch_ms_avg": round(ms, 4),
+            "what": "HIP events around every launch inside the step; each event adds its own packet"}
+
+
 def graph_step_ms(torch, args, g):
     """Average time of one replay of a captured step (same warm-up and step
     counts as the eager timing)."""
@@ -521,12 +541,15 @@ def bench_flush(args, w, mode):
     value = step_bytes / (ms_step / 1e3) / 1e9
     log(f"[bench] step {ms_step:.3f} ms, {value:.1f} GB/s; flush kernels {kern.sum(axis=1).mean():.3f} ms "
         f"({flush_gbs:.1f} GB/s); per bucket ms {np.round(kern.mean(axis=0), 4).tolist()}")
-    once_ms = time_steps(torch, args, flushes_only)
-    roofline = {"bound": "hbm", "achieved": round(flush_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(flush_gbs / HBM_PEAK_GBS, 4),
+    once_ms = region_launch_ms(torch, args, flushes_only, 1)
+    region_gbs = sum(per_launch) / (once_ms / 1e3) / 1e9
+    log(f"[bench] flushes back to back: {once_ms:.4f} ms per step, {region_gbs:.1f} GB/s")
+    roofline = {"bound": "hbm", "achieved": round(region_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(region_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile(args.workload, w.name),
                 "kernel": "k_flush_planned" if not args.searched else "k_flush",
-                "launch_ms_avg": round(avg_launch_ms, 4),
+                "launch_ms_avg": round(once_ms / nb, 4), "timing": REGION_TIMING,
+                "per_launch_events": per_launch_events(flush_gbs, avg_launch_ms),
                 "bytes_per_launch_avg": int(np.mean(per_launch)),
                 "bytes_per_launch": [int(b) for b in per_launch]}
     ref = flush_mix_reference(w, owner, x, y, ld, ex.h_psize if zero2 else None)
@@ -634,18 +657,25 @@ def bench_flush_buffers(args, w):
             if timer is not None:
                 timer.ev[b][1].record()
 
+    def flushes_only():
+        for b in range(nb):
+            ex.flush_buffers(b)
+
     ms_step, kern_all = run_timed(torch, args, step, nb + 1)
     kern, owner_map_ms = kern_all[:, :nb], kern_all[:, nb]
-    gbs = sum(per_launch) / (kern.sum(axis=1).mean() / 1e3) / 1e9
+    ev_gbs = sum(per_launch) / (kern.sum(axis=1).mean() / 1e3) / 1e9
+    once_ms = region_launch_ms(torch, args, flushes_only, 1)
+    gbs = sum(per_launch) / (once_ms / 1e3) / 1e9
     gbs_median = sum(per_launch) / (np.median(kern.sum(axis=1)) / 1e3) / 1e9
     value = step_bytes / (ms_step / 1e3) / 1e9
-    log(f"[bench] step {ms_step:.3f} ms, {value:.1f} GB/s; fused flush kernels "
-        f"{kern.sum(axis=1).mean():.3f} ms ({gbs:.1f} GB/s); per bucket ms "
+    log(f"[bench] step {ms_step:.3f} ms, {value:.1f} GB/s; fused flush kernels back to back "
+        f"{once_ms:.3f} ms ({gbs:.1f} GB/s), with events {kern.sum(axis=1).mean():.3f} ms; per bucket ms "
         f"{np.round(kern.mean(axis=0), 4).tolist()}")
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile(args.workload, w.name),
-                "kernel": "k_flush_buffers", "launch_ms_avg": round(float(kern.mean()), 4),
+                "kernel": "k_flush_buffers", "launch_ms_avg": round(once_ms / nb, 4),
+                "timing": REGION_TIMING, "per_launch_events": per_launch_events(ev_gbs, float(kern.mean())),
                 "bytes_per_launch_avg": int(np.mean(per_launch)),
                 "bytes_per_launch": [int(b) for b in per_launch]}
     ref = flush_mix_reference(w, None, x, y, ld, split=(one_b, many_b))
@@ -698,7 +728,7 @@ def deferred_oracle(w, K, gpu, chunks=8):
                          "status quo (1 row)"}
     # CPU baseline: the deferred step (K accumulates, then the reduce) on a
     # sample of the columns, inputs generated first
-    ns = 1 << 24
+    ns = 1 << 26
     xs = [OC.host_rows(1, w.value_seed, 0, w.scale, W, 0, ns, stream_of=lambda r, k=k: so(k, r))
           for k in range(K)]
     xs = [np.ascontiguousarray(x[:, :ns]) for x in xs]
@@ -791,16 +821,27 @@ def bench_deferred(args, K, check=True):
 
         ms_step, kern_all = run_timed(torch, args, step, n_acc + 1)
         kern = kern_all.mean(axis=0)
-        red_gbs = red_b / (kern[-1] / 1e3) / 1e9
+        ev_gbs = red_b / (kern[-1] / 1e3) / 1e9
+        if fused:
+            # repeated, it keeps adding the last micro-batch to the
+            # accumulators; the outputs are recomputed from scratch below
+            red_ms = region_launch_ms(torch, args, lambda: dc.dc_accumulate_reduce(
+                W, xs[K - 1], ld, a_t, ld, 1 if K == 1 else 0, 0, o_t, ld, W, M), 1)
+        else:
+            red_ms = region_launch_ms(torch, args, lambda: dc.dc_deferred_reduce(
+                W, a_t, ld, o_t, ld, M, W), 1)
+        red_gbs = red_b / (red_ms / 1e3) / 1e9
         acc_gbs = sum(acc_b) / (kern[:-1].sum() / 1e3) / 1e9 if n_acc else 0.0
         name = "k_accum_reduce" if fused else "k_deferred"
         log(f"[bench] deferred K={K}{' fused' if fused else ''}: step {ms_step:.3f} ms; accumulate "
-            f"{acc_gbs:.1f} GB/s; {name} {red_gbs:.1f} GB/s ({kern[-1]:.3f} ms)")
+            f"{acc_gbs:.1f} GB/s; {name} {red_gbs:.1f} GB/s ({red_ms:.3f} ms back to back, "
+            f"{kern[-1]:.3f} ms with events)")
         roofline = {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(red_gbs / HBM_PEAK_GBS, 4),
                     "traffic": traffic_from_profile("deferred_fused" if fused else "deferred",
                                                     w.name, {"ga": K}),
-                    "kernel": name, "launch_ms_avg": round(float(kern[-1]), 4),
+                    "kernel": name, "launch_ms_avg": round(red_ms, 4), "timing": REGION_TIMING,
+                    "per_launch_events": per_launch_events(ev_gbs, float(kern[-1])),
                     "bytes_per_launch_avg": red_b, "bytes_per_launch": [red_b]}
         if not fused:
             add_mix_reference(roofline, best_reference(acc, ld // 4, W, out_f, ld // 4, W, M // 4),
@@ -934,12 +975,20 @@ def bench_rs_ag(args):
 
     ms_step, kern_all = run_timed(torch, args, step, 3)
     kern = kern_all.mean(axis=0)
-    gbs = [rs_b / (kern[0] / 1e3) / 1e9, ag_b / (kern[1] / 1e3) / 1e9, ag_b / (kern[2] / 1e3) / 1e9]
-    log(f"[bench] rs {gbs[0]:.1f} GB/s, ag rank {gbs[1]:.1f} GB/s, ag ring {gbs[2]:.1f} GB/s")
+    ev = [rs_b / (kern[0] / 1e3) / 1e9, ag_b / (kern[1] / 1e3) / 1e9, ag_b / (kern[2] / 1e3) / 1e9]
+    reg = [region_launch_ms(torch, args, lambda: dc.dc_reduce_scatter(W, 0, x, w.ld, sh, ld_sh, M, 0), 1),
+           region_launch_ms(torch, args, lambda: dc.dc_all_gather(W, 0, sh, ld_sh, out, w.ld, L,
+                                                                  dc.DC_ORDER_RANK, -1), 1),
+           region_launch_ms(torch, args, lambda: dc.dc_all_gather(W, 0, sh, ld_sh, out_ring, w.ld, L,
+                                                                  dc.DC_ORDER_RING, -1), 1)]
+    gbs = [b / (t / 1e3) / 1e9 for b, t in zip((rs_b, ag_b, ag_b), reg)]
+    log(f"[bench] back to back: rs {gbs[0]:.1f} GB/s, ag rank {gbs[1]:.1f} GB/s, ag ring {gbs[2]:.1f} GB/s; "
+        f"with events: {ev[0]:.1f}, {ev[1]:.1f}, {ev[2]:.1f}")
     roofline = {"bound": "hbm", "achieved": round(gbs[0], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs[0] / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile("rs_ag", w.name), "kernel": "k_rs_vec",
-                "launch_ms_avg": round(float(kern[0]), 4), "bytes_per_launch_avg": rs_b,
+                "launch_ms_avg": round(reg[0], 4), "timing": REGION_TIMING,
+                "per_launch_events": per_launch_events(ev[0], float(kern[0])), "bytes_per_launch_avg": rs_b,
                 "bytes_per_launch": [rs_b]}
     tmp = torch.empty((W, w.ld), dtype=torch.int16, device=dev)
     add_mix_reference(roofline, best_reference(x, w.ld // 8, W, tmp, w.ld // 8, 1, M // 8),
@@ -947,7 +996,9 @@ def bench_rs_ag(args):
     del tmp
     extra = {"all_gather_rank_gbs": round(gbs[1], 1), "all_gather_ring_gbs": round(gbs[2], 1),
              "all_gather_rank_frac": round(gbs[1] / HBM_PEAK_GBS, 4),
-             "all_gather_ring_frac": round(gbs[2] / HBM_PEAK_GBS, 4)}
+             "all_gather_ring_frac": round(gbs[2] / HBM_PEAK_GBS, 4),
+             "all_gather_launch_ms": {"rank": round(reg[1], 4), "ring": round(reg[2], 4)},
+             "all_gather_gbs_with_events": {"rank": round(ev[1], 1), "ring": round(ev[2], 1)}}
     step()
     torch.cuda.synchronize()
     del x
@@ -1005,10 +1056,14 @@ def bench_schedules(args):
     byts = [rs_b, rs_b] + [ag_b] * len(scheds)
     gbs = {n: b / (t / 1e3) / 1e9 for n, b, t in zip(names, byts, kern)}
     log("[bench] " + ", ".join(f"{n} {kern[i]:.3f} ms {gbs[n]:.1f} GB/s" for i, n in enumerate(names)))
-    roofline = {"bound": "hbm", "achieved": round(gbs["rs_ring"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(gbs["rs_ring"] / HBM_PEAK_GBS, 4),
+    ring_ms = region_launch_ms(torch, args, lambda: dc.dc_reduce_scatter_ring(W, 0, x, w.ld, sh, ld_sh, M, 1), 1)
+    ring_gbs = rs_b / (ring_ms / 1e3) / 1e9
+    log(f"[bench] rs_ring back to back: {ring_ms:.4f} ms, {ring_gbs:.1f} GB/s")
+    roofline = {"bound": "hbm", "achieved": round(ring_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ring_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile("schedules_w8", w.name),
-                "kernel": "k_rs_ring", "launch_ms_avg": round(float(kern[1]), 4),
+                "kernel": "k_rs_ring", "launch_ms_avg": round(ring_ms, 4), "timing": REGION_TIMING,
+                "per_launch_events": per_launch_events(gbs["rs_ring"], float(kern[1])),
                 "bytes_per_launch_avg": rs_b, "bytes_per_launch": [rs_b]}
     tmp = torch.empty((W, w.ld), dtype=torch.int16, device=dev)
     add_mix_reference(roofline, best_reference(x, w.ld // 8, W, tmp, w.ld // 8, 1, M // 8),
@@ -1132,13 +1187,22 @@ def bench_relayout_rs(args):
     ms_step, kern_all = run_timed(torch, args, step, 2 * nb)
     kern = kern_all.mean(axis=0)
     rl_gbs = sum(rl_b) / (kern[0::2].sum() / 1e3) / 1e9
-    rs_gbs = sum(rs_b) / (kern[1::2].sum() / 1e3) / 1e9
+    ev_rs_gbs = sum(rs_b) / (kern[1::2].sum() / 1e3) / 1e9
+
+    def rs_only():
+        for k in range(nb):
+            dc.dc_reduce_scatter_v(W, 0, relaid, ld_r, shards, ld_s, plans[k][2], w.pre_div)
+
+    rs_ms = region_launch_ms(torch, args, rs_only, 1)
+    rs_gbs = sum(rs_b) / (rs_ms / 1e3) / 1e9
     log(f"[bench] relayout + reduce-scatter-v: step {ms_step:.3f} ms; relayout {rl_gbs:.1f} GB/s "
-        f"({kern[0::2].sum():.3f} ms); reduce-scatter-v {rs_gbs:.1f} GB/s ({kern[1::2].sum():.3f} ms)")
+        f"({kern[0::2].sum():.3f} ms); reduce-scatter-v {rs_gbs:.1f} GB/s back to back ({rs_ms:.3f} ms), "
+        f"{ev_rs_gbs:.1f} GB/s with events ({kern[1::2].sum():.3f} ms)")
     roofline = {"bound": "hbm", "achieved": round(rs_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(rs_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile("relayout_rs_w8", w.name), "kernel": "k_rs_v",
-                "launch_ms_avg": round(float(kern[1::2].mean()), 4),
+                "launch_ms_avg": round(rs_ms / nb, 4), "timing": REGION_TIMING,
+                "per_launch_events": per_launch_events(ev_rs_gbs, float(kern[1::2].mean())),
                 "bytes_per_launch_avg": int(np.mean(rs_b)),
                 "bytes_per_launch": [int(b) for b in rs_b]}
     extra = {"relayout_gbs": round(rl_gbs, 1), "relayout_ms": round(float(kern[0::2].sum()), 4),
