@@ -77,9 +77,9 @@ __device__ __forceinline__ void store_run(u32x4* row, int64_t t0, int64_t n, int
 
 // Fold the W rows of vector column `v` (rows `ldv` vectors apart).  With W
 // known at compile time every row load is issued before the first add.
-template <bool BF16, int WT, bool PRE>
-__device__ __forceinline__ u32x4 fold_rows(const u32x4* in, int64_t ldv, int64_t v, int32_t W,
-                                           float inv, float c) {
+template <bool BF16, int WT, int MODE>
+__device__ __forceinline__ u32x4 fold_rows_m(const u32x4* in, int64_t ldv, int64_t v, int32_t W,
+                                             float inv, float c) {
   constexpr int E = BF16 ? 8 : 4;
   float acc[E];
   if constexpr (WT > 0) {
@@ -87,12 +87,20 @@ __device__ __forceinline__ u32x4 fold_rows(const u32x4* in, int64_t ldv, int64_t
 #pragma unroll
     for (int r = 0; r < WT; ++r) x[r] = load16<kNT>(in + r * ldv + v);
 #pragma unroll
-    for (int r = 0; r < WT; ++r) fold16<BF16, PRE>(acc, x[r], r == 0, inv, c);
+    for (int r = 0; r < WT; ++r) fold16m<BF16, MODE>(acc, x[r], r == 0, inv, c);
   } else {
 #pragma unroll 4
-    for (int32_t r = 0; r < W; ++r) fold16<BF16, PRE>(acc, load16<kNT>(in + r * ldv + v), r == 0, inv, c);
+    for (int32_t r = 0; r < W; ++r) fold16m<BF16, MODE>(acc, load16<kNT>(in + r * ldv + v), r == 0, inv, c);
   }
   return pack16<BF16>(acc);
+}
+
+template <bool BF16, int WT, bool PRE>
+__device__ __forceinline__ u32x4 fold_rows(const u32x4* in, int64_t ldv, int64_t v, int32_t W,
+                                           float inv, float c) {
+  return with_pre_mode<PRE>(inv, [&](auto m) {
+    return fold_rows_m<BF16, WT, decltype(m)::value>(in, ldv, v, W, inv, c);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -213,8 +221,11 @@ __global__ __launch_bounds__(kST) void k_rs_v(int32_t W, const void* __restrict_
           a[r] = load16<kNT>(in4 + r * ldv + v);
           b[r] = load16<kNT>(in4 + r * ldv + v + 1);
         }
+        with_pre_mode<PRE>(inv, [&](auto m) {
 #pragma unroll
-        for (int r = 0; r < WT; ++r) fold16<BF16, PRE>(acc, funnel16(a[r], b[r], wo, bs), r == 0, inv, c);
+          for (int r = 0; r < WT; ++r)
+            fold16m<BF16, decltype(m)::value>(acc, funnel16(a[r], b[r], wo, bs), r == 0, inv, c);
+        });
       } else {
         for (int32_t r = 0; r < W; ++r)
           fold16<BF16, PRE>(acc, funnel16(load16<kNT>(in4 + r * ldv + v), load16<kNT>(in4 + r * ldv + v + 1), wo, bs),
@@ -255,8 +266,10 @@ __global__ __launch_bounds__(kST) void k_rs_ring(int32_t W, const u32x4* __restr
     u32x4 x[WT];
 #pragma unroll
     for (int j = 0; j < WT; ++j) x[j] = load16<kNT>(in + (int64_t)((s + j) % WT) * ldv_in + v);
+    with_pre_mode<PRE>(inv, [&](auto m) {
 #pragma unroll
-    for (int j = 0; j < WT; ++j) fold16<BF16, PRE>(acc, x[j], j == 0, inv, c);
+      for (int j = 0; j < WT; ++j) fold16m<BF16, decltype(m)::value>(acc, x[j], j == 0, inv, c);
+    });
   } else {
     for (int32_t j = 0; j < W; ++j)
       fold16<BF16, PRE>(acc, load16<kNT>(in + (int64_t)((s + j) % W) * ldv_in + v), j == 0, inv, c);
