@@ -546,7 +546,7 @@ def bench_flush(args, w, mode):
     log(f"[bench] flushes back to back: {once_ms:.4f} ms per step, {region_gbs:.1f} GB/s")
     roofline = {"bound": "hbm", "achieved": round(region_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(region_gbs / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profile(args.workload, w.name),
+                "traffic": None if args.searched else traffic_from_profile(args.workload, w.name),
                 "kernel": "k_flush_planned" if not args.searched else "k_flush",
                 "launch_ms_avg": round(once_ms / nb, 4), "timing": REGION_TIMING,
                 "per_launch_events": per_launch_events(flush_gbs, avg_launch_ms),
@@ -673,7 +673,7 @@ def bench_flush_buffers(args, w):
         f"{np.round(kern.mean(axis=0), 4).tolist()}")
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profile(args.workload, w.name),
+                "traffic": None if args.searched else traffic_from_profile(args.workload, w.name),
                 "kernel": "k_flush_buffers", "launch_ms_avg": round(once_ms / nb, 4),
                 "timing": REGION_TIMING, "per_launch_events": per_launch_events(ev_gbs, float(kern.mean())),
                 "bytes_per_launch_avg": int(np.mean(per_launch)),
@@ -1164,22 +1164,30 @@ def bench_relayout_rs(args):
     for bk in w.buckets:
         t = dc.tasks_array([(k.offset, k.numel, k.param, k.comm) for k in bk.tasks])
         pieces, seg = dc.dc_plan_relayout(W, t, len(t), flat, ex.h_psize, w.P)
-        plans.append((torch.from_numpy(pieces.view(np.uint8).copy()).to(dev), len(pieces), seg))
+        tiles = dc.dc_plan_relayout_tiles(0, bk.col, bk.numel, pieces, len(pieces), int(seg[-1]))
+        plans.append((torch.from_numpy(pieces.view(np.uint8).copy()).to(dev), len(pieces), seg,
+                      torch.from_numpy(tiles).to(dev), len(tiles)))
     maxn = max(int(p[2][-1]) for p in plans)
     maxseg = max(int(max(p[2][1:] - p[2][:-1])) for p in plans)
     ld_r, ld_s = wl.round_up(maxn, 64), wl.round_up(maxseg, 64)
     relaid = torch.empty((W, ld_r), dtype=torch.int16, device=dev)
     shards = torch.empty((W, ld_s), dtype=torch.int16, device=dev)
     nb = len(w.buckets)
-    rl_b = [2 * W * int(p[2][-1]) * b + 32 * p[1] for p in plans]
+    # per bucket: W rows read and written, the piece table, and with a tile
+    # plan 8 bytes per tile record
+    rl_b = [2 * W * int(p[2][-1]) * b + 32 * p[1] + (0 if args.searched else 8 * p[4]) for p in plans]
     rs_b = [W * int(p[2][-1]) * b + int(p[2][-1]) * b for p in plans]
 
     def step(tm=None):
         for k, bk in enumerate(w.buckets):
-            d_pieces, npc, seg = plans[k]
+            d_pieces, npc, seg, d_tiles, ntiles = plans[k]
             if tm: tm.ev[2 * k][0].record()
-            dc.dc_relayout_bucket(W, 0, x, ld, relaid, ld_r, bk.col, bk.numel, d_pieces, npc,
-                                  int(seg[-1]))
+            if args.searched:
+                dc.dc_relayout_bucket(W, 0, x, ld, relaid, ld_r, bk.col, bk.numel, d_pieces, npc,
+                                      int(seg[-1]))
+            else:
+                dc.dc_relayout_bucket_planned(W, 0, x, ld, relaid, ld_r, bk.col, bk.numel, d_pieces,
+                                              npc, int(seg[-1]), d_tiles, ntiles)
             if tm: tm.ev[2 * k][1].record(); tm.ev[2 * k + 1][0].record()
             dc.dc_reduce_scatter_v(W, 0, relaid, ld_r, shards, ld_s, seg, w.pre_div)
             if tm: tm.ev[2 * k + 1][1].record()
@@ -1205,7 +1213,9 @@ def bench_relayout_rs(args):
                 "per_launch_events": per_launch_events(ev_rs_gbs, float(kern[1::2].mean())),
                 "bytes_per_launch_avg": int(np.mean(rs_b)),
                 "bytes_per_launch": [int(b) for b in rs_b]}
-    extra = {"relayout_gbs": round(rl_gbs, 1), "relayout_ms": round(float(kern[0::2].sum()), 4),
+    extra = {"relayout": ("searched: each tile looks up its pieces" if args.searched else
+                          "planned: per-bucket tile plans built once on the host"),
+             "relayout_gbs": round(rl_gbs, 1), "relayout_ms": round(float(kern[0::2].sum()), 4),
              "reduce_scatter_v_ms": round(float(kern[1::2].sum()), 4)}
     # references at the largest relaid bucket: reduce-scatter-v reads W rows and
     # writes one row's worth; the relayout reads and writes all W rows (the
@@ -1290,8 +1300,9 @@ def main():
     ap.add_argument("--no-deferred", action="store_true",
                     help="headline run: leave out the deferred-reduce step in detail.deferred")
     ap.add_argument("--searched", action="store_true",
-                    help="flush and fused workloads: flush without plans (each tile searches "
-                         "the task table) instead of with the per-bucket tile plans")
+                    help="flush, fused and relayout workloads: run without tile plans (each "
+                         "tile searches the task or piece table) instead of with the per-bucket "
+                         "tile plans")
     ap.add_argument("--load-sample-s", type=float, default=1.5,
                     help="flush workloads: seconds of steps run while rocm-smi samples the GPU's "
                          "clocks and power (0: no sample, e.g. under a profiler)")

@@ -698,8 +698,77 @@ dc_status dc_relayout_bucket(int32_t W, int32_t dtype, const void* slab_in, int6
   const int64_t b = elem_bytes(dtype);
   if (overlaps(slab_in, W * ld_in * b, out, W * ld_out * b)) return fail(DC_ERR_ARG, "slab_in and out overlap");
   return hip_status(dc::launch_relayout(W, dtype, slab_in, ld_in, out, ld_out, bucket_col, bucket_numel,
-                                        pieces, num_pieces, out_numel, static_cast<hipStream_t>(stream)),
+                                        pieces, num_pieces, out_numel, nullptr,
+                                        static_cast<hipStream_t>(stream)),
                     "relayout launch");
+}
+
+dc_status dc_plan_relayout_tiles(int32_t dtype, int64_t bucket_col, int64_t bucket_numel,
+                                 const dc_piece* pieces, int32_t num_pieces, int64_t out_numel,
+                                 int64_t* tiles, int64_t tiles_capacity, int64_t* num_tiles) {
+  dc_status st;
+  if ((st = check_dtype(dtype))) return st;
+  if (bucket_col < 0 || bucket_numel < 0 || out_numel < 0 || num_pieces < 0)
+    return fail(DC_ERR_ARG, "negative bucket_col, bucket_numel, out_numel or num_pieces");
+  if ((st = check_extent("bucket_col", bucket_col)) || (st = check_extent("bucket_numel", bucket_numel)) ||
+      (st = check_extent("out_numel", out_numel)))
+    return st;
+  if (num_tiles == nullptr) return fail(DC_ERR_NULL, "num_tiles is NULL");
+  if (num_pieces > 0 && pieces == nullptr) return fail(DC_ERR_NULL, "pieces is NULL");
+  for (int32_t k = 0; k < num_pieces; ++k) {
+    if (pieces[k].len < 0) return fail(DC_ERR_ARG, "piece %d has a negative length", k);
+    if (k > 0 && pieces[k].dst < pieces[k - 1].dst) return fail(DC_ERR_ARG, "pieces not sorted by dst at %d", k);
+  }
+  const int64_t n = dc::relayout_tile_count(dtype, out_numel);
+  *num_tiles = n;
+  if (tiles == nullptr) return ok();  // size query
+  if (tiles_capacity < n)
+    return fail(DC_ERR_SHAPE, "tiles_capacity=%lld < %lld tiles", (long long)tiles_capacity, (long long)n);
+  // one sweep over the tiles in destination order beside the pieces: a tile
+  // copies straight from one piece when its whole destination run lies in
+  // the piece and its source run starts on a vector and stays in the bucket
+  const int64_t E = 16 / elem_bytes(dtype), span = dc::kRelayoutTile * E;
+  int32_t k = 0;
+  for (int64_t t = 0; t < n; ++t) {
+    const int64_t d0 = t * span, d1 = d0 + span;
+    while (k + 1 < num_pieces && pieces[k + 1].dst <= d0) ++k;
+    int64_t rec = -1;
+    if (num_pieces > 0 && d1 <= out_numel && pieces[k].dst <= d0 && d1 <= pieces[k].dst + pieces[k].len) {
+      const int64_t src0 = pieces[k].src + (d0 - pieces[k].dst);
+      if (src0 >= 0 && src0 + span <= bucket_numel && (bucket_col + src0) % E == 0) rec = (bucket_col + src0) / E;
+    }
+    tiles[dc::tile_slot(t, n)] = rec;
+  }
+  return ok();
+}
+
+dc_status dc_relayout_bucket_planned(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                                     void* out, int64_t ld_out, int64_t bucket_col, int64_t bucket_numel,
+                                     const dc_piece* pieces, int32_t num_pieces, int64_t out_numel,
+                                     const int64_t* tiles, int64_t num_tiles, void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype))) return st;
+  if (bucket_col < 0 || bucket_numel < 0 || out_numel < 0 || num_pieces < 0)
+    return fail(DC_ERR_ARG, "negative bucket_col, bucket_numel, out_numel or num_pieces");
+  if ((st = check_extent("bucket_col", bucket_col)) || (st = check_extent("bucket_numel", bucket_numel)))
+    return st;
+  if ((st = check_slab("slab_in", slab_in, ld_in, bucket_col + bucket_numel, dtype)) ||
+      (st = check_slab("out", out, ld_out, out_numel, dtype)))
+    return st;
+  if (num_pieces > 0 && pieces == nullptr) return fail(DC_ERR_NULL, "pieces is NULL");
+  if (out_numel > 0 && num_pieces > 0) {
+    const int64_t n = dc::relayout_tile_count(dtype, out_numel);
+    if (num_tiles != n)
+      return fail(DC_ERR_SHAPE, "num_tiles=%lld, the plan of out_numel=%lld has %lld", (long long)num_tiles,
+                  (long long)out_numel, (long long)n);
+    if (tiles == nullptr) return fail(DC_ERR_NULL, "tiles is NULL");
+  }
+  const int64_t b = elem_bytes(dtype);
+  if (overlaps(slab_in, W * ld_in * b, out, W * ld_out * b)) return fail(DC_ERR_ARG, "slab_in and out overlap");
+  return hip_status(dc::launch_relayout(W, dtype, slab_in, ld_in, out, ld_out, bucket_col, bucket_numel,
+                                        pieces, num_pieces, out_numel, tiles,
+                                        static_cast<hipStream_t>(stream)),
+                    "planned relayout launch");
 }
 
 dc_status dc_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,

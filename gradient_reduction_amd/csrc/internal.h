@@ -102,10 +102,23 @@ hipError_t launch_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int
                                    void* out, int64_t ld_out, const int64_t* seg_start,
                                    int32_t pre_div, hipStream_t stream);
 
+// The planned relayout's grid: tiles of kRelayoutTile destination vectors,
+// one per one-wave workgroup; a plan holds one int64 record per tile, at
+// tile_slot(t, count): the absolute source vector of the tile's first
+// vector when the whole tile copies from one piece with its source on a
+// vector boundary, else -1.
+constexpr int64_t kRelayoutTile = 64;
+inline int64_t relayout_tile_count(int32_t dtype, int64_t out_numel) {
+  const int64_t E = 16 / (dtype == DC_BF16 ? 2 : 4);
+  const int64_t nvec = (out_numel + E - 1) / E;
+  return (nvec + kRelayoutTile - 1) / kRelayoutTile;
+}
+
+// tiles == nullptr: every tile searches the piece table.
 hipError_t launch_relayout(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
                            int64_t ld_out, int64_t bucket_col, int64_t bucket_numel,
                            const dc_piece* pieces, int32_t npieces, int64_t out_numel,
-                           hipStream_t stream);
+                           const int64_t* tiles, hipStream_t stream);
 
 hipError_t launch_flush_buffers(int32_t W, int32_t dtype, int64_t bucket_numel, const dc_task* tasks,
                                 int32_t num_tasks, const void* const* in_ptrs, void* const* out_ptrs,

@@ -632,11 +632,25 @@ __global__ __launch_bounds__(kST) void k_stream_rows_g(const u32x4* __restrict__
 }
 
 // Row accesses in flight per compute unit (KB) at which each kernel below
-// measured fastest on the 7B-layer reduce-scatter / all-gather (W = 8) and
-// the W = 4 deferred reduce, 5-8% over a full compute unit (within 2% for
-// the ring-order reduce-scatter); other W keep the same budget.  The
-// variable-shard reduce-scatter measured no gain and keeps no cap.
-constexpr int kKbRs = 96, kKbRsRing = 144, kKbDeferred = 96, kKbAccRed = 120;
+// measured fastest, 5-10% over a full compute unit, in interleaved sweeps
+// on the 7B-layer reduce-scatter / all-gather (W = 8), the relaid buckets of
+// the 402.8M-element gradient and the W = 4 deferred reduce.  The
+// reduce-scatters in rank and ring order run at 9 workgroups per compute
+// unit at W = 8 (ring order 6.93 TB/s, against 6.71 at 10 and 6.31 at 16;
+// rank order 6.64 against 6.57 at 10 and 6.43 at 12); the variable-shard
+// one at 10 (6.62, against 6.53 at 8 or 9 and 6.34 uncapped).  Other W keep
+// the same budget.
+#ifndef DC_KB_RS
+#define DC_KB_RS 84
+#endif
+#ifndef DC_KB_RS_RING
+#define DC_KB_RS_RING 84
+#endif
+#ifndef DC_KB_RSV
+#define DC_KB_RSV 96
+#endif
+constexpr int kKbRs = DC_KB_RS, kKbRsRing = DC_KB_RS_RING, kKbRsv = DC_KB_RSV, kKbDeferred = 96,
+              kKbAccRed = 120;
 
 // All-gather launch shapes (vectors per thread, store policy; workgroups per
 // compute unit), from interleaved sweeps on the 7B-layer all-gather (W = 8
@@ -743,11 +757,13 @@ hipError_t rs_v_w(int32_t W, const void* in, int64_t ld_in, void* out, int64_t l
                   const SegArgs& sa, int64_t maxlen, float inv, float c, hipStream_t stream) {
   const dim3 grid((unsigned)sa.bpre[W]);
   (void)maxlen;
+  const int cap = stream_cap(W + 1, 1, kKbRsv);
   switch (W) {
 #define DC_RSV_W(w)                                                                          \
   case w:                                                                                    \
-    hipLaunchKernelGGL((k_rs_v<BF16, w, PRE>), grid, dim3(kST), 0, stream, W, in, ld_in, \
-                       out, ld_out, sa, inv, c);                                             \
+    hipLaunchKernelGGL((k_rs_v<BF16, w, PRE>), grid, dim3(kST),                              \
+                       pad_for(k_rs_v<BF16, w, PRE>, cap), stream, W, in, ld_in, out, ld_out, \
+                       sa, inv, c);                                                          \
     break;
     DC_RSV_W(1)
     DC_RSV_W(2)
@@ -756,8 +772,8 @@ hipError_t rs_v_w(int32_t W, const void* in, int64_t ld_in, void* out, int64_t l
     DC_RSV_W(16)
 #undef DC_RSV_W
     default:
-      hipLaunchKernelGGL((k_rs_v<BF16, 0, PRE>), grid, dim3(kST), 0, stream, W, in, ld_in,
-                         out, ld_out, sa, inv, c);
+      hipLaunchKernelGGL((k_rs_v<BF16, 0, PRE>), grid, dim3(kST), pad_for(k_rs_v<BF16, 0, PRE>, cap),
+                         stream, W, in, ld_in, out, ld_out, sa, inv, c);
   }
   return hipGetLastError();
 }

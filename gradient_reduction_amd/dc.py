@@ -73,6 +73,9 @@ _SIGS = {
     "dc_plan_relayout": ([_i32, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp], _i32),
     "dc_relayout_bucket": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp],
                            _i32),
+    "dc_plan_relayout_tiles": ([_i32, _i64, _i64, _vp, _i32, _i64, _vp, _i64, _vp], _i32),
+    "dc_relayout_bucket_planned": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _i64,
+                                    _vp, _i64, _vp], _i32),
     "dc_reduce_scatter_v": ([_i32, _i32, _vp, _i64, _vp, _i64, _vp, _i32, _vp], _i32),
     "dc_reduce_scatter": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
     "dc_reduce_scatter_ring": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i32, _vp], _i32),
@@ -329,6 +332,27 @@ def dc_relayout_bucket(W, dtype, slab_in, ld_in, out, ld_out, bucket_col, bucket
     _check("dc_relayout_bucket", lib().dc_relayout_bucket(
         W, dtype, _dev(slab_in), ld_in, _dev(out), ld_out, bucket_col, bucket_numel, _dev(pieces),
         num_pieces, out_numel, _stream(stream)))
+
+
+def dc_plan_relayout_tiles(dtype, bucket_col, bucket_numel, pieces, num_pieces, out_numel):
+    """Host only; returns the int64 tile plan (size query first, then the
+    fill)."""
+    pp, _a = (None, None) if num_pieces == 0 else _host(pieces, PIECE_DTYPE)
+    n = ctypes.c_int64(0)
+    _check("dc_plan_relayout_tiles", lib().dc_plan_relayout_tiles(
+        dtype, bucket_col, bucket_numel, pp, num_pieces, out_numel, None, 0, ctypes.byref(n)))
+    tiles = np.zeros(max(n.value, 1), np.int64)
+    _check("dc_plan_relayout_tiles", lib().dc_plan_relayout_tiles(
+        dtype, bucket_col, bucket_numel, pp, num_pieces, out_numel, tiles.ctypes.data_as(_vp),
+        n.value, ctypes.byref(n)))
+    return tiles[:n.value].copy()
+
+
+def dc_relayout_bucket_planned(W, dtype, slab_in, ld_in, out, ld_out, bucket_col, bucket_numel,
+                               pieces, num_pieces, out_numel, tiles, num_tiles, stream=None):
+    _check("dc_relayout_bucket_planned", lib().dc_relayout_bucket_planned(
+        W, dtype, _dev(slab_in), ld_in, _dev(out), ld_out, bucket_col, bucket_numel, _dev(pieces),
+        num_pieces, out_numel, _dev(tiles), num_tiles, _stream(stream)))
 
 
 def dc_reduce_scatter_v(W, dtype, in_, ld_in, out, ld_out, seg_start, pre_div, stream=None):

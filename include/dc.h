@@ -495,6 +495,43 @@ dc_status dc_relayout_bucket(int32_t W, int32_t dtype, const void* slab_in, int6
                              const dc_piece* pieces, int32_t num_pieces, int64_t out_numel,
                              void* stream);
 
+/* Tile plan for dc_relayout_bucket_planned: the relayout above, taken to
+ * the grain of the kernel's tiles once per bucket layout ([DS] Design
+ * points: a bucket's layout is fixed, so what its flush needs is worked out
+ * ahead of it).  The relaid bucket's columns [0, out_numel) fall into tiles
+ * of 64 16-byte vectors (512 bf16 or 256 fp32 columns); one int64 per
+ * tile, in an order private to the library, records where a tile copies
+ * from when the whole tile lies inside one piece whose source run starts
+ * on a 16-byte vector of the slab and stays in the bucket.  Host only.
+ *   dtype, bucket_col, bucket_numel, pieces, num_pieces, out_numel
+ *                    as for dc_relayout_bucket (pieces on the host, sorted
+ *                    by dst as dc_plan_relayout writes them)
+ *   tiles            host int64[tiles_capacity] out; NULL asks for the
+ *                    count only
+ *   num_tiles        out: ceil(ceil(out_numel / E) / 64), E = 8 (bf16) or
+ *                    4 (fp32)
+ * A negative piece length or pieces out of dst order is DC_ERR_ARG; fewer
+ * than num_tiles slots is DC_ERR_SHAPE. */
+dc_status dc_plan_relayout_tiles(int32_t dtype, int64_t bucket_col, int64_t bucket_numel,
+                                 const dc_piece* pieces, int32_t num_pieces, int64_t out_numel,
+                                 int64_t* tiles, int64_t tiles_capacity, int64_t* num_tiles);
+
+/* dc_relayout_bucket from a tile plan: the same result, bit for bit.  A
+ * tile with a record copies straight from it; any other tile searches the
+ * pieces as dc_relayout_bucket does.  Arguments as for dc_relayout_bucket,
+ * plus
+ *   tiles, num_tiles  device int64[num_tiles] from dc_plan_relayout_tiles
+ *                     on the same dtype, bucket, pieces and out_numel;
+ *                     num_tiles must be the count it gives (else
+ *                     DC_ERR_SHAPE)
+ * A record is checked against the bucket before it is used: a plan made for
+ * other pieces can misplace data inside the bucket's columns of `out`, but
+ * never reads or writes outside them. */
+dc_status dc_relayout_bucket_planned(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                                     void* out, int64_t ld_out, int64_t bucket_col, int64_t bucket_numel,
+                                     const dc_piece* pieces, int32_t num_pieces, int64_t out_numel,
+                                     const int64_t* tiles, int64_t num_tiles, void* stream);
+
 /* Reduce-scatter with variable shards: shard q is columns
  * [seg_start[q], seg_start[q+1]) of `in`, and
  *   out[q][k] = round_dtype(fold over r of pre(in[r][seg_start[q] + k]))

@@ -589,3 +589,134 @@ def test_plan_flush_buffers_argument_checks():
     expect(dc.DC_ERR_NULL, call, in_ptrs=None)
     expect(dc.DC_ERR_ARG, call, pre_div=3)
     expect(dc.DC_ERR_ARG, call, W=0)
+
+
+def _xcd_major(recs):
+    """Records in tile order placed XCD-major (tile b at (b mod 8)
+    floor(n/8) + min(b mod 8, n mod 8) + floor(b/8))."""
+    n = len(recs)
+    b = np.arange(n)
+    r, q, rem = b % 8, n // 8, n % 8
+    out = np.zeros_like(recs)
+    out[r * q + np.minimum(r, rem) + b // 8] = recs
+    return out
+
+
+def _brute_relayout_tiles(dtype, bucket_col, bucket_numel, pieces, out_numel):
+    """The relayout tile records as the header defines them, from a
+    per-column piece index: tile t covers relaid columns [t*64E, (t+1)*64E);
+    it gets the slab vector its source starts at when all of its columns lie
+    in [0, out_numel) and in one piece whose source run starts on a vector
+    and stays in the bucket, else -1."""
+    E = 8 if dtype == wl.DT_BF16 else 4
+    span = 64 * E
+    n = -(-(-(-out_numel // E)) // 64)
+    pid = np.full(n * span, -1, np.int64)
+    for k, pc in enumerate(pieces):
+        lo, hi = max(int(pc["dst"]), 0), min(int(pc["dst"]) + int(pc["len"]), n * span)
+        if hi > lo:
+            pid[lo:hi] = k
+    recs = np.full(n, -1, np.int64)
+    for t in range(n):
+        d0 = t * span
+        ids = pid[d0:d0 + span]
+        if d0 + span > out_numel or ids[0] < 0 or np.any(ids != ids[0]):
+            continue
+        pc = pieces[int(ids[0])]
+        src0 = int(pc["src"]) + d0 - int(pc["dst"])
+        if src0 >= 0 and src0 + span <= bucket_numel and (bucket_col + src0) % E == 0:
+            recs[t] = (bucket_col + src0) // E
+    return _xcd_major(recs)
+
+
+def test_plan_relayout_tiles_matches_definition():
+    """dc_plan_relayout_tiles (host code) against the records the header
+    defines: the planner's pieces of small and random workloads at several
+    bucket-start residues, and random piece tables with unaligned sources,
+    gaps and empty pieces."""
+    rng = random.Random(12)
+    cases = []
+    ws = [wl.tiny_flush()]
+    for k in range(5):
+        W = rng.choice([2, 4, 8])
+        dt = rng.choice([wl.DT_BF16, wl.DT_F32])
+        sizes = [rng.choice([0, 3, 64, 700, 2048, 4096, 9000]) for _ in range(60)]
+        ws.append(wl.custom_flush(f"t{k}", W, dt, sizes, group_begin=[0, 40, 60], group_comm=[0, 0],
+                                  comms=[wl.Comm(W, 1)], capacity=40_000))
+    for w in ws:
+        flat, ps, off, pids = oracle.partition_ids(w.numel, w.group_begin, w.group_parts())
+        psize = np.zeros(w.P, np.int64)
+        for g in range(w.G):
+            psize[w.group_begin[g]:w.group_begin[g + 1]] = ps[g]
+        for bk in w.buckets:
+            t = dc.tasks_array([(x.offset, x.numel, x.param, x.comm) for x in bk.tasks])
+            pieces, seg = dc.dc_plan_relayout(w.W, t, len(t), flat, psize, w.P)
+            for shift in (0, 1, 8):
+                cases.append((w.dtype, bk.col + shift, bk.numel, pieces, int(seg[-1])))
+    for k in range(40):
+        dt = rng.choice([wl.DT_BF16, wl.DT_F32])
+        numel = rng.randint(0, 20_000)
+        dst, pcs = 0, []
+        for _ in range(rng.randint(0, 12)):
+            dst += rng.choice([0, 0, 1, 8, 300])
+            ln = rng.choice([0, 5, 512, 1024, 3000])
+            src = rng.randint(-4, numel) if rng.random() < 0.2 else rng.choice([0, 8, 512, 1000])
+            pcs.append((src, dst, ln, 0))
+            dst += ln
+        pieces = np.array(pcs, dc.PIECE_DTYPE) if pcs else np.zeros(0, dc.PIECE_DTYPE)
+        cases.append((dt, rng.choice([0, 3, 64, 4096]), numel, pieces, dst + rng.choice([0, 7, 600])))
+    whole = 0
+    for dt, col, numel, pieces, out_numel in cases:
+        got = dc.dc_plan_relayout_tiles(dt, col, numel, pieces, len(pieces), out_numel)
+        want = _brute_relayout_tiles(dt, col, numel, pieces, out_numel)
+        assert np.array_equal(got, want), (dt, col, numel, out_numel)
+        whole += int(np.sum(got >= 0))
+    assert whole > 100        # the cases reach the straight copy, not only the search
+
+
+def test_plan_relayout_tiles_argument_checks():
+    pcs = np.array([(0, 0, 600, 0), (600, 600, 600, 0)], dc.PIECE_DTYPE)
+    assert len(dc.dc_plan_relayout_tiles(0, 0, 1200, pcs, 2, 1200)) == 3
+    assert len(dc.dc_plan_relayout_tiles(1, 0, 1200, pcs, 2, 1200)) == 5
+    assert len(dc.dc_plan_relayout_tiles(0, 0, 0, None, 0, 0)) == 0
+    bad = pcs.copy()
+    bad[1]["dst"] = 0
+    bad[0]["dst"] = 600
+    expect(dc.DC_ERR_ARG, dc.dc_plan_relayout_tiles, 0, 0, 1200, bad, 2, 1200)   # out of dst order
+    bad = pcs.copy()
+    bad[0]["len"] = -1
+    expect(dc.DC_ERR_ARG, dc.dc_plan_relayout_tiles, 0, 0, 1200, bad, 2, 1200)
+    expect(dc.DC_ERR_ARG, dc.dc_plan_relayout_tiles, 0, -1, 1200, pcs, 2, 1200)
+    expect(dc.DC_ERR_DTYPE, dc.dc_plan_relayout_tiles, 5, 0, 1200, pcs, 2, 1200)
+    n = ctypes.c_int64(0)
+    rc = dc.lib().dc_plan_relayout_tiles(0, 0, 1200, pcs.ctypes.data_as(ctypes.c_void_p), 2, 1200,
+                                         np.zeros(2, np.int64).ctypes.data_as(ctypes.c_void_p), 2,
+                                         ctypes.byref(n))
+    assert rc == dc.DC_ERR_SHAPE and n.value == 3
+    rc = dc.lib().dc_plan_relayout_tiles(0, 0, 1200, pcs.ctypes.data_as(ctypes.c_void_p), 2, 1200,
+                                         None, 0, None)
+    assert rc == dc.DC_ERR_NULL
+    rc = dc.lib().dc_plan_relayout_tiles(0, 0, 1200, None, 2, 1200, None, 0, ctypes.byref(n))
+    assert rc == dc.DC_ERR_NULL
+
+
+def test_relayout_planned_argument_checks():
+    f = dc.dc_relayout_bucket_planned
+    ok = dict(W=8, dtype=0, slab_in=FAKE, ld_in=2048, out=FAKE + (1 << 30), ld_out=2048,
+              bucket_col=0, bucket_numel=2048, pieces=TASK_PTR, num_pieces=1, out_numel=2048,
+              tiles=TASK_PTR + 4096, num_tiles=4, stream=0)
+
+    def call(**ch):
+        a = dict(ok)
+        a.update(ch)
+        return f(**a)
+
+    expect(dc.DC_ERR_SHAPE, call, num_tiles=3)               # 2048 bf16 columns: 4 tiles
+    expect(dc.DC_ERR_SHAPE, call, dtype=1, num_tiles=4)      # fp32: 8 tiles
+    expect(dc.DC_ERR_NULL, call, tiles=None)
+    expect(dc.DC_ERR_NULL, call, pieces=None)
+    expect(dc.DC_ERR_ARG, call, W=0)
+    expect(dc.DC_ERR_ARG, call, bucket_col=-1)
+    expect(dc.DC_ERR_NULL, call, slab_in=None)
+    expect(dc.DC_ERR_ARG, call, out=FAKE)                    # overlaps slab_in
+    expect(dc.DC_ERR_SHAPE, call, ld_out=1024)               # out_numel past ld_out

@@ -24,9 +24,10 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def run_bucket(w, b, x, ld, col_shift=0):
-    """Relayout + reduce-scatter-v of bucket b on the GPU; returns host
-    (relaid, shards, seg, pieces)."""
+def run_bucket(w, b, x, ld, col_shift=0, planned=False, keep=None):
+    """Relayout (searched, or from its tile plan) + reduce-scatter-v of
+    bucket b on the GPU; returns host (relaid, shards, seg, pieces, flat,
+    psize).  keep: a dict that receives the device relaid slab."""
     import torch
     bk = w.buckets[b]
     flat, psize = U.psize_per_param(w)
@@ -37,13 +38,22 @@ def run_bucket(w, b, x, ld, col_shift=0):
     relaid = U.empty_slab(w.dtype, w.W, ld_r)
     d_pieces = torch.from_numpy(pieces.view(np.uint8).copy()).cuda() if len(pieces) else \
         torch.zeros(32, dtype=torch.uint8, device="cuda")
-    dc.dc_relayout_bucket(w.W, w.dtype, x, ld, relaid, ld_r, bk.col + col_shift, bk.numel, d_pieces,
-                          len(pieces), n)
+    if planned:
+        tiles = dc.dc_plan_relayout_tiles(w.dtype, bk.col + col_shift, bk.numel, pieces, len(pieces), n)
+        d_tiles = torch.from_numpy(tiles).cuda() if len(tiles) else None
+        dc.dc_relayout_bucket_planned(w.W, w.dtype, x, ld, relaid, ld_r, bk.col + col_shift, bk.numel,
+                                      d_pieces, len(pieces), n, d_tiles, len(tiles))
+    else:
+        dc.dc_relayout_bucket(w.W, w.dtype, x, ld, relaid, ld_r, bk.col + col_shift, bk.numel,
+                              d_pieces, len(pieces), n)
     maxlen = int(max(seg[1:] - seg[:-1])) if w.W else 0
     ld_s = max(64, wl.round_up(maxlen, 64))
     shards = U.empty_slab(w.dtype, w.W, ld_s)
     dc.dc_reduce_scatter_v(w.W, w.dtype, relaid, ld_r, shards, ld_s, seg, w.pre_div)
     torch.cuda.synchronize()
+    if keep is not None:
+        keep["relaid"], keep["ld_r"] = relaid, ld_r
+        return None, U.to_host(shards, w.dtype), seg, pieces, flat, psize
     return U.to_host(relaid, w.dtype), U.to_host(shards, w.dtype), seg, pieces, flat, psize
 
 
@@ -60,14 +70,15 @@ def small_workloads():
     return out
 
 
+@pytest.mark.parametrize("planned", [False, True], ids=["searched", "planned"])
 @pytest.mark.parametrize("w", small_workloads(), ids=lambda w: w.name)
-def test_relayout_reduce_scatter_small(w):
-    U.say("relayout", w.name)
+def test_relayout_reduce_scatter_small(w, planned):
+    U.say("relayout", w.name, "planned" if planned else "searched")
     ld = w.ld
     x = U.gen_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, w.scale)
     hx = U.host_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, w.scale)
     for b, bk in enumerate(w.buckets):
-        relaid, shards, seg, pieces, flat, psize = run_bucket(w, b, x, ld)
+        relaid, shards, seg, pieces, flat, psize = run_bucket(w, b, x, ld, planned=planned)
         t_off = [k.offset for k in bk.tasks]
         t_numel = [k.numel for k in bk.tasks]
         t_param = [k.param for k in bk.tasks]
@@ -85,16 +96,18 @@ def test_relayout_reduce_scatter_small(w):
         assert np.array_equal(U.bits(shards, w.dtype), U.bits(hs, w.dtype)), (w.name, b)
 
 
-def test_relayout_unaligned_bucket_start():
+@pytest.mark.parametrize("planned", [False, True], ids=["searched", "planned"])
+def test_relayout_unaligned_bucket_start(planned):
     """A bucket whose first column is not vector aligned: every source vector
-    is misaligned, so the element path moves everything."""
+    is misaligned, so the element path moves everything (the tile plan
+    records no straight copy)."""
     import torch
     w = wl.custom_flush("unaligned", 8, wl.DT_BF16, [100, 37, 2000, 5], capacity=10 ** 9, pre_div=1)
     shift = 3
     ld = wl.round_up(w.total + shift, 64)
     x = U.gen_slab(w.dtype, w.W, ld, ld, 5, 0, w.scale)
     hx = U.host_slab(w.dtype, w.W, ld, ld, 5, 0, w.scale)
-    relaid, shards, seg, pieces, flat, psize = run_bucket(w, 0, x, ld, col_shift=shift)
+    relaid, shards, seg, pieces, flat, psize = run_bucket(w, 0, x, ld, col_shift=shift, planned=planned)
     bk = w.buckets[0]
     dest, oseg = oracle.relayout_map(w.W, [k.offset for k in bk.tasks], [k.numel for k in bk.tasks],
                                      [k.param for k in bk.tasks], [k.comm for k in bk.tasks], flat,
@@ -105,15 +118,28 @@ def test_relayout_unaligned_bucket_start():
 
 
 def test_relayout_reduce_scatter_w8_402m_full_size():
-    """Every bucket of the 402.8M-element W=8 workload: sampled shard
-    positions against the oracle's ZeRO-2 values of their source columns."""
+    """Every bucket of the 402.8M-element W=8 workload, relaid from its tile
+    plan as the bench does: every relaid column of every row against the
+    relayout's definition (out[r][dst + i] = in[r][bucket_col + src + i],
+    gathered by torch), and sampled shard positions against the oracle's
+    ZeRO-2 values of their source columns."""
     import torch
     w = wl.owner_flush_w8()
     U.say("relayout full size", w.total)
     x = U.gen_slab(w.dtype, w.W, w.ld, w.total, w.value_seed, 0, w.scale)
     rng = np.random.default_rng(2)
     for b, bk in enumerate(w.buckets):
-        _, shards, seg, pieces, flat, psize = run_bucket(w, b, x, w.ld)
+        keep = {}
+        _, shards, seg, pieces, flat, psize = run_bucket(w, b, x, w.ld, planned=True, keep=keep)
+        n = int(seg[-1])
+        src_of = np.full(n, -1, np.int64)
+        for pc in pieces:
+            src_of[pc["dst"]:pc["dst"] + pc["len"]] = bk.col + pc["src"] + np.arange(pc["len"])
+        assert np.all(src_of >= 0), b
+        idx = torch.from_numpy(src_of).cuda()
+        want = torch.index_select(x, 1, idx)
+        assert torch.equal(keep["relaid"][:, :n], want), b
+        del keep, idx, want
         # sample destination positions: piece ends and random
         picks = set()
         for pc in pieces[rng.choice(len(pieces), size=min(40, len(pieces)), replace=False)]:
