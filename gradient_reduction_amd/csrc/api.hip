@@ -461,7 +461,7 @@ dc_status dc_plan_flush_buffers(int32_t W, int32_t dtype, int64_t bucket_numel, 
   const int64_t nslots = (bucket_numel + E - 1) / E;
   int32_t k = 0;
   for (int64_t b = 0; b < count; ++b) {
-    const int64_t s0 = b * 128, s1 = std::min(s0 + 128, nslots);
+    const int64_t s0 = b * dc::kBufTile, s1 = std::min(s0 + dc::kBufTile, nslots);
     const int64_t lo = s0 * E, hi = std::min(s1 * E, bucket_numel);
     // first: the last task starting at or before lo; last: the last starting before hi
     while (k + 1 < num_tasks && tasks[k + 1].offset <= lo) ++k;

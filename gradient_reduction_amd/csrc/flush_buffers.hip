@@ -18,14 +18,19 @@
 namespace dc {
 namespace {
 
-#ifndef DC_BUF_U
-#define DC_BUF_U 2                  // vector slots per thread per tile
-#endif
 #ifndef DC_BUF_TPB
 #define DC_BUF_TPB 64               // threads per workgroup (one wave)
 #endif
-constexpr int kBufU = DC_BUF_U;
 constexpr int kBT = DC_BUF_TPB;
+// Vector slots per thread of a tile: planned launches take the plan's tiles;
+// a searched launch takes two per thread (1-7% faster than one or four,
+// where each tile searches and stages its tasks).
+constexpr int kBufU = (int)(kBufTile / kBT);
+#ifndef DC_BUF_US
+#define DC_BUF_US 2
+#endif
+constexpr int kBufUSearched = DC_BUF_US;
+static_assert(kBufU * kBT == kBufTile, "a tile is whole slots per thread");
 #ifndef DC_BUF_PTRS
 #define DC_BUF_PTRS 256             // staged pointers per table (LDS): small enough
                                     // that one-wave workgroups are not LDS bound
@@ -55,7 +60,8 @@ __device__ __forceinline__ void comm_recip(int32_t c, float* inv, float* cf) {
   *inv = (c & (c - 1)) == 0 ? 1.0f / (float)c : 0.0f;  // exact for powers of two
 }
 
-template <bool BF16, int WT, bool PRE>
+// U: vector slots per thread of the launch's tiles (kBufU when planned).
+template <bool BF16, int WT, bool PRE, int U>
 __global__ __launch_bounds__(kBT) void k_flush_buffers(BufParams p) {
   constexpr int E = BF16 ? 8 : 4;
   constexpr int EB = BF16 ? 2 : 4;
@@ -77,8 +83,8 @@ __global__ __launch_bounds__(kBT) void k_flush_buffers(BufParams p) {
       s_cst[q] = p.cstride[q];
     }
   }
-  const int64_t t0 = (int64_t)blockIdx.x * (kBT * kBufU);
-  const int64_t t1 = min(t0 + (int64_t)(kBT * kBufU), p.nslots);
+  const int64_t t0 = (int64_t)blockIdx.x * (kBT * U);
+  const int64_t t1 = min(t0 + (int64_t)(kBT * U), p.nslots);
   const int64_t lo = t0 * E, hi = min(t1 * E, p.bucket_numel);
   int32_t first, last;
   if (p.tiles != nullptr) {
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(kBT) void k_flush_buffers(BufParams p) {
           float inv, cf;
           comm_recip(WT, &inv, &cf);
 #pragma unroll 1
-          for (int u = 0; u < kBufU; ++u) {
+          for (int u = 0; u < U; ++u) {
             const int64_t v = t0 + threadIdx.x + (int64_t)u * kBT;
             if (v >= t1) break;
             const int64_t byte = (v * E - t.offset) * EB;
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(kBT) void k_flush_buffers(BufParams p) {
     }
     __syncthreads();
 #pragma unroll 1
-    for (int u = 0; u < kBufU; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int64_t v = t0 + threadIdx.x + (int64_t)u * kBT;
       if (v >= t1) break;
       const int64_t d0 = v * E;
@@ -226,21 +232,27 @@ __global__ __launch_bounds__(kBT) void k_flush_buffers(BufParams p) {
   }
 }
 
-// Workgroups per compute unit for a planned launch at W <= 8: 12 measured
-// 3-4% faster than a full compute unit at W = 8 bf16 (6 and 8 less so);
-// at W = 16 fp32 every cap tried (6-12) was 10-30% slower, so none.
-constexpr int kBufPlannedCap = 12;
+// Workgroups per compute unit for a planned launch at W <= 8, from
+// interleaved sweeps with one-slot-per-thread tiles at W = 8 bf16: 12 (6.28
+// TB/s) against 6.25 at 14, 6.16 at 16, 5.94 at 10 and 5.78 at 8; at W = 16
+// fp32 caps of 8 and 12 were 8-20% slower than none.
+#ifndef DC_BUF_CAP8
+#define DC_BUF_CAP8 12
+#endif
+#ifndef DC_BUF_CAP16
+#define DC_BUF_CAP16 0
+#endif
+constexpr int kBufPlannedCap = DC_BUF_CAP8;
 
-template <bool BF16, bool PRE>
-hipError_t launch_w(const BufParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.nslots + kBT * kBufU - 1) / (kBT * kBufU)));
-  const int cap = (p.tiles != nullptr && p.W <= 8) ? kBufPlannedCap : 0;
+template <bool BF16, bool PRE, int U>
+hipError_t launch_wu(const BufParams& p, int cap, hipStream_t stream) {
+  const dim3 grid((unsigned)((p.nslots + kBT * U - 1) / (kBT * U)));
   switch (p.W) {
-#define DC_FB_W(w)                                                                          \
-  case w:                                                                                   \
-    hipLaunchKernelGGL((k_flush_buffers<BF16, w, PRE>), grid, dim3(kBT),                    \
-                       occupancy_pad(reinterpret_cast<const void*>(&k_flush_buffers<BF16, w, PRE>), cap), \
-                       stream, p);                                                          \
+#define DC_FB_W(w)                                                                              \
+  case w:                                                                                       \
+    hipLaunchKernelGGL((k_flush_buffers<BF16, w, PRE, U>), grid, dim3(kBT),                     \
+                       occupancy_pad(reinterpret_cast<const void*>(&k_flush_buffers<BF16, w, PRE, U>), cap), \
+                       stream, p);                                                              \
     break;
     DC_FB_W(2)
     DC_FB_W(4)
@@ -248,9 +260,15 @@ hipError_t launch_w(const BufParams& p, hipStream_t stream) {
     DC_FB_W(16)
 #undef DC_FB_W
     default:
-      hipLaunchKernelGGL((k_flush_buffers<BF16, 0, PRE>), grid, dim3(kBT), 0, stream, p);
+      hipLaunchKernelGGL((k_flush_buffers<BF16, 0, PRE, U>), grid, dim3(kBT), 0, stream, p);
   }
   return hipGetLastError();
+}
+
+template <bool BF16, bool PRE>
+hipError_t launch_w(const BufParams& p, hipStream_t stream) {
+  if (p.tiles == nullptr) return launch_wu<BF16, PRE, kBufUSearched>(p, 0, stream);
+  return launch_wu<BF16, PRE, kBufU>(p, p.W <= 8 ? kBufPlannedCap : DC_BUF_CAP16, stream);
 }
 
 }  // namespace

@@ -367,7 +367,7 @@ dc_status dc_flush_bucket_buffers(int32_t W, int32_t dtype, int64_t bucket_numel
 
 /* Plan of a fused flush (dc_flush_bucket_buffers' tables), host only, once
  * per registration: the fused kernel cuts the bucket's coordinates
- * [0, bucket_numel) into tiles of 128 slots of 16 bytes (slot v covers
+ * [0, bucket_numel) into tiles of 64 slots of 16 bytes (slot v covers
  * coordinates [v E, v E + E), E elements per 16 bytes), and tile b's record
  * names the first task starting at or before the tile and the last starting
  * inside it (last < first: none), and sets flags bit 0 when the tile's slots
@@ -377,7 +377,7 @@ dc_status dc_flush_bucket_buffers(int32_t W, int32_t dtype, int64_t bucket_numel
  *   tasks, comms        host copies: tasks sorted, disjoint, inside the
  *                       bucket, comm in range (else DC_ERR_TASKS)
  *   tiles, capacity     host dc_tile[capacity] out; NULL asks for the count
- *   num_tiles           out: ceil(ceil(bucket_numel / E) / 128), 0 with no
+ *   num_tiles           out: ceil(ceil(bucket_numel / E) / 64), 0 with no
  *                       tasks; fewer slots than that is DC_ERR_SHAPE */
 dc_status dc_plan_flush_buffers(int32_t W, int32_t dtype, int64_t bucket_numel, const dc_task* tasks,
                                 int32_t num_tasks, const dc_comm* comms, int32_t num_comms,

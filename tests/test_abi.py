@@ -524,11 +524,11 @@ def _brute_plan_buffers(dtype, numel, tasks):
     tile's coordinate range, XCD-major."""
     E = 8 if dtype == wl.DT_BF16 else 4
     nslots = -(-numel // E)
-    count = -(-nslots // 128) if len(tasks) else 0
+    count = -(-nslots // 64) if len(tasks) else 0
     off = tasks["offset"].astype(np.int64)
     out = np.zeros(count, dc.TILE_DTYPE)
     for b in range(count):
-        lo, s1 = 128 * b * E, min(128 * (b + 1), nslots)
+        lo, s1 = 64 * b * E, min(64 * (b + 1), nslots)
         hi = min(s1 * E, numel)
         first = max(int(np.searchsorted(off, lo, side="right")) - 1, 0)
         last = int(np.searchsorted(off, hi, side="left")) - 1
@@ -577,7 +577,7 @@ def test_plan_flush_buffers_argument_checks():
     f = dc.dc_flush_bucket_buffers_planned
     ok = dict(W=8, dtype=0, bucket_numel=2048, tasks=TASK_PTR, num_tasks=1, in_ptrs=FAKE,
               out_ptrs=FAKE, comms=comms, num_comms=1, pre_div=1, tiles=TASK_PTR + 4096,
-              num_tiles=2, stream=0)
+              num_tiles=4, stream=0)      # 2048 bf16 coordinates: 256 slots, 4 tiles
 
     def call(**ch):
         a = dict(ok)
@@ -585,6 +585,7 @@ def test_plan_flush_buffers_argument_checks():
         return f(**a)
 
     expect(dc.DC_ERR_SHAPE, call, num_tiles=3)
+    expect(dc.DC_ERR_SHAPE, call, num_tiles=2)
     expect(dc.DC_ERR_NULL, call, tiles=None)
     expect(dc.DC_ERR_NULL, call, in_ptrs=None)
     expect(dc.DC_ERR_ARG, call, pre_div=3)
