@@ -649,8 +649,14 @@ __global__ __launch_bounds__(kST) void k_stream_rows_g(const u32x4* __restrict__
 #ifndef DC_KB_RSV
 #define DC_KB_RSV 96
 #endif
-constexpr int kKbRs = DC_KB_RS, kKbRsRing = DC_KB_RS_RING, kKbRsv = DC_KB_RSV, kKbDeferred = 96,
-              kKbAccRed = 120;
+#ifndef DC_KB_DEFERRED
+#define DC_KB_DEFERRED 96
+#endif
+#ifndef DC_KB_ACCRED
+#define DC_KB_ACCRED 120
+#endif
+constexpr int kKbRs = DC_KB_RS, kKbRsRing = DC_KB_RS_RING, kKbRsv = DC_KB_RSV,
+              kKbDeferred = DC_KB_DEFERRED, kKbAccRed = DC_KB_ACCRED;
 
 // All-gather launch shapes (vectors per thread, store policy; workgroups per
 // compute unit), from interleaved sweeps on the 7B-layer all-gather (W = 8
