@@ -338,6 +338,7 @@ TRAFFIC_PROFILES = {
     "deferred": ("deferred_qwen3_k8", "slab_ops.hip"),
     "deferred_fused": ("deferred_qwen3_k8_fused", "slab_ops.hip"),
     "rs_ag": ("rs_ag_w8_202m", "slab_ops.hip"),
+    "rs_ag_allgather": ("allgather_w8_202m", "slab_ops.hip"),
     "schedules_w8": ("schedules_w8_202m", "slab_ops.hip"),
 }
 
@@ -998,6 +999,7 @@ def bench_rs_ag(args):
              "all_gather_rank_frac": round(gbs[1] / HBM_PEAK_GBS, 4),
              "all_gather_ring_frac": round(gbs[2] / HBM_PEAK_GBS, 4),
              "all_gather_launch_ms": {"rank": round(reg[1], 4), "ring": round(reg[2], 4)},
+             "all_gather_traffic": traffic_from_profile("rs_ag_allgather", w.name),
              "all_gather_gbs_with_events": {"rank": round(ev[1], 1), "ring": round(ev[2], 1)}}
     step()
     torch.cuda.synchronize()
