@@ -189,3 +189,47 @@ def planned_flush(W, dtype, x, ld_in, y, ld_out, col0, numel, tasks, d_tasks, P,
     dc.dc_flush_bucket_planned(W, dtype, x, ld_in, y, ld_out, col0, numel, d_tasks, len(tasks), d_own,
                                d_flat, d_ps, P, comms, len(comms), pre, keep[0], len(tiles), roots)
     return keep
+
+
+def fused_flush_full_size(w, planned=True):
+    """Per-rank gradient arenas [W, ld] holding each param at a 128-byte
+    aligned position with the slab's values, grad-buffer arenas of the same
+    layout for the holders, the executor's tables, and every bucket flushed."""
+    import torch
+    from gradient_reduction_amd import executor
+    ex = executor.from_workload(w, reduce_to_owner=True)
+    ex.build_owner_map()
+    ex.fetch_metadata()
+    eb = w.elem_bytes()
+    pcol = np.zeros(w.P, np.int64)
+    for bk in w.buckets:
+        for t in bk.tasks:
+            pcol[t.param] = bk.col + t.offset
+    pad = 128 // eb
+    poff = np.zeros(w.P, np.int64)
+    pos = 0
+    for p in range(w.P):
+        poff[p] = pos
+        pos = wl.round_up(pos + w.numel[p], pad)
+    ld = wl.round_up(max(pos, 1), 64)
+    say("full-size arenas", w.name, "ld", ld)
+    d_in = empty_slab(w.dtype, w.W, ld, sentinel=False)
+    stream = torch.cuda.current_stream().cuda_stream
+    for p in range(w.P):
+        if w.numel[p]:
+            synth.fill_slab_device(w.dtype, w.value_seed, 0, w.scale, w.W, ld, w.numel[p],
+                                   d_in.data_ptr() + int(poff[p]) * eb, stream, col0=int(pcol[p]))
+    d_out = empty_slab(w.dtype, w.W, ld)
+    hold = np.zeros((w.W, w.P), bool)
+    for b, bk in enumerate(w.buckets):
+        h = ex.holders(b)
+        for k, t in enumerate(bk.tasks):
+            hold[:, t.param] |= h[k]
+    rows = np.arange(w.W, dtype=np.int64)[:, None] * ld
+    in_addr = (d_in.data_ptr() + (rows + poff[None, :]) * eb).astype(np.uint64)
+    out_addr = np.where(hold, d_out.data_ptr() + (rows + poff[None, :]) * eb, 0).astype(np.uint64)
+    ex.register_buffers(in_addr, out_addr, planned=planned)
+    for b in range(len(w.buckets)):
+        ex.flush_buffers(b)
+    torch.cuda.synchronize()
+    return ex, d_out, ld, poff, pcol, hold

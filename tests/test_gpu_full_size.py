@@ -19,7 +19,9 @@ for bit over every column of every row:
     accumulate, in column chunks (MaxText PR "Defer the data-parallel
     gradient all-reduce to update() under gradient accumulation", What);
   * the 7B-layer W = 8 bf16 reduce-scatter and the all-gather in rank and
-    in ring order ("AllGather", semantic definition and Ring AllGather).
+    in ring order ("AllGather", semantic definition and Ring AllGather);
+  * the W = 8 fused copy-in / copy-out flush, searched and planned: every
+    element of every rank's grad-buffer arena.
 """
 import numpy as np
 import pytest
@@ -217,3 +219,34 @@ def test_reduce_scatter_all_gather_7b_layer_every_column():
         _check(_host_cols(y, 0, M, dtype), want, f"all-gather, {name} order")
         U.say(f"  all-gather in {name} order equals the oracle")
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("planned", [True, False], ids=["planned", "searched"])
+def test_flush_buffers_w8_402m_every_element(planned):
+    """The fused copy-in / copy-out flush of the 402.8M-element W = 8
+    gradient (DeepSpeed issue, problem statement: the copy-out skips every
+    rank whose grad buffer is empty), from per-rank arenas with every param
+    at a 128-byte aligned position: every element of every rank's grad-buffer
+    arena.  A holder's buffer of param p equals the oracle's flush of p's
+    slab columns, every other element (non-holders, padding) keeps the
+    sentinel."""
+    import torch
+    w = wl.owner_flush_w8()
+    U.say("whole-output fused flush", w.name, "planned" if planned else "searched")
+    ex, d_out, ld, poff, pcol, hold = U.fused_flush_full_size(w, planned)
+    got = d_out.cpu().numpy().view(np.uint16)
+    del d_out
+    torch.cuda.empty_cache()
+    owner = OC.owner_of(w)
+    want = np.full((w.W, ld), U.SENTINEL16, np.uint16)
+    for b, bk in enumerate(w.buckets):
+        out = _bits(OC.flush_bucket(w, b, owner=owner, init=U.SENTINEL16), w.dtype)
+        for t in bk.tasks:
+            p, n = t.param, t.numel
+            assert pcol[p] == bk.col + t.offset
+            ref = out[owner[p] if owner[p] >= 0 else 0, t.offset:t.offset + n]
+            rows = np.nonzero(hold[:, p])[0]
+            want[rows, poff[p]:poff[p] + n] = ref
+        U.say(f"  bucket {b}: oracle done")
+    _check(got, want, "fused flush arenas")
+    U.say(f"  {int(hold.sum())} holder buffers and every other element of {w.W} x {ld} checked")
