@@ -76,10 +76,8 @@ struct FlushParams {
   int64_t root_tiles;        // planned: tiles that write one row (host side: the residency cap)
 };
 
-// Pre-division modes: none, multiply by an exact power-of-two reciprocal
-// (the same correctly rounded result as dividing), or a true division.
-enum { kPreNone = 0, kPreMul = 1, kPreDiv = 2 };
-
+// A contribution pre-divided in mode kPreNone, kPreMul (an exact power-of-two
+// reciprocal: the same correctly rounded result as dividing) or kPreDiv.
 __device__ __forceinline__ float pre_scale(float x, int mode, float inv, float c) {
   if (mode == kPreMul) return x * inv;
   if (mode == kPreDiv) return x / c;
