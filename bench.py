@@ -729,7 +729,7 @@ def deferred_oracle(w, K, gpu, chunks=8):
                          "status quo (1 row)"}
     # CPU baseline: the deferred step (K accumulates, then the reduce) on a
     # sample of the columns, inputs generated first
-    ns = 1 << 26
+    ns = 1 << 27
     xs = [OC.host_rows(1, w.value_seed, 0, w.scale, W, 0, ns, stream_of=lambda r, k=k: so(k, r))
           for k in range(K)]
     xs = [np.ascontiguousarray(x[:, :ns]) for x in xs]
