@@ -724,16 +724,20 @@ dc_status dc_plan_relayout_tiles(int32_t dtype, int64_t bucket_col, int64_t buck
   if (tiles == nullptr) return ok();  // size query
   if (tiles_capacity < n)
     return fail(DC_ERR_SHAPE, "tiles_capacity=%lld < %lld tiles", (long long)tiles_capacity, (long long)n);
-  // one sweep over the tiles in destination order beside the pieces: a tile
-  // copies straight from one piece when its whole destination run lies in
-  // the piece and its source run starts on a vector and stays in the bucket
+  // one sweep over the tiles in destination order beside the pieces.  A
+  // destination column belongs to the last piece starting at or before it
+  // (as in the searched relayout); a tile copies straight from piece k when
+  // all its columns belong to k -- k covers the tile and no later piece
+  // starts inside it -- and its source run starts on a vector and stays in
+  // the bucket
   const int64_t E = 16 / elem_bytes(dtype), span = dc::kRelayoutTile * E;
   int32_t k = 0;
   for (int64_t t = 0; t < n; ++t) {
     const int64_t d0 = t * span, d1 = d0 + span;
     while (k + 1 < num_pieces && pieces[k + 1].dst <= d0) ++k;
     int64_t rec = -1;
-    if (num_pieces > 0 && d1 <= out_numel && pieces[k].dst <= d0 && d1 <= pieces[k].dst + pieces[k].len) {
+    if (num_pieces > 0 && d1 <= out_numel && pieces[k].dst <= d0 && d1 <= pieces[k].dst + pieces[k].len &&
+        (k + 1 == num_pieces || pieces[k + 1].dst >= d1)) {
       const int64_t src0 = pieces[k].src + (d0 - pieces[k].dst);
       if (src0 >= 0 && src0 + span <= bucket_numel && (bucket_col + src0) % E == 0) rec = (bucket_col + src0) / E;
     }

@@ -501,8 +501,10 @@ dc_status dc_relayout_bucket(int32_t W, int32_t dtype, const void* slab_in, int6
  * ahead of it).  The relaid bucket's columns [0, out_numel) fall into tiles
  * of 64 16-byte vectors (512 bf16 or 256 fp32 columns); one int64 per
  * tile, in an order private to the library, records where a tile copies
- * from when the whole tile lies inside one piece whose source run starts
- * on a 16-byte vector of the slab and stays in the bucket.  Host only.
+ * from when all of its columns belong to one piece (a column belongs to the
+ * last piece whose dst is at or before it, if that piece reaches it) and
+ * the piece's source run for the tile starts on a 16-byte vector of the
+ * slab and stays in the bucket.  Host only.
  *   dtype, bucket_col, bucket_numel, pieces, num_pieces, out_numel
  *                    as for dc_relayout_bucket (pieces on the host, sorted
  *                    by dst as dc_plan_relayout writes them)

@@ -612,11 +612,17 @@ def _brute_relayout_tiles(dtype, bucket_col, bucket_numel, pieces, out_numel):
     E = 8 if dtype == wl.DT_BF16 else 4
     span = 64 * E
     n = -(-(-(-out_numel // E)) // 64)
+    # a column belongs to the last piece starting at or before it, if that
+    # piece reaches it
+    cols = np.arange(n * span)
+    dst = pieces["dst"].astype(np.int64)
+    last = np.searchsorted(dst, cols, side="right") - 1
     pid = np.full(n * span, -1, np.int64)
-    for k, pc in enumerate(pieces):
-        lo, hi = max(int(pc["dst"]), 0), min(int(pc["dst"]) + int(pc["len"]), n * span)
-        if hi > lo:
-            pid[lo:hi] = k
+    has = last >= 0
+    ends = dst + pieces["len"].astype(np.int64)
+    inside = np.zeros(n * span, bool)
+    inside[has] = cols[has] < ends[last[has]]
+    pid[inside] = last[inside]
     recs = np.full(n, -1, np.int64)
     for t in range(n):
         d0 = t * span
@@ -654,16 +660,17 @@ def test_plan_relayout_tiles_matches_definition():
             pieces, seg = dc.dc_plan_relayout(w.W, t, len(t), flat, psize, w.P)
             for shift in (0, 1, 8):
                 cases.append((w.dtype, bk.col + shift, bk.numel, pieces, int(seg[-1])))
-    for k in range(40):
+    for k in range(60):
         dt = rng.choice([wl.DT_BF16, wl.DT_F32])
         numel = rng.randint(0, 20_000)
         dst, pcs = 0, []
+        overlap = k >= 40          # later pieces may start inside earlier ones
         for _ in range(rng.randint(0, 12)):
             dst += rng.choice([0, 0, 1, 8, 300])
             ln = rng.choice([0, 5, 512, 1024, 3000])
             src = rng.randint(-4, numel) if rng.random() < 0.2 else rng.choice([0, 8, 512, 1000])
             pcs.append((src, dst, ln, 0))
-            dst += ln
+            dst += rng.choice([0, 100, ln // 2]) if overlap else ln
         pieces = np.array(pcs, dc.PIECE_DTYPE) if pcs else np.zeros(0, dc.PIECE_DTYPE)
         cases.append((dt, rng.choice([0, 3, 64, 4096]), numel, pieces, dst + rng.choice([0, 7, 600])))
     whole = 0

@@ -223,3 +223,51 @@ def test_reduce_scatter_v_all_residues():
         hs[:] = U.SENTINEL16
         oracle.reduce_scatter_v(W, dtype, hx, hs, seg, pre)
         assert np.array_equal(U.to_host(sh, dtype), hs), pre
+
+
+def test_relayout_planned_equals_searched_random_pieces():
+    """dc_relayout_bucket_planned against dc_relayout_bucket on random piece
+    tables (gaps, empty pieces, unaligned sources, and pieces that start
+    inside earlier ones, where a column belongs to the last piece starting at
+    or before it): the same output, bit for bit, sentinel where no piece
+    writes."""
+    import torch
+    rng = random.Random(31)
+    whole = 0
+    for case in range(24):
+        W = rng.choice([2, 4, 8, 16, 5])
+        dtype = rng.choice([wl.DT_BF16, wl.DT_F32])
+        numel = rng.randint(1, 30_000)
+        col = rng.choice([0, 8, 64, 3, 1024])
+        overlap = case % 2 == 1
+        dst, pcs = 0, []
+        for _ in range(rng.randint(1, 14)):
+            dst += rng.choice([0, 0, 1, 8, 300])
+            ln = rng.choice([0, 5, 512, 1024, 3000, 7000])
+            src = rng.choice([0, 8, 512, 1000, rng.randint(0, numel)])
+            ln = max(0, min(ln, numel - src))
+            pcs.append((src, dst, ln, 0))
+            dst += rng.choice([0, 100, ln // 2]) if overlap else ln
+        pieces = np.array(pcs, dc.PIECE_DTYPE)
+        out_numel = dst + rng.choice([0, 7, 600])
+        ld_in = wl.round_up(col + numel, 64)
+        ld_out = max(64, wl.round_up(out_numel, 64))
+        U.say("relayout planned vs searched", case, W, wl.DTYPE_NAME[dtype], numel, len(pcs), out_numel)
+        x = U.gen_slab(dtype, W, ld_in, ld_in, 50 + case, 0, wl.sigma_scale(0.01))
+        d_pieces = torch.from_numpy(pieces.view(np.uint8).copy()).cuda()
+        tiles = dc.dc_plan_relayout_tiles(dtype, col, numel, pieces, len(pieces), out_numel)
+        d_tiles = torch.from_numpy(tiles).cuda() if len(tiles) else None
+        outs = []
+        for planned in (False, True):
+            y = U.empty_slab(dtype, W, ld_out)
+            if planned:
+                dc.dc_relayout_bucket_planned(W, dtype, x, ld_in, y, ld_out, col, numel, d_pieces,
+                                              len(pieces), out_numel, d_tiles, len(tiles))
+            else:
+                dc.dc_relayout_bucket(W, dtype, x, ld_in, y, ld_out, col, numel, d_pieces, len(pieces),
+                                      out_numel)
+            outs.append(y)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1]), case
+        whole += int((tiles >= 0).sum())
+    assert whole > 20          # the straight copy ran, not only the search
