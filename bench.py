@@ -254,8 +254,9 @@ def stream_rows_gbs(src, src_ld_vec, rows_read, dst, dst_ld_vec, rows_written, n
 # one vector per thread, and (runs of 64 vectors per workgroup, workgroups
 # per compute unit) covering the shapes the library's streaming kernels
 # launch with.  The reference for a mix is the best of them.
-REFERENCE_SHAPES = [None, (1, 0), (1, 3), (1, 4), (1, 5), (1, 6), (1, 8), (1, 10), (1, 12),
-                    (2, 6), (2, 8), (2, 10), (2, 12), (4, 5), (4, 6), (4, 7), (4, 8)]
+REFERENCE_SHAPES = [None, (1, 0), (1, 3), (1, 4), (1, 5), (1, 6), (1, 7), (1, 8), (1, 9), (1, 10),
+                    (1, 12), (1, 14), (2, 6), (2, 8), (2, 10), (2, 12), (4, 5), (4, 6), (4, 7),
+                    (4, 8)]
 
 
 def shape_name(sh):
