@@ -681,10 +681,12 @@ dc_status dc_plan_relayout(int32_t W, const dc_task* tasks, int32_t num_tasks,
   return ok();
 }
 
-dc_status dc_relayout_bucket(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
-                             void* out, int64_t ld_out, int64_t bucket_col, int64_t bucket_numel,
-                             const dc_piece* pieces, int32_t num_pieces, int64_t out_numel,
-                             void* stream) {
+// Checks and launch shared by the searched and the planned relayout
+// (tiles == nullptr: searched).
+static dc_status relayout_common(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in, void* out,
+                                 int64_t ld_out, int64_t bucket_col, int64_t bucket_numel,
+                                 const dc_piece* pieces, int32_t num_pieces, int64_t out_numel,
+                                 const int64_t* tiles, void* stream) {
   dc_status st;
   if ((st = check_w(W)) || (st = check_dtype(dtype))) return st;
   if (bucket_col < 0 || bucket_numel < 0 || out_numel < 0 || num_pieces < 0)
@@ -698,9 +700,17 @@ dc_status dc_relayout_bucket(int32_t W, int32_t dtype, const void* slab_in, int6
   const int64_t b = elem_bytes(dtype);
   if (overlaps(slab_in, W * ld_in * b, out, W * ld_out * b)) return fail(DC_ERR_ARG, "slab_in and out overlap");
   return hip_status(dc::launch_relayout(W, dtype, slab_in, ld_in, out, ld_out, bucket_col, bucket_numel,
-                                        pieces, num_pieces, out_numel, nullptr,
+                                        pieces, num_pieces, out_numel, tiles,
                                         static_cast<hipStream_t>(stream)),
-                    "relayout launch");
+                    tiles != nullptr ? "planned relayout launch" : "relayout launch");
+}
+
+dc_status dc_relayout_bucket(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
+                             void* out, int64_t ld_out, int64_t bucket_col, int64_t bucket_numel,
+                             const dc_piece* pieces, int32_t num_pieces, int64_t out_numel,
+                             void* stream) {
+  return relayout_common(W, dtype, slab_in, ld_in, out, ld_out, bucket_col, bucket_numel, pieces,
+                         num_pieces, out_numel, nullptr, stream);
 }
 
 dc_status dc_plan_relayout_tiles(int32_t dtype, int64_t bucket_col, int64_t bucket_numel,
@@ -751,15 +761,7 @@ dc_status dc_relayout_bucket_planned(int32_t W, int32_t dtype, const void* slab_
                                      const dc_piece* pieces, int32_t num_pieces, int64_t out_numel,
                                      const int64_t* tiles, int64_t num_tiles, void* stream) {
   dc_status st;
-  if ((st = check_w(W)) || (st = check_dtype(dtype))) return st;
-  if (bucket_col < 0 || bucket_numel < 0 || out_numel < 0 || num_pieces < 0)
-    return fail(DC_ERR_ARG, "negative bucket_col, bucket_numel, out_numel or num_pieces");
-  if ((st = check_extent("bucket_col", bucket_col)) || (st = check_extent("bucket_numel", bucket_numel)))
-    return st;
-  if ((st = check_slab("slab_in", slab_in, ld_in, bucket_col + bucket_numel, dtype)) ||
-      (st = check_slab("out", out, ld_out, out_numel, dtype)))
-    return st;
-  if (num_pieces > 0 && pieces == nullptr) return fail(DC_ERR_NULL, "pieces is NULL");
+  if ((st = check_dtype(dtype))) return st;
   if (out_numel > 0 && num_pieces > 0) {
     const int64_t n = dc::relayout_tile_count(dtype, out_numel);
     if (num_tiles != n)
@@ -767,12 +769,8 @@ dc_status dc_relayout_bucket_planned(int32_t W, int32_t dtype, const void* slab_
                   (long long)out_numel, (long long)n);
     if (tiles == nullptr) return fail(DC_ERR_NULL, "tiles is NULL");
   }
-  const int64_t b = elem_bytes(dtype);
-  if (overlaps(slab_in, W * ld_in * b, out, W * ld_out * b)) return fail(DC_ERR_ARG, "slab_in and out overlap");
-  return hip_status(dc::launch_relayout(W, dtype, slab_in, ld_in, out, ld_out, bucket_col, bucket_numel,
-                                        pieces, num_pieces, out_numel, tiles,
-                                        static_cast<hipStream_t>(stream)),
-                    "planned relayout launch");
+  return relayout_common(W, dtype, slab_in, ld_in, out, ld_out, bucket_col, bucket_numel, pieces,
+                         num_pieces, out_numel, tiles, stream);
 }
 
 dc_status dc_reduce_scatter_v(int32_t W, int32_t dtype, const void* in, int64_t ld_in, void* out,
