@@ -36,6 +36,17 @@ static_assert(kBufU * kBT == kBufTile, "a tile is whole slots per thread");
                                     // that one-wave workgroups are not LDS bound
 #endif
 constexpr int kPtrStage = DC_BUF_PTRS;
+// Result stores of whole planned tiles at W <= 8 and at W = 16: nontemporal
+// global stores (-1), or buffer stores over the tile's run with these
+// cache-policy bits.  Interleaved A/B: sc0 sc1 nt and nt sc1 +0.9% at W = 8
+// bf16 (6.33 against 6.27 TB/s); at W = 16 fp32 1.2% slower in the faster of
+// the runs' two placement modes, equal in the other.
+#ifndef DC_BUF_SP8
+#define DC_BUF_SP8 19
+#endif
+#ifndef DC_BUF_SP16
+#define DC_BUF_SP16 -1
+#endif
 
 struct BufParams {
   const dc_task* tasks;
@@ -123,9 +134,20 @@ __global__ __launch_bounds__(kBT) void k_flush_buffers(BufParams p) {
 #pragma unroll
             for (int r = 0; r < WT; ++r) fold16<BF16, PRE>(acc, x[r], r == 0, inv, cf);
             const u32x4 y = pack16<BF16>(acc);
+            constexpr int SP = WT <= 8 ? DC_BUF_SP8 : DC_BUF_SP16;
+            if constexpr (SP >= 0) {
+              // the tile's run of each output buffer, from the tile's first slot
+              const int64_t tb = (t0 * E - t.offset) * EB;
+              const int32_t rb = (int32_t)((t1 - t0) * 16), off = (int32_t)(byte - tb);
 #pragma unroll
-            for (int r = 0; r < WT; ++r)
-              if (out[r] != nullptr) store16<true>(reinterpret_cast<u32x4*>(out[r] + byte), y);
+              for (int r = 0; r < WT; ++r)
+                if (out[r] != nullptr)
+                  store_buf<(SP >= 0 ? SP : 0)>(reinterpret_cast<u32x4*>(out[r] + tb), rb, off, y);
+            } else {
+#pragma unroll
+              for (int r = 0; r < WT; ++r)
+                if (out[r] != nullptr) store16<true>(reinterpret_cast<u32x4*>(out[r] + byte), y);
+            }
           }
           return;
         }
