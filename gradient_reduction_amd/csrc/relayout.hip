@@ -169,10 +169,13 @@ __global__ __launch_bounds__(kRT) void k_relayout_planned(RelayoutParams p) {
   const int64_t t0 = (int64_t)blockIdx.x * kRelayoutTile;
   const int64_t t1 = min(t0 + kRelayoutTile, nvec);
   if constexpr (WT > 0) {
+    // the record's source run must lie in the bucket: vectors
+    // [ceil(bucket_col / E), floor(bucket end / E) - kRelayoutTile], checked
+    // without multiplying the record (any int64 is safe)
     const int64_t rec = p.tiles[tile_slot((int64_t)blockIdx.x, (int64_t)gridDim.x)];
-    const int64_t c0 = rec * E;
-    if (rec >= 0 && t1 * E <= p.out_numel && t1 - t0 == kRelayoutTile && c0 >= p.bucket_col &&
-        c0 + kRelayoutTile * E <= p.bucket_col + p.bucket_numel) {
+    const int64_t rec_lo = (p.bucket_col + E - 1) / E;
+    const int64_t rec_hi = (p.bucket_col + p.bucket_numel) / E - kRelayoutTile;
+    if (rec >= rec_lo && rec <= rec_hi && t1 * E <= p.out_numel && t1 - t0 == kRelayoutTile) {
       const u32x4* src = reinterpret_cast<const u32x4*>(p.in) + rec + threadIdx.x;
       u32x4 x[WT];
 #pragma unroll

@@ -67,7 +67,11 @@ CASES = [
 NUMEL = [0, 1, 7, 8, 9, 64, 1000, 4099, 5000, 3, 8197, 16]
 
 
-def run_case(W, dtype, pre, comms, numel, seed, aligned, padded, inplace, planned=False):
+def run_case(W, dtype, pre, comms, numel, seed, aligned, padded, inplace, planned=False,
+             stale=False):
+    """stale: plan with random records instead of the planner's; then only
+    the contract is checked: nothing outside the holders' buffers is written
+    and the inputs are unchanged."""
     import torch
     rng = random.Random(seed)
     n = len(numel)
@@ -118,12 +122,28 @@ def run_case(W, dtype, pre, comms, numel, seed, aligned, padded, inplace, planne
           "padded" if padded else "packed", "in place" if inplace else "", "planned" if planned else "")
     if planned:
         tiles = dc.dc_plan_flush_buffers(W, dtype, extent, tasks, n, comms, len(comms))
+        if stale:
+            tiles["first"] = [rng.randint(-3, n + 3) for _ in range(len(tiles))]
+            tiles["last"] = [rng.randint(-3, n + 3) for _ in range(len(tiles))]
+            tiles["root"] = [rng.randint(-3, W + 3) for _ in range(len(tiles))]
+            tiles["flags"] = [rng.randint(0, 1) | (rng.randint(0, 4) << 8) for _ in range(len(tiles))]
         d_tiles = torch.from_numpy(tiles.view(np.uint8).copy()).cuda() if len(tiles) else None
         dc.dc_flush_bucket_buffers_planned(W, dtype, extent, d_tasks, n, p_in, p_out, comms, len(comms),
                                            pre, d_tiles, len(tiles))
     else:
         dc.dc_flush_bucket_buffers(W, dtype, extent, d_tasks, n, p_in, p_out, comms, len(comms), pre)
     torch.cuda.synchronize()
+    if stale:
+        got = U.bits(U.to_host(d_out, dtype)[0], dtype)
+        legit = np.zeros(len(got), bool)
+        for t in range(n):
+            for r in range(W):
+                if out_off[t, r] >= 0:
+                    legit[out_off[t, r]:out_off[t, r] + numel[t]] = True
+        sent = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
+        assert np.all(got[~legit] == sent), "a stale plan wrote outside the holders' buffers"
+        assert np.array_equal(U.bits(U.to_host(d_in, dtype)[0], dtype), U.bits(h_in, dtype))
+        return
     oracle.flush_buffers(W, dtype, h_in, in_off, h_out, out_off, numel, t_comm, cs, cst, pre)
     got = U.to_host(d_out, dtype)[0]
     assert np.array_equal(U.bits(got, dtype), U.bits(h_out, dtype))
@@ -141,6 +161,16 @@ def test_flush_buffers_small(W, dtype, pre, comms, aligned, padded, planned):
 @pytest.mark.parametrize("planned", [False, True], ids=["searched", "planned"])
 def test_flush_buffers_in_place(W, dtype, pre, comms, planned):
     run_case(W, dtype, pre, comms, NUMEL, 200 + W, True, True, inplace=True, planned=planned)
+
+
+@pytest.mark.parametrize("W,dtype,pre,comms", CASES, ids=lambda v: str(v))
+def test_flush_buffers_stale_plan_stays_in_buffers(W, dtype, pre, comms):
+    """A plan of random records (the kernel reads the plan without checking
+    it on the host): sums may be wrong, but nothing outside the holders'
+    grad buffers is written and the inputs are left as they were."""
+    for aligned, padded in ((True, True), (False, True)):
+        run_case(W, dtype, pre, comms, NUMEL, 300 + W, aligned, padded, inplace=False, planned=True,
+                 stale=True)
 
 
 def test_flush_buffers_many_tiny_tasks():

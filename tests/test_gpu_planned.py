@@ -175,3 +175,49 @@ def test_planned_flush_w8_402m_full_size(mode):
     """Sampled columns of the full-size planned flush against the oracle."""
     F.full_size_flush(wl.owner_flush_w8(), mode == "owner", in_place=False, zero2=mode == "zero2",
                       planned=True)
+
+
+def test_planned_flush_stale_plan_stays_in_slabs():
+    """The plan is device data that the kernel reads without a host check: a
+    plan of random records (task ranges, roots, flags and communicators out
+    of range included) can give wrong sums, but every write stays in the
+    columns of the bucket's tile grid and the input slab is left as it was.
+    Buckets sit behind a guard of columns on both sides to show it."""
+    import torch
+    rng = random.Random(77)
+    for w in F.small_flush_workloads()[::3] + [wl.tiny_flush()]:
+        E = 8 if w.dtype == wl.DT_BF16 else 4
+        G = 64 * E * 4
+        ld = wl.round_up(w.total + 2 * G, 64 * E)
+        x = U.gen_slab(w.dtype, w.W, ld, ld, w.value_seed, 0, w.scale)
+        hx = U.bits(U.to_host(x, w.dtype), w.dtype).copy()
+        y = U.empty_slab(w.dtype, w.W, ld)
+        ex = executor.from_workload(w, reduce_to_owner=True)
+        ex.build_owner_map()
+        ex.fetch_metadata()
+        span = np.zeros(ld, bool)
+        U.say("stale plan", w.name)
+        for b, bk in enumerate(w.buckets):
+            t = ex.h_tasks[b]
+            c0 = G + bk.col
+            tiles, _ = dc.dc_plan_flush(w.W, w.dtype, c0, bk.numel, t, len(t), ex.h_owner, None, None,
+                                        w.P, ex.comms, len(ex.comms))
+            n = len(tiles)
+            if n == 0:
+                continue
+            tiles["first"] = [rng.randint(-3, len(t) + 3) for _ in range(n)]
+            tiles["last"] = [rng.randint(-3, len(t) + 3) for _ in range(n)]
+            tiles["root"] = [rng.randint(-3, w.W + 3) for _ in range(n)]
+            tiles["flags"] = [rng.randint(0, 1) | (rng.randint(0, len(ex.comms) + 2) << 8)
+                              for _ in range(n)]
+            d_tiles = torch.from_numpy(tiles.view(np.uint8).copy()).cuda()
+            dc.dc_flush_bucket_planned(w.W, w.dtype, x, ld, y, ld, c0, bk.numel, ex.task_table(b),
+                                       len(t), ex.d_owner, None, None, w.P, ex.comms, len(ex.comms),
+                                       w.pre_div, d_tiles, n, rng.randint(0, n))
+            v0 = (c0 // E) // 64 * 64
+            span[v0 * E:-(-(c0 + bk.numel) // E) * E] = True
+        torch.cuda.synchronize()
+        got = U.bits(U.to_host(y, w.dtype), w.dtype)
+        sent = U.SENTINEL16 if w.dtype == wl.DT_BF16 else U.SENTINEL32
+        assert np.all(got[:, ~span] == sent), f"{w.name}: a write left the buckets' tile grid"
+        assert np.array_equal(U.bits(U.to_host(x, w.dtype), w.dtype), hx), f"{w.name}: input changed"

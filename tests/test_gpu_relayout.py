@@ -271,3 +271,47 @@ def test_relayout_planned_equals_searched_random_pieces():
         assert torch.equal(outs[0], outs[1]), case
         whole += int((tiles >= 0).sum())
     assert whole > 20          # the straight copy ran, not only the search
+
+
+def test_relayout_stale_plan_stays_in_bounds():
+    """A tile plan of random records (negative, huge, near the bucket's ends,
+    other tiles' sources): the planned relayout may misplace data inside
+    [0, out_numel) but writes nothing past it and leaves the input alone."""
+    import torch
+    rng = random.Random(5)
+    for case in range(12):
+        W = [1, 2, 4, 8, 16, 3][case % 6]
+        dtype = rng.choice([wl.DT_BF16, wl.DT_F32])
+        E = 8 if dtype == wl.DT_BF16 else 4
+        numel = rng.randint(2000, 30_000)
+        col = rng.choice([0, 8, 64, 3])
+        dst, pcs = 0, []
+        for _ in range(rng.randint(1, 10)):
+            ln = rng.choice([512, 1024, 3000, 7000])
+            src = rng.choice([0, 8, 512, rng.randint(0, numel)])
+            ln = max(0, min(ln, numel - src))
+            pcs.append((src, dst, ln, 0))
+            dst += ln
+        pieces = np.array(pcs, dc.PIECE_DTYPE)
+        out_numel = dst
+        tiles = dc.dc_plan_relayout_tiles(dtype, col, numel, pieces, len(pieces), out_numel)
+        if len(tiles) == 0:
+            continue
+        hi = (col + numel) // E
+        pool = [-1, -(2 ** 62), 2 ** 62, 2 ** 61 + 3, hi, hi - 64, hi - 63, col // E, 0]
+        tiles = np.array([rng.choice(pool + [int(v) for v in tiles] + [rng.randint(0, hi + 100)])
+                          for _ in range(len(tiles))], np.int64)
+        ld_in = wl.round_up(col + numel, 64)
+        ld_out = wl.round_up(out_numel + 1024, 64)
+        U.say("relayout stale plan", case, W, wl.DTYPE_NAME[dtype], numel, out_numel)
+        x = U.gen_slab(dtype, W, ld_in, ld_in, 70 + case, 0, wl.sigma_scale(0.01))
+        hx = U.bits(U.to_host(x, dtype), dtype).copy()
+        y = U.empty_slab(dtype, W, ld_out)
+        d_pieces = torch.from_numpy(pieces.view(np.uint8).copy()).cuda()
+        dc.dc_relayout_bucket_planned(W, dtype, x, ld_in, y, ld_out, col, numel, d_pieces, len(pieces),
+                                      out_numel, torch.from_numpy(tiles).cuda(), len(tiles))
+        torch.cuda.synchronize()
+        got = U.bits(U.to_host(y, dtype), dtype)
+        sent = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
+        assert np.all(got[:, out_numel:] == sent), case
+        assert np.array_equal(U.bits(U.to_host(x, dtype), dtype), hx), case
