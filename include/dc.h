@@ -318,8 +318,9 @@ dc_status dc_plan_flush(int32_t W, int32_t dtype, int64_t bucket_col, int64_t bu
  *                      every row, and any value gives the same results
  * Other arguments and checks as in dc_flush_bucket.  The plan is read on
  * the device and not checked: a stale or altered plan can give wrong sums,
- * and write columns of slab_out's rows outside the bucket, but never makes
- * the kernel touch memory outside the two slabs' W rows of ld columns (task
+ * and write columns of slab_out's rows outside the bucket but inside its
+ * tile grid (the 64-vector tiles that cover the bucket), but never makes the
+ * kernel touch memory outside the two slabs' W rows of ld columns (task
  * indices, roots and communicators are clamped to their ranges). */
 dc_status dc_flush_bucket_planned(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,
                                   void* slab_out, int64_t ld_out, int64_t bucket_col,
