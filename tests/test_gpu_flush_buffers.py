@@ -63,6 +63,8 @@ CASES = [
     (3, wl.DT_BF16, 1, [(3, 1)]),
     (2, wl.DT_BF16, 1, [(2, 1)]),
     (1, wl.DT_F32, 1, [(1, 1)]),
+    (32, wl.DT_BF16, 1, [(32, 1), (8, 4)]),
+    (64, wl.DT_F32, 0, [(64, 1), (16, 1)]),
 ]
 NUMEL = [0, 1, 7, 8, 9, 64, 1000, 4099, 5000, 3, 8197, 16]
 

@@ -234,8 +234,8 @@ def test_relayout_planned_equals_searched_random_pieces():
     import torch
     rng = random.Random(31)
     whole = 0
-    for case in range(28):
-        W = [1, 3, 2, 4, 8, 16, 5][case % 7]
+    for case in range(36):
+        W = [1, 3, 2, 4, 8, 16, 5, 32, 64][case % 9]
         dtype = rng.choice([wl.DT_BF16, wl.DT_F32])
         numel = rng.randint(1, 30_000)
         col = rng.choice([0, 8, 64, 3, 1024])
