@@ -338,6 +338,7 @@ TRAFFIC_PROFILES = {
     "relayout_rs_w8": ("relayout_rs_w8_402m", "slab_ops.hip"),
     "deferred": ("deferred_qwen3_k8", "slab_ops.hip"),
     "deferred_fused": ("deferred_qwen3_k8_fused", "slab_ops.hip"),
+    "deferred_accumulate": ("deferred_qwen3_k8_accumulate", "slab_ops.hip"),
     "rs_ag": ("rs_ag_w8_202m", "slab_ops.hip"),
     "rs_ag_allgather": ("allgather_w8_202m", "slab_ops.hip"),
     "schedules_w8": ("schedules_w8_202m", "slab_ops.hip"),
@@ -834,9 +835,16 @@ def bench_deferred(args, K, check=True):
                 W, a_t, ld, o_t, ld, M, W), 1)
         red_gbs = red_b / (red_ms / 1e3) / 1e9
         acc_gbs = sum(acc_b) / (kern[:-1].sum() / 1e3) / 1e9 if n_acc else 0.0
+        # the accumulates alone, back to back (each round starts from init,
+        # so repeating them recomputes the same accumulators)
+        acc_ms = region_launch_ms(torch, args, lambda: [
+            dc.dc_accumulate(W, xs[k], ld, a_t, ld, M, 1 if k == 0 else 0) for k in range(n_acc)],
+            n_acc) if n_acc else 0.0
+        acc_region_gbs = sum(acc_b) / (acc_ms * n_acc / 1e3) / 1e9 if n_acc else 0.0
         name = "k_accum_reduce" if fused else "k_deferred"
         log(f"[bench] deferred K={K}{' fused' if fused else ''}: step {ms_step:.3f} ms; accumulate "
-            f"{acc_gbs:.1f} GB/s; {name} {red_gbs:.1f} GB/s ({red_ms:.3f} ms back to back, "
+            f"{acc_region_gbs:.1f} GB/s back to back ({acc_gbs:.1f} with events); {name} {red_gbs:.1f} GB/s "
+            f"({red_ms:.3f} ms back to back, "
             f"{kern[-1]:.3f} ms with events)")
         roofline = {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(red_gbs / HBM_PEAK_GBS, 4),
@@ -848,9 +856,19 @@ def bench_deferred(args, K, check=True):
         if not fused:
             add_mix_reference(roofline, best_reference(acc, ld // 4, W, out_f, ld // 4, W, M // 4),
                               f"read {W} rows, write {W}")
+        accumulate = {"kernel": "k_accumulate", "bound": "hbm", "achieved": round(acc_region_gbs, 1),
+                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(acc_region_gbs / HBM_PEAK_GBS, 4),
+                      "launch_ms_avg": round(acc_ms, 4), "timing": REGION_TIMING,
+                      "per_launch_events": per_launch_events(acc_gbs, float(kern[:-1].mean()) if n_acc else 0.0),
+                      "bytes_per_launch": [int(b) for b in acc_b],
+                      "traffic": None if fused else traffic_from_profile("deferred_accumulate", w.name,
+                                                                         {"ga": K}),
+                      "what": "the step's accumulates (most of its time), timed back to back"}
         res["fused" if fused else "unfused"] = {
             "ms_per_step": round(ms_step, 4), "value": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
-            "step_bytes": int(step_bytes), "accumulate_gbs": round(acc_gbs, 1), "roofline": roofline,
+            "step_bytes": int(step_bytes), "accumulate_gbs": round(acc_region_gbs, 1),
+            "accumulate": accumulate, "roofline": roofline,
             "step": ("K-1 accumulates + fused accumulate-reduce" if fused
                      else "K accumulates + deferred reduce")}
     # both steps once more, so the outputs hold exactly one step's results
