@@ -336,6 +336,7 @@ TRAFFIC_PROFILES = {
     "fused_w8": ("flush_buffers_w8_402m", "flush_buffers.hip"),
     "fused_mixed": ("flush_buffers_w16_1200m", "flush_buffers.hip"),
     "relayout_rs_w8": ("relayout_rs_w8_402m", "slab_ops.hip"),
+    "relayout_rs_relayout": ("relayout_w8_402m", "relayout.hip"),
     "deferred": ("deferred_qwen3_k8", "slab_ops.hip"),
     "deferred_fused": ("deferred_qwen3_k8_fused", "slab_ops.hip"),
     "deferred_accumulate": ("deferred_qwen3_k8_accumulate", "slab_ops.hip"),
@@ -1019,6 +1020,14 @@ def bench_rs_ag(args):
              "all_gather_ring_frac": round(gbs[2] / HBM_PEAK_GBS, 4),
              "all_gather_launch_ms": {"rank": round(reg[1], 4), "ring": round(reg[2], 4)},
              "all_gather_traffic": traffic_from_profile("rs_ag_allgather", w.name),
+             "all_gather_roofline": {
+                 "kernel": "k_ag_vec", "bound": "hbm",
+                 "achieved": round(2 * ag_b / ((reg[1] + reg[2]) / 1e3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": round(2 * ag_b / ((reg[1] + reg[2]) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "launch_ms_avg": round((reg[1] + reg[2]) / 2, 4), "timing": REGION_TIMING,
+                 "bytes_per_launch": [ag_b, ag_b],
+                 "traffic": traffic_from_profile("rs_ag_allgather", w.name),
+                 "what": "the two all-gathers (rank and ring order), the step's larger share of time"},
              "all_gather_gbs_with_events": {"rank": round(ev[1], 1), "ring": round(ev[2], 1)}}
     step()
     torch.cuda.synchronize()
@@ -1224,9 +1233,23 @@ def bench_relayout_rs(args):
 
     rs_ms = region_launch_ms(torch, args, rs_only, 1)
     rs_gbs = sum(rs_b) / (rs_ms / 1e3) / 1e9
-    log(f"[bench] relayout + reduce-scatter-v: step {ms_step:.3f} ms; relayout {rl_gbs:.1f} GB/s "
-        f"({kern[0::2].sum():.3f} ms); reduce-scatter-v {rs_gbs:.1f} GB/s back to back ({rs_ms:.3f} ms), "
-        f"{ev_rs_gbs:.1f} GB/s with events ({kern[1::2].sum():.3f} ms)")
+
+    def rl_only():
+        for k, bk in enumerate(w.buckets):
+            d_pieces, npc, seg, d_tiles, ntiles = plans[k]
+            if args.searched:
+                dc.dc_relayout_bucket(W, 0, x, ld, relaid, ld_r, bk.col, bk.numel, d_pieces, npc,
+                                      int(seg[-1]))
+            else:
+                dc.dc_relayout_bucket_planned(W, 0, x, ld, relaid, ld_r, bk.col, bk.numel, d_pieces,
+                                              npc, int(seg[-1]), d_tiles, ntiles)
+
+    ev_rl_gbs = rl_gbs
+    rl_ms = region_launch_ms(torch, args, rl_only, 1)
+    rl_gbs = sum(rl_b) / (rl_ms / 1e3) / 1e9
+    log(f"[bench] relayout + reduce-scatter-v: step {ms_step:.3f} ms; relayout {rl_gbs:.1f} GB/s back to "
+        f"back ({rl_ms:.3f} ms), {ev_rl_gbs:.1f} with events; reduce-scatter-v {rs_gbs:.1f} GB/s back to "
+        f"back ({rs_ms:.3f} ms), {ev_rs_gbs:.1f} GB/s with events ({kern[1::2].sum():.3f} ms)")
     roofline = {"bound": "hbm", "achieved": round(rs_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(rs_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile("relayout_rs_w8", w.name), "kernel": "k_rs_v",
@@ -1236,8 +1259,17 @@ def bench_relayout_rs(args):
                 "bytes_per_launch": [int(b) for b in rs_b]}
     extra = {"relayout": ("searched: each tile looks up its pieces" if args.searched else
                           "planned: per-bucket tile plans built once on the host"),
-             "relayout_gbs": round(rl_gbs, 1), "relayout_ms": round(float(kern[0::2].sum()), 4),
-             "reduce_scatter_v_ms": round(float(kern[1::2].sum()), 4)}
+             "relayout_gbs": round(rl_gbs, 1), "relayout_ms": round(rl_ms, 4),
+             "reduce_scatter_v_ms": round(rs_ms, 4),
+             "relayout_roofline": {
+                 "kernel": "k_relayout" if args.searched else "k_relayout_planned", "bound": "hbm",
+                 "achieved": round(rl_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(rl_gbs / HBM_PEAK_GBS, 4), "launch_ms_avg": round(rl_ms / nb, 4),
+                 "timing": REGION_TIMING,
+                 "per_launch_events": per_launch_events(ev_rl_gbs, float(kern[0::2].mean())),
+                 "bytes_per_launch": [int(b) for b in rl_b],
+                 "traffic": None if args.searched else traffic_from_profile("relayout_rs_relayout", w.name),
+                 "what": "the relayouts, the step's larger share of time, timed back to back"}}
     # references at the largest relaid bucket: reduce-scatter-v reads W rows and
     # writes one row's worth; the relayout reads and writes all W rows (the
     # input slab is not used after the timed steps)
