@@ -269,6 +269,8 @@ def best_reference(src, src_ld_vec, rows_read, dst, dst_ld_vec, rows_written, nv
     """(best GB/s, its shape) of the access-mix reference over REFERENCE_SHAPES."""
     best, shape = 0.0, None
     for sh in REFERENCE_SHAPES:
+        if sh is None and rows_read == 1:
+            continue          # one row read to many: shaped launches only
         g = stream_rows_gbs(src, src_ld_vec, rows_read, dst, dst_ld_vec, rows_written, nvec, sh)
         if g > best:
             best, shape = g, sh
@@ -1014,6 +1016,9 @@ def bench_rs_ag(args):
     tmp = torch.empty((W, w.ld), dtype=torch.int16, device=dev)
     add_mix_reference(roofline, best_reference(x, w.ld // 8, W, tmp, w.ld // 8, 1, M // 8),
                       f"read {W} rows, write 1")
+    # the all-gather's mix: one row of M read, all W rows of M written (the
+    # outputs are recomputed by the step below)
+    ag_ref, ag_shape = best_reference(x, w.ld // 8, 1, tmp, w.ld // 8, W, M // 8)
     del tmp
     extra = {"all_gather_rank_gbs": round(gbs[1], 1), "all_gather_ring_gbs": round(gbs[2], 1),
              "all_gather_rank_frac": round(gbs[1] / HBM_PEAK_GBS, 4),
@@ -1027,6 +1032,10 @@ def bench_rs_ag(args):
                  "launch_ms_avg": round((reg[1] + reg[2]) / 2, 4), "timing": REGION_TIMING,
                  "bytes_per_launch": [ag_b, ag_b],
                  "traffic": traffic_from_profile("rs_ag_allgather", w.name),
+                 "access_mix_reference_gbs": round(ag_ref, 1),
+                 "frac_of_access_mix_reference": round(2 * ag_b / ((reg[1] + reg[2]) / 1e3) / 1e9 / ag_ref, 4),
+                 "access_mix_reference": (f"read 1 row, write {W}, xor only: the best of "
+                                          f"{len(REFERENCE_SHAPES)} launch shapes ({ag_shape})"),
                  "what": "the two all-gathers (rank and ring order), the step's larger share of time"},
              "all_gather_gbs_with_events": {"rank": round(ev[1], 1), "ring": round(ev[2], 1)}}
     step()

@@ -668,8 +668,10 @@ dc_status dc_stream_rows(const void* src, int64_t src_ld_vec, int32_t rows_read,
  * resident per compute unit (0: no cap, at most 64), and the stores use the
  * planned flush's cache policies.  A sweep over shapes that includes a
  * kernel's own gives a reference its access mix cannot beat with xor for
- * arithmetic.  Other arguments and checks as in dc_stream_rows; a group
- * outside {1, 2, 4} is DC_ERR_UNSUPPORTED. */
+ * arithmetic.  Other arguments and checks as in dc_stream_rows, except
+ * that rows_read 1 with rows_written 4, 8 or 16 (the all-gather's mix: one
+ * row read, every row written) is also supported; a group outside
+ * {1, 2, 4} is DC_ERR_UNSUPPORTED. */
 dc_status dc_stream_rows_shaped(const void* src, int64_t src_ld_vec, int32_t rows_read, void* dst,
                                 int64_t dst_ld_vec, int32_t rows_written, int64_t nvec,
                                 int32_t group, int32_t cap, void* stream);

@@ -402,6 +402,28 @@ def test_stream_rows_reference(R, NW):
     assert np.all(got[NW:, :] == U.SENTINEL32) and np.all(got[:, nvec * 4:] == U.SENTINEL32)
 
 
+@pytest.mark.parametrize("R,NW", [(4, 1), (8, 8), (16, 16), (1, 8), (1, 16), (8, 1)])
+@pytest.mark.parametrize("group,cap", [(1, 0), (2, 8), (4, 6)])
+def test_stream_rows_shaped_reference(R, NW, group, cap):
+    """The shaped access-mix reference (every launch shape the bench sweeps,
+    one row read to every row written included) stores the xor of the R rows
+    in NW rows, over full runs of 64 vectors and a ragged tail."""
+    import torch
+    nvec = 64 * group * 7 + 37
+    ld = wl.round_up(nvec * 4, 64)
+    x = U.gen_slab(wl.DT_F32, R, ld, ld, 23, 0, wl.sigma_scale(1e-3))
+    rows = max(NW, 2)
+    y = U.empty_slab(wl.DT_F32, rows, ld)
+    dc.dc_stream_rows_shaped(x, ld // 4, R, y, ld // 4, NW, nvec, group, cap)
+    torch.cuda.synchronize()
+    hx = x.cpu().numpy().view(np.uint32)
+    want = np.bitwise_xor.reduce(hx[:, :nvec * 4], axis=0)
+    got = y.cpu().numpy().view(np.uint32)
+    for r in range(NW):
+        assert np.array_equal(got[r, :nvec * 4], want), r
+    assert np.all(got[NW:, :] == U.SENTINEL32) and np.all(got[:, nvec * 4:] == U.SENTINEL32)
+
+
 AR_CASES = [(4, 1003, 0, 1, 4, "none"), (4, 1003, 1, 0, 1, "none"), (3, 517, 0, 0, 3, "out=acc"),
             (16, 4100, 0, 1, 1, "none"), (8, 2048, 1, 1, 8, "x=acc"), (5, 33, 0, 1, 5, "none"),
             (4, 0, 0, 0, 1, "none")]
