@@ -269,8 +269,8 @@ def best_reference(src, src_ld_vec, rows_read, dst, dst_ld_vec, rows_written, nv
     """(best GB/s, its shape) of the access-mix reference over REFERENCE_SHAPES."""
     best, shape = 0.0, None
     for sh in REFERENCE_SHAPES:
-        if sh is None and rows_read == 1:
-            continue          # one row read to many: shaped launches only
+        if sh is None and not (rows_read in (4, 8, 16) and rows_written in (1, rows_read)):
+            continue          # other mixes: shaped launches only
         g = stream_rows_gbs(src, src_ld_vec, rows_read, dst, dst_ld_vec, rows_written, nvec, sh)
         if g > best:
             best, shape = g, sh
@@ -859,6 +859,11 @@ def bench_deferred(args, K, check=True):
         if not fused:
             add_mix_reference(roofline, best_reference(acc, ld // 4, W, out_f, ld // 4, W, M // 4),
                               f"read {W} rows, write {W}")
+        elif W == 4:
+            # accumulators and micro-batch read (2W rows: the first two
+            # micro-batches' rows stand in), every replica row written
+            add_mix_reference(roofline, best_reference(xs, ld // 4, 2 * W, out, ld // 4, W, M // 4),
+                              f"read {2 * W} rows, write {W}")
         accumulate = {"kernel": "k_accumulate", "bound": "hbm", "achieved": round(acc_region_gbs, 1),
                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(acc_region_gbs / HBM_PEAK_GBS, 4),

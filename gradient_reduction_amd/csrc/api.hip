@@ -955,12 +955,9 @@ dc_status dc_stream_copy(const void* src, void* dst, int64_t bytes, void* stream
 
 dc_status dc_stream_rows(const void* src, int64_t src_ld_vec, int32_t rows_read, void* dst,
                          int64_t dst_ld_vec, int32_t rows_written, int64_t nvec, void* stream) {
-  const bool wide = rows_written == 4 || rows_written == 8 || rows_written == 16;
-  if (!(((rows_read == 4 || rows_read == 8 || rows_read == 16) &&
-         (rows_written == 1 || rows_written == rows_read)) ||
-        (rows_read == 1 && wide)))
-    return fail(DC_ERR_UNSUPPORTED,
-                "rows_read=%d rows_written=%d (need 4/8/16 and 1 or rows_read, or 1 and 4/8/16)",
+  if (!((rows_read == 4 || rows_read == 8 || rows_read == 16) &&
+        (rows_written == 1 || rows_written == rows_read)))
+    return fail(DC_ERR_UNSUPPORTED, "rows_read=%d rows_written=%d (need 4/8/16 and 1 or rows_read)",
                 rows_read, rows_written);
   if (check_extent("src_ld_vec", src_ld_vec) || check_extent("dst_ld_vec", dst_ld_vec)) return DC_ERR_SHAPE;
   if (nvec < 0 || src_ld_vec < nvec || dst_ld_vec < nvec)
@@ -983,9 +980,9 @@ dc_status dc_stream_rows_shaped(const void* src, int64_t src_ld_vec, int32_t row
   const bool wide = rows_written == 4 || rows_written == 8 || rows_written == 16;
   if (!(((rows_read == 4 || rows_read == 8 || rows_read == 16) &&
          (rows_written == 1 || rows_written == rows_read)) ||
-        (rows_read == 1 && wide)))
+        (rows_read == 1 && wide) || (rows_read == 8 && rows_written == 4)))
     return fail(DC_ERR_UNSUPPORTED,
-                "rows_read=%d rows_written=%d (need 4/8/16 and 1 or rows_read, or 1 and 4/8/16)",
+                "rows_read=%d rows_written=%d (need 4/8/16 and 1 or rows_read, 1 and 4/8/16, or 8 and 4)",
                 rows_read, rows_written);
   if (check_extent("src_ld_vec", src_ld_vec) || check_extent("dst_ld_vec", dst_ld_vec)) return DC_ERR_SHAPE;
   if (nvec < 0 || src_ld_vec < nvec || dst_ld_vec < nvec)

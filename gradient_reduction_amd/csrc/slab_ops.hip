@@ -1015,7 +1015,7 @@ hipError_t launch_stream_rows_shaped(const void* src, int64_t src_ld_vec, int32_
   }
 #define DC_SRG3(R, NW) DC_SRG(R, NW, 1) DC_SRG(R, NW, 2) DC_SRG(R, NW, 4)
   DC_SRG3(4, 1) DC_SRG3(4, 4) DC_SRG3(8, 1) DC_SRG3(8, 8) DC_SRG3(16, 1) DC_SRG3(16, 16)
-  DC_SRG3(1, 4) DC_SRG3(1, 8) DC_SRG3(1, 16)
+  DC_SRG3(1, 4) DC_SRG3(1, 8) DC_SRG3(1, 16) DC_SRG3(8, 4)
 #undef DC_SRG3
 #undef DC_SRG
   return hipErrorInvalidValue;

@@ -670,8 +670,10 @@ dc_status dc_stream_rows(const void* src, int64_t src_ld_vec, int32_t rows_read,
  * kernel's own gives a reference its access mix cannot beat with xor for
  * arithmetic.  Other arguments and checks as in dc_stream_rows, except
  * that rows_read 1 with rows_written 4, 8 or 16 (the all-gather's mix: one
- * row read, every row written) is also supported; a group outside
- * {1, 2, 4} is DC_ERR_UNSUPPORTED. */
+ * row read, every row written) and rows_read 8 with rows_written 4 (the
+ * W = 4 fused accumulate-reduce's: accumulators and micro-batch read, every
+ * replica row written) are also supported; a group outside {1, 2, 4} is
+ * DC_ERR_UNSUPPORTED. */
 dc_status dc_stream_rows_shaped(const void* src, int64_t src_ld_vec, int32_t rows_read, void* dst,
                                 int64_t dst_ld_vec, int32_t rows_written, int64_t nvec,
                                 int32_t group, int32_t cap, void* stream);

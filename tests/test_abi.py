@@ -117,6 +117,17 @@ def test_other_argument_checks():
     expect(dc.DC_ERR_UNSUPPORTED, dc.dc_stream_rows, FAKE, 64, 3, FAKE << 1, 64, 1, 64, stream=0)
     expect(dc.DC_ERR_UNSUPPORTED, dc.dc_stream_rows, FAKE, 64, 8, FAKE << 1, 64, 2, 64, stream=0)
     expect(dc.DC_ERR_SHAPE, dc.dc_stream_rows, FAKE, 32, 8, FAKE << 1, 64, 1, 64, stream=0)
+    # the plain reference takes W rows to 1 or W; the shaped one also 1 to many and 8 to 4
+    expect(dc.DC_ERR_UNSUPPORTED, dc.dc_stream_rows, FAKE, 64, 1, FAKE << 1, 64, 8, 64, stream=0)
+    expect(dc.DC_ERR_UNSUPPORTED, dc.dc_stream_rows, FAKE, 64, 8, FAKE << 1, 64, 4, 64, stream=0)
+    sh = dc.dc_stream_rows_shaped
+    expect(dc.DC_ERR_UNSUPPORTED, sh, FAKE, 64, 2, FAKE << 1, 64, 1, 64, 1, 0, stream=0)
+    expect(dc.DC_ERR_UNSUPPORTED, sh, FAKE, 64, 1, FAKE << 1, 64, 2, 64, 1, 0, stream=0)
+    expect(dc.DC_ERR_UNSUPPORTED, sh, FAKE, 64, 4, FAKE << 1, 64, 2, 64, 1, 0, stream=0)
+    expect(dc.DC_ERR_UNSUPPORTED, sh, FAKE, 64, 8, FAKE << 1, 64, 1, 64, 3, 0, stream=0)
+    expect(dc.DC_ERR_ARG, sh, FAKE, 64, 8, FAKE << 1, 64, 1, 64, 1, 65, stream=0)
+    expect(dc.DC_ERR_SHAPE, sh, FAKE, 32, 1, FAKE << 1, 64, 8, 64, 1, 0, stream=0)
+    expect(dc.DC_ERR_ARG, sh, FAKE, 64, 8, FAKE + 1024, 64, 4, 64, 2, 8, stream=0)
     expect(dc.DC_ERR_ARG, dc.dc_stream_rows, FAKE, 64, 8, FAKE + 1024, 64, 1, 64, stream=0)
     expect(dc.DC_ERR_ARG, dc.dc_stream_copy, FAKE, FAKE + 16, 64, stream=0)
     huge = 1 << 60

@@ -402,7 +402,7 @@ def test_stream_rows_reference(R, NW):
     assert np.all(got[NW:, :] == U.SENTINEL32) and np.all(got[:, nvec * 4:] == U.SENTINEL32)
 
 
-@pytest.mark.parametrize("R,NW", [(4, 1), (8, 8), (16, 16), (1, 8), (1, 16), (8, 1)])
+@pytest.mark.parametrize("R,NW", [(4, 1), (8, 8), (16, 16), (1, 8), (1, 16), (8, 1), (8, 4)])
 @pytest.mark.parametrize("group,cap", [(1, 0), (2, 8), (4, 6)])
 def test_stream_rows_shaped_reference(R, NW, group, cap):
     """The shaped access-mix reference (every launch shape the bench sweeps,
