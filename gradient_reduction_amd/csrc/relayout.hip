@@ -3,8 +3,10 @@
 // AllReduce", "Describe alternatives": a reduce-scatter over the bucket needs
 // the payload contiguous by destination rank, so the bucket is first
 // relaid).  A plan of column pieces (src, dst, len), sorted by dst, moves
-// every data-parallel element of a bucket to its segment; this kernel applies
-// it to all W rows.  Pure data movement: HBM bound, W*n*b read + W*n*b written.
+// every data-parallel element of a bucket to its segment; these kernels apply
+// it to all W rows, either searching the pieces per tile or from a tile plan
+// that gives each destination tile inside one piece its source.  Pure data
+// movement: HBM bound, W*n*b read + W*n*b written.
 #include "device_common.h"
 #include "internal.h"
 

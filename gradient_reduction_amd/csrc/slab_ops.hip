@@ -571,12 +571,13 @@ __global__ __launch_bounds__(kST) void k_stream_rows(const u32x4* __restrict__ s
   for (int r = 0; r < NW; ++r) store16<kNTS>(dst + r * dld + k, y);
 }
 
-// The same mix at a launch shape of the planned flush: each one-wave
+// The same mix at a launch shape of the planned kernels: each one-wave
 // workgroup takes G runs of 64 vectors; with one row written the G results
-// are stored together after the last load, with every row written each
-// vector's rows are stored as soon as it is folded; stores use the planned
-// flush's cache policies.  A workgroup short of G full runs (the tail) goes
-// vector by vector.
+// are stored together after the last load, with several rows written each
+// vector's rows are stored as soon as it is folded (R = 1 is the
+// all-gather's one-row-to-every-row mix); stores use the planned flush's
+// cache policies.  A workgroup short of G full runs (the tail) goes vector
+// by vector.
 template <int R, int NW, int G>
 __global__ __launch_bounds__(kST) void k_stream_rows_g(const u32x4* __restrict__ src,
                                                        int64_t sld, u32x4* __restrict__ dst,
