@@ -125,11 +125,10 @@ hipError_t launch_flush_buffers(int32_t W, int32_t dtype, int64_t bucket_numel, 
                                 const dc_comm* comms, int32_t num_comms, int32_t pre_div,
                                 hipStream_t stream, const dc_tile* tiles = nullptr);
 
-// Tiles of the fused flush over a bucket of n coordinates: 128 slots of E
-// elements each, from coordinate 0.
-// The fused flush's tiles: kBufTile 16-byte slots each, one per thread of a
-// one-wave workgroup.  Against two per thread: +4% at W = 8 bf16 with 12
-// workgroups per compute unit (planned), +1.3% at W = 16 fp32.
+// The planned fused flush's tiles over a bucket of n coordinates, from
+// coordinate 0: kBufTile slots of E elements (16 bytes) each, one per thread
+// of a one-wave workgroup.  Against two per thread: +4% at W = 8 bf16 with
+// 12 workgroups per compute unit, +1.3% at W = 16 fp32.
 #ifndef DC_BUF_TILE
 #define DC_BUF_TILE 64
 #endif
