@@ -1,6 +1,7 @@
 /* A plain C11 client of libdc.so, used by the GPU tests: device memory from
- * hipMalloc, the owner map built on the device, one bucket flush and one
- * reduce-scatter through the C ABI, results copied back.  No Python and no
+ * hipMalloc, the owner map built on the device, one bucket flush (searched,
+ * and again from a host-made plan) and one reduce-scatter through the C ABI,
+ * results copied back.  No Python and no
  * torch in this file: it shows that the ABI needs nothing but the HIP runtime.
  *
  * One data-parallel parameter group over W ranks; the bucket holds every
@@ -13,6 +14,8 @@
  *             keep the input)
  *   rs_out    host [W, ld_rs] or NULL: reduce-scatter of the input slab's first
  *             M = W * ld_rs columns (when M fits the bucket)
+ *   planned_out host [W, ld] or NULL: the same flush from a plan made on the
+ *             host with dc_plan_flush (the owner map copied back first)
  * Returns 0, a DC_ERR_* code from the library, or 100 + a HIP error code. */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -40,7 +43,8 @@
 
 int c_client_run(int32_t W, int32_t dtype, const void* slab_in, int64_t ld, int32_t P,
                  const int64_t* numel, int32_t reduce_to_owner, int32_t pre_div,
-                 int32_t* owner_out, void* flush_out, int64_t ld_rs, void* rs_out) {
+                 int32_t* owner_out, void* flush_out, int64_t ld_rs, void* rs_out,
+                 void* planned_out) {
   int rc = 0;
   const size_t eb = dtype == DC_BF16 ? 2 : 4;
   const size_t slab_bytes = (size_t)W * (size_t)ld * eb;
@@ -53,7 +57,9 @@ int c_client_run(int32_t W, int32_t dtype, const void* slab_in, int64_t ld, int3
   int32_t* rank_to_global = (int32_t*)malloc(sizeof(int32_t) * (size_t)W);
   dc_task* tasks = (dc_task*)calloc((size_t)(P > 0 ? P : 1), sizeof(dc_task));
   const dc_comm comms[1] = {{W, 1}};
-  void *d_in = NULL, *d_out = NULL, *d_rs = NULL;
+  void *d_in = NULL, *d_out = NULL, *d_rs = NULL, *d_out2 = NULL;
+  dc_tile* tiles = NULL;
+  dc_tile* d_tiles = NULL;
   int64_t *d_numel = NULL, *d_flat = NULL, *d_psize = NULL;
   int32_t *d_pid_off = NULL, *d_pids = NULL, *d_owner = NULL, *d_counts = NULL;
   dc_task* d_tasks = NULL;
@@ -111,6 +117,30 @@ int c_client_run(int32_t W, int32_t dtype, const void* slab_in, int64_t ld, int3
                          stream));
   HIP_TRY(hipMemcpyAsync(flush_out, d_out, slab_bytes, hipMemcpyDeviceToHost, stream));
   HIP_TRY(hipStreamSynchronize(stream));
+  if (planned_out != NULL) {
+    /* plan on the host from the owner map just copied back, then flush again */
+    int64_t ntiles = 0, roots = 0;
+    const int32_t* own = reduce_to_owner ? owner_out : NULL;
+    DC_TRY(dc_plan_flush(W, dtype, 0, total, tasks, P, own, NULL, NULL, P, comms, 1, NULL, 0, &ntiles,
+                         NULL));
+    tiles = (dc_tile*)calloc((size_t)(ntiles > 0 ? ntiles : 1), sizeof(dc_tile));
+    if (tiles == NULL) {
+      rc = DC_ERR_ARG;
+      goto done;
+    }
+    DC_TRY(dc_plan_flush(W, dtype, 0, total, tasks, P, own, NULL, NULL, P, comms, 1, tiles, ntiles,
+                         &ntiles, &roots));
+    HIP_TRY(hipMalloc(&d_out2, slab_bytes));
+    HIP_TRY(hipMalloc((void**)&d_tiles, sizeof(dc_tile) * (size_t)(ntiles > 0 ? ntiles : 1)));
+    HIP_TRY(hipMemcpyAsync(d_out2, slab_in, slab_bytes, hipMemcpyHostToDevice, stream));
+    HIP_TRY(hipMemcpyAsync(d_tiles, tiles, sizeof(dc_tile) * (size_t)ntiles, hipMemcpyHostToDevice,
+                           stream));
+    DC_TRY(dc_flush_bucket_planned(W, dtype, d_in, ld, d_out2, ld, 0, total, d_tasks, P,
+                                   reduce_to_owner ? d_owner : NULL, NULL, NULL, P, comms, 1, pre_div,
+                                   d_tiles, ntiles, roots, stream));
+    HIP_TRY(hipMemcpyAsync(planned_out, d_out2, slab_bytes, hipMemcpyDeviceToHost, stream));
+    HIP_TRY(hipStreamSynchronize(stream));
+  }
 
 done:
   if (stream != NULL) hipStreamSynchronize(stream);
@@ -125,7 +155,10 @@ done:
   hipFree(d_owner);
   hipFree(d_counts);
   hipFree(d_tasks);
+  hipFree(d_out2);
+  hipFree(d_tiles);
   if (stream != NULL) hipStreamDestroy(stream);
+  free(tiles);
   free(rank_to_global);
   free(tasks);
   return rc;

@@ -1,6 +1,7 @@
 """GPU: a plain C client of the ABI (tests/c_client.c: hipMalloc'd buffers,
-the owner map built on the device, one bucket flush and one reduce-scatter,
-no Python or torch in the client), bit-exact against the oracle."""
+the owner map built on the device, one bucket flush (searched, and again
+from a plan made on the host) and one reduce-scatter, no Python or torch in
+the client), bit-exact against the oracle."""
 import ctypes
 import os
 import random
@@ -27,7 +28,7 @@ def client():
     L = ctypes.CDLL(path)
     f = L.c_client_run
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-    f.argtypes = [i32, i32, vp, i64, i32, vp, i32, i32, vp, vp, i64, vp]
+    f.argtypes = [i32, i32, vp, i64, i32, vp, i32, i32, vp, vp, i64, vp, vp]
     f.restype = ctypes.c_int
     return f
 
@@ -54,9 +55,10 @@ def test_c_client_matches_oracle(client, W, dtype, owner, pre):
     P = len(numel)
     owner_out = np.full(P, -7, np.int32)
     flush_out = np.zeros_like(hin)
+    planned_out = np.zeros_like(hin)
     rs_out = np.zeros((W, max(ld_rs, 64)), hin.dtype)
     rc = client(W, dtype, _ptr(hin), ld, P, _ptr(numel), owner, pre, _ptr(owner_out),
-                _ptr(flush_out), ld_rs, _ptr(rs_out) if ld_rs else None)
+                _ptr(flush_out), ld_rs, _ptr(rs_out) if ld_rs else None, _ptr(planned_out))
     assert rc == 0, rc
 
     flat, ps, off, pids = oracle.partition_ids(list(numel), [0, P], [W])
@@ -68,6 +70,7 @@ def test_c_client_matches_oracle(client, W, dtype, owner, pre):
                  want_owner if owner else None, [W], [1], pre)
     bits = np.uint16 if dtype == wl.DT_BF16 else np.uint32
     assert np.array_equal(flush_out.view(bits), want.view(bits))
+    assert np.array_equal(planned_out.view(bits), want.view(bits))
     if ld_rs:
         want_rs = np.zeros_like(rs_out)
         oracle.reduce_scatter(W, dtype, hin, want_rs, W * ld_rs, pre)
@@ -82,6 +85,6 @@ def test_c_client_reports_library_errors(client):
     out = np.zeros_like(hin)
     own = np.zeros(2, np.int32)
     assert client(0, wl.DT_F32, _ptr(hin), 320, 2, _ptr(numel), 1, 0, _ptr(own), _ptr(out), 0,
-                  None) == dc.DC_ERR_ARG
+                  None, None) == dc.DC_ERR_ARG
     assert client(4, 7, _ptr(hin), 320, 2, _ptr(numel), 1, 0, _ptr(own), _ptr(out), 0,
-                  None) == dc.DC_ERR_DTYPE
+                  None, _ptr(out)) == dc.DC_ERR_DTYPE
