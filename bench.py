@@ -415,6 +415,7 @@ def flush_oracle(w, y, mode, init="zero", max_buckets=None, sample_buckets=2):
     psize = zero2[1] if zero2 is not None else None
     per = flush_bytes(w, owner, psize)
     nb = len(w.buckets) if max_buckets is None else min(max_buckets, len(w.buckets))
+    sample_buckets = min(sample_buckets, nb)
     k = OC.nthreads()
     cols = elems = bad = 0
     first_bad = None
@@ -552,7 +553,8 @@ def bench_flush(args, w, mode):
     log(f"[bench] flushes back to back: {once_ms:.4f} ms per step, {region_gbs:.1f} GB/s")
     roofline = {"bound": "hbm", "achieved": round(region_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(region_gbs / HBM_PEAK_GBS, 4),
-                "traffic": None if args.searched else traffic_from_profile(args.workload, w.name),
+                "traffic": (None if args.searched or getattr(args, "bucket_numel", 0)
+                            else traffic_from_profile(args.workload, w.name)),
                 "kernel": "k_flush_planned" if not args.searched else "k_flush",
                 "launch_ms_avg": round(once_ms / nb, 4), "timing": REGION_TIMING,
                 "per_launch_events": per_launch_events(flush_gbs, avg_launch_ms),
@@ -1373,10 +1375,19 @@ def main():
     ap.add_argument("--load-sample-s", type=float, default=1.5,
                     help="flush workloads: seconds of steps run while rocm-smi samples the GPU's "
                          "clocks and power (0: no sample, e.g. under a profiler)")
+    ap.add_argument("--bucket-numel", type=int, default=0,
+                    help="flush workloads but tiny: bucket capacity in elements (default: the "
+                         "workload's 52,428,800); the same gradient, packed into buckets of "
+                         "this size")
     ap.add_argument("--probe", action="store_true",
                     help="flush workloads: print the probe line of each of the first 20 flushes "
                          "(the executor's reduce_probe), as they are issued")
     args = ap.parse_args()
+    if args.bucket_numel and (args.workload not in FLUSH_WORKLOADS or args.workload == "tiny"
+                              or args.bucket_numel < 1):
+        print("--bucket-numel takes a positive size and applies to the 402.8M and mixed flush "
+              "workloads only", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path simulates W data-parallel ranks as rows "
               f"of one GPU's gradient slab, so --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -1395,7 +1406,7 @@ def main():
     parity_bad = 0
     if args.workload in FLUSH_WORKLOADS:
         fn, mode = FLUSH_WORKLOADS[args.workload]
-        w = getattr(wl, fn)()
+        w = getattr(wl, fn)(**({"capacity": args.bucket_numel} if args.bucket_numel else {}))
         r = bench_flush(args, w, mode)
         ms, value, roof, extra = r["ms"], r["value"], r["roofline"], r["extra"]
         name, dtype = w.name, wl.DTYPE_NAME[w.dtype]
