@@ -14,6 +14,7 @@
 
 #include "dc.h"
 #include "internal.h"
+#include "plan.h"
 
 namespace {
 
@@ -415,6 +416,47 @@ dc_status dc_plan_flush(int32_t W, int32_t dtype, int64_t bucket_col, int64_t bu
   }
   if (root_tiles != nullptr) *root_tiles = roots;
   return ok();
+}
+
+dc_status dc_plan_flush_device(int32_t W, int32_t dtype, int64_t bucket_col, int64_t bucket_numel,
+                               const dc_task* tasks, int32_t num_tasks, const int32_t* owner,
+                               const int64_t* flat_offset, const int64_t* part_size,
+                               int32_t num_params, const dc_comm* comms, int32_t num_comms,
+                               dc_tile* tiles, int64_t capacity, int64_t* num_tiles,
+                               int64_t* root_tiles, void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype)) || (st = check_comms(W, comms, num_comms))) return st;
+  if (num_tiles == nullptr) return fail(DC_ERR_NULL, "num_tiles is NULL");
+  if (bucket_col < 0 || bucket_numel < 0)
+    return fail(DC_ERR_ARG, "bucket_col=%lld, bucket_numel=%lld", (long long)bucket_col, (long long)bucket_numel);
+  if ((st = check_extent("bucket_col", bucket_col)) || (st = check_extent("bucket_numel", bucket_numel)))
+    return st;
+  if (num_tasks < 0 || num_params < 0) return fail(DC_ERR_ARG, "num_tasks or num_params < 0");
+  if ((flat_offset == nullptr) != (part_size == nullptr))
+    return fail(DC_ERR_NULL, "flat_offset and part_size go together");
+  if (flat_offset != nullptr && owner != nullptr)
+    return fail(DC_ERR_ARG, "ZeRO-2 mode (flat_offset given) takes no owner map");
+  const dc::FlushTiles g = dc::plan_tiles(dtype, bucket_col, bucket_col + bucket_numel);
+  *num_tiles = g.count;
+  if (tiles == nullptr) return ok();  // size query: nothing is launched
+  if (capacity < g.count)
+    return fail(DC_ERR_SHAPE, "capacity=%lld < %lld tiles", (long long)capacity, (long long)g.count);
+  if (num_tasks > 0 && tasks == nullptr) return fail(DC_ERR_NULL, "tasks is NULL");
+  dc::PlanLaunch a{};
+  a.W = W;
+  a.dtype = dtype;
+  a.c0 = bucket_col;
+  a.numel = bucket_numel;
+  a.tasks = tasks;
+  a.ntasks = num_tasks;
+  a.owner = owner;
+  a.flat = flat_offset;
+  a.psize = part_size;
+  a.nparams = num_params;
+  a.ncomms = num_comms;
+  a.tiles = tiles;
+  a.root_tiles = root_tiles;
+  return hip_status(dc::launch_plan_flush(a, static_cast<hipStream_t>(stream)), "device flush planner launch");
 }
 
 dc_status dc_flush_bucket_buffers(int32_t W, int32_t dtype, int64_t bucket_numel,

@@ -65,6 +65,8 @@ _SIGS = {
                                _i32, _vp, _i32, _i32, _vp], _i32),
     "dc_plan_flush": ([_i32, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i64,
                        _vp, _vp], _i32),
+    "dc_plan_flush_device": ([_i32, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp,
+                              _i64, _vp, _vp, _vp], _i32),
     "dc_flush_bucket_planned": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
                                  _vp, _i32, _vp, _i32, _i32, _vp, _i64, _i64, _vp], _i32),
     "dc_probe_flush": ([_i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp], _i32),
@@ -298,6 +300,22 @@ def dc_plan_flush(W, dtype, bucket_col, bucket_numel, tasks, num_tasks, owner, f
         W, dtype, bucket_col, bucket_numel, tp, num_tasks, op, fo, ps, num_params, cp, num_comms,
         tiles.ctypes.data_as(_vp), n.value, ctypes.byref(n), ctypes.byref(r)))
     return tiles[:n.value].copy(), r.value
+
+
+def dc_plan_flush_device(W, dtype, bucket_col, bucket_numel, tasks, num_tasks, owner, flat_offset,
+                         part_size, num_params, comms, num_comms, tiles, capacity, root_tiles=None,
+                         stream=None):
+    """tasks, owner, flat_offset, part_size, tiles, root_tiles: device
+    pointers (tensors or ints) or None.  Returns the tile count; with tiles
+    None it only asks for it (nothing is launched, no stream is needed)."""
+    cp, _a = _host(comms, COMM_DTYPE)
+    n = ctypes.c_int64(0)
+    s = _stream(stream) if tiles is not None else stream
+    _check("dc_plan_flush_device", lib().dc_plan_flush_device(
+        W, dtype, bucket_col, bucket_numel, _dev(tasks), num_tasks, _dev(owner), _dev(flat_offset),
+        _dev(part_size), num_params, cp, num_comms, _dev(tiles), capacity, ctypes.byref(n),
+        _dev(root_tiles), s))
+    return n.value
 
 
 def dc_flush_bucket_planned(W, dtype, slab_in, ld_in, slab_out, ld_out, bucket_col, bucket_numel,

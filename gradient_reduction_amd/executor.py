@@ -14,8 +14,9 @@ in the grad buffers of the ranks that keep one, with no bucket in between.
 
 plan() builds each bucket's flush plan once on the host (dc_plan_flush: the
 tasks each tile of the flush grid overlaps and, for a tile inside one task,
-the rows its sums go to); flush() then launches dc_flush_bucket_planned, the
-same sums with no per-tile search.
+the rows its sums go to), or on the device (dc_plan_flush_device, the same
+records); flush() then launches dc_flush_bucket_planned, the same sums with
+no per-tile search.
 
 torch supplies device memory and the stream; every step runs in libdc.so.
 """
@@ -122,12 +123,19 @@ class Zero1FlushExecutor:
     def task_table(self, b: int) -> int:
         return self.d_tasks.data_ptr() + 32 * int(self.t_begin[b])
 
-    def plan(self) -> None:
+    def plan(self, on_device: bool = False, stream=None) -> None:
         """Plan every bucket's flush on the host (dc_plan_flush: per tile, the
         tasks it overlaps and, for a tile inside one task, its rows), from
         the owner map (or the ZeRO-2 partition sizes), and keep the plans on
         the device; flush() then takes the planned path.  Synchronizes: call
-        it at init, after build_owner_map, not while a graph is captured."""
+        it at init, after build_owner_map, not while a graph is captured.
+        on_device: the same plans from dc_plan_flush_device, straight from
+        the device task table and owner map (no host copies); one
+        synchronization reads back the root counts, which pick each planned
+        launch's shape."""
+        if on_device:
+            self._plan_on_device(stream)
+            return
         torch = self.torch
         if self.h_owner is None:
             self.fetch_metadata()
@@ -150,6 +158,28 @@ class Zero1FlushExecutor:
         allr = np.concatenate(recs) if recs else np.zeros(0, dc.TILE_DTYPE)
         raw = torch.from_numpy(allr.view(np.uint8).copy()) if len(allr) else torch.zeros(16, dtype=torch.uint8)
         self.d_tiles = raw.to(self.d_tasks.device)
+
+    def _plan_on_device(self, stream=None) -> None:
+        torch = self.torch
+        dev = self.d_tasks.device
+        counts = [dc.dc_plan_flush_device(self.W, self.dtype, bk.col, bk.numel, self.task_table(b),
+                                          len(bk.tasks), None, None, None, self.P, self.comms,
+                                          len(self.comms), None, 0)
+                  for b, bk in enumerate(self.buckets)]
+        self.tile_begin = np.concatenate([[0], np.cumsum(counts)]).astype(int)
+        self.d_tiles = torch.empty(16 * max(int(self.tile_begin[-1]), 1), dtype=torch.uint8, device=dev)
+        roots = torch.empty(max(len(self.buckets), 1), dtype=torch.int64, device=dev)
+        if self.zero2:
+            owner, flat, psize = None, self.d_flat, self.d_psize
+        else:
+            owner, flat, psize = (self.d_owner if self.reduce_to_owner else None), None, None
+        for b, bk in enumerate(self.buckets):
+            dc.dc_plan_flush_device(self.W, self.dtype, bk.col, bk.numel, self.task_table(b),
+                                    len(bk.tasks), owner, flat, psize, self.P, self.comms,
+                                    len(self.comms), self.d_tiles.data_ptr() + 16 * int(self.tile_begin[b]),
+                                    counts[b], roots.data_ptr() + 8 * b, stream)
+        torch.cuda.synchronize()
+        self.root_tiles = [int(v) for v in roots.cpu().numpy()[:len(self.buckets)]]
 
     def flush(self, b: int, slab_in, ld_in: int, slab_out, ld_out: int, stream=None) -> None:
         bk = self.buckets[b]

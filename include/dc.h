@@ -300,6 +300,42 @@ dc_status dc_plan_flush(int32_t W, int32_t dtype, int64_t bucket_col, int64_t bu
                         const dc_comm* comms, int32_t num_comms, dc_tile* tiles,
                         int64_t capacity, int64_t* num_tiles, int64_t* root_tiles);
 
+/* The plan of dc_plan_flush computed on the device ([DS] Design points: a
+ * bucket's reduction destinations are settled for the whole bucket before
+ * it is reduced), for callers whose task table and owner map (or ZeRO-2
+ * partition sizes) live in device memory: no host copy and no
+ * synchronization.  The records are those dc_plan_flush writes for the same
+ * arguments, bit for bit, and serve dc_flush_bucket_planned the same way.
+ * One thread per tile binary-searches the task offsets.
+ *   tasks                 device dc_task[num_tasks]; must be a table that
+ *                         passes dc_validate_tasks (not checked here: another
+ *                         table gives other records, and its params and
+ *                         communicators index owner, flat_offset and
+ *                         part_size only inside [0, num_params) and
+ *                         [0, num_comms))
+ *   owner                 device int32[num_params] or NULL (owner-map mode)
+ *   flat_offset, part_size device int64[num_params] or NULL (ZeRO-2, as for
+ *                         dc_plan_flush)
+ *   comms, num_comms      host, as for dc_flush_bucket (checked)
+ *   tiles, capacity       device dc_tile[capacity] out; NULL asks for the
+ *                         count only (nothing is launched)
+ *   num_tiles             host out: the tile count (as dc_plan_flush's)
+ *   root_tiles            device int64 out, or NULL: set on the stream to
+ *                         the count dc_plan_flush reports as root_tiles
+ *                         (whole tiles with root >= 0); a caller that does
+ *                         not read it back may pass num_tiles for
+ *                         reduce-to-owner or ZeRO-2 buckets and 0 otherwise to
+ *                         dc_flush_bucket_planned, which uses it only to pick
+ *                         the launch shape
+ * Fewer than *num_tiles slots is DC_ERR_SHAPE.  Stream-ordered: the plan is
+ * ready for a planned flush later on the same stream. */
+dc_status dc_plan_flush_device(int32_t W, int32_t dtype, int64_t bucket_col, int64_t bucket_numel,
+                               const dc_task* tasks, int32_t num_tasks, const int32_t* owner,
+                               const int64_t* flat_offset, const int64_t* part_size,
+                               int32_t num_params, const dc_comm* comms, int32_t num_comms,
+                               dc_tile* tiles, int64_t capacity, int64_t* num_tiles,
+                               int64_t* root_tiles, void* stream);
+
 /* Bucket flush with a plan (dc_plan_flush): the same results, bit for bit,
  * as dc_flush_bucket (flat_offset == NULL) or dc_flush_bucket_zero2
  * (flat_offset and part_size given, owner NULL) with the same arguments.  A

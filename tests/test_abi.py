@@ -503,6 +503,37 @@ def test_plan_flush_argument_checks():
     assert dc.TILE_DTYPE.itemsize == 16
 
 
+def test_plan_flush_device_argument_checks():
+    """dc_plan_flush_device's checks, all before any launch: the size query
+    launches nothing and needs no stream."""
+    f = dc.dc_plan_flush_device
+    comms = [(8, 1)]
+    ok = dict(W=8, dtype=0, bucket_col=0, bucket_numel=5000, tasks=TASK_PTR, num_tasks=1,
+              owner=None, flat_offset=None, part_size=None, num_params=1, comms=comms,
+              num_comms=1, tiles=FAKE, capacity=4, stream=0)
+    # 625 vectors: 10 tiles of 64; the size query answers without a launch
+    assert f(**dict(ok, tiles=None, capacity=0)) == 10
+    assert f(**dict(ok, bucket_col=8, tiles=None, capacity=0)) == 10
+    assert f(**dict(ok, bucket_numel=0, tiles=None, capacity=0)) == 0
+    for code, kw in [(dc.DC_ERR_ARG, dict(W=0)), (dc.DC_ERR_ARG, dict(W=65)),
+                     (dc.DC_ERR_DTYPE, dict(dtype=2)),
+                     (dc.DC_ERR_ARG, dict(comms=[(4, 1)])), (dc.DC_ERR_NULL, dict(comms=None)),
+                     (dc.DC_ERR_ARG, dict(bucket_col=-1)), (dc.DC_ERR_ARG, dict(bucket_numel=-5)),
+                     (dc.DC_ERR_SHAPE, dict(bucket_numel=(1 << 44) + 8)),
+                     (dc.DC_ERR_ARG, dict(num_tasks=-1)), (dc.DC_ERR_ARG, dict(num_params=-1)),
+                     (dc.DC_ERR_NULL, dict(flat_offset=FAKE)),
+                     (dc.DC_ERR_NULL, dict(part_size=FAKE)),
+                     (dc.DC_ERR_ARG, dict(owner=FAKE, flat_offset=FAKE, part_size=FAKE)),
+                     (dc.DC_ERR_SHAPE, dict(capacity=9)),
+                     (dc.DC_ERR_NULL, dict(tasks=None, capacity=10))]:
+        expect(code, f, **dict(ok, **kw))
+    # a NULL count pointer
+    cp = dc.comms_array(comms)
+    assert dc.lib().dc_plan_flush_device(8, 0, 0, 5000, None, 0, None, None, None, 1,
+                                         cp.ctypes.data_as(ctypes.c_void_p), 1, None, 0, None, None,
+                                         None) == dc.DC_ERR_NULL
+
+
 def test_flush_planned_argument_checks():
     f = dc.dc_flush_bucket_planned
     ok = dict(W=8, dtype=0, slab_in=FAKE, ld_in=2048, slab_out=FAKE, ld_out=2048, bucket_col=0,

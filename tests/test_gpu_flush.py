@@ -126,10 +126,11 @@ def test_partition_ids_and_owner_map(w):
 def flush_case(w, reduce_to_owner, in_place=False, probe=True, zero2=False, planned=False):
     """Run every bucket of w on the GPU and on the oracle; compare all of the
     output slab bit for bit, and the probe records.  planned: the executor
-    plans every bucket first and flushes with the plans."""
+    plans every bucket first (on the host, or with planned="device" on the
+    device) and flushes with the plans."""
     import torch
     U.say("flush", w.name, "zero2" if zero2 else ("owner" if reduce_to_owner else "allreduce"),
-          "in-place" if in_place else "", "planned" if planned else "")
+          "in-place" if in_place else "", {False: "", True: "planned", "device": "planned on device"}[planned])
     scale = w.scale
     ld = w.ld
     x = U.gen_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, scale)
@@ -137,7 +138,7 @@ def flush_case(w, reduce_to_owner, in_place=False, probe=True, zero2=False, plan
     ex = executor.from_workload(w, reduce_to_owner=reduce_to_owner, zero2=zero2)
     ex.build_owner_map()
     if planned:
-        ex.plan()
+        ex.plan(on_device=planned == "device")
     for b in range(len(w.buckets)):
         ex.flush(b, x, ld, y, ld)
     torch.cuda.synchronize()
