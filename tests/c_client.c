@@ -1,8 +1,8 @@
 /* A plain C11 client of libdc.so, used by the GPU tests: device memory from
  * hipMalloc, the owner map built on the device, one bucket flush (searched,
- * and again from a host-made plan) and one reduce-scatter through the C ABI,
- * results copied back.  No Python and no
- * torch in this file: it shows that the ABI needs nothing but the HIP runtime.
+ * and again from a host-made and a device-made plan) and one reduce-scatter
+ * through the C ABI, results copied back.  No Python and no torch in this
+ * file: it shows that the ABI needs nothing but the HIP runtime.
  *
  * One data-parallel parameter group over W ranks; the bucket holds every
  * parameter in order (task t = parameter t on communicator 0).
@@ -15,8 +15,12 @@
  *   rs_out    host [W, ld_rs] or NULL: reduce-scatter of the input slab's first
  *             M = W * ld_rs columns (when M fits the bucket)
  *   planned_out host [W, ld] or NULL: the same flush from a plan made on the
- *             host with dc_plan_flush (the owner map copied back first)
- * Returns 0, a DC_ERR_* code from the library, or 100 + a HIP error code. */
+ *             host with dc_plan_flush (the owner map copied back first); the
+ *             plan is also built on the device with dc_plan_flush_device and
+ *             the flush run again from it
+ * Returns 0, a DC_ERR_* code from the library, 100 + a HIP error code, or 200
+ * when the device-built plan, its root count or its flush differs from the
+ * host plan's. */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -58,8 +62,10 @@ int c_client_run(int32_t W, int32_t dtype, const void* slab_in, int64_t ld, int3
   dc_task* tasks = (dc_task*)calloc((size_t)(P > 0 ? P : 1), sizeof(dc_task));
   const dc_comm comms[1] = {{W, 1}};
   void *d_in = NULL, *d_out = NULL, *d_rs = NULL, *d_out2 = NULL;
-  dc_tile* tiles = NULL;
-  dc_tile* d_tiles = NULL;
+  dc_tile *tiles = NULL, *tiles2 = NULL;
+  dc_tile *d_tiles = NULL, *d_tiles2 = NULL;
+  int64_t* d_roots = NULL;
+  void* planned2 = NULL;
   int64_t *d_numel = NULL, *d_flat = NULL, *d_psize = NULL;
   int32_t *d_pid_off = NULL, *d_pids = NULL, *d_owner = NULL, *d_counts = NULL;
   dc_task* d_tasks = NULL;
@@ -140,6 +146,36 @@ int c_client_run(int32_t W, int32_t dtype, const void* slab_in, int64_t ld, int3
                                    d_tiles, ntiles, roots, stream));
     HIP_TRY(hipMemcpyAsync(planned_out, d_out2, slab_bytes, hipMemcpyDeviceToHost, stream));
     HIP_TRY(hipStreamSynchronize(stream));
+    /* the same plan built on the device from the device task table and owner
+       map, and the flush again from it: the records and the output must be
+       the host plan's, byte for byte (else 200) */
+    {
+      int64_t ntiles_dev = 0, roots_host = 0;
+      HIP_TRY(hipMalloc((void**)&d_tiles2, sizeof(dc_tile) * (size_t)(ntiles > 0 ? ntiles : 1)));
+      HIP_TRY(hipMalloc((void**)&d_roots, sizeof(int64_t)));
+      DC_TRY(dc_plan_flush_device(W, dtype, 0, total, d_tasks, P, reduce_to_owner ? d_owner : NULL,
+                                  NULL, NULL, P, comms, 1, d_tiles2, ntiles, &ntiles_dev, d_roots,
+                                  stream));
+      tiles2 = (dc_tile*)calloc((size_t)(ntiles > 0 ? ntiles : 1), sizeof(dc_tile));
+      planned2 = malloc(slab_bytes);
+      if (tiles2 == NULL || planned2 == NULL) {
+        rc = DC_ERR_ARG;
+        goto done;
+      }
+      HIP_TRY(hipMemcpyAsync(tiles2, d_tiles2, sizeof(dc_tile) * (size_t)ntiles, hipMemcpyDeviceToHost,
+                             stream));
+      HIP_TRY(hipMemcpyAsync(&roots_host, d_roots, sizeof(int64_t), hipMemcpyDeviceToHost, stream));
+      HIP_TRY(hipMemcpyAsync(d_out2, slab_in, slab_bytes, hipMemcpyHostToDevice, stream));
+      DC_TRY(dc_flush_bucket_planned(W, dtype, d_in, ld, d_out2, ld, 0, total, d_tasks, P,
+                                     reduce_to_owner ? d_owner : NULL, NULL, NULL, P, comms, 1, pre_div,
+                                     d_tiles2, ntiles, roots, stream));
+      HIP_TRY(hipMemcpyAsync(planned2, d_out2, slab_bytes, hipMemcpyDeviceToHost, stream));
+      HIP_TRY(hipStreamSynchronize(stream));
+      if (ntiles_dev != ntiles || roots_host != roots ||
+          memcmp(tiles2, tiles, sizeof(dc_tile) * (size_t)ntiles) != 0 ||
+          memcmp(planned2, planned_out, slab_bytes) != 0)
+        rc = 200;
+    }
   }
 
 done:
@@ -157,8 +193,12 @@ done:
   hipFree(d_tasks);
   hipFree(d_out2);
   hipFree(d_tiles);
+  hipFree(d_tiles2);
+  hipFree(d_roots);
   if (stream != NULL) hipStreamDestroy(stream);
   free(tiles);
+  free(tiles2);
+  free(planned2);
   free(rank_to_global);
   free(tasks);
   return rc;
