@@ -518,6 +518,26 @@ dc_status dc_plan_flush_buffers(int32_t W, int32_t dtype, int64_t bucket_numel, 
   return ok();
 }
 
+dc_status dc_plan_flush_buffers_device(int32_t W, int32_t dtype, int64_t bucket_numel,
+                                       const dc_task* tasks, int32_t num_tasks,
+                                       const dc_comm* comms, int32_t num_comms, dc_tile* tiles,
+                                       int64_t capacity, int64_t* num_tiles, void* stream) {
+  dc_status st;
+  if ((st = check_w(W)) || (st = check_dtype(dtype)) || (st = check_comms(W, comms, num_comms))) return st;
+  if (num_tiles == nullptr) return fail(DC_ERR_NULL, "num_tiles is NULL");
+  if (bucket_numel < 0 || num_tasks < 0) return fail(DC_ERR_ARG, "bucket_numel or num_tasks < 0");
+  if ((st = check_extent("bucket_numel", bucket_numel))) return st;
+  const int64_t count = num_tasks > 0 ? dc::buffer_tiles(dtype, bucket_numel) : 0;
+  *num_tiles = count;
+  if (tiles == nullptr) return ok();  // size query: nothing is launched
+  if (capacity < count)
+    return fail(DC_ERR_SHAPE, "capacity=%lld < %lld tiles", (long long)capacity, (long long)count);
+  if (num_tasks > 0 && tasks == nullptr) return fail(DC_ERR_NULL, "tasks is NULL");
+  return hip_status(dc::launch_plan_flush_buffers(dtype, bucket_numel, tasks, num_tasks, tiles, count,
+                                                  static_cast<hipStream_t>(stream)),
+                    "device fused-flush planner launch");
+}
+
 dc_status dc_flush_bucket_buffers_planned(int32_t W, int32_t dtype, int64_t bucket_numel,
                                           const dc_task* tasks, int32_t num_tasks,
                                           const void* const* in_ptrs, void* const* out_ptrs,
@@ -796,6 +816,29 @@ dc_status dc_plan_relayout_tiles(int32_t dtype, int64_t bucket_col, int64_t buck
     tiles[dc::tile_slot(t, n)] = rec;
   }
   return ok();
+}
+
+dc_status dc_plan_relayout_tiles_device(int32_t dtype, int64_t bucket_col, int64_t bucket_numel,
+                                        const dc_piece* pieces, int32_t num_pieces,
+                                        int64_t out_numel, int64_t* tiles, int64_t tiles_capacity,
+                                        int64_t* num_tiles, void* stream) {
+  dc_status st;
+  if ((st = check_dtype(dtype))) return st;
+  if (bucket_col < 0 || bucket_numel < 0 || out_numel < 0 || num_pieces < 0)
+    return fail(DC_ERR_ARG, "negative bucket_col, bucket_numel, out_numel or num_pieces");
+  if ((st = check_extent("bucket_col", bucket_col)) || (st = check_extent("bucket_numel", bucket_numel)) ||
+      (st = check_extent("out_numel", out_numel)))
+    return st;
+  if (num_tiles == nullptr) return fail(DC_ERR_NULL, "num_tiles is NULL");
+  const int64_t n = dc::relayout_tile_count(dtype, out_numel);
+  *num_tiles = n;
+  if (tiles == nullptr) return ok();  // size query: nothing is launched
+  if (tiles_capacity < n)
+    return fail(DC_ERR_SHAPE, "tiles_capacity=%lld < %lld tiles", (long long)tiles_capacity, (long long)n);
+  if (num_pieces > 0 && pieces == nullptr) return fail(DC_ERR_NULL, "pieces is NULL");
+  return hip_status(dc::launch_plan_relayout_tiles(dtype, bucket_col, bucket_numel, pieces, num_pieces,
+                                                   out_numel, tiles, n, static_cast<hipStream_t>(stream)),
+                    "device relayout planner launch");
 }
 
 dc_status dc_relayout_bucket_planned(int32_t W, int32_t dtype, const void* slab_in, int64_t ld_in,

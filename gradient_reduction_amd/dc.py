@@ -59,6 +59,8 @@ _SIGS = {
     "dc_flush_bucket_buffers": ([_i32, _i32, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp], _i32),
     "dc_validate_buffer_tasks": ([_i32, _i32, _vp, _i32, _i64, _vp, _i32, _vp, _vp], _i32),
     "dc_plan_flush_buffers": ([_i32, _i32, _i64, _vp, _i32, _vp, _i32, _vp, _i64, _vp], _i32),
+    "dc_plan_flush_buffers_device": ([_i32, _i32, _i64, _vp, _i32, _vp, _i32, _vp, _i64, _vp, _vp],
+                                     _i32),
     "dc_flush_bucket_buffers_planned": ([_i32, _i32, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp,
                                          _i64, _vp], _i32),
     "dc_flush_bucket_zero2": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
@@ -76,6 +78,7 @@ _SIGS = {
     "dc_relayout_bucket": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp],
                            _i32),
     "dc_plan_relayout_tiles": ([_i32, _i64, _i64, _vp, _i32, _i64, _vp, _i64, _vp], _i32),
+    "dc_plan_relayout_tiles_device": ([_i32, _i64, _i64, _vp, _i32, _i64, _vp, _i64, _vp, _vp], _i32),
     "dc_relayout_bucket_planned": ([_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _i64,
                                     _vp, _i64, _vp], _i32),
     "dc_reduce_scatter_v": ([_i32, _i32, _vp, _i64, _vp, _i64, _vp, _i32, _vp], _i32),
@@ -315,6 +318,31 @@ def dc_plan_flush_device(W, dtype, bucket_col, bucket_numel, tasks, num_tasks, o
         W, dtype, bucket_col, bucket_numel, _dev(tasks), num_tasks, _dev(owner), _dev(flat_offset),
         _dev(part_size), num_params, cp, num_comms, _dev(tiles), capacity, ctypes.byref(n),
         _dev(root_tiles), s))
+    return n.value
+
+
+def dc_plan_flush_buffers_device(W, dtype, bucket_numel, tasks, num_tasks, comms, num_comms, tiles,
+                                 capacity, stream=None):
+    """tasks, tiles: device pointers (tensors or ints) or None.  Returns the
+    tile count; with tiles None it only asks for it (nothing is launched)."""
+    cp, _a = _host(comms, COMM_DTYPE)
+    n = ctypes.c_int64(0)
+    s = _stream(stream) if tiles is not None else stream
+    _check("dc_plan_flush_buffers_device", lib().dc_plan_flush_buffers_device(
+        W, dtype, bucket_numel, _dev(tasks), num_tasks, cp, num_comms, _dev(tiles), capacity,
+        ctypes.byref(n), s))
+    return n.value
+
+
+def dc_plan_relayout_tiles_device(dtype, bucket_col, bucket_numel, pieces, num_pieces, out_numel,
+                                  tiles, tiles_capacity, stream=None):
+    """pieces, tiles: device pointers (tensors or ints) or None.  Returns the
+    tile count; with tiles None it only asks for it (nothing is launched)."""
+    n = ctypes.c_int64(0)
+    s = _stream(stream) if tiles is not None else stream
+    _check("dc_plan_relayout_tiles_device", lib().dc_plan_relayout_tiles_device(
+        dtype, bucket_col, bucket_numel, _dev(pieces), num_pieces, out_numel, _dev(tiles),
+        tiles_capacity, ctypes.byref(n), s))
     return n.value
 
 

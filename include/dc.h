@@ -420,6 +420,23 @@ dc_status dc_plan_flush_buffers(int32_t W, int32_t dtype, int64_t bucket_numel, 
                                 int32_t num_tasks, const dc_comm* comms, int32_t num_comms,
                                 dc_tile* tiles, int64_t capacity, int64_t* num_tiles);
 
+/* dc_plan_flush_buffers' records computed on the device, bit for bit, from a
+ * task table in device memory (one thread per tile, binary search of the
+ * task offsets): no host copy and no synchronization.
+ *   tasks             device dc_task[num_tasks] in buffer coordinates; must
+ *                     pass dc_validate_buffer_tasks (not checked here:
+ *                     another table gives other records, every read and
+ *                     write stays in the table and the plan)
+ *   comms, num_comms  host, checked as for dc_plan_flush_buffers
+ *   tiles, capacity   device dc_tile[capacity] out; NULL asks for the count
+ *                     only (nothing is launched)
+ *   num_tiles         host out: the tile count (dc_plan_flush_buffers')
+ * Fewer than *num_tiles slots is DC_ERR_SHAPE.  Stream-ordered. */
+dc_status dc_plan_flush_buffers_device(int32_t W, int32_t dtype, int64_t bucket_numel,
+                                       const dc_task* tasks, int32_t num_tasks,
+                                       const dc_comm* comms, int32_t num_comms, dc_tile* tiles,
+                                       int64_t capacity, int64_t* num_tiles, void* stream);
+
 /* dc_flush_bucket_buffers with a plan from dc_plan_flush_buffers: the same
  * results, bit for bit.  A tile the plan marks whole, whose task the kernel
  * finds covering the tile and whose W input and output pointers are 16-byte
@@ -554,6 +571,22 @@ dc_status dc_relayout_bucket(int32_t W, int32_t dtype, const void* slab_in, int6
 dc_status dc_plan_relayout_tiles(int32_t dtype, int64_t bucket_col, int64_t bucket_numel,
                                  const dc_piece* pieces, int32_t num_pieces, int64_t out_numel,
                                  int64_t* tiles, int64_t tiles_capacity, int64_t* num_tiles);
+
+/* dc_plan_relayout_tiles' records computed on the device, bit for bit, from
+ * a piece table in device memory (one thread per destination tile, binary
+ * search of the pieces' destinations): no host copy and no synchronization.
+ *   pieces            device dc_piece[num_pieces]; must be sorted by dst with
+ *                     no negative length (not checked here: another table
+ *                     gives other records, every read and write stays in the
+ *                     table and the plan)
+ *   tiles, capacity   device int64[capacity] out; NULL asks for the count
+ *                     only (nothing is launched)
+ *   num_tiles         host out: the tile count (dc_plan_relayout_tiles')
+ * Other arguments and checks as for dc_plan_relayout_tiles.  Stream-ordered. */
+dc_status dc_plan_relayout_tiles_device(int32_t dtype, int64_t bucket_col, int64_t bucket_numel,
+                                        const dc_piece* pieces, int32_t num_pieces,
+                                        int64_t out_numel, int64_t* tiles, int64_t tiles_capacity,
+                                        int64_t* num_tiles, void* stream);
 
 /* dc_relayout_bucket from a tile plan: the same result, bit for bit.  A
  * tile with a record copies straight from it; any other tile searches the

@@ -534,6 +534,36 @@ def test_plan_flush_device_argument_checks():
                                          None) == dc.DC_ERR_NULL
 
 
+def test_plan_device_variants_argument_checks():
+    """The fused-flush and relayout device planners' checks, all before any
+    launch; their size queries launch nothing."""
+    f = dc.dc_plan_flush_buffers_device
+    ok = dict(W=8, dtype=0, bucket_numel=5000, tasks=TASK_PTR, num_tasks=2, comms=[(8, 1)],
+              num_comms=1, tiles=FAKE, capacity=2, stream=0)
+    # 625 slots of 8: 10 tiles of 64; no tasks, no tiles
+    assert f(**dict(ok, tiles=None, capacity=0)) == 10
+    assert f(**dict(ok, num_tasks=0, tiles=None, capacity=0)) == 0
+    for code, kw in [(dc.DC_ERR_ARG, dict(W=0)), (dc.DC_ERR_DTYPE, dict(dtype=9)),
+                     (dc.DC_ERR_ARG, dict(comms=[(4, 1)])), (dc.DC_ERR_ARG, dict(bucket_numel=-1)),
+                     (dc.DC_ERR_ARG, dict(num_tasks=-2)),
+                     (dc.DC_ERR_SHAPE, dict(bucket_numel=(1 << 44) + 8)),
+                     (dc.DC_ERR_SHAPE, dict(capacity=9)),
+                     (dc.DC_ERR_NULL, dict(tasks=None, capacity=10))]:
+        expect(code, f, **dict(ok, **kw))
+    g = dc.dc_plan_relayout_tiles_device
+    ok = dict(dtype=1, bucket_col=0, bucket_numel=4096, pieces=TASK_PTR, num_pieces=3,
+              out_numel=4096, tiles=FAKE, tiles_capacity=2, stream=0)
+    # 1024 vectors of 4: 16 tiles of 64
+    assert g(**dict(ok, tiles=None, tiles_capacity=0)) == 16
+    assert g(**dict(ok, out_numel=0, tiles=None, tiles_capacity=0)) == 0
+    for code, kw in [(dc.DC_ERR_DTYPE, dict(dtype=4)), (dc.DC_ERR_ARG, dict(bucket_col=-1)),
+                     (dc.DC_ERR_ARG, dict(out_numel=-1)), (dc.DC_ERR_ARG, dict(num_pieces=-1)),
+                     (dc.DC_ERR_SHAPE, dict(out_numel=(1 << 44) + 4)),
+                     (dc.DC_ERR_SHAPE, dict(tiles_capacity=15)),
+                     (dc.DC_ERR_NULL, dict(pieces=None, tiles_capacity=16))]:
+        expect(code, g, **dict(ok, **kw))
+
+
 def test_flush_planned_argument_checks():
     f = dc.dc_flush_bucket_planned
     ok = dict(W=8, dtype=0, slab_in=FAKE, ld_in=2048, slab_out=FAKE, ld_out=2048, bucket_col=0,
@@ -585,9 +615,12 @@ def _brute_plan_buffers(dtype, numel, tasks):
     return placed
 
 
-def test_plan_flush_buffers_matches_definition():
-    rng = random.Random(12)
-    for k in range(30):
+def buffer_plan_cases(seed, count=30):
+    """Seeded buffer-coordinate task tables: (W, dtype, bucket_numel, tasks,
+    comms), with gaps, empty tasks and offsets on and off slot boundaries."""
+    rng = random.Random(seed)
+    cases = []
+    for _ in range(count):
         W = rng.choice([2, 4, 6, 8, 16])
         dtype = rng.choice([wl.DT_BF16, wl.DT_F32])
         E = 8 if dtype == wl.DT_BF16 else 4
@@ -600,7 +633,12 @@ def test_plan_flush_buffers_matches_definition():
             if rng.random() < 0.5:
                 pos = -(-pos // (4 * E)) * 4 * E
         numel = rows[-1][0] + rows[-1][1] + rng.choice([0, 3, 100])
-        t = dc.tasks_array(rows)
+        cases.append((W, dtype, numel, dc.tasks_array(rows), comms))
+    return cases
+
+
+def test_plan_flush_buffers_matches_definition():
+    for k, (W, dtype, numel, t, comms) in enumerate(buffer_plan_cases(12)):
         got = dc.dc_plan_flush_buffers(W, dtype, numel, t, len(t), comms, len(comms))
         want = _brute_plan_buffers(dtype, numel, t)
         assert np.array_equal(got, want), k
@@ -678,12 +716,12 @@ def _brute_relayout_tiles(dtype, bucket_col, bucket_numel, pieces, out_numel):
     return _xcd_major(recs)
 
 
-def test_plan_relayout_tiles_matches_definition():
-    """dc_plan_relayout_tiles (host code) against the records the header
-    defines: the planner's pieces of small and random workloads at several
-    bucket-start residues, and random piece tables with unaligned sources,
-    gaps and empty pieces."""
-    rng = random.Random(12)
+def relayout_tile_cases(seed):
+    """(dtype, bucket_col, bucket_numel, pieces, out_numel): the relayout
+    planner's pieces of small and random workloads at several bucket-start
+    residues, and random piece tables with unaligned sources, gaps, empty
+    pieces and pieces starting inside earlier ones."""
+    rng = random.Random(seed)
     cases = []
     ws = [wl.tiny_flush()]
     for k in range(5):
@@ -715,8 +753,14 @@ def test_plan_relayout_tiles_matches_definition():
             dst += rng.choice([0, 100, ln // 2]) if overlap else ln
         pieces = np.array(pcs, dc.PIECE_DTYPE) if pcs else np.zeros(0, dc.PIECE_DTYPE)
         cases.append((dt, rng.choice([0, 3, 64, 4096]), numel, pieces, dst + rng.choice([0, 7, 600])))
+    return cases
+
+
+def test_plan_relayout_tiles_matches_definition():
+    """dc_plan_relayout_tiles (host code) against the records the header
+    defines, on relayout_tile_cases."""
     whole = 0
-    for dt, col, numel, pieces, out_numel in cases:
+    for dt, col, numel, pieces, out_numel in relayout_tile_cases(12):
         got = dc.dc_plan_relayout_tiles(dt, col, numel, pieces, len(pieces), out_numel)
         want = _brute_relayout_tiles(dt, col, numel, pieces, out_numel)
         assert np.array_equal(got, want), (dt, col, numel, out_numel)

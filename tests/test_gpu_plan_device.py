@@ -1,9 +1,10 @@
-"""GPU: the device-side flush planner (dc_plan_flush_device).  Its records
-against the tile records the header defines (the brute-force definition of
-the CPU tests) and against the host planner's, bit for bit, with the root
-count; flushes from its plans against the oracle; the full-size layouts'
-plans equal to the host's; a replayed graph of it; and a task table that
-breaks its contract keeps every write inside the plan."""
+"""GPU: the device-side planners (dc_plan_flush_device,
+dc_plan_flush_buffers_device, dc_plan_relayout_tiles_device).  Their records
+against the tile records the header defines (the brute-force definitions of
+the CPU tests) and against the host planners', bit for bit, with the flush
+planner's root count; flushes from its plans against the oracle; the
+full-size layouts' plans equal to the host's; a replayed graph of it; and
+tables that break their contract keep every write inside the plan."""
 import random
 
 import numpy as np
@@ -14,7 +15,8 @@ from gradient_reduction_amd import dc, executor
 from synth import workloads as wl
 from tests import gpu_util as U
 from tests import test_gpu_flush as F
-from tests.test_abi import _brute_plan
+from tests.test_abi import (_brute_plan, _brute_plan_buffers, _brute_relayout_tiles,
+                            buffer_plan_cases, relayout_tile_cases)
 
 pytestmark = pytest.mark.gpu
 
@@ -208,3 +210,124 @@ def test_device_plan_contract_breaking_tables_stay_in_range():
             assert np.all((got["last"] >= -1) & (got["last"] < n))
             assert np.all((got["root"] >= -1) & (got["root"] < 8))
             assert roots == int(np.sum((got["flags"] & 1).astype(bool) & (got["root"] >= 0)))
+
+
+def _device_records(n, fill, call, width=4):
+    """Run `call(buf)` on a device buffer of n records of `width` int32 each
+    plus a guard; check the guard, return the n records' int32 words."""
+    import torch
+    buf = torch.full(((n + GUARD) * width,), fill, dtype=torch.int32, device="cuda")
+    call(buf)
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy()
+    assert np.all(h[n * width:] == fill), "a record past the plan was written"
+    return h[:n * width]
+
+
+def _device_buffer_plan(W, dtype, numel, t, comms):
+    import torch
+    n = dc.dc_plan_flush_buffers_device(W, dtype, numel, None, len(t), comms, len(comms), None, 0)
+    d_t = torch.from_numpy(t.view(np.uint8).copy()).cuda() if len(t) else None
+    words = _device_records(n, -7, lambda buf: dc.dc_plan_flush_buffers_device(
+        W, dtype, numel, d_t, len(t), comms, len(comms), buf, n))
+    return words.view(dc.TILE_DTYPE).copy()
+
+
+def _device_relayout_tiles(dtype, col, numel, pieces, out_numel):
+    import torch
+    n = dc.dc_plan_relayout_tiles_device(dtype, col, numel, None, len(pieces), out_numel, None, 0)
+    d_p = torch.from_numpy(pieces.view(np.uint8).copy()).cuda() if len(pieces) else None
+    words = _device_records(n, -7, lambda buf: dc.dc_plan_relayout_tiles_device(
+        dtype, col, numel, d_p, len(pieces), out_numel, buf, n), width=2)
+    return words.view(np.int64).copy()
+
+
+@pytest.mark.parametrize("seed", [12, 13])
+def test_device_buffer_plan_matches_definition_and_host(seed):
+    """Seeded buffer-coordinate task tables (gaps, empty tasks, offsets on
+    and off slot boundaries, a sub-communicator)."""
+    U.say("device fused plan", seed)
+    for k, (W, dtype, numel, t, comms) in enumerate(buffer_plan_cases(seed)):
+        got = _device_buffer_plan(W, dtype, numel, t, comms)
+        assert np.array_equal(got, _brute_plan_buffers(dtype, numel, t)), k
+        assert np.array_equal(got, dc.dc_plan_flush_buffers(W, dtype, numel, t, len(t), comms,
+                                                             len(comms))), k
+
+
+@pytest.mark.parametrize("name", ["owner_flush_w8", "mixed_flush_w16"])
+def test_device_buffer_plans_of_full_size_layouts(name):
+    """The fused flush's full-size layouts: each bucket's tasks re-laid at
+    128-byte steps in buffer coordinates, as the executor registers them."""
+    w = getattr(wl, name)()
+    step = 128 // w.elem_bytes()
+    comms = [(c.size, c.stride) for c in w.comms]
+    U.say("device fused plans", w.name)
+    for bk in w.buckets:
+        rows, pos = [], 0
+        for x in bk.tasks:
+            rows.append((pos, x.numel, x.param, x.comm))
+            pos = -(-(pos + x.numel) // step) * step
+        t = dc.tasks_array(rows)
+        numel = rows[-1][0] + rows[-1][1]
+        got = _device_buffer_plan(w.W, w.dtype, numel, t, comms)
+        assert np.array_equal(got, dc.dc_plan_flush_buffers(w.W, w.dtype, numel, t, len(t), comms,
+                                                             len(comms)))
+
+
+@pytest.mark.parametrize("seed", [12, 14])
+def test_device_relayout_tiles_match_definition_and_host(seed):
+    """The relayout planner's pieces of seeded workloads at several start
+    residues, and random piece tables (unaligned sources, gaps, empty and
+    overlapping pieces)."""
+    U.say("device relayout plan", seed)
+    whole = 0
+    for dt, col, numel, pieces, out_numel in relayout_tile_cases(seed):
+        got = _device_relayout_tiles(dt, col, numel, pieces, out_numel)
+        assert np.array_equal(got, _brute_relayout_tiles(dt, col, numel, pieces, out_numel))
+        assert np.array_equal(got, dc.dc_plan_relayout_tiles(dt, col, numel, pieces, len(pieces),
+                                                             out_numel))
+        whole += int(np.sum(got >= 0))
+    assert whole > 100
+
+
+def test_device_relayout_tiles_full_size():
+    """Every bucket of the 402.8M-element W = 8 relayout (pieces from
+    dc_plan_relayout over the eight equal partitions)."""
+    w = wl.owner_flush_w8()
+    flat, ps, _, _ = oracle.partition_ids(w.numel, w.group_begin, w.group_parts())
+    psize = np.full(w.P, ps[0], np.int64)
+    U.say("device relayout plans", w.name)
+    for bk in w.buckets:
+        t = dc.tasks_array([(x.offset, x.numel, x.param, x.comm) for x in bk.tasks])
+        pieces, seg = dc.dc_plan_relayout(w.W, t, len(t), flat, psize, w.P)
+        got = _device_relayout_tiles(w.dtype, bk.col, bk.numel, pieces, int(seg[-1]))
+        want = dc.dc_plan_relayout_tiles(w.dtype, bk.col, bk.numel, pieces, len(pieces), int(seg[-1]))
+        assert np.array_equal(got, want) and np.sum(got >= 0) > 0.99 * len(got)
+
+
+def test_device_plan_variants_contract_breaking_tables_stay_in_range():
+    """Task and piece tables that break their contracts (out of order,
+    negative offsets, sizes and sources) give other records, but every
+    record stays in its range and nothing past the plan is written: a fused
+    record's task range inside the table, a relayout record inside the
+    bucket's vectors or -1."""
+    rng = random.Random(93)
+    for k in range(12):
+        n = rng.randint(1, 40)
+        dtype = rng.choice([wl.DT_BF16, wl.DT_F32])
+        E = 8 if dtype == wl.DT_BF16 else 4
+        t = dc.tasks_array([(rng.randint(-5000, 60_000), rng.randint(-100, 9000), rng.randint(-5, 50),
+                             rng.randint(-3, 5)) for _ in range(n)])
+        numel = rng.randint(1, 70_000)
+        U.say("contract-breaking fused/relayout tables", k, n, numel, dtype)
+        got = _device_buffer_plan(8, dtype, numel, t, [(8, 1), (4, 1)])
+        assert np.all((got["first"] >= 0) & (got["first"] < n))
+        assert np.all((got["last"] >= -1) & (got["last"] < n))
+        assert np.all(got["root"] == -1) and np.all((got["flags"] == 0) | (got["flags"] == 1))
+        pieces = np.array([(rng.randint(-3000, numel), rng.randint(-2000, 40_000), rng.randint(-50, 8000), 0)
+                           for _ in range(n)], dc.PIECE_DTYPE)
+        col = rng.randint(0, 5000)
+        out_numel = rng.randint(0, 50_000)
+        rec = _device_relayout_tiles(dtype, col, numel, pieces, out_numel)
+        lo, hi = -(-col // E), (col + numel) // E - 64
+        assert np.all((rec == -1) | ((rec >= lo) & (rec <= hi)))
