@@ -313,7 +313,7 @@ def dc_plan_flush_device(W, dtype, bucket_col, bucket_numel, tasks, num_tasks, o
     None it only asks for it (nothing is launched, no stream is needed)."""
     cp, _a = _host(comms, COMM_DTYPE)
     n = ctypes.c_int64(0)
-    s = _stream(stream) if tiles is not None else stream
+    s = None if tiles is None and stream is None else _stream(stream)
     _check("dc_plan_flush_device", lib().dc_plan_flush_device(
         W, dtype, bucket_col, bucket_numel, _dev(tasks), num_tasks, _dev(owner), _dev(flat_offset),
         _dev(part_size), num_params, cp, num_comms, _dev(tiles), capacity, ctypes.byref(n),
@@ -327,7 +327,7 @@ def dc_plan_flush_buffers_device(W, dtype, bucket_numel, tasks, num_tasks, comms
     tile count; with tiles None it only asks for it (nothing is launched)."""
     cp, _a = _host(comms, COMM_DTYPE)
     n = ctypes.c_int64(0)
-    s = _stream(stream) if tiles is not None else stream
+    s = None if tiles is None and stream is None else _stream(stream)
     _check("dc_plan_flush_buffers_device", lib().dc_plan_flush_buffers_device(
         W, dtype, bucket_numel, _dev(tasks), num_tasks, cp, num_comms, _dev(tiles), capacity,
         ctypes.byref(n), s))
@@ -339,7 +339,7 @@ def dc_plan_relayout_tiles_device(dtype, bucket_col, bucket_numel, pieces, num_p
     """pieces, tiles: device pointers (tensors or ints) or None.  Returns the
     tile count; with tiles None it only asks for it (nothing is launched)."""
     n = ctypes.c_int64(0)
-    s = _stream(stream) if tiles is not None else stream
+    s = None if tiles is None and stream is None else _stream(stream)
     _check("dc_plan_relayout_tiles_device", lib().dc_plan_relayout_tiles_device(
         dtype, bucket_col, bucket_numel, _dev(pieces), num_pieces, out_numel, _dev(tiles),
         tiles_capacity, ctypes.byref(n), s))
