@@ -486,6 +486,44 @@ def flush_oracle(w, y, mode, init="zero", max_buckets=None, sample_buckets=2):
 # Flush workloads
 # ---------------------------------------------------------------------------
 
+def device_plan_check(torch, args, ex, host_plan_s):
+    """The step's plans built again on the device (dc_plan_flush_device, from
+    the device task table and owner map), compared with the host planner's
+    record for record, and the device planner's launches timed as one region
+    per step.  The flushes keep the host's plans."""
+    from gradient_reduction_amd import dc
+    host_tiles, host_roots, host_begin = ex.d_tiles, list(ex.root_tiles), ex.tile_begin.copy()
+    ex.plan(on_device=True)
+    same = (np.array_equal(ex.tile_begin, host_begin) and ex.root_tiles == host_roots
+            and bool(torch.equal(ex.d_tiles, host_tiles)))
+    dev_tiles = ex.d_tiles
+    nb = len(ex.buckets)
+    counts = np.diff(host_begin)
+    roots = torch.empty(max(nb, 1), dtype=torch.int64, device=dev_tiles.device)
+    if ex.zero2:
+        owner, flat, psize = None, ex.d_flat, ex.d_psize
+    else:
+        owner, flat, psize = (ex.d_owner if ex.reduce_to_owner else None), None, None
+
+    def launches():
+        for b, bk in enumerate(ex.buckets):
+            dc.dc_plan_flush_device(ex.W, ex.dtype, bk.col, bk.numel, ex.task_table(b), len(bk.tasks),
+                                    owner, flat, psize, ex.P, ex.comms, len(ex.comms),
+                                    dev_tiles.data_ptr() + 16 * int(host_begin[b]), int(counts[b]),
+                                    roots.data_ptr() + 8 * b)
+    ms = region_launch_ms(torch, args, launches, 1)
+    ex.d_tiles, ex.root_tiles = host_tiles, host_roots
+    log(f"[bench] device-built plans {'equal' if same else 'DIFFER FROM'} the host's; device planner "
+        f"{ms * 1e3:.1f} us per step, host planner {host_plan_s * 1e3:.1f} ms")
+    return {"records_equal_host": same, "device_us_per_step": round(ms * 1e3, 2),
+            "device_us_per_bucket": round(ms * 1e3 / max(nb, 1), 2),
+            "host_ms_per_step": round(host_plan_s * 1e3, 2), "tiles": int(host_begin[-1]),
+            "timing": REGION_TIMING.replace("the kernel's launches", "the planner's launches (one "
+                                            "per bucket, with its root count)"),
+            "what": ("the step's flush plans built on the device (dc_plan_flush_device) against the "
+                     "host planner's, record for record; the flushes use the host's")}
+
+
 def bench_flush(args, w, mode):
     """The step (owner map + every bucket flush) of flush workload w in mode
     "owner", "allreduce" or "zero2"."""
@@ -515,10 +553,14 @@ def bench_flush(args, w, mode):
             log("[bench] " + ex.probe_line(b, b))
     owner = ex.h_owner if mode == "owner" else None
     tiles = None
+    device_plans = None
     if not args.searched:
+        t0 = time.perf_counter()
         ex.plan()
+        host_plan_s = time.perf_counter() - t0
         tiles = np.diff(ex.tile_begin)
         log(f"[bench] flush plans: {tiles.tolist()} records per bucket")
+        device_plans = device_plan_check(torch, args, ex, host_plan_s)
     per_launch = flush_bytes(w, owner, ex.h_psize if zero2 else None, tiles)
     step_bytes = sum(per_launch) + owner_map_bytes(w)
     nb = len(w.buckets)
@@ -571,6 +613,8 @@ def bench_flush(args, w, mode):
                  "value": round(sum(per_launch) / (once_ms / 1e3) / 1e9, 1),
                  "what": "the same step with the owner map built once at init (the issue's design "
                          "points build it at init and reuse it), flushes only"}}
+    if device_plans is not None:
+        extra["device_plans"] = device_plans
     extra["graph_ms_per_step"] = round(graph_step_ms(torch, args, ex.capture_step(x, ld, y, ld)), 4)
     log(f"[bench] owner map once: {once_ms:.4f} ms per step; the step replayed as one HIP graph: "
         f"{extra['graph_ms_per_step']:.4f} ms")
@@ -1409,6 +1453,8 @@ def main():
         w = getattr(wl, fn)(**({"capacity": args.bucket_numel} if args.bucket_numel else {}))
         r = bench_flush(args, w, mode)
         ms, value, roof, extra = r["ms"], r["value"], r["roofline"], r["extra"]
+        if not extra.get("device_plans", {}).get("records_equal_host", True):
+            parity_bad += 1
         name, dtype = w.name, wl.DTYPE_NAME[w.dtype]
         metric = METRIC.format(W=w.W)
         config = {"workload": name, "W": w.W, "elements": w.total, "buckets": len(w.buckets),
@@ -1483,7 +1529,8 @@ def main():
             "system": system_info()}
     print(json.dumps(line), flush=True)
     if parity_bad:
-        log(f"[bench] PARITY FAILURE: {parity_bad} output elements differ from the oracle")
+        log(f"[bench] PARITY FAILURE: {parity_bad} output elements differ from the oracle (or the "
+            f"device-built plans from the host's)")
         sys.exit(PARITY_EXIT)
 
 
