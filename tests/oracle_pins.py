@@ -919,7 +919,9 @@ def pin_ag_step_executors():
     transfers come from a neighbour only; per-step volumes are one chunk
     (ring), at most one per direction (bidirectional) and 2^(j-1) chunks
     (recursive doubling, the printed N = 8 table); ring step s delivers
-    position s of the printed N = 4 table."""
+    position s of the printed N = 4 table; the bidirectional ring's step s is
+    that ring rule run in both directions (chunk (i-s) mod N from the left,
+    (i+s) mod N from the right, once when the two coincide)."""
     ring4 = _ring_table()
     rd8 = {1: 1, 2: 2, 3: 4}
     rng = np.random.default_rng(67)
@@ -960,6 +962,14 @@ def pin_ag_step_executors():
                     for d in range(N):
                         srcs = [src for dd, src, _ in tr if dd == d]
                         assert len(set(srcs)) == len(srcs), (N, s, d)
+                    # each direction is the printed ring rule: at step s node d
+                    # takes chunk (d - s) mod N from its left neighbour and
+                    # (d + s) mod N from its right one; the two coincide only
+                    # at the last step of an even N, where the chunk comes once
+                    want_tr = {(d, (d - 1) % N, (d - s) % N) for d in range(N)}
+                    want_tr |= {(d, (d + 1) % N, (d + s) % N) for d in range(N)
+                                if (d + s) % N != (d - s) % N}
+                    assert {tuple(x) for x in tr} == want_tr, (N, s)
                 else:
                     assert np.all(per_node == 1 << (s - 1)), (N, s)
                     if N == 8:

@@ -97,6 +97,9 @@ MUTANTS = {
     "bidir_chunk_taken_twice": (
         "if (algo == 1 && !held[(int64_t)i * N + nr[i]]) {",
         "if (algo == 1) {"),
+    "bidir_tie_taken_from_right": (
+        "        if (!held[(int64_t)i * N + nl[i]]) {",
+        "        if (!held[(int64_t)i * N + nl[i]] && !(algo == 1 && nl[i] == nr[i])) {"),
     "ag_step_forwards_own_chunk": (
         "        from_left[i] = nl[i];\n",
         "        from_left[i] = from_left[i];\n"),
