@@ -14,6 +14,22 @@
  *        under gradient accumulation"
  *   [AG] "AllGather" (collective-communication notes)
  *
+ * Typical use:
+ *   once per layout   dc_partition_ids, then dc_build_owner_map (device
+ *                     tables); per bucket, dc_validate_tasks on the host
+ *                     copy of its task table and a plan (dc_plan_flush on
+ *                     the host, or dc_plan_flush_device)
+ *   every step        per bucket, as its gradients are complete,
+ *                     dc_flush_bucket_planned (dc_flush_bucket without a
+ *                     plan; dc_flush_bucket_buffers[_planned] to read each
+ *                     rank's own gradient buffers and write the grad buffers)
+ *   under gradient    dc_accumulate for each micro-batch, then one
+ *   accumulation      dc_deferred_reduce (or dc_accumulate_reduce for the
+ *                     last micro-batch) ([MT] What)
+ *   collectives       dc_reduce_scatter / dc_all_gather and their ring-order,
+ *                     step-by-step and relaid (dc_relayout_bucket +
+ *                     dc_reduce_scatter_v) forms
+ *
  * Conventions shared by every function:
  *   - Return value: DC_OK (0) or one of the DC_ERR_* codes below.  Argument
  *     checks run on the host before anything is enqueued; a failed check
