@@ -518,8 +518,9 @@ def device_plan_check(torch, args, ex, host_plan_s):
     return {"records_equal_host": same, "device_us_per_step": round(ms * 1e3, 2),
             "device_us_per_bucket": round(ms * 1e3 / max(nb, 1), 2),
             "host_ms_per_step": round(host_plan_s * 1e3, 2), "tiles": int(host_begin[-1]),
-            "timing": REGION_TIMING.replace("the kernel's launches", "the planner's launches (one "
-                                            "per bucket, with its root count)"),
+            "timing": ("one HIP event pair around args.steps rounds of the step's planner calls "
+                       "(per bucket: the count-clearing kernel and k_plan_flush) issued back to back "
+                       "on the stream after warm-up; device_us_per_step = that time / rounds"),
             "what": ("the step's flush plans built on the device (dc_plan_flush_device) against the "
                      "host planner's, record for record; the flushes use the host's")}
 
