@@ -331,3 +331,40 @@ def test_device_plan_variants_contract_breaking_tables_stay_in_range():
         rec = _device_relayout_tiles(dtype, col, numel, pieces, out_numel)
         lo, hi = -(-col // E), (col + numel) // E - 64
         assert np.all((rec == -1) | ((rec >= lo) & (rec <= hi)))
+
+
+def test_device_planners_on_drawn_layouts():
+    """The property tests' hypothesis-drawn layouts (tests/test_planner_properties.py),
+    planned on the device: every record equal to the brute-force definition,
+    and the flush planner's root count."""
+    from hypothesis import given
+    from tests.test_planner_properties import (SETTINGS, buffer_layouts, flush_layouts,
+                                               relayout_layouts)
+
+    @SETTINGS
+    @given(flush_layouts())
+    def flush(layout):
+        W, dtype, col0, numel, tasks, owner, flat, psize, comms = layout
+        got, roots = _plan_on_device(W, dtype, col0, numel, tasks, owner, flat, psize, len(tasks),
+                                     comms)
+        want = _brute_plan(W, dtype, col0, numel, tasks, owner, flat, psize)
+        assert np.array_equal(got, want) and roots == int(np.sum(want["root"] >= 0))
+
+    @SETTINGS
+    @given(buffer_layouts())
+    def buffers(layout):
+        W, dtype, numel, tasks, comms = layout
+        assert np.array_equal(_device_buffer_plan(W, dtype, numel, tasks, comms),
+                              _brute_plan_buffers(dtype, numel, tasks))
+
+    @SETTINGS
+    @given(relayout_layouts())
+    def relayout(layout):
+        dtype, col, numel, pieces, out_numel = layout
+        assert np.array_equal(_device_relayout_tiles(dtype, col, numel, pieces, out_numel),
+                              _brute_relayout_tiles(dtype, col, numel, pieces, out_numel))
+
+    U.say("device planners on drawn layouts")
+    flush()
+    buffers()
+    relayout()
