@@ -222,3 +222,64 @@ def test_planned_flush_stale_plan_stays_in_slabs():
         sent = U.SENTINEL16 if w.dtype == wl.DT_BF16 else U.SENTINEL32
         assert np.all(got[:, ~span] == sent), f"{w.name}: a write left the buckets' tile grid"
         assert np.array_equal(U.bits(U.to_host(x, w.dtype), w.dtype), hx), f"{w.name}: input changed"
+
+
+def test_flush_on_drawn_layouts():
+    """The property tests' hypothesis-drawn bucket layouts
+    (tests/test_planner_properties.py: W up to 64, sub-communicators, owners
+    in and out of range, ZeRO-2 partitions, any start column) flushed on the
+    GPU, searched and from a host plan, every element against the oracle
+    (which takes the library's reading of owners outside [0, W))."""
+    import torch
+    from hypothesis import given, settings
+    from tests.test_planner_properties import flush_layouts
+
+    @settings(max_examples=100, deadline=None, derandomize=True)
+    @given(flush_layouts())
+    def run(layout):
+        W, dtype, col0, numel, t, owner, flat, psize, comms = layout
+        P = len(t)
+        if flat is not None:
+            # the ZeRO-2 contract: a param's flat range lies inside its W partitions
+            psize = np.where(flat + t["numel"] <= psize * W, psize, 0).astype(np.int64)
+        # the oracle takes the library's reading of owners outside [0, W): AllReduce
+        own_fixed = None if owner is None else np.where((owner >= 0) & (owner < W), owner, -1)
+        ld = max(64, wl.round_up(col0 + numel + 5, 64))
+        scale = wl.sigma_scale(1e-2)
+        x = U.gen_slab(dtype, W, ld, ld, 77, 0, scale)
+        hin = U.host_slab(dtype, W, ld, ld, 77, 0, scale)
+        hout = np.zeros_like(hin)
+        U.bits(hout, dtype)[:] = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
+        offs, sizes = t["offset"].tolist(), t["numel"].tolist()
+        t_comm = t["comm"].tolist()
+        csz, cst = [c for c, _ in comms], [s for _, s in comms]
+        if flat is not None:
+            oracle.flush_zero2(W, dtype, hin, hout, col0, offs, sizes, list(range(P)), t_comm, flat,
+                               psize, csz, cst, 1)
+        else:
+            oracle.flush(W, dtype, hin, hout, col0, offs, sizes, list(range(P)), t_comm, own_fixed,
+                         csz, cst, 1)
+        d_tasks = torch.from_numpy(t.view(np.uint8).copy()).cuda()
+        d_owner = torch.from_numpy(owner).cuda() if owner is not None else None
+        d_flat = torch.from_numpy(flat).cuda() if flat is not None else None
+        d_psize = torch.from_numpy(psize).cuda() if flat is not None else None
+        tiles, roots = dc.dc_plan_flush(W, dtype, col0, numel, t, P, owner, flat, psize, P, comms,
+                                        len(comms))
+        d_tiles = torch.from_numpy(tiles.view(np.uint8).copy()).cuda() if len(tiles) else None
+        for planned in (False, True):
+            y = U.empty_slab(dtype, W, ld)
+            if planned:
+                dc.dc_flush_bucket_planned(W, dtype, x, ld, y, ld, col0, numel, d_tasks, P, d_owner,
+                                           d_flat, d_psize, P, comms, len(comms), 1, d_tiles,
+                                           len(tiles), roots)
+            elif flat is not None:
+                dc.dc_flush_bucket_zero2(W, dtype, x, ld, y, ld, col0, numel, d_tasks, P, d_flat,
+                                         d_psize, P, comms, len(comms), 1)
+            else:
+                dc.dc_flush_bucket(W, dtype, x, ld, y, ld, col0, numel, d_tasks, P, d_owner, P,
+                                   comms, len(comms), 1)
+            torch.cuda.synchronize()
+            assert np.array_equal(U.bits(U.to_host(y, dtype), dtype), U.bits(hout, dtype)), planned
+
+    U.say("flush on drawn layouts")
+    run()
