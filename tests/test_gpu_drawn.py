@@ -1,0 +1,122 @@
+"""GPU: the slab collectives and the deferred path on hypothesis-drawn shapes
+(derandomized, so every run draws the same cases): W from 1 to 64, both
+dtypes, shard lengths and column counts from empty to several tiles with
+ragged tails, padded row strides, pre-division on and off.  Every output
+element against the oracle, bit for bit."""
+import numpy as np
+import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
+
+import oracle
+from gradient_reduction_amd import dc
+from synth import workloads as wl
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+SET = settings(max_examples=120, deadline=None, derandomize=True)
+SCALE = wl.sigma_scale(1e-2)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dc.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _host_sentinel(dtype, rows, ld):
+    a = np.zeros((rows, ld), np.uint16 if dtype == wl.DT_BF16 else np.float32)
+    U.bits(a, dtype)[:] = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
+    return a
+
+
+def _same(dev, host, dtype):
+    return np.array_equal(U.bits(U.to_host(dev, dtype), dtype), U.bits(host, dtype))
+
+
+@st.composite
+def collective_shapes(draw):
+    W = draw(st.sampled_from([1, 2, 3, 4, 5, 7, 8, 12, 16, 33, 64]))
+    dtype = draw(st.sampled_from([wl.DT_BF16, wl.DT_F32]))
+    L = draw(st.one_of(st.integers(0, 70), st.integers(0, 3000), st.sampled_from([64, 512, 1024])))
+    pad_in = draw(st.sampled_from([0, 8, 64, 8000]))
+    pad_sh = draw(st.sampled_from([0, 8, 24]))
+    pre = draw(st.integers(0, 1))
+    seed = draw(st.integers(0, 1000))
+    return W, dtype, L, pad_in, pad_sh, pre, seed
+
+
+def test_reduce_scatter_and_all_gather_on_drawn_shapes():
+    """dc_reduce_scatter, then dc_all_gather of its shards in rank and in
+    ring order ([AG] eq:ag-semantic-output, Ring AllGather)."""
+    import torch
+
+    @SET
+    @given(collective_shapes())
+    def run(shape):
+        W, dtype, L, pad_in, pad_sh, pre, seed = shape
+        M = W * L
+        ld = wl.round_up(max(M, 1), 8) + pad_in
+        ld_sh = wl.round_up(max(L, 1), 8) + pad_sh
+        x = U.gen_slab(dtype, W, ld, M, seed, 0, SCALE)
+        hin = U.host_slab(dtype, W, ld, M, seed, 0, SCALE)
+        sh = U.empty_slab(dtype, W, ld_sh)
+        dc.dc_reduce_scatter(W, dtype, x, ld, sh, ld_sh, M, pre)
+        want_sh = _host_sentinel(dtype, W, ld_sh)
+        oracle.reduce_scatter(W, dtype, hin, want_sh, M, pre)
+        torch.cuda.synchronize()
+        assert _same(sh, want_sh, dtype), ("reduce-scatter", shape)
+        for order in (dc.DC_ORDER_RANK, dc.DC_ORDER_RING):
+            out = U.empty_slab(dtype, W, ld)
+            dc.dc_all_gather(W, dtype, sh, ld_sh, out, ld, L, order, -1)
+            want = _host_sentinel(dtype, W, ld)
+            oracle.all_gather(W, dtype, want_sh, want, L, order)
+            torch.cuda.synchronize()
+            assert _same(out, want, dtype), ("all-gather", order, shape)
+
+    U.say("reduce-scatter / all-gather on drawn shapes")
+    run()
+
+
+@st.composite
+def deferred_shapes(draw):
+    W = draw(st.sampled_from([1, 2, 3, 4, 8, 16]))
+    M = draw(st.one_of(st.integers(0, 100), st.integers(0, 5000)))
+    K = draw(st.integers(1, 4))
+    out_rows = draw(st.sampled_from([1, W]))
+    pad = draw(st.sampled_from([0, 4, 12, 400]))
+    seed = draw(st.integers(0, 1000))
+    return W, M, K, out_rows, pad, seed
+
+
+def test_accumulate_and_deferred_reduce_on_drawn_shapes():
+    """K replica-local accumulates from a zero start, then the deferred
+    cross-replica reduce ([MT] What): the accumulators and the reduced rows."""
+    import torch
+
+    @SET
+    @given(deferred_shapes())
+    def run(shape):
+        W, M, K, out_rows, pad, seed = shape
+        ld = wl.round_up(max(M, 1), 4) + pad
+        acc = U.empty_slab(wl.DT_F32, W, ld)
+        h_acc = _host_sentinel(wl.DT_F32, W, ld)
+        for k in range(K):
+            x = U.gen_slab(wl.DT_F32, W, ld, M, seed, k * W, SCALE)
+            hx = U.host_slab(wl.DT_F32, W, ld, M, seed, k * W, SCALE)
+            dc.dc_accumulate(W, x, ld, acc, ld, M, 1 if k == 0 else 0)
+            oracle.accumulate(W, hx, h_acc, M, 1 if k == 0 else 0)
+        out = U.empty_slab(wl.DT_F32, out_rows, ld)
+        dc.dc_deferred_reduce(W, acc, ld, out, ld, M, out_rows)
+        h_out = _host_sentinel(wl.DT_F32, out_rows, ld)
+        oracle.deferred_reduce(W, h_acc, h_out, M, out_rows)
+        torch.cuda.synchronize()
+        assert _same(acc, h_acc, wl.DT_F32), ("accumulators", shape)
+        assert _same(out, h_out, wl.DT_F32), ("deferred reduce", shape)
+
+    U.say("accumulate / deferred reduce on drawn shapes")
+    run()
