@@ -120,3 +120,72 @@ def test_accumulate_and_deferred_reduce_on_drawn_shapes():
 
     U.say("accumulate / deferred reduce on drawn shapes")
     run()
+
+
+def test_ring_reduce_scatter_and_all_gather_steps_on_drawn_shapes():
+    """The ring-order reduce-scatter (shard s folded in the order s, s+1, ...),
+    and every step of the ring, bidirectional-ring and (at powers of two)
+    recursive-doubling all-gather schedules replayed one launch per step, the
+    output checked after each step ([AG] Ring AllGather, eq:ag-bidir-ring,
+    Recursive Doubling AllGather)."""
+    import torch
+
+    @SET
+    @given(collective_shapes())
+    def run(shape):
+        W, dtype, L, pad_in, pad_sh, pre, seed = shape
+        M = W * L
+        ld = wl.round_up(max(M, 1), 8) + pad_in
+        ld_sh = wl.round_up(max(L, 1), 8) + pad_sh
+        x = U.gen_slab(dtype, W, ld, M, seed, 0, SCALE)
+        hin = U.host_slab(dtype, W, ld, M, seed, 0, SCALE)
+        sh = U.empty_slab(dtype, W, ld_sh)
+        dc.dc_reduce_scatter_ring(W, dtype, x, ld, sh, ld_sh, M, pre)
+        want_sh = _host_sentinel(dtype, W, ld_sh)
+        oracle.reduce_scatter_ring(W, dtype, hin, want_sh, M, pre)
+        torch.cuda.synchronize()
+        assert _same(sh, want_sh, dtype), ("ring reduce-scatter", shape)
+        algos = [dc.DC_SCHED_RING, dc.DC_SCHED_BIDIR]
+        if W & (W - 1) == 0:
+            algos.append(dc.DC_SCHED_RD)
+        steps = {dc.DC_SCHED_RING: W - 1, dc.DC_SCHED_BIDIR: W // 2,
+                 dc.DC_SCHED_RD: W.bit_length() - 1}
+        for algo in algos:
+            out = U.empty_slab(dtype, W, ld)
+            want = _host_sentinel(dtype, W, ld)
+            for s in range(steps[algo] + 1):
+                dc.dc_all_gather_step(W, dtype, sh, ld_sh, out, ld, L, algo, s)
+                oracle.all_gather_step(W, dtype, want_sh, want, L, algo, s)
+                torch.cuda.synchronize()
+                assert _same(out, want, dtype), ("all-gather step", algo, s, shape)
+
+    U.say("ring reduce-scatter / all-gather steps on drawn shapes")
+    run()
+
+
+def test_fused_accumulate_reduce_on_drawn_shapes():
+    """The last accumulate fused into the deferred reduce, keeping the
+    accumulator or not, against the oracle's accumulate then reduce."""
+    import torch
+
+    @SET
+    @given(deferred_shapes(), st.integers(0, 1), st.integers(0, 1))
+    def run(shape, init, keep):
+        W, M, K, out_rows, pad, seed = shape
+        ld = wl.round_up(max(M, 1), 4) + pad
+        acc = U.gen_slab(wl.DT_F32, W, ld, M, seed + 1, 0, SCALE)
+        h_acc = U.host_slab(wl.DT_F32, W, ld, M, seed + 1, 0, SCALE)
+        x = U.gen_slab(wl.DT_F32, W, ld, M, seed, 7 * W, SCALE)
+        hx = U.host_slab(wl.DT_F32, W, ld, M, seed, 7 * W, SCALE)
+        out = U.empty_slab(wl.DT_F32, out_rows, ld)
+        dc.dc_accumulate_reduce(W, x, ld, acc, ld, init, keep, out, ld, out_rows, M)
+        h_acc2 = h_acc.copy()
+        oracle.accumulate(W, hx, h_acc2, M, init)
+        h_out = _host_sentinel(wl.DT_F32, out_rows, ld)
+        oracle.deferred_reduce(W, h_acc2, h_out, M, out_rows)
+        torch.cuda.synchronize()
+        assert _same(out, h_out, wl.DT_F32), ("fused reduce", shape, init, keep)
+        assert _same(acc, h_acc2 if keep else h_acc, wl.DT_F32), ("accumulator", shape, init, keep)
+
+    U.say("fused accumulate-reduce on drawn shapes")
+    run()
