@@ -189,3 +189,52 @@ def test_fused_accumulate_reduce_on_drawn_shapes():
 
     U.say("fused accumulate-reduce on drawn shapes")
     run()
+
+
+@st.composite
+def relayout_workloads(draw):
+    W = draw(st.sampled_from([1, 2, 3, 4, 5, 8, 16]))
+    dtype = draw(st.sampled_from([wl.DT_BF16, wl.DT_F32]))
+    sizes = draw(st.lists(st.one_of(st.integers(0, 20), st.integers(0, 3000),
+                                    st.sampled_from([64, 1024, 4096])), min_size=1, max_size=40))
+    split = draw(st.integers(0, len(sizes)))
+    capacity = draw(st.sampled_from([500, 5000, 20_000, 10 ** 6]))
+    pre = draw(st.integers(0, 1))
+    seed = draw(st.integers(0, 1000))
+    return wl.custom_flush("drawn", W, dtype, sizes, group_begin=[0, split, len(sizes)],
+                           group_comm=[0, 0], comms=[wl.Comm(W, 1)], capacity=capacity,
+                           pre_div=pre, value_seed=seed)
+
+
+def test_relayout_and_reduce_scatter_v_on_drawn_workloads():
+    """Every bucket of drawn workloads (two parameter groups, buckets of any
+    start residue, empty and one-element tensors) relaid by destination rank,
+    searched and from its tile plan, then reduced by reduce-scatter-v: the
+    relaid slab and the shards against the oracle's relayout map and
+    reduce-scatter-v ([DS] "Describe alternatives")."""
+    from tests import test_gpu_relayout as TR
+
+    @settings(max_examples=60, deadline=None, derandomize=True)
+    @given(relayout_workloads(), st.booleans())
+    def run(w, planned):
+        ld = w.ld
+        x = U.gen_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, w.scale)
+        hx = U.host_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, w.scale)
+        sent = U.SENTINEL16 if w.dtype == wl.DT_BF16 else U.SENTINEL32
+        for b, bk in enumerate(w.buckets):
+            relaid, shards, seg, pieces, flat, psize = TR.run_bucket(w, b, x, ld, planned=planned)
+            dest, oseg = oracle.relayout_map(w.W, [k.offset for k in bk.tasks],
+                                             [k.numel for k in bk.tasks], [k.param for k in bk.tasks],
+                                             [k.comm for k in bk.tasks], flat, psize, bk.numel)
+            assert np.array_equal(seg, oseg)
+            hr = np.zeros_like(relaid)
+            U.bits(hr, w.dtype)[:] = sent
+            oracle.relayout_apply(w.W, w.dtype, hx, hr, bk.col, bk.numel, dest)
+            assert np.array_equal(U.bits(relaid, w.dtype), U.bits(hr, w.dtype)), (b, planned)
+            hs = np.zeros_like(shards)
+            U.bits(hs, w.dtype)[:] = sent
+            oracle.reduce_scatter_v(w.W, w.dtype, hr, hs, oseg, w.pre_div)
+            assert np.array_equal(U.bits(shards, w.dtype), U.bits(hs, w.dtype)), (b, planned)
+
+    U.say("relayout + reduce-scatter-v on drawn workloads")
+    run()
