@@ -238,3 +238,27 @@ def test_relayout_and_reduce_scatter_v_on_drawn_workloads():
 
     U.say("relayout + reduce-scatter-v on drawn workloads")
     run()
+
+
+def test_fused_flush_on_drawn_layouts():
+    """The flush with copy-in and copy-out fused in, on drawn task sizes,
+    holder sets, buffer placements (aligned or not, packed or padded task
+    coordinates, in place or not), searched and planned, W from 1 to 64 with
+    sub-communicators: every element of every buffer against the oracle's
+    or_flush_buffers ([DS] problem statement: copy-in and copy-out around
+    the bucket)."""
+    from tests import test_gpu_flush_buffers as FB
+
+    sizes = st.lists(st.one_of(st.integers(0, 20), st.integers(0, 5000),
+                               st.sampled_from([64, 1000, 4099, 8197])), min_size=1, max_size=16)
+
+    @settings(max_examples=80, deadline=None, derandomize=True)
+    @given(st.sampled_from(FB.CASES), sizes, st.integers(0, 10 ** 6),
+           st.sampled_from([(True, True), (True, False), (False, True)]), st.booleans(),
+           st.booleans())
+    def run(case, numel, seed, aligned_padded, inplace, planned):
+        W, dtype, pre, comms = case
+        FB.run_case(W, dtype, pre, comms, numel, seed, aligned_padded[0], aligned_padded[1], inplace,
+                    planned=planned)
+
+    run()
