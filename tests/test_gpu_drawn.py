@@ -262,3 +262,44 @@ def test_fused_flush_on_drawn_layouts():
                     planned=planned)
 
     run()
+
+
+@st.composite
+def flush_workloads(draw):
+    W = draw(st.sampled_from([1, 2, 3, 4, 6, 8, 12, 16, 32, 64]))
+    dtype = draw(st.sampled_from([wl.DT_BF16, wl.DT_F32]))
+    sizes = draw(st.lists(st.one_of(st.integers(0, 20), st.integers(0, 4000),
+                                    st.sampled_from([512, 1024, 4096, 9000])), min_size=1, max_size=50))
+    P = len(sizes)
+    a = draw(st.integers(0, P))
+    b = draw(st.integers(a, P))
+    comms = [wl.Comm(W, 1)]
+    divs = [c for c in range(1, W) if W % c == 0]
+    group_comm = [0, 0, 0]
+    if divs and draw(st.booleans()):
+        c = draw(st.sampled_from(divs))
+        comms.append(wl.Comm(c, draw(st.sampled_from([1, W // c]))))
+        group_comm[2] = 1
+    return wl.custom_flush("drawn", W, dtype, sizes, group_begin=[0, a, b, P], group_comm=group_comm,
+                           comms=comms, capacity=draw(st.sampled_from([700, 6000, 40_000, 10 ** 6])),
+                           pre_div=draw(st.integers(0, 1)), value_seed=draw(st.integers(0, 1000)),
+                           arrival=draw(st.permutations(list(range(P)))))
+
+
+def test_owner_map_flush_and_probe_on_drawn_workloads():
+    """Drawn workloads -- three parameter groups (one possibly on a
+    sub-communicator), empty and one-element tensors, any arrival order and
+    bucket capacity -- through the executor: partition lists, owner map and
+    counts, the flush of every bucket (AllReduce, reduce-to-owner or ZeRO-2;
+    searched, host-planned or device-planned) and the probe records, all
+    against the oracle ([DS] Design points, problem statement)."""
+    from tests import test_gpu_flush as F
+
+    @settings(max_examples=60, deadline=None, derandomize=True)
+    @given(flush_workloads(), st.sampled_from(["allreduce", "owner", "zero2"]),
+           st.sampled_from([False, True, "device"]))
+    def run(w, mode, planned):
+        F.test_partition_ids_and_owner_map(w)
+        F.flush_case(w, mode == "owner", zero2=mode == "zero2", planned=planned)
+
+    run()
