@@ -225,7 +225,7 @@ class Zero1FlushExecutor:
         return dc.dc_holders(self.W, t, len(t), self.P, self.h_pid_off, self.h_pids, self.comms,
                              len(self.comms))
 
-    def register_buffers(self, in_addr: np.ndarray, out_addr: np.ndarray, planned: bool = True) -> None:
+    def register_buffers(self, in_addr: np.ndarray, out_addr: np.ndarray, planned=True) -> None:
         """in_addr, out_addr: [W, P] device addresses of rank r's gradient of
         param p and of its grad buffer (0 = empty buffer).  A task's slice
         starts at its position within its param (the params' tasks in bucket
@@ -234,7 +234,9 @@ class Zero1FlushExecutor:
         wave's accesses on whole cache lines.  Tables are validated on the
         host and kept on the device; with planned (the default) each bucket's
         tile plan (dc_plan_flush_buffers) is built here too, and flush_buffers
-        launches the planned kernel."""
+        launches the planned kernel.  planned="device": the same plans from
+        dc_plan_flush_buffers_device, built on the device from the uploaded
+        task tables."""
         torch = self.torch
         W = self.W
         eb = 2 if self.dtype == dc.DC_BF16 else 4
@@ -265,7 +267,11 @@ class Zero1FlushExecutor:
             outs.append(tout.ravel())
             self.buf_extent.append(extent)
             self.buf_begin.append(self.buf_begin[-1] + len(t))
-            if planned:
+            if planned == "device":
+                n = dc.dc_plan_flush_buffers_device(W, self.dtype, extent, None, len(t), self.comms,
+                                                    len(self.comms), None, 0)
+                self.buf_tile_begin.append(self.buf_tile_begin[-1] + n)
+            elif planned:
                 pl = dc.dc_plan_flush_buffers(W, self.dtype, extent, t, len(t), self.comms,
                                               len(self.comms))
                 plans.append(pl)
@@ -276,7 +282,20 @@ class Zero1FlushExecutor:
         self.d_bin = torch.from_numpy(np.concatenate(ins).view(np.int64)).to(dev)
         self.d_bout = torch.from_numpy(np.concatenate(outs).view(np.int64)).to(dev)
         self.d_btiles = None
-        if planned:
+        if planned == "device":
+            self.d_btiles = torch.empty(16 * max(int(self.buf_tile_begin[-1]), 1), dtype=torch.uint8,
+                                        device=dev)
+            for b in range(len(self.buckets)):
+                n = int(self.buf_tile_begin[b + 1] - self.buf_tile_begin[b])
+                k = self.buf_begin[b + 1] - self.buf_begin[b]
+                if n == 0:
+                    continue
+                dc.dc_plan_flush_buffers_device(
+                    W, self.dtype, self.buf_extent[b], self.d_btasks.data_ptr() + 32 * self.buf_begin[b],
+                    k, self.comms, len(self.comms),
+                    self.d_btiles.data_ptr() + 16 * int(self.buf_tile_begin[b]), n)
+            torch.cuda.synchronize()   # the plans are ready for a flush on any stream
+        elif planned:
             allp = np.concatenate(plans) if plans else np.zeros(0, dc.TILE_DTYPE)
             raw = allp.view(np.uint8).copy() if len(allp) else np.zeros(16, np.uint8)
             self.d_btiles = torch.from_numpy(raw).to(dev)

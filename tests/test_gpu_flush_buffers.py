@@ -234,11 +234,13 @@ def test_flush_buffers_mixed_w16_full_size():
     _check_sampled(w, d_out, ld, poff, pcol, hold)
 
 
-def test_flush_buffers_split_params_via_executor():
+@pytest.mark.parametrize("planned", [True, "device"], ids=["host-plans", "device-plans"])
+def test_flush_buffers_split_params_via_executor(planned):
     """Params split over buckets through the executor: each task's slice
     continues where the param's previous task ended, in the input buffers and
     in the holders' grad buffers; the whole output arena matches the oracle
-    (sentinel wherever no holder keeps a buffer)."""
+    (sentinel wherever no holder keeps a buffer).  The plans are built on the
+    host or on the device (the same records, compared here)."""
     import torch
     W, dtype, pre = 4, wl.DT_BF16, 1
     numel = [100, 5000, 37, 777, 4096]
@@ -270,7 +272,13 @@ def test_flush_buffers_split_params_via_executor():
     po = np.array(poff, np.int64)[None, :]
     in_addr = (x.data_ptr() + (rows + po) * eb).astype(np.uint64)
     out_addr = np.where(hold, y.data_ptr() + (rows + po) * eb, 0).astype(np.uint64)
-    ex.register_buffers(in_addr, out_addr)
+    ex.register_buffers(in_addr, out_addr, planned=planned)
+    if planned == "device":
+        dev_tiles, dev_begin = ex.d_btiles.cpu().numpy(), list(ex.buf_tile_begin)
+        ex.register_buffers(in_addr, out_addr, planned=True)
+        assert dev_begin == list(ex.buf_tile_begin)
+        assert np.array_equal(dev_tiles, ex.d_btiles.cpu().numpy())
+        ex.register_buffers(in_addr, out_addr, planned=planned)
     for b in range(len(buckets)):
         ex.flush_buffers(b)
     torch.cuda.synchronize()

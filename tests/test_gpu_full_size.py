@@ -221,7 +221,8 @@ def test_reduce_scatter_all_gather_7b_layer_every_column():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("planned", [True, False], ids=["planned", "searched"])
+@pytest.mark.parametrize("planned", [True, False, "device"],
+                         ids=["planned", "searched", "planned-on-device"])
 def test_flush_buffers_w8_402m_every_element(planned):
     """The fused copy-in / copy-out flush of the 402.8M-element W = 8
     gradient (DeepSpeed issue, problem statement: the copy-out skips every
@@ -232,7 +233,8 @@ def test_flush_buffers_w8_402m_every_element(planned):
     sentinel."""
     import torch
     w = wl.owner_flush_w8()
-    U.say("whole-output fused flush", w.name, "planned" if planned else "searched")
+    U.say("whole-output fused flush", w.name,
+          {True: "planned", False: "searched", "device": "planned on the device"}[planned])
     ex, d_out, ld, poff, pcol, hold = U.fused_flush_full_size(w, planned)
     got = d_out.cpu().numpy().view(np.uint16)
     del d_out
