@@ -20,8 +20,9 @@ for bit over every column of every row:
     gradient all-reduce to update() under gradient accumulation", What);
   * the 7B-layer W = 8 bf16 reduce-scatter and the all-gather in rank and
     in ring order ("AllGather", semantic definition and Ring AllGather);
-  * the W = 8 fused copy-in / copy-out flush, searched and planned: every
-    element of every rank's grad-buffer arena.
+  * the W = 8 fused copy-in / copy-out flush, searched and planned (plans
+    built on the host and on the device): every element of every rank's
+    grad-buffer arena.
 """
 import numpy as np
 import pytest
