@@ -212,6 +212,66 @@ class Zero1FlushExecutor:
             self.log(self.probe_line(b, self.flushes))
         self.flushes += 1
 
+    # -- relayout by destination rank + reduce-scatter-v ------------------------
+
+    def plan_relayout(self, planned=True) -> None:
+        """The reduce-scatter alternative of the flush ([DS] "Describe
+        alternatives"): per bucket, the relayout's pieces and segment starts
+        (dc_plan_relayout, from the ZeRO-2 flat offsets and partition sizes:
+        build_owner_map must have run in ZeRO-2 mode) and, with planned, its
+        tile plan (dc_plan_relayout_tiles on the host, or with
+        planned="device" dc_plan_relayout_tiles_device), kept on the device.
+        relayout_reduce_scatter() then runs the path.  Synchronizes."""
+        torch = self.torch
+        if not self.zero2:
+            raise ValueError("plan_relayout needs the executor in ZeRO-2 mode (zero2=True)")
+        dev = self.d_tasks.device
+        flat = self.d_flat[:self.P].cpu().numpy()
+        self.rl = []
+        for b, bk in enumerate(self.buckets):
+            t = self.h_tasks[b]
+            pieces, seg = dc.dc_plan_relayout(self.W, t, len(t), flat, self.h_psize, self.P)
+            n = int(seg[-1])
+            d_pieces = (torch.from_numpy(pieces.view(np.uint8).copy()).to(dev) if len(pieces)
+                        else None)
+            d_tiles, ntiles = None, 0
+            if planned == "device":
+                ntiles = dc.dc_plan_relayout_tiles_device(self.dtype, bk.col, bk.numel, None,
+                                                          len(pieces), n, None, 0)
+                d_tiles = torch.empty(max(ntiles, 1), dtype=torch.int64, device=dev)
+                dc.dc_plan_relayout_tiles_device(self.dtype, bk.col, bk.numel, d_pieces, len(pieces),
+                                                 n, d_tiles, ntiles)
+            elif planned:
+                tiles = dc.dc_plan_relayout_tiles(self.dtype, bk.col, bk.numel, pieces, len(pieces), n)
+                ntiles = len(tiles)
+                d_tiles = torch.from_numpy(tiles).to(dev) if ntiles else None
+            self.rl.append((d_pieces, len(pieces), seg, d_tiles, ntiles if planned else -1))
+        torch.cuda.synchronize()
+
+    def relayout_sizes(self, b: int) -> Tuple[int, int]:
+        """(relaid columns, longest segment) of bucket b: the relaid slab
+        needs ld >= the first, the shards ld >= the second."""
+        seg = self.rl[b][2]
+        return int(seg[-1]), int(max(seg[1:] - seg[:-1])) if len(seg) > 1 else 0
+
+    def relayout_reduce_scatter(self, b: int, slab_in, ld_in: int, relaid, ld_relaid: int, shards,
+                                ld_shards: int, stream=None) -> None:
+        """Bucket b relaid by destination rank into `relaid` ([W, ld_relaid])
+        and reduced by reduce-scatter-v into `shards` ([W, ld_shards]): row q
+        of the shards holds partition q's sums, the values the ZeRO-2 flush
+        writes to row q."""
+        bk = self.buckets[b]
+        d_pieces, npieces, seg, d_tiles, ntiles = self.rl[b]
+        n = int(seg[-1])
+        if ntiles >= 0:
+            dc.dc_relayout_bucket_planned(self.W, self.dtype, slab_in, ld_in, relaid, ld_relaid, bk.col,
+                                          bk.numel, d_pieces, npieces, n, d_tiles, ntiles, stream)
+        else:
+            dc.dc_relayout_bucket(self.W, self.dtype, slab_in, ld_in, relaid, ld_relaid, bk.col,
+                                  bk.numel, d_pieces, npieces, n, stream)
+        dc.dc_reduce_scatter_v(self.W, self.dtype, relaid, ld_relaid, shards, ld_shards, seg,
+                               self.pre_div, stream)
+
     # -- copy-in and copy-out fused into the flush ------------------------------
 
     def holders(self, b: int) -> np.ndarray:

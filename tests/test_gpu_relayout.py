@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from gradient_reduction_amd import dc
+from gradient_reduction_amd import dc, executor
 from synth import workloads as wl
 from tests import gpu_util as U
 
@@ -315,3 +315,40 @@ def test_relayout_stale_plan_stays_in_bounds():
         sent = U.SENTINEL16 if dtype == wl.DT_BF16 else U.SENTINEL32
         assert np.all(got[:, out_numel:] == sent), case
         assert np.array_equal(U.bits(U.to_host(x, dtype), dtype), hx), case
+
+
+@pytest.mark.parametrize("planned", [False, True, "device"],
+                         ids=["searched", "host-planned", "device-planned"])
+@pytest.mark.parametrize("w", small_workloads()[::3], ids=lambda w: w.name)
+def test_relayout_reduce_scatter_via_executor(w, planned):
+    """The executor's relayout path (plan_relayout, relayout_reduce_scatter),
+    searched or from tile plans built on the host or on the device: every
+    bucket's relaid slab and shards against the oracle."""
+    import torch
+    U.say("executor relayout", w.name, planned)
+    ld = w.ld
+    x = U.gen_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, w.scale)
+    hx = U.host_slab(w.dtype, w.W, ld, w.total, w.value_seed, 0, w.scale)
+    ex = executor.from_workload(w, reduce_to_owner=False, zero2=True)
+    ex.build_owner_map()
+    ex.plan_relayout(planned=planned)
+    flat, psize = U.psize_per_param(w)
+    sent = U.SENTINEL16 if w.dtype == wl.DT_BF16 else U.SENTINEL32
+    for b, bk in enumerate(w.buckets):
+        n, longest = ex.relayout_sizes(b)
+        ld_r, ld_s = max(64, wl.round_up(n, 64)), max(64, wl.round_up(longest, 64))
+        relaid = U.empty_slab(w.dtype, w.W, ld_r)
+        shards = U.empty_slab(w.dtype, w.W, ld_s)
+        ex.relayout_reduce_scatter(b, x, ld, relaid, ld_r, shards, ld_s)
+        torch.cuda.synchronize()
+        dest, oseg = oracle.relayout_map(w.W, [k.offset for k in bk.tasks], [k.numel for k in bk.tasks],
+                                         [k.param for k in bk.tasks], [k.comm for k in bk.tasks], flat,
+                                         psize, bk.numel)
+        hr = np.zeros((w.W, ld_r), hx.dtype)
+        U.bits(hr, w.dtype)[:] = sent
+        oracle.relayout_apply(w.W, w.dtype, hx, hr, bk.col, bk.numel, dest)
+        assert np.array_equal(U.bits(U.to_host(relaid, w.dtype), w.dtype), U.bits(hr, w.dtype)), b
+        hs = np.zeros((w.W, ld_s), hx.dtype)
+        U.bits(hs, w.dtype)[:] = sent
+        oracle.reduce_scatter_v(w.W, w.dtype, hr, hs, oseg, w.pre_div)
+        assert np.array_equal(U.bits(U.to_host(shards, w.dtype), w.dtype), U.bits(hs, w.dtype)), b
