@@ -74,3 +74,10 @@ def test_register_buffers_rejects_overlap():
     assert e.value.code == dc.DC_ERR_TASKS
 
 
+
+
+def test_deferred_reducer_rejects_short_stride():
+    """DeferredReducer checks its accumulator's stride before allocating."""
+    from gradient_reduction_amd.deferred import DeferredReducer
+    with pytest.raises(ValueError):
+        DeferredReducer(4, 100, ld=64)

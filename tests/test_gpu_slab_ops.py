@@ -549,3 +549,58 @@ def test_accumulator_lifetime_restore_and_round_trip():
     S = sum(np.abs(x[:, :M].astype(np.float64)).sum(axis=0) for x in hxs)
     err = np.abs(D_rt[0, :M].cpu().numpy().astype(np.float64) - D_full[0, :M].cpu().numpy())
     assert np.all(err <= 5e-5 * S)
+
+
+@pytest.mark.parametrize("W,out_rows", [(4, 1), (4, 4), (3, 3), (8, 1)])
+def test_deferred_reducer_steps_and_lifetime(W, out_rows):
+    """gradient_reduction_amd.deferred.DeferredReducer ([MT] What, accumulator
+    lifetime): a step of K micro-batches reduced at update() equals the
+    oracle's accumulate-then-reduce bit for bit; the fused last micro-batch
+    gives the same; a second step starts from zero; and a state saved after
+    two micro-batches, restored into a fresh reducer, finishes the step with
+    the uninterrupted step's result."""
+    import torch
+    from gradient_reduction_amd.deferred import DeferredReducer
+    M, K = 5000 + W, 4
+    ld = wl.round_up(M, 64)
+    scale = wl.sigma_scale(1e-2)
+    xs = [U.gen_slab(wl.DT_F32, W, ld, M, 900 + W, k * W, scale) for k in range(K)]
+    hxs = [U.host_slab(wl.DT_F32, W, ld, M, 900 + W, k * W, scale) for k in range(K)]
+    h_acc = np.zeros((W, ld), np.float32)
+    for k in range(K):
+        oracle.accumulate(W, hxs[k], h_acc, M, 1 if k == 0 else 0)
+    want = np.zeros((out_rows, ld), np.float32)
+    oracle.deferred_reduce(W, h_acc, want, M, out_rows)
+    U.say("deferred reducer", W, out_rows)
+
+    def bits(t):
+        return t.cpu().numpy()[:, :M].view(np.uint32)
+
+    red = DeferredReducer(W, M, ld)
+    for step in range(2):                 # the second step must start from zero
+        for k in range(K):
+            red.accumulate(xs[k], ld)
+        out = torch.zeros((out_rows, ld), dtype=torch.float32, device="cuda")
+        red.reduce(out, ld, out_rows)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), want[:, :M].view(np.uint32)), step
+    for k in range(K - 1):                # the last micro-batch fused into the reduce
+        red.accumulate(xs[k], ld)
+    out = torch.zeros((out_rows, ld), dtype=torch.float32, device="cuda")
+    red.reduce(out, ld, out_rows, last=xs[K - 1], ld_last=ld, keep_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), want[:, :M].view(np.uint32))
+    assert np.array_equal(bits(red.acc), h_acc[:, :M].view(np.uint32))
+    red.accumulate(xs[0], ld)             # save mid-step, restore elsewhere, finish
+    red.accumulate(xs[1], ld)
+    state = red.state_dict()
+    other = DeferredReducer(W, M, ld)
+    other.load_state_dict(state)
+    for k in range(2, K):
+        other.accumulate(xs[k], ld)
+    out = torch.zeros((out_rows, ld), dtype=torch.float32, device="cuda")
+    other.reduce(out, ld, out_rows)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), want[:, :M].view(np.uint32))
+    with pytest.raises(RuntimeError):
+        other.reduce(out, ld, out_rows)   # a new step has no micro-batch yet
